@@ -1,0 +1,341 @@
+"""Plain fp64 CPU oracle for the speculative-sampling verification step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links
+this module; only the tests, the smoke check and the CPU-baseline leg of the
+benchmark do.  It shares no code with the HIP path.
+
+What it computes, step by step, in the pages' notation (p = target
+distribution, q = draft distribution, x = drafted token, K = draft length):
+
+* Each drafted token x_i is accepted with probability min(1, p_i(x_i)/q_i(x_i));
+  on rejection a replacement is drawn from norm(max(0, p - q)).  Sources: page
+  www.cf-1.com/news/5155685 §2.2 (the accept/reject rule and its losslessness)
+  and page www.2kiu.com/news/5895634 §2.2 (same rule, residual written (p-q)_+).
+* Verification walks the positions in order and stops at the first rejection
+  (the first wrong position is rolled back and the target supplies that one
+  token): page www.cf-1.com/news/5155685 §2.1, page www.gsyq.cn/news/428210
+  §3.1 (steps 3 and 4), page www.2kiu.com/news/5895634 §2.
+* When all K drafts are accepted the target's distribution at position K gives
+  one more token.  The pages state this only through the expected count
+  1 + a + ... + a^K of tokens per target forward (page www.gsyq.cn/news/428210
+  §3.2, page www.2kiu.com/news/5895634 §3.1), whose last term is the
+  all-accepted case.
+* Temperature, top-k and top-p are applied identically to p and q: page
+  www.gsyq.cn/news/428210 §3.3 (sampling parameters must be aligned).
+
+Readings where the pages are silent (each is also listed in the design notes):
+
+* Accept test is ``u * q(x) < p(x)`` with u ~ U[0,1): the division-free strict
+  form of "accept with probability min(1, p/q)".  p(x) = 0 never accepts.
+* Uniforms are one [B, K+1] array: column i < K drives the accept test at
+  draft i, column K is the single sampling uniform (residual or bonus).
+* Inverse-CDF sampling runs in ascending vocabulary order:
+  token = min{j : u*Z < C_j}, C the running sum of the weights, Z their total;
+  if round-off leaves no such j, the last token with positive weight is taken.
+* An empty residual (Z == 0, reachable only through round-off) falls back to p.
+* T == 0 means greedy: p and q are one-hot at their arg-max, ties to the
+  lowest index.
+* top-k keeps every token whose scaled logit is >= the k-th largest
+  (duplicates counted, ties kept); top-p then keeps the smallest
+  descending-probability prefix whose mass reaches top_p, again keeping ties
+  of its last member; top-k is applied before top-p, both after temperature.
+* T and top_p are used at the float32 value the C ABI receives.
+* A sequence whose rows include one with every logit -inf (no distribution),
+  or whose drafted token lies outside [0, V), yields the sentinel n = -1 and
+  tokens all -1.  NaN and +inf logits are rejected with ValueError.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "widen",
+    "filtered_probs",
+    "inverse_cdf",
+    "sample_tokens",
+    "verify",
+    "verify_one",
+]
+
+BF16 = "bf16"
+F32 = "f32"
+
+
+# ---------------------------------------------------------------------------
+# input widening (exact)
+# ---------------------------------------------------------------------------
+def widen(logits: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen logits exactly to float64.
+
+    ``dtype == "bf16"``: ``logits`` is a uint16 array of bfloat16 bit patterns;
+    the pattern is the upper half of the float32 with the same value, so the
+    widening is exact.  ``dtype == "f32"``: a float32 array.
+    """
+    if dtype == BF16:
+        a = np.asarray(logits)
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 logits must be given as uint16 bit patterns")
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == F32:
+        a = np.asarray(logits)
+        if a.dtype != np.float32:
+            raise TypeError("f32 logits must be a float32 array")
+        return a.astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _check_params(temperature, top_k, top_p):
+    t = float(np.float32(temperature))
+    if not (t >= 0.0):  # also rejects NaN
+        raise ValueError("temperature must be >= 0")
+    tp = float(np.float32(top_p))
+    if not (0.0 < tp <= 1.0):
+        raise ValueError("top_p must lie in (0, 1]")
+    k = int(top_k)
+    if k < 0:
+        raise ValueError("top_k must be >= 0")
+    return t, k, tp
+
+
+# ---------------------------------------------------------------------------
+# the filtered distribution of one row (A1..A3 of the path)
+# ---------------------------------------------------------------------------
+def filtered_probs(logits: np.ndarray, temperature: float, top_k: int, top_p: float) -> np.ndarray:
+    """Probabilities after temperature, top-k and top-p, for every row.
+
+    ``logits``: float64 array [N, V] (exactly widened).  Returns float64 [N, V].
+    Rows whose logits are all -inf come back as all-NaN (no distribution);
+    callers treat them as bad rows.
+    """
+    T, k, tp = _check_params(temperature, top_k, top_p)
+    z_in = np.asarray(logits, dtype=np.float64)
+    if z_in.ndim != 2:
+        raise ValueError("logits must be 2-D [rows, V]")
+    N, V = z_in.shape
+    out = np.zeros((N, V), dtype=np.float64)
+    if N == 0:
+        return out
+    row_max = z_in.max(axis=1)
+    dead = row_max == -np.inf
+    out[dead] = np.nan
+    live = ~dead
+    if not live.any():
+        return out
+    z = z_in[live]
+    n = z.shape[0]
+    rows = np.arange(n)
+
+    if T == 0.0:
+        # greedy: one-hot at the first (lowest-index) maximum
+        a = np.argmax(z, axis=1)
+        p = np.zeros_like(z)
+        p[rows, a] = 1.0
+        out[live] = p
+        return out
+
+    z = z / T
+    keep = np.ones_like(z, dtype=bool)
+
+    if 0 < k < V:
+        # k-th largest scaled logit, duplicates counted; every token >= it is kept
+        kth = np.partition(z, V - k, axis=1)[:, V - k]
+        keep &= z >= kth[:, None]
+
+    if tp < 1.0:
+        # softmax over the tokens kept so far
+        zk = np.where(keep, z, -np.inf)
+        m = zk.max(axis=1, keepdims=True)
+        e = np.exp(zk - m)
+        pi = e / e.sum(axis=1, keepdims=True)
+        # probabilities in descending order and their running mass
+        desc = -np.sort(-pi, axis=1)
+        mass = np.cumsum(desc, axis=1)
+        reach = mass >= tp
+        # first prefix length whose mass reaches top_p (the whole row if
+        # round-off keeps the total just below top_p)
+        nstar = np.where(reach.any(axis=1), np.argmax(reach, axis=1), V - 1)
+        tau = desc[rows, nstar]
+        keep &= pi >= tau[:, None]
+
+    zk = np.where(keep, z, -np.inf)
+    m = zk.max(axis=1, keepdims=True)
+    e = np.exp(zk - m)
+    out[live] = e / e.sum(axis=1, keepdims=True)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# inverse-CDF sampling in vocabulary order (A6)
+# ---------------------------------------------------------------------------
+def inverse_cdf(w: np.ndarray, u: np.ndarray):
+    """Sample one index per row of non-negative weights ``w`` [N, V].
+
+    token = min{j : u*Z < C_j} with C the running sum of w in index order and
+    Z = sum(w); if round-off leaves no such j, the last j with w_j > 0.
+    Returns (tokens int64 [N], Z float64 [N]).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64).reshape(-1)
+    Z = w.sum(axis=1)
+    C = np.cumsum(w, axis=1)
+    t = u * Z
+    hit = t[:, None] < C
+    tok = np.argmax(hit, axis=1)
+    none = ~hit.any(axis=1)
+    if none.any():
+        pos = w[none] > 0
+        last = w.shape[1] - 1 - np.argmax(pos[:, ::-1], axis=1)
+        tok[none] = last
+    return tok.astype(np.int64), Z
+
+
+def sample_tokens(logits: np.ndarray, temperature, top_k, top_p, u: np.ndarray) -> np.ndarray:
+    """Draw one token per row from the filtered distribution (used to prepare
+    drafted tokens x ~ q for test inputs).  ``u``: float64 uniforms [N]."""
+    q = filtered_probs(logits, temperature, top_k, top_p)
+    if np.isnan(q).any():
+        raise ValueError("cannot sample from a row with no distribution")
+    tok, _ = inverse_cdf(q, u)
+    return tok
+
+
+# ---------------------------------------------------------------------------
+# the verification step (A4..A7)
+# ---------------------------------------------------------------------------
+def _check_finite(x: np.ndarray):
+    if np.isnan(x).any() or np.isposinf(x).any():
+        raise ValueError("NaN or +inf logits are outside the defined input range")
+
+
+def _draft_probs(draft, dtype, T, k, tp):
+    nb, K, V = draft.shape
+    if K == 0:
+        return np.zeros((nb, 0, V))
+    d64 = widen(draft, dtype)
+    _check_finite(d64)
+    Q = filtered_probs(d64.reshape(nb * K, V), T, k, tp).reshape(nb, K, V)
+    if T == 0.0:
+        # Greedy: the outcome does not depend on q.  With p one-hot at a and q
+        # one-hot at b, x is accepted iff x == a, and a rejection's residual is
+        # one-hot at a (or empty, falling back to p); so a draft row with no
+        # distribution is given zero mass instead of making the sequence bad.
+        Q = np.where(np.isnan(Q), 0.0, Q)
+    return Q
+
+
+def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
+           dtype: str = F32, block: int | None = None, diag: bool = False):
+    """Run verification for a batch.
+
+    target: [B, K+1, V] logits (float32, or uint16 bf16 patterns when
+    dtype == "bf16"); draft: [B, K, V]; draft_tokens: [B, K] ints;
+    uniforms: float32 [B, K+1].
+
+    Returns (out_tokens int32 [B, K+1], out_num_accepted int32 [B]) and, when
+    ``diag``, a dict with p(x_i), q(x_i) float64 [B, K] and Z float64 [B].
+    """
+    T, k, tp = _check_params(temperature, top_k, top_p)
+    target = np.asarray(target)
+    draft = np.asarray(draft)
+    X = np.asarray(draft_tokens).astype(np.int64)
+    U = np.asarray(uniforms)
+    if U.dtype != np.float32:
+        raise TypeError("uniforms must be float32")
+    B, K1, V = target.shape
+    K = K1 - 1
+    if draft.shape != (B, K, V) or X.shape != (B, K) or U.shape != (B, K + 1):
+        raise ValueError("shape mismatch")
+    out_tok = np.full((B, K + 1), -1, dtype=np.int32)
+    out_n = np.full((B,), -1, dtype=np.int32)
+    px_all = np.full((B, K), np.nan)
+    qx_all = np.full((B, K), np.nan)
+    Z_all = np.full((B,), np.nan)
+    if B == 0:
+        return (out_tok, out_n, dict(px=px_all, qx=qx_all, Z=Z_all)) if diag else (out_tok, out_n)
+    if block is None:
+        block = max(1, int(2**26 // max(1, (2 * K + 1) * V)))
+    for s in range(0, B, block):
+        e = min(B, s + block)
+        nb = e - s
+        t64 = widen(target[s:e], dtype)
+        _check_finite(t64)
+        P = filtered_probs(t64.reshape(nb * (K + 1), V), T, k, tp).reshape(nb, K + 1, V)
+        del t64
+        Q = _draft_probs(draft[s:e], dtype, T, k, tp)
+        x = X[s:e]
+        u = U[s:e].astype(np.float64)
+        # bad sequences: a row with no distribution, or a drafted token out of range
+        bad = np.isnan(P).any(axis=(1, 2))
+        if T != 0.0 and K > 0:
+            # at T == 0 only the target rows matter (q drops out of the rule)
+            bad |= np.isnan(Q).any(axis=(1, 2))
+        bad |= ((x < 0) | (x >= V)).any(axis=1)
+        xs = np.clip(x, 0, V - 1)
+        ii = np.arange(nb)[:, None]
+        kk = np.arange(K)[None, :]
+        px = P[ii, kk, xs]
+        qx = Q[ii, kk, xs]
+        # accept test at each position
+        acc = u[:, :K] * qx < px
+        # first rejection
+        n = np.where(acc.all(axis=1), K, np.argmin(acc, axis=1)) if K > 0 else np.zeros(nb, np.int64)
+        # sampled row: residual at n < K, bonus at n == K
+        rows_p = P[np.arange(nb), n]
+        w = np.empty((nb, V))
+        rej = n < K
+        if rej.any():
+            nr = n[rej]
+            idx = np.flatnonzero(rej)
+            res = np.maximum(0.0, P[idx, nr] - Q[idx, nr])
+            empty = res.sum(axis=1) == 0.0
+            res[empty] = P[idx[empty], nr[empty]]
+            w[rej] = res
+        w[~rej] = rows_p[~rej]
+        w = np.where(np.isnan(w), 0.0, w)
+        tok, Z = inverse_cdf(w, u[:, K])
+        # emit: accepted drafts, then the sampled token, then -1 padding
+        pos = np.arange(K + 1)[None, :]
+        row = np.where(pos < n[:, None], np.pad(x, ((0, 0), (0, 1))), -1)
+        row = np.where(pos == n[:, None], tok[:, None], row)
+        row[bad] = -1
+        out_tok[s:e] = row
+        out_n[s:e] = np.where(bad, -1, n)
+        px_all[s:e] = px
+        qx_all[s:e] = qx
+        Z_all[s:e] = np.where(bad, np.nan, Z)
+    if diag:
+        return out_tok, out_n, dict(px=px_all, qx=qx_all, Z=Z_all)
+    return out_tok, out_n
+
+
+def verify_one(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype: str = F32):
+    """All intermediate values for one sequence (used to classify a mismatch).
+
+    Returns a dict: P [K+1, V], Q [K, V], px, qx, accept [K], n, w [V],
+    Z, C [V], token.  The arithmetic is exactly that of ``verify``.
+    """
+    out_tok, out_n = verify(target_b[None], draft_b[None], np.asarray(x_b)[None],
+                            np.asarray(u_b, dtype=np.float32)[None],
+                            temperature, top_k, top_p, dtype=dtype)
+    T, k, tp = _check_params(temperature, top_k, top_p)
+    K = draft_b.shape[0]
+    V = target_b.shape[-1]
+    P = filtered_probs(widen(target_b, dtype), T, k, tp)
+    Q = _draft_probs(np.asarray(draft_b)[None], dtype, T, k, tp)[0]
+    x = np.clip(np.asarray(x_b, dtype=np.int64), 0, V - 1)
+    u = np.asarray(u_b, dtype=np.float32).astype(np.float64)
+    px = P[np.arange(K), x]
+    qx = Q[np.arange(K), x]
+    accept = u[:K] * qx < px
+    n = int(out_n[0])
+    if n < 0:
+        return dict(P=P, Q=Q, px=px, qx=qx, accept=accept, n=n, w=None, Z=None, C=None,
+                    token=-1, out_tokens=out_tok[0])
+    if n < K:
+        w = np.maximum(0.0, P[n] - Q[n])
+        if w.sum() == 0.0:
+            w = P[n].copy()
+    else:
+        w = P[K].copy()
+    return dict(P=P, Q=Q, px=px, qx=qx, accept=accept, n=n, w=w, Z=w.sum(),
+                C=np.cumsum(w), token=int(out_tok[0, n]), out_tokens=out_tok[0])

@@ -1,0 +1,152 @@
+"""Pins of the fp64 oracle to facts fixed by the pages and by mathematics (CPU)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import spec_verify as ov
+from tests import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _worked_values():
+    with open(os.path.join(GOLDEN, "worked_values.json")) as f:
+        return json.load(f)["entries"]
+
+
+@pytest.mark.parametrize("e", _worked_values(), ids=lambda e: f"{e['source'].split('/')[0]}-a{e['alpha']}-K{e['K']}")
+def test_worked_values_closed_form(e):
+    """The closed form reproduces every page value marked 'agrees' at the page's
+    two-decimal rounding, and each 'erratum' entry is a genuine disagreement
+    whose correct value is recorded in the fixture."""
+    E = pins.closed_form(e["alpha"], e["K"])
+    if e["status"] == "agrees":
+        assert abs(E - e["page_value"]) <= 0.005 + 1e-12, (E, e)
+    else:
+        assert abs(E - e["page_value"]) > 0.01, (E, e)
+        assert abs(E - e["closed_form"]) < 5e-5, (E, e)
+
+
+def test_erratum_095_is_closed_form_at_k3():
+    # the value printed for K=5 at alpha 0.8 is the closed form at K=3
+    assert abs(pins.closed_form(0.8, 3) - 2.95) <= 0.005
+
+
+@pytest.mark.parametrize("alpha,K", [(0.75, 5), (0.8, 5), (0.6, 6), (0.9, 6), (0.4, 6), (0.8, 3), (0.6, 5)])
+def test_oracle_accept_count_matches_closed_form(alpha, K):
+    """Mean emitted tokens of the oracle on fixed-alpha rows equals
+    (1 - a^(K+1)) / (1 - a) within 4 standard errors, and the accepted count is
+    truncated-geometric.  (0.75, 5) is the pages' 3.29 example."""
+    pins.check_accept_count(ov, alpha, K)
+
+
+@pytest.mark.parametrize("case", ["random", "close", "equal", "disjoint", "masked"])
+def test_oracle_lossless_chi2(case):
+    pins.check_lossless(ov, case, N=1_000_000)
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_oracle_exact_integration(seed):
+    pins.check_exact_integration(ov, seed=seed)
+
+
+def test_oracle_softmax_matches_scipy():
+    pins.check_softmax(ov)
+
+
+def test_oracle_inverse_cdf_matches_searchsorted():
+    pins.check_inverse_cdf(ov)
+
+
+def test_oracle_greedy_is_argmax_matching():
+    pins.check_greedy(ov)
+
+
+def test_oracle_filters_brute_force():
+    pins.check_filters(ov)
+
+
+def test_oracle_zero_weight_tokens():
+    pins.check_zero_weight_never_sampled(ov)
+
+
+def test_topk1_equals_greedy_on_unique_maxima():
+    rng = np.random.default_rng(7)
+    N, K, V = 500, 3, 40
+    tl = rng.normal(0, 1, (N, K + 1, V)).astype(np.float32)
+    dl = (tl[:, :K] + rng.normal(0, 0.5, (N, K, V))).astype(np.float32)
+    x = rng.integers(0, V, (N, K))
+    x[:, 0] = np.argmax(tl[:, 0], axis=1)
+    u = rng.random((N, K + 1), dtype=np.float32)
+    a = oracle.verify(tl, dl, x, u, 1.0, 1, 1.0)
+    b = oracle.verify(tl, dl, x, u, 0.0, 0, 1.0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_filters_off_are_identity():
+    rng = np.random.default_rng(1)
+    z = rng.normal(0, 2, (8, 100))
+    base = oracle.filtered_probs(z, 0.8, 0, 1.0)
+    assert np.array_equal(oracle.filtered_probs(z, 0.8, 100, 1.0), base)
+    assert np.array_equal(oracle.filtered_probs(z, 0.8, 1000, 1.0), base)
+
+
+def test_single_token_vocabulary():
+    N, K = 10, 4
+    tl = np.zeros((N, K + 1, 1), np.float32)
+    dl = np.zeros((N, K, 1), np.float32)
+    tok, n = oracle.verify(tl, dl, np.zeros((N, K), int), np.random.default_rng(0).random((N, K + 1), dtype=np.float32), 1.0, 0, 1.0)
+    assert np.all(n == K) and np.all(tok == 0)
+
+
+def test_no_drafts_is_plain_sampling():
+    rng = np.random.default_rng(2)
+    N, V = 300, 50
+    tl = rng.normal(0, 1, (N, 1, V)).astype(np.float32)
+    u = rng.random((N, 1), dtype=np.float32)
+    tok, n = oracle.verify(tl, np.zeros((N, 0, V), np.float32), np.zeros((N, 0), int), u, 1.0, 0, 1.0)
+    assert np.all(n == 0)
+    P = pins.softmax_rows(tl[:, 0])
+    for r in range(N):
+        C = np.cumsum(P[r])
+        assert tok[r, 0] == np.searchsorted(C, u[r, 0].astype(np.float64) * P[r].sum(), side="right")
+
+
+def test_sentinels():
+    rng = np.random.default_rng(0)
+    B, K, V = 4, 2, 16
+    tl = rng.normal(0, 1, (B, K + 1, V)).astype(np.float32)
+    dl = rng.normal(0, 1, (B, K, V)).astype(np.float32)
+    x = rng.integers(0, V, (B, K))
+    u = rng.random((B, K + 1), dtype=np.float32)
+    tl[1, 2] = -np.inf            # a target row with no distribution
+    x[2, 1] = V                   # a drafted token out of range
+    dl[3, 0] = -np.inf            # a draft row with no distribution
+    tok, n = oracle.verify(tl, dl, x, u, 1.0, 0, 1.0)
+    assert list(n[1:]) == [-1, -1, -1] and n[0] >= 0
+    assert np.all(tok[1:] == -1)
+    # at temperature 0 the draft rows are not part of the rule
+    tok0, n0 = oracle.verify(tl, dl, x, u, 0.0, 0, 1.0)
+    assert n0[3] >= 0 and n0[1] == -1 and n0[2] == -1
+    bad = tl.copy()
+    bad[0, 0, 0] = np.nan
+    with pytest.raises(ValueError):
+        oracle.verify(bad, dl, x, u, 1.0, 0, 1.0)
+
+
+def test_parameter_validation():
+    z = np.zeros((1, 4))
+    for T, k, p in [(-1.0, 0, 1.0), (float("nan"), 0, 1.0), (1.0, -1, 1.0), (1.0, 0, 0.0), (1.0, 0, 1.5)]:
+        with pytest.raises(ValueError):
+            oracle.filtered_probs(z, T, k, p)
+
+
+def test_bf16_widening_is_exact():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    w = oracle.widen(bits, "bf16")
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    finite = np.isfinite(f)
+    assert np.array_equal(w[finite], f[finite].astype(np.float64))
