@@ -1,0 +1,154 @@
+/*
+ * specverify.h - C ABI of the MI355X (gfx950) speculative-sampling
+ * verification library (libspecverify.so).
+ *
+ * The operation: given the target model's logits over K+1 positions and the
+ * draft model's logits over K positions, each drafted token x_i is accepted
+ * with probability min(1, p_i(x_i) / q_i(x_i)); verification stops at the
+ * first rejection and replaces that token with a draw from
+ * norm(max(0, p_i - q_i)); if all K drafts are accepted one more token is
+ * drawn from p_K.  Sources: page www.cf-1.com/news/5155685 section 2.2 and
+ * page www.2kiu.com/news/5895634 section 2.2 (the accept/reject rule and its
+ * lossless output law), page www.gsyq.cn/news/428210 section 3.1 (one target
+ * forward scores every drafted position; positions are judged in order and
+ * the first wrong one is replaced), page www.gsyq.cn/news/428210 section 3.2
+ * and page www.2kiu.com/news/5895634 section 3.1 (1 + a + ... + a^K tokens per
+ * target forward: the last term is the all-accepted draw), and page
+ * www.gsyq.cn/news/428210 section 3.3 (temperature, top-k and top-p applied
+ * identically to the target and the draft).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named *_logits, draft_tokens, uniforms and out_* are DEVICE
+ *   pointers on the current HIP device, owned by the caller; the library never
+ *   frees or retains them.  Logit tensors are row-major with the vocabulary
+ *   contiguous.  Any alignment is accepted; 16-byte aligned bases with
+ *   V * sizeof(dtype) a multiple of 16 take the vectorised path.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on it and returns without synchronising.
+ * - Scratch: the library keeps one device scratch buffer per device, grown on
+ *   demand (a call that needs more than the buffer holds synchronises the
+ *   device, reallocates and zero-fills it).  Calls on one device that may
+ *   overlap in time (different streams without ordering) race on it and must
+ *   be serialised by the caller.  sv_release() frees it.
+ * - Temperature T: 0 selects greedy decoding (p and q one-hot at their
+ *   arg-max, ties to the lowest index); otherwise T must be a finite normal
+ *   float >= FLT_MIN.  top_k: 0 or >= V disables it.  top_p in (0, 1]; 1
+ *   disables it.  top-k is applied before top-p, both after temperature; both
+ *   keep every token tied with their last kept token.
+ * - Logits may be -inf (token masked out).  NaN and +inf logits are outside
+ *   the defined input range.  uniforms must lie in [0, 1).
+ * - Return value: SV_OK or a negative sv_status.  Argument errors are
+ *   detected on the host before anything is enqueued; SV_ERR_HIP reports a
+ *   failed HIP runtime call (allocation or launch).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  SV_ERR_SHAPE = -2,     /* B < 0, K < 0, K > SV_MAX_K, V < 1, or too large       */
+  SV_ERR_DTYPE = -3,     /* dtype is not one of sv_dtype                          */
+  SV_ERR_PARAM = -4,     /* temperature, top_k or top_p out of range              */
+  SV_ERR_HIP = -5,       /* a HIP runtime call failed                             */
+  SV_ERR_WORKSPACE = -6  /* scratch could not be provided                         */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+#define SV_MAX_K 64
+
+/*
+ * sv_spec_verify - verify one round of K drafted tokens for B sequences.
+ *
+ * target_logits    [B, K+1, V] dtype   target logits for positions 0..K
+ * draft_logits     [B, K,   V] dtype   draft logits for positions 0..K-1
+ *                                      (not read when temperature == 0)
+ * draft_tokens     [B, K] int32        drafted tokens x_i, drawn from q_i
+ * uniforms         [B, K+1] float32    U[0,1): column i < K drives the accept
+ *                                      test at draft i (accept iff
+ *                                      u_i * q_i(x_i) < p_i(x_i)); column K is
+ *                                      the one uniform of the inverse-CDF draw
+ *                                      (residual or bonus), taken in ascending
+ *                                      vocabulary order: token = min{j :
+ *                                      u*Z < C_j}
+ * out_tokens       [B, K+1] int32      written: x_0..x_{n-1}, then the drawn
+ *                                      token at index n, then -1 padding
+ * out_num_accepted [B] int32           written: n in [0, K], the number of
+ *                                      accepted drafts (n + 1 tokens are
+ *                                      emitted).  A sequence with a row whose
+ *                                      logits are all -inf, or a drafted token
+ *                                      outside [0, V), gets n = -1 and tokens
+ *                                      all -1.
+ * B, K, V, dtype   shapes and logit type (sv_dtype)
+ * stream           hipStream_t
+ *
+ * B == 0 returns SV_OK without touching any pointer.
+ */
+int sv_spec_verify(const void* target_logits, const void* draft_logits,
+                   const int32_t* draft_tokens, const float* uniforms,
+                   float temperature, int32_t top_k, float top_p,
+                   int32_t* out_tokens, int32_t* out_num_accepted,
+                   int32_t B, int32_t K, int32_t V, int32_t dtype,
+                   void* stream);
+
+/*
+ * sv_spec_verify_debug - sv_spec_verify plus the intermediate values the
+ * decisions were taken on (for tests and diagnostics).
+ *
+ * out_p   [B, K] double   p_i(x_i): the filtered target probability of each
+ *                         drafted token (NaN for a sentinel sequence)
+ * out_q   [B, K] double   q_i(x_i): the same for the draft
+ * out_z   [B]    double   Z: total weight of the row the last token was drawn
+ *                         from (residual or bonus), as used by the draw
+ * Any of out_p, out_q, out_z may be NULL.  Same return values as
+ * sv_spec_verify.
+ */
+int sv_spec_verify_debug(const void* target_logits, const void* draft_logits,
+                         const int32_t* draft_tokens, const float* uniforms,
+                         float temperature, int32_t top_k, float top_p,
+                         int32_t* out_tokens, int32_t* out_num_accepted,
+                         double* out_p, double* out_q, double* out_z,
+                         int32_t B, int32_t K, int32_t V, int32_t dtype,
+                         void* stream);
+
+/*
+ * sv_filtered_probs - the filtered distribution of every row: temperature,
+ * then top-k, then top-p, then the softmax over the kept tokens (page
+ * www.gsyq.cn/news/428210 section 3.3 for the parameters; the distribution
+ * is the p or q of the accept test).
+ *
+ * logits     [rows, V] dtype   device
+ * out_probs  [rows, V] float   device; written with the probabilities
+ *                              (0 for tokens outside the kept set).  A row
+ *                              with every logit -inf is written as all NaN.
+ * temperature must be > 0 here (greedy rows are one-hot by definition).
+ */
+int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype,
+                      float temperature, int32_t top_k, float top_p,
+                      float* out_probs, void* stream);
+
+/* Frees the per-device scratch of every device the library has used. */
+int sv_release(void);
+
+/* Bytes of device scratch currently held on `device` (0 if none). */
+int64_t sv_scratch_bytes(int device);
+
+/* Human-readable name of a status code. */
+const char* sv_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

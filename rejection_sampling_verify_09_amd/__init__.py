@@ -1,0 +1,18 @@
+"""MI355X (gfx950) speculative-sampling verification.
+
+The computation runs in libspecverify.so (hand-written HIP kernels behind the
+C ABI of include/specverify.h); this package is its Python binding.
+"""
+from ._lib import (  # noqa: F401
+    SV_BF16,
+    SV_F32,
+    SV_MAX_K,
+    SpecVerifyError,
+    filtered_probs,
+    lib,
+    release,
+    spec_verify,
+    status_string,
+)
+
+__all__ = ["spec_verify", "filtered_probs", "release", "status_string", "lib", "SpecVerifyError"]

@@ -1,0 +1,157 @@
+"""ctypes binding of libspecverify.so (argument marshalling only).
+
+Every step of the verification runs in the library's HIP kernels; this module
+only checks tensor metadata, passes device pointers and the current HIP
+stream, and allocates the output tensors.  It never falls back to another
+implementation: if the library is missing it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so the library binds to the HIP runtime torch uses
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_PARAM, SV_ERR_HIP, SV_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6
+SV_F32, SV_BF16 = 0, 1
+SV_MAX_K = 64
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with rejection_sampling_verify_09_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        L.sv_spec_verify.argtypes = [vp, vp, vp, vp, f32, i32, f32, vp, vp, i32, i32, i32, i32, vp]
+        L.sv_spec_verify.restype = ctypes.c_int
+        L.sv_spec_verify_debug.argtypes = [vp, vp, vp, vp, f32, i32, f32, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        L.sv_spec_verify_debug.restype = ctypes.c_int
+        L.sv_filtered_probs.argtypes = [vp, i32, i32, i32, f32, i32, f32, vp, vp]
+        L.sv_filtered_probs.restype = ctypes.c_int
+        L.sv_release.argtypes = []
+        L.sv_release.restype = ctypes.c_int
+        L.sv_scratch_bytes.argtypes = [ctypes.c_int]
+        L.sv_scratch_bytes.restype = ctypes.c_int64
+        L.sv_status_string.argtypes = [ctypes.c_int]
+        L.sv_status_string.restype = ctypes.c_char_p
+        L.sv_version.argtypes = []
+        L.sv_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sv_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def spec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor | None, draft_tokens: torch.Tensor,
+                uniforms: torch.Tensor, temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+                out_tokens: torch.Tensor | None = None, out_num_accepted: torch.Tensor | None = None,
+                stream=None, debug: bool = False):
+    """Verify one round of drafted tokens on the GPU.
+
+    target_logits [B, K+1, V] and draft_logits [B, K, V] (float32 or
+    bfloat16, same dtype); draft_tokens [B, K] int32; uniforms [B, K+1]
+    float32.  Returns (out_tokens [B, K+1] int32, out_num_accepted [B] int32),
+    plus a dict of p(x), q(x) and Z when ``debug``.
+    """
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    dev = target_logits.device
+    tp = _dev(target_logits, "target_logits")
+    if draft_logits is not None and K > 0:
+        if tuple(draft_logits.shape) != (B, K, V) or draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft_logits must be [B, K, V] with the target's dtype")
+        dp = _dev(draft_logits, "draft_logits")
+    elif float(temperature) == 0.0 or K == 0:
+        dp = None
+    else:
+        raise ValueError("draft_logits are required unless temperature == 0")
+    if tuple(draft_tokens.shape) != (B, K) or tuple(uniforms.shape) != (B, K + 1):
+        raise ValueError("draft_tokens must be [B, K] and uniforms [B, K+1]")
+    xp = _dev(draft_tokens, "draft_tokens", torch.int32) if K > 0 else None
+    up = _dev(uniforms, "uniforms", torch.float32)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    op = _dev(out_tokens, "out_tokens", torch.int32)
+    onp = _dev(out_num_accepted, "out_num_accepted", torch.int32)
+    s = _stream(stream)
+    if debug:
+        out_p = torch.empty((B, K), dtype=torch.float64, device=dev)
+        out_q = torch.empty((B, K), dtype=torch.float64, device=dev)
+        out_z = torch.empty((B,), dtype=torch.float64, device=dev)
+        st = lib().sv_spec_verify_debug(tp, dp, xp, up, float(temperature), int(top_k), float(top_p), op, onp,
+                                        out_p.data_ptr() if K > 0 else None, out_q.data_ptr() if K > 0 else None,
+                                        out_z.data_ptr(), B, K, V, code, s)
+        if st != SV_OK:
+            raise SpecVerifyError(st, "sv_spec_verify_debug")
+        return out_tokens, out_num_accepted, dict(p=out_p, q=out_q, z=out_z)
+    st = lib().sv_spec_verify(tp, dp, xp, up, float(temperature), int(top_k), float(top_p), op, onp, B, K, V, code, s)
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_spec_verify")
+    return out_tokens, out_num_accepted
+
+
+def filtered_probs(logits: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Filtered probabilities of every row of ``logits`` [rows, V] (float32 out)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, V]")
+    rows, V = logits.shape
+    code = _dtype_code(logits)
+    if out is None:
+        out = torch.empty((rows, V), dtype=torch.float32, device=logits.device)
+    st = lib().sv_filtered_probs(_dev(logits, "logits"), rows, V, code, float(temperature), int(top_k),
+                                 float(top_p), _dev(out, "out", torch.float32), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_filtered_probs")
+    return out
+
+
+def release() -> None:
+    st = lib().sv_release()
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_release")

@@ -1,0 +1,290 @@
+// Host side of libspecverify: argument validation, scratch management and
+// kernel dispatch for the C ABI declared in include/specverify.h.
+#include "sv_common.hpp"
+#include "specverify.h"
+
+#include <cfloat>
+#include <cmath>
+#include <mutex>
+
+namespace sv {
+hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s);
+hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s);
+hipError_t launch_probs(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
+}  // namespace sv
+
+using namespace sv;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// A launch must satisfy grid * WG < 2^32.
+constexpr int64_t kMaxGrid = (int64_t(1) << 32) / WG - 1;
+
+struct Scratch {
+  char* ptr = nullptr;
+  size_t bytes = 0;
+  int64_t cap_rows = 0;  // arrival counters sized at allocation (zero-filled)
+  int64_t cap_seq = 0;
+};
+
+std::mutex g_mu;
+Scratch g_scr[kMaxDevices];
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t row_cnt, seq_cnt, smp_cnt, pub, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, total;
+};
+
+// Counters first (a fixed region for the life of the allocation: the kernels
+// leave every counter at zero, so it never needs clearing), then the data
+// records of the call.
+Layout make_layout(int64_t cap_rows, int64_t cap_seq, int64_t rows, int64_t nchunks, bool filt, int64_t B,
+                   int64_t nseg) {
+  Layout L;
+  size_t o = 0;
+  L.row_cnt = o; o += al256(cap_rows * 4);
+  L.seq_cnt = o; o += al256(cap_seq * 4);
+  L.smp_cnt = o; o += al256(cap_seq * 4);
+  L.pub = o; o += al256(cap_rows * 4);
+  L.chunk = o; o += al256(rows * nchunks * sizeof(ChunkRec));
+  L.cand = o; o += filt ? al256(rows * nchunks * CAND_CAP * sizeof(uint64_t)) : 0;
+  L.row = o; o += al256(rows * sizeof(RowRec));
+  L.kidx = o; o += filt ? al256(rows * KEEP_CAP * sizeof(int32_t)) : 0;
+  L.kprob = o; o += filt ? al256(rows * KEEP_CAP * sizeof(double)) : 0;
+  L.seq = o; o += al256(B * sizeof(SeqRec));
+  L.seg_sum = o; o += al256(B * nseg * sizeof(double));
+  L.seg_last = o; o += al256(B * nseg * sizeof(int32_t));
+  L.total = o;
+  return L;
+}
+
+// Returns the scratch of the current device, large enough for this call.
+int get_scratch(int64_t rows, int64_t nchunks, bool filt, int64_t B, int64_t nseg, char** base, Layout* lay) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Scratch& s = g_scr[dev];
+  Layout L = make_layout(s.cap_rows, s.cap_seq, rows, nchunks, filt, B, nseg);
+  if (s.ptr == nullptr || s.cap_rows < rows || s.cap_seq < B || s.bytes < L.total) {
+    const int64_t cr = std::max(rows, s.cap_rows), cs = std::max(B, s.cap_seq);
+    L = make_layout(cr, cs, rows, nchunks, filt, B, nseg);
+    const size_t want = std::max(L.total, s.bytes);
+    if (s.ptr) {
+      if (hipDeviceSynchronize() != hipSuccess) return SV_ERR_HIP;
+      (void)hipFree(s.ptr);
+      s.ptr = nullptr;
+      s.bytes = 0;
+      s.cap_rows = s.cap_seq = 0;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) return SV_ERR_WORKSPACE;
+    if (hipMemset(p, 0, want) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipFree(p);
+      return SV_ERR_HIP;
+    }
+    s.ptr = (char*)p;
+    s.bytes = want;
+    s.cap_rows = cr;
+    s.cap_seq = cs;
+  }
+  *base = s.ptr;
+  *lay = make_layout(s.cap_rows, s.cap_seq, rows, nchunks, filt, B, nseg);
+  return SV_OK;
+}
+
+void bind_scratch(Args& a, char* base, const Layout& L) {
+  a.row_cnt = (uint32_t*)(base + L.row_cnt);
+  a.seq_cnt = (uint32_t*)(base + L.seq_cnt);
+  a.smp_cnt = (uint32_t*)(base + L.smp_cnt);
+  a.pub = (uint32_t*)(base + L.pub);
+  a.chunk = (ChunkRec*)(base + L.chunk);
+  a.cand = (uint64_t*)(base + L.cand);
+  a.row = (RowRec*)(base + L.row);
+  a.kidx = (int32_t*)(base + L.kidx);
+  a.kprob = (double*)(base + L.kprob);
+  a.seq = (SeqRec*)(base + L.seq);
+  a.seg_sum = (double*)(base + L.seg_sum);
+  a.seg_last = (int32_t*)(base + L.seg_last);
+}
+
+int check_params(float T, int32_t top_k, float top_p) {
+  if (!(T >= 0.0f) || !std::isfinite(T) || (T > 0.0f && T < FLT_MIN)) return SV_ERR_PARAM;
+  if (top_k < 0) return SV_ERR_PARAM;
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return SV_ERR_PARAM;
+  return SV_OK;
+}
+
+int pick_mode(float T, int32_t top_k, float top_p, int32_t V) {
+  if (T == 0.0f) return M_GREEDY;
+  const bool k = top_k > 0 && top_k < V;
+  const bool p = top_p < 1.0f;
+  return k && p ? M_TOPKP : k ? M_TOPK : p ? M_TOPP : M_PLAIN;
+}
+
+void set_scalars(Args& a, float T, int32_t top_k, float top_p) {
+  a.top_k = top_k;
+  a.top_p = (double)top_p;
+  if (T > 0.0f) {
+    a.invT = 1.0 / (double)T;
+    a.c2 = (float)(1.4426950408889634074 / (double)T);
+    a.win = TOPP_WINDOW_Z * T;
+  } else {
+    a.invT = 0.0;
+    a.c2 = 0.0f;
+    a.win = 0.0f;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, int32_t top_k,
+                float top_p, int32_t* out_tok, int32_t* out_n, double* out_p, double* out_q, double* out_z,
+                int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
+  if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_ERR_SHAPE;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  int st = check_params(T, top_k, top_p);
+  if (st != SV_OK) return st;
+  if (B == 0) return SV_OK;
+  const int mode = pick_mode(T, top_k, top_p, V);
+  if (!tgt || !U || !out_tok || !out_n) return SV_ERR_NULL;
+  if (K > 0 && !X) return SV_ERR_NULL;
+  if (K > 0 && mode != M_GREEDY && !drf) return SV_ERR_NULL;
+  const int esz = dtype == SV_BF16 ? 2 : 4;
+  const int64_t rps = mode == M_GREEDY ? (int64_t)K + 1 : 2 * (int64_t)K + 1;
+  const int64_t rows = (int64_t)B * rps;
+  const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
+  const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
+  if (rows * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
+  const bool filt = mode == M_TOPK || mode == M_TOPP || mode == M_TOPKP;
+  char* base = nullptr;
+  Layout L;
+  st = get_scratch(rows, nchunks, filt, B, nsc * SEG_PER_SCE, &base, &L);
+  if (st != SV_OK) return st;
+
+  Args a;
+  a.tgt = tgt;
+  a.drf = mode == M_GREEDY ? nullptr : drf;
+  a.X = X;
+  a.U = U;
+  a.out_tok = out_tok;
+  a.out_n = out_n;
+  a.out_p = out_p;
+  a.out_q = out_q;
+  a.out_z = out_z;
+  a.out_probs = nullptr;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.rps = (int32_t)rps;
+  a.nchunks = (int32_t)nchunks;
+  a.nsc = (int32_t)nsc;
+  a.do_seq = 1;
+  set_scalars(a, T, top_k, top_p);
+  bind_scratch(a, base, L);
+
+  const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
+  if (mode == M_PLAIN) {
+    if (launch_sample(a, dtype, (unsigned)((int64_t)B * nsc), s) != hipSuccess) return SV_ERR_HIP;
+  }
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                   const float* uniforms, float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
+                   int32_t* out_num_accepted, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, top_k, top_p, out_tokens,
+                     out_num_accepted, nullptr, nullptr, nullptr, B, K, V, dtype, stream);
+}
+
+int sv_spec_verify_debug(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                         const float* uniforms, float temperature, int32_t top_k, float top_p,
+                         int32_t* out_tokens, int32_t* out_num_accepted, double* out_p, double* out_q,
+                         double* out_z, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, top_k, top_p, out_tokens,
+                     out_num_accepted, out_p, out_q, out_z, B, K, V, dtype, stream);
+}
+
+int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype, float temperature, int32_t top_k,
+                      float top_p, float* out_probs, void* stream) {
+  if (rows < 0 || V < 1) return SV_ERR_SHAPE;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  int st = check_params(temperature, top_k, top_p);
+  if (st != SV_OK) return st;
+  if (temperature == 0.0f) return SV_ERR_PARAM;
+  if (rows == 0) return SV_OK;
+  if (!logits || !out_probs) return SV_ERR_NULL;
+  const int mode = pick_mode(temperature, top_k, top_p, V);
+  const int esz = dtype == SV_BF16 ? 2 : 4;
+  const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
+  const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
+  if ((int64_t)rows * nchunks > kMaxGrid || (int64_t)rows * nsc > kMaxGrid) return SV_ERR_SHAPE;
+  const bool filt = mode != M_PLAIN;
+  char* base = nullptr;
+  Layout L;
+  st = get_scratch(rows, nchunks, filt, rows, 0, &base, &L);
+  if (st != SV_OK) return st;
+  Args a = {};
+  a.tgt = logits;
+  a.out_probs = out_probs;
+  a.B = rows;
+  a.K = 0;
+  a.V = V;
+  a.rps = 1;
+  a.nchunks = (int32_t)nchunks;
+  a.nsc = (int32_t)nsc;
+  a.do_seq = 0;
+  set_scalars(a, temperature, top_k, top_p);
+  bind_scratch(a, base, L);
+  const bool vec = aligned16(logits) && ((int64_t)V * esz) % 16 == 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_probs(a, dtype, mode, (unsigned)((int64_t)rows * nsc), s) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int rc = SV_OK;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_HIP;
+  for (int d = 0; d < kMaxDevices; ++d) {
+    Scratch& s = g_scr[d];
+    if (!s.ptr) continue;
+    if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess || hipFree(s.ptr) != hipSuccess)
+      rc = SV_ERR_HIP;
+    s = Scratch();
+  }
+  (void)hipSetDevice(cur);
+  return rc;
+}
+
+int64_t sv_scratch_bytes(int device) {
+  if (device < 0 || device >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lk(g_mu);
+  return (int64_t)g_scr[device].bytes;
+}
+
+const char* sv_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_NULL: return "SV_ERR_NULL: a required pointer is NULL";
+    case SV_ERR_SHAPE: return "SV_ERR_SHAPE: B, K or V out of range";
+    case SV_ERR_DTYPE: return "SV_ERR_DTYPE: unknown logit dtype";
+    case SV_ERR_PARAM: return "SV_ERR_PARAM: temperature, top_k or top_p out of range";
+    case SV_ERR_HIP: return "SV_ERR_HIP: a HIP runtime call failed";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: scratch allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int sv_version(void) { return 100; }
+
+}  // extern "C"

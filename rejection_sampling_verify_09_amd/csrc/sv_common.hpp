@@ -1,0 +1,259 @@
+// Shared definitions of the gfx950 verification kernels: tile sizes, scratch
+// records, kernel arguments and small wave/block primitives (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int WG = 256;          // threads per workgroup (4 wave64)
+constexpr int NWAVE = WG / 64;
+constexpr int CE = 8192;         // logits per streaming chunk
+constexpr int EPT = CE / WG;     // logits held in registers per thread (32)
+constexpr int CAND_CAP = 128;    // candidate slots per chunk
+constexpr int KEEP_CAP = 256;    // kept-list capacity per row (one entry per thread)
+constexpr int SCE = 2048;        // logits per sampling chunk (8 per thread)
+constexpr int SEG = 512;         // logits per sampling segment (one wave)
+constexpr int SEG_PER_SCE = SCE / SEG;
+constexpr int MAX_K = 64;
+constexpr int MAX_RPS = 2 * MAX_K + 1;
+// top-p candidates: every logit within this many units of z = logit / T below
+// the row maximum (the cut is verified against the mass at the row merge)
+constexpr float TOPP_WINDOW_Z = 8.0f;
+
+enum Mode : int { M_PLAIN = 0, M_TOPK = 1, M_TOPP = 2, M_TOPKP = 3, M_GREEDY = 4 };
+enum DType : int { D_F32 = 0, D_BF16 = 1 };
+
+// row flags
+constexpr int RF_BAD = 1;       // no distribution (all -inf or non-finite normaliser)
+constexpr int RF_BIG = 2;       // kept set larger than KEEP_CAP: no kept list stored
+constexpr int RF_FALLBACK = 4;  // threshold found by the full-row search
+
+// per (row, chunk) summary, 32 bytes
+struct ChunkRec {
+  double s;        // sum over the chunk of exp((x - m) / T), relative to the chunk max
+  float m;         // chunk max logit
+  uint32_t bound;  // key of the candidate threshold used by this chunk
+  int32_t ncand;   // candidates found (> CAND_CAP means some were dropped)
+  int32_t arg;     // lowest index of the chunk max (greedy)
+  int32_t pad0, pad1;
+};
+
+// per row, 48 bytes
+struct RowRec {
+  double S;        // full-row normaliser sum exp((x - m) / T)
+  double S_kept;   // normaliser over the kept set (filtered rows)
+  double px;       // probability of the drafted token of this row
+  float m;         // row max logit
+  uint32_t tau;    // key threshold: token kept iff key(logit) >= tau (0 = all)
+  int32_t nkept;   // kept-list length (filtered rows, valid unless RF_BIG)
+  int32_t flags;
+  int32_t arg;     // greedy arg-max
+  int32_t pad;
+};
+
+// per sequence, 16 bytes
+struct SeqRec {
+  double Z;
+  int32_t n;       // accepted drafts, -1 for a sentinel sequence
+  int32_t flags;
+};
+
+struct Args {
+  const void* tgt;
+  const void* drf;
+  const int32_t* X;
+  const float* U;
+  int32_t* out_tok;
+  int32_t* out_n;
+  double* out_p;
+  double* out_q;
+  double* out_z;
+  float* out_probs;
+  int32_t B, K, V, rps, nchunks, nsc, top_k, do_seq;
+  float c2;        // log2(e) / T, the exp2 scale of the streaming pass
+  float win;       // top-p candidate window in logit units
+  double invT;     // 1 / T in double
+  double top_p;
+  ChunkRec* chunk;
+  uint64_t* cand;
+  RowRec* row;
+  int32_t* kidx;
+  double* kprob;
+  SeqRec* seq;
+  uint32_t* pub;      // per-row published bound (reset to 0 by the row merge)
+  uint32_t* row_cnt;  // per-row arrival counters (reset to 0 by the last arrival)
+  uint32_t* seq_cnt;
+  uint32_t* smp_cnt;
+  double* seg_sum;
+  int32_t* seg_last;
+};
+
+// Order-preserving map float -> uint32 (larger float, larger key).
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_val(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+constexpr uint32_t KEY_NEG_INF = 0x007FFFFFu;  // ord_key(-inf)
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const char* row, int j) {
+  if (DT == D_BF16) {
+    uint32_t h = *reinterpret_cast<const uint16_t*>(row + (size_t)j * 2);
+    return __uint_as_float(h << 16);
+  }
+  return *reinterpret_cast<const float*>(row + (size_t)j * 4);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_fmax(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Block-wide reductions over the 256 threads, fixed combination order.
+struct Red {
+  double d[NWAVE];
+  float f[NWAVE];
+  int32_t i[NWAVE];
+  uint32_t u[NWAVE];
+};
+
+__device__ __forceinline__ float block_fmax(float v, Red& r) {
+  v = wave_fmax(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.f[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(r.f[0], r.f[1]), fmaxf(r.f[2], r.f[3]));
+}
+__device__ __forceinline__ double block_sum(double v, Red& r) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.d[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (r.d[0] + r.d[1]) + (r.d[2] + r.d[3]);
+}
+__device__ __forceinline__ int32_t block_min_i(int32_t v, Red& r) {
+  v = wave_min(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.i[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return min(min(r.i[0], r.i[1]), min(r.i[2], r.i[3]));
+}
+__device__ __forceinline__ int32_t block_max_i(int32_t v, Red& r) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.i[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return max(max(r.i[0], r.i[1]), max(r.i[2], r.i[3]));
+}
+__device__ __forceinline__ uint32_t block_max_u(uint32_t v, Red& r) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.u[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return max(max(r.u[0], r.u[1]), max(r.u[2], r.u[3]));
+}
+__device__ __forceinline__ int32_t block_sum_i(int32_t v, Red& r) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.i[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (r.i[0] + r.i[1]) + (r.i[2] + r.i[3]);
+}
+
+// Inclusive prefix sum over the block (one value per thread, thread order).
+__device__ __forceinline__ double block_incl_scan(double v, Red& r, double* total) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    double y = __shfl_up(v, o);
+    if (l >= o) v += y;
+  }
+  __syncthreads();
+  if (l == 63) r.d[w] = v;
+  __syncthreads();
+  double off = 0.0;
+  for (int i = 0; i < w; ++i) off += r.d[i];
+  *total = ((r.d[0] + r.d[1]) + r.d[2]) + r.d[3];
+  return v + off;
+}
+
+// Bitonic sort of n (power of two, <= 4 * WG) 64-bit keys in LDS, descending.
+__device__ __forceinline__ void bitonic_desc(uint64_t* a, int n) {
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += WG) {
+        int p = i ^ j;
+        if (p > i) {
+          uint64_t x = a[i], y = a[p];
+          bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            a[i] = y;
+            a[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Last-arrival detection for a counter shared by `total` workgroups.  Every
+// thread releases its prior global writes; the last workgroup to arrive
+// acquires everything the others released and resets the counter to zero.
+__device__ __forceinline__ bool last_arrival(uint32_t* cnt, uint32_t total, int* flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t prev = atomicAdd(cnt, 1u);
+    int last = prev == total - 1;
+    if (last) atomicExch(cnt, 0u);
+    *flag = last;
+  }
+  __syncthreads();
+  bool last = *flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+__device__ __forceinline__ const char* row_ptr(const Args& a, int rl, int esz) {
+  const int b = rl / a.rps, j = rl - b * a.rps;
+  if (j <= a.K) return (const char*)a.tgt + ((size_t)b * (a.K + 1) + j) * (size_t)a.V * esz;
+  return (const char*)a.drf + ((size_t)b * a.K + (j - a.K - 1)) * (size_t)a.V * esz;
+}
+
+}  // namespace sv

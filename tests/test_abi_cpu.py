@@ -1,0 +1,95 @@
+"""The C-ABI library loads and exports what include/specverify.h declares;
+argument validation answers before any HIP call (CPU, no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from rejection_sampling_verify_09_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_filtered_probs", "sv_release", "sv_scratch_bytes",
+              "sv_status_string", "sv_version"]:
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for s in declared_symbols():
+        assert hasattr(lib, s), f"{s} is declared but not exported"
+
+
+def test_version_and_status_strings():
+    lib = L.lib()
+    assert lib.sv_version() >= 100
+    for code in range(-6, 1):
+        assert L.status_string(code).startswith("SV_")
+    assert L.status_string(123) == "unknown status"
+    assert lib.sv_scratch_bytes(0) == 0
+    assert lib.sv_scratch_bytes(-1) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def call_verify(B=2, K=3, V=16, T=1.0, top_k=0, top_p=1.0, dtype=L.SV_F32, tgt=FAKE, drf=FAKE, X=FAKE, U=FAKE,
+                out_t=FAKE, out_n=FAKE):
+    return L.lib().sv_spec_verify(tgt, drf, X, U, T, top_k, top_p, out_t, out_n, B, K, V, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), L.SV_ERR_SHAPE),
+    (dict(K=-1), L.SV_ERR_SHAPE),
+    (dict(K=L.SV_MAX_K + 1), L.SV_ERR_SHAPE),
+    (dict(V=0), L.SV_ERR_SHAPE),
+    (dict(dtype=7), L.SV_ERR_DTYPE),
+    (dict(T=-0.5), L.SV_ERR_PARAM),
+    (dict(T=float("nan")), L.SV_ERR_PARAM),
+    (dict(T=float("inf")), L.SV_ERR_PARAM),
+    (dict(T=1e-45), L.SV_ERR_PARAM),
+    (dict(top_k=-3), L.SV_ERR_PARAM),
+    (dict(top_p=0.0), L.SV_ERR_PARAM),
+    (dict(top_p=1.5), L.SV_ERR_PARAM),
+    (dict(top_p=float("nan")), L.SV_ERR_PARAM),
+    (dict(tgt=None), L.SV_ERR_NULL),
+    (dict(drf=None), L.SV_ERR_NULL),
+    (dict(X=None), L.SV_ERR_NULL),
+    (dict(U=None), L.SV_ERR_NULL),
+    (dict(out_t=None), L.SV_ERR_NULL),
+    (dict(out_n=None), L.SV_ERR_NULL),
+    (dict(B=1 << 30, K=64, V=1 << 20), L.SV_ERR_SHAPE),
+])
+def test_validation_codes(kw, code):
+    assert call_verify(**kw) == code
+
+
+def test_empty_batch_touches_nothing():
+    assert call_verify(B=0, tgt=None, drf=None, X=None, U=None, out_t=None, out_n=None) == L.SV_OK
+
+
+def test_greedy_does_not_need_draft_logits_but_validates_the_rest():
+    # at T = 0 a NULL draft pointer is accepted; a NULL uniforms pointer is not
+    assert call_verify(T=0.0, drf=None, U=None) == L.SV_ERR_NULL
+
+
+def test_filtered_probs_validation():
+    f = L.lib().sv_filtered_probs
+    assert f(FAKE, -1, 10, 0, 1.0, 0, 1.0, FAKE, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, 4, 0, 0, 1.0, 0, 1.0, FAKE, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, 4, 10, 2, 1.0, 0, 1.0, FAKE, None) == L.SV_ERR_DTYPE
+    assert f(FAKE, 4, 10, 0, 0.0, 0, 1.0, FAKE, None) == L.SV_ERR_PARAM
+    assert f(None, 4, 10, 0, 1.0, 0, 1.0, FAKE, None) == L.SV_ERR_NULL
+    assert f(None, 0, 10, 0, 1.0, 0, 1.0, None, None) == L.SV_OK
