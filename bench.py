@@ -1,0 +1,214 @@
+"""Benchmark of the speculative-sampling verification step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one sv_spec_verify call (the whole hot path: streaming pass,
+filter thresholds, accept tests, first-rejection scan, final draw) over one
+batch whose logits are already resident in HBM.  The input batch is rotated
+over several device copies whose total exceeds the 256 MB last-level cache,
+so every step reads its logits from HBM.  Prints one JSON line.
+
+The CPU-baseline leg times the fp64 oracle (test infrastructure) on a bounded
+sample of the same workload; it is a reported baseline, not the target.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_09_amd", "csrc", f)
+                  for f in ("sv_common.hpp", "sv_kernels.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_draft_tokens(name: str, B: int, K: int):
+    import numpy as np
+
+    path = os.path.join(ROOT, "tests", "golden", "draft_tokens", f"{name}.txt")
+    rows = [list(map(int, ln.split())) for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    x = np.array(rows, dtype=np.int32).reshape(B, K)
+    return x
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the streaming kernel from the committed counter
+    summary, or None when the summary is absent or predates the kernel source."""
+    path = os.path.join(PROFILES, f"traffic_stream_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, d, x, budget_s: float):
+    """Time the fp64 oracle on whole batches of the workload until about
+    budget_s of CPU time has been spent (at least one batch)."""
+    import numpy as np
+
+    import oracle
+
+    sample_B = w.B
+    t0 = time.perf_counter()
+    n_done = 0
+    toks = 0
+    while True:
+        tok, n = oracle.verify(d["target"], d["draft"], x, d["uniforms"], w.temperature, w.top_k, w.top_p,
+                               dtype=w.dtype)
+        n_done += sample_B
+        toks += int(np.sum(n + 1))
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=n_done / el, unit="sequences/s", cores=1, kind="oracle",
+                sample=f"{n_done // sample_B} x the full {sample_B}-sequence batch of {w.name}, "
+                       f"fp64 NumPy, single thread, {el:.1f} s", tokens_per_s=toks / el)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--copies", type=int, default=0, help="device copies of the inputs (0 = enough for 640 MB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the verification step shards over sequences with no communication, so one GPU's "
+              "throughput is the figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from synth import HEADLINE, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": 5}), flush=True)
+        return
+
+    from rejection_sampling_verify_09_amd import spec_verify
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    d = make_inputs(w)
+    x = load_draft_tokens(name, w.B, w.K)
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    tgt0 = dev(d["target"])
+    drf0 = dev(d["draft"]) if w.K > 0 else None
+    bytes_per_step = w.logit_bytes  # every logit the step must read, once
+    R = args.copies or max(3, -(-640_000_000 // bytes_per_step))
+    tgts = [tgt0] + [tgt0.clone() for _ in range(R - 1)]
+    drfs = [drf0] + [drf0.clone() for _ in range(R - 1)] if drf0 is not None else [None] * R
+    X = torch.from_numpy(x).cuda()
+    U = torch.from_numpy(d["uniforms"]).cuda()
+    out_t = torch.empty((w.B, w.K + 1), dtype=torch.int32, device="cuda")
+    out_n = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        spec_verify(tgts[i % R], drfs[i % R], X, U, w.temperature, w.top_k, w.top_p, out_tokens=out_t,
+                    out_num_accepted=out_n)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+
+    n_host = out_n.cpu().numpy()
+    emitted = int(np.sum(n_host[n_host >= 0] + 1))
+    seq_per_s = w.B / (ms_per_step / 1e3)
+    achieved = bytes_per_step / (ms_per_step / 1e3) / 1e9
+    traffic = measured_traffic(name)
+
+    result = {
+        "metric": "spec-verify sequences/s + % HBM peak at B=64 K=6 V=128256 bf16",
+        "value": seq_per_s,
+        "unit": "sequences/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded logits of the workload's shape; no model weights)",
+        "config": {
+            "workload": name, "B": w.B, "K": w.K, "V": w.V, "logits": w.dtype, "temperature": w.temperature,
+            "top_k": w.top_k, "top_p": w.top_p, "rows": w.rows, "input_copies": R,
+            "logit_bytes_per_step": bytes_per_step,
+        },
+        "tokens_per_s": emitted / (ms_per_step / 1e3),
+        "mean_emitted_per_sequence": emitted / w.B,
+        "wall_s_timed": t_wall,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "stream_kernel (single launch per step for this workload)",
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, d, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

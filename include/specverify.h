@@ -54,7 +54,8 @@ extern "C" {
 typedef enum {
   SV_OK = 0,
   SV_ERR_NULL = -1,      /* a required pointer is NULL                          */
-  SV_ERR_SHAPE = -2,     /* B < 0, K < 0, K > SV_MAX_K, V < 1, or too large       */
+  SV_ERR_SHAPE = -2,     /* B < 0, K < 0, K > SV_MAX_K, V < 1, V > SV_MAX_V, or a
+                            launch grid that would exceed 2^32 threads           */
   SV_ERR_DTYPE = -3,     /* dtype is not one of sv_dtype                          */
   SV_ERR_PARAM = -4,     /* temperature, top_k or top_p out of range              */
   SV_ERR_HIP = -5,       /* a HIP runtime call failed                             */
@@ -64,6 +65,7 @@ typedef enum {
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 #define SV_MAX_K 64
+#define SV_MAX_V 2097152 /* 256 chunks of 8192 logits per row */
 
 /*
  * sv_spec_verify - verify one round of K drafted tokens for B sequences.

@@ -24,6 +24,7 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 32) / WG - 1;
 struct Scratch {
   char* ptr = nullptr;
   size_t bytes = 0;
+  int cus = 0;           // compute units of the device (persistent grid size)
   int64_t cap_rows = 0;  // arrival counters sized at allocation (zero-filled)
   int64_t cap_seq = 0;
 };
@@ -34,7 +35,7 @@ Scratch g_scr[kMaxDevices];
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t row_cnt, seq_cnt, smp_cnt, pub, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, total;
+  size_t row_cnt, seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, total;
 };
 
 // Counters first (a fixed region for the life of the allocation: the kernels
@@ -47,7 +48,6 @@ Layout make_layout(int64_t cap_rows, int64_t cap_seq, int64_t rows, int64_t nchu
   L.row_cnt = o; o += al256(cap_rows * 4);
   L.seq_cnt = o; o += al256(cap_seq * 4);
   L.smp_cnt = o; o += al256(cap_seq * 4);
-  L.pub = o; o += al256(cap_rows * 4);
   L.chunk = o; o += al256(rows * nchunks * sizeof(ChunkRec));
   L.cand = o; o += filt ? al256(rows * nchunks * CAND_CAP * sizeof(uint64_t)) : 0;
   L.row = o; o += al256(rows * sizeof(RowRec));
@@ -61,7 +61,8 @@ Layout make_layout(int64_t cap_rows, int64_t cap_seq, int64_t rows, int64_t nchu
 }
 
 // Returns the scratch of the current device, large enough for this call.
-int get_scratch(int64_t rows, int64_t nchunks, bool filt, int64_t B, int64_t nseg, char** base, Layout* lay) {
+int get_scratch(int64_t rows, int64_t nchunks, bool filt, int64_t B, int64_t nseg, char** base, Layout* lay,
+                int* cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
   std::lock_guard<std::mutex> lk(g_mu);
@@ -86,11 +87,15 @@ int get_scratch(int64_t rows, int64_t nchunks, bool filt, int64_t B, int64_t nse
     }
     s.ptr = (char*)p;
     s.bytes = want;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    s.cus = cus;
     s.cap_rows = cr;
     s.cap_seq = cs;
   }
   *base = s.ptr;
   *lay = make_layout(s.cap_rows, s.cap_seq, rows, nchunks, filt, B, nseg);
+  *cus = s.cus;
   return SV_OK;
 }
 
@@ -98,7 +103,6 @@ void bind_scratch(Args& a, char* base, const Layout& L) {
   a.row_cnt = (uint32_t*)(base + L.row_cnt);
   a.seq_cnt = (uint32_t*)(base + L.seq_cnt);
   a.smp_cnt = (uint32_t*)(base + L.smp_cnt);
-  a.pub = (uint32_t*)(base + L.pub);
   a.chunk = (ChunkRec*)(base + L.chunk);
   a.cand = (uint64_t*)(base + L.cand);
   a.row = (RowRec*)(base + L.row);
@@ -139,10 +143,15 @@ void set_scalars(Args& a, float T, int32_t top_k, float top_p) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Items per row of the streaming kernel: the chunks, plus one item without
+// data when their number is even (an odd stride rotates the XCD that merges
+// each row).
+int64_t row_stride(int64_t nchunks) { return nchunks + ((nchunks & 1) ? 0 : 1); }
+
 int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, int32_t top_k,
                 float top_p, int32_t* out_tok, int32_t* out_n, double* out_p, double* out_q, double* out_z,
                 int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
-  if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_ERR_SHAPE;
+  if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > MAX_V) return SV_ERR_SHAPE;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
   int st = check_params(T, top_k, top_p);
   if (st != SV_OK) return st;
@@ -156,11 +165,12 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   const int64_t rows = (int64_t)B * rps;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
-  if (rows * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
+  if (rows * row_stride(nchunks) > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
   const bool filt = mode == M_TOPK || mode == M_TOPP || mode == M_TOPKP;
   char* base = nullptr;
   Layout L;
-  st = get_scratch(rows, nchunks, filt, B, nsc * SEG_PER_SCE, &base, &L);
+  int cus = 1;
+  st = get_scratch(rows, nchunks, filt, B, nsc * SEG_PER_SCE, &base, &L, &cus);
   if (st != SV_OK) return st;
 
   Args a;
@@ -180,13 +190,14 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.rps = (int32_t)rps;
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
+  a.rstride = (int32_t)row_stride(nchunks);
   a.do_seq = 1;
   set_scalars(a, T, top_k, top_p);
   bind_scratch(a, base, L);
 
   const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
   hipStream_t s = (hipStream_t)stream;
-  if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * a.rstride), s) != hipSuccess) return SV_ERR_HIP;
   if (mode == M_PLAIN) {
     if (launch_sample(a, dtype, (unsigned)((int64_t)B * nsc), s) != hipSuccess) return SV_ERR_HIP;
   }
@@ -214,7 +225,7 @@ int sv_spec_verify_debug(const void* target_logits, const void* draft_logits, co
 
 int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype, float temperature, int32_t top_k,
                       float top_p, float* out_probs, void* stream) {
-  if (rows < 0 || V < 1) return SV_ERR_SHAPE;
+  if (rows < 0 || V < 1 || V > MAX_V) return SV_ERR_SHAPE;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
   int st = check_params(temperature, top_k, top_p);
   if (st != SV_OK) return st;
@@ -225,11 +236,12 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   const int esz = dtype == SV_BF16 ? 2 : 4;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
-  if ((int64_t)rows * nchunks > kMaxGrid || (int64_t)rows * nsc > kMaxGrid) return SV_ERR_SHAPE;
+  if ((int64_t)rows * row_stride(nchunks) > kMaxGrid || (int64_t)rows * nsc > kMaxGrid) return SV_ERR_SHAPE;
   const bool filt = mode != M_PLAIN;
   char* base = nullptr;
   Layout L;
-  st = get_scratch(rows, nchunks, filt, rows, 0, &base, &L);
+  int cus = 1;
+  st = get_scratch(rows, nchunks, filt, rows, 0, &base, &L, &cus);
   if (st != SV_OK) return st;
   Args a = {};
   a.tgt = logits;
@@ -240,12 +252,13 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   a.rps = 1;
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
+  a.rstride = (int32_t)row_stride(nchunks);
   a.do_seq = 0;
   set_scalars(a, temperature, top_k, top_p);
   bind_scratch(a, base, L);
   const bool vec = aligned16(logits) && ((int64_t)V * esz) % 16 == 0;
   hipStream_t s = (hipStream_t)stream;
-  if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * a.rstride), s) != hipSuccess) return SV_ERR_HIP;
   if (launch_probs(a, dtype, mode, (unsigned)((int64_t)rows * nsc), s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }

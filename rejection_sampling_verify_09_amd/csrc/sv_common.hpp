@@ -17,6 +17,9 @@ constexpr int SCE = 2048;        // logits per sampling chunk (8 per thread)
 constexpr int SEG = 512;         // logits per sampling segment (one wave)
 constexpr int SEG_PER_SCE = SCE / SEG;
 constexpr int MAX_K = 64;
+constexpr int STREAM_WG_PER_CU = 6;  // register budget of the streaming kernel: 6 resident workgroups per CU
+constexpr int MAX_CHUNKS = WG;           // chunks per row (one chunk record per thread in a row merge)
+constexpr int64_t MAX_V = (int64_t)MAX_CHUNKS * CE;  // 2,097,152
 constexpr int MAX_RPS = 2 * MAX_K + 1;
 // top-p candidates: every logit within this many units of z = logit / T below
 // the row maximum (the cut is verified against the mass at the row merge)
@@ -82,10 +85,10 @@ struct Args {
   int32_t* kidx;
   double* kprob;
   SeqRec* seq;
-  uint32_t* pub;      // per-row published bound (reset to 0 by the row merge)
   uint32_t* row_cnt;  // per-row arrival counters (reset to 0 by the last arrival)
   uint32_t* seq_cnt;
   uint32_t* smp_cnt;
+  int32_t rstride;     // items per row: nchunks, made odd (see stream_kernel)
   double* seg_sum;
   int32_t* seg_last;
 };
@@ -136,6 +139,47 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// Wave64 reductions with DPP row operations (quad swaps, half-row and row
+// mirrors, then row broadcasts 15 and 31); the complete result is in lane 63
+// and is returned to every lane through readlane.  Fixed combination order.
+template <int CTRL, int RM = 0xF, int BM = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, RM, BM, false);
+}
+constexpr int DPP_QP_1032 = 0xB1, DPP_QP_2301 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140,
+              DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143;
+
+__device__ __forceinline__ float dpp_wave_fmax(float v) {
+  const uint32_t NI = 0xFF800000u;
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QP_1032>(NI, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QP_2301>(NI, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(NI, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_MIRROR>(NI, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_BCAST15, 0xA>(NI, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_BCAST31, 0xC>(NI, __float_as_uint(v))));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL, RM>(0u, (uint32_t)u);
+  const uint32_t hi = dpp_u32<CTRL, RM>(0u, (uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double dpp_wave_sum(double v) {
+  v += dpp_f64<DPP_QP_1032>(v);
+  v += dpp_f64<DPP_QP_2301>(v);
+  v += dpp_f64<DPP_HALF_MIRROR>(v);
+  v += dpp_f64<DPP_MIRROR>(v);
+  v += dpp_f64<DPP_BCAST15, 0xA>(v);
+  v += dpp_f64<DPP_BCAST31, 0xC>(v);
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Block-wide reductions over the 256 threads, fixed combination order.
 struct Red {
   double d[NWAVE];
@@ -145,14 +189,14 @@ struct Red {
 };
 
 __device__ __forceinline__ float block_fmax(float v, Red& r) {
-  v = wave_fmax(v);
+  v = dpp_wave_fmax(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.f[threadIdx.x >> 6] = v;
   __syncthreads();
   return fmaxf(fmaxf(r.f[0], r.f[1]), fmaxf(r.f[2], r.f[3]));
 }
 __device__ __forceinline__ double block_sum(double v, Red& r) {
-  v = wave_sum(v);
+  v = dpp_wave_sum(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.d[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -232,22 +276,36 @@ __device__ __forceinline__ int pow2_at_least(int n) {
   return p;
 }
 
+// Data handed from one workgroup to another within a launch is written and
+// read only through these device-scope (agent) relaxed atomics: on gfx950
+// they are coherent across the XCDs' separate L2 caches by themselves, so the
+// hand-off needs no whole-cache writeback or invalidate (which a device-scope
+// fence would issue from every workgroup).
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Last-arrival detection for a counter shared by `total` workgroups.  Every
-// thread releases its prior global writes; the last workgroup to arrive
-// acquires everything the others released and resets the counter to zero.
+// thread first waits until its own st_dev stores have completed; the barrier
+// then orders all of them before thread 0's increment.  The workgroup that
+// sees the final count reads the others' records with ld_dev, and resets the
+// counter to zero for the next launch.
 __device__ __forceinline__ bool last_arrival(uint32_t* cnt, uint32_t total, int* flag) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t prev = atomicAdd(cnt, 1u);
-    int last = prev == total - 1;
-    if (last) atomicExch(cnt, 0u);
+    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == total - 1;
+    if (last) st_dev(cnt, 0u);
     *flag = last;
   }
   __syncthreads();
-  bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *flag != 0;
 }
 
 __device__ __forceinline__ const char* row_ptr(const Args& a, int rl, int esz) {

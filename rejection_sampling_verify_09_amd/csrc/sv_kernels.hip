@@ -30,13 +30,59 @@
 
 namespace sv {
 
+constexpr int NCH_LDS = MAX_CHUNKS;  // chunk records of one row held in LDS during its merge
+constexpr int ROW_CAND = 1024;       // top-k candidates of one row held in LDS during its merge
+constexpr int LOAD_BATCH = 4;        // candidate loads in flight per thread
+constexpr int ROW_LOAD_MAX = 4096;   // candidate slots a merge will read before giving up on the lists
+
+// exp(x) in double for the full-row paths: x = (k + 64 i) ln2/64 + r with
+// |r| <= ln2/128, exp(x) = 2^i * 2^(k/64) * e^r, the 64 powers 2^(k/64) from a
+// table in LDS (built with the library exp2 when such a path starts) and e^r
+// from its degree-5 Taylor polynomial (remainder below 4e-17).  Few registers
+// and no loop-invariant constants to hoist.
+__device__ __forceinline__ double exp_tab(double x, const double* tab) {
+  if (!(x > -800.0)) return 0.0;                   // also -inf
+  x = x < 800.0 ? x : 800.0;
+  const double kf = rint(x * 92.33248261689366);   // 64 / ln2
+  // x - kf * ln2/64 with ln2/64 = hi + lo, hi having 22 trailing zero bits
+  const double r = fma(kf, -6.619564634077006e-12, fma(kf, -0.01083042468962958, x));
+  const double p = fma(fma(fma(fma(fma(r, 1.0 / 120.0, 1.0 / 24.0), r, 1.0 / 6.0), r, 0.5), r, 1.0), r, 1.0);
+  const int ki = (int)kf;
+  const int j = ki & 63;
+  return ldexp(tab[j] * p, (ki - j) >> 6);
+}
+__device__ __forceinline__ void build_exp_tab(double* tab) {
+  __syncthreads();
+  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+  __syncthreads();
+}
+
+struct DrawRow {
+  double snorm;
+  float m;
+  uint32_t tau;
+};
+
 struct SmemStream {
   uint64_t cand[CAND_CAP];
   uint64_t tk[WG];
+  uint32_t hist[256];
 };
 struct SmemRow {
   uint64_t keys[KEEP_CAP];
   uint32_t hist[256];
+  uint32_t cb[NCH_LDS];
+  int32_t cn[NCH_LDS];
+  int32_t off[NCH_LDS + 1];
+  union {
+    struct {  // chunk records, read once at the start of the merge
+      double cs[NCH_LDS];
+      float cm[NCH_LDS];
+      int32_t carg[NCH_LDS];
+    };
+    uint64_t cand[ROW_CAND];              // top-k candidates at or above the bound
+    unsigned long long hist64[256];       // full-row search
+  };
 };
 struct SmemSeq {
   int32_t pidx[KEEP_CAP];
@@ -45,6 +91,10 @@ struct SmemSeq {
   double qprob[KEEP_CAP];
   double px[MAX_RPS];
   int32_t rf[MAX_RPS];
+  int32_t nk[MAX_RPS];
+  int32_t arg[MAX_RPS];
+  int32_t x[MAX_K];
+  float u[MAX_K + 1];
 };
 struct Smem {
   union {
@@ -54,10 +104,14 @@ struct Smem {
     double scan[WG];
   };
   Red red;
+  DrawRow dr[2];
+  double etab[64];  // 2^(j/64) for exp_tab (full-row paths)
   int32_t ncand;
   int32_t flag;
+  int32_t next_item;
   int32_t i0, i1;
   uint32_t u0;
+  float lx;
   double d0;
 };
 
@@ -122,43 +176,124 @@ __device__ __forceinline__ void load_chunk(const char* rp, int c0, int cn, float
   }
 }
 
+// Reload register group g (slots 8g..8g+7) of thread t from memory: the chunk
+// was just streamed, so this reads L2.  Used for the rare candidate work, so
+// that the 32 values need not stay live in registers past the streaming pass.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_group(const char* rp, int c0, int cn, int g, float (&w)[8]) {
+  constexpr int ESZ = ElemT<DT>::ESZ;
+  const int t = threadIdx.x;
+  if (VEC) {
+    constexpr int EPV = ElemT<DT>::EPV;
+    const uint4* p = reinterpret_cast<const uint4*>(rp + (size_t)c0 * ESZ);
+#pragma unroll
+    for (int h = 0; h < 8 / EPV; ++h) {
+      const int u = g * (8 / EPV) + h;
+      const int base = (u * WG + t) * EPV;
+      uint4 r = make_uint4(0u, 0u, 0u, 0u);
+      if (base < cn) r = p[u * WG + t];
+      const uint32_t q[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (DT == D_BF16) {
+          w[h * 8 + 2 * e] = base < cn ? bf16_lo(q[e]) : -INFINITY;
+          w[h * 8 + 2 * e + 1] = base < cn ? bf16_hi(q[e]) : -INFINITY;
+        } else {
+          w[h * 4 + e] = base < cn ? __uint_as_float(q[e]) : -INFINITY;
+        }
+      }
+    }
+  } else {
+    const char* cp = rp + (size_t)c0 * ESZ;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int l = (8 * g + e) * WG + t;
+      w[e] = l < cn ? load_elem<DT>(cp, l) : -INFINITY;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // row merge helpers
 // ---------------------------------------------------------------------------
 
-// F(t) over the whole row: number of logits with key >= max(t, lo), or their
-// probability mass exp((x - m) / T) / snorm.
+// Fixed-point scale of probability masses in the full-row search: sums of
+// integers are exact in any order, so the search is deterministic.
+constexpr double MASS_SCALE = 4503599627370496.0;  // 2^52
+
+// Largest key t >= lo such that F(t) >= target, where F(t) is the number of
+// logits of the row with key >= t, or (mass) their probability mass
+// exp((x - m) / T) / snorm.  F is non-increasing in t, so t is the key of an
+// actual logit: the cut of a top-k (counts) or top-p (mass) set.  Radix
+// search, 8 key bits per pass over the whole row (used only when the
+// candidate lists cannot decide the cut).
 template <int DT>
-__device__ double row_F(const char* rp, int V, uint32_t tk, uint32_t lo, bool mass, float m, double invT,
-                        double snorm, Smem& sm) {
-  const uint32_t th = tk > lo ? tk : lo;
+__device__ uint32_t row_radix(const char* rp, int V, uint32_t lo, bool mass, float m, double invT, double snorm,
+                              double target, Smem& sm) {
+  const int t = threadIdx.x;
+  const unsigned long long tgt = mass ? (unsigned long long)(target * MASS_SCALE) : (unsigned long long)target;
+  uint32_t prefix = 0, pmask = 0;
+  unsigned long long above = 0;  // F of everything in higher bins at the levels fixed so far
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    __syncthreads();
+    for (int d = t; d < 256; d += WG) sm.r.hist64[d] = 0ull;
+    __syncthreads();
+    for (int j = t; j < V; j += WG) {
+      const float x = load_elem<DT>(rp, j);
+      const uint32_t key = ord_key(x);
+      if (key >= lo && (key & pmask) == prefix) {
+        const unsigned long long w =
+            mass ? (unsigned long long)(exp_tab(((double)x - (double)m) * invT, sm.etab) / snorm * MASS_SCALE) : 1ull;
+        atomicAdd(&sm.r.hist64[(key >> shift) & 255u], w);
+      }
+    }
+    __syncthreads();
+    if (t == 0) {
+      unsigned long long cum = above;
+      int d = 255;
+      for (; d > 0; --d) {
+        const unsigned long long h = sm.r.hist64[d];
+        if (cum + h >= tgt) break;
+        cum += h;
+      }
+      // digits below lo's own digit at this level cannot hold a qualifying key
+      sm.i0 = d;
+      sm.d0 = __longlong_as_double((long long)cum);
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sm.i0 << shift;
+    pmask |= 255u << shift;
+    above = (unsigned long long)__double_as_longlong(sm.d0);
+  }
+  return prefix > lo ? prefix : lo;
+}
+
+// One pass over the row for a cut tau: the number of kept logits, their
+// normaliser sum exp((x - m) / T), and (when they fit) the kept entries in
+// sm.r.keys.
+template <int DT>
+__device__ int row_keep(const char* rp, int V, uint32_t tau, float m, double invT, double* skept, Smem& sm) {
+  const int t = threadIdx.x;
+  __syncthreads();
+  if (t == 0) sm.ncand = 0;
+  __syncthreads();
   double acc = 0.0;
-  for (int j = threadIdx.x; j < V; j += WG) {
+  for (int j = t; j < V; j += WG) {
     const float x = load_elem<DT>(rp, j);
-    if (ord_key(x) >= th) acc += mass ? exp(((double)x - (double)m) * invT) / snorm : 1.0;
+    const uint32_t key = ord_key(x);
+    if (key >= tau) {
+      acc += exp_tab(((double)x - (double)m) * invT, sm.etab);
+      const int slot = atomicAdd(&sm.ncand, 1);
+      if (slot < KEEP_CAP) sm.r.keys[slot] = ((uint64_t)key << 32) | (uint32_t)j;
+    }
   }
-  return block_sum(acc, sm.red);
+  *skept = block_sum(acc, sm.red);
+  return sm.ncand;
 }
 
-// Largest key t >= lo with F(t) >= target (F is non-increasing in t); this is
-// the key of an actual logit, the cut of a top-k (counts) or top-p (mass) set.
-template <int DT>
-__device__ uint32_t row_bisect(const char* rp, int V, uint32_t lo, bool mass, float m, double invT, double snorm,
-                               double target, Smem& sm) {
-  uint32_t hi = 0xFFFFFFFFu;
-  while (lo < hi) {
-    const uint32_t mid = lo + (uint32_t)((((uint64_t)hi - lo) + 1) >> 1);
-    if (row_F<DT>(rp, V, mid, lo, mass, m, invT, snorm, sm) >= target)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
-// k-th largest candidate key among the candidates with key >= lo (radix
-// select, 8 bits per pass, counts in LDS).
-__device__ uint32_t cand_select(const ChunkRec* cr, const uint64_t* cand, int nch, uint32_t lo, int k, Smem& sm) {
+// Radix select (8 bits per pass, counts in LDS) of the k-th largest key among
+// the n candidates in sm.r.cand.
+__device__ uint32_t cand_select(int n, int k, Smem& sm) {
   const int t = threadIdx.x;
   uint32_t prefix = 0, pmask = 0;
   int need = k;
@@ -166,12 +301,9 @@ __device__ uint32_t cand_select(const ChunkRec* cr, const uint64_t* cand, int nc
     __syncthreads();
     for (int d = t; d < 256; d += WG) sm.r.hist[d] = 0;
     __syncthreads();
-    for (int p = t; p < nch * CAND_CAP; p += WG) {
-      const int c = p / CAND_CAP, s = p - c * CAND_CAP;
-      if (s < min(cr[c].ncand, CAND_CAP)) {
-        const uint32_t key = (uint32_t)(cand[p] >> 32);
-        if (key >= lo && (key & pmask) == prefix) atomicAdd(&sm.r.hist[(key >> shift) & 255u], 1u);
-      }
+    for (int e = t; e < n; e += WG) {
+      const uint32_t key = (uint32_t)(sm.r.cand[e] >> 32);
+      if ((key & pmask) == prefix) atomicAdd(&sm.r.hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (t == 0) {
@@ -192,43 +324,22 @@ __device__ uint32_t cand_select(const ChunkRec* cr, const uint64_t* cand, int nc
   return prefix;
 }
 
-// Gather candidates with key >= th into sm.r.keys (value-key << 32 | index);
-// returns how many qualified (entries beyond KEEP_CAP are not stored).
-__device__ int cand_gather(const ChunkRec* cr, const uint64_t* cand, int nch, uint32_t th, Smem& sm) {
-  const int t = threadIdx.x;
-  __syncthreads();
-  if (t == 0) sm.ncand = 0;
-  __syncthreads();
-  for (int p = t; p < nch * CAND_CAP; p += WG) {
-    const int c = p / CAND_CAP, s = p - c * CAND_CAP;
-    if (s < min(cr[c].ncand, CAND_CAP)) {
-      const uint64_t e = cand[p];
-      if ((uint32_t)(e >> 32) >= th) {
-        const int slot = atomicAdd(&sm.ncand, 1);
-        if (slot < KEEP_CAP) sm.r.keys[slot] = e;
-      }
-    }
+// Exclusive prefix sum of one int per thread (thread order); *total gets the sum.
+__device__ __forceinline__ int block_excl_scan_i(int v, Red& r, int* total) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (l >= o) x += y;
   }
   __syncthreads();
-  return sm.ncand;
-}
-
-// Gather every logit of the row with key >= th (full-row pass).
-template <int DT>
-__device__ int row_gather(const char* rp, int V, uint32_t th, Smem& sm) {
-  const int t = threadIdx.x;
+  if (l == 63) r.i[w] = x;
   __syncthreads();
-  if (t == 0) sm.ncand = 0;
-  __syncthreads();
-  for (int j = t; j < V; j += WG) {
-    const uint32_t key = ord_key(load_elem<DT>(rp, j));
-    if (key >= th) {
-      const int slot = atomicAdd(&sm.ncand, 1);
-      if (slot < KEEP_CAP) sm.r.keys[slot] = ((uint64_t)key << 32) | (uint32_t)j;
-    }
-  }
-  __syncthreads();
-  return sm.ncand;
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += r.i[i];
+  *total = ((r.i[0] + r.i[1]) + r.i[2]) + r.i[3];
+  return x + off - v;
 }
 
 // Sort the first n entries of sm.r.keys descending (pads with zeros).
@@ -239,83 +350,108 @@ __device__ void sort_keys_desc(int n, Smem& sm) {
   bitonic_desc(sm.r.keys, np2);
 }
 
-// Top-k / top-p threshold of one row and its kept list.  On entry the row is
-// valid (finite max m; for top-p also a finite normaliser rr.S).
+// Top-k / top-p threshold of one row and its kept list.  On entry the chunk
+// records are in sm.r (cm, cb, cn) and the row is valid (finite max m;
+// for top-p also a finite normaliser rr.S).
 template <int DT, int MODE>
 __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRec& rr, Smem& sm) {
   const int t = threadIdx.x, nch = a.nchunks;
-  const ChunkRec* cr = a.chunk + (size_t)rl * nch;
   const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
   const double invT = a.invT;
 
-  // Every logit with key >= lo is among the candidates (each chunk emitted
-  // all its finite logits at or above its own bound, and every bound <= lo),
-  // unless a chunk that may hold such logits ran out of slots.
-  uint32_t lo;
-  if (MODE == M_TOPP) {
-    lo = ord_key(m - a.win);
-  } else {
-    uint32_t mb = 0;
-    for (int c = t; c < nch; c += WG) mb = max(mb, cr[c].bound);
-    lo = block_max_u(mb, sm.red);
-  }
-  int spoil = 0;
-  for (int c = t; c < nch; c += WG) {
-    const ChunkRec q = cr[c];
-    if (q.ncand > CAND_CAP && ord_key(q.m) >= lo) spoil = 1;
-  }
-  spoil = block_max_i(spoil, sm.red);
+  // Every finite logit with key >= lo is among the candidates: each chunk
+  // emitted all of its finite logits at or above its own bound, and lo is the
+  // largest bound (and, for top-p, at least the window below the row max).
+  uint32_t lo = block_max_u(t < nch ? sm.r.cb[t] : 0u, sm.red);
+  if (MODE == M_TOPP) lo = max(lo, ord_key(m - a.win));
+  int ncand_total;
+  const int my_off = block_excl_scan_i(t < nch ? sm.r.cn[t] : 0, sm.red, &ncand_total);
+  if (t < nch) sm.r.off[t] = my_off;
+  if (t == 0) sm.r.off[nch] = ncand_total;
+  __syncthreads();
 
   uint32_t tau = 0;
   int nk = 0;          // kept entries held in sm.r.keys, sorted descending
   bool big = false;    // kept set larger than KEEP_CAP
   double skept = 0.0;  // normaliser over the kept set (when big)
-  bool fb = spoil != 0;
+  bool fb = ncand_total > ROW_LOAD_MAX;
 
   if (!fb) {
+    // Candidates at or above lo, read in batches of LOAD_BATCH loads per
+    // thread: top-p gathers them straight into sm.r.keys (at most KEEP_CAP),
+    // top-k into sm.r.cand (at most ROW_CAND) for the radix select.
+    uint64_t* dstv = (MODE == M_TOPP) ? sm.r.keys : sm.r.cand;
+    const int cap = (MODE == M_TOPP) ? KEEP_CAP : ROW_CAND;
+    if (t == 0) sm.ncand = 0;
+    __syncthreads();
+    for (int base = 0; base < ncand_total; base += WG * LOAD_BATCH) {
+      uint64_t ck[LOAD_BATCH];
+#pragma unroll
+      for (int j = 0; j < LOAD_BATCH; ++j) {
+        const int e = base + t + j * WG;
+        ck[j] = 0ull;
+        if (e < ncand_total) {
+          int lo_c = 0, hi_c = nch;  // last chunk with off <= e
+          while (hi_c - lo_c > 1) {
+            const int mid = (lo_c + hi_c) >> 1;
+            if (sm.r.off[mid] <= e) lo_c = mid;
+            else hi_c = mid;
+          }
+          ck[j] = ld_dev(&cand[(size_t)lo_c * CAND_CAP + (e - sm.r.off[lo_c])]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < LOAD_BATCH; ++j) {
+        if (ck[j] != 0ull && (uint32_t)(ck[j] >> 32) >= lo) {
+          const int slot = atomicAdd(&sm.ncand, 1);
+          if (slot < cap) dstv[slot] = ck[j];
+        }
+      }
+    }
+    __syncthreads();
+    const int cnt = sm.ncand;
     double snorm = rr.S;  // top-p normaliser
     int ns = 0;           // sorted entries available for the top-p walk
-    if (MODE == M_TOPK || MODE == M_TOPKP) {
-      int cnt = 0;
-      for (int p = t; p < nch * CAND_CAP; p += WG) {
-        const int c = p / CAND_CAP, s = p - c * CAND_CAP;
-        if (s < min(cr[c].ncand, CAND_CAP) && (uint32_t)(cand[p] >> 32) >= lo) ++cnt;
-      }
-      cnt = block_sum_i(cnt, sm.red);
-      // fewer than k finite logits: every bound was -inf and all of them are kept
-      const uint32_t tk = cnt < a.top_k ? KEY_NEG_INF : cand_select(cr, cand, nch, lo, a.top_k, sm);
-      const int nall = cand_gather(cr, cand, nch, tk, sm);
-      tau = tk;
-      if (nall <= KEEP_CAP) {
-        sort_keys_desc(nall, sm);
-        ns = nall;
-        nk = nall;
-        if (MODE == M_TOPKP) {
-          const double e = t < ns ? exp(((double)key_val((uint32_t)(sm.r.keys[t] >> 32)) - (double)m) * invT) : 0.0;
-          snorm = block_sum(e, sm.red);
-        }
-      } else if (MODE == M_TOPK) {
-        big = true;
-        double s = 0.0;
-        for (int p = t; p < nch * CAND_CAP; p += WG) {
-          const int c = p / CAND_CAP, sl = p - c * CAND_CAP;
-          if (sl < min(cr[c].ncand, CAND_CAP)) {
-            const uint32_t key = (uint32_t)(cand[p] >> 32);
-            if (key >= tk) s += exp(((double)key_val(key) - (double)m) * invT);
+    if (cnt > cap) {
+      fb = true;
+    } else if (MODE == M_TOPK || MODE == M_TOPKP) {
+      // fewer than k candidates: with every bound at -inf the row has fewer
+      // than k finite logits and all are kept; otherwise the lists cannot decide
+      if (cnt < a.top_k && lo > KEY_NEG_INF) fb = true;
+      if (!fb) {
+        const uint32_t tk = cnt < a.top_k ? KEY_NEG_INF : cand_select(cnt, a.top_k, sm);
+        tau = tk;
+        // kept set: candidates with key >= tk, into sm.r.keys
+        __syncthreads();
+        if (t == 0) sm.i1 = 0;
+        __syncthreads();
+        double sacc = 0.0;
+        for (int e = t; e < cnt; e += WG) {
+          const uint64_t ce = sm.r.cand[e];
+          const uint32_t key = (uint32_t)(ce >> 32);
+          if (key >= tk) {
+            sacc += exp(((double)key_val(key) - (double)m) * invT);
+            const int slot = atomicAdd(&sm.i1, 1);
+            if (slot < KEEP_CAP) sm.r.keys[slot] = ce;
           }
         }
-        skept = block_sum(s, sm.red);
-      } else {
-        fb = true;  // top-p over a top-k set too large for LDS
+        const double sk = block_sum(sacc, sm.red);
+        const int nall = sm.i1;
+        if (nall <= KEEP_CAP) {
+          sort_keys_desc(nall, sm);
+          ns = nall;
+          nk = nall;
+          snorm = sk;
+        } else if (MODE == M_TOPK) {
+          big = true;
+          skept = sk;
+        } else {
+          fb = true;  // top-p over a top-k set too large for LDS
+        }
       }
     } else {  // M_TOPP
-      const int nall = cand_gather(cr, cand, nch, lo, sm);
-      if (nall > KEEP_CAP) {
-        fb = true;
-      } else {
-        sort_keys_desc(nall, sm);
-        ns = nall;
-      }
+      sort_keys_desc(cnt, sm);
+      ns = cnt;
     }
     if (!fb && (MODE == M_TOPP || MODE == M_TOPKP)) {
       // smallest descending prefix whose mass reaches top_p, ties included
@@ -340,28 +476,27 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
   }
 
   if (fb) {
-    // exact threshold by bisection over the whole row (slow, rare)
+    // exact cut by a radix search over the whole row (slow, rare)
     rr.flags |= RF_FALLBACK;
+    build_exp_tab(sm.etab);
     uint32_t tk = 0;
     double sk = 0.0;
     if (MODE == M_TOPK || MODE == M_TOPKP) {
-      tk = row_bisect<DT>(rp, a.V, 0u, false, m, invT, 1.0, (double)a.top_k, sm);
-      sk = row_F<DT>(rp, a.V, tk, 0u, true, m, invT, 1.0, sm);
+      tk = row_radix<DT>(rp, a.V, 0u, false, m, invT, 1.0, (double)a.top_k, sm);
+      if (MODE == M_TOPKP) (void)row_keep<DT>(rp, a.V, tk, m, invT, &sk, sm);
     }
     if (MODE == M_TOPP || MODE == M_TOPKP) {
       const double sn = MODE == M_TOPP ? rr.S : sk;
-      tau = row_bisect<DT>(rp, a.V, tk, true, m, invT, sn, a.top_p, sm);
+      tau = row_radix<DT>(rp, a.V, tk, true, m, invT, sn, a.top_p, sm);
     } else {
       tau = tk;
     }
-    const int nall = (int)row_F<DT>(rp, a.V, tau, 0u, false, m, invT, 1.0, sm);
+    const int nall = row_keep<DT>(rp, a.V, tau, m, invT, &skept, sm);
     if (nall <= KEEP_CAP) {
-      row_gather<DT>(rp, a.V, tau, sm);
       sort_keys_desc(nall, sm);
       nk = nall;
     } else {
       big = true;
-      skept = row_F<DT>(rp, a.V, tau, 0u, true, m, invT, 1.0, sm);
     }
   }
 
@@ -380,8 +515,8 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
       const uint64_t f = sm.r.keys[t];
       const int idx = (int)~(uint32_t)(f >> 32);
       const float x = key_val((uint32_t)f);
-      a.kidx[(size_t)rl * KEEP_CAP + t] = idx;
-      a.kprob[(size_t)rl * KEEP_CAP + t] = exp(((double)x - (double)m) * invT) / skept;
+      st_dev(&a.kidx[(size_t)rl * KEEP_CAP + t], idx);
+      st_dev(&a.kprob[(size_t)rl * KEEP_CAP + t], exp(((double)x - (double)m) * invT) / skept);
     }
   }
   rr.tau = tau;
@@ -390,15 +525,52 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
   if (big) rr.flags |= RF_BIG;
 }
 
+__device__ __forceinline__ void store_row(RowRec* p, const RowRec& r) {
+  st_dev(&p->S, r.S);
+  st_dev(&p->S_kept, r.S_kept);
+  st_dev(&p->px, r.px);
+  st_dev(&p->m, r.m);
+  st_dev(&p->tau, r.tau);
+  st_dev(&p->nkept, r.nkept);
+  st_dev(&p->flags, r.flags);
+  st_dev(&p->arg, r.arg);
+}
+__device__ __forceinline__ RowRec load_row(const RowRec* p) {
+  RowRec r;
+  r.S = ld_dev(&p->S);
+  r.S_kept = ld_dev(&p->S_kept);
+  r.px = ld_dev(&p->px);
+  r.m = ld_dev(&p->m);
+  r.tau = ld_dev(&p->tau);
+  r.nkept = ld_dev(&p->nkept);
+  r.flags = ld_dev(&p->flags);
+  r.arg = ld_dev(&p->arg);
+  r.pad = 0;
+  return r;
+}
+
 template <int DT, int MODE>
-__device__ void row_finalize(const Args& a, int rl, Smem& sm) {
+__device__ void row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
   constexpr int ESZ = ElemT<DT>::ESZ;
+  constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x, nch = a.nchunks;
   const ChunkRec* cr = a.chunk + (size_t)rl * nch;
   const char* rp = row_ptr(a, rl, ESZ);
-  float m = -INFINITY;
-  for (int c = t; c < nch; c += WG) m = fmaxf(m, cr[c].m);
-  m = block_fmax(m, sm.red);
+  // one round trip: every chunk record, and the logit of the drafted token
+  if (t < nch) {
+    sm.r.cm[t] = ld_dev(&cr[t].m);
+    if (MODE == M_PLAIN || MODE == M_TOPP) sm.r.cs[t] = ld_dev(&cr[t].s);
+    if (FILT) {
+      sm.r.cb[t] = ld_dev(&cr[t].bound);
+      const int nc = ld_dev(&cr[t].ncand);
+      sm.r.cn[t] = min(nc, CAND_CAP);
+    }
+    if (MODE == M_GREEDY) sm.r.carg[t] = ld_dev(&cr[t].arg);
+  }
+  const bool hx = xtok >= 0 && xtok < a.V;
+  if (t == WG - 1) sm.lx = (MODE != M_GREEDY && hx) ? load_elem<DT>(rp, xtok) : -INFINITY;
+  __syncthreads();
+  const float m = block_fmax(t < nch ? sm.r.cm[t] : -INFINITY, sm.red);
   RowRec rr;
   rr.S = 0.0;
   rr.S_kept = 0.0;
@@ -411,49 +583,30 @@ __device__ void row_finalize(const Args& a, int rl, Smem& sm) {
   rr.pad = 0;
   bool bad = !(m > -INFINITY && m < INFINITY);
   if (MODE == M_PLAIN || MODE == M_TOPP) {
-    double s = 0.0;
-    for (int c = t; c < nch; c += WG) {
-      const ChunkRec q = cr[c];
-      if (q.m > -INFINITY) s += q.s * exp(((double)q.m - (double)m) * a.invT);
-    }
+    const float qm = t < nch ? sm.r.cm[t] : -INFINITY;
+    const double s = qm > -INFINITY ? sm.r.cs[t] * exp(((double)qm - (double)m) * a.invT) : 0.0;
     const double S = block_sum(s, sm.red);
     rr.S = S;
     if (!(S > 0.0 && S < INFINITY)) bad = true;
   }
   if (MODE == M_GREEDY) {
-    int best = INT_MAX;
-    for (int c = t; c < nch; c += WG)
-      if (cr[c].m == m) best = min(best, cr[c].arg);
-    best = block_min_i(best, sm.red);
+    const int best = block_min_i((t < nch && sm.r.cm[t] == m) ? sm.r.carg[t] : INT_MAX, sm.red);
     rr.arg = best == INT_MAX ? 0 : best;
   }
-  if (MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP) {
+  if (FILT) {
     if (!bad) filter_row<DT, MODE>(a, rl, rp, m, rr, sm);
   }
-  const int b = rl / a.rps, j = rl - b * a.rps;
-  const int i = j <= a.K ? j : j - a.K - 1;
-  if (!bad && i < a.K) {
-    const int x = a.X[(size_t)b * a.K + i];
-    double px = 0.0;
-    if (x >= 0 && x < a.V) {
-      if (MODE == M_GREEDY) {
-        px = x == rr.arg ? 1.0 : 0.0;
-      } else {
-        const float lx = load_elem<DT>(rp, x);
-        if (ord_key(lx) >= rr.tau) {
-          const double e = exp(((double)lx - (double)m) * a.invT);
-          px = e / (MODE == M_PLAIN ? rr.S : rr.S_kept);
-        }
-      }
+  if (!bad && hx) {
+    if (MODE == M_GREEDY) {
+      rr.px = xtok == rr.arg ? 1.0 : 0.0;
+    } else {
+      const float lx = sm.lx;
+      if (ord_key(lx) >= rr.tau) rr.px = exp(((double)lx - (double)m) * a.invT) / (MODE == M_PLAIN ? rr.S : rr.S_kept);
     }
-    rr.px = px;
   }
   if (bad) rr.flags |= RF_BAD;
   __syncthreads();
-  if (t == 0) {
-    a.row[rl] = rr;
-    a.pub[rl] = 0u;
-  }
+  if (t == 0) store_row(&a.row[rl], rr);
 }
 
 // ---------------------------------------------------------------------------
@@ -467,12 +620,12 @@ __device__ int list_sample(const Args& a, double u, int rlP, int np, int rlQ, in
   const int t = threadIdx.x;
   __syncthreads();
   if (t < np) {
-    sm.q.pidx[t] = a.kidx[(size_t)rlP * KEEP_CAP + t];
-    sm.q.pprob[t] = a.kprob[(size_t)rlP * KEEP_CAP + t];
+    sm.q.pidx[t] = ld_dev(&a.kidx[(size_t)rlP * KEEP_CAP + t]);
+    sm.q.pprob[t] = ld_dev(&a.kprob[(size_t)rlP * KEEP_CAP + t]);
   }
   if (res && t < nq) {
-    sm.q.qidx[t] = a.kidx[(size_t)rlQ * KEEP_CAP + t];
-    sm.q.qprob[t] = a.kprob[(size_t)rlQ * KEEP_CAP + t];
+    sm.q.qidx[t] = ld_dev(&a.kidx[(size_t)rlQ * KEEP_CAP + t]);
+    sm.q.qprob[t] = ld_dev(&a.kprob[(size_t)rlQ * KEEP_CAP + t]);
   }
   __syncthreads();
   double p = 0.0, w = 0.0;
@@ -507,6 +660,7 @@ __device__ int list_sample(const Args& a, double u, int rlP, int np, int rlQ, in
   return sm.q.pidx[first];
 }
 
+// Probability of token j in a row's kept set (0 outside it).
 template <int DT>
 __device__ __forceinline__ double kept_prob(const char* rp, int j, const RowRec& R, bool filtered, double invT) {
   const float x = load_elem<DT>(rp, j);
@@ -515,18 +669,31 @@ __device__ __forceinline__ double kept_prob(const char* rp, int j, const RowRec&
 }
 
 // Full-row draw by one workgroup (kept sets too large for a list; an empty
-// residual of an unfiltered row).  Tiles of 2048 consecutive logits.
+// residual of an unfiltered row).  Tiles of 2048 consecutive logits, 8 per
+// thread.  Weights are recomputed rather than held, and the two rows'
+// parameters are kept in LDS, so that this rare path stays light on registers
+// (it shares a kernel, and so a register allocation, with the streaming pass).
 template <int DT>
-__device__ int full_row_sample(const Args& a, double u, const char* pr, const RowRec& P, const char* qr,
-                               const RowRec& Q, bool res, bool filtered, Smem& sm, double* Zout) {
+__device__ __forceinline__ double draw_weight(const char* pr, const char* qr, int j, const DrawRow* dr, bool use_res,
+                                              double invT, const double* tab) {
+  const float xp = load_elem<DT>(pr, j);
+  double w = ord_key(xp) >= dr[0].tau ? exp_tab(((double)xp - (double)dr[0].m) * invT, tab) / dr[0].snorm : 0.0;
+  if (use_res) {
+    const float xq = load_elem<DT>(qr, j);
+    const double q = ord_key(xq) >= dr[1].tau ? exp_tab(((double)xq - (double)dr[1].m) * invT, tab) / dr[1].snorm : 0.0;
+    const double d = w - q;
+    w = d > 0.0 ? d : 0.0;
+  }
+  return w;
+}
+
+template <int DT>
+__device__ int full_row_sample(const Args& a, double u, const char* pr, const char* qr, bool res, Smem& sm,
+                               double* Zout) {
   const int t = threadIdx.x, V = a.V;
   const double invT = a.invT;
-  auto wt = [&](int j, bool use_res) -> double {
-    const double p = kept_prob<DT>(pr, j, P, filtered, invT);
-    if (!use_res) return p;
-    const double d = p - kept_prob<DT>(qr, j, Q, filtered, invT);
-    return d > 0.0 ? d : 0.0;
-  };
+  const DrawRow* dr = sm.dr;
+  build_exp_tab(sm.etab);
   bool use_res = res;
   double Z = 0.0;
   int lastpos = -1;
@@ -535,10 +702,11 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const Ro
     lastpos = -1;
     for (int base = 0; base < V; base += SCE) {
       double ts = 0.0;
+#pragma unroll 1
       for (int e = 0; e < 8; ++e) {
         const int j = base + t * 8 + e;
         if (j < V) {
-          const double w = wt(j, use_res);
+          const double w = draw_weight<DT>(pr, qr, j, dr, use_res, invT, sm.etab);
           ts += w;
           if (w > 0.0) lastpos = j;
         }
@@ -553,12 +721,11 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const Ro
   double run = 0.0;
   int tok = -1;
   for (int base = 0; base < V && tok < 0; base += SCE) {
-    double w8[8];
     double ts = 0.0;
+#pragma unroll 1
     for (int e = 0; e < 8; ++e) {
       const int j = base + t * 8 + e;
-      w8[e] = j < V ? wt(j, use_res) : 0.0;
-      ts += w8[e];
+      if (j < V) ts += draw_weight<DT>(pr, qr, j, dr, use_res, invT, sm.etab);
     }
     const double tile = block_sum(ts, sm.red);
     if (run + tile > target) {
@@ -569,12 +736,16 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const Ro
       __syncthreads();
       double C = run + (t > 0 ? sm.scan[t - 1] : 0.0);
       int first = INT_MAX, lastp = -1;
+#pragma unroll 1
       for (int e = 0; e < 8; ++e) {
         const int j = base + t * 8 + e;
-        C += w8[e];
-        if (j < V && w8[e] > 0.0) {
-          lastp = j;
-          if (first == INT_MAX && target < C) first = j;
+        if (j < V) {
+          const double w = draw_weight<DT>(pr, qr, j, dr, use_res, invT, sm.etab);
+          C += w;
+          if (w > 0.0) {
+            lastp = j;
+            if (first == INT_MAX && target < C) first = j;
+          }
         }
       }
       first = block_min_i(first, sm.red);
@@ -587,34 +758,42 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const Ro
   return tok;
 }
 
+// Parameters of a row for the full-row draw, into sm.dr[slot].
+__device__ __forceinline__ void set_draw_row(const RowRec* r, bool filtered, int slot, Smem& sm) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    sm.dr[slot].m = ld_dev(&r->m);
+    sm.dr[slot].tau = ld_dev(&r->tau);
+    sm.dr[slot].snorm = filtered ? ld_dev(&r->S_kept) : ld_dev(&r->S);
+  }
+  __syncthreads();
+}
+
 template <int DT, int MODE>
 __device__ void seq_finalize(const Args& a, int b, Smem& sm) {
   constexpr int ESZ = ElemT<DT>::ESZ;
   const int t = threadIdx.x, K = a.K, rps = a.rps;
   const RowRec* rr = a.row + (size_t)b * rps;
   __syncthreads();
-  for (int j = t; j < rps; j += WG) {
-    sm.q.px[j] = rr[j].px;
-    sm.q.rf[j] = rr[j].flags;
+  // one round trip: row records, drafted tokens and uniforms
+  if (t < rps) {
+    sm.q.px[t] = ld_dev(&rr[t].px);
+    sm.q.rf[t] = ld_dev(&rr[t].flags);
+    if (MODE == M_GREEDY) sm.q.arg[t] = ld_dev(&rr[t].arg);
+    else sm.q.nk[t] = ld_dev(&rr[t].nkept);
   }
+  if (t < K) sm.q.x[t] = a.X[(size_t)b * K + t];
+  if (t <= K) sm.q.u[t] = a.U[(size_t)b * (K + 1) + t];
   __syncthreads();
   if (t == 0) {
     int bad = 0;
     for (int j = 0; j < rps; ++j) bad |= sm.q.rf[j] & RF_BAD;
-    for (int i = 0; i < K; ++i) {
-      const int x = a.X[(size_t)b * K + i];
-      if (x < 0 || x >= a.V) bad = 1;
-    }
+    for (int i = 0; i < K; ++i)
+      if (sm.q.x[i] < 0 || sm.q.x[i] >= a.V) bad = 1;
     int n = K;
     for (int i = 0; i < K; ++i) {
       const double p = sm.q.px[i];
-      bool acc;
-      if (MODE == M_GREEDY) {
-        acc = p > 0.0;
-      } else {
-        const double q = sm.q.px[K + 1 + i];
-        acc = (double)a.U[(size_t)b * (K + 1) + i] * q < p;
-      }
+      const bool acc = MODE == M_GREEDY ? p > 0.0 : (double)sm.q.u[i] * sm.q.px[K + 1 + i] < p;
       if (!acc) {
         n = i;
         break;
@@ -626,8 +805,8 @@ __device__ void seq_finalize(const Args& a, int b, Smem& sm) {
   const int n = sm.i0;
   int32_t* ot = a.out_tok + (size_t)b * (K + 1);
   if (a.out_p || a.out_q) {
+    const double nanv = __longlong_as_double(0x7FF8000000000000ll);
     for (int i = t; i < K; i += WG) {
-      const double nanv = __longlong_as_double(0x7FF8000000000000ll);
       if (a.out_p) a.out_p[(size_t)b * K + i] = n < 0 ? nanv : sm.q.px[i];
       if (a.out_q) a.out_q[(size_t)b * K + i] = (n < 0 || MODE == M_GREEDY) ? nanv : sm.q.px[K + 1 + i];
     }
@@ -646,7 +825,7 @@ __device__ void seq_finalize(const Args& a, int b, Smem& sm) {
     return;
   }
   for (int j = t; j <= K; j += WG) {
-    if (j < n) ot[j] = a.X[(size_t)b * K + j];
+    if (j < n) ot[j] = sm.q.x[j];
     else if (j > n) ot[j] = -1;
   }
   if (t == 0) a.out_n[b] = n;
@@ -663,18 +842,19 @@ __device__ void seq_finalize(const Args& a, int b, Smem& sm) {
   int tok;
   double Z = 1.0;
   if (MODE == M_GREEDY) {
-    tok = rr[n].arg;
+    tok = sm.q.arg[n];
   } else {
-    const double u = (double)a.U[(size_t)b * (K + 1) + K];
+    const double u = (double)sm.q.u[K];
     const bool res = n < K;
-    const int rlP = b * rps + n, rlQ = b * rps + K + 1 + (res ? n : 0);
-    const RowRec P = rr[n];
-    const RowRec Q = rr[res ? K + 1 + n : n];
-    if ((P.flags & RF_BIG) || (res && (Q.flags & RF_BIG))) {
-      tok = full_row_sample<DT>(a, u, row_ptr(a, rlP, ESZ), P, row_ptr(a, res ? rlQ : rlP, ESZ), Q, res, true, sm,
-                                &Z);
+    const int jq = res ? K + 1 + n : n;
+    const int rlP = b * rps + n, rlQ = b * rps + jq;
+    const int np = sm.q.nk[n], nq = sm.q.nk[jq];
+    if (np < 0 || (res && nq < 0)) {
+      set_draw_row(&rr[n], true, 0, sm);
+      set_draw_row(&rr[jq], true, 1, sm);
+      tok = full_row_sample<DT>(a, u, row_ptr(a, rlP, ESZ), row_ptr(a, rlQ, ESZ), res, sm, &Z);
     } else {
-      tok = list_sample(a, u, rlP, P.nkept, rlQ, res ? Q.nkept : 0, res, sm, &Z);
+      tok = list_sample(a, u, rlP, np, rlQ, nq, res, sm, &Z);
     }
   }
   if (t == 0) {
@@ -687,21 +867,46 @@ __device__ void seq_finalize(const Args& a, int b, Smem& sm) {
 // kernels
 // ---------------------------------------------------------------------------
 
+// One chunk item: stream it, and merge its row / finish its sequence when it
+// is the last to arrive.
 template <int DT, int MODE, bool VEC>
-__global__ void __launch_bounds__(WG) stream_kernel(Args a) {
-  __shared__ Smem sm;
+__device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
   constexpr int ESZ = ElemT<DT>::ESZ;
+  constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x;
-  const int rl = (int)(blockIdx.x / (unsigned)a.nchunks);
-  const int c = (int)blockIdx.x - rl * a.nchunks;
+  const int rl = item / a.rstride;
+  const int c = item - rl * a.rstride;
+  const int b = rl / a.rps, jr = rl - b * a.rps;
+  if (c >= a.nchunks) {  // the row's item without data: it only arrives
+    if (t == 0) sm.ncand = 0;
+    if (!last_arrival(&a.row_cnt[rl], (uint32_t)a.rstride, &sm.flag)) return;
+    const int ir = jr <= a.K ? jr : jr - a.K - 1;
+    __builtin_amdgcn_s_setprio(3);
+    row_finalize<DT, MODE>(a, rl, ir < a.K ? a.X[(size_t)b * a.K + ir] : -1, sm);
+    if (a.do_seq && last_arrival(&a.seq_cnt[b], (uint32_t)a.rps, &sm.flag)) seq_finalize<DT, MODE>(a, b, sm);
+    __builtin_amdgcn_s_setprio(0);
+    return;
+  }
+  const int chunk_id = rl * a.nchunks + c;
   const char* rp = row_ptr(a, rl, ESZ);
   const int c0 = c * CE, cn = min(CE, a.V - c0);
+  const int ir = jr <= a.K ? jr : jr - a.K - 1;
+  // drafted token of this row (used if this workgroup merges the row)
+  const int xtok = ir < a.K ? a.X[(size_t)b * a.K + ir] : -1;
 
   float v[EPT];
   load_chunk<DT, VEC>(rp, c0, cn, v);
-  float tm = -INFINITY;
+  // maxima of 4 groups of 8 register slots, then of the thread
+  float gm[4];
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) tm = fmaxf(tm, v[k]);
+  for (int g = 0; g < 4; ++g) {
+    float x = v[8 * g];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) x = fmaxf(x, v[8 * g + e]);
+    gm[g] = x;
+  }
+  const float tm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
+  if (t == 0) sm.ncand = 0;
   const float mc = block_fmax(tm, sm.red);
 
   ChunkRec rec;
@@ -712,14 +917,52 @@ __global__ void __launch_bounds__(WG) stream_kernel(Args a) {
   rec.arg = 0;
   rec.pad0 = rec.pad1 = 0;
 
+  // candidate bound of this chunk: every finite logit at or above it is emitted
+  uint32_t bound = 0u;
+  float thr = 0.0f;
+  if (FILT) {
+    if (MODE == M_TOPP) {
+      // window below the chunk max (which is <= the row max)
+      bound = ord_key(mc - a.win);
+    } else {
+      // the k-th largest of the 256 thread maxima is <= the row's k-th largest
+      // logit (for k > 256 no bound follows: every finite logit qualifies)
+      sm.s.tk[t] = ord_key(tm);
+      bitonic_desc(sm.s.tk, WG);
+      bound = a.top_k <= WG ? (uint32_t)sm.s.tk[a.top_k - 1] : KEY_NEG_INF;
+    }
+    thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
+  }
+  auto emit = [&](float x, int k) {
+    const int s2 = atomicAdd(&sm.ncand, 1);
+    if (s2 < CAND_CAP) sm.s.cand[s2] = ((uint64_t)ord_key(x) << 32) | (uint32_t)(c0 + local_index<DT, VEC>(k, t));
+  };
+
   if (MODE == M_PLAIN || MODE == M_TOPP) {
+    // sum of exp2((x - mc) * c2): one fma per logit against M = fl(mc * c2);
+    // the (exactly known) rounding of M is a common factor fixed once per
+    // chunk.  Top-p candidates are taken in the same pass.
     float acc = 0.0f;
+    double corr = 1.0;
     if (mc > -INFINITY) {
       const float c2 = a.c2;
+      const float M = mc * c2;
+      if (M > -INFINITY && M < INFINITY) {
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) acc += __builtin_amdgcn_exp2f((v[k] - mc) * c2);
+        for (int k = 0; k < EPT; ++k) {
+          acc += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -M));
+          if (MODE == M_TOPP && v[k] >= thr) emit(v[k], k);
+        }
+        corr = exp2((double)M - (double)mc * (double)c2);
+      } else {
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+          acc += __builtin_amdgcn_exp2f((v[k] - mc) * c2);
+          if (MODE == M_TOPP && v[k] >= thr) emit(v[k], k);
+        }
+      }
     }
-    rec.s = block_sum((double)acc, sm.red);
+    rec.s = block_sum((double)acc, sm.red) * corr;
   }
 
   if (MODE == M_GREEDY) {
@@ -731,53 +974,108 @@ __global__ void __launch_bounds__(WG) stream_kernel(Args a) {
     rec.arg = c0 + (best == INT_MAX ? 0 : best);
   }
 
-  if (MODE == M_TOPP || MODE == M_TOPK || MODE == M_TOPKP) {
-    uint32_t bound;
-    if (MODE == M_TOPP) {
-      // window below the larger of the chunk max and the row max published so far
-      if (t == 0) sm.u0 = atomicMax(&a.pub[rl], ord_key(mc));
-      __syncthreads();
-      const float ref = sm.u0 > ord_key(mc) ? key_val(sm.u0) : mc;
-      bound = ord_key(ref - a.win);
-    } else {
-      // k-th largest of the 256 thread maxima is <= the row's k-th largest logit
-      sm.s.tk[t] = ord_key(tm);
-      bitonic_desc(sm.s.tk, WG);
-      // (for k > 256 no bound follows from 256 maxima: every finite logit qualifies)
-      const uint32_t L = a.top_k <= WG ? (uint32_t)sm.s.tk[a.top_k - 1] : KEY_NEG_INF;
-      if (t == 0) sm.u0 = atomicMax(&a.pub[rl], L);
-      __syncthreads();
-      bound = max(L, sm.u0);
-    }
-    // finite logits at or above the bound become candidates
-    const float thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
-    if (t == 0) sm.ncand = 0;
-    __syncthreads();
+  if (MODE == M_TOPK || MODE == M_TOPKP) {
     if (tm >= thr) {
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) {
-        if (v[k] >= thr) {
-          const int s = atomicAdd(&sm.ncand, 1);
-          if (s < CAND_CAP)
-            sm.s.cand[s] = ((uint64_t)ord_key(v[k]) << 32) | (uint32_t)(c0 + local_index<DT, VEC>(k, t));
+      for (int k = 0; k < EPT; ++k)
+        if (v[k] >= thr) emit(v[k], k);
+    }
+  }
+
+  if (FILT) {
+    __syncthreads();
+    int nc = sm.ncand;
+    if (nc > CAND_CAP) {
+      // Too many: keep exactly the candidates above the (CAND_CAP+1)-th largest
+      // key (radix select over the registers) and raise the bound to match.
+      uint32_t prefix = 0, pmask = 0;
+      int need = CAND_CAP + 1;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        __syncthreads();
+        sm.s.hist[t] = 0u;
+        __syncthreads();
+        for (int g = 0; g < 4; ++g) {
+          if (gm[g] >= thr) {
+            float w[8];
+            load_group<DT, VEC>(rp, c0, cn, g, w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t key = ord_key(w[e]);
+              if (w[e] >= thr && (key & pmask) == prefix) atomicAdd(&sm.s.hist[(key >> shift) & 255u], 1u);
+            }
+          }
+        }
+        __syncthreads();
+        if (t == 0) {
+          int cum = 0, d = 255;
+          for (; d > 0; --d) {
+            const int h = (int)sm.s.hist[d];
+            if (cum + h >= need) break;
+            cum += h;
+          }
+          sm.i0 = d;
+          sm.i1 = need - cum;
+          sm.ncand = 0;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sm.i0 << shift;
+        pmask |= 255u << shift;
+        need = sm.i1;
+      }
+      bound = prefix + 1u;  // every candidate with key >= bound fits
+      for (int g = 0; g < 4; ++g) {
+        if (gm[g] >= thr) {
+          float w[8];
+          load_group<DT, VEC>(rp, c0, cn, g, w);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t key = ord_key(w[e]);
+            if (w[e] >= thr && key >= bound) {
+              const int s2 = atomicAdd(&sm.ncand, 1);
+              if (s2 < CAND_CAP)
+                sm.s.cand[s2] = ((uint64_t)key << 32) | (uint32_t)(c0 + local_index<DT, VEC>(8 * g + e, t));
+            }
+          }
         }
       }
+      __syncthreads();
+      nc = sm.ncand;
     }
-    __syncthreads();
-    const int nc = sm.ncand;
-    uint64_t* dst = a.cand + (size_t)blockIdx.x * CAND_CAP;
-    for (int s = t; s < min(nc, CAND_CAP); s += WG) dst[s] = sm.s.cand[s];
+    uint64_t* dst = a.cand + (size_t)chunk_id * CAND_CAP;
+    for (int s = t; s < min(nc, CAND_CAP); s += WG) st_dev(&dst[s], sm.s.cand[s]);
     rec.ncand = nc;
     rec.bound = bound;
   }
-  if (t == 0) a.chunk[blockIdx.x] = rec;
+  if (t == 0) {
+    ChunkRec* cp = &a.chunk[chunk_id];
+    if (MODE == M_PLAIN || MODE == M_TOPP) st_dev(&cp->s, rec.s);
+    st_dev(&cp->m, rec.m);
+    if (FILT) {
+      st_dev(&cp->bound, rec.bound);
+      st_dev(&cp->ncand, rec.ncand);
+    }
+    if (MODE == M_GREEDY) st_dev(&cp->arg, rec.arg);
+  }
 
-  if (!last_arrival(&a.row_cnt[rl], (uint32_t)a.nchunks, &sm.flag)) return;
-  row_finalize<DT, MODE>(a, rl, sm);
-  if (!a.do_seq) return;
-  const int b = rl / a.rps;
-  if (!last_arrival(&a.seq_cnt[b], (uint32_t)a.rps, &sm.flag)) return;
-  seq_finalize<DT, MODE>(a, b, sm);
+  if (!last_arrival(&a.row_cnt[rl], (uint32_t)a.rstride, &sm.flag)) return;
+  // the merge and the final draw sit on the critical path of the launch: let
+  // their waves issue ahead of the streaming waves sharing the SIMDs
+  __builtin_amdgcn_s_setprio(3);
+  row_finalize<DT, MODE>(a, rl, xtok, sm);
+  if (a.do_seq && last_arrival(&a.seq_cnt[b], (uint32_t)a.rps, &sm.flag)) seq_finalize<DT, MODE>(a, b, sm);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// One workgroup per item.  Workgroups are dispatched to the XCDs round-robin
+// by index, and the last chunk of a row to arrive (the one dispatched last)
+// merges the row; rows are therefore laid out on an odd number of items
+// (rstride: nchunks, plus one item without data when nchunks is even), so
+// that the merging position rotates over the XCDs from row to row instead of
+// landing on the same XCD every time.
+template <int DT, int MODE, bool VEC>
+__global__ void __launch_bounds__(WG, STREAM_WG_PER_CU) stream_kernel(Args a) {
+  __shared__ Smem sm;
+  stream_item<DT, MODE, VEC>(a, (int)blockIdx.x, sm);
 }
 
 template <int DT>
@@ -828,8 +1126,8 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     const int sl = wave_max(lastp);
     if ((t & 63) == 0) {
       const size_t s = (size_t)b * nseg + c * SEG_PER_SCE + (t >> 6);
-      a.seg_sum[s] = ss;
-      a.seg_last[s] = sl;
+      st_dev(&a.seg_sum[s], ss);
+      st_dev(&a.seg_last[s], sl);
     }
   }
   if (!last_arrival(&a.smp_cnt[b], (uint32_t)a.nsc, &sm.flag)) return;
@@ -842,8 +1140,8 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   double loc = 0.0;
   int lastseg = -1;
   for (int s = s0; s < s1; ++s) {
-    loc += ssum[s];
-    if (slast[s] >= 0) lastseg = s;
+    loc += ld_dev(&ssum[s]);
+    if (ld_dev(&slast[s]) >= 0) lastseg = s;
   }
   double Z;
   const double incl = block_incl_scan(loc, sm.red, &Z);
@@ -852,7 +1150,8 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   int tok;
   if (!(Z > 0.0)) {
     // empty residual (round-off only): draw from p
-    tok = full_row_sample<DT>(a, u, pr, P, qr, Q, false, false, sm, &Z);
+    set_draw_row(&a.row[rlP], false, 0, sm);
+    tok = full_row_sample<DT>(a, u, pr, qr, false, sm, &Z);
   } else {
     const double target = u * Z;
     __syncthreads();
@@ -862,7 +1161,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     int found = INT_MAX;
     double cstart = 0.0;
     for (int s = s0; s < s1; ++s) {
-      const double ce = run + ssum[s];
+      const double ce = run + ld_dev(&ssum[s]);
       if (found == INT_MAX && target < ce) {
         found = s;
         cstart = run;
@@ -871,7 +1170,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     }
     const int sf = block_min_i(found, sm.red);
     if (sf == INT_MAX) {
-      tok = lastseg >= 0 ? slast[lastseg] : 0;
+      tok = lastseg >= 0 ? ld_dev(&slast[lastseg]) : 0;
     } else {
       __syncthreads();
       if (found == sf) sm.d0 = cstart;
@@ -891,8 +1190,8 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
       if (j0 < a.V && w0 > 0.0 && target < C0) first = j0;
       else if (j0 + 1 < a.V && w1 > 0.0 && target < C1) first = j0 + 1;
       first = block_min_i(first, sm.red);
-      tok = first != INT_MAX ? first : slast[sf];
-      if (tok < 0) tok = lastseg >= 0 ? slast[lastseg] : 0;
+      tok = first != INT_MAX ? first : ld_dev(&slast[sf]);
+      if (tok < 0) tok = lastseg >= 0 ? ld_dev(&slast[lastseg]) : 0;
     }
   }
   if (t == 0) {

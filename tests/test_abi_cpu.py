@@ -55,6 +55,7 @@ def call_verify(B=2, K=3, V=16, T=1.0, top_k=0, top_p=1.0, dtype=L.SV_F32, tgt=F
     (dict(K=-1), L.SV_ERR_SHAPE),
     (dict(K=L.SV_MAX_K + 1), L.SV_ERR_SHAPE),
     (dict(V=0), L.SV_ERR_SHAPE),
+    (dict(V=2097153), L.SV_ERR_SHAPE),
     (dict(dtype=7), L.SV_ERR_DTYPE),
     (dict(T=-0.5), L.SV_ERR_PARAM),
     (dict(T=float("nan")), L.SV_ERR_PARAM),
@@ -71,6 +72,7 @@ def call_verify(B=2, K=3, V=16, T=1.0, top_k=0, top_p=1.0, dtype=L.SV_F32, tgt=F
     (dict(out_t=None), L.SV_ERR_NULL),
     (dict(out_n=None), L.SV_ERR_NULL),
     (dict(B=1 << 30, K=64, V=1 << 20), L.SV_ERR_SHAPE),
+    (dict(B=1 << 17, K=64, V=1 << 20), L.SV_ERR_SHAPE),
 ])
 def test_validation_codes(kw, code):
     assert call_verify(**kw) == code
