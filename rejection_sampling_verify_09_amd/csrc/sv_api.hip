@@ -9,6 +9,7 @@
 
 namespace sv {
 hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s);
+hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
 hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s);
 hipError_t launch_probs(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
 }  // namespace sv
@@ -25,8 +26,7 @@ struct Scratch {
   char* ptr = nullptr;
   size_t bytes = 0;
   int cus = 0;           // compute units of the device (persistent grid size)
-  int64_t cap_rows = 0;  // arrival counters sized at allocation (zero-filled)
-  int64_t cap_seq = 0;
+  int64_t cap_seq = 0;   // sequences the (zero-filled) arrival counters cover
 };
 
 std::mutex g_mu;
@@ -35,17 +35,16 @@ Scratch g_scr[kMaxDevices];
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t row_cnt, seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, total;
+  size_t seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, total;
 };
 
 // Counters first (a fixed region for the life of the allocation: the kernels
 // leave every counter at zero, so it never needs clearing), then the data
 // records of the call.
-Layout make_layout(int64_t cap_rows, int64_t cap_seq, int64_t rows, int64_t nchunks, bool filt, int64_t B,
+Layout make_layout(int64_t cap_seq, int64_t rows, int64_t nchunks, bool filt, int64_t B,
                    int64_t nseg) {
   Layout L;
   size_t o = 0;
-  L.row_cnt = o; o += al256(cap_rows * 4);
   L.seq_cnt = o; o += al256(cap_seq * 4);
   L.smp_cnt = o; o += al256(cap_seq * 4);
   L.chunk = o; o += al256(rows * nchunks * sizeof(ChunkRec));
@@ -67,17 +66,17 @@ int get_scratch(int64_t rows, int64_t nchunks, bool filt, int64_t B, int64_t nse
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
   std::lock_guard<std::mutex> lk(g_mu);
   Scratch& s = g_scr[dev];
-  Layout L = make_layout(s.cap_rows, s.cap_seq, rows, nchunks, filt, B, nseg);
-  if (s.ptr == nullptr || s.cap_rows < rows || s.cap_seq < B || s.bytes < L.total) {
-    const int64_t cr = std::max(rows, s.cap_rows), cs = std::max(B, s.cap_seq);
-    L = make_layout(cr, cs, rows, nchunks, filt, B, nseg);
+  Layout L = make_layout(s.cap_seq, rows, nchunks, filt, B, nseg);
+  if (s.ptr == nullptr || s.cap_seq < B || s.bytes < L.total) {
+    const int64_t cs = std::max(B, s.cap_seq);
+    L = make_layout(cs, rows, nchunks, filt, B, nseg);
     const size_t want = std::max(L.total, s.bytes);
     if (s.ptr) {
       if (hipDeviceSynchronize() != hipSuccess) return SV_ERR_HIP;
       (void)hipFree(s.ptr);
       s.ptr = nullptr;
       s.bytes = 0;
-      s.cap_rows = s.cap_seq = 0;
+      s.cap_seq = 0;
     }
     void* p = nullptr;
     if (hipMalloc(&p, want) != hipSuccess) return SV_ERR_WORKSPACE;
@@ -90,17 +89,15 @@ int get_scratch(int64_t rows, int64_t nchunks, bool filt, int64_t B, int64_t nse
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
     s.cus = cus;
-    s.cap_rows = cr;
     s.cap_seq = cs;
   }
   *base = s.ptr;
-  *lay = make_layout(s.cap_rows, s.cap_seq, rows, nchunks, filt, B, nseg);
+  *lay = make_layout(s.cap_seq, rows, nchunks, filt, B, nseg);
   *cus = s.cus;
   return SV_OK;
 }
 
 void bind_scratch(Args& a, char* base, const Layout& L) {
-  a.row_cnt = (uint32_t*)(base + L.row_cnt);
   a.seq_cnt = (uint32_t*)(base + L.seq_cnt);
   a.smp_cnt = (uint32_t*)(base + L.smp_cnt);
   a.chunk = (ChunkRec*)(base + L.chunk);
@@ -143,11 +140,6 @@ void set_scalars(Args& a, float T, int32_t top_k, float top_p) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Items per row of the streaming kernel: the chunks, plus one item without
-// data when their number is even (an odd stride rotates the XCD that merges
-// each row).
-int64_t row_stride(int64_t nchunks) { return nchunks + ((nchunks & 1) ? 0 : 1); }
-
 int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, int32_t top_k,
                 float top_p, int32_t* out_tok, int32_t* out_n, double* out_p, double* out_q, double* out_z,
                 int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
@@ -165,7 +157,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   const int64_t rows = (int64_t)B * rps;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
-  if (rows * row_stride(nchunks) > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
+  if (rows * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
   const bool filt = mode == M_TOPK || mode == M_TOPP || mode == M_TOPKP;
   char* base = nullptr;
   Layout L;
@@ -190,14 +182,14 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.rps = (int32_t)rps;
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
-  a.rstride = (int32_t)row_stride(nchunks);
   a.do_seq = 1;
   set_scalars(a, T, top_k, top_p);
   bind_scratch(a, base, L);
 
   const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
   hipStream_t s = (hipStream_t)stream;
-  if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * a.rstride), s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (mode == M_PLAIN) {
     if (launch_sample(a, dtype, (unsigned)((int64_t)B * nsc), s) != hipSuccess) return SV_ERR_HIP;
   }
@@ -236,7 +228,7 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   const int esz = dtype == SV_BF16 ? 2 : 4;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
-  if ((int64_t)rows * row_stride(nchunks) > kMaxGrid || (int64_t)rows * nsc > kMaxGrid) return SV_ERR_SHAPE;
+  if ((int64_t)rows * nchunks > kMaxGrid || (int64_t)rows * nsc > kMaxGrid) return SV_ERR_SHAPE;
   const bool filt = mode != M_PLAIN;
   char* base = nullptr;
   Layout L;
@@ -252,13 +244,13 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   a.rps = 1;
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
-  a.rstride = (int32_t)row_stride(nchunks);
   a.do_seq = 0;
   set_scalars(a, temperature, top_k, top_p);
   bind_scratch(a, base, L);
   const bool vec = aligned16(logits) && ((int64_t)V * esz) % 16 == 0;
   hipStream_t s = (hipStream_t)stream;
-  if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * a.rstride), s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (launch_probs(a, dtype, mode, (unsigned)((int64_t)rows * nsc), s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }

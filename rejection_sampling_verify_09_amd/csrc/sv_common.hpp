@@ -11,7 +11,7 @@ constexpr int WG = 256;          // threads per workgroup (4 wave64)
 constexpr int NWAVE = WG / 64;
 constexpr int CE = 8192;         // logits per streaming chunk
 constexpr int EPT = CE / WG;     // logits held in registers per thread (32)
-constexpr int CAND_CAP = 128;    // candidate slots per chunk
+constexpr int CAND_CAP = 256;    // candidate slots per chunk
 constexpr int KEEP_CAP = 256;    // kept-list capacity per row (one entry per thread)
 constexpr int SCE = 2048;        // logits per sampling chunk (8 per thread)
 constexpr int SEG = 512;         // logits per sampling segment (one wave)
@@ -85,10 +85,8 @@ struct Args {
   int32_t* kidx;
   double* kprob;
   SeqRec* seq;
-  uint32_t* row_cnt;  // per-row arrival counters (reset to 0 by the last arrival)
-  uint32_t* seq_cnt;
+  uint32_t* seq_cnt;  // per-sequence arrival counters (reset to 0 by the last arrival)
   uint32_t* smp_cnt;
-  int32_t rstride;     // items per row: nchunks, made odd (see stream_kernel)
   double* seg_sum;
   int32_t* seg_last;
 };

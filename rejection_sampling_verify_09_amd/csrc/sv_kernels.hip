@@ -64,9 +64,10 @@ struct DrawRow {
 };
 
 struct SmemStream {
-  uint64_t cand[CAND_CAP];
+  uint64_t cand[NWAVE * CAND_CAP];  // per-wave candidate lists (one flat list after an overflow cut)
   uint64_t tk[WG];
   uint32_t hist[256];
+  int32_t wn[NWAVE];
 };
 struct SmemRow {
   uint64_t keys[KEEP_CAP];
@@ -108,7 +109,6 @@ struct Smem {
   double etab[64];  // 2^(j/64) for exp_tab (full-row paths)
   int32_t ncand;
   int32_t flag;
-  int32_t next_item;
   int32_t i0, i1;
   uint32_t u0;
   float lx;
@@ -867,32 +867,43 @@ __device__ void seq_finalize(const Args& a, int b, Smem& sm) {
 // kernels
 // ---------------------------------------------------------------------------
 
-// One chunk item: stream it, and merge its row / finish its sequence when it
-// is the last to arrive.
+// Append every logit of this thread at or above thr to its wave's candidate
+// list wl (entries ord_key << 32 | index, slots past CAND_CAP dropped) and
+// return the wave's count.  Compaction by ballot: a register slot costs one
+// compare and a scalar branch unless some lane of the wave qualifies.  Called
+// with every lane of the wave active.
+template <int DT, bool VEC>
+__device__ __forceinline__ int wave_emit(const float (&v)[EPT], float tm, float thr, int c0, uint64_t* wl) {
+  int wn = 0;
+  if (__ballot(tm >= thr) == 0ull) return 0;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const bool pr = v[k] >= thr;
+    const unsigned long long bm = __ballot(pr);
+    if (bm != 0ull) {
+      if (pr) {
+        const int pos =
+            wn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+        if (pos < CAND_CAP)
+          wl[pos] = ((uint64_t)ord_key(v[k]) << 32) | (uint32_t)(c0 + local_index<DT, VEC>(k, threadIdx.x));
+      }
+      wn += __popcll(bm);
+    }
+  }
+  return wn;
+}
+
+// One chunk item: stream it and leave its record (max, sum, candidates).
 template <int DT, int MODE, bool VEC>
 __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x;
-  const int rl = item / a.rstride;
-  const int c = item - rl * a.rstride;
-  const int b = rl / a.rps, jr = rl - b * a.rps;
-  if (c >= a.nchunks) {  // the row's item without data: it only arrives
-    if (t == 0) sm.ncand = 0;
-    if (!last_arrival(&a.row_cnt[rl], (uint32_t)a.rstride, &sm.flag)) return;
-    const int ir = jr <= a.K ? jr : jr - a.K - 1;
-    __builtin_amdgcn_s_setprio(3);
-    row_finalize<DT, MODE>(a, rl, ir < a.K ? a.X[(size_t)b * a.K + ir] : -1, sm);
-    if (a.do_seq && last_arrival(&a.seq_cnt[b], (uint32_t)a.rps, &sm.flag)) seq_finalize<DT, MODE>(a, b, sm);
-    __builtin_amdgcn_s_setprio(0);
-    return;
-  }
-  const int chunk_id = rl * a.nchunks + c;
+  const int rl = item / a.nchunks;
+  const int c = item - rl * a.nchunks;
+  const int chunk_id = item;
   const char* rp = row_ptr(a, rl, ESZ);
   const int c0 = c * CE, cn = min(CE, a.V - c0);
-  const int ir = jr <= a.K ? jr : jr - a.K - 1;
-  // drafted token of this row (used if this workgroup merges the row)
-  const int xtok = ir < a.K ? a.X[(size_t)b * a.K + ir] : -1;
 
   float v[EPT];
   load_chunk<DT, VEC>(rp, c0, cn, v);
@@ -933,15 +944,10 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
     }
     thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
   }
-  auto emit = [&](float x, int k) {
-    const int s2 = atomicAdd(&sm.ncand, 1);
-    if (s2 < CAND_CAP) sm.s.cand[s2] = ((uint64_t)ord_key(x) << 32) | (uint32_t)(c0 + local_index<DT, VEC>(k, t));
-  };
-
   if (MODE == M_PLAIN || MODE == M_TOPP) {
     // sum of exp2((x - mc) * c2): one fma per logit against M = fl(mc * c2);
     // the (exactly known) rounding of M is a common factor fixed once per
-    // chunk.  Top-p candidates are taken in the same pass.
+    // chunk.
     float acc = 0.0f;
     double corr = 1.0;
     if (mc > -INFINITY) {
@@ -951,14 +957,12 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
           acc += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -M));
-          if (MODE == M_TOPP && v[k] >= thr) emit(v[k], k);
         }
         corr = exp2((double)M - (double)mc * (double)c2);
       } else {
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
           acc += __builtin_amdgcn_exp2f((v[k] - mc) * c2);
-          if (MODE == M_TOPP && v[k] >= thr) emit(v[k], k);
         }
       }
     }
@@ -974,18 +978,18 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
     rec.arg = c0 + (best == INT_MAX ? 0 : best);
   }
 
-  if (MODE == M_TOPK || MODE == M_TOPKP) {
-    if (tm >= thr) {
-#pragma unroll
-      for (int k = 0; k < EPT; ++k)
-        if (v[k] >= thr) emit(v[k], k);
-    }
-  }
-
   if (FILT) {
+    const int w = t >> 6;
+    const int wn = wave_emit<DT, VEC>(v, tm, thr, c0, &sm.s.cand[w * CAND_CAP]);
+    if ((t & 63) == 0) sm.s.wn[w] = wn;
     __syncthreads();
-    int nc = sm.ncand;
-    if (nc > CAND_CAP) {
+    int nc = (sm.s.wn[0] + sm.s.wn[1]) + (sm.s.wn[2] + sm.s.wn[3]);
+    uint64_t* dst = a.cand + (size_t)chunk_id * CAND_CAP;
+    if (nc <= CAND_CAP) {
+      int off = 0;
+      for (int i = 0; i < w; ++i) off += sm.s.wn[i];
+      for (int s = t & 63; s < wn; s += 64) st_dev(&dst[off + s], sm.s.cand[w * CAND_CAP + s]);
+    } else {
       // Too many: keep exactly the candidates above the (CAND_CAP+1)-th largest
       // key (radix select over the registers) and raise the bound to match.
       uint32_t prefix = 0, pmask = 0;
@@ -996,12 +1000,12 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
         __syncthreads();
         for (int g = 0; g < 4; ++g) {
           if (gm[g] >= thr) {
-            float w[8];
-            load_group<DT, VEC>(rp, c0, cn, g, w);
+            float wv[8];
+            load_group<DT, VEC>(rp, c0, cn, g, wv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const uint32_t key = ord_key(w[e]);
-              if (w[e] >= thr && (key & pmask) == prefix) atomicAdd(&sm.s.hist[(key >> shift) & 255u], 1u);
+              const uint32_t key = ord_key(wv[e]);
+              if (wv[e] >= thr && (key & pmask) == prefix) atomicAdd(&sm.s.hist[(key >> shift) & 255u], 1u);
             }
           }
         }
@@ -1025,12 +1029,12 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
       bound = prefix + 1u;  // every candidate with key >= bound fits
       for (int g = 0; g < 4; ++g) {
         if (gm[g] >= thr) {
-          float w[8];
-          load_group<DT, VEC>(rp, c0, cn, g, w);
+          float wv[8];
+          load_group<DT, VEC>(rp, c0, cn, g, wv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const uint32_t key = ord_key(w[e]);
-            if (w[e] >= thr && key >= bound) {
+            const uint32_t key = ord_key(wv[e]);
+            if (wv[e] >= thr && key >= bound) {
               const int s2 = atomicAdd(&sm.ncand, 1);
               if (s2 < CAND_CAP)
                 sm.s.cand[s2] = ((uint64_t)key << 32) | (uint32_t)(c0 + local_index<DT, VEC>(8 * g + e, t));
@@ -1040,9 +1044,8 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
       }
       __syncthreads();
       nc = sm.ncand;
+      for (int s = t; s < nc; s += WG) st_dev(&dst[s], sm.s.cand[s]);
     }
-    uint64_t* dst = a.cand + (size_t)chunk_id * CAND_CAP;
-    for (int s = t; s < min(nc, CAND_CAP); s += WG) st_dev(&dst[s], sm.s.cand[s]);
     rec.ncand = nc;
     rec.bound = bound;
   }
@@ -1057,25 +1060,30 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
     if (MODE == M_GREEDY) st_dev(&cp->arg, rec.arg);
   }
 
-  if (!last_arrival(&a.row_cnt[rl], (uint32_t)a.rstride, &sm.flag)) return;
-  // the merge and the final draw sit on the critical path of the launch: let
-  // their waves issue ahead of the streaming waves sharing the SIMDs
-  __builtin_amdgcn_s_setprio(3);
-  row_finalize<DT, MODE>(a, rl, xtok, sm);
-  if (a.do_seq && last_arrival(&a.seq_cnt[b], (uint32_t)a.rps, &sm.flag)) seq_finalize<DT, MODE>(a, b, sm);
-  __builtin_amdgcn_s_setprio(0);
 }
 
-// One workgroup per item.  Workgroups are dispatched to the XCDs round-robin
-// by index, and the last chunk of a row to arrive (the one dispatched last)
-// merges the row; rows are therefore laid out on an odd number of items
-// (rstride: nchunks, plus one item without data when nchunks is even), so
-// that the merging position rotates over the XCDs from row to row instead of
-// landing on the same XCD every time.
+// One workgroup per (row, chunk).  No workgroup waits on another: the row
+// merge runs in the next launch, when HBM is no longer saturated and its few
+// dependent round trips are short.
 template <int DT, int MODE, bool VEC>
 __global__ void __launch_bounds__(WG, STREAM_WG_PER_CU) stream_kernel(Args a) {
   __shared__ Smem sm;
   stream_item<DT, MODE, VEC>(a, (int)blockIdx.x, sm);
+}
+
+// One workgroup per row: merge the chunk records into the row's max,
+// normaliser, filter threshold, kept list and the probability of its drafted
+// token; the last row of a sequence to finish runs the accept tests, the
+// first-rejection scan and (filtered and greedy rows) the final draw.
+template <int DT, int MODE>
+__global__ void __launch_bounds__(WG) row_kernel(Args a) {
+  __shared__ Smem sm;
+  const int rl = (int)blockIdx.x;
+  const int b = rl / a.rps, jr = rl - b * a.rps;
+  const int ir = jr <= a.K ? jr : jr - a.K - 1;
+  const int xtok = (a.do_seq && ir < a.K) ? a.X[(size_t)b * a.K + ir] : -1;
+  row_finalize<DT, MODE>(a, rl, xtok, sm);
+  if (a.do_seq && last_arrival(&a.seq_cnt[b], (uint32_t)a.rps, &sm.flag)) seq_finalize<DT, MODE>(a, b, sm);
 }
 
 template <int DT>
@@ -1242,6 +1250,17 @@ static KFn pick_stream_mode(int mode, bool vec) {
 }
 
 template <int DT>
+static KFn pick_row(int mode) {
+  switch (mode) {
+    case M_PLAIN: return (KFn)row_kernel<DT, M_PLAIN>;
+    case M_TOPK: return (KFn)row_kernel<DT, M_TOPK>;
+    case M_TOPP: return (KFn)row_kernel<DT, M_TOPP>;
+    case M_TOPKP: return (KFn)row_kernel<DT, M_TOPKP>;
+    default: return (KFn)row_kernel<DT, M_GREEDY>;
+  }
+}
+
+template <int DT>
 static KFn pick_probs(int mode) {
   switch (mode) {
     case M_PLAIN: return (KFn)probs_kernel<DT, M_PLAIN>;
@@ -1253,6 +1272,12 @@ static KFn pick_probs(int mode) {
 
 hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s) {
   KFn f = dtype == D_BF16 ? pick_stream_mode<D_BF16>(mode, vec) : pick_stream_mode<D_F32>(mode, vec);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
+  KFn f = dtype == D_BF16 ? pick_row<D_BF16>(mode) : pick_row<D_F32>(mode);
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
   return hipGetLastError();
 }
