@@ -125,7 +125,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": 5}), flush=True)
         return
 
-    from rejection_sampling_verify_09_amd import spec_verify
+    from rejection_sampling_verify_09_amd import profile_start, profile_stop, spec_verify
 
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
@@ -158,6 +158,9 @@ def main():
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    # the library also records HIP events around its streaming kernel on the
+    # launch stream, so that kernel's own average duration is measured live
+    profile_start()
     t_wall0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
@@ -165,13 +168,16 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
+    prof = profile_stop()
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
+    stream_ms = prof["stream_kernel_ms"] / max(1, prof["calls"])
+    other_ms = prof["other_kernels_ms"] / max(1, prof["calls"])
 
     n_host = out_n.cpu().numpy()
     emitted = int(np.sum(n_host[n_host >= 0] + 1))
     seq_per_s = w.B / (ms_per_step / 1e3)
-    achieved = bytes_per_step / (ms_per_step / 1e3) / 1e9
+    achieved = bytes_per_step / (stream_ms / 1e3) / 1e9  # the streaming kernel reads every logit once
     traffic = measured_traffic(name)
 
     result = {
@@ -202,7 +208,11 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "stream_kernel (single launch per step for this workload)",
+            "kernel": "stream_kernel",
+            "kernel_ms": stream_ms,
+            "other_kernels_ms": other_ms,
+            "timed_calls": prof["calls"],
+            "step_frac": bytes_per_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         },
     }
     if not args.no_cpu_baseline:

@@ -137,6 +137,21 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
                       float temperature, int32_t top_k, float top_p,
                       float* out_probs, void* stream);
 
+/*
+ * Launch timing for benchmarks.  Between sv_profile_start() and
+ * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug call records
+ * three HIP events on its own stream: before its streaming kernel (the pass
+ * that reads every logit once), after it, and after the call's last kernel.
+ * sv_profile_stop() waits for the recorded events and returns the summed
+ * durations in milliseconds of the streaming kernel and of the kernels that
+ * follow it (row merge, sequence finalisation, full-row draw), and the number
+ * of calls timed.  Any output pointer may be NULL.  Timing is host-global (not
+ * per device); it adds one event record per kernel boundary to each call.
+ * Returns SV_ERR_HIP if an event could not be created, recorded or read.
+ */
+int sv_profile_start(void);
+int sv_profile_stop(double* stream_kernel_ms, double* other_kernels_ms, int64_t* calls);
+
 /* Frees the per-device scratch of every device the library has used. */
 int sv_release(void);
 

@@ -10,9 +10,12 @@ from ._lib import (  # noqa: F401
     SpecVerifyError,
     filtered_probs,
     lib,
+    profile_start,
+    profile_stop,
     release,
     spec_verify,
     status_string,
 )
 
-__all__ = ["spec_verify", "filtered_probs", "release", "status_string", "lib", "SpecVerifyError"]
+__all__ = ["spec_verify", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
+           "SpecVerifyError"]

@@ -50,6 +50,11 @@ def lib() -> ctypes.CDLL:
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_version.argtypes = []
         L.sv_version.restype = ctypes.c_int
+        L.sv_profile_start.argtypes = []
+        L.sv_profile_start.restype = ctypes.c_int
+        L.sv_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64)]
+        L.sv_profile_stop.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -149,6 +154,23 @@ def filtered_probs(logits: torch.Tensor, temperature: float, top_k: int = 0, top
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_filtered_probs")
     return out
+
+
+def profile_start() -> None:
+    """Start timing every verification call's kernels with HIP events."""
+    st = lib().sv_profile_start()
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_profile_start")
+
+
+def profile_stop() -> dict:
+    """Stop timing; returns the summed streaming-kernel and follow-up kernel
+    durations (ms) and the number of calls timed."""
+    a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    st = lib().sv_profile_stop(ctypes.byref(a), ctypes.byref(b), ctypes.byref(n))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_profile_stop")
+    return dict(stream_kernel_ms=a.value, other_kernels_ms=b.value, calls=n.value)
 
 
 def release() -> None:

@@ -32,6 +32,51 @@ struct Scratch {
 std::mutex g_mu;
 Scratch g_scr[kMaxDevices];
 
+// Launch timing (sv_profile_start / sv_profile_stop): three events per call,
+// recorded on the call's stream before the streaming kernel, after it, and
+// after the call's last kernel.  Slots are reused round-robin; a slot is
+// folded into the totals (synchronising on its last event) before reuse.
+constexpr int kProfSlots = 1024;
+struct ProfSlot {
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  bool pending = false;
+};
+struct Profile {
+  bool on = false;
+  int next = 0;
+  double stream_ms = 0.0, rest_ms = 0.0;
+  int64_t calls = 0;
+  ProfSlot slot[kProfSlots];
+};
+std::mutex g_prof_mu;
+Profile g_prof;
+
+// Folds a recorded slot into the totals (caller holds g_prof_mu).
+int prof_fold(ProfSlot& sl) {
+  if (!sl.pending) return SV_OK;
+  sl.pending = false;
+  float a = 0.f, b = 0.f;
+  if (hipEventSynchronize(sl.ev[2]) != hipSuccess || hipEventElapsedTime(&a, sl.ev[0], sl.ev[1]) != hipSuccess ||
+      hipEventElapsedTime(&b, sl.ev[1], sl.ev[2]) != hipSuccess)
+    return SV_ERR_HIP;
+  g_prof.stream_ms += a;
+  g_prof.rest_ms += b;
+  g_prof.calls += 1;
+  return SV_OK;
+}
+
+// Takes the next slot for a call (nullptr when timing is off).
+ProfSlot* prof_begin() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof.on) return nullptr;
+  ProfSlot& sl = g_prof.slot[g_prof.next];
+  g_prof.next = (g_prof.next + 1) % kProfSlots;
+  if (prof_fold(sl) != SV_OK) return nullptr;
+  for (hipEvent_t& e : sl.ev)
+    if (!e && hipEventCreate(&e) != hipSuccess) return nullptr;
+  return &sl;
+}
+
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
@@ -188,10 +233,18 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
 
   const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
   hipStream_t s = (hipStream_t)stream;
+  ProfSlot* prof = prof_begin();
+  if (prof && hipEventRecord(prof->ev[0], s) != hipSuccess) return SV_ERR_HIP;
   if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
+  if (prof && hipEventRecord(prof->ev[1], s) != hipSuccess) return SV_ERR_HIP;
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (mode == M_PLAIN) {
     if (launch_sample(a, dtype, (unsigned)((int64_t)B * nsc), s) != hipSuccess) return SV_ERR_HIP;
+  }
+  if (prof) {
+    if (hipEventRecord(prof->ev[2], s) != hipSuccess) return SV_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    prof->pending = true;
   }
   return SV_OK;
 }
@@ -253,6 +306,30 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (launch_probs(a, dtype, mode, (unsigned)((int64_t)rows * nsc), s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
+}
+
+int sv_profile_start(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (ProfSlot& sl : g_prof.slot) sl.pending = false;
+  g_prof.on = true;
+  g_prof.next = 0;
+  g_prof.stream_ms = g_prof.rest_ms = 0.0;
+  g_prof.calls = 0;
+  return SV_OK;
+}
+
+int sv_profile_stop(double* stream_kernel_ms, double* other_kernels_ms, int64_t* calls) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.on = false;
+  int rc = SV_OK;
+  for (int i = 0; i < kProfSlots; ++i) {
+    ProfSlot& sl = g_prof.slot[(g_prof.next + i) % kProfSlots];
+    if (prof_fold(sl) != SV_OK) rc = SV_ERR_HIP;
+  }
+  if (stream_kernel_ms) *stream_kernel_ms = g_prof.stream_ms;
+  if (other_kernels_ms) *other_kernels_ms = g_prof.rest_ms;
+  if (calls) *calls = g_prof.calls;
+  return rc;
 }
 
 int sv_release(void) {

@@ -22,7 +22,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_filtered_probs", "sv_release", "sv_scratch_bytes",
-              "sv_status_string", "sv_version"]:
+              "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
         assert s in syms
 
 
@@ -95,3 +95,9 @@ def test_filtered_probs_validation():
     assert f(FAKE, 4, 10, 0, 0.0, 0, 1.0, FAKE, None) == L.SV_ERR_PARAM
     assert f(None, 4, 10, 0, 1.0, 0, 1.0, FAKE, None) == L.SV_ERR_NULL
     assert f(None, 0, 10, 0, 1.0, 0, 1.0, None, None) == L.SV_OK
+
+
+def test_profile_without_calls_reports_nothing():
+    L.profile_start()
+    r = L.profile_stop()
+    assert r == dict(stream_kernel_ms=0.0, other_kernels_ms=0.0, calls=0)
