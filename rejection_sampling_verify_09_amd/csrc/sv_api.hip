@@ -25,7 +25,6 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 32) / WG - 1;
 struct Scratch {
   char* ptr = nullptr;
   size_t bytes = 0;
-  int cus = 0;           // compute units of the device (persistent grid size)
   int64_t cap_seq = 0;   // sequences the (zero-filled) arrival counters cover
 };
 
@@ -80,41 +79,46 @@ ProfSlot* prof_begin() {
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, total;
+  size_t seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, xlogit, total;
+};
+
+// What one call needs from the scratch.
+struct Need {
+  int64_t rows = 0, nchunks = 0, B = 0, nseg = 0;  // nseg: sampling segments per sequence
+  bool filt = false;                               // candidate and kept lists
 };
 
 // Counters first (a fixed region for the life of the allocation: the kernels
 // leave every counter at zero, so it never needs clearing), then the data
 // records of the call.
-Layout make_layout(int64_t cap_seq, int64_t rows, int64_t nchunks, bool filt, int64_t B,
-                   int64_t nseg) {
+Layout make_layout(int64_t cap_seq, const Need& n) {
   Layout L;
   size_t o = 0;
   L.seq_cnt = o; o += al256(cap_seq * 4);
   L.smp_cnt = o; o += al256(cap_seq * 4);
-  L.chunk = o; o += al256(rows * nchunks * sizeof(ChunkRec));
-  L.cand = o; o += filt ? al256(rows * nchunks * CAND_CAP * sizeof(uint64_t)) : 0;
-  L.row = o; o += al256(rows * sizeof(RowRec));
-  L.kidx = o; o += filt ? al256(rows * KEEP_CAP * sizeof(int32_t)) : 0;
-  L.kprob = o; o += filt ? al256(rows * KEEP_CAP * sizeof(double)) : 0;
-  L.seq = o; o += al256(B * sizeof(SeqRec));
-  L.seg_sum = o; o += al256(B * nseg * sizeof(double));
-  L.seg_last = o; o += al256(B * nseg * sizeof(int32_t));
+  L.chunk = o; o += al256(n.rows * n.nchunks * sizeof(ChunkRec));
+  L.cand = o; o += n.filt ? al256(n.rows * n.nchunks * CAND_CAP * sizeof(uint64_t)) : 0;
+  L.row = o; o += al256(n.rows * sizeof(RowRec));
+  L.kidx = o; o += n.filt ? al256(n.rows * KEEP_CAP * sizeof(int32_t)) : 0;
+  L.kprob = o; o += n.filt ? al256(n.rows * KEEP_CAP * sizeof(double)) : 0;
+  L.seq = o; o += al256(n.B * sizeof(SeqRec));
+  L.seg_sum = o; o += al256(n.B * n.nseg * sizeof(double));
+  L.seg_last = o; o += al256(n.B * n.nseg * sizeof(int32_t));
+  L.xlogit = o; o += al256(n.rows * sizeof(float));
   L.total = o;
   return L;
 }
 
 // Returns the scratch of the current device, large enough for this call.
-int get_scratch(int64_t rows, int64_t nchunks, bool filt, int64_t B, int64_t nseg, char** base, Layout* lay,
-                int* cus) {
+int get_scratch(const Need& n, char** base, Layout* lay) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
   std::lock_guard<std::mutex> lk(g_mu);
   Scratch& s = g_scr[dev];
-  Layout L = make_layout(s.cap_seq, rows, nchunks, filt, B, nseg);
-  if (s.ptr == nullptr || s.cap_seq < B || s.bytes < L.total) {
-    const int64_t cs = std::max(B, s.cap_seq);
-    L = make_layout(cs, rows, nchunks, filt, B, nseg);
+  Layout L = make_layout(s.cap_seq, n);
+  if (s.ptr == nullptr || s.cap_seq < n.B || s.bytes < L.total) {
+    const int64_t cs = std::max(n.B, s.cap_seq);
+    L = make_layout(cs, n);
     const size_t want = std::max(L.total, s.bytes);
     if (s.ptr) {
       if (hipDeviceSynchronize() != hipSuccess) return SV_ERR_HIP;
@@ -131,14 +135,10 @@ int get_scratch(int64_t rows, int64_t nchunks, bool filt, int64_t B, int64_t nse
     }
     s.ptr = (char*)p;
     s.bytes = want;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-    s.cus = cus;
     s.cap_seq = cs;
   }
   *base = s.ptr;
-  *lay = make_layout(s.cap_seq, rows, nchunks, filt, B, nseg);
-  *cus = s.cus;
+  *lay = make_layout(s.cap_seq, n);
   return SV_OK;
 }
 
@@ -153,6 +153,7 @@ void bind_scratch(Args& a, char* base, const Layout& L) {
   a.seq = (SeqRec*)(base + L.seq);
   a.seg_sum = (double*)(base + L.seg_sum);
   a.seg_last = (int32_t*)(base + L.seg_last);
+  a.xlogit = (float*)(base + L.xlogit);
 }
 
 int check_params(float T, int32_t top_k, float top_p) {
@@ -203,11 +204,16 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
   if (rows * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
-  const bool filt = mode == M_TOPK || mode == M_TOPP || mode == M_TOPKP;
+  Need need;
+  need.rows = rows;
+  need.nchunks = nchunks;
+  need.B = B;
+  need.nseg = nsc * SEG_PER_SCE;
+  need.filt = mode == M_TOPK || mode == M_TOPP || mode == M_TOPKP;
+
   char* base = nullptr;
   Layout L;
-  int cus = 1;
-  st = get_scratch(rows, nchunks, filt, B, nsc * SEG_PER_SCE, &base, &L, &cus);
+  st = get_scratch(need, &base, &L);
   if (st != SV_OK) return st;
 
   Args a;
@@ -232,12 +238,15 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   bind_scratch(a, base, L);
 
   const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
+  a.ulen = vec ? 16 / esz : 1;
   hipStream_t s = (hipStream_t)stream;
   ProfSlot* prof = prof_begin();
   if (prof && hipEventRecord(prof->ev[0], s) != hipSuccess) return SV_ERR_HIP;
+  // chunk-parallel streaming pass, then one workgroup per sequence merges its
+  // rows and finishes it
   if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
   if (prof && hipEventRecord(prof->ev[1], s) != hipSuccess) return SV_ERR_HIP;
-  if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_row(a, dtype, mode, (unsigned)B, s) != hipSuccess) return SV_ERR_HIP;
   if (mode == M_PLAIN) {
     if (launch_sample(a, dtype, (unsigned)((int64_t)B * nsc), s) != hipSuccess) return SV_ERR_HIP;
   }
@@ -282,11 +291,15 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
   if ((int64_t)rows * nchunks > kMaxGrid || (int64_t)rows * nsc > kMaxGrid) return SV_ERR_SHAPE;
-  const bool filt = mode != M_PLAIN;
+  Need need;
+  need.rows = rows;
+  need.nchunks = nchunks;
+  need.B = rows;
+  need.filt = mode != M_PLAIN;
+
   char* base = nullptr;
   Layout L;
-  int cus = 1;
-  st = get_scratch(rows, nchunks, filt, rows, 0, &base, &L, &cus);
+  st = get_scratch(need, &base, &L);
   if (st != SV_OK) return st;
   Args a = {};
   a.tgt = logits;
@@ -301,6 +314,7 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   set_scalars(a, temperature, top_k, top_p);
   bind_scratch(a, base, L);
   const bool vec = aligned16(logits) && ((int64_t)V * esz) % 16 == 0;
+  a.ulen = vec ? 16 / esz : 1;
   hipStream_t s = (hipStream_t)stream;
   if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;

@@ -17,10 +17,15 @@ constexpr int SCE = 2048;        // logits per sampling chunk (8 per thread)
 constexpr int SEG = 512;         // logits per sampling segment (one wave)
 constexpr int SEG_PER_SCE = SCE / SEG;
 constexpr int MAX_K = 64;
-constexpr int STREAM_WG_PER_CU = 6;  // register budget of the streaming kernel: 6 resident workgroups per CU
+// register budget of the streaming kernel: resident workgroups per CU
+// (vector-loaded bf16 chunks need the fewest registers)
+template <int DT, bool VEC>
+constexpr int stream_wg_per_cu() { return (DT == 1 && VEC) ? 8 : 5; }
 constexpr int MAX_CHUNKS = WG;           // chunks per row (one chunk record per thread in a row merge)
 constexpr int64_t MAX_V = (int64_t)MAX_CHUNKS * CE;  // 2,097,152
 constexpr int MAX_RPS = 2 * MAX_K + 1;
+constexpr int ROW_WG = 1024;       // row kernel: one workgroup per sequence, one wave per row at a time
+constexpr int ROW_NW = ROW_WG / 64;
 // top-p candidates: every logit within this many units of z = logit / T below
 // the row maximum (the cut is verified against the mass at the row merge)
 constexpr float TOPP_WINDOW_Z = 8.0f;
@@ -89,6 +94,8 @@ struct Args {
   uint32_t* smp_cnt;
   double* seg_sum;
   int32_t* seg_last;
+  float* xlogit;  // per row: the logit of its drafted token (written by the streaming pass)
+  int32_t ulen;   // logits per candidate unit (16-byte vector; 1 on the element-load path)
 };
 
 // Order-preserving map float -> uint32 (larger float, larger key).
@@ -102,8 +109,22 @@ __device__ __forceinline__ float key_val(uint32_t k) {
 }
 constexpr uint32_t KEY_NEG_INF = 0x007FFFFFu;  // ord_key(-inf)
 
+// A candidate entry as written by the streaming pass (float bits << 32 |
+// index) turned into (order key << 32 | index); never 0.
+__device__ __forceinline__ uint64_t cand_entry_key(uint64_t raw) {
+  return ((uint64_t)ord_key(__uint_as_float((uint32_t)(raw >> 32))) << 32) | (uint32_t)raw;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Logit i of a 16-byte vector of logits (8 bf16 or 4 f32).
+template <int DT>
+__device__ __forceinline__ float unit_elem(const uint4& r, int i) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  if (DT == D_BF16) return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+  return __uint_as_float(w[i]);
+}
 
 template <int DT>
 __device__ __forceinline__ float load_elem(const char* row, int j) {
@@ -178,59 +199,149 @@ __device__ __forceinline__ double dpp_wave_sum(double v) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// Block-wide reductions over the 256 threads, fixed combination order.
+// Inclusive prefix sums over the 64 lanes of a wave with DPP: shifts of 1, 2,
+// 4 and 8 lanes within each row of 16, then the row broadcasts 15 and 31.
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ uint32_t dppz(uint32_t v) {  // 0 where the source lane is outside the row
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, RM, 0xF, false);
+}
+constexpr int DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118;
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
+  v += dppz<DPP_SHR1>(v);
+  v += dppz<DPP_SHR2>(v);
+  v += dppz<DPP_SHR4>(v);
+  v += dppz<DPP_SHR8>(v);
+  v += dppz<DPP_BCAST15, 0xA>(v);
+  v += dppz<DPP_BCAST31, 0xC>(v);
+  return v;
+}
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ uint64_t dppz64(uint64_t v) {
+  return ((uint64_t)dppz<CTRL, RM>((uint32_t)(v >> 32)) << 32) | dppz<CTRL, RM>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
+  v += dppz64<DPP_SHR1>(v);
+  v += dppz64<DPP_SHR2>(v);
+  v += dppz64<DPP_SHR4>(v);
+  v += dppz64<DPP_SHR8>(v);
+  v += dppz64<DPP_BCAST15, 0xA>(v);
+  v += dppz64<DPP_BCAST31, 0xC>(v);
+  return v;
+}
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ double dppz_f64(double v) {
+  return __longlong_as_double((long long)dppz64<CTRL, RM>((uint64_t)__double_as_longlong(v)));
+}
+__device__ __forceinline__ double wave_scan_f64(double v) {
+  v += dppz_f64<DPP_SHR1>(v);
+  v += dppz_f64<DPP_SHR2>(v);
+  v += dppz_f64<DPP_SHR4>(v);
+  v += dppz_f64<DPP_SHR8>(v);
+  v += dppz_f64<DPP_BCAST15, 0xA>(v);
+  v += dppz_f64<DPP_BCAST31, 0xC>(v);
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T lane63(T v) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  }
+}
+__device__ __forceinline__ uint32_t dpp_wave_umax(uint32_t v) {
+  v = max(v, dpp_u32<DPP_QP_1032>(0u, v));
+  v = max(v, dpp_u32<DPP_QP_2301>(0u, v));
+  v = max(v, dpp_u32<DPP_HALF_MIRROR>(0u, v));
+  v = max(v, dpp_u32<DPP_MIRROR>(0u, v));
+  v = max(v, dpp_u32<DPP_BCAST15, 0xA>(0u, v));
+  v = max(v, dpp_u32<DPP_BCAST31, 0xC>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Block-wide reductions over NW waves (one partial per wave in LDS), fixed
+// combination order.
+constexpr int MAX_NW = 16;
 struct Red {
-  double d[NWAVE];
-  float f[NWAVE];
-  int32_t i[NWAVE];
-  uint32_t u[NWAVE];
+  double d[MAX_NW];
+  float f[MAX_NW];
+  int32_t i[MAX_NW];
+  uint32_t u[MAX_NW];
 };
 
+template <int NW = NWAVE>
 __device__ __forceinline__ float block_fmax(float v, Red& r) {
   v = dpp_wave_fmax(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.f[threadIdx.x >> 6] = v;
   __syncthreads();
-  return fmaxf(fmaxf(r.f[0], r.f[1]), fmaxf(r.f[2], r.f[3]));
+  float x = r.f[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) x = fmaxf(x, r.f[i]);
+  return x;
 }
+template <int NW = NWAVE>
 __device__ __forceinline__ double block_sum(double v, Red& r) {
   v = dpp_wave_sum(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.d[threadIdx.x >> 6] = v;
   __syncthreads();
-  return (r.d[0] + r.d[1]) + (r.d[2] + r.d[3]);
+  double x = r.d[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) x += r.d[i];
+  return x;
 }
+template <int NW = NWAVE>
 __device__ __forceinline__ int32_t block_min_i(int32_t v, Red& r) {
   v = wave_min(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.i[threadIdx.x >> 6] = v;
   __syncthreads();
-  return min(min(r.i[0], r.i[1]), min(r.i[2], r.i[3]));
+  int32_t x = r.i[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) x = min(x, r.i[i]);
+  return x;
 }
+template <int NW = NWAVE>
 __device__ __forceinline__ int32_t block_max_i(int32_t v, Red& r) {
   v = wave_max(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.i[threadIdx.x >> 6] = v;
   __syncthreads();
-  return max(max(r.i[0], r.i[1]), max(r.i[2], r.i[3]));
+  int32_t x = r.i[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) x = max(x, r.i[i]);
+  return x;
 }
+template <int NW = NWAVE>
 __device__ __forceinline__ uint32_t block_max_u(uint32_t v, Red& r) {
   v = wave_max(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.u[threadIdx.x >> 6] = v;
   __syncthreads();
-  return max(max(r.u[0], r.u[1]), max(r.u[2], r.u[3]));
+  uint32_t x = r.u[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) x = max(x, r.u[i]);
+  return x;
 }
+template <int NW = NWAVE>
 __device__ __forceinline__ int32_t block_sum_i(int32_t v, Red& r) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) r.i[threadIdx.x >> 6] = v;
   __syncthreads();
-  return (r.i[0] + r.i[1]) + (r.i[2] + r.i[3]);
+  int32_t x = r.i[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) x += r.i[i];
+  return x;
 }
 
 // Inclusive prefix sum over the block (one value per thread, thread order).
+template <int NW = NWAVE>
 __device__ __forceinline__ double block_incl_scan(double v, Red& r, double* total) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -243,16 +354,21 @@ __device__ __forceinline__ double block_incl_scan(double v, Red& r, double* tota
   __syncthreads();
   double off = 0.0;
   for (int i = 0; i < w; ++i) off += r.d[i];
-  *total = ((r.d[0] + r.d[1]) + r.d[2]) + r.d[3];
+  double tot = r.d[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) tot += r.d[i];
+  *total = tot;
   return v + off;
 }
 
-// Bitonic sort of n (power of two, <= 4 * WG) 64-bit keys in LDS, descending.
+// Bitonic sort of n (power of two) 64-bit keys in LDS, descending, by a
+// block of BS threads.
+template <int BS = WG>
 __device__ __forceinline__ void bitonic_desc(uint64_t* a, int n) {
   __syncthreads();
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += WG) {
+      for (int i = threadIdx.x; i < n; i += BS) {
         int p = i ^ j;
         if (p > i) {
           uint64_t x = a[i], y = a[p];
@@ -306,10 +422,17 @@ __device__ __forceinline__ bool last_arrival(uint32_t* cnt, uint32_t total, int*
   return *flag != 0;
 }
 
+// Row rl of the verification (per sequence: K+1 target rows, then K draft
+// rows).  The base is chosen by arithmetic on the two pointer values: a
+// choice between the two argument fields themselves can be compiled into a
+// load from a computed address inside the argument block, which moves the
+// whole block to scratch memory.
 __device__ __forceinline__ const char* row_ptr(const Args& a, int rl, int esz) {
   const int b = rl / a.rps, j = rl - b * a.rps;
-  if (j <= a.K) return (const char*)a.tgt + ((size_t)b * (a.K + 1) + j) * (size_t)a.V * esz;
-  return (const char*)a.drf + ((size_t)b * a.K + (j - a.K - 1)) * (size_t)a.V * esz;
+  const bool dr = j > a.K;
+  const size_t idx = dr ? (size_t)b * a.K + (j - a.K - 1) : (size_t)b * (a.K + 1) + j;
+  const uintptr_t t = (uintptr_t)a.tgt, d = (uintptr_t)a.drf;
+  return (const char*)(t + (dr ? d - t : (uintptr_t)0)) + idx * (size_t)a.V * esz;
 }
 
 }  // namespace sv

@@ -65,6 +65,7 @@ struct DrawRow {
 
 struct SmemStream {
   uint64_t cand[NWAVE * CAND_CAP];  // per-wave candidate lists (one flat list after an overflow cut)
+  uint64_t junk[NWAVE][64];         // per-lane target of the emission's writes that keep nothing
   uint64_t tk[WG];
   uint32_t hist[256];
   int32_t wn[NWAVE];
@@ -102,7 +103,7 @@ struct Smem {
     SmemStream s;
     SmemRow r;
     SmemSeq q;
-    double scan[WG];
+    double scan[ROW_WG];
   };
   Red red;
   DrawRow dr[2];
@@ -227,7 +228,7 @@ constexpr double MASS_SCALE = 4503599627370496.0;  // 2^52
 // actual logit: the cut of a top-k (counts) or top-p (mass) set.  Radix
 // search, 8 key bits per pass over the whole row (used only when the
 // candidate lists cannot decide the cut).
-template <int DT>
+template <int DT, int BS>
 __device__ uint32_t row_radix(const char* rp, int V, uint32_t lo, bool mass, float m, double invT, double snorm,
                               double target, Smem& sm) {
   const int t = threadIdx.x;
@@ -236,9 +237,9 @@ __device__ uint32_t row_radix(const char* rp, int V, uint32_t lo, bool mass, flo
   unsigned long long above = 0;  // F of everything in higher bins at the levels fixed so far
   for (int shift = 24; shift >= 0; shift -= 8) {
     __syncthreads();
-    for (int d = t; d < 256; d += WG) sm.r.hist64[d] = 0ull;
+    for (int d = t; d < 256; d += BS) sm.r.hist64[d] = 0ull;
     __syncthreads();
-    for (int j = t; j < V; j += WG) {
+    for (int j = t; j < V; j += BS) {
       const float x = load_elem<DT>(rp, j);
       const uint32_t key = ord_key(x);
       if (key >= lo && (key & pmask) == prefix) {
@@ -271,14 +272,14 @@ __device__ uint32_t row_radix(const char* rp, int V, uint32_t lo, bool mass, flo
 // One pass over the row for a cut tau: the number of kept logits, their
 // normaliser sum exp((x - m) / T), and (when they fit) the kept entries in
 // sm.r.keys.
-template <int DT>
+template <int DT, int BS>
 __device__ int row_keep(const char* rp, int V, uint32_t tau, float m, double invT, double* skept, Smem& sm) {
   const int t = threadIdx.x;
   __syncthreads();
   if (t == 0) sm.ncand = 0;
   __syncthreads();
   double acc = 0.0;
-  for (int j = t; j < V; j += WG) {
+  for (int j = t; j < V; j += BS) {
     const float x = load_elem<DT>(rp, j);
     const uint32_t key = ord_key(x);
     if (key >= tau) {
@@ -287,21 +288,22 @@ __device__ int row_keep(const char* rp, int V, uint32_t tau, float m, double inv
       if (slot < KEEP_CAP) sm.r.keys[slot] = ((uint64_t)key << 32) | (uint32_t)j;
     }
   }
-  *skept = block_sum(acc, sm.red);
+  *skept = block_sum<BS / 64>(acc, sm.red);
   return sm.ncand;
 }
 
 // Radix select (8 bits per pass, counts in LDS) of the k-th largest key among
 // the n candidates in sm.r.cand.
+template <int BS>
 __device__ uint32_t cand_select(int n, int k, Smem& sm) {
   const int t = threadIdx.x;
   uint32_t prefix = 0, pmask = 0;
   int need = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
     __syncthreads();
-    for (int d = t; d < 256; d += WG) sm.r.hist[d] = 0;
+    for (int d = t; d < 256; d += BS) sm.r.hist[d] = 0;
     __syncthreads();
-    for (int e = t; e < n; e += WG) {
+    for (int e = t; e < n; e += BS) {
       const uint32_t key = (uint32_t)(sm.r.cand[e] >> 32);
       if ((key & pmask) == prefix) atomicAdd(&sm.r.hist[(key >> shift) & 255u], 1u);
     }
@@ -325,6 +327,7 @@ __device__ uint32_t cand_select(int n, int k, Smem& sm) {
 }
 
 // Exclusive prefix sum of one int per thread (thread order); *total gets the sum.
+template <int NW>
 __device__ __forceinline__ int block_excl_scan_i(int v, Red& r, int* total) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   int x = v;
@@ -336,24 +339,27 @@ __device__ __forceinline__ int block_excl_scan_i(int v, Red& r, int* total) {
   __syncthreads();
   if (l == 63) r.i[w] = x;
   __syncthreads();
-  int off = 0;
+  int off = 0, tot = 0;
   for (int i = 0; i < w; ++i) off += r.i[i];
-  *total = ((r.i[0] + r.i[1]) + r.i[2]) + r.i[3];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) tot += r.i[i];
+  *total = tot;
   return x + off - v;
 }
 
 // Sort the first n entries of sm.r.keys descending (pads with zeros).
+template <int BS>
 __device__ void sort_keys_desc(int n, Smem& sm) {
   const int np2 = pow2_at_least(n < 2 ? 2 : n);
   __syncthreads();
-  for (int e = n + threadIdx.x; e < np2; e += WG) sm.r.keys[e] = 0;
-  bitonic_desc(sm.r.keys, np2);
+  for (int e = n + threadIdx.x; e < np2; e += BS) sm.r.keys[e] = 0;
+  bitonic_desc<BS>(sm.r.keys, np2);
 }
 
 // Top-k / top-p threshold of one row and its kept list.  On entry the chunk
 // records are in sm.r (cm, cb, cn) and the row is valid (finite max m;
 // for top-p also a finite normaliser rr.S).
-template <int DT, int MODE>
+template <int DT, int MODE, int BS>
 __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRec& rr, Smem& sm) {
   const int t = threadIdx.x, nch = a.nchunks;
   const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
@@ -362,10 +368,10 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
   // Every finite logit with key >= lo is among the candidates: each chunk
   // emitted all of its finite logits at or above its own bound, and lo is the
   // largest bound (and, for top-p, at least the window below the row max).
-  uint32_t lo = block_max_u(t < nch ? sm.r.cb[t] : 0u, sm.red);
+  uint32_t lo = block_max_u<BS / 64>(t < nch ? sm.r.cb[t] : 0u, sm.red);
   if (MODE == M_TOPP) lo = max(lo, ord_key(m - a.win));
   int ncand_total;
-  const int my_off = block_excl_scan_i(t < nch ? sm.r.cn[t] : 0, sm.red, &ncand_total);
+  const int my_off = block_excl_scan_i<BS / 64>(t < nch ? sm.r.cn[t] : 0, sm.red, &ncand_total);
   if (t < nch) sm.r.off[t] = my_off;
   if (t == 0) sm.r.off[nch] = ncand_total;
   __syncthreads();
@@ -384,11 +390,11 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
     const int cap = (MODE == M_TOPP) ? KEEP_CAP : ROW_CAND;
     if (t == 0) sm.ncand = 0;
     __syncthreads();
-    for (int base = 0; base < ncand_total; base += WG * LOAD_BATCH) {
+    for (int base = 0; base < ncand_total; base += BS * LOAD_BATCH) {
       uint64_t ck[LOAD_BATCH];
 #pragma unroll
       for (int j = 0; j < LOAD_BATCH; ++j) {
-        const int e = base + t + j * WG;
+        const int e = base + t + j * BS;
         ck[j] = 0ull;
         if (e < ncand_total) {
           int lo_c = 0, hi_c = nch;  // last chunk with off <= e
@@ -397,14 +403,28 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
             if (sm.r.off[mid] <= e) lo_c = mid;
             else hi_c = mid;
           }
-          ck[j] = ld_dev(&cand[(size_t)lo_c * CAND_CAP + (e - sm.r.off[lo_c])]);
+          ck[j] = cand_entry_key(ld_dev(&cand[(size_t)lo_c * CAND_CAP + (e - sm.r.off[lo_c])]));
         }
       }
 #pragma unroll
       for (int j = 0; j < LOAD_BATCH; ++j) {
         if (ck[j] != 0ull && (uint32_t)(ck[j] >> 32) >= lo) {
-          const int slot = atomicAdd(&sm.ncand, 1);
-          if (slot < cap) dstv[slot] = ck[j];
+          if (a.ulen > 1) {
+            // a candidate unit: its logits at or above lo
+            const int st = (int)(uint32_t)ck[j];
+            const uint4 r = *reinterpret_cast<const uint4*>(rp + (size_t)st * ElemT<DT>::ESZ);
+            for (int i = 0; i < 16 / ElemT<DT>::ESZ; ++i) {
+              const float x = unit_elem<DT>(r, i);
+              const uint32_t key = ord_key(x);
+              if (key >= lo && x > -INFINITY) {
+                const int slot = atomicAdd(&sm.ncand, 1);
+                if (slot < cap) dstv[slot] = ((uint64_t)key << 32) | (uint32_t)(st + i);
+              }
+            }
+          } else {
+            const int slot = atomicAdd(&sm.ncand, 1);
+            if (slot < cap) dstv[slot] = ck[j];
+          }
         }
       }
     }
@@ -419,14 +439,14 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
       // than k finite logits and all are kept; otherwise the lists cannot decide
       if (cnt < a.top_k && lo > KEY_NEG_INF) fb = true;
       if (!fb) {
-        const uint32_t tk = cnt < a.top_k ? KEY_NEG_INF : cand_select(cnt, a.top_k, sm);
+        const uint32_t tk = cnt < a.top_k ? KEY_NEG_INF : cand_select<BS>(cnt, a.top_k, sm);
         tau = tk;
         // kept set: candidates with key >= tk, into sm.r.keys
         __syncthreads();
         if (t == 0) sm.i1 = 0;
         __syncthreads();
         double sacc = 0.0;
-        for (int e = t; e < cnt; e += WG) {
+        for (int e = t; e < cnt; e += BS) {
           const uint64_t ce = sm.r.cand[e];
           const uint32_t key = (uint32_t)(ce >> 32);
           if (key >= tk) {
@@ -435,10 +455,10 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
             if (slot < KEEP_CAP) sm.r.keys[slot] = ce;
           }
         }
-        const double sk = block_sum(sacc, sm.red);
+        const double sk = block_sum<BS / 64>(sacc, sm.red);
         const int nall = sm.i1;
         if (nall <= KEEP_CAP) {
-          sort_keys_desc(nall, sm);
+          sort_keys_desc<BS>(nall, sm);
           ns = nall;
           nk = nall;
           snorm = sk;
@@ -450,7 +470,7 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
         }
       }
     } else {  // M_TOPP
-      sort_keys_desc(cnt, sm);
+      sort_keys_desc<BS>(cnt, sm);
       ns = cnt;
     }
     if (!fb && (MODE == M_TOPP || MODE == M_TOPKP)) {
@@ -458,9 +478,9 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
       const uint32_t key = t < ns ? (uint32_t)(sm.r.keys[t] >> 32) : 0u;
       const double w = t < ns ? exp(((double)key_val(key) - (double)m) * invT) / snorm : 0.0;
       double tot;
-      const double C = block_incl_scan(w, sm.red, &tot);
+      const double C = block_incl_scan<BS / 64>(w, sm.red, &tot);
       int first = (t < ns && C >= a.top_p) ? t : INT_MAX;
-      first = block_min_i(first, sm.red);
+      first = block_min_i<BS / 64>(first, sm.red);
       if (first == INT_MAX) {
         if (MODE == M_TOPP) fb = true;  // the nucleus reaches below the candidate window
         else first = ns - 1;             // round-off kept the top-k mass just below top_p
@@ -470,7 +490,7 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
         __syncthreads();
         const uint32_t tp = (uint32_t)(sm.r.keys[first] >> 32);
         tau = tp > tau ? tp : tau;
-        nk = block_sum_i((t < ns && key >= tau) ? 1 : 0, sm.red);
+        nk = block_sum_i<BS / 64>((t < ns && key >= tau) ? 1 : 0, sm.red);
       }
     }
   }
@@ -482,18 +502,18 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
     uint32_t tk = 0;
     double sk = 0.0;
     if (MODE == M_TOPK || MODE == M_TOPKP) {
-      tk = row_radix<DT>(rp, a.V, 0u, false, m, invT, 1.0, (double)a.top_k, sm);
-      if (MODE == M_TOPKP) (void)row_keep<DT>(rp, a.V, tk, m, invT, &sk, sm);
+      tk = row_radix<DT, BS>(rp, a.V, 0u, false, m, invT, 1.0, (double)a.top_k, sm);
+      if (MODE == M_TOPKP) (void)row_keep<DT, BS>(rp, a.V, tk, m, invT, &sk, sm);
     }
     if (MODE == M_TOPP || MODE == M_TOPKP) {
       const double sn = MODE == M_TOPP ? rr.S : sk;
-      tau = row_radix<DT>(rp, a.V, tk, true, m, invT, sn, a.top_p, sm);
+      tau = row_radix<DT, BS>(rp, a.V, tk, true, m, invT, sn, a.top_p, sm);
     } else {
       tau = tk;
     }
-    const int nall = row_keep<DT>(rp, a.V, tau, m, invT, &skept, sm);
+    const int nall = row_keep<DT, BS>(rp, a.V, tau, m, invT, &skept, sm);
     if (nall <= KEEP_CAP) {
-      sort_keys_desc(nall, sm);
+      sort_keys_desc<BS>(nall, sm);
       nk = nall;
     } else {
       big = true;
@@ -505,11 +525,11 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
     const uint64_t e = t < nk ? sm.r.keys[t] : 0ull;
     const uint32_t key = (uint32_t)(e >> 32);
     const double ex = t < nk ? exp(((double)key_val(key) - (double)m) * invT) : 0.0;
-    skept = block_sum(ex, sm.red);
+    skept = block_sum<BS / 64>(ex, sm.red);
     // kept list in ascending vocabulary order: re-key as (~index << 32 | key)
     __syncthreads();
     if (t < nk) sm.r.keys[t] = ((uint64_t)(~(uint32_t)e) << 32) | key;
-    sort_keys_desc(nk, sm);
+    sort_keys_desc<BS>(nk, sm);
     __syncthreads();
     if (t < nk) {
       const uint64_t f = sm.r.keys[t];
@@ -549,8 +569,8 @@ __device__ __forceinline__ RowRec load_row(const RowRec* p) {
   return r;
 }
 
-template <int DT, int MODE>
-__device__ void row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
+template <int DT, int MODE, int BS>
+__device__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x, nch = a.nchunks;
@@ -568,9 +588,9 @@ __device__ void row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
     if (MODE == M_GREEDY) sm.r.carg[t] = ld_dev(&cr[t].arg);
   }
   const bool hx = xtok >= 0 && xtok < a.V;
-  if (t == WG - 1) sm.lx = (MODE != M_GREEDY && hx) ? load_elem<DT>(rp, xtok) : -INFINITY;
+  if (t == BS - 1) sm.lx = (MODE != M_GREEDY && hx) ? load_elem<DT>(rp, xtok) : -INFINITY;
   __syncthreads();
-  const float m = block_fmax(t < nch ? sm.r.cm[t] : -INFINITY, sm.red);
+  const float m = block_fmax<BS / 64>(t < nch ? sm.r.cm[t] : -INFINITY, sm.red);
   RowRec rr;
   rr.S = 0.0;
   rr.S_kept = 0.0;
@@ -585,16 +605,16 @@ __device__ void row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
   if (MODE == M_PLAIN || MODE == M_TOPP) {
     const float qm = t < nch ? sm.r.cm[t] : -INFINITY;
     const double s = qm > -INFINITY ? sm.r.cs[t] * exp(((double)qm - (double)m) * a.invT) : 0.0;
-    const double S = block_sum(s, sm.red);
+    const double S = block_sum<BS / 64>(s, sm.red);
     rr.S = S;
     if (!(S > 0.0 && S < INFINITY)) bad = true;
   }
   if (MODE == M_GREEDY) {
-    const int best = block_min_i((t < nch && sm.r.cm[t] == m) ? sm.r.carg[t] : INT_MAX, sm.red);
+    const int best = block_min_i<BS / 64>((t < nch && sm.r.cm[t] == m) ? sm.r.carg[t] : INT_MAX, sm.red);
     rr.arg = best == INT_MAX ? 0 : best;
   }
   if (FILT) {
-    if (!bad) filter_row<DT, MODE>(a, rl, rp, m, rr, sm);
+    if (!bad) filter_row<DT, MODE, BS>(a, rl, rp, m, rr, sm);
   }
   if (!bad && hx) {
     if (MODE == M_GREEDY) {
@@ -607,58 +627,12 @@ __device__ void row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
   if (bad) rr.flags |= RF_BAD;
   __syncthreads();
   if (t == 0) store_row(&a.row[rl], rr);
+  return rr;
 }
 
 // ---------------------------------------------------------------------------
 // final draw
 // ---------------------------------------------------------------------------
-
-// Draw from the kept lists (filtered rows): residual max(0, p - q) over the
-// target's kept tokens, or p itself (bonus, or an empty residual).
-__device__ int list_sample(const Args& a, double u, int rlP, int np, int rlQ, int nq, bool res, Smem& sm,
-                           double* Zout) {
-  const int t = threadIdx.x;
-  __syncthreads();
-  if (t < np) {
-    sm.q.pidx[t] = ld_dev(&a.kidx[(size_t)rlP * KEEP_CAP + t]);
-    sm.q.pprob[t] = ld_dev(&a.kprob[(size_t)rlP * KEEP_CAP + t]);
-  }
-  if (res && t < nq) {
-    sm.q.qidx[t] = ld_dev(&a.kidx[(size_t)rlQ * KEEP_CAP + t]);
-    sm.q.qprob[t] = ld_dev(&a.kprob[(size_t)rlQ * KEEP_CAP + t]);
-  }
-  __syncthreads();
-  double p = 0.0, w = 0.0;
-  if (t < np) {
-    p = sm.q.pprob[t];
-    w = p;
-    if (res) {
-      const int idx = sm.q.pidx[t];
-      int lo = 0, hi = nq;  // first position with qidx >= idx
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sm.q.qidx[mid] < idx) lo = mid + 1;
-        else hi = mid;
-      }
-      const double q = (lo < nq && sm.q.qidx[lo] == idx) ? sm.q.qprob[lo] : 0.0;
-      const double d = p - q;
-      w = d > 0.0 ? d : 0.0;
-    }
-  }
-  double Z;
-  double C = block_incl_scan(w, sm.red, &Z);
-  if (res && !(Z > 0.0)) {
-    w = p;
-    C = block_incl_scan(w, sm.red, &Z);
-  }
-  const double target = u * Z;
-  int first = (t < np && target < C) ? t : INT_MAX;
-  first = block_min_i(first, sm.red);
-  if (first == INT_MAX) first = block_max_i((t < np && w > 0.0) ? t : -1, sm.red);
-  if (first < 0) first = 0;
-  *Zout = Z;
-  return sm.q.pidx[first];
-}
 
 // Probability of token j in a row's kept set (0 outside it).
 template <int DT>
@@ -687,7 +661,7 @@ __device__ __forceinline__ double draw_weight(const char* pr, const char* qr, in
   return w;
 }
 
-template <int DT>
+template <int DT, int BS>
 __device__ int full_row_sample(const Args& a, double u, const char* pr, const char* qr, bool res, Smem& sm,
                                double* Zout) {
   const int t = threadIdx.x, V = a.V;
@@ -700,7 +674,7 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const ch
   for (int pass = 0; pass < 2; ++pass) {
     Z = 0.0;
     lastpos = -1;
-    for (int base = 0; base < V; base += SCE) {
+    for (int base = 0; base < V; base += BS * 8) {
       double ts = 0.0;
 #pragma unroll 1
       for (int e = 0; e < 8; ++e) {
@@ -711,26 +685,26 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const ch
           if (w > 0.0) lastpos = j;
         }
       }
-      Z += block_sum(ts, sm.red);
+      Z += block_sum<BS / 64>(ts, sm.red);
     }
-    lastpos = block_max_i(lastpos, sm.red);
+    lastpos = block_max_i<BS / 64>(lastpos, sm.red);
     if (!use_res || Z > 0.0) break;
     use_res = false;  // empty residual: draw from p
   }
   const double target = u * Z;
   double run = 0.0;
   int tok = -1;
-  for (int base = 0; base < V && tok < 0; base += SCE) {
+  for (int base = 0; base < V && tok < 0; base += BS * 8) {
     double ts = 0.0;
 #pragma unroll 1
     for (int e = 0; e < 8; ++e) {
       const int j = base + t * 8 + e;
       if (j < V) ts += draw_weight<DT>(pr, qr, j, dr, use_res, invT, sm.etab);
     }
-    const double tile = block_sum(ts, sm.red);
+    const double tile = block_sum<BS / 64>(ts, sm.red);
     if (run + tile > target) {
       double tot;
-      const double incl = block_incl_scan(ts, sm.red, &tot);
+      const double incl = block_incl_scan<BS / 64>(ts, sm.red, &tot);
       __syncthreads();
       sm.scan[t] = incl;
       __syncthreads();
@@ -748,8 +722,8 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const ch
           }
         }
       }
-      first = block_min_i(first, sm.red);
-      tok = first != INT_MAX ? first : block_max_i(lastp, sm.red);
+      first = block_min_i<BS / 64>(first, sm.red);
+      tok = first != INT_MAX ? first : block_max_i<BS / 64>(lastp, sm.red);
     }
     run += tile;
   }
@@ -769,129 +743,59 @@ __device__ __forceinline__ void set_draw_row(const RowRec* r, bool filtered, int
   __syncthreads();
 }
 
-template <int DT, int MODE>
-__device__ void seq_finalize(const Args& a, int b, Smem& sm) {
-  constexpr int ESZ = ElemT<DT>::ESZ;
-  const int t = threadIdx.x, K = a.K, rps = a.rps;
-  const RowRec* rr = a.row + (size_t)b * rps;
-  __syncthreads();
-  // one round trip: row records, drafted tokens and uniforms
-  if (t < rps) {
-    sm.q.px[t] = ld_dev(&rr[t].px);
-    sm.q.rf[t] = ld_dev(&rr[t].flags);
-    if (MODE == M_GREEDY) sm.q.arg[t] = ld_dev(&rr[t].arg);
-    else sm.q.nk[t] = ld_dev(&rr[t].nkept);
-  }
-  if (t < K) sm.q.x[t] = a.X[(size_t)b * K + t];
-  if (t <= K) sm.q.u[t] = a.U[(size_t)b * (K + 1) + t];
-  __syncthreads();
-  if (t == 0) {
-    int bad = 0;
-    for (int j = 0; j < rps; ++j) bad |= sm.q.rf[j] & RF_BAD;
-    for (int i = 0; i < K; ++i)
-      if (sm.q.x[i] < 0 || sm.q.x[i] >= a.V) bad = 1;
-    int n = K;
-    for (int i = 0; i < K; ++i) {
-      const double p = sm.q.px[i];
-      const bool acc = MODE == M_GREEDY ? p > 0.0 : (double)sm.q.u[i] * sm.q.px[K + 1 + i] < p;
-      if (!acc) {
-        n = i;
-        break;
-      }
-    }
-    sm.i0 = bad ? -1 : n;
-  }
-  __syncthreads();
-  const int n = sm.i0;
-  int32_t* ot = a.out_tok + (size_t)b * (K + 1);
-  if (a.out_p || a.out_q) {
-    const double nanv = __longlong_as_double(0x7FF8000000000000ll);
-    for (int i = t; i < K; i += WG) {
-      if (a.out_p) a.out_p[(size_t)b * K + i] = n < 0 ? nanv : sm.q.px[i];
-      if (a.out_q) a.out_q[(size_t)b * K + i] = (n < 0 || MODE == M_GREEDY) ? nanv : sm.q.px[K + 1 + i];
-    }
-  }
-  if (n < 0) {
-    for (int j = t; j <= K; j += WG) ot[j] = -1;
-    if (t == 0) {
-      a.out_n[b] = -1;
-      SeqRec s;
-      s.Z = 0.0;
-      s.n = -1;
-      s.flags = RF_BAD;
-      a.seq[b] = s;
-      if (a.out_z) a.out_z[b] = __longlong_as_double(0x7FF8000000000000ll);
-    }
-    return;
-  }
-  for (int j = t; j <= K; j += WG) {
-    if (j < n) ot[j] = sm.q.x[j];
-    else if (j > n) ot[j] = -1;
-  }
-  if (t == 0) a.out_n[b] = n;
-  if (MODE == M_PLAIN) {
-    if (t == 0) {
-      SeqRec s;
-      s.Z = 0.0;
-      s.n = n;
-      s.flags = 0;
-      a.seq[b] = s;
-    }
-    return;  // the sampling kernel draws the last token
-  }
-  int tok;
-  double Z = 1.0;
-  if (MODE == M_GREEDY) {
-    tok = sm.q.arg[n];
-  } else {
-    const double u = (double)sm.q.u[K];
-    const bool res = n < K;
-    const int jq = res ? K + 1 + n : n;
-    const int rlP = b * rps + n, rlQ = b * rps + jq;
-    const int np = sm.q.nk[n], nq = sm.q.nk[jq];
-    if (np < 0 || (res && nq < 0)) {
-      set_draw_row(&rr[n], true, 0, sm);
-      set_draw_row(&rr[jq], true, 1, sm);
-      tok = full_row_sample<DT>(a, u, row_ptr(a, rlP, ESZ), row_ptr(a, rlQ, ESZ), res, sm, &Z);
-    } else {
-      tok = list_sample(a, u, rlP, np, rlQ, nq, res, sm, &Z);
-    }
-  }
-  if (t == 0) {
-    ot[n] = tok;
-    if (a.out_z) a.out_z[b] = Z;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // kernels
 // ---------------------------------------------------------------------------
 
-// Append every logit of this thread at or above thr to its wave's candidate
-// list wl (entries ord_key << 32 | index, slots past CAND_CAP dropped) and
-// return the wave's count.  Compaction by ballot: a register slot costs one
-// compare and a scalar branch unless some lane of the wave qualifies.  Called
-// with every lane of the wave active.
+// Candidate units: the filter candidates are taken per unit of contiguous
+// logits, the 16 bytes of one vector load (8 bf16 or 4 f32 logits; one logit
+// on the element-load path).  A unit is a candidate when its max is at or
+// above the chunk's bound, so every logit at or above the bound lies in a
+// candidate unit; the row merge reads those units back and keeps their logits
+// at or above its own bound.  Register slots u*L .. u*L+L-1 hold unit u.
 template <int DT, bool VEC>
-__device__ __forceinline__ int wave_emit(const float (&v)[EPT], float tm, float thr, int c0, uint64_t* wl) {
+struct UnitT {
+  static constexpr int L = VEC ? ElemT<DT>::EPV : 1;  // logits per unit
+  static constexpr int N = EPT / L;                    // units per thread and chunk
+};
+
+// Append every unit of this thread whose max um[u] is at or above thr to its
+// wave's candidate list wl and return the wave's count.  Entries are (bits of
+// the unit max << 32 | index of its first logit); readers turn the bits into
+// an order key (cand_entry_key).  Slots from cap on are dropped.  gm[q] is the
+// max of register slots 8q .. 8q+7: a group with no lane of the wave at or
+// above thr costs one compare and one scalar branch.  In the others every
+// lane writes every unit without a branch: a qualifying one to its slot in
+// the list (mbcnt over the ballot), the others to the lane's own junk slot.
+// Called with every lane active.
+template <int DT, bool VEC>
+__device__ __forceinline__ int wave_emit(const float (&um)[UnitT<DT, VEC>::N], const float (&gm)[4], float thr,
+                                         int c0, uint64_t* wl, int cap, uint64_t* junk) {
+  constexpr int L = UnitT<DT, VEC>::L, UPG = 8 / L;  // units per group of 8 slots
   int wn = 0;
-  if (__ballot(tm >= thr) == 0ull) return 0;
+  const int lb = c0 + local_index<DT, VEC>(0, threadIdx.x);  // slot k's index is lb + local_index(k, 0)
+  uint64_t* jl = junk + (threadIdx.x & 63);
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    const bool pr = v[k] >= thr;
-    const unsigned long long bm = __ballot(pr);
-    if (bm != 0ull) {
-      if (pr) {
-        const int pos =
-            wn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-        if (pos < CAND_CAP)
-          wl[pos] = ((uint64_t)ord_key(v[k]) << 32) | (uint32_t)(c0 + local_index<DT, VEC>(k, threadIdx.x));
-      }
+  for (int q = 0; q < 4; ++q) {
+    if (__ballot(gm[q] >= thr) == 0ull) continue;
+#pragma unroll
+    for (int i = 0; i < UPG; ++i) {
+      const int u = q * UPG + i;
+      const bool pr = um[u] >= thr;
+      const unsigned long long bm = __ballot(pr);
+      const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bm, (uint32_t)wn));
+      uint64_t* dst = (pr && pos < cap) ? wl + pos : jl;
+      *dst = ((uint64_t)__float_as_uint(um[u]) << 32) | (uint32_t)(lb + local_index<DT, VEC>(u * L, 0));
       wn += __popcll(bm);
     }
   }
   return wn;
 }
+
+// Max without the canonicalisation an IEEE maxnum needs (gfx950
+// v_maximum3_f32); logits are never NaN inside the defined input range.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // One chunk item: stream it and leave its record (max, sum, candidates).
 template <int DT, int MODE, bool VEC>
@@ -904,19 +808,37 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
   const int chunk_id = item;
   const char* rp = row_ptr(a, rl, ESZ);
   const int c0 = c * CE, cn = min(CE, a.V - c0);
+  // drafted token of this row (its logit is kept for the row merge when it
+  // falls in this chunk)
+  int xt = -1;
+  if (MODE != M_GREEDY && a.do_seq) {
+    const int b = rl / a.rps, jr = rl - b * a.rps;
+    const int ir = jr <= a.K ? jr : jr - a.K - 1;
+    if (ir < a.K) xt = a.X[(size_t)b * a.K + ir];
+  }
 
   float v[EPT];
   load_chunk<DT, VEC>(rp, c0, cn, v);
-  // maxima of 4 groups of 8 register slots, then of the thread
+  // maxima of the candidate units, of 4 groups of 8 register slots, and of
+  // the thread
+  constexpr int UL = UnitT<DT, VEC>::L, UN = UnitT<DT, VEC>::N;
+  float um[UN];
+#pragma unroll
+  for (int u = 0; u < UN; ++u) {
+    float x = v[u * UL];
+#pragma unroll
+    for (int e = 1; e < UL; ++e) x = fmax2(x, v[u * UL + e]);
+    um[u] = x;
+  }
   float gm[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    float x = v[8 * g];
+    float x = um[g * (8 / UL)];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) x = fmaxf(x, v[8 * g + e]);
+    for (int i = 1; i < 8 / UL; ++i) x = fmax2(x, um[g * (8 / UL) + i]);
     gm[g] = x;
   }
-  const float tm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
+  const float tm = fmax2(fmax2(gm[0], gm[1]), fmax2(gm[2], gm[3]));
   if (t == 0) sm.ncand = 0;
   const float mc = block_fmax(tm, sm.red);
 
@@ -969,6 +891,26 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
     rec.s = block_sum((double)acc, sm.red) * corr;
   }
 
+  if (xt >= c0 && xt < c0 + cn) {
+    const int li = xt - c0;
+    int owner, kx;
+    if (VEC) {
+      constexpr int EPV = ElemT<DT>::EPV;
+      owner = (li / EPV) % WG;
+      kx = (li / (EPV * WG)) * EPV + li % EPV;
+    } else {
+      owner = li % WG;
+      kx = li / WG;
+    }
+    if (t == owner) {
+      float val = v[0];
+#pragma unroll
+      for (int k = 1; k < EPT; ++k)
+        if (k == kx) val = v[k];
+      a.xlogit[rl] = val;
+    }
+  }
+
   if (MODE == M_GREEDY) {
     int best = INT_MAX;
 #pragma unroll
@@ -980,7 +922,7 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
 
   if (FILT) {
     const int w = t >> 6;
-    const int wn = wave_emit<DT, VEC>(v, tm, thr, c0, &sm.s.cand[w * CAND_CAP]);
+    const int wn = wave_emit<DT, VEC>(um, gm, thr, c0, &sm.s.cand[w * CAND_CAP], CAND_CAP, sm.s.junk[w]);
     if ((t & 63) == 0) sm.s.wn[w] = wn;
     __syncthreads();
     int nc = (sm.s.wn[0] + sm.s.wn[1]) + (sm.s.wn[2] + sm.s.wn[3]);
@@ -990,24 +932,18 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
       for (int i = 0; i < w; ++i) off += sm.s.wn[i];
       for (int s = t & 63; s < wn; s += 64) st_dev(&dst[off + s], sm.s.cand[w * CAND_CAP + s]);
     } else {
-      // Too many: keep exactly the candidates above the (CAND_CAP+1)-th largest
-      // key (radix select over the registers) and raise the bound to match.
+      // Too many: keep exactly the units above the (CAND_CAP+1)-th largest
+      // unit max (radix select over the registers) and raise the bound to match.
       uint32_t prefix = 0, pmask = 0;
       int need = CAND_CAP + 1;
       for (int shift = 24; shift >= 0; shift -= 8) {
         __syncthreads();
         sm.s.hist[t] = 0u;
         __syncthreads();
-        for (int g = 0; g < 4; ++g) {
-          if (gm[g] >= thr) {
-            float wv[8];
-            load_group<DT, VEC>(rp, c0, cn, g, wv);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t key = ord_key(wv[e]);
-              if (wv[e] >= thr && (key & pmask) == prefix) atomicAdd(&sm.s.hist[(key >> shift) & 255u], 1u);
-            }
-          }
+        for (int u = 0; u < UN; ++u) {
+          const uint32_t key = ord_key(um[u]);
+          if (um[u] >= thr && (key & pmask) == prefix) atomicAdd(&sm.s.hist[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
         if (t == 0) {
@@ -1026,20 +962,13 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
         pmask |= 255u << shift;
         need = sm.i1;
       }
-      bound = prefix + 1u;  // every candidate with key >= bound fits
-      for (int g = 0; g < 4; ++g) {
-        if (gm[g] >= thr) {
-          float wv[8];
-          load_group<DT, VEC>(rp, c0, cn, g, wv);
+      bound = prefix + 1u;  // every unit with max key >= bound fits
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t key = ord_key(wv[e]);
-            if (wv[e] >= thr && key >= bound) {
-              const int s2 = atomicAdd(&sm.ncand, 1);
-              if (s2 < CAND_CAP)
-                sm.s.cand[s2] = ((uint64_t)key << 32) | (uint32_t)(c0 + local_index<DT, VEC>(8 * g + e, t));
-            }
-          }
+      for (int u = 0; u < UN; ++u) {
+        if (um[u] >= thr && ord_key(um[u]) >= bound) {
+          const int s2 = atomicAdd(&sm.ncand, 1);
+          if (s2 < CAND_CAP)
+            sm.s.cand[s2] = ((uint64_t)__float_as_uint(um[u]) << 32) | (uint32_t)(c0 + local_index<DT, VEC>(u * UL, t));
         }
       }
       __syncthreads();
@@ -1066,24 +995,690 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
 // merge runs in the next launch, when HBM is no longer saturated and its few
 // dependent round trips are short.
 template <int DT, int MODE, bool VEC>
-__global__ void __launch_bounds__(WG, STREAM_WG_PER_CU) stream_kernel(Args a) {
+__global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, VEC>())) stream_kernel(Args a) {
   __shared__ Smem sm;
   stream_item<DT, MODE, VEC>(a, (int)blockIdx.x, sm);
 }
 
-// One workgroup per row: merge the chunk records into the row's max,
-// normaliser, filter threshold, kept list and the probability of its drafted
-// token; the last row of a sequence to finish runs the accept tests, the
-// first-rejection scan and (filtered and greedy rows) the final draw.
+// ---------------------------------------------------------------------------
+// row kernel: wave-level row merge, then the sequence's accept tests and draw
+// ---------------------------------------------------------------------------
+
+// Orders LDS accesses of the lanes of one wave (the wave's LDS operations
+// execute in order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T>
+__device__ __forceinline__ T lane_bcast(T v, int lane) {
+  return __shfl(v, lane);
+}
+
+constexpr int WR_EPL = KEEP_CAP / 64;  // candidate entries per lane in a wave merge
+constexpr int WR_LOADS = 16;           // candidate loads per lane in one round trip
+constexpr int WR_ITER = 32;            // distinct keys the descending walk takes before the radix search
+
+struct WaveRowSm {
+  union {
+    uint64_t keys[KEEP_CAP];       // candidates at or above lo (ord_key << 32 | index)
+    unsigned long long hist[256];  // radix-select bins
+    int32_t kept[KEEP_CAP];        // kept indices (for their ascending order)
+  };
+  int32_t off[MAX_CHUNKS + 1];     // candidate offsets of the row's chunks
+};
+struct WaveList {  // kept list of a row: ascending index, filtered probability
+  int32_t idx[KEEP_CAP];
+  double prob[KEEP_CAP];
+};
+
+// Largest key t among the wave's entries (key ek, weight wt; weight 0 = no
+// entry) whose weight at or above t, F(t), reaches target: the cut of a
+// top-k set (weights 1) or a top-p set (weights the probability in fixed
+// point).  F is non-increasing in t, so the result is the key of an entry.
+// Returns 0 when the total weight is below target.  Radix search over the
+// key, 8 bits per pass, bins in LDS.
+__device__ __forceinline__ uint32_t wave_radix(const uint32_t (&ek)[WR_EPL], const unsigned long long (&wt)[WR_EPL],
+                               unsigned long long target, unsigned long long* hist) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long tot = 0;
+#pragma unroll
+  for (int r = 0; r < WR_EPL; ++r) tot += wt[r];
+  tot = lane63(wave_scan_u64(tot));
+  if (tot < target) return 0u;
+  uint32_t prefix = 0, pmask = 0;
+  unsigned long long above = 0;  // F of everything in higher bins at the levels fixed so far
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    wave_sync();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0ull;
+    wave_sync();
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r)
+      if (wt[r] != 0ull && (ek[r] & pmask) == prefix) atomicAdd(&hist[(ek[r] >> shift) & 255u], wt[r]);
+    wave_sync();
+    // lane L holds digits 255 - 4L - q (descending digit order across the wave)
+    unsigned long long h[4], ls = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h[q] = hist[255 - 4 * lane - q];
+      ls += h[q];
+    }
+    const unsigned long long ex = above + wave_scan_u64(ls) - ls;
+    const bool cross = ex < target && ex + ls >= target;
+    const unsigned long long bm = __ballot(cross);
+    const int src = bm ? __ffsll((unsigned long long)bm) - 1 : 63;
+    int d = 0;
+    unsigned long long na = ex;
+    if (cross) {
+      unsigned long long c = ex;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (c + h[q] >= target) {
+          d = 255 - 4 * lane - q;
+          na = c;
+          break;
+        }
+        c += h[q];
+      }
+    }
+    d = lane_bcast(d, src);
+    na = lane_bcast(na, src);
+    prefix |= (uint32_t)d << shift;
+    pmask |= 255u << shift;
+    above = na;
+  }
+  return prefix;
+}
+
+// Descending walk over the distinct keys of the wave's entries: returns the
+// first key at which the running mass reaches target (mass of a key = its
+// number of entries times ew / snorm), 0 when the entries run out first, or 1
+// (not the key of any finite logit) when WR_ITER keys were not enough; the
+// caller then uses the radix search.
+__device__ __forceinline__ uint32_t wave_walk(const uint32_t (&ek)[WR_EPL], const double (&ew)[WR_EPL], double snorm,
+                              double target) {
+  double run = 0.0;
+  uint32_t hi = 0xFFFFFFFFu;
+  for (int it = 0; it < WR_ITER; ++it) {
+    uint32_t lm = 0;
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r)
+      if (ek[r] < hi && ek[r] > lm) lm = ek[r];
+    const uint32_t km = dpp_wave_umax(lm);
+    if (km == 0u) return 0u;
+    int cnt = 0;
+    double wk = 0.0;
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r) {
+      const unsigned long long bm = __ballot(ek[r] == km);
+      cnt += __popcll(bm);
+      if (bm != 0ull && wk == 0.0) {
+        const int src = __ffsll(bm) - 1;
+        const uint64_t u = (uint64_t)__double_as_longlong(ew[r]);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+        wk = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+      }
+    }
+    run += (double)cnt * (wk / snorm);
+    if (run >= target) return km;
+    hi = km;
+  }
+  return 1u;
+}
+
+// Merge of one row by one wave: max, normaliser, filter threshold, kept list
+// (ascending index, into `list`, and into the scratch lists when to_global)
+// and the probability of the drafted token.  Returns false, having written
+// nothing, when the candidate lists cannot decide the threshold this way (the
+// block-level merge then takes the row).
 template <int DT, int MODE>
-__global__ void __launch_bounds__(WG) row_kernel(Args a) {
-  __shared__ Smem sm;
-  const int rl = (int)blockIdx.x;
-  const int b = rl / a.rps, jr = rl - b * a.rps;
-  const int ir = jr <= a.K ? jr : jr - a.K - 1;
-  const int xtok = (a.do_seq && ir < a.K) ? a.X[(size_t)b * a.K + ir] : -1;
-  row_finalize<DT, MODE>(a, rl, xtok, sm);
-  if (a.do_seq && last_arrival(&a.seq_cnt[b], (uint32_t)a.rps, &sm.flag)) seq_finalize<DT, MODE>(a, b, sm);
+__device__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, WaveList& list, bool to_global,
+                         RowRec& rr) {
+  constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
+  const int lane = threadIdx.x & 63, nch = a.nchunks;
+  const ChunkRec* cr = a.chunk + (size_t)rl * nch;
+  const bool hx = xtok >= 0 && xtok < a.V;
+  const double invT = a.invT;
+
+  // one round trip: the chunk records (chunk lane + 64 i) and the drafted
+  // token's logit, which the streaming pass stored
+  float cm[4];
+  double cs[4];
+  uint32_t cb[4];
+  int cn[4], carg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + 64 * i;
+    cm[i] = -INFINITY;
+    cs[i] = 0.0;
+    cb[i] = 0u;
+    cn[i] = 0;
+    carg[i] = INT_MAX;
+    if (c < nch) {
+      cm[i] = cr[c].m;
+      if (MODE == M_PLAIN || MODE == M_TOPP) cs[i] = cr[c].s;
+      if (FILT) {
+        cb[i] = cr[c].bound;
+        cn[i] = min(cr[c].ncand, CAND_CAP);
+      }
+      if (MODE == M_GREEDY) carg[i] = cr[c].arg;
+    }
+  }
+  const float lx = (MODE != M_GREEDY && hx) ? a.xlogit[rl] : -INFINITY;
+
+  const float m = dpp_wave_fmax(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])));
+  rr.S = 0.0;
+  rr.S_kept = 0.0;
+  rr.px = 0.0;
+  rr.m = m;
+  rr.tau = 0u;
+  rr.nkept = 0;
+  rr.flags = 0;
+  rr.arg = 0;
+  rr.pad = 0;
+  bool bad = !(m > -INFINITY && m < INFINITY);
+  if (MODE == M_PLAIN || MODE == M_TOPP) {
+    double sl = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (cm[i] > -INFINITY) sl += cs[i] * exp(((double)cm[i] - (double)m) * invT);
+    const double S = dpp_wave_sum(sl);
+    rr.S = S;
+    if (!(S > 0.0 && S < INFINITY)) bad = true;
+  }
+  if (MODE == M_GREEDY) {
+    int best = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (cm[i] == m) best = min(best, carg[i]);
+    best = wave_min(best);
+    rr.arg = best == INT_MAX ? 0 : best;
+  }
+
+  if (FILT && !bad) {
+    // every finite logit with key >= lo is a candidate of its chunk; a chunk
+    // whose max lies below lo holds none of them
+    uint32_t lo = dpp_wave_umax(max(max(cb[0], cb[1]), max(cb[2], cb[3])));
+    if (MODE == M_TOPP) lo = max(lo, ord_key(m - a.win));
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (64 * i < nch) {
+        const int ce = (cn[i] > 0 && ord_key(cm[i]) >= lo) ? cn[i] : 0;
+        const int inc = (int)wave_scan_u32((uint32_t)ce);
+        const int c = lane + 64 * i;
+        if (c < nch) ws.off[c] = run + inc - ce;
+        run += lane63(inc);
+      }
+    }
+    const int total = run;
+    if (total > ROW_LOAD_MAX) return false;
+    if (lane == 0) ws.off[nch] = total;
+    wave_sync();
+    const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
+    const int top = nch > 1 ? 1 << (31 - __clz(nch - 1)) : 0;  // largest power of two below nch
+    int n = 0;
+    for (int base = 0; base < total; base += 64 * WR_LOADS) {
+      // chunk of each entry: the last chunk whose offset is <= the entry
+      int ch[WR_LOADS];
+#pragma unroll
+      for (int j = 0; j < WR_LOADS; ++j) ch[j] = 0;
+      for (int step = top; step > 0; step >>= 1) {
+        // branch-free, so that the LDS reads of all entries are in flight
+        // together (off[nch] = total is above every entry)
+        int o[WR_LOADS];
+#pragma unroll
+        for (int j = 0; j < WR_LOADS; ++j) o[j] = ws.off[min(ch[j] + step, nch)];
+#pragma unroll
+        for (int j = 0; j < WR_LOADS; ++j) ch[j] = o[j] <= base + lane + 64 * j ? min(ch[j] + step, nch) : ch[j];
+      }
+      uint64_t ck[WR_LOADS];
+#pragma unroll
+      for (int j = 0; j < WR_LOADS; ++j) {
+        const int e = base + lane + 64 * j;
+        ck[j] = e < total ? cand_entry_key(cand[(size_t)ch[j] * CAND_CAP + (e - ws.off[ch[j]])]) : 0ull;
+      }
+      wave_sync();
+#pragma unroll
+      for (int j = 0; j < WR_LOADS; ++j) {
+        const bool pr = ck[j] != 0ull && (uint32_t)(ck[j] >> 32) >= lo;
+        const unsigned long long bm = __ballot(pr);
+        if (pr) {
+          const int pos =
+              n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+          if (pos < KEEP_CAP) ws.keys[pos] = ck[j];
+        }
+        n += __popcll(bm);
+      }
+      wave_sync();
+    }
+    if (n > KEEP_CAP) return false;
+    if (a.ulen > 1) {
+      // read the candidate units back: their logits at or above lo are the
+      // candidates (one 16-byte load per unit, all in flight together)
+      constexpr int UL = 16 / ElemT<DT>::ESZ;
+      const char* rp = row_ptr(a, rl, ElemT<DT>::ESZ);
+      uint4 raw[WR_EPL];
+      int st[WR_EPL];
+#pragma unroll
+      for (int r = 0; r < WR_EPL; ++r) {
+        const int e = lane + 64 * r;
+        st[r] = -1;
+        raw[r] = make_uint4(0u, 0u, 0u, 0u);
+        if (e < n) {
+          st[r] = (int)(uint32_t)ws.keys[e];
+          raw[r] = *reinterpret_cast<const uint4*>(rp + (size_t)st[r] * ElemT<DT>::ESZ);
+        }
+      }
+      wave_sync();
+      int ne = 0;
+#pragma unroll
+      for (int r = 0; r < WR_EPL; ++r) {
+#pragma unroll
+        for (int i = 0; i < UL; ++i) {
+          const float x = unit_elem<DT>(raw[r], i);
+          const uint32_t key = ord_key(x);
+          const bool pr = st[r] >= 0 && key >= lo && x > -INFINITY;
+          const unsigned long long bm = __ballot(pr);
+          const int pos = ne + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+          if (pr && pos < KEEP_CAP) ws.keys[pos] = ((uint64_t)key << 32) | (uint32_t)(st[r] + i);
+          ne += __popcll(bm);
+        }
+      }
+      if (ne > KEEP_CAP) return false;
+      n = ne;
+      wave_sync();
+    }
+    uint32_t ek[WR_EPL];
+    int ei[WR_EPL];
+    double ew[WR_EPL];  // exp((x - m) / T)
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r) {
+      const int e = lane + 64 * r;
+      const uint64_t v = e < n ? ws.keys[e] : 0ull;
+      ek[r] = (uint32_t)(v >> 32);
+      ei[r] = (int)(uint32_t)v;
+      ew[r] = e < n ? exp(((double)key_val(ek[r]) - (double)m) * invT) : 0.0;
+    }
+    wave_sync();
+    unsigned long long wt[WR_EPL];
+    uint32_t tau = lo;
+    double snorm = rr.S;  // top-p normaliser
+    if (MODE == M_TOPK || MODE == M_TOPKP) {
+      // k-th largest key among the candidates, ties kept
+#pragma unroll
+      for (int r = 0; r < WR_EPL; ++r) wt[r] = ek[r] != 0u ? 1ull : 0ull;
+      const uint32_t tk = wave_radix(ek, wt, (unsigned long long)a.top_k, ws.hist);
+      if (tk == 0u) {
+        // fewer than k candidates: with every bound at -inf the row has fewer
+        // than k finite logits and all are kept; otherwise undecided here
+        if (lo > KEY_NEG_INF) return false;
+        tau = KEY_NEG_INF;
+      } else {
+        tau = tk;
+      }
+      if (MODE == M_TOPKP) {
+        double sk = 0.0;
+#pragma unroll
+        for (int r = 0; r < WR_EPL; ++r)
+          if (ek[r] != 0u && ek[r] >= tau) sk += ew[r];
+        snorm = dpp_wave_sum(sk);
+      }
+    }
+    if (MODE == M_TOPP || MODE == M_TOPKP) {
+      // smallest descending prefix whose mass reaches top_p, ties included
+      uint32_t ekp[WR_EPL];
+#pragma unroll
+      for (int r = 0; r < WR_EPL; ++r) ekp[r] = ek[r] >= tau ? ek[r] : 0u;
+      uint32_t tp = wave_walk(ekp, ew, snorm, a.top_p);
+      if (tp == 1u) {
+#pragma unroll
+        for (int r = 0; r < WR_EPL; ++r)
+          wt[r] = ekp[r] != 0u ? (unsigned long long)(ew[r] / snorm * MASS_SCALE) : 0ull;
+        tp = wave_radix(ekp, wt, (unsigned long long)(a.top_p * MASS_SCALE), ws.hist);
+      }
+      if (tp == 0u) {
+        if (MODE == M_TOPP) return false;  // the nucleus reaches below the candidate window
+        // top-k then top-p: round-off kept the top-k mass just below top_p; keep the top-k set
+      } else {
+        tau = max(tau, tp);
+      }
+    }
+    // kept set: candidates at or above tau
+    int nk = 0;
+    double skl = 0.0;
+    bool kp[WR_EPL];
+    wave_sync();
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r) {
+      kp[r] = ek[r] != 0u && ek[r] >= tau;
+      if (kp[r]) skl += ew[r];
+      const unsigned long long bm = __ballot(kp[r]);
+      if (kp[r]) {
+        const int pos =
+            nk + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+        ws.kept[pos] = ei[r];
+      }
+      nk += __popcll(bm);
+    }
+    const double skept = dpp_wave_sum(skl);
+    wave_sync();
+    // position in ascending index order = number of kept indices below it
+    int pos[WR_EPL];
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r) pos[r] = 0;
+    for (int j = 0; j < nk; ++j) {
+      const int kj = ws.kept[j];
+#pragma unroll
+      for (int r = 0; r < WR_EPL; ++r) pos[r] += kj < ei[r] ? 1 : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r) {
+      if (kp[r]) {
+        const double pr = ew[r] / skept;
+        list.idx[pos[r]] = ei[r];
+        list.prob[pos[r]] = pr;
+        if (to_global) {
+          a.kidx[(size_t)rl * KEEP_CAP + pos[r]] = ei[r];
+          a.kprob[(size_t)rl * KEEP_CAP + pos[r]] = pr;
+        }
+      }
+    }
+    rr.tau = tau;
+    rr.S_kept = skept;
+    rr.nkept = nk;
+  }
+  if (!bad && hx) {
+    if (MODE == M_GREEDY) {
+      rr.px = xtok == rr.arg ? 1.0 : 0.0;
+    } else if (ord_key(lx) >= rr.tau) {
+      rr.px = exp(((double)lx - (double)m) * invT) / (MODE == M_PLAIN ? rr.S : rr.S_kept);
+    }
+  }
+  if (bad) rr.flags |= RF_BAD;
+  if (lane == 0) a.row[rl] = rr;
+  return true;
+}
+
+struct RowKSm {
+  union {
+    WaveRowSm w[ROW_NW];
+    Smem blk;  // block-level merge, list copies and full-row draw
+  };
+  WaveList list[ROW_NW];  // kept list of each wave's last row
+  double px[MAX_RPS];     // p or q of each row's drafted token
+  double sk[MAX_RPS];     // normaliser of the kept set
+  float rm[MAX_RPS];      // row max
+  uint32_t rtau[MAX_RPS];
+  int32_t rf[MAX_RPS];
+  int32_t nk[MAX_RPS];
+  int32_t arg[MAX_RPS];
+  int32_t lsrc[MAX_RPS];  // wave whose list holds the row's kept list, -1: the scratch lists
+  int32_t slow[MAX_RPS];
+  int32_t x[MAX_K];
+  float u[MAX_K + 1];
+  int32_t nslow;
+  int32_t big;  // the sequence's last token needs the full-row draw
+  int32_t n;
+};
+
+// Final draw from kept lists by one wave (filtered rows): residual
+// max(0, p - q) over the target's kept tokens, or p itself (bonus, or an
+// empty residual); inverse CDF in ascending vocabulary order.
+__device__ int wave_list_sample(double u, const int32_t* pidx, const double* pprob, int np, const int32_t* qidx,
+                                const double* qprob, int nq, bool res, double* Zout) {
+  const int lane = threadIdx.x & 63;
+  // entries WR_EPL * lane + r: each lane a contiguous run
+  int pi[WR_EPL];
+  double pp[WR_EPL], w[WR_EPL];
+#pragma unroll
+  for (int r = 0; r < WR_EPL; ++r) {
+    const int e = WR_EPL * lane + r;
+    pi[r] = e < np ? pidx[e] : 0;
+    pp[r] = e < np ? pprob[e] : 0.0;
+    w[r] = pp[r];
+  }
+  if (res) {
+    // position of each target token among the draft's kept indices: the
+    // number of draft indices below it (branch-free search, all entries'
+    // LDS reads in flight together)
+    int ps[WR_EPL];
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r) ps[r] = 0;
+    for (int step = KEEP_CAP; step > 0; step >>= 1) {
+      int q[WR_EPL];
+#pragma unroll
+      for (int r = 0; r < WR_EPL; ++r) q[r] = qidx[max(min(ps[r] + step, nq) - 1, 0)];
+#pragma unroll
+      for (int r = 0; r < WR_EPL; ++r) ps[r] += (ps[r] + step <= nq && q[r] < pi[r]) ? step : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r) {
+      if (WR_EPL * lane + r < np) {
+        const double qv = (ps[r] < nq && qidx[ps[r]] == pi[r]) ? qprob[ps[r]] : 0.0;
+        const double d = pp[r] - qv;
+        w[r] = d > 0.0 ? d : 0.0;
+      }
+    }
+  }
+  double ls = 0.0;
+#pragma unroll
+  for (int r = 0; r < WR_EPL; ++r) ls += w[r];
+  double inc = wave_scan_f64(ls);
+  double Z = lane63(inc);
+  if (res && !(Z > 0.0)) {  // empty residual: draw from p
+    ls = 0.0;
+#pragma unroll
+    for (int r = 0; r < WR_EPL; ++r) {
+      w[r] = pp[r];
+      ls += w[r];
+    }
+    inc = wave_scan_f64(ls);
+    Z = lane63(inc);
+  }
+  const double target = u * Z;
+  double C = inc - ls;
+  int first = INT_MAX, lastp = -1, tf = 0, tl = 0;
+#pragma unroll
+  for (int r = 0; r < WR_EPL; ++r) {
+    const int e = WR_EPL * lane + r;
+    C += w[r];
+    if (e < np && w[r] > 0.0) {
+      lastp = e;
+      tl = pi[r];
+      if (first == INT_MAX && target < C) {
+        first = e;
+        tf = pi[r];
+      }
+    }
+  }
+  const unsigned long long fm = __ballot(first != INT_MAX);
+  int tok;
+  if (fm) {
+    tok = lane_bcast(tf, __ffsll(fm) - 1);
+  } else {
+    const unsigned long long lm = __ballot(lastp >= 0);
+    tok = lm ? lane_bcast(tl, 63 - __clzll(lm)) : 0;
+  }
+  *Zout = Z;
+  return tok;
+}
+
+// One workgroup per sequence, one wave per row (rows w, w + 16, ...): every
+// row of the sequence is merged in parallel; rows the wave-level merge cannot
+// decide are merged by the whole block afterwards; then wave 0 runs the accept
+// tests, the first-rejection scan and the final draw from the kept lists (the
+// whole block draws from full rows when a kept set is too large for a list).
+// With do_seq == 0 (filtered probabilities) only the merges run.
+template <int DT, int MODE>
+__global__ void __launch_bounds__(ROW_WG) row_kernel(Args a) {
+  __shared__ RowKSm sm;
+  constexpr int ESZ = ElemT<DT>::ESZ;
+  constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int b = (int)blockIdx.x, K = a.K, rps = a.rps;
+  const bool lds_lists = rps <= ROW_NW;  // otherwise a wave merges several rows and the lists go to scratch
+  if (a.do_seq && w == 0) {
+    if (lane < K) sm.x[lane] = a.X[(size_t)b * K + lane];
+    for (int j = lane; j <= K; j += 64) sm.u[j] = a.U[(size_t)b * (K + 1) + j];
+  }
+  if (t == 0) sm.nslow = 0;
+  __syncthreads();
+  for (int jr = w; jr < rps; jr += ROW_NW) {
+    const int rl = b * rps + jr;
+    const int ir = jr <= K ? jr : jr - K - 1;
+    const int xtok = (a.do_seq && ir < K) ? a.X[(size_t)b * K + ir] : -1;
+    RowRec rr;
+    if (wave_row<DT, MODE>(a, rl, xtok, sm.w[w], sm.list[w], !lds_lists, rr)) {
+      if (lane == 0) {
+        sm.px[jr] = rr.px;
+        sm.sk[jr] = rr.S_kept;
+        sm.rm[jr] = rr.m;
+        sm.rtau[jr] = rr.tau;
+        sm.rf[jr] = rr.flags;
+        sm.nk[jr] = rr.nkept;
+        sm.arg[jr] = rr.arg;
+        sm.lsrc[jr] = lds_lists ? w : -1;
+      }
+    } else if (lane == 0) {
+      sm.slow[atomicAdd(&sm.nslow, 1)] = jr;
+    }
+  }
+  if (!lds_lists) __builtin_amdgcn_s_waitcnt(0);  // scratch lists are read back by wave 0
+  __syncthreads();
+  const int nslow = sm.nslow;
+  for (int s = 0; s < nslow; ++s) {
+    const int jr = sm.slow[s];
+    const int ir = jr <= K ? jr : jr - K - 1;
+    const int xtok = (a.do_seq && ir < K) ? sm.x[ir] : -1;
+    const RowRec rr = row_finalize<DT, MODE, ROW_WG>(a, b * rps + jr, xtok, sm.blk);
+    if (t == 0) {
+      sm.px[jr] = rr.px;
+      sm.sk[jr] = rr.S_kept;
+      sm.rm[jr] = rr.m;
+      sm.rtau[jr] = rr.tau;
+      sm.rf[jr] = rr.flags;
+      sm.nk[jr] = rr.nkept;
+      sm.arg[jr] = rr.arg;
+      sm.lsrc[jr] = -1;
+    }
+  }
+  if (!a.do_seq) return;
+  if (nslow > 0) __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (w == 0) {
+    // accept tests: draft i is accepted iff u_i * q_i(x_i) < p_i(x_i)
+    bool rej = false, badx = false;
+    if (lane < K) {
+      const double p = sm.px[lane];
+      rej = MODE == M_GREEDY ? !(p > 0.0) : !((double)sm.u[lane] * sm.px[K + 1 + lane] < p);
+      badx = sm.x[lane] < 0 || sm.x[lane] >= a.V;
+    }
+    bool badr = false;
+    for (int j = lane; j < rps; j += 64) badr |= (sm.rf[j] & RF_BAD) != 0;
+    const unsigned long long rm = __ballot(rej);
+    const bool bad = __ballot(badx || badr) != 0ull;
+    const int n = bad ? -1 : (rm ? __ffsll(rm) - 1 : K);
+    int32_t* ot = a.out_tok + (size_t)b * (K + 1);
+    const double nanv = __longlong_as_double(0x7FF8000000000000ll);
+    if (lane < K) {
+      if (a.out_p) a.out_p[(size_t)b * K + lane] = n < 0 ? nanv : sm.px[lane];
+      if (a.out_q) a.out_q[(size_t)b * K + lane] = (n < 0 || MODE == M_GREEDY) ? nanv : sm.px[K + 1 + lane];
+    }
+    for (int j = lane; j <= K; j += 64) {
+      if (n < 0 || j > n) ot[j] = -1;
+      else if (j < n) ot[j] = sm.x[j];
+    }
+    int big = 0;
+    if (lane == 0) {
+      a.out_n[b] = n;
+      SeqRec sr;
+      sr.Z = 0.0;
+      sr.n = n;
+      sr.flags = n < 0 ? RF_BAD : 0;
+      a.seq[b] = sr;
+      if (n < 0 && a.out_z) a.out_z[b] = nanv;
+      if (n >= 0 && MODE == M_GREEDY) {
+        ot[n] = sm.arg[n];
+        if (a.out_z) a.out_z[b] = 1.0;
+      }
+    }
+    if (FILT && n >= 0) {
+      const bool res = n < K;
+      const int jq = res ? K + 1 + n : n;
+      const int np = sm.nk[n], nq = sm.nk[jq];
+      if (np < 0 || (res && nq < 0)) {
+        big = 1;
+      } else {
+        // the two kept lists, from LDS or from the scratch lists
+        const int32_t* pidx;
+        const double* pprob;
+        const int32_t* qidx;
+        const double* qprob;
+        if (sm.lsrc[n] >= 0) {
+          pidx = sm.list[sm.lsrc[n]].idx;
+          pprob = sm.list[sm.lsrc[n]].prob;
+        } else {
+          const size_t o = (size_t)(b * rps + n) * KEEP_CAP;
+          for (int e = lane; e < np; e += 64) {
+            sm.blk.q.pidx[e] = ld_dev(&a.kidx[o + e]);
+            sm.blk.q.pprob[e] = ld_dev(&a.kprob[o + e]);
+          }
+          pidx = sm.blk.q.pidx;
+          pprob = sm.blk.q.pprob;
+        }
+        if (!res || sm.lsrc[jq] >= 0) {
+          qidx = sm.list[res ? sm.lsrc[jq] : 0].idx;
+          qprob = sm.list[res ? sm.lsrc[jq] : 0].prob;
+        } else {
+          const size_t o = (size_t)(b * rps + jq) * KEEP_CAP;
+          for (int e = lane; e < nq; e += 64) {
+            sm.blk.q.qidx[e] = ld_dev(&a.kidx[o + e]);
+            sm.blk.q.qprob[e] = ld_dev(&a.kprob[o + e]);
+          }
+          qidx = sm.blk.q.qidx;
+          qprob = sm.blk.q.qprob;
+        }
+        wave_sync();
+        double Z;
+        const int tok = wave_list_sample((double)sm.u[K], pidx, pprob, np, qidx, qprob, nq, res, &Z);
+        if (lane == 0) {
+          ot[n] = tok;
+          if (a.out_z) a.out_z[b] = Z;
+        }
+      }
+    }
+    if (lane == 0) {
+      sm.big = big;
+      sm.n = n;
+    }
+  }
+  __syncthreads();
+  if (FILT && sm.big) {
+    // a kept set too large for a list: the whole block draws from the full rows
+    const int n = sm.n;
+    const bool res = n < K;
+    const int jq = res ? K + 1 + n : n;
+    if (t < 2) {
+      const int j = t == 0 ? n : jq;
+      sm.blk.dr[t].m = sm.rm[j];
+      sm.blk.dr[t].tau = sm.rtau[j];
+      sm.blk.dr[t].snorm = sm.sk[j];
+    }
+    __syncthreads();
+    double Z;
+    const int tok = full_row_sample<DT, ROW_WG>(a, (double)sm.u[K], row_ptr(a, b * rps + n, ESZ),
+                                                row_ptr(a, b * rps + jq, ESZ), res, sm.blk, &Z);
+    if (t == 0) {
+      a.out_tok[(size_t)b * (K + 1) + n] = tok;
+      if (a.out_z) a.out_z[b] = Z;
+    }
+  }
 }
 
 template <int DT>
@@ -1159,7 +1754,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   if (!(Z > 0.0)) {
     // empty residual (round-off only): draw from p
     set_draw_row(&a.row[rlP], false, 0, sm);
-    tok = full_row_sample<DT>(a, u, pr, qr, false, sm, &Z);
+    tok = full_row_sample<DT, WG>(a, u, pr, qr, false, sm, &Z);
   } else {
     const double target = u * Z;
     __syncthreads();
@@ -1278,7 +1873,7 @@ hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned 
 
 hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
   KFn f = dtype == D_BF16 ? pick_row<D_BF16>(mode) : pick_row<D_F32>(mode);
-  hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(ROW_WG), 0, s, a);
   return hipGetLastError();
 }
 
