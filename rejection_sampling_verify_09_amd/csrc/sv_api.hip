@@ -242,11 +242,11 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   hipStream_t s = (hipStream_t)stream;
   ProfSlot* prof = prof_begin();
   if (prof && hipEventRecord(prof->ev[0], s) != hipSuccess) return SV_ERR_HIP;
-  // chunk-parallel streaming pass, then one workgroup per sequence merges its
-  // rows and finishes it
+  // chunk-parallel streaming pass, then one workgroup per row merges it; the
+  // last row of each sequence finishes the sequence
   if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
   if (prof && hipEventRecord(prof->ev[1], s) != hipSuccess) return SV_ERR_HIP;
-  if (launch_row(a, dtype, mode, (unsigned)B, s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (mode == M_PLAIN) {
     if (launch_sample(a, dtype, (unsigned)((int64_t)B * nsc), s) != hipSuccess) return SV_ERR_HIP;
   }

@@ -24,8 +24,6 @@ constexpr int stream_wg_per_cu() { return (DT == 1 && VEC) ? 8 : 5; }
 constexpr int MAX_CHUNKS = WG;           // chunks per row (one chunk record per thread in a row merge)
 constexpr int64_t MAX_V = (int64_t)MAX_CHUNKS * CE;  // 2,097,152
 constexpr int MAX_RPS = 2 * MAX_K + 1;
-constexpr int ROW_WG = 1024;       // row kernel: one workgroup per sequence, one wave per row at a time
-constexpr int ROW_NW = ROW_WG / 64;
 // top-p candidates: every logit within this many units of z = logit / T below
 // the row maximum (the cut is verified against the mass at the row merge)
 constexpr float TOPP_WINDOW_Z = 8.0f;

@@ -103,7 +103,7 @@ struct Smem {
     SmemStream s;
     SmemRow r;
     SmemSeq q;
-    double scan[ROW_WG];
+    double scan[WG];
   };
   Red red;
   DrawRow dr[2];
@@ -1017,6 +1017,26 @@ __device__ __forceinline__ T lane_bcast(T v, int lane) {
   return __shfl(v, lane);
 }
 
+// Appends each lane's entries vals[i] with pred[i] to the wave's list
+// (lane-major order) after the n entries already there; entries from cap on
+// are dropped.  Returns the new count.  One prefix sum over the lanes' counts
+// instead of a ballot per entry, so the entries are independent work.
+template <int N>
+__device__ __forceinline__ int wave_append(const uint64_t (&vals)[N], const bool (&pred)[N], uint64_t* list, int n,
+                                           int cap) {
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) cnt += pred[i] ? 1u : 0u;
+  const uint32_t incl = wave_scan_u32(cnt);
+  int pos = n + (int)(incl - cnt);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (pred[i] && pos < cap) list[pos] = vals[i];
+    pos += pred[i] ? 1 : 0;
+  }
+  return n + (int)lane63(incl);
+}
+
 constexpr int WR_EPL = KEEP_CAP / 64;  // candidate entries per lane in a wave merge
 constexpr int WR_LOADS = 16;           // candidate loads per lane in one round trip
 constexpr int WR_ITER = 32;            // distinct keys the descending walk takes before the radix search
@@ -1028,10 +1048,6 @@ struct WaveRowSm {
     int32_t kept[KEEP_CAP];        // kept indices (for their ascending order)
   };
   int32_t off[MAX_CHUNKS + 1];     // candidate offsets of the row's chunks
-};
-struct WaveList {  // kept list of a row: ascending index, filtered probability
-  int32_t idx[KEEP_CAP];
-  double prob[KEEP_CAP];
 };
 
 // Largest key t among the wave's entries (key ek, weight wt; weight 0 = no
@@ -1131,13 +1147,12 @@ __device__ __forceinline__ uint32_t wave_walk(const uint32_t (&ek)[WR_EPL], cons
 }
 
 // Merge of one row by one wave: max, normaliser, filter threshold, kept list
-// (ascending index, into `list`, and into the scratch lists when to_global)
-// and the probability of the drafted token.  Returns false, having written
-// nothing, when the candidate lists cannot decide the threshold this way (the
-// block-level merge then takes the row).
+// (ascending index, into the scratch lists), the probability of the drafted
+// token, and the row record.  Returns false, having written nothing, when the
+// candidate lists cannot decide the threshold this way (the block-level merge
+// then takes the row).
 template <int DT, int MODE>
-__device__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, WaveList& list, bool to_global,
-                         RowRec& rr) {
+__device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, RowRec& rr) {
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int lane = threadIdx.x & 63, nch = a.nchunks;
   const ChunkRec* cr = a.chunk + (size_t)rl * nch;
@@ -1169,6 +1184,15 @@ __device__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, WaveLis
     }
   }
   const float lx = (MODE != M_GREEDY && hx) ? a.xlogit[rl] : -INFINITY;
+  // with them, speculatively, entry `lane` of the first SPECC chunks' lists
+  // (most lists are shorter than 64 units): one round trip for most rows
+  constexpr int SPECC = 16;
+  uint64_t spec[SPECC];
+  const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
+  if (FILT) {
+#pragma unroll
+    for (int i = 0; i < SPECC; ++i) spec[i] = i < nch ? cand[(size_t)i * CAND_CAP + lane] : 0ull;
+  }
 
   const float m = dpp_wave_fmax(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])));
   rr.S = 0.0;
@@ -1204,58 +1228,45 @@ __device__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, WaveLis
     // whose max lies below lo holds none of them
     uint32_t lo = dpp_wave_umax(max(max(cb[0], cb[1]), max(cb[2], cb[3])));
     if (MODE == M_TOPP) lo = max(lo, ord_key(m - a.win));
-    int run = 0;
+    // a chunk whose max lies below lo holds none of them
+    int ce4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (64 * i < nch) {
-        const int ce = (cn[i] > 0 && ord_key(cm[i]) >= lo) ? cn[i] : 0;
-        const int inc = (int)wave_scan_u32((uint32_t)ce);
-        const int c = lane + 64 * i;
-        if (c < nch) ws.off[c] = run + inc - ce;
-        run += lane63(inc);
-      }
-    }
-    const int total = run;
-    if (total > ROW_LOAD_MAX) return false;
-    if (lane == 0) ws.off[nch] = total;
-    wave_sync();
-    const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
-    const int top = nch > 1 ? 1 << (31 - __clz(nch - 1)) : 0;  // largest power of two below nch
+    for (int i = 0; i < 4; ++i) ce4[i] = (cn[i] > 0 && ord_key(cm[i]) >= lo) ? cn[i] : 0;
     int n = 0;
-    for (int base = 0; base < total; base += 64 * WR_LOADS) {
-      // chunk of each entry: the last chunk whose offset is <= the entry
-      int ch[WR_LOADS];
+    auto take = [&](uint64_t raw, bool valid) {
+      const uint64_t ent = valid ? cand_entry_key(raw) : 0ull;
+      const bool pr = valid && (uint32_t)(ent >> 32) >= lo;
+      const unsigned long long bm = __ballot(pr);
+      const int pos =
+          n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+      if (pr && pos < KEEP_CAP) ws.keys[pos] = ent;
+      n += __popcll(bm);
+    };
+    bool more = nch > SPECC;
+    {
+      uint64_t sv[SPECC];
+      bool sp[SPECC];
 #pragma unroll
-      for (int j = 0; j < WR_LOADS; ++j) ch[j] = 0;
-      for (int step = top; step > 0; step >>= 1) {
-        // branch-free, so that the LDS reads of all entries are in flight
-        // together (off[nch] = total is above every entry)
-        int o[WR_LOADS];
-#pragma unroll
-        for (int j = 0; j < WR_LOADS; ++j) o[j] = ws.off[min(ch[j] + step, nch)];
-#pragma unroll
-        for (int j = 0; j < WR_LOADS; ++j) ch[j] = o[j] <= base + lane + 64 * j ? min(ch[j] + step, nch) : ch[j];
+      for (int i = 0; i < SPECC; ++i) {
+        const int cei = i < nch ? __builtin_amdgcn_readlane(ce4[0], i) : 0;  // chunk i < 64 lives in lane i
+        more |= cei > 64;
+        sv[i] = cand_entry_key(spec[i]);
+        sp[i] = lane < cei && (uint32_t)(sv[i] >> 32) >= lo;
       }
-      uint64_t ck[WR_LOADS];
-#pragma unroll
-      for (int j = 0; j < WR_LOADS; ++j) {
-        const int e = base + lane + 64 * j;
-        ck[j] = e < total ? cand_entry_key(cand[(size_t)ch[j] * CAND_CAP + (e - ws.off[ch[j]])]) : 0ull;
-      }
-      wave_sync();
-#pragma unroll
-      for (int j = 0; j < WR_LOADS; ++j) {
-        const bool pr = ck[j] != 0ull && (uint32_t)(ck[j] >> 32) >= lo;
-        const unsigned long long bm = __ballot(pr);
-        if (pr) {
-          const int pos =
-              n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-          if (pos < KEEP_CAP) ws.keys[pos] = ck[j];
-        }
-        n += __popcll(bm);
-      }
-      wave_sync();
+      n = wave_append(sv, sp, ws.keys, n, KEEP_CAP);
     }
+    if (more) {
+      // the rest: chunks past the speculated ones, entries past the first 64
+      for (int c = 0; c < nch; ++c) {
+        const int cv = c < 64 ? ce4[0] : c < 128 ? ce4[1] : c < 192 ? ce4[2] : ce4[3];
+        const int cec = __builtin_amdgcn_readlane(cv, c & 63);
+        for (int e0 = c < SPECC ? 64 : 0; e0 < cec; e0 += 64) {
+          const int e = e0 + lane;
+          take(e < cec ? cand[(size_t)c * CAND_CAP + e] : 0ull, e < cec);
+        }
+      }
+    }
+    wave_sync();
     if (n > KEEP_CAP) return false;
     if (a.ulen > 1) {
       // read the candidate units back: their logits at or above lo are the
@@ -1275,21 +1286,19 @@ __device__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, WaveLis
         }
       }
       wave_sync();
-      int ne = 0;
+      uint64_t xv[WR_EPL * UL];
+      bool xp[WR_EPL * UL];
 #pragma unroll
       for (int r = 0; r < WR_EPL; ++r) {
 #pragma unroll
         for (int i = 0; i < UL; ++i) {
           const float x = unit_elem<DT>(raw[r], i);
           const uint32_t key = ord_key(x);
-          const bool pr = st[r] >= 0 && key >= lo && x > -INFINITY;
-          const unsigned long long bm = __ballot(pr);
-          const int pos = ne + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-          if (pr && pos < KEEP_CAP) ws.keys[pos] = ((uint64_t)key << 32) | (uint32_t)(st[r] + i);
-          ne += __popcll(bm);
+          xp[r * UL + i] = st[r] >= 0 && key >= lo && x > -INFINITY;
+          xv[r * UL + i] = ((uint64_t)key << 32) | (uint32_t)(st[r] + i);
         }
       }
+      const int ne = wave_append(xv, xp, ws.keys, 0, KEEP_CAP);
       if (ne > KEEP_CAP) return false;
       n = ne;
       wave_sync();
@@ -1380,13 +1389,8 @@ __device__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, WaveLis
 #pragma unroll
     for (int r = 0; r < WR_EPL; ++r) {
       if (kp[r]) {
-        const double pr = ew[r] / skept;
-        list.idx[pos[r]] = ei[r];
-        list.prob[pos[r]] = pr;
-        if (to_global) {
-          a.kidx[(size_t)rl * KEEP_CAP + pos[r]] = ei[r];
-          a.kprob[(size_t)rl * KEEP_CAP + pos[r]] = pr;
-        }
+        st_dev(&a.kidx[(size_t)rl * KEEP_CAP + pos[r]], ei[r]);
+        st_dev(&a.kprob[(size_t)rl * KEEP_CAP + pos[r]], ew[r] / skept);
       }
     }
     rr.tau = tau;
@@ -1401,30 +1405,22 @@ __device__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, WaveLis
     }
   }
   if (bad) rr.flags |= RF_BAD;
-  if (lane == 0) a.row[rl] = rr;
+  if (lane == 0) store_row(&a.row[rl], rr);
   return true;
 }
 
 struct RowKSm {
   union {
-    WaveRowSm w[ROW_NW];
-    Smem blk;  // block-level merge, list copies and full-row draw
+    WaveRowSm w;  // wave-level merge
+    Smem blk;     // block-level merge, list copies and full-row draw
   };
-  WaveList list[ROW_NW];  // kept list of each wave's last row
-  double px[MAX_RPS];     // p or q of each row's drafted token
-  double sk[MAX_RPS];     // normaliser of the kept set
-  float rm[MAX_RPS];      // row max
-  uint32_t rtau[MAX_RPS];
+  double px[MAX_RPS];  // p or q of each row's drafted token
   int32_t rf[MAX_RPS];
   int32_t nk[MAX_RPS];
   int32_t arg[MAX_RPS];
-  int32_t lsrc[MAX_RPS];  // wave whose list holds the row's kept list, -1: the scratch lists
-  int32_t slow[MAX_RPS];
   int32_t x[MAX_K];
   float u[MAX_K + 1];
-  int32_t nslow;
-  int32_t big;  // the sequence's last token needs the full-row draw
-  int32_t n;
+  int32_t fast, big, n, flag;
 };
 
 // Final draw from kept lists by one wave (filtered rows): residual
@@ -1509,67 +1505,43 @@ __device__ int wave_list_sample(double u, const int32_t* pidx, const double* ppr
   return tok;
 }
 
-// One workgroup per sequence, one wave per row (rows w, w + 16, ...): every
-// row of the sequence is merged in parallel; rows the wave-level merge cannot
-// decide are merged by the whole block afterwards; then wave 0 runs the accept
-// tests, the first-rejection scan and the final draw from the kept lists (the
-// whole block draws from full rows when a kept set is too large for a list).
+// One workgroup per row.  Its first wave merges the row (wave_row: one round
+// trip for the chunk records and most candidate units, one to read the units
+// back); when the lists cannot decide the cut the whole block merges it
+// (row_finalize).  The last row of a sequence to be merged then runs, on its
+// first wave, the accept tests, the first-rejection scan and the draw from the
+// kept lists (the whole block draws from full rows when a kept set is too
+// large for a list; unfiltered rows: the sampling kernel draws afterwards).
 // With do_seq == 0 (filtered probabilities) only the merges run.
 template <int DT, int MODE>
-__global__ void __launch_bounds__(ROW_WG) row_kernel(Args a) {
+__global__ void __launch_bounds__(WG) row_kernel(Args a) {
   __shared__ RowKSm sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  const int b = (int)blockIdx.x, K = a.K, rps = a.rps;
-  const bool lds_lists = rps <= ROW_NW;  // otherwise a wave merges several rows and the lists go to scratch
-  if (a.do_seq && w == 0) {
-    if (lane < K) sm.x[lane] = a.X[(size_t)b * K + lane];
-    for (int j = lane; j <= K; j += 64) sm.u[j] = a.U[(size_t)b * (K + 1) + j];
-  }
-  if (t == 0) sm.nslow = 0;
-  __syncthreads();
-  for (int jr = w; jr < rps; jr += ROW_NW) {
-    const int rl = b * rps + jr;
-    const int ir = jr <= K ? jr : jr - K - 1;
-    const int xtok = (a.do_seq && ir < K) ? a.X[(size_t)b * K + ir] : -1;
+  const int rl = (int)blockIdx.x, K = a.K, rps = a.rps;
+  const int b = rl / rps, jr = rl - b * rps;
+  const int ir = jr <= K ? jr : jr - K - 1;
+  const int xtok = (a.do_seq && ir < K) ? a.X[(size_t)b * K + ir] : -1;
+  if (w == 0) {
     RowRec rr;
-    if (wave_row<DT, MODE>(a, rl, xtok, sm.w[w], sm.list[w], !lds_lists, rr)) {
-      if (lane == 0) {
-        sm.px[jr] = rr.px;
-        sm.sk[jr] = rr.S_kept;
-        sm.rm[jr] = rr.m;
-        sm.rtau[jr] = rr.tau;
-        sm.rf[jr] = rr.flags;
-        sm.nk[jr] = rr.nkept;
-        sm.arg[jr] = rr.arg;
-        sm.lsrc[jr] = lds_lists ? w : -1;
-      }
-    } else if (lane == 0) {
-      sm.slow[atomicAdd(&sm.nslow, 1)] = jr;
-    }
+    const bool ok = wave_row<DT, MODE>(a, rl, xtok, sm.w, rr);
+    if (lane == 0) sm.fast = ok;
   }
-  if (!lds_lists) __builtin_amdgcn_s_waitcnt(0);  // scratch lists are read back by wave 0
   __syncthreads();
-  const int nslow = sm.nslow;
-  for (int s = 0; s < nslow; ++s) {
-    const int jr = sm.slow[s];
-    const int ir = jr <= K ? jr : jr - K - 1;
-    const int xtok = (a.do_seq && ir < K) ? sm.x[ir] : -1;
-    const RowRec rr = row_finalize<DT, MODE, ROW_WG>(a, b * rps + jr, xtok, sm.blk);
-    if (t == 0) {
-      sm.px[jr] = rr.px;
-      sm.sk[jr] = rr.S_kept;
-      sm.rm[jr] = rr.m;
-      sm.rtau[jr] = rr.tau;
-      sm.rf[jr] = rr.flags;
-      sm.nk[jr] = rr.nkept;
-      sm.arg[jr] = rr.arg;
-      sm.lsrc[jr] = -1;
-    }
+  if (!sm.fast) (void)row_finalize<DT, MODE, WG>(a, rl, xtok, sm.blk);
+  if (!a.do_seq || !last_arrival(&a.seq_cnt[b], (uint32_t)rps, &sm.flag)) return;
+
+  // ---- the sequence: its rows' records, drafted tokens and uniforms (one round trip)
+  const RowRec* rr = a.row + (size_t)b * rps;
+  for (int j = t; j < rps; j += WG) {
+    sm.px[j] = ld_dev(&rr[j].px);
+    sm.rf[j] = ld_dev(&rr[j].flags);
+    sm.nk[j] = ld_dev(&rr[j].nkept);
+    sm.arg[j] = ld_dev(&rr[j].arg);
   }
-  if (!a.do_seq) return;
-  if (nslow > 0) __builtin_amdgcn_s_waitcnt(0);
+  if (t < K) sm.x[t] = a.X[(size_t)b * K + t];
+  if (t <= K) sm.u[t] = a.U[(size_t)b * (K + 1) + t];
   __syncthreads();
   if (w == 0) {
     // accept tests: draft i is accepted iff u_i * q_i(x_i) < p_i(x_i)
@@ -1615,38 +1587,22 @@ __global__ void __launch_bounds__(ROW_WG) row_kernel(Args a) {
       if (np < 0 || (res && nq < 0)) {
         big = 1;
       } else {
-        // the two kept lists, from LDS or from the scratch lists
-        const int32_t* pidx;
-        const double* pprob;
-        const int32_t* qidx;
-        const double* qprob;
-        if (sm.lsrc[n] >= 0) {
-          pidx = sm.list[sm.lsrc[n]].idx;
-          pprob = sm.list[sm.lsrc[n]].prob;
-        } else {
-          const size_t o = (size_t)(b * rps + n) * KEEP_CAP;
-          for (int e = lane; e < np; e += 64) {
-            sm.blk.q.pidx[e] = ld_dev(&a.kidx[o + e]);
-            sm.blk.q.pprob[e] = ld_dev(&a.kprob[o + e]);
-          }
-          pidx = sm.blk.q.pidx;
-          pprob = sm.blk.q.pprob;
+        // the two kept lists (one round trip)
+        SmemSeq& q = sm.blk.q;
+        const size_t op = (size_t)(b * rps + n) * KEEP_CAP, oq = (size_t)(b * rps + jq) * KEEP_CAP;
+        for (int e = lane; e < np; e += 64) {
+          q.pidx[e] = ld_dev(&a.kidx[op + e]);
+          q.pprob[e] = ld_dev(&a.kprob[op + e]);
         }
-        if (!res || sm.lsrc[jq] >= 0) {
-          qidx = sm.list[res ? sm.lsrc[jq] : 0].idx;
-          qprob = sm.list[res ? sm.lsrc[jq] : 0].prob;
-        } else {
-          const size_t o = (size_t)(b * rps + jq) * KEEP_CAP;
+        if (res) {
           for (int e = lane; e < nq; e += 64) {
-            sm.blk.q.qidx[e] = ld_dev(&a.kidx[o + e]);
-            sm.blk.q.qprob[e] = ld_dev(&a.kprob[o + e]);
+            q.qidx[e] = ld_dev(&a.kidx[oq + e]);
+            q.qprob[e] = ld_dev(&a.kprob[oq + e]);
           }
-          qidx = sm.blk.q.qidx;
-          qprob = sm.blk.q.qprob;
         }
         wave_sync();
         double Z;
-        const int tok = wave_list_sample((double)sm.u[K], pidx, pprob, np, qidx, qprob, nq, res, &Z);
+        const int tok = wave_list_sample((double)sm.u[K], q.pidx, q.pprob, np, q.qidx, q.qprob, nq, res, &Z);
         if (lane == 0) {
           ot[n] = tok;
           if (a.out_z) a.out_z[b] = Z;
@@ -1664,16 +1620,11 @@ __global__ void __launch_bounds__(ROW_WG) row_kernel(Args a) {
     const int n = sm.n;
     const bool res = n < K;
     const int jq = res ? K + 1 + n : n;
-    if (t < 2) {
-      const int j = t == 0 ? n : jq;
-      sm.blk.dr[t].m = sm.rm[j];
-      sm.blk.dr[t].tau = sm.rtau[j];
-      sm.blk.dr[t].snorm = sm.sk[j];
-    }
-    __syncthreads();
+    set_draw_row(&rr[n], true, 0, sm.blk);
+    set_draw_row(&rr[jq], true, 1, sm.blk);
     double Z;
-    const int tok = full_row_sample<DT, ROW_WG>(a, (double)sm.u[K], row_ptr(a, b * rps + n, ESZ),
-                                                row_ptr(a, b * rps + jq, ESZ), res, sm.blk, &Z);
+    const int tok = full_row_sample<DT, WG>(a, (double)sm.u[K], row_ptr(a, b * rps + n, ESZ),
+                                            row_ptr(a, b * rps + jq, ESZ), res, sm.blk, &Z);
     if (t == 0) {
       a.out_tok[(size_t)b * (K + 1) + n] = tok;
       if (a.out_z) a.out_z[b] = Z;
@@ -1873,7 +1824,7 @@ hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned 
 
 hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
   KFn f = dtype == D_BF16 ? pick_row<D_BF16>(mode) : pick_row<D_F32>(mode);
-  hipLaunchKernelGGL(f, dim3(grid), dim3(ROW_WG), 0, s, a);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
   return hipGetLastError();
 }
 
