@@ -79,7 +79,7 @@ ProfSlot* prof_begin() {
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, xlogit, total;
+  size_t seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, total;
 };
 
 // What one call needs from the scratch.
@@ -104,7 +104,6 @@ Layout make_layout(int64_t cap_seq, const Need& n) {
   L.seq = o; o += al256(n.B * sizeof(SeqRec));
   L.seg_sum = o; o += al256(n.B * n.nseg * sizeof(double));
   L.seg_last = o; o += al256(n.B * n.nseg * sizeof(int32_t));
-  L.xlogit = o; o += al256(n.rows * sizeof(float));
   L.total = o;
   return L;
 }
@@ -153,7 +152,6 @@ void bind_scratch(Args& a, char* base, const Layout& L) {
   a.seq = (SeqRec*)(base + L.seq);
   a.seg_sum = (double*)(base + L.seg_sum);
   a.seg_last = (int32_t*)(base + L.seg_last);
-  a.xlogit = (float*)(base + L.xlogit);
 }
 
 int check_params(float T, int32_t top_k, float top_p) {

@@ -17,10 +17,9 @@ constexpr int SCE = 2048;        // logits per sampling chunk (8 per thread)
 constexpr int SEG = 512;         // logits per sampling segment (one wave)
 constexpr int SEG_PER_SCE = SCE / SEG;
 constexpr int MAX_K = 64;
-// register budget of the streaming kernel: resident workgroups per CU
-// (vector-loaded bf16 chunks need the fewest registers)
+// register budget of the streaming kernels: resident workgroups per CU
 template <int DT, bool VEC>
-constexpr int stream_wg_per_cu() { return (DT == 1 && VEC) ? 8 : 5; }
+constexpr int stream_wg_per_cu() { return VEC ? 8 : 5; }
 constexpr int MAX_CHUNKS = WG;           // chunks per row (one chunk record per thread in a row merge)
 constexpr int64_t MAX_V = (int64_t)MAX_CHUNKS * CE;  // 2,097,152
 constexpr int MAX_RPS = 2 * MAX_K + 1;
@@ -38,7 +37,7 @@ constexpr int RF_FALLBACK = 4;  // threshold found by the full-row search
 
 // per (row, chunk) summary, 32 bytes
 struct ChunkRec {
-  double s;        // sum over the chunk of exp((x - m) / T), relative to the chunk max
+  double s;        // sum over the chunk of exp2(x * c2), relative to 2^ceil(m * c2) (see chunk_weight)
   float m;         // chunk max logit
   uint32_t bound;  // key of the candidate threshold used by this chunk
   int32_t ncand;   // candidates found (> CAND_CAP means some were dropped)
@@ -92,9 +91,19 @@ struct Args {
   uint32_t* smp_cnt;
   double* seg_sum;
   int32_t* seg_last;
-  float* xlogit;  // per row: the logit of its drafted token (written by the streaming pass)
   int32_t ulen;   // logits per candidate unit (16-byte vector; 1 on the element-load path)
 };
+
+// Weight of chunk record (m_c, s_c) in a row whose max is m: the chunk's sum
+// of exp((x - m) / T).  The streaming pass sums exp2(x * c2) (c2 = log2(e) / T
+// in float) against the integer offset 2^ceil(m_c * c2), or against 2^(m_c * c2)
+// itself when that offset overflows float.
+__device__ __forceinline__ double chunk_weight(double s_c, float m_c, float m, float c2, double invT) {
+  if (!(m_c > -INFINITY)) return 0.0;
+  const float Mi = __builtin_ceilf(m_c * c2);
+  const double f = Mi < INFINITY ? exp2((double)Mi - (double)m_c * (double)c2) : 1.0;
+  return s_c * f * exp(((double)m_c - (double)m) * invT);
+}
 
 // Order-preserving map float -> uint32 (larger float, larger key).
 __device__ __forceinline__ uint32_t ord_key(float f) {
@@ -165,23 +174,33 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
 }
 constexpr int DPP_QP_1032 = 0xB1, DPP_QP_2301 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140,
               DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143;
-
-__device__ __forceinline__ float dpp_wave_fmax(float v) {
-  const uint32_t NI = 0xFF800000u;
-  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QP_1032>(NI, __float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QP_2301>(NI, __float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(NI, __float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_MIRROR>(NI, __float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_BCAST15, 0xA>(NI, __float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_BCAST31, 0xC>(NI, __float_as_uint(v))));
-  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+// DPP move whose lanes outside the row mask are left unspecified: the
+// reductions below read lane 63 only, which every step writes, and without an
+// old value the move folds into the instruction that uses it.
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, RM, 0xF, false);
 }
+
+__device__ __forceinline__ uint32_t dpp_wave_umax(uint32_t v) {
+  v = max(v, dpp_mov<DPP_QP_1032>(v));
+  v = max(v, dpp_mov<DPP_QP_2301>(v));
+  v = max(v, dpp_mov<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp_mov<DPP_MIRROR>(v));
+  v = max(v, dpp_mov<DPP_BCAST15, 0xA>(v));
+  v = max(v, dpp_mov<DPP_BCAST31, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Max over the order keys (no NaN canonicalisation, and the integer max folds
+// with the DPP moves).
+__device__ __forceinline__ float dpp_wave_fmax(float v) { return key_val(dpp_wave_umax(ord_key(v))); }
 
 template <int CTRL, int RM = 0xF>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = dpp_u32<CTRL, RM>(0u, (uint32_t)u);
-  const uint32_t hi = dpp_u32<CTRL, RM>(0u, (uint32_t)(u >> 32));
+  const uint32_t lo = dpp_mov<CTRL, RM>((uint32_t)u);
+  const uint32_t hi = dpp_mov<CTRL, RM>((uint32_t)(u >> 32));
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 __device__ __forceinline__ double dpp_wave_sum(double v) {
@@ -249,15 +268,6 @@ __device__ __forceinline__ T lane63(T v) {
   } else {
     return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
   }
-}
-__device__ __forceinline__ uint32_t dpp_wave_umax(uint32_t v) {
-  v = max(v, dpp_u32<DPP_QP_1032>(0u, v));
-  v = max(v, dpp_u32<DPP_QP_2301>(0u, v));
-  v = max(v, dpp_u32<DPP_HALF_MIRROR>(0u, v));
-  v = max(v, dpp_u32<DPP_MIRROR>(0u, v));
-  v = max(v, dpp_u32<DPP_BCAST15, 0xA>(0u, v));
-  v = max(v, dpp_u32<DPP_BCAST31, 0xC>(0u, v));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Block-wide reductions over NW waves (one partial per wave in LDS), fixed

@@ -65,10 +65,11 @@ struct DrawRow {
 
 struct SmemStream {
   uint64_t cand[NWAVE * CAND_CAP];  // per-wave candidate lists (one flat list after an overflow cut)
-  uint64_t junk[NWAVE][64];         // per-lane target of the emission's writes that keep nothing
   uint64_t tk[WG];
   uint32_t hist[256];
   int32_t wn[NWAVE];
+  float rm[NWAVE];   // per-wave chunk maxima
+  double rs[NWAVE];  // per-wave chunk sums
 };
 struct SmemRow {
   uint64_t keys[KEEP_CAP];
@@ -604,7 +605,7 @@ __device__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
   bool bad = !(m > -INFINITY && m < INFINITY);
   if (MODE == M_PLAIN || MODE == M_TOPP) {
     const float qm = t < nch ? sm.r.cm[t] : -INFINITY;
-    const double s = qm > -INFINITY ? sm.r.cs[t] * exp(((double)qm - (double)m) * a.invT) : 0.0;
+    const double s = chunk_weight(sm.r.cs[t], qm, m, a.c2, a.invT);
     const double S = block_sum<BS / 64>(s, sm.red);
     rr.S = S;
     if (!(S > 0.0 && S < INFINITY)) bad = true;
@@ -762,31 +763,30 @@ struct UnitT {
 // Append every unit of this thread whose max um[u] is at or above thr to its
 // wave's candidate list wl and return the wave's count.  Entries are (bits of
 // the unit max << 32 | index of its first logit); readers turn the bits into
-// an order key (cand_entry_key).  Slots from cap on are dropped.  gm[q] is the
-// max of register slots 8q .. 8q+7: a group with no lane of the wave at or
-// above thr costs one compare and one scalar branch.  In the others every
-// lane writes every unit without a branch: a qualifying one to its slot in
-// the list (mbcnt over the ballot), the others to the lane's own junk slot.
-// Called with every lane active.
+// an order key (cand_entry_key).  Slots from cap on are dropped (a list of
+// 64 * N slots holds every unit of the wave, and then no check is made).
+// gm[q] is the max of register slots 8q .. 8q+7: a group with no lane of the
+// wave at or above thr costs one compare and one scalar branch.  Called with
+// every lane active.
 template <int DT, bool VEC>
 __device__ __forceinline__ int wave_emit(const float (&um)[UnitT<DT, VEC>::N], const float (&gm)[4], float thr,
-                                         int c0, uint64_t* wl, int cap, uint64_t* junk) {
-  constexpr int L = UnitT<DT, VEC>::L, UPG = 8 / L;  // units per group of 8 slots
+                                         int c0, uint64_t* wl, int cap) {
+  constexpr int L = UnitT<DT, VEC>::L, UN = UnitT<DT, VEC>::N, UPG = UN / 4;  // units per group of 8 slots
   int wn = 0;
   const int lb = c0 + local_index<DT, VEC>(0, threadIdx.x);  // slot k's index is lb + local_index(k, 0)
-  uint64_t* jl = junk + (threadIdx.x & 63);
+  const bool full = UN * 64 <= cap;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (__ballot(gm[q] >= thr) == 0ull) continue;
+    if (__builtin_amdgcn_ballot_w64(gm[q] >= thr) == 0ull) continue;
 #pragma unroll
     for (int i = 0; i < UPG; ++i) {
       const int u = q * UPG + i;
       const bool pr = um[u] >= thr;
-      const unsigned long long bm = __ballot(pr);
+      const unsigned long long bm = __builtin_amdgcn_ballot_w64(pr);
       const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bm, (uint32_t)wn));
-      uint64_t* dst = (pr && pos < cap) ? wl + pos : jl;
-      *dst = ((uint64_t)__float_as_uint(um[u]) << 32) | (uint32_t)(lb + local_index<DT, VEC>(u * L, 0));
+      if (pr && (full || pos < cap))
+        wl[pos] = ((uint64_t)__float_as_uint(um[u]) << 32) | (uint32_t)(lb + local_index<DT, VEC>(u * L, 0));
       wn += __popcll(bm);
     }
   }
@@ -797,140 +797,50 @@ __device__ __forceinline__ int wave_emit(const float (&um)[UnitT<DT, VEC>::N], c
 // v_maximum3_f32); logits are never NaN inside the defined input range.
 __device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-// One chunk item: stream it and leave its record (max, sum, candidates).
+// Candidate emission and the chunk record, once the chunk max mc (and for
+// sum modes the chunk sum s in the record's convention, chunk_weight; in
+// greedy mode the arg-max) are known.  um / gm are the unit and group maxima
+// of this thread, tm its max.  Shared memory written here is first written
+// after a barrier of this call, so a workgroup can run it for consecutive
+// items without a barrier in between.  Only the next launch reads what is
+// stored here, so plain stores suffice.
 template <int DT, int MODE, bool VEC>
-__device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
-  constexpr int ESZ = ElemT<DT>::ESZ;
+__device__ __forceinline__ void stream_emit(const Args& a, int item, const float (&um)[UnitT<DT, VEC>::N],
+                                            const float (&gm)[4], float tm, float mc, double s, int arg,
+                                            Smem& sm) {
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
+  constexpr int UL = UnitT<DT, VEC>::L, UN = UnitT<DT, VEC>::N;
   const int t = threadIdx.x;
   const int rl = item / a.nchunks;
-  const int c = item - rl * a.nchunks;
+  const int c0 = (item - rl * a.nchunks) * CE;
   const int chunk_id = item;
-  const char* rp = row_ptr(a, rl, ESZ);
-  const int c0 = c * CE, cn = min(CE, a.V - c0);
-  // drafted token of this row (its logit is kept for the row merge when it
-  // falls in this chunk)
-  int xt = -1;
-  if (MODE != M_GREEDY && a.do_seq) {
-    const int b = rl / a.rps, jr = rl - b * a.rps;
-    const int ir = jr <= a.K ? jr : jr - a.K - 1;
-    if (ir < a.K) xt = a.X[(size_t)b * a.K + ir];
-  }
-
-  float v[EPT];
-  load_chunk<DT, VEC>(rp, c0, cn, v);
-  // maxima of the candidate units, of 4 groups of 8 register slots, and of
-  // the thread
-  constexpr int UL = UnitT<DT, VEC>::L, UN = UnitT<DT, VEC>::N;
-  float um[UN];
-#pragma unroll
-  for (int u = 0; u < UN; ++u) {
-    float x = v[u * UL];
-#pragma unroll
-    for (int e = 1; e < UL; ++e) x = fmax2(x, v[u * UL + e]);
-    um[u] = x;
-  }
-  float gm[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float x = um[g * (8 / UL)];
-#pragma unroll
-    for (int i = 1; i < 8 / UL; ++i) x = fmax2(x, um[g * (8 / UL) + i]);
-    gm[g] = x;
-  }
-  const float tm = fmax2(fmax2(gm[0], gm[1]), fmax2(gm[2], gm[3]));
-  if (t == 0) sm.ncand = 0;
-  const float mc = block_fmax(tm, sm.red);
-
-  ChunkRec rec;
-  rec.s = 0.0;
-  rec.m = mc;
-  rec.bound = 0u;
-  rec.ncand = 0;
-  rec.arg = 0;
-  rec.pad0 = rec.pad1 = 0;
-
   // candidate bound of this chunk: every finite logit at or above it is emitted
   uint32_t bound = 0u;
-  float thr = 0.0f;
+  int nc = 0;
   if (FILT) {
+    float thr;
     if (MODE == M_TOPP) {
       // window below the chunk max (which is <= the row max)
       bound = ord_key(mc - a.win);
     } else {
       // the k-th largest of the 256 thread maxima is <= the row's k-th largest
       // logit (for k > 256 no bound follows: every finite logit qualifies)
+      __syncthreads();
       sm.s.tk[t] = ord_key(tm);
       bitonic_desc(sm.s.tk, WG);
       bound = a.top_k <= WG ? (uint32_t)sm.s.tk[a.top_k - 1] : KEY_NEG_INF;
     }
     thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
-  }
-  if (MODE == M_PLAIN || MODE == M_TOPP) {
-    // sum of exp2((x - mc) * c2): one fma per logit against M = fl(mc * c2);
-    // the (exactly known) rounding of M is a common factor fixed once per
-    // chunk.
-    float acc = 0.0f;
-    double corr = 1.0;
-    if (mc > -INFINITY) {
-      const float c2 = a.c2;
-      const float M = mc * c2;
-      if (M > -INFINITY && M < INFINITY) {
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) {
-          acc += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -M));
-        }
-        corr = exp2((double)M - (double)mc * (double)c2);
-      } else {
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) {
-          acc += __builtin_amdgcn_exp2f((v[k] - mc) * c2);
-        }
-      }
-    }
-    rec.s = block_sum((double)acc, sm.red) * corr;
-  }
-
-  if (xt >= c0 && xt < c0 + cn) {
-    const int li = xt - c0;
-    int owner, kx;
-    if (VEC) {
-      constexpr int EPV = ElemT<DT>::EPV;
-      owner = (li / EPV) % WG;
-      kx = (li / (EPV * WG)) * EPV + li % EPV;
-    } else {
-      owner = li % WG;
-      kx = li / WG;
-    }
-    if (t == owner) {
-      float val = v[0];
-#pragma unroll
-      for (int k = 1; k < EPT; ++k)
-        if (k == kx) val = v[k];
-      a.xlogit[rl] = val;
-    }
-  }
-
-  if (MODE == M_GREEDY) {
-    int best = INT_MAX;
-#pragma unroll
-    for (int k = 0; k < EPT; ++k)
-      if (v[k] == mc) best = min(best, local_index<DT, VEC>(k, t));
-    best = block_min_i(best, sm.red);
-    rec.arg = c0 + (best == INT_MAX ? 0 : best);
-  }
-
-  if (FILT) {
     const int w = t >> 6;
-    const int wn = wave_emit<DT, VEC>(um, gm, thr, c0, &sm.s.cand[w * CAND_CAP], CAND_CAP, sm.s.junk[w]);
+    const int wn = wave_emit<DT, VEC>(um, gm, thr, c0, &sm.s.cand[w * CAND_CAP], CAND_CAP);
     if ((t & 63) == 0) sm.s.wn[w] = wn;
     __syncthreads();
-    int nc = (sm.s.wn[0] + sm.s.wn[1]) + (sm.s.wn[2] + sm.s.wn[3]);
+    nc = (sm.s.wn[0] + sm.s.wn[1]) + (sm.s.wn[2] + sm.s.wn[3]);
     uint64_t* dst = a.cand + (size_t)chunk_id * CAND_CAP;
     if (nc <= CAND_CAP) {
       int off = 0;
       for (int i = 0; i < w; ++i) off += sm.s.wn[i];
-      for (int s = t & 63; s < wn; s += 64) st_dev(&dst[off + s], sm.s.cand[w * CAND_CAP + s]);
+      for (int j = t & 63; j < wn; j += 64) dst[off + j] = sm.s.cand[w * CAND_CAP + j];
     } else {
       // Too many: keep exactly the units above the (CAND_CAP+1)-th largest
       // unit max (radix select over the registers) and raise the bound to match.
@@ -973,31 +883,225 @@ __device__ __forceinline__ void stream_item(const Args& a, int item, Smem& sm) {
       }
       __syncthreads();
       nc = sm.ncand;
-      for (int s = t; s < nc; s += WG) st_dev(&dst[s], sm.s.cand[s]);
+      for (int j = t; j < nc; j += WG) dst[j] = sm.s.cand[j];
     }
-    rec.ncand = nc;
-    rec.bound = bound;
   }
   if (t == 0) {
-    ChunkRec* cp = &a.chunk[chunk_id];
-    if (MODE == M_PLAIN || MODE == M_TOPP) st_dev(&cp->s, rec.s);
-    st_dev(&cp->m, rec.m);
-    if (FILT) {
-      st_dev(&cp->bound, rec.bound);
-      st_dev(&cp->ncand, rec.ncand);
-    }
-    if (MODE == M_GREEDY) st_dev(&cp->arg, rec.arg);
+    ChunkRec rec;
+    rec.s = s;
+    rec.m = mc;
+    rec.bound = bound;
+    rec.ncand = nc;
+    rec.arg = arg;
+    rec.pad0 = rec.pad1 = 0;
+    a.chunk[chunk_id] = rec;
   }
-
 }
 
-// One workgroup per (row, chunk).  No workgroup waits on another: the row
-// merge runs in the next launch, when HBM is no longer saturated and its few
-// dependent round trips are short.
-template <int DT, int MODE, bool VEC>
-__global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, VEC>())) stream_kernel(Args a) {
+// Element-load path (rows not 16-byte aligned): one workgroup per (row,
+// chunk).  No workgroup waits on another: the row merge runs in the next
+// launch.
+template <int DT, int MODE>
+__global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, false>())) stream_kernel_elem(Args a) {
   __shared__ Smem sm;
-  stream_item<DT, MODE, VEC>(a, (int)blockIdx.x, sm);
+  constexpr int ESZ = ElemT<DT>::ESZ;
+  const int t = threadIdx.x;
+  const int item = (int)blockIdx.x;
+  const int rl = item / a.nchunks;
+  const int c0 = (item - rl * a.nchunks) * CE;
+  const int cn = min(CE, a.V - c0);
+  const char* rp = row_ptr(a, rl, ESZ);
+  float v[EPT];
+  load_chunk<DT, false>(rp, c0, cn, v);
+  // units are single logits here: the unit maxima are v itself
+  float gm[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float x = v[8 * g];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) x = fmax2(x, v[8 * g + i]);
+    gm[g] = x;
+  }
+  const float tm = fmax2(fmax2(gm[0], gm[1]), fmax2(gm[2], gm[3]));
+  const float mc = block_fmax(tm, sm.red);
+  double s = 0.0;
+  if (MODE == M_PLAIN || MODE == M_TOPP) {
+    // in the record's convention (chunk_weight)
+    double acc = 0.0;
+    if (mc > -INFINITY) {
+      const double c2 = (double)a.c2;
+      const float Mi = __builtin_ceilf(mc * a.c2);
+      const double off = Mi < INFINITY ? (double)Mi : (double)mc * c2;
+#pragma unroll
+      for (int k = 0; k < EPT; ++k)
+        if (v[k] > -INFINITY) acc += exp2((double)v[k] * c2 - off);
+    }
+    s = block_sum(acc, sm.red);
+  }
+  int arg = 0;
+  if (MODE == M_GREEDY) {
+    int best = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      if (v[k] == mc) best = min(best, k * WG + t);
+    best = block_min_i(best, sm.red);
+    arg = c0 + (best == INT_MAX ? 0 : best);
+  }
+  stream_emit<DT, MODE, false>(a, item, v, gm, tm, mc, s, arg, sm);
+}
+
+// 16-byte vectors of one chunk per thread (thread t, vector u holds the
+// chunk's vector u*WG + t).
+template <int DT>
+struct ChunkRaw {
+  uint4 r[EPT / ElemT<DT>::EPV];
+};
+
+// Issue the loads of the chunk of row rl at logit c0 (cn logits) as buffer
+// loads whose range ends with the chunk: a vector past the row end reads as
+// zero without a memory access, so no load depends on a lane condition.
+// Vector u of the threads has its own descriptor, based at the chunk's byte
+// u*WG*16 and sized to what is left of the chunk, so that the range check
+// sees the whole offset (the lane offset t*16 is the only offset of the load).
+template <int DT>
+__device__ __forceinline__ void issue_chunk(const Args& a, int rl, int c0, int cn, ChunkRaw<DT>& cr) {
+  constexpr int ESZ = ElemT<DT>::ESZ, NV = EPT / ElemT<DT>::EPV;
+  const char* cp = row_ptr(a, rl, ESZ) + (size_t)c0 * ESZ;
+  const int nbytes = cn * ESZ;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int ub = u * WG * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cp + ub), (short)0, max(nbytes - ub, 0), 0x00020000);
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16, 0, 0);
+    cr.r[u] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Widen 16-byte vector r into its EPV logits.
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4& r, float* v) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (DT == D_BF16) {
+      v[2 * q] = bf16_lo(w[q]);
+      v[2 * q + 1] = bf16_hi(w[q]);
+    } else {
+      v[q] = __uint_as_float(w[q]);
+    }
+  }
+}
+
+// Sum over chunk logits cp[0 .. cn) of exp2((x - mc) * c2) in double, this
+// thread's share (strided by the workgroup).  Used only when mc * c2
+// overflows float; kept out of line so that its constants do not occupy
+// registers in the streaming loop.
+template <int DT>
+__device__ __noinline__ double chunk_sum_slow(const char* cp, int cn, float mc, float c2) {
+  double d = 0.0;
+  for (int l = threadIdx.x; l < cn; l += WG) {
+    const double x = (double)load_elem<DT>(cp, l);
+    if (x > -INFINITY) d += exp2((x - (double)mc) * (double)c2);
+  }
+  return d;
+}
+
+// Vector path: one workgroup per (row, chunk), loading through buffer loads
+// (issue_chunk).  The exp sum of each thread is taken against the integer
+// offset Mt = ceil(tm * c2) of its max tm (so every term is exp2 of at most a
+// fraction above 0), and per-thread sums meet at the chunk's offset
+// Mi = ceil(mc * c2) by exact ldexp (offsets far apart scale a term to zero
+// either way): that is the record's convention (chunk_weight), reached with
+// one barrier for the chunk max and sum together.  Only when mc * c2
+// overflows float is the chunk summed again, in double, from memory.  No
+// workgroup waits on another: the row merge runs in the next launch.
+template <int DT, int MODE>
+__global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_kernel_vec(Args a) {
+  __shared__ Smem sm;
+  constexpr int EPV = ElemT<DT>::EPV, NV = EPT / EPV;
+  constexpr bool SUM = MODE == M_PLAIN || MODE == M_TOPP;
+  const int t = threadIdx.x, w = t >> 6;
+  const int item = (int)blockIdx.x;
+  const int rl = item / a.nchunks;
+  const int c0 = (item - rl * a.nchunks) * CE;
+  const int cn = min(CE, a.V - c0);
+  const float c2 = a.c2;
+  ChunkRaw<DT> cr;
+  issue_chunk<DT>(a, rl, c0, cn, cr);
+
+  float v[EPT], um[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    unpack16<DT>(cr.r[u], &v[u * EPV]);
+    if (cn < CE) {
+      const bool out = (u * WG + t) * EPV >= cn;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) v[u * EPV + e] = out ? -INFINITY : v[u * EPV + e];
+    }
+    float x = v[u * EPV];
+#pragma unroll
+    for (int e = 1; e < EPV; ++e) x = fmax2(x, v[u * EPV + e]);
+    um[u] = x;
+  }
+  float gm[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    constexpr int UPG = NV / 4;
+    float x = um[g * UPG];
+#pragma unroll
+    for (int i = 1; i < UPG; ++i) x = fmax2(x, um[g * UPG + i]);
+    gm[g] = x;
+  }
+  const float tm = fmax2(fmax2(gm[0], gm[1]), fmax2(gm[2], gm[3]));
+  float acc = 0.0f, Mt = 0.0f;
+  if (SUM) {
+    Mt = fmax2(__builtin_ceilf(tm * c2), -1.0e30f);  // -1e30 for an all -inf thread: its terms are 0
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -Mt));
+  }
+
+  // chunk max and sum: one wave-level pass each, one barrier
+  const float mw = dpp_wave_fmax(tm);
+  if (SUM) {
+    // exponent in [-2048, 0]: an all -inf wave (Mw = -inf) has acc = 0
+    const float Mw = __builtin_ceilf(mw * c2);
+    const double sw = dpp_wave_sum(__builtin_amdgcn_ldexp((double)acc, (int)fminf(fmaxf(Mt - Mw, -2048.0f), 0.0f)));
+    if ((t & 63) == 0) sm.s.rs[w] = sw;
+  }
+  if ((t & 63) == 0) sm.s.rm[w] = mw;
+  __syncthreads();
+  float mc = sm.s.rm[0];
+#pragma unroll
+  for (int i = 1; i < NWAVE; ++i) mc = fmax2(mc, sm.s.rm[i]);
+  double s = 0.0;  // the record's sum: thread 0 stores it
+  if (SUM && mc > -INFINITY) {
+    const float Mi = __builtin_ceilf(mc * c2);
+    if (Mi < INFINITY) {
+      if (w == 0) {
+#pragma unroll
+        for (int i = 0; i < NWAVE; ++i) {
+          const float m = sm.s.rm[i];
+          if (m > -INFINITY)
+            s += __builtin_amdgcn_ldexp(sm.s.rs[i], (int)fmaxf(__builtin_ceilf(m * c2) - Mi, -2048.0f));
+        }
+      }
+    } else {
+      constexpr int ESZ = ElemT<DT>::ESZ;
+      s = block_sum(chunk_sum_slow<DT>(row_ptr(a, rl, ESZ) + (size_t)c0 * ESZ, cn, mc, c2), sm.red);
+    }
+  }
+
+  int arg = 0;
+  if (MODE == M_GREEDY) {
+    int best = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      if (v[k] == mc) best = min(best, local_index<DT, true>(k, t));
+    best = block_min_i(best, sm.red);
+    arg = c0 + (best == INT_MAX ? 0 : best);
+  }
+  stream_emit<DT, MODE, true>(a, item, um, gm, tm, mc, s, arg, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1160,7 +1264,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
   const double invT = a.invT;
 
   // one round trip: the chunk records (chunk lane + 64 i) and the drafted
-  // token's logit, which the streaming pass stored
+  // token's logit
   float cm[4];
   double cs[4];
   uint32_t cb[4];
@@ -1183,7 +1287,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       if (MODE == M_GREEDY) carg[i] = cr[c].arg;
     }
   }
-  const float lx = (MODE != M_GREEDY && hx) ? a.xlogit[rl] : -INFINITY;
+  const float lx = (MODE != M_GREEDY && hx) ? load_elem<DT>(row_ptr(a, rl, ElemT<DT>::ESZ), xtok) : -INFINITY;
   // with them, speculatively, entry `lane` of the first SPECC chunks' lists
   // (most lists are shorter than 64 units): one round trip for most rows
   constexpr int SPECC = 16;
@@ -1209,7 +1313,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     double sl = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (cm[i] > -INFINITY) sl += cs[i] * exp(((double)cm[i] - (double)m) * invT);
+      sl += chunk_weight(cs[i], cm[i], m, a.c2, invT);
     const double S = dpp_wave_sum(sl);
     rr.S = S;
     if (!(S > 0.0 && S < INFINITY)) bad = true;
@@ -1781,7 +1885,7 @@ typedef void (*KFn)(Args);
 
 template <int DT, int MODE>
 static KFn pick_stream(bool vec) {
-  return vec ? (KFn)stream_kernel<DT, MODE, true> : (KFn)stream_kernel<DT, MODE, false>;
+  return vec ? (KFn)stream_kernel_vec<DT, MODE> : (KFn)stream_kernel_elem<DT, MODE>;
 }
 
 template <int DT>
@@ -1816,6 +1920,7 @@ static KFn pick_probs(int mode) {
   }
 }
 
+// grid: the number of streaming items (one workgroup each).
 hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s) {
   KFn f = dtype == D_BF16 ? pick_stream_mode<D_BF16>(mode, vec) : pick_stream_mode<D_F32>(mode, vec);
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
