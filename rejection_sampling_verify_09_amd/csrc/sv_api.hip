@@ -237,6 +237,8 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
 
   const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
   a.ulen = vec ? 16 / esz : 1;
+  a.dch = make_udiv((uint32_t)a.nchunks);
+  a.drps = make_udiv((uint32_t)a.rps);
   hipStream_t s = (hipStream_t)stream;
   ProfSlot* prof = prof_begin();
   if (prof && hipEventRecord(prof->ev[0], s) != hipSuccess) return SV_ERR_HIP;
@@ -313,6 +315,8 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   bind_scratch(a, base, L);
   const bool vec = aligned16(logits) && ((int64_t)V * esz) % 16 == 0;
   a.ulen = vec ? 16 / esz : 1;
+  a.dch = make_udiv((uint32_t)a.nchunks);
+  a.drps = make_udiv((uint32_t)a.rps);
   hipStream_t s = (hipStream_t)stream;
   if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;

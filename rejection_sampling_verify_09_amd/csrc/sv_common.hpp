@@ -65,6 +65,23 @@ struct SeqRec {
   int32_t flags;
 };
 
+// Unsigned division by a launch constant d >= 1 as a multiply and a shift:
+// with l = ceil(log2 d) and m = ceil(2^(31+l) / d) < 2^32, n / d equals
+// (n * m) >> (31 + l) for every n < 2^31 (m * d - 2^(31+l) < d <= 2^l keeps
+// the error below the distance to the next multiple).  Uniform operands make
+// it scalar work.
+struct UDiv {
+  uint32_t m;
+  int32_t s;
+};
+__host__ __device__ inline UDiv make_udiv(uint32_t d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  const unsigned long long p = 1ull << (31 + l);
+  return UDiv{(uint32_t)((p + d - 1) / d), 31 + l};
+}
+__device__ __forceinline__ int udiv(int n, UDiv d) { return (int)(((uint64_t)(uint32_t)n * d.m) >> d.s); }
+
 struct Args {
   const void* tgt;
   const void* drf;
@@ -92,6 +109,8 @@ struct Args {
   double* seg_sum;
   int32_t* seg_last;
   int32_t ulen;   // logits per candidate unit (16-byte vector; 1 on the element-load path)
+  UDiv dch;       // division by nchunks
+  UDiv drps;      // division by rps
 };
 
 // Weight of chunk record (m_c, s_c) in a row whose max is m: the chunk's sum
@@ -202,6 +221,15 @@ __device__ __forceinline__ double dpp_f64(double v) {
   const uint32_t lo = dpp_mov<CTRL, RM>((uint32_t)u);
   const uint32_t hi = dpp_mov<CTRL, RM>((uint32_t)(u >> 32));
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ float dpp_wave_fsum(float v) {
+  v += __uint_as_float(dpp_mov<DPP_QP_1032>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<DPP_QP_2301>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<DPP_HALF_MIRROR>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<DPP_MIRROR>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<DPP_BCAST15, 0xA>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<DPP_BCAST31, 0xC>(__float_as_uint(v)));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
 __device__ __forceinline__ double dpp_wave_sum(double v) {
   v += dpp_f64<DPP_QP_1032>(v);
@@ -436,7 +464,7 @@ __device__ __forceinline__ bool last_arrival(uint32_t* cnt, uint32_t total, int*
 // load from a computed address inside the argument block, which moves the
 // whole block to scratch memory.
 __device__ __forceinline__ const char* row_ptr(const Args& a, int rl, int esz) {
-  const int b = rl / a.rps, j = rl - b * a.rps;
+  const int b = udiv(rl, a.drps), j = rl - b * a.rps;
   const bool dr = j > a.K;
   const size_t idx = dr ? (size_t)b * a.K + (j - a.K - 1) : (size_t)b * (a.K + 1) + j;
   const uintptr_t t = (uintptr_t)a.tgt, d = (uintptr_t)a.drf;

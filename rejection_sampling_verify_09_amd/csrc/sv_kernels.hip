@@ -69,7 +69,7 @@ struct SmemStream {
   uint32_t hist[256];
   int32_t wn[NWAVE];
   float rm[NWAVE];   // per-wave chunk maxima
-  double rs[NWAVE];  // per-wave chunk sums
+  float rs[NWAVE];   // per-wave chunk sums (against the wave's offset)
 };
 struct SmemRow {
   uint64_t keys[KEEP_CAP];
@@ -768,6 +768,7 @@ struct UnitT {
 // gm[q] is the max of register slots 8q .. 8q+7: a group with no lane of the
 // wave at or above thr costs one compare and one scalar branch.  Called with
 // every lane active.
+constexpr int FCMP_OGE = 3;  // ordered >= (wave compare mask)
 template <int DT, bool VEC>
 __device__ __forceinline__ int wave_emit(const float (&um)[UnitT<DT, VEC>::N], const float (&gm)[4], float thr,
                                          int c0, uint64_t* wl, int cap) {
@@ -777,12 +778,12 @@ __device__ __forceinline__ int wave_emit(const float (&um)[UnitT<DT, VEC>::N], c
   const bool full = UN * 64 <= cap;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (__builtin_amdgcn_ballot_w64(gm[q] >= thr) == 0ull) continue;
+    if (__builtin_amdgcn_fcmpf(gm[q], thr, FCMP_OGE) == 0ull) continue;
 #pragma unroll
     for (int i = 0; i < UPG; ++i) {
       const int u = q * UPG + i;
       const bool pr = um[u] >= thr;
-      const unsigned long long bm = __builtin_amdgcn_ballot_w64(pr);
+      const unsigned long long bm = __builtin_amdgcn_fcmpf(um[u], thr, FCMP_OGE);
       const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bm, (uint32_t)wn));
       if (pr && (full || pos < cap))
@@ -811,7 +812,7 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   constexpr int UL = UnitT<DT, VEC>::L, UN = UnitT<DT, VEC>::N;
   const int t = threadIdx.x;
-  const int rl = item / a.nchunks;
+  const int rl = udiv(item, a.dch);
   const int c0 = (item - rl * a.nchunks) * CE;
   const int chunk_id = item;
   // candidate bound of this chunk: every finite logit at or above it is emitted
@@ -835,11 +836,11 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
     const int wn = wave_emit<DT, VEC>(um, gm, thr, c0, &sm.s.cand[w * CAND_CAP], CAND_CAP);
     if ((t & 63) == 0) sm.s.wn[w] = wn;
     __syncthreads();
-    nc = (sm.s.wn[0] + sm.s.wn[1]) + (sm.s.wn[2] + sm.s.wn[3]);
+    const int n0 = sm.s.wn[0], n1 = sm.s.wn[1], n2 = sm.s.wn[2], n3 = sm.s.wn[3];
+    nc = (n0 + n1) + (n2 + n3);
     uint64_t* dst = a.cand + (size_t)chunk_id * CAND_CAP;
     if (nc <= CAND_CAP) {
-      int off = 0;
-      for (int i = 0; i < w; ++i) off += sm.s.wn[i];
+      const int off = (w > 0 ? n0 : 0) + (w > 1 ? n1 : 0) + (w > 2 ? n2 : 0);
       for (int j = t & 63; j < wn; j += 64) dst[off + j] = sm.s.cand[w * CAND_CAP + j];
     } else {
       // Too many: keep exactly the units above the (CAND_CAP+1)-th largest
@@ -907,7 +908,7 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, false>())) stream_ke
   constexpr int ESZ = ElemT<DT>::ESZ;
   const int t = threadIdx.x;
   const int item = (int)blockIdx.x;
-  const int rl = item / a.nchunks;
+  const int rl = udiv(item, a.dch);
   const int c0 = (item - rl * a.nchunks) * CE;
   const int cn = min(CE, a.V - c0);
   const char* rp = row_ptr(a, rl, ESZ);
@@ -1008,34 +1009,29 @@ __device__ __noinline__ double chunk_sum_slow(const char* cp, int cn, float mc, 
 }
 
 // Vector path: one workgroup per (row, chunk), loading through buffer loads
-// (issue_chunk).  The exp sum of each thread is taken against the integer
-// offset Mt = ceil(tm * c2) of its max tm (so every term is exp2 of at most a
-// fraction above 0), and per-thread sums meet at the chunk's offset
+// (issue_chunk).  The exp sum of each wave is taken against the integer
+// offset Mw = ceil(mw * c2) of its max mw (so every term is exp2 of at most a
+// fraction above 0), and the wave sums meet at the chunk's offset
 // Mi = ceil(mc * c2) by exact ldexp (offsets far apart scale a term to zero
 // either way): that is the record's convention (chunk_weight), reached with
 // one barrier for the chunk max and sum together.  Only when mc * c2
 // overflows float is the chunk summed again, in double, from memory.  No
 // workgroup waits on another: the row merge runs in the next launch.
 template <int DT, int MODE>
-__global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_kernel_vec(Args a) {
-  __shared__ Smem sm;
+__device__ __forceinline__ void stream_vec_body(const Args& a, int item, int rl, int c0, int cn,
+                                                const ChunkRaw<DT>& cr, Smem& sm) {
   constexpr int EPV = ElemT<DT>::EPV, NV = EPT / EPV;
   constexpr bool SUM = MODE == M_PLAIN || MODE == M_TOPP;
   const int t = threadIdx.x, w = t >> 6;
-  const int item = (int)blockIdx.x;
-  const int rl = item / a.nchunks;
-  const int c0 = (item - rl * a.nchunks) * CE;
-  const int cn = min(CE, a.V - c0);
   const float c2 = a.c2;
-  ChunkRaw<DT> cr;
-  issue_chunk<DT>(a, rl, c0, cn, cr);
 
   float v[EPT], um[NV];
+  const int nvec = cn / EPV;  // vectors in the chunk (the row's last chunk has fewer than WG * NV)
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     unpack16<DT>(cr.r[u], &v[u * EPV]);
-    if (cn < CE) {
-      const bool out = (u * WG + t) * EPV >= cn;
+    if (nvec < WG * NV) {
+      const bool out = t >= nvec - u * WG;  // vector u*WG + t lies past the row end (it read as zero)
 #pragma unroll
       for (int e = 0; e < EPV; ++e) v[u * EPV + e] = out ? -INFINITY : v[u * EPV + e];
     }
@@ -1054,19 +1050,22 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_ker
     gm[g] = x;
   }
   const float tm = fmax2(fmax2(gm[0], gm[1]), fmax2(gm[2], gm[3]));
-  float acc = 0.0f, Mt = 0.0f;
-  if (SUM) {
-    Mt = fmax2(__builtin_ceilf(tm * c2), -1.0e30f);  // -1e30 for an all -inf thread: its terms are 0
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -Mt));
-  }
 
-  // chunk max and sum: one wave-level pass each, one barrier
+  // chunk max and sum: one wave-level pass each, one barrier.  The terms are
+  // taken against the wave's offset Mw (-1e30 for an all -inf wave: its terms
+  // are 0) and summed pairwise.
   const float mw = dpp_wave_fmax(tm);
   if (SUM) {
-    // exponent in [-2048, 0]: an all -inf wave (Mw = -inf) has acc = 0
-    const float Mw = __builtin_ceilf(mw * c2);
-    const double sw = dpp_wave_sum(__builtin_amdgcn_ldexp((double)acc, (int)fminf(fmaxf(Mt - Mw, -2048.0f), 0.0f)));
+    const float Mw = fmax2(__builtin_ceilf(mw * c2), -1.0e30f);
+    float e[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -Mw));
+#pragma unroll
+    for (int h = 1; h < EPT; h *= 2) {
+#pragma unroll
+      for (int k = 0; k < EPT; k += 2 * h) e[k] += e[k + h];
+    }
+    const float sw = dpp_wave_fsum(e[0]);
     if ((t & 63) == 0) sm.s.rs[w] = sw;
   }
   if ((t & 63) == 0) sm.s.rm[w] = mw;
@@ -1083,7 +1082,7 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_ker
         for (int i = 0; i < NWAVE; ++i) {
           const float m = sm.s.rm[i];
           if (m > -INFINITY)
-            s += __builtin_amdgcn_ldexp(sm.s.rs[i], (int)fmaxf(__builtin_ceilf(m * c2) - Mi, -2048.0f));
+            s += __builtin_amdgcn_ldexp((double)sm.s.rs[i], (int)fmaxf(__builtin_ceilf(m * c2) - Mi, -2048.0f));
         }
       }
     } else {
@@ -1102,6 +1101,18 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_ker
     arg = c0 + (best == INT_MAX ? 0 : best);
   }
   stream_emit<DT, MODE, true>(a, item, um, gm, tm, mc, s, arg, sm);
+}
+
+template <int DT, int MODE>
+__global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_kernel_vec(Args a) {
+  __shared__ Smem sm;
+  const int item = (int)blockIdx.x;
+  const int rl = udiv(item, a.dch);
+  const int c0 = (item - rl * a.nchunks) * CE;
+  const int cn = min(CE, a.V - c0);
+  ChunkRaw<DT> cr;
+  issue_chunk<DT>(a, rl, c0, cn, cr);
+  stream_vec_body<DT, MODE>(a, item, rl, c0, cn, cr, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1624,7 +1635,7 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   const int rl = (int)blockIdx.x, K = a.K, rps = a.rps;
-  const int b = rl / rps, jr = rl - b * rps;
+  const int b = udiv(rl, a.drps), jr = rl - b * rps;
   const int ir = jr <= K ? jr : jr - K - 1;
   const int xtok = (a.do_seq && ir < K) ? a.X[(size_t)b * K + ir] : -1;
   if (w == 0) {
