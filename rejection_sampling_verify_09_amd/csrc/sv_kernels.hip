@@ -1161,6 +1161,10 @@ struct WaveRowSm {
     uint64_t keys[KEEP_CAP];       // candidates at or above lo (ord_key << 32 | index)
     unsigned long long hist[256];  // radix-select bins
     int32_t kept[KEEP_CAP];        // kept indices (for their ascending order)
+    struct {                       // rank cut of at most 64 entries
+      uint32_t k[64], ks[64];
+      unsigned long long ws[64];
+    } cut;
   };
   int32_t off[MAX_CHUNKS + 1];     // candidate offsets of the row's chunks
 };
@@ -1259,6 +1263,34 @@ __device__ __forceinline__ uint32_t wave_walk(const uint32_t (&ek)[WR_EPL], cons
     hi = km;
   }
   return 1u;
+}
+
+// The same cut as wave_radix for at most n <= 64 entries, one per lane (key k,
+// 0 for none; weight wt): each entry's stable rank in descending key order
+// (one pass over the others' keys), the weights in that order, one prefix
+// sum, and the key at the first position where it reaches target.  The
+// weights of a key's ties all precede the next smaller key, so that key is
+// the largest t whose weight at or above t reaches target.
+__device__ __forceinline__ uint32_t wave_cut64(uint32_t k, unsigned long long wt, unsigned long long target, int n,
+                                               WaveRowSm& ws) {
+  const int lane = threadIdx.x & 63;
+  ws.cut.k[lane] = k;
+  wave_sync();
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const uint32_t kj = ws.cut.k[j];
+    rank += (kj > k || (kj == k && j < lane)) ? 1 : 0;
+  }
+  if (lane < n) {
+    ws.cut.ks[rank] = k;
+    ws.cut.ws[rank] = wt;
+  }
+  wave_sync();
+  const uint32_t ks = lane < n ? ws.cut.ks[lane] : 0u;
+  const unsigned long long inc = wave_scan_u64(lane < n ? ws.cut.ws[lane] : 0ull);
+  const unsigned long long hit = __ballot(ks != 0u && inc >= target);
+  wave_sync();
+  return hit ? (uint32_t)__builtin_amdgcn_readlane((int)ks, __ffsll(hit) - 1) : 0u;
 }
 
 // Merge of one row by one wave: max, normaliser, filter threshold, kept list
@@ -1424,10 +1456,15 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
 #pragma unroll
     for (int r = 0; r < WR_EPL; ++r) {
       const int e = lane + 64 * r;
-      const uint64_t v = e < n ? ws.keys[e] : 0ull;
-      ek[r] = (uint32_t)(v >> 32);
-      ei[r] = (int)(uint32_t)v;
-      ew[r] = e < n ? exp(((double)key_val(ek[r]) - (double)m) * invT) : 0.0;
+      ek[r] = 0u;
+      ei[r] = 0;
+      ew[r] = 0.0;
+      if (64 * r < n) {
+        const uint64_t v = e < n ? ws.keys[e] : 0ull;
+        ek[r] = (uint32_t)(v >> 32);
+        ei[r] = (int)(uint32_t)v;
+        ew[r] = e < n ? exp(((double)key_val(ek[r]) - (double)m) * invT) : 0.0;
+      }
     }
     wave_sync();
     unsigned long long wt[WR_EPL];
@@ -1437,7 +1474,8 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       // k-th largest key among the candidates, ties kept
 #pragma unroll
       for (int r = 0; r < WR_EPL; ++r) wt[r] = ek[r] != 0u ? 1ull : 0ull;
-      const uint32_t tk = wave_radix(ek, wt, (unsigned long long)a.top_k, ws.hist);
+      const uint32_t tk = n <= 64 ? wave_cut64(ek[0], wt[0], (unsigned long long)a.top_k, n, ws)
+                                  : wave_radix(ek, wt, (unsigned long long)a.top_k, ws.hist);
       if (tk == 0u) {
         // fewer than k candidates: with every bound at -inf the row has fewer
         // than k finite logits and all are kept; otherwise undecided here
@@ -1459,12 +1497,18 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       uint32_t ekp[WR_EPL];
 #pragma unroll
       for (int r = 0; r < WR_EPL; ++r) ekp[r] = ek[r] >= tau ? ek[r] : 0u;
-      uint32_t tp = wave_walk(ekp, ew, snorm, a.top_p);
-      if (tp == 1u) {
+      uint32_t tp;
+      if (n <= 64) {
+        const unsigned long long w0 = ekp[0] != 0u ? (unsigned long long)(ew[0] / snorm * MASS_SCALE) : 0ull;
+        tp = wave_cut64(ekp[0], w0, (unsigned long long)(a.top_p * MASS_SCALE), n, ws);
+      } else {
+        tp = wave_walk(ekp, ew, snorm, a.top_p);
+        if (tp == 1u) {
 #pragma unroll
-        for (int r = 0; r < WR_EPL; ++r)
-          wt[r] = ekp[r] != 0u ? (unsigned long long)(ew[r] / snorm * MASS_SCALE) : 0ull;
-        tp = wave_radix(ekp, wt, (unsigned long long)(a.top_p * MASS_SCALE), ws.hist);
+          for (int r = 0; r < WR_EPL; ++r)
+            wt[r] = ekp[r] != 0u ? (unsigned long long)(ew[r] / snorm * MASS_SCALE) : 0ull;
+          tp = wave_radix(ekp, wt, (unsigned long long)(a.top_p * MASS_SCALE), ws.hist);
+        }
       }
       if (tp == 0u) {
         if (MODE == M_TOPP) return false;  // the nucleus reaches below the candidate window
@@ -1524,10 +1568,19 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
   return true;
 }
 
+// Kept lists read ahead at a sequence's finish: the first 64 entries of each
+// of up to SPEC_ROWS rows.
+constexpr int SPEC_ROWS = 16;
+struct SpecLists {
+  int32_t idx[SPEC_ROWS][64];
+  double prob[SPEC_ROWS][64];
+};
+
 struct RowKSm {
   union {
-    WaveRowSm w;  // wave-level merge
-    Smem blk;     // block-level merge, list copies and full-row draw
+    WaveRowSm w;     // wave-level merge
+    Smem blk;        // block-level merge, list copies and full-row draw
+    SpecLists spec;  // kept lists read with the sequence's records
   };
   double px[MAX_RPS];  // p or q of each row's drafted token
   int32_t rf[MAX_RPS];
@@ -1555,24 +1608,21 @@ __device__ int wave_list_sample(double u, const int32_t* pidx, const double* ppr
     w[r] = pp[r];
   }
   if (res) {
-    // position of each target token among the draft's kept indices: the
-    // number of draft indices below it (branch-free search, all entries'
-    // LDS reads in flight together)
-    int ps[WR_EPL];
+    // q of each target token: one pass over the draft's kept list (each entry
+    // read by all lanes at once)
+    double qv[WR_EPL];
 #pragma unroll
-    for (int r = 0; r < WR_EPL; ++r) ps[r] = 0;
-    for (int step = KEEP_CAP; step > 0; step >>= 1) {
-      int q[WR_EPL];
+    for (int r = 0; r < WR_EPL; ++r) qv[r] = 0.0;
+    for (int j = 0; j < nq; ++j) {
+      const int qi = qidx[j];
+      const double qp = qprob[j];
 #pragma unroll
-      for (int r = 0; r < WR_EPL; ++r) q[r] = qidx[max(min(ps[r] + step, nq) - 1, 0)];
-#pragma unroll
-      for (int r = 0; r < WR_EPL; ++r) ps[r] += (ps[r] + step <= nq && q[r] < pi[r]) ? step : 0;
+      for (int r = 0; r < WR_EPL; ++r) qv[r] = qi == pi[r] ? qp : qv[r];
     }
 #pragma unroll
     for (int r = 0; r < WR_EPL; ++r) {
       if (WR_EPL * lane + r < np) {
-        const double qv = (ps[r] < nq && qidx[ps[r]] == pi[r]) ? qprob[ps[r]] : 0.0;
-        const double d = pp[r] - qv;
+        const double d = pp[r] - qv[r];
         w[r] = d > 0.0 ? d : 0.0;
       }
     }
@@ -1647,8 +1697,20 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   if (!sm.fast) (void)row_finalize<DT, MODE, WG>(a, rl, xtok, sm.blk);
   if (!a.do_seq || !last_arrival(&a.seq_cnt[b], (uint32_t)rps, &sm.flag)) return;
 
-  // ---- the sequence: its rows' records, drafted tokens and uniforms (one round trip)
+  // ---- the sequence: its rows' records, drafted tokens and uniforms, and
+  // (up to SPEC_ROWS rows) the head of every row's kept list: one round trip
   const RowRec* rr = a.row + (size_t)b * rps;
+  const bool spec = FILT && rps <= SPEC_ROWS;
+  int32_t si[SPEC_ROWS / NWAVE];
+  double sp[SPEC_ROWS / NWAVE];
+  if (spec) {
+#pragma unroll
+    for (int i = 0; i < SPEC_ROWS / NWAVE; ++i) {
+      const size_t o = (size_t)(b * rps + min(w + NWAVE * i, rps - 1)) * KEEP_CAP + lane;
+      si[i] = ld_dev(&a.kidx[o]);
+      sp[i] = ld_dev(&a.kprob[o]);
+    }
+  }
   for (int j = t; j < rps; j += WG) {
     sm.px[j] = ld_dev(&rr[j].px);
     sm.rf[j] = ld_dev(&rr[j].flags);
@@ -1657,6 +1719,13 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   }
   if (t < K) sm.x[t] = a.X[(size_t)b * K + t];
   if (t <= K) sm.u[t] = a.U[(size_t)b * (K + 1) + t];
+  if (spec) {
+#pragma unroll
+    for (int i = 0; i < SPEC_ROWS / NWAVE; ++i) {
+      sm.spec.idx[w + NWAVE * i][lane] = si[i];
+      sm.spec.prob[w + NWAVE * i][lane] = sp[i];
+    }
+  }
   __syncthreads();
   if (w == 0) {
     // accept tests: draft i is accepted iff u_i * q_i(x_i) < p_i(x_i)
@@ -1702,22 +1771,36 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
       if (np < 0 || (res && nq < 0)) {
         big = 1;
       } else {
-        // the two kept lists (one round trip)
-        SmemSeq& q = sm.blk.q;
-        const size_t op = (size_t)(b * rps + n) * KEEP_CAP, oq = (size_t)(b * rps + jq) * KEEP_CAP;
-        for (int e = lane; e < np; e += 64) {
-          q.pidx[e] = ld_dev(&a.kidx[op + e]);
-          q.pprob[e] = ld_dev(&a.kprob[op + e]);
-        }
-        if (res) {
-          for (int e = lane; e < nq; e += 64) {
-            q.qidx[e] = ld_dev(&a.kidx[oq + e]);
-            q.qprob[e] = ld_dev(&a.kprob[oq + e]);
+        const int32_t *pidx, *qidx;
+        const double *pprob, *qprob;
+        if (spec && np <= 64 && nq <= 64) {
+          // read ahead with the records
+          pidx = sm.spec.idx[n];
+          pprob = sm.spec.prob[n];
+          qidx = sm.spec.idx[jq];
+          qprob = sm.spec.prob[jq];
+        } else {
+          // the two kept lists (one round trip)
+          SmemSeq& q = sm.blk.q;
+          const size_t op = (size_t)(b * rps + n) * KEEP_CAP, oq = (size_t)(b * rps + jq) * KEEP_CAP;
+          for (int e = lane; e < np; e += 64) {
+            q.pidx[e] = ld_dev(&a.kidx[op + e]);
+            q.pprob[e] = ld_dev(&a.kprob[op + e]);
           }
+          if (res) {
+            for (int e = lane; e < nq; e += 64) {
+              q.qidx[e] = ld_dev(&a.kidx[oq + e]);
+              q.qprob[e] = ld_dev(&a.kprob[oq + e]);
+            }
+          }
+          wave_sync();
+          pidx = q.pidx;
+          pprob = q.pprob;
+          qidx = q.qidx;
+          qprob = q.qprob;
         }
-        wave_sync();
         double Z;
-        const int tok = wave_list_sample((double)sm.u[K], q.pidx, q.pprob, np, q.qidx, q.qprob, nq, res, &Z);
+        const int tok = wave_list_sample((double)sm.u[K], pidx, pprob, np, qidx, qprob, nq, res, &Z);
         if (lane == 0) {
           ot[n] = tok;
           if (a.out_z) a.out_z[b] = Z;
