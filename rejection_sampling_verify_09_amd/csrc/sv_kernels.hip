@@ -1274,12 +1274,15 @@ __device__ __forceinline__ uint32_t wave_walk(const uint32_t (&ek)[WR_EPL], cons
 __device__ __forceinline__ uint32_t wave_cut64(uint32_t k, unsigned long long wt, unsigned long long target, int n,
                                                WaveRowSm& ws) {
   const int lane = threadIdx.x & 63;
-  ws.cut.k[lane] = k;
+  ws.cut.k[lane] = k;  // lanes from n on hold key 0 and never precede an entry
   wave_sync();
   int rank = 0;
-  for (int j = 0; j < n; ++j) {
-    const uint32_t kj = ws.cut.k[j];
-    rank += (kj > k || (kj == k && j < lane)) ? 1 : 0;
+#pragma unroll
+  for (int j0 = 0; j0 < 64; j0 += 4) {
+    const uint4 q = *reinterpret_cast<const uint4*>(&ws.cut.k[j0]);
+    const uint32_t kq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rank += (kq[i] > k || (kq[i] == k && j0 + i < lane)) ? 1 : 0;
   }
   if (lane < n) {
     ws.cut.ks[rank] = k;
@@ -1291,6 +1294,29 @@ __device__ __forceinline__ uint32_t wave_cut64(uint32_t k, unsigned long long wt
   const unsigned long long hit = __ballot(ks != 0u && inc >= target);
   wave_sync();
   return hit ? (uint32_t)__builtin_amdgcn_readlane((int)ks, __ffsll(hit) - 1) : 0u;
+}
+
+// The same cut for at most 64 entries, one per lane, by a walk down the
+// distinct keys (entries with equal keys have equal weights, so a key's
+// weight is its count times one of them, exactly): cheap when the cut lies
+// within the first few keys, as a nucleus usually does.  After WR_ITER keys
+// the rank cut takes over.
+__device__ __forceinline__ uint32_t wave_walk64(uint32_t k, unsigned long long wt, unsigned long long target, int n,
+                                                WaveRowSm& ws) {
+  unsigned long long run = 0;
+  uint32_t hi = 0xFFFFFFFFu;
+  for (int it = 0; it < WR_ITER; ++it) {
+    const uint32_t km = dpp_wave_umax(k < hi ? k : 0u);
+    if (km == 0u) return 0u;
+    const unsigned long long bm = __ballot(k == km);
+    const int src = __ffsll(bm) - 1;
+    const unsigned long long w = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(wt >> 32), src) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wt, src);
+    run += (unsigned long long)__popcll(bm) * w;
+    if (run >= target) return km;
+    hi = km;
+  }
+  return wave_cut64(k, wt, target, n, ws);
 }
 
 // Merge of one row by one wave: max, normaliser, filter threshold, kept list
@@ -1433,19 +1459,21 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
         }
       }
       wave_sync();
-      uint64_t xv[WR_EPL * UL];
-      bool xp[WR_EPL * UL];
+      int ne = 0;
 #pragma unroll
       for (int r = 0; r < WR_EPL; ++r) {
+        if (64 * r >= n) break;  // no units in this slot on any lane
+        uint64_t xv[UL];
+        bool xp[UL];
 #pragma unroll
         for (int i = 0; i < UL; ++i) {
           const float x = unit_elem<DT>(raw[r], i);
           const uint32_t key = ord_key(x);
-          xp[r * UL + i] = st[r] >= 0 && key >= lo && x > -INFINITY;
-          xv[r * UL + i] = ((uint64_t)key << 32) | (uint32_t)(st[r] + i);
+          xp[i] = st[r] >= 0 && key >= lo && x > -INFINITY;
+          xv[i] = ((uint64_t)key << 32) | (uint32_t)(st[r] + i);
         }
+        ne = wave_append(xv, xp, ws.keys, ne, KEEP_CAP);
       }
-      const int ne = wave_append(xv, xp, ws.keys, 0, KEEP_CAP);
       if (ne > KEEP_CAP) return false;
       n = ne;
       wave_sync();
@@ -1474,7 +1502,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       // k-th largest key among the candidates, ties kept
 #pragma unroll
       for (int r = 0; r < WR_EPL; ++r) wt[r] = ek[r] != 0u ? 1ull : 0ull;
-      const uint32_t tk = n <= 64 ? wave_cut64(ek[0], wt[0], (unsigned long long)a.top_k, n, ws)
+      const uint32_t tk = n <= 64 ? wave_walk64(ek[0], wt[0], (unsigned long long)a.top_k, n, ws)
                                   : wave_radix(ek, wt, (unsigned long long)a.top_k, ws.hist);
       if (tk == 0u) {
         // fewer than k candidates: with every bound at -inf the row has fewer
@@ -1500,7 +1528,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       uint32_t tp;
       if (n <= 64) {
         const unsigned long long w0 = ekp[0] != 0u ? (unsigned long long)(ew[0] / snorm * MASS_SCALE) : 0ull;
-        tp = wave_cut64(ekp[0], w0, (unsigned long long)(a.top_p * MASS_SCALE), n, ws);
+        tp = wave_walk64(ekp[0], w0, (unsigned long long)(a.top_p * MASS_SCALE), n, ws);
       } else {
         tp = wave_walk(ekp, ew, snorm, a.top_p);
         if (tp == 1u) {
