@@ -71,8 +71,10 @@ ProfSlot* prof_begin() {
   ProfSlot& sl = g_prof.slot[g_prof.next];
   g_prof.next = (g_prof.next + 1) % kProfSlots;
   if (prof_fold(sl) != SV_OK) return nullptr;
+  // timing only: no system-scope fence (cache writeback and invalidation)
+  // when an event is reached, which would add to the measured launches
   for (hipEvent_t& e : sl.ev)
-    if (!e && hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (!e && hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return &sl;
 }
 
