@@ -138,9 +138,35 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
                       float* out_probs, void* stream);
 
 /*
+ * sv_sample - draw one token per row from the row's filtered distribution:
+ * the drafting step that comes before verification (x ~ q, and q(x) for the
+ * accept test).  Page www.gsyq.cn/news/428210 section 3.1 (the small model
+ * samples the drafted tokens) and section 3.3 (the same sampling parameters
+ * as the target).  The draw is the one sv_spec_verify makes for its last
+ * token: inverse CDF in ascending vocabulary order, token = min{j : u*Z < C_j}
+ * over the filtered probabilities (in greedy mode the arg-max, lowest index on
+ * ties).
+ *
+ * logits      [rows, V] dtype   device
+ * uniforms    [rows] float32    device; U[0, 1), one per row
+ * out_tokens  [rows] int32      device; written with the drawn token, or -1
+ *                               for a row whose logits are all -inf
+ * out_prob    [rows] double     device, may be NULL; written with the
+ *                               filtered probability of the drawn token (1 in
+ *                               greedy mode; NaN for an all -inf row)
+ * temperature, top_k, top_p as for sv_spec_verify.  Errors as for
+ * sv_spec_verify with B = rows and K = 0 (rows < 0, V < 1 or V > SV_MAX_V:
+ * SV_ERR_SHAPE); rows == 0 returns SV_OK without touching any pointer.
+ */
+int sv_sample(const void* logits, const float* uniforms, float temperature,
+              int32_t top_k, float top_p, int32_t* out_tokens, double* out_prob,
+              int32_t rows, int32_t V, int32_t dtype, void* stream);
+
+/*
  * Launch timing for benchmarks.  Between sv_profile_start() and
- * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug call records
- * three HIP events on its own stream: before its streaming kernel (the pass
+ * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug / sv_sample
+ * call records three HIP events on its own stream: before its streaming
+ * kernel (the pass
  * that reads every logit once), after it, and after the call's last kernel.
  * sv_profile_stop() waits for the recorded events and returns the summed
  * durations in milliseconds of the streaming kernel and of the kernels that

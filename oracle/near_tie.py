@@ -118,3 +118,21 @@ def at_risk(ref: dict, u_b, eps: float = 1e-5) -> bool:
         if 0 <= jj < C.shape[0] and abs(C[jj] - t) <= eps * Z:
             return True
     return False
+
+
+def classify_sample(row: np.ndarray, temperature, top_k, top_p, u: float, got: int, ref: int,
+                    eps: float = 1e-5) -> str:
+    """Classify a device draw ``got`` against the oracle's ``ref`` for one row
+    (widened logits [V]) drawn with uniform ``u``: flagged when the oracle
+    itself could draw ``got`` with u moved by at most eps*Z, under top_p or
+    top_p moved by a relative eps (a kept set at its boundary)."""
+    if got == ref:
+        return MATCH
+    tps = [top_p]
+    if top_p < 1.0:
+        tps += [top_p * (1.0 - eps), min(1.0, top_p * (1.0 + eps))]
+    for tp in tps:
+        q = filtered_probs(np.asarray(row, dtype=np.float64)[None], temperature, top_k, tp)[0]
+        if not np.isnan(q).any() and _token_reachable(q, float(u), int(got), eps):
+            return FLAGGED
+    return FAIL

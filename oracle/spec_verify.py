@@ -53,6 +53,7 @@ __all__ = [
     "filtered_probs",
     "inverse_cdf",
     "sample_tokens",
+    "sample",
     "verify",
     "verify_one",
 ]
@@ -205,6 +206,42 @@ def sample_tokens(logits: np.ndarray, temperature, top_k, top_p, u: np.ndarray) 
 def _check_finite(x: np.ndarray):
     if np.isnan(x).any() or np.isposinf(x).any():
         raise ValueError("NaN or +inf logits are outside the defined input range")
+
+
+# ---------------------------------------------------------------------------
+# the drafting draw: x ~ q, and q(x)
+# ---------------------------------------------------------------------------
+def sample(logits: np.ndarray, temperature, top_k, top_p, u: np.ndarray, dtype: str = F32):
+    """Draw one token per row from the row's filtered distribution, as the
+    draft model does for each drafted position (page www.gsyq.cn/news/428210
+    section 3.1, step 1: the small model samples the tokens that the large
+    model then scores), with the sampling parameters shared with the target
+    (section 3.3).  The draw is ``inverse_cdf`` over ``filtered_probs``; the
+    probability reported is q(x) of the token drawn, the value the accept
+    test of ``verify`` divides by.
+
+    logits [N, V] (float32, or uint16 bf16 patterns with dtype="bf16");
+    u [N] uniforms (their float64 values).  Returns (tokens int64 [N],
+    prob float64 [N]); a row whose logits are all -inf has no distribution
+    and gives token -1 and prob NaN.
+    """
+    z = widen(logits, dtype)
+    if z.ndim != 2:
+        raise ValueError("logits must be [rows, V]")
+    _check_finite(z)
+    N = z.shape[0]
+    u = np.asarray(u, dtype=np.float64).reshape(-1)
+    if u.shape[0] != N:
+        raise ValueError("one uniform per row")
+    q = filtered_probs(z, temperature, top_k, top_p)
+    live = ~np.isnan(q).any(axis=1)
+    tok = np.full(N, -1, dtype=np.int64)
+    prob = np.full(N, np.nan)
+    if live.any():
+        t, _ = inverse_cdf(q[live], u[live])
+        tok[live] = t
+        prob[live] = q[live][np.arange(t.shape[0]), t]
+    return tok, prob
 
 
 def _draft_probs(draft, dtype, T, k, tp):

@@ -13,9 +13,10 @@ from ._lib import (  # noqa: F401
     profile_start,
     profile_stop,
     release,
+    sample,
     spec_verify,
     status_string,
 )
 
-__all__ = ["spec_verify", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
+__all__ = ["spec_verify", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
            "SpecVerifyError"]

@@ -42,6 +42,8 @@ def lib() -> ctypes.CDLL:
         L.sv_spec_verify_debug.restype = ctypes.c_int
         L.sv_filtered_probs.argtypes = [vp, i32, i32, i32, f32, i32, f32, vp, vp]
         L.sv_filtered_probs.restype = ctypes.c_int
+        L.sv_sample.argtypes = [vp, vp, f32, i32, f32, vp, vp, i32, i32, i32, vp]
+        L.sv_sample.restype = ctypes.c_int
         L.sv_release.argtypes = []
         L.sv_release.restype = ctypes.c_int
         L.sv_scratch_bytes.argtypes = [ctypes.c_int]
@@ -154,6 +156,32 @@ def filtered_probs(logits: torch.Tensor, temperature: float, top_k: int = 0, top
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_filtered_probs")
     return out
+
+
+def sample(logits: torch.Tensor, uniforms: torch.Tensor, temperature: float = 1.0, top_k: int = 0,
+           top_p: float = 1.0, out_tokens: torch.Tensor | None = None, out_prob: torch.Tensor | None = None,
+           with_prob: bool = True, stream=None):
+    """Draw one token per row of ``logits`` [rows, V] from its filtered
+    distribution with ``uniforms`` [rows] float32.  Returns (tokens [rows]
+    int32, the drawn tokens' probabilities [rows] float64 or None)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, V]")
+    rows, V = logits.shape
+    code = _dtype_code(logits)
+    if tuple(uniforms.shape) != (rows,):
+        raise ValueError("uniforms must be [rows]")
+    dev = logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((rows,), dtype=torch.int32, device=dev)
+    if with_prob and out_prob is None:
+        out_prob = torch.empty((rows,), dtype=torch.float64, device=dev)
+    pp = _dev(out_prob, "out_prob", torch.float64) if with_prob else None
+    st = lib().sv_sample(_dev(logits, "logits"), _dev(uniforms, "uniforms", torch.float32), float(temperature),
+                         int(top_k), float(top_p), _dev(out_tokens, "out_tokens", torch.int32), pp, rows, V, code,
+                         _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_sample")
+    return out_tokens, (out_prob if with_prob else None)
 
 
 def profile_start() -> None:

@@ -186,16 +186,19 @@ void set_scalars(Args& a, float T, int32_t top_k, float top_p) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// need_n: out_n is required (the sampler passes none).  out_px: probability
+// of each sequence's last drawn token under the row it was drawn from (the
+// sampler, K == 0).
 int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, int32_t top_k,
-                float top_p, int32_t* out_tok, int32_t* out_n, double* out_p, double* out_q, double* out_z,
-                int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
+                float top_p, int32_t* out_tok, int32_t* out_n, bool need_n, double* out_p, double* out_q,
+                double* out_z, double* out_px, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > MAX_V) return SV_ERR_SHAPE;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
   int st = check_params(T, top_k, top_p);
   if (st != SV_OK) return st;
   if (B == 0) return SV_OK;
   const int mode = pick_mode(T, top_k, top_p, V);
-  if (!tgt || !U || !out_tok || !out_n) return SV_ERR_NULL;
+  if (!tgt || !U || !out_tok || (need_n && !out_n)) return SV_ERR_NULL;
   if (K > 0 && !X) return SV_ERR_NULL;
   if (K > 0 && mode != M_GREEDY && !drf) return SV_ERR_NULL;
   const int esz = dtype == SV_BF16 ? 2 : 4;
@@ -226,6 +229,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.out_p = out_p;
   a.out_q = out_q;
   a.out_z = out_z;
+  a.out_px = out_px;
   a.out_probs = nullptr;
   a.B = B;
   a.K = K;
@@ -268,7 +272,7 @@ int sv_spec_verify(const void* target_logits, const void* draft_logits, const in
                    const float* uniforms, float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
                    int32_t* out_num_accepted, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
   return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, top_k, top_p, out_tokens,
-                     out_num_accepted, nullptr, nullptr, nullptr, B, K, V, dtype, stream);
+                     out_num_accepted, true, nullptr, nullptr, nullptr, nullptr, B, K, V, dtype, stream);
 }
 
 int sv_spec_verify_debug(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
@@ -276,7 +280,16 @@ int sv_spec_verify_debug(const void* target_logits, const void* draft_logits, co
                          int32_t* out_tokens, int32_t* out_num_accepted, double* out_p, double* out_q,
                          double* out_z, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
   return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, top_k, top_p, out_tokens,
-                     out_num_accepted, out_p, out_q, out_z, B, K, V, dtype, stream);
+                     out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream);
+}
+
+// The draw of a verification with no drafts: each row is a sequence of one
+// position whose only token is drawn from its own filtered distribution with
+// its own uniform.
+int sv_sample(const void* logits, const float* uniforms, float temperature, int32_t top_k, float top_p,
+              int32_t* out_tokens, double* out_prob, int32_t rows, int32_t V, int32_t dtype, void* stream) {
+  return verify_impl(logits, nullptr, nullptr, uniforms, temperature, top_k, top_p, out_tokens, nullptr, false,
+                     nullptr, nullptr, nullptr, out_prob, rows, 0, V, dtype, stream);
 }
 
 int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype, float temperature, int32_t top_k,

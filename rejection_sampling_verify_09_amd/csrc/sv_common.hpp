@@ -92,6 +92,7 @@ struct Args {
   double* out_p;
   double* out_q;
   double* out_z;
+  double* out_px;  // per sequence: probability of the last drawn token under the row it was drawn from
   float* out_probs;
   int32_t B, K, V, rps, nchunks, nsc, top_k, do_seq;
   float c2;        // log2(e) / T, the exp2 scale of the streaming pass

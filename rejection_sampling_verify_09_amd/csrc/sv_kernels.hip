@@ -1621,9 +1621,10 @@ struct RowKSm {
 
 // Final draw from kept lists by one wave (filtered rows): residual
 // max(0, p - q) over the target's kept tokens, or p itself (bonus, or an
-// empty residual); inverse CDF in ascending vocabulary order.
+// empty residual); inverse CDF in ascending vocabulary order.  *Zout gets the
+// total weight, *wout the drawn token's weight.
 __device__ int wave_list_sample(double u, const int32_t* pidx, const double* pprob, int np, const int32_t* qidx,
-                                const double* qprob, int nq, bool res, double* Zout) {
+                                const double* qprob, int nq, bool res, double* Zout, double* wout) {
   const int lane = threadIdx.x & 63;
   // entries WR_EPL * lane + r: each lane a contiguous run
   int pi[WR_EPL];
@@ -1673,6 +1674,7 @@ __device__ int wave_list_sample(double u, const int32_t* pidx, const double* ppr
   const double target = u * Z;
   double C = inc - ls;
   int first = INT_MAX, lastp = -1, tf = 0, tl = 0;
+  double wf = 0.0, wl = 0.0;
 #pragma unroll
   for (int r = 0; r < WR_EPL; ++r) {
     const int e = WR_EPL * lane + r;
@@ -1680,21 +1682,27 @@ __device__ int wave_list_sample(double u, const int32_t* pidx, const double* ppr
     if (e < np && w[r] > 0.0) {
       lastp = e;
       tl = pi[r];
+      wl = w[r];
       if (first == INT_MAX && target < C) {
         first = e;
         tf = pi[r];
+        wf = w[r];
       }
     }
   }
   const unsigned long long fm = __ballot(first != INT_MAX);
   int tok;
+  double wt = 0.0;
   if (fm) {
     tok = lane_bcast(tf, __ffsll(fm) - 1);
+    wt = lane_bcast(wf, __ffsll(fm) - 1);
   } else {
     const unsigned long long lm = __ballot(lastp >= 0);
     tok = lm ? lane_bcast(tl, 63 - __clzll(lm)) : 0;
+    wt = lm ? lane_bcast(wl, 63 - __clzll(lm)) : 0.0;
   }
   *Zout = Z;
+  *wout = wt;
   return tok;
 }
 
@@ -1780,16 +1788,18 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     }
     int big = 0;
     if (lane == 0) {
-      a.out_n[b] = n;
+      if (a.out_n) a.out_n[b] = n;
       SeqRec sr;
       sr.Z = 0.0;
       sr.n = n;
       sr.flags = n < 0 ? RF_BAD : 0;
       a.seq[b] = sr;
       if (n < 0 && a.out_z) a.out_z[b] = nanv;
+      if (n < 0 && a.out_px) a.out_px[b] = nanv;
       if (n >= 0 && MODE == M_GREEDY) {
         ot[n] = sm.arg[n];
         if (a.out_z) a.out_z[b] = 1.0;
+        if (a.out_px) a.out_px[b] = 1.0;
       }
     }
     if (FILT && n >= 0) {
@@ -1827,11 +1837,12 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
           qidx = q.qidx;
           qprob = q.qprob;
         }
-        double Z;
-        const int tok = wave_list_sample((double)sm.u[K], pidx, pprob, np, qidx, qprob, nq, res, &Z);
+        double Z, wtok;
+        const int tok = wave_list_sample((double)sm.u[K], pidx, pprob, np, qidx, qprob, nq, res, &Z, &wtok);
         if (lane == 0) {
           ot[n] = tok;
           if (a.out_z) a.out_z[b] = Z;
+          if (a.out_px) a.out_px[b] = res ? nanv : wtok;  // a bonus draw's weight is the kept probability
         }
       }
     }
@@ -1854,6 +1865,9 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     if (t == 0) {
       a.out_tok[(size_t)b * (K + 1) + n] = tok;
       if (a.out_z) a.out_z[b] = Z;
+      if (a.out_px)
+        a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll)
+                          : kept_prob<DT>(row_ptr(a, b * rps + n, ESZ), tok, load_row(&rr[n]), true, a.invT);
     }
   }
 }
@@ -1977,6 +1991,8 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   if (t == 0) {
     a.out_tok[(size_t)b * (K + 1) + n] = tok;
     if (a.out_z) a.out_z[b] = Z;
+    if (a.out_px)
+      a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll) : plain_weight<DT>(pr, qr, tok, P, Q, false, a.invT);
   }
 }
 

@@ -21,7 +21,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_filtered_probs", "sv_release", "sv_scratch_bytes",
+    for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_filtered_probs", "sv_sample", "sv_release", "sv_scratch_bytes",
               "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
         assert s in syms
 
@@ -95,6 +95,22 @@ def test_filtered_probs_validation():
     assert f(FAKE, 4, 10, 0, 0.0, 0, 1.0, FAKE, None) == L.SV_ERR_PARAM
     assert f(None, 4, 10, 0, 1.0, 0, 1.0, FAKE, None) == L.SV_ERR_NULL
     assert f(None, 0, 10, 0, 1.0, 0, 1.0, None, None) == L.SV_OK
+
+
+def test_sample_validation():
+    f = L.lib().sv_sample  # (logits, uniforms, T, top_k, top_p, out_tokens, out_prob, rows, V, dtype, stream)
+    assert f(FAKE, FAKE, 1.0, 0, 1.0, FAKE, None, -1, 10, 0, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, FAKE, 1.0, 0, 1.0, FAKE, None, 4, 0, 0, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, FAKE, 1.0, 0, 1.0, FAKE, None, 4, 2097153, 0, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, FAKE, 1.0, 0, 1.0, FAKE, None, 4, 10, 5, None) == L.SV_ERR_DTYPE
+    assert f(FAKE, FAKE, -1.0, 0, 1.0, FAKE, None, 4, 10, 0, None) == L.SV_ERR_PARAM
+    assert f(FAKE, FAKE, 1.0, 0, 2.0, FAKE, None, 4, 10, 0, None) == L.SV_ERR_PARAM
+    assert f(None, FAKE, 1.0, 0, 1.0, FAKE, None, 4, 10, 0, None) == L.SV_ERR_NULL
+    assert f(FAKE, None, 1.0, 0, 1.0, FAKE, None, 4, 10, 0, None) == L.SV_ERR_NULL
+    assert f(FAKE, FAKE, 1.0, 0, 1.0, None, None, 4, 10, 0, None) == L.SV_ERR_NULL
+    # greedy draws need neither draft logits nor drafted tokens, but the rest is validated
+    assert f(FAKE, None, 0.0, 0, 1.0, FAKE, None, 4, 10, 0, None) == L.SV_ERR_NULL
+    assert f(None, None, 1.0, 0, 1.0, None, None, 0, 10, 0, None) == L.SV_OK
 
 
 def test_profile_without_calls_reports_nothing():

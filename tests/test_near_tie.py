@@ -79,3 +79,16 @@ def test_top_p_boundary_near_tie():
     dev = np.array([0, alt])
     v, why = classify(tl, d, [0], np.array([0.2, 0.95], np.float32), 1.0, 0, tp, "f32", dev, 1)
     assert v == FLAGGED, why
+
+
+def test_sample_classifier():
+    from oracle import classify_sample
+    row = np.log(np.array([0.25, 0.25, 0.5]))  # running sums 0.25, 0.5, 1
+    # u*Z a hair below the boundary at 0.5: the next token is a near-tie
+    assert classify_sample(row, 1.0, 0, 1.0, 0.5 - 1e-9, 2, 1) == FLAGGED
+    # far from any boundary a different token is a failure
+    assert classify_sample(row, 1.0, 0, 1.0, 0.3, 2, 1) == FAIL
+    assert classify_sample(row, 1.0, 0, 1.0, 0.3, 1, 1) == MATCH
+    # top_p = 0.5 keeps token 2 alone: a token outside the kept set is never a near-tie
+    assert classify_sample(row, 1.0, 0, 0.5, 0.49, 2, 2) == MATCH
+    assert classify_sample(row, 1.0, 0, 0.5, 0.49, 0, 2) == FAIL

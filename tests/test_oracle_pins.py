@@ -150,3 +150,51 @@ def test_bf16_widening_is_exact():
     f = (bits.astype(np.uint32) << 16).view(np.float32)
     finite = np.isfinite(f)
     assert np.array_equal(w[finite], f[finite].astype(np.float64))
+
+
+# --- the drafting draw (oracle.sample) ---------------------------------------
+
+def test_sample_worked_case():
+    # logits 0, ln 2, ln 3, -inf at T = 1: q = 1/6, 2/6, 3/6, 0; the inverse
+    # CDF in vocabulary order splits [0, 1) at 1/6 and 1/2
+    z = np.array([[0.0, np.log(2.0), np.log(3.0), -np.inf]] * 5, dtype=np.float32)
+    u = np.array([0.0, 0.1, 0.2, 0.6, 0.999])
+    tok, prob = oracle.sample(z, 1.0, 0, 1.0, u)
+    assert tok.tolist() == [0, 0, 1, 2, 2]
+    want = np.array([1, 1, 2, 3, 3]) / 6.0
+    assert np.allclose(prob, want, rtol=1e-7, atol=0)
+
+
+def test_sample_follows_q_chi2():
+    from scipy import stats
+    rng = np.random.default_rng(11)
+    V, N = 12, 60000
+    row = rng.normal(0, 1.5, V).astype(np.float32)
+    for T, k, p in [(1.0, 0, 1.0), (0.7, 0, 0.9), (1.3, 5, 1.0)]:
+        q = oracle.filtered_probs(row[None].astype(np.float64), T, k, p)[0]
+        tok, prob = oracle.sample(np.repeat(row[None], N, 0), T, k, p, rng.random(N))
+        counts = np.bincount(tok, minlength=V)
+        assert np.all(counts[q == 0] == 0), "a token outside the kept set was drawn"
+        keep = q > 0
+        res = stats.chisquare(counts[keep], q[keep] / q[keep].sum() * N)
+        assert res.pvalue > 1e-4, (T, k, p, res.pvalue)
+        assert np.allclose(prob, q[tok], rtol=0, atol=0)
+
+
+def test_sample_agrees_with_verify_without_drafts():
+    rng = np.random.default_rng(12)
+    N, V = 200, 40
+    z = rng.normal(0, 2, (N, V)).astype(np.float32)
+    u = rng.random((N, 1), dtype=np.float32)
+    for T, k, p in [(1.0, 0, 1.0), (0.8, 7, 0.95), (0.0, 0, 1.0)]:
+        tok, prob = oracle.sample(z, T, k, p, u[:, 0])
+        vt, n = oracle.verify(z[:, None, :], np.zeros((N, 0, V), np.float32), np.zeros((N, 0), int), u, T, k, p)
+        assert np.all(n == 0)
+        assert np.array_equal(tok, vt[:, 0])
+
+
+def test_sample_greedy_and_dead_rows():
+    z = np.array([[1.0, 3.0, 3.0, -1.0], [-np.inf] * 4, [0.5, -np.inf, 0.5, 0.5]], dtype=np.float32)
+    tok, prob = oracle.sample(z, 0.0, 0, 1.0, np.array([0.99, 0.5, 0.3]))
+    assert tok.tolist() == [1, -1, 0]
+    assert prob[0] == 1.0 and np.isnan(prob[1]) and prob[2] == 1.0
