@@ -1,12 +1,16 @@
 """Benchmark of the speculative-sampling verification step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --sampler [--steps K] [--warmup W] [--workload NAME]
 
 One step = one sv_spec_verify call (the whole hot path: streaming pass,
 filter thresholds, accept tests, first-rejection scan, final draw) over one
 batch whose logits are already resident in HBM.  The input batch is rotated
 over several device copies whose total exceeds the 256 MB last-level cache,
 so every step reads its logits from HBM.  Prints one JSON line.
+
+With --sampler, one step is one sv_sample call (the drafting draw: x ~ q and
+q(x)) over the workload's B*K draft rows, with their draft uniforms.
 
 The CPU-baseline leg times the fp64 oracle (test infrastructure) on a bounded
 sample of the same workload; it is a reported baseline, not the target.
@@ -47,10 +51,11 @@ def load_draft_tokens(name: str, B: int, K: int):
     return x
 
 
-def measured_traffic(workload: str):
+def measured_traffic(key: str):
     """HBM bytes per launch of the streaming kernel from the committed counter
-    summary, or None when the summary is absent or predates the kernel source."""
-    path = os.path.join(PROFILES, f"traffic_stream_kernel_{workload}.md")
+    summary for ``key`` (the workload name, "sample-" + name for the draft
+    draw), or None when the summary is absent or predates the kernel source."""
+    path = os.path.join(PROFILES, f"traffic_stream_kernel_{key}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -85,6 +90,100 @@ def cpu_baseline(w, d, x, budget_s: float):
                        f"fp64 NumPy, single thread, {el:.1f} s", tokens_per_s=toks / el)
 
 
+def cpu_baseline_sample(w, rows, u, budget_s: float):
+    """Time the fp64 oracle's draw on the draft rows until about budget_s."""
+    import oracle
+
+    t0 = time.perf_counter()
+    n_done = 0
+    while True:
+        oracle.sample(rows, w.temperature, w.top_k, w.top_p, u.astype("float64"), w.dtype)
+        n_done += rows.shape[0]
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=n_done / el, unit="rows/s", cores=1, kind="oracle",
+                sample=f"{n_done // rows.shape[0]} x the {rows.shape[0]} draft rows of {w.name}, fp64 NumPy, "
+                       f"single thread, {el:.1f} s")
+
+
+def run_sampler(args, w, d):
+    """The drafting draw over the workload's B*K draft rows."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_09_amd import profile_start, profile_stop, sample
+
+    rows_np = d["draft"].reshape(w.B * w.K, w.V)
+    u_np = d["draft_u"].reshape(-1).astype(np.float32)
+    n_rows = rows_np.shape[0]
+    esz = 2 if w.dtype == "bf16" else 4
+    bytes_per_step = n_rows * w.V * esz
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    L0 = dev(rows_np)
+    R = args.copies or max(3, -(-640_000_000 // bytes_per_step))
+    Ls = [L0] + [L0.clone() for _ in range(R - 1)]
+    U = torch.from_numpy(u_np).cuda()
+    out_t = torch.empty((n_rows,), dtype=torch.int32, device="cuda")
+    out_p = torch.empty((n_rows,), dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        sample(Ls[i % R], U, w.temperature, w.top_k, w.top_p, out_tokens=out_t, out_prob=out_p)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    profile_start()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = profile_stop()
+    stream_ms = prof["stream_kernel_ms"] / max(1, prof["calls"])
+    other_ms = prof["other_kernels_ms"] / max(1, prof["calls"])
+    achieved = bytes_per_step / (stream_ms / 1e3) / 1e9
+    result = {
+        "metric": f"draft-draw rows/s + % HBM peak at {n_rows} rows V={w.V} {w.dtype}",
+        "value": n_rows / (ms_per_step / 1e3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded draft logits of the workload's shape; no model weights)",
+        "config": {"workload": f"draft rows of {w.name}", "rows": n_rows, "V": w.V, "logits": w.dtype,
+                   "temperature": w.temperature, "top_k": w.top_k, "top_p": w.top_p, "input_copies": R,
+                   "logit_bytes_per_step": bytes_per_step},
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("sample-" + w.name),
+            "kernel": "stream_kernel", "kernel_ms": stream_ms, "other_kernels_ms": other_ms,
+            "timed_calls": prof["calls"],
+            "step_frac": bytes_per_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_sample(w, rows_np, u_np, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +195,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--sampler", action="store_true",
+                    help="measure the drafting draw (sv_sample) over the workload's draft rows instead")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -130,6 +231,9 @@ def main():
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
     d = make_inputs(w)
+    if args.sampler:
+        run_sampler(args, w, d)
+        return
     x = load_draft_tokens(name, w.B, w.K)
 
     def dev(a):
