@@ -122,6 +122,27 @@ int sv_spec_verify_debug(const void* target_logits, const void* draft_logits,
                          void* stream);
 
 /*
+ * sv_spec_verify_dt - sv_spec_verify (with the outputs of
+ * sv_spec_verify_debug) for drafts that were sampled at their own
+ * temperature draft_temperature (page www.2kiu.com/news/5895634 section 7:
+ * a lower draft temperature such as 0.5 makes the drafts more certain).  The
+ * draft rows' q is then the filtered distribution at draft_temperature, with
+ * the shared top_k and top_p: each draft is tested against the q it was drawn
+ * from, so the output still follows p.  In greedy mode (temperature == 0)
+ * draft_temperature is not used; otherwise it must be a valid temperature
+ * above 0 (SV_ERR_PARAM).  With draft_temperature == temperature the results
+ * equal sv_spec_verify's.
+ */
+int sv_spec_verify_dt(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      float temperature, float draft_temperature,
+                      int32_t top_k, float top_p,
+                      int32_t* out_tokens, int32_t* out_num_accepted,
+                      double* out_p, double* out_q, double* out_z,
+                      int32_t B, int32_t K, int32_t V, int32_t dtype,
+                      void* stream);
+
+/*
  * sv_filtered_probs - the filtered distribution of every row: temperature,
  * then top-k, then top-p, then the softmax over the kept tokens (page
  * www.gsyq.cn/news/428210 section 3.3 for the parameters; the distribution
@@ -164,16 +185,16 @@ int sv_sample(const void* logits, const float* uniforms, float temperature,
 
 /*
  * Launch timing for benchmarks.  Between sv_profile_start() and
- * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug / sv_sample
- * call records three HIP events on its own stream: before its streaming
- * kernel (the pass
- * that reads every logit once), after it, and after the call's last kernel.
- * sv_profile_stop() waits for the recorded events and returns the summed
- * durations in milliseconds of the streaming kernel and of the kernels that
- * follow it (row merge, sequence finalisation, full-row draw), and the number
- * of calls timed.  Any output pointer may be NULL.  Timing is host-global (not
- * per device); it adds one event record per kernel boundary to each call.
- * Returns SV_ERR_HIP if an event could not be created, recorded or read.
+ * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug /
+ * sv_spec_verify_dt / sv_sample call records three HIP events on its own
+ * stream: before its streaming kernel (the pass that reads every logit once),
+ * after it, and after the call's last kernel.  sv_profile_stop() waits for
+ * the recorded events and returns the summed durations in milliseconds of the
+ * streaming kernel and of the kernels that follow it (row merge, sequence
+ * finalisation, full-row draw), and the number of calls timed.  Any output
+ * pointer may be NULL.  Timing is host-global (not per device); it adds one
+ * event record per kernel boundary to each call.  Returns SV_ERR_HIP if an
+ * event could not be created, recorded or read.
  */
 int sv_profile_start(void);
 int sv_profile_stop(double* stream_kernel_ms, double* other_kernels_ms, int64_t* calls);

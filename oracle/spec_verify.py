@@ -260,18 +260,34 @@ def _draft_probs(draft, dtype, T, k, tp):
     return Q
 
 
+def _draft_temperature(T, draft_temperature, k, tp):
+    """The temperature of the draft rows: the target's unless the drafts were
+    sampled at their own (page www.2kiu.com/news/5895634 section 7: a lower
+    draft temperature such as 0.5).  The drafts are then verified against
+    the q they were drawn from, which keeps the rule lossless.  Ignored in
+    greedy mode; otherwise it must be a valid temperature above 0."""
+    if draft_temperature is None or T == 0.0:
+        return T
+    Td = _check_params(draft_temperature, k, tp)[0]
+    if not Td > 0.0:
+        raise ValueError("the draft temperature must be > 0 when the target's is")
+    return Td
+
+
 def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
-           dtype: str = F32, block: int | None = None, diag: bool = False):
+           dtype: str = F32, block: int | None = None, diag: bool = False, draft_temperature=None):
     """Run verification for a batch.
 
     target: [B, K+1, V] logits (float32, or uint16 bf16 patterns when
     dtype == "bf16"); draft: [B, K, V]; draft_tokens: [B, K] ints;
-    uniforms: float32 [B, K+1].
+    uniforms: float32 [B, K+1].  draft_temperature: the temperature the
+    drafts were sampled at, when it differs from the target's.
 
     Returns (out_tokens int32 [B, K+1], out_num_accepted int32 [B]) and, when
     ``diag``, a dict with p(x_i), q(x_i) float64 [B, K] and Z float64 [B].
     """
     T, k, tp = _check_params(temperature, top_k, top_p)
+    Td = _draft_temperature(T, draft_temperature, k, tp)
     target = np.asarray(target)
     draft = np.asarray(draft)
     X = np.asarray(draft_tokens).astype(np.int64)
@@ -298,7 +314,7 @@ def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
         _check_finite(t64)
         P = filtered_probs(t64.reshape(nb * (K + 1), V), T, k, tp).reshape(nb, K + 1, V)
         del t64
-        Q = _draft_probs(draft[s:e], dtype, T, k, tp)
+        Q = _draft_probs(draft[s:e], dtype, Td, k, tp)
         x = X[s:e]
         u = U[s:e].astype(np.float64)
         # bad sequences: a row with no distribution, or a drafted token out of range
@@ -345,7 +361,7 @@ def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
     return out_tok, out_n
 
 
-def verify_one(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype: str = F32):
+def verify_one(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype: str = F32, draft_temperature=None):
     """All intermediate values for one sequence (used to classify a mismatch).
 
     Returns a dict: P [K+1, V], Q [K, V], px, qx, accept [K], n, w [V],
@@ -353,12 +369,13 @@ def verify_one(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype: st
     """
     out_tok, out_n = verify(target_b[None], draft_b[None], np.asarray(x_b)[None],
                             np.asarray(u_b, dtype=np.float32)[None],
-                            temperature, top_k, top_p, dtype=dtype)
+                            temperature, top_k, top_p, dtype=dtype, draft_temperature=draft_temperature)
     T, k, tp = _check_params(temperature, top_k, top_p)
+    Td = _draft_temperature(T, draft_temperature, k, tp)
     K = draft_b.shape[0]
     V = target_b.shape[-1]
     P = filtered_probs(widen(target_b, dtype), T, k, tp)
-    Q = _draft_probs(np.asarray(draft_b)[None], dtype, T, k, tp)[0]
+    Q = _draft_probs(np.asarray(draft_b)[None], dtype, Td, k, tp)[0]
     x = np.clip(np.asarray(x_b, dtype=np.int64), 0, V - 1)
     u = np.asarray(u_b, dtype=np.float32).astype(np.float64)
     px = P[np.arange(K), x]

@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
         L.sv_filtered_probs.restype = ctypes.c_int
         L.sv_sample.argtypes = [vp, vp, f32, i32, f32, vp, vp, i32, i32, i32, vp]
         L.sv_sample.restype = ctypes.c_int
+        L.sv_spec_verify_dt.argtypes = [vp, vp, vp, vp, f32, f32, i32, f32, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        L.sv_spec_verify_dt.restype = ctypes.c_int
         L.sv_release.argtypes = []
         L.sv_release.restype = ctypes.c_int
         L.sv_scratch_bytes.argtypes = [ctypes.c_int]
@@ -92,13 +94,15 @@ def _stream(stream) -> int:
 def spec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor | None, draft_tokens: torch.Tensor,
                 uniforms: torch.Tensor, temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
                 out_tokens: torch.Tensor | None = None, out_num_accepted: torch.Tensor | None = None,
-                stream=None, debug: bool = False):
+                stream=None, debug: bool = False, draft_temperature: float | None = None):
     """Verify one round of drafted tokens on the GPU.
 
     target_logits [B, K+1, V] and draft_logits [B, K, V] (float32 or
     bfloat16, same dtype); draft_tokens [B, K] int32; uniforms [B, K+1]
-    float32.  Returns (out_tokens [B, K+1] int32, out_num_accepted [B] int32),
-    plus a dict of p(x), q(x) and Z when ``debug``.
+    float32.  draft_temperature: the temperature the drafts were sampled at,
+    when it differs from the target's.  Returns (out_tokens [B, K+1] int32,
+    out_num_accepted [B] int32), plus a dict of p(x), q(x) and Z when
+    ``debug``.
     """
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, K+1, V]")
@@ -126,6 +130,20 @@ def spec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor | None, 
     op = _dev(out_tokens, "out_tokens", torch.int32)
     onp = _dev(out_num_accepted, "out_num_accepted", torch.int32)
     s = _stream(stream)
+    if draft_temperature is not None:
+        out_p = torch.empty((B, K), dtype=torch.float64, device=dev) if debug else None
+        out_q = torch.empty((B, K), dtype=torch.float64, device=dev) if debug else None
+        out_z = torch.empty((B,), dtype=torch.float64, device=dev) if debug else None
+        st = lib().sv_spec_verify_dt(tp, dp, xp, up, float(temperature), float(draft_temperature), int(top_k),
+                                     float(top_p), op, onp,
+                                     out_p.data_ptr() if debug and K > 0 else None,
+                                     out_q.data_ptr() if debug and K > 0 else None,
+                                     out_z.data_ptr() if debug else None, B, K, V, code, s)
+        if st != SV_OK:
+            raise SpecVerifyError(st, "sv_spec_verify_dt")
+        if debug:
+            return out_tokens, out_num_accepted, dict(p=out_p, q=out_q, z=out_z)
+        return out_tokens, out_num_accepted
     if debug:
         out_p = torch.empty((B, K), dtype=torch.float64, device=dev)
         out_q = torch.empty((B, K), dtype=torch.float64, device=dev)

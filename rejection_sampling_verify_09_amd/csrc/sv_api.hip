@@ -170,18 +170,25 @@ int pick_mode(float T, int32_t top_k, float top_p, int32_t V) {
   return k && p ? M_TOPKP : k ? M_TOPK : p ? M_TOPP : M_PLAIN;
 }
 
-void set_scalars(Args& a, float T, int32_t top_k, float top_p) {
+void temp_scalars(float T, float* c2, float* win, double* invT) {
+  if (T > 0.0f) {
+    *invT = 1.0 / (double)T;
+    *c2 = (float)(1.4426950408889634074 / (double)T);
+    *win = TOPP_WINDOW_Z * T;
+  } else {
+    *invT = 0.0;
+    *c2 = 0.0f;
+    *win = 0.0f;
+  }
+}
+
+// Td: the draft rows' temperature (the target's unless the drafts were
+// sampled at another one).
+void set_scalars(Args& a, float T, int32_t top_k, float top_p, float Td) {
   a.top_k = top_k;
   a.top_p = (double)top_p;
-  if (T > 0.0f) {
-    a.invT = 1.0 / (double)T;
-    a.c2 = (float)(1.4426950408889634074 / (double)T);
-    a.win = TOPP_WINDOW_Z * T;
-  } else {
-    a.invT = 0.0;
-    a.c2 = 0.0f;
-    a.win = 0.0f;
-  }
+  temp_scalars(T, &a.c2, &a.win, &a.invT);
+  temp_scalars(T > 0.0f ? Td : T, &a.c2d, &a.wind, &a.invTd);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -189,13 +196,16 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // need_n: out_n is required (the sampler passes none).  out_px: probability
 // of each sequence's last drawn token under the row it was drawn from (the
 // sampler, K == 0).
-int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, int32_t top_k,
-                float top_p, int32_t* out_tok, int32_t* out_n, bool need_n, double* out_p, double* out_q,
-                double* out_z, double* out_px, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
+int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, float Td,
+                int32_t top_k, float top_p, int32_t* out_tok, int32_t* out_n, bool need_n, double* out_p,
+                double* out_q, double* out_z, double* out_px, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                void* stream) {
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > MAX_V) return SV_ERR_SHAPE;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
   int st = check_params(T, top_k, top_p);
   if (st != SV_OK) return st;
+  // at T > 0 the draft temperature must be a valid temperature above 0
+  if (T > 0.0f && (check_params(Td, top_k, top_p) != SV_OK || !(Td > 0.0f))) return SV_ERR_PARAM;
   if (B == 0) return SV_OK;
   const int mode = pick_mode(T, top_k, top_p, V);
   if (!tgt || !U || !out_tok || (need_n && !out_n)) return SV_ERR_NULL;
@@ -238,7 +248,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
   a.do_seq = 1;
-  set_scalars(a, T, top_k, top_p);
+  set_scalars(a, T, top_k, top_p, Td);
   bind_scratch(a, base, L);
 
   const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
@@ -271,16 +281,24 @@ extern "C" {
 int sv_spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                    const float* uniforms, float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
                    int32_t* out_num_accepted, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
-  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, top_k, top_p, out_tokens,
-                     out_num_accepted, true, nullptr, nullptr, nullptr, nullptr, B, K, V, dtype, stream);
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, temperature, top_k, top_p,
+                     out_tokens, out_num_accepted, true, nullptr, nullptr, nullptr, nullptr, B, K, V, dtype, stream);
 }
 
 int sv_spec_verify_debug(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                          const float* uniforms, float temperature, int32_t top_k, float top_p,
                          int32_t* out_tokens, int32_t* out_num_accepted, double* out_p, double* out_q,
                          double* out_z, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
-  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, top_k, top_p, out_tokens,
-                     out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream);
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, temperature, top_k, top_p,
+                     out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream);
+}
+
+int sv_spec_verify_dt(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                      const float* uniforms, float temperature, float draft_temperature, int32_t top_k, float top_p,
+                      int32_t* out_tokens, int32_t* out_num_accepted, double* out_p, double* out_q, double* out_z,
+                      int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, draft_temperature, top_k,
+                     top_p, out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream);
 }
 
 // The draw of a verification with no drafts: each row is a sequence of one
@@ -288,8 +306,8 @@ int sv_spec_verify_debug(const void* target_logits, const void* draft_logits, co
 // its own uniform.
 int sv_sample(const void* logits, const float* uniforms, float temperature, int32_t top_k, float top_p,
               int32_t* out_tokens, double* out_prob, int32_t rows, int32_t V, int32_t dtype, void* stream) {
-  return verify_impl(logits, nullptr, nullptr, uniforms, temperature, top_k, top_p, out_tokens, nullptr, false,
-                     nullptr, nullptr, nullptr, out_prob, rows, 0, V, dtype, stream);
+  return verify_impl(logits, nullptr, nullptr, uniforms, temperature, temperature, top_k, top_p, out_tokens, nullptr,
+                     false, nullptr, nullptr, nullptr, out_prob, rows, 0, V, dtype, stream);
 }
 
 int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype, float temperature, int32_t top_k,
@@ -326,7 +344,7 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
   a.do_seq = 0;
-  set_scalars(a, temperature, top_k, top_p);
+  set_scalars(a, temperature, top_k, top_p, temperature);
   bind_scratch(a, base, L);
   const bool vec = aligned16(logits) && ((int64_t)V * esz) % 16 == 0;
   a.ulen = vec ? 16 / esz : 1;

@@ -98,6 +98,8 @@ struct Args {
   float c2;        // log2(e) / T, the exp2 scale of the streaming pass
   float win;       // top-p candidate window in logit units
   double invT;     // 1 / T in double
+  float c2d, wind;  // the same for the draft rows (their own temperature)
+  double invTd;
   double top_p;
   ChunkRec* chunk;
   uint64_t* cand;
@@ -457,6 +459,19 @@ __device__ __forceinline__ bool last_arrival(uint32_t* cnt, uint32_t total, int*
   }
   __syncthreads();
   return *flag != 0;
+}
+
+// Temperature-derived scalars of row rl: the draft rows' own (a draft
+// sampled at its own temperature is verified against that q), the target's
+// for every other row.
+struct RowT {
+  float c2;     // log2(e) / T
+  float win;    // top-p candidate window in logit units
+  double invT;  // 1 / T
+};
+__device__ __forceinline__ RowT row_temp(const Args& a, int rl) {
+  const int j = rl - udiv(rl, a.drps) * a.rps;
+  return j > a.K ? RowT{a.c2d, a.wind, a.invTd} : RowT{a.c2, a.win, a.invT};
 }
 
 // Row rl of the verification (per sequence: K+1 target rows, then K draft

@@ -59,6 +59,7 @@ __device__ __forceinline__ void build_exp_tab(double* tab) {
 
 struct DrawRow {
   double snorm;
+  double invT;
   float m;
   uint32_t tau;
 };
@@ -364,13 +365,14 @@ template <int DT, int MODE, int BS>
 __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRec& rr, Smem& sm) {
   const int t = threadIdx.x, nch = a.nchunks;
   const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
-  const double invT = a.invT;
+  const RowT rt = row_temp(a, rl);
+  const double invT = rt.invT;
 
   // Every finite logit with key >= lo is among the candidates: each chunk
   // emitted all of its finite logits at or above its own bound, and lo is the
   // largest bound (and, for top-p, at least the window below the row max).
   uint32_t lo = block_max_u<BS / 64>(t < nch ? sm.r.cb[t] : 0u, sm.red);
-  if (MODE == M_TOPP) lo = max(lo, ord_key(m - a.win));
+  if (MODE == M_TOPP) lo = max(lo, ord_key(m - rt.win));
   int ncand_total;
   const int my_off = block_excl_scan_i<BS / 64>(t < nch ? sm.r.cn[t] : 0, sm.red, &ncand_total);
   if (t < nch) sm.r.off[t] = my_off;
@@ -605,7 +607,7 @@ __device__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
   bool bad = !(m > -INFINITY && m < INFINITY);
   if (MODE == M_PLAIN || MODE == M_TOPP) {
     const float qm = t < nch ? sm.r.cm[t] : -INFINITY;
-    const double s = chunk_weight(sm.r.cs[t], qm, m, a.c2, a.invT);
+    const double s = chunk_weight(sm.r.cs[t], qm, m, row_temp(a, rl).c2, row_temp(a, rl).invT);
     const double S = block_sum<BS / 64>(s, sm.red);
     rr.S = S;
     if (!(S > 0.0 && S < INFINITY)) bad = true;
@@ -622,7 +624,8 @@ __device__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
       rr.px = xtok == rr.arg ? 1.0 : 0.0;
     } else {
       const float lx = sm.lx;
-      if (ord_key(lx) >= rr.tau) rr.px = exp(((double)lx - (double)m) * a.invT) / (MODE == M_PLAIN ? rr.S : rr.S_kept);
+      if (ord_key(lx) >= rr.tau)
+        rr.px = exp(((double)lx - (double)m) * row_temp(a, rl).invT) / (MODE == M_PLAIN ? rr.S : rr.S_kept);
     }
   }
   if (bad) rr.flags |= RF_BAD;
@@ -650,12 +653,13 @@ __device__ __forceinline__ double kept_prob(const char* rp, int j, const RowRec&
 // (it shares a kernel, and so a register allocation, with the streaming pass).
 template <int DT>
 __device__ __forceinline__ double draw_weight(const char* pr, const char* qr, int j, const DrawRow* dr, bool use_res,
-                                              double invT, const double* tab) {
+                                              const double* tab) {
   const float xp = load_elem<DT>(pr, j);
-  double w = ord_key(xp) >= dr[0].tau ? exp_tab(((double)xp - (double)dr[0].m) * invT, tab) / dr[0].snorm : 0.0;
+  double w = ord_key(xp) >= dr[0].tau ? exp_tab(((double)xp - (double)dr[0].m) * dr[0].invT, tab) / dr[0].snorm : 0.0;
   if (use_res) {
     const float xq = load_elem<DT>(qr, j);
-    const double q = ord_key(xq) >= dr[1].tau ? exp_tab(((double)xq - (double)dr[1].m) * invT, tab) / dr[1].snorm : 0.0;
+    const double q =
+        ord_key(xq) >= dr[1].tau ? exp_tab(((double)xq - (double)dr[1].m) * dr[1].invT, tab) / dr[1].snorm : 0.0;
     const double d = w - q;
     w = d > 0.0 ? d : 0.0;
   }
@@ -666,7 +670,6 @@ template <int DT, int BS>
 __device__ int full_row_sample(const Args& a, double u, const char* pr, const char* qr, bool res, Smem& sm,
                                double* Zout) {
   const int t = threadIdx.x, V = a.V;
-  const double invT = a.invT;
   const DrawRow* dr = sm.dr;
   build_exp_tab(sm.etab);
   bool use_res = res;
@@ -681,7 +684,7 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const ch
       for (int e = 0; e < 8; ++e) {
         const int j = base + t * 8 + e;
         if (j < V) {
-          const double w = draw_weight<DT>(pr, qr, j, dr, use_res, invT, sm.etab);
+          const double w = draw_weight<DT>(pr, qr, j, dr, use_res, sm.etab);
           ts += w;
           if (w > 0.0) lastpos = j;
         }
@@ -700,7 +703,7 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const ch
 #pragma unroll 1
     for (int e = 0; e < 8; ++e) {
       const int j = base + t * 8 + e;
-      if (j < V) ts += draw_weight<DT>(pr, qr, j, dr, use_res, invT, sm.etab);
+      if (j < V) ts += draw_weight<DT>(pr, qr, j, dr, use_res, sm.etab);
     }
     const double tile = block_sum<BS / 64>(ts, sm.red);
     if (run + tile > target) {
@@ -715,7 +718,7 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const ch
       for (int e = 0; e < 8; ++e) {
         const int j = base + t * 8 + e;
         if (j < V) {
-          const double w = draw_weight<DT>(pr, qr, j, dr, use_res, invT, sm.etab);
+          const double w = draw_weight<DT>(pr, qr, j, dr, use_res, sm.etab);
           C += w;
           if (w > 0.0) {
             lastp = j;
@@ -734,9 +737,10 @@ __device__ int full_row_sample(const Args& a, double u, const char* pr, const ch
 }
 
 // Parameters of a row for the full-row draw, into sm.dr[slot].
-__device__ __forceinline__ void set_draw_row(const RowRec* r, bool filtered, int slot, Smem& sm) {
+__device__ __forceinline__ void set_draw_row(const RowRec* r, bool filtered, int slot, double invT, Smem& sm) {
   __syncthreads();
   if (threadIdx.x == 0) {
+    sm.dr[slot].invT = invT;
     sm.dr[slot].m = ld_dev(&r->m);
     sm.dr[slot].tau = ld_dev(&r->tau);
     sm.dr[slot].snorm = filtered ? ld_dev(&r->S_kept) : ld_dev(&r->S);
@@ -822,7 +826,7 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
     float thr;
     if (MODE == M_TOPP) {
       // window below the chunk max (which is <= the row max)
-      bound = ord_key(mc - a.win);
+      bound = ord_key(mc - row_temp(a, rl).win);
     } else {
       // the k-th largest of the 256 thread maxima is <= the row's k-th largest
       // logit (for k > 256 no bound follows: every finite logit qualifies)
@@ -930,8 +934,9 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, false>())) stream_ke
     // in the record's convention (chunk_weight)
     double acc = 0.0;
     if (mc > -INFINITY) {
-      const double c2 = (double)a.c2;
-      const float Mi = __builtin_ceilf(mc * a.c2);
+      const float c2f = row_temp(a, rl).c2;
+      const double c2 = (double)c2f;
+      const float Mi = __builtin_ceilf(mc * c2f);
       const double off = Mi < INFINITY ? (double)Mi : (double)mc * c2;
 #pragma unroll
       for (int k = 0; k < EPT; ++k)
@@ -1023,7 +1028,7 @@ __device__ __forceinline__ void stream_vec_body(const Args& a, int item, int rl,
   constexpr int EPV = ElemT<DT>::EPV, NV = EPT / EPV;
   constexpr bool SUM = MODE == M_PLAIN || MODE == M_TOPP;
   const int t = threadIdx.x, w = t >> 6;
-  const float c2 = a.c2;
+  const float c2 = row_temp(a, rl).c2;
 
   float v[EPT], um[NV];
   const int nvec = cn / EPV;  // vectors in the chunk (the row's last chunk has fewer than WG * NV)
@@ -1330,7 +1335,8 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
   const int lane = threadIdx.x & 63, nch = a.nchunks;
   const ChunkRec* cr = a.chunk + (size_t)rl * nch;
   const bool hx = xtok >= 0 && xtok < a.V;
-  const double invT = a.invT;
+  const RowT rt = row_temp(a, rl);
+  const double invT = rt.invT;
 
   // one round trip: the chunk records (chunk lane + 64 i) and the drafted
   // token's logit
@@ -1382,7 +1388,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     double sl = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      sl += chunk_weight(cs[i], cm[i], m, a.c2, invT);
+      sl += chunk_weight(cs[i], cm[i], m, rt.c2, invT);
     const double S = dpp_wave_sum(sl);
     rr.S = S;
     if (!(S > 0.0 && S < INFINITY)) bad = true;
@@ -1400,7 +1406,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     // every finite logit with key >= lo is a candidate of its chunk; a chunk
     // whose max lies below lo holds none of them
     uint32_t lo = dpp_wave_umax(max(max(cb[0], cb[1]), max(cb[2], cb[3])));
-    if (MODE == M_TOPP) lo = max(lo, ord_key(m - a.win));
+    if (MODE == M_TOPP) lo = max(lo, ord_key(m - rt.win));
     // a chunk whose max lies below lo holds none of them
     int ce4[4];
 #pragma unroll
@@ -1857,8 +1863,8 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     const int n = sm.n;
     const bool res = n < K;
     const int jq = res ? K + 1 + n : n;
-    set_draw_row(&rr[n], true, 0, sm.blk);
-    set_draw_row(&rr[jq], true, 1, sm.blk);
+    set_draw_row(&rr[n], true, 0, row_temp(a, b * rps + n).invT, sm.blk);
+    set_draw_row(&rr[jq], true, 1, row_temp(a, b * rps + jq).invT, sm.blk);
     double Z;
     const int tok = full_row_sample<DT, WG>(a, (double)sm.u[K], row_ptr(a, b * rps + n, ESZ),
                                             row_ptr(a, b * rps + jq, ESZ), res, sm.blk, &Z);
@@ -1867,17 +1873,18 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
       if (a.out_z) a.out_z[b] = Z;
       if (a.out_px)
         a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll)
-                          : kept_prob<DT>(row_ptr(a, b * rps + n, ESZ), tok, load_row(&rr[n]), true, a.invT);
+                          : kept_prob<DT>(row_ptr(a, b * rps + n, ESZ), tok, load_row(&rr[n]), true,
+                                          row_temp(a, b * rps + n).invT);
     }
   }
 }
 
 template <int DT>
 __device__ __forceinline__ double plain_weight(const char* pr, const char* qr, int j, const RowRec& P,
-                                               const RowRec& Q, bool res, double invT) {
-  const double p = exp(((double)load_elem<DT>(pr, j) - (double)P.m) * invT) / P.S;
+                                               const RowRec& Q, bool res, double invTp, double invTq) {
+  const double p = exp(((double)load_elem<DT>(pr, j) - (double)P.m) * invTp) / P.S;
   if (!res) return p;
-  const double q = exp(((double)load_elem<DT>(qr, j) - (double)Q.m) * invT) / Q.S;
+  const double q = exp(((double)load_elem<DT>(qr, j) - (double)Q.m) * invTq) / Q.S;
   const double d = p - q;
   return d > 0.0 ? d : 0.0;
 }
@@ -1897,6 +1904,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   const bool res = active && n < K;
   const int rlP = b * a.rps + (active ? n : 0);
   const int rlQ = b * a.rps + (res ? K + 1 + n : (active ? n : 0));
+  const double iTp = row_temp(a, rlP).invT, iTq = row_temp(a, rlQ).invT;
   RowRec P, Q;
   const char* pr = nullptr;
   const char* qr = nullptr;
@@ -1911,7 +1919,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     for (int e = 0; e < 8; ++e) {
       const int j = j0 + e;
       if (j < a.V) {
-        const double w = plain_weight<DT>(pr, qr, j, P, Q, res, a.invT);
+        const double w = plain_weight<DT>(pr, qr, j, P, Q, res, iTp, iTq);
         ts += w;
         if (w > 0.0) lastp = j;
       }
@@ -1944,7 +1952,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   int tok;
   if (!(Z > 0.0)) {
     // empty residual (round-off only): draw from p
-    set_draw_row(&a.row[rlP], false, 0, sm);
+    set_draw_row(&a.row[rlP], false, 0, row_temp(a, rlP).invT, sm);
     tok = full_row_sample<DT, WG>(a, u, pr, qr, false, sm, &Z);
   } else {
     const double target = u * Z;
@@ -1971,8 +1979,8 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
       __syncthreads();
       const double cs = sm.d0;
       const int j0 = sf * SEG + 2 * t;
-      const double w0 = j0 < a.V ? plain_weight<DT>(pr, qr, j0, P, Q, res, a.invT) : 0.0;
-      const double w1 = j0 + 1 < a.V ? plain_weight<DT>(pr, qr, j0 + 1, P, Q, res, a.invT) : 0.0;
+      const double w0 = j0 < a.V ? plain_weight<DT>(pr, qr, j0, P, Q, res, iTp, iTq) : 0.0;
+      const double w1 = j0 + 1 < a.V ? plain_weight<DT>(pr, qr, j0 + 1, P, Q, res, iTp, iTq) : 0.0;
       double tot;
       const double inc2 = block_incl_scan(w0 + w1, sm.red, &tot);
       __syncthreads();
@@ -1992,7 +2000,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     a.out_tok[(size_t)b * (K + 1) + n] = tok;
     if (a.out_z) a.out_z[b] = Z;
     if (a.out_px)
-      a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll) : plain_weight<DT>(pr, qr, tok, P, Q, false, a.invT);
+      a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll) : plain_weight<DT>(pr, qr, tok, P, Q, false, iTp, iTq);
   }
 }
 
@@ -2010,7 +2018,7 @@ __global__ void __launch_bounds__(WG) probs_kernel(Args a) {
     if (j < a.V) {
       float out;
       if (R.flags & RF_BAD) out = __int_as_float(0x7FC00000);
-      else out = (float)kept_prob<DT>(rp, j, R, filtered, a.invT);
+      else out = (float)kept_prob<DT>(rp, j, R, filtered, row_temp(a, rl).invT);
       a.out_probs[(size_t)rl * a.V + j] = out;
     }
   }

@@ -34,7 +34,7 @@ def to_device(arr: np.ndarray, dtype: str, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
 
 
-def run_device(w: Workload, d: dict, x: np.ndarray, debug: bool = True):
+def run_device(w: Workload, d: dict, x: np.ndarray, debug: bool = True, draft_temperature=None):
     import torch
 
     from rejection_sampling_verify_09_amd import spec_verify
@@ -43,18 +43,20 @@ def run_device(w: Workload, d: dict, x: np.ndarray, debug: bool = True):
     drf = to_device(d["draft"], w.dtype) if w.K > 0 else None
     X = torch.from_numpy(x.astype(np.int32)).cuda()
     U = torch.from_numpy(d["uniforms"]).cuda()
-    res = spec_verify(tgt, drf, X, U, w.temperature, w.top_k, w.top_p, debug=debug)
+    res = spec_verify(tgt, drf, X, U, w.temperature, w.top_k, w.top_p, debug=debug,
+                      draft_temperature=draft_temperature)
     torch.cuda.synchronize()
     out = [r.cpu().numpy() if not isinstance(r, dict) else {k: v.cpu().numpy() for k, v in r.items()} for r in res]
     return out
 
 
-def compare(w: Workload, d: dict, x: np.ndarray, dev_tok, dev_n, dev_dbg=None, prob_tol: float = 1e-6):
+def compare(w: Workload, d: dict, x: np.ndarray, dev_tok, dev_n, dev_dbg=None, prob_tol: float = 1e-6,
+            draft_temperature=None):
     """Compare device outputs with the oracle.  Returns a dict of counts and
     the list of failures (sequence, reason)."""
     t0 = time.time()
     ref_tok, ref_n, ref_dg = oracle.verify(d["target"], d["draft"], x, d["uniforms"], w.temperature, w.top_k,
-                                           w.top_p, dtype=w.dtype, diag=True)
+                                           w.top_p, dtype=w.dtype, diag=True, draft_temperature=draft_temperature)
     t_oracle = time.time() - t0
     stats = dict(match=0, flagged=0, fail=0, oracle_s=t_oracle, max_prob_err=0.0)
     fails, flags = [], []
@@ -63,7 +65,7 @@ def compare(w: Workload, d: dict, x: np.ndarray, dev_tok, dev_n, dev_dbg=None, p
             stats["match"] += 1
             continue
         v, why = oracle.classify(d["target"][b], d["draft"][b], x[b], d["uniforms"][b], w.temperature, w.top_k,
-                                 w.top_p, w.dtype, dev_tok[b], dev_n[b])
+                                 w.top_p, w.dtype, dev_tok[b], dev_n[b], draft_temperature=draft_temperature)
         if v == oracle.MATCH:
             stats["match"] += 1
         elif v == oracle.FLAGGED:

@@ -100,6 +100,26 @@ def check_lossless(mod, case: str = "random", N: int = 400_000, seed: int = 11):
         assert np.all(n == 0), "disjoint supports must reject the first draft"
 
 
+def check_lossless_draft_temperature(mod, T: float = 1.0, Td: float = 0.5, N: int = 300_000, seed: int = 21):
+    """Drafts sampled from q at their own temperature Td and verified against
+    that q: the emitted tokens follow p at T.  Verifying them against q at T
+    instead (the draft temperature ignored) breaks the law, which the same
+    chi-square detects: returns that p-value for the caller to assert on."""
+    V, K = 8, 3
+    tl, dl = lossless_case("close", V, K, seed)
+    P = softmax_rows(tl, T)
+    Qd = softmax_rows(dl, Td)
+    rng = np.random.default_rng(seed + 1)
+    x = np.stack([rng.choice(V, size=N, p=Qd[i]) for i in range(K)], axis=1)
+    u = rng.random((N, K + 1), dtype=np.float32)
+    tok, n = mod.verify(tile_rows(tl, N), tile_rows(dl, N), x, u, T, 0, 1.0, draft_temperature=Td)
+    counts = np.bincount(tok[:, 0], minlength=V)
+    pv = _chi2_pvalue(counts, P[0])
+    assert pv > CHI2_MIN_P, f"draft temperature {Td}: position 0 differs from p (chi2 p={pv:.2e})"
+    tok_w, _ = mod.verify(tile_rows(tl, N), tile_rows(dl, N), x, u, T, 0, 1.0)
+    return _chi2_pvalue(np.bincount(tok_w[:, 0], minlength=V), P[0])
+
+
 # ---------------------------------------------------------------------------
 # accepted-count distribution at a fixed alpha
 # ---------------------------------------------------------------------------

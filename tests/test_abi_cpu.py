@@ -21,7 +21,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_filtered_probs", "sv_sample", "sv_release", "sv_scratch_bytes",
+    for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_spec_verify_dt", "sv_filtered_probs", "sv_sample",
+              "sv_release", "sv_scratch_bytes",
               "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
         assert s in syms
 
@@ -111,6 +112,19 @@ def test_sample_validation():
     # greedy draws need neither draft logits nor drafted tokens, but the rest is validated
     assert f(FAKE, None, 0.0, 0, 1.0, FAKE, None, 4, 10, 0, None) == L.SV_ERR_NULL
     assert f(None, None, 1.0, 0, 1.0, None, None, 0, 10, 0, None) == L.SV_OK
+
+
+def test_draft_temperature_validation():
+    def f(T=1.0, Td=0.5, B=2, out_n=FAKE):
+        return L.lib().sv_spec_verify_dt(FAKE, FAKE, FAKE, FAKE, T, Td, 0, 1.0, FAKE, out_n, None, None, None, B, 3,
+                                         16, 0, None)
+    assert f(Td=0.0) == L.SV_ERR_PARAM            # a sampling draft needs a temperature above 0
+    assert f(Td=-1.0) == L.SV_ERR_PARAM
+    assert f(Td=float("nan")) == L.SV_ERR_PARAM
+    assert f(Td=float("inf")) == L.SV_ERR_PARAM
+    assert f(B=-1) == L.SV_ERR_SHAPE
+    assert f(out_n=None) == L.SV_ERR_NULL
+    assert f(B=0) == L.SV_OK
 
 
 def test_profile_without_calls_reports_nothing():

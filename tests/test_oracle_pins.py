@@ -198,3 +198,29 @@ def test_sample_greedy_and_dead_rows():
     tok, prob = oracle.sample(z, 0.0, 0, 1.0, np.array([0.99, 0.5, 0.3]))
     assert tok.tolist() == [1, -1, 0]
     assert prob[0] == 1.0 and np.isnan(prob[1]) and prob[2] == 1.0
+
+
+# --- drafts sampled at their own temperature ----------------------------------
+
+def test_draft_temperature_keeps_the_law():
+    p_wrong = pins.check_lossless_draft_temperature(oracle, T=1.0, Td=0.5)
+    # the pin has power: ignoring the draft temperature is detected
+    assert p_wrong < 1e-6, p_wrong
+
+
+def test_draft_temperature_equal_or_greedy_changes_nothing():
+    rng = np.random.default_rng(31)
+    B, K, V = 50, 3, 30
+    tl = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    dl = rng.normal(0, 2, (B, K, V)).astype(np.float32)
+    x = rng.integers(0, V, (B, K))
+    u = rng.random((B, K + 1), dtype=np.float32)
+    for T, k, p in [(0.8, 0, 1.0), (1.0, 5, 0.9)]:
+        a = oracle.verify(tl, dl, x, u, T, k, p)
+        b = oracle.verify(tl, dl, x, u, T, k, p, draft_temperature=T)
+        assert all(np.array_equal(i, j) for i, j in zip(a, b))
+    g = oracle.verify(tl, dl, x, u, 0.0, 0, 1.0)
+    h = oracle.verify(tl, dl, x, u, 0.0, 0, 1.0, draft_temperature=0.3)
+    assert all(np.array_equal(i, j) for i, j in zip(g, h))
+    with pytest.raises(ValueError):
+        oracle.verify(tl, dl, x, u, 1.0, 0, 1.0, draft_temperature=0.0)
