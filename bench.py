@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --sampler [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --draft-temperature TD [--steps K] [--warmup W] [--workload NAME]
 
 One step = one sv_spec_verify call (the whole hot path: streaming pass,
 filter thresholds, accept tests, first-rejection scan, final draw) over one
@@ -10,7 +11,9 @@ over several device copies whose total exceeds the 256 MB last-level cache,
 so every step reads its logits from HBM.  Prints one JSON line.
 
 With --sampler, one step is one sv_sample call (the drafting draw: x ~ q and
-q(x)) over the workload's B*K draft rows, with their draft uniforms.
+q(x)) over the workload's B*K draft rows, with their draft uniforms.  With
+--draft-temperature, the drafts are drawn on the GPU (sv_sample) at that
+temperature before timing, and one step is one sv_spec_verify_dt call.
 
 The CPU-baseline leg times the fp64 oracle (test infrastructure) on a bounded
 sample of the same workload; it is a reported baseline, not the target.
@@ -66,7 +69,7 @@ def measured_traffic(key: str):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(w, d, x, budget_s: float):
+def cpu_baseline(w, d, x, budget_s: float, draft_temperature=None):
     """Time the fp64 oracle on whole batches of the workload until about
     budget_s of CPU time has been spent (at least one batch)."""
     import numpy as np
@@ -79,7 +82,7 @@ def cpu_baseline(w, d, x, budget_s: float):
     toks = 0
     while True:
         tok, n = oracle.verify(d["target"], d["draft"], x, d["uniforms"], w.temperature, w.top_k, w.top_p,
-                               dtype=w.dtype)
+                               dtype=w.dtype, draft_temperature=draft_temperature)
         n_done += sample_B
         toks += int(np.sum(n + 1))
         el = time.perf_counter() - t0
@@ -197,6 +200,8 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--sampler", action="store_true",
                     help="measure the drafting draw (sv_sample) over the workload's draft rows instead")
+    ap.add_argument("--draft-temperature", type=float, default=None,
+                    help="verify drafts drawn (on the GPU) at this temperature (sv_spec_verify_dt)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -226,7 +231,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": 5}), flush=True)
         return
 
-    from rejection_sampling_verify_09_amd import profile_start, profile_stop, spec_verify
+    from rejection_sampling_verify_09_amd import profile_start, profile_stop, sample, spec_verify
 
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
@@ -234,7 +239,18 @@ def main():
     if args.sampler:
         run_sampler(args, w, d)
         return
-    x = load_draft_tokens(name, w.B, w.K)
+    Td = args.draft_temperature
+    if Td is None:
+        x = load_draft_tokens(name, w.B, w.K)
+    else:
+        # the drafts x ~ q at Td, drawn by the library itself (not timed)
+        rows = torch.from_numpy(np.ascontiguousarray(d["draft"].reshape(w.B * w.K, w.V)))
+        if w.dtype == "bf16":
+            rows = rows.view(torch.int16).view(torch.bfloat16)
+        ud = torch.from_numpy(d["draft_u"].reshape(-1).astype(np.float32)).cuda()
+        xt, _ = sample(rows.cuda(), ud, Td if w.temperature > 0 else 0.0, w.top_k, w.top_p, with_prob=False)
+        x = xt.cpu().numpy().reshape(w.B, w.K).astype(np.int32)
+        del rows, ud, xt
 
     def dev(a):
         if w.dtype == "bf16":
@@ -255,7 +271,7 @@ def main():
 
     def step(i):
         spec_verify(tgts[i % R], drfs[i % R], X, U, w.temperature, w.top_k, w.top_p, out_tokens=out_t,
-                    out_num_accepted=out_n)
+                    out_num_accepted=out_n, draft_temperature=Td)
 
     for i in range(args.warmup):
         step(i)
@@ -293,7 +309,8 @@ def main():
     traffic = measured_traffic(name)
 
     result = {
-        "metric": "spec-verify sequences/s + % HBM peak at B=64 K=6 V=128256 bf16",
+        "metric": "spec-verify sequences/s + % HBM peak at B=64 K=6 V=128256 bf16"
+                  + ("" if Td is None else f" (drafts at T_d={Td})"),
         "value": seq_per_s,
         "unit": "sequences/s",
         "n_gpus": 1,
@@ -309,6 +326,7 @@ def main():
             "workload": name, "B": w.B, "K": w.K, "V": w.V, "logits": w.dtype, "temperature": w.temperature,
             "top_k": w.top_k, "top_p": w.top_p, "rows": w.rows, "input_copies": R,
             "logit_bytes_per_step": bytes_per_step,
+            **({} if Td is None else {"draft_temperature": Td}),
         },
         "tokens_per_s": emitted / (ms_per_step / 1e3),
         "mean_emitted_per_sequence": emitted / w.B,
@@ -328,7 +346,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, d, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, d, x, args.cpu_seconds, draft_temperature=Td)
     print(json.dumps(result), flush=True)
 
 
