@@ -55,6 +55,8 @@ __all__ = [
     "sample_tokens",
     "sample",
     "verify",
+    "verify_ragged",
+    "ragged_offsets_ok",
     "verify_one",
 ]
 
@@ -356,6 +358,84 @@ def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
         px_all[s:e] = px
         qx_all[s:e] = qx
         Z_all[s:e] = np.where(bad, np.nan, Z)
+    if diag:
+        return out_tok, out_n, dict(px=px_all, qx=qx_all, Z=Z_all)
+    return out_tok, out_n
+
+
+def ragged_offsets_ok(cu, n_draft_rows: int, max_k: int) -> bool:
+    """True when ``cu`` [B+1] describes B sequences of 0..max_k drafts that
+    tile ``n_draft_rows`` packed draft rows in order: cu[0] = 0, each
+    K_b = cu[b+1] - cu[b] in [0, max_k], cu[B] = n_draft_rows."""
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu.ndim != 1 or cu.shape[0] < 1 or cu[0] != 0 or cu[-1] != n_draft_rows:
+        return False
+    k = np.diff(cu)
+    return bool(np.all((k >= 0) & (k <= max_k)))
+
+
+def verify_ragged(target, draft, draft_tokens, uniforms, cu_num_draft, temperature, top_k, top_p,
+                  dtype: str = F32, max_k: int | None = None, diag: bool = False, draft_temperature=None):
+    """Verification of a batch whose sequences carry different numbers of drafts.
+
+    The draft length varies from step to step and from input to input when it
+    is tuned by the acceptance history (page www.cf-1.com/news/5155685 §2.4,
+    page www.2kiu.com/news/5895634 §4.4); each sequence is still verified by
+    the rule of ``verify`` with its own K_b = cu[b+1] - cu[b] (0 allowed:
+    then the sequence only draws its bonus token).
+
+    Packed layout: target [cu[B] + B, V] (sequence b's K_b + 1 rows from row
+    cu[b] + b), draft [cu[B], V] (its K_b rows from row cu[b]), draft_tokens
+    [cu[B]] (from cu[b]), uniforms float32 [cu[B] + B] (its K_b accept
+    uniforms then its sampling uniform, from cu[b] + b).
+
+    Returns (out_tokens int32 [B, max_k + 1] padded with -1, out_num_accepted
+    int32 [B]); with ``diag`` also px, qx float64 [cu[B]] and Z float64 [B].
+    max_k defaults to the largest K_b.  Offsets that do not describe such a
+    packing (cu[0] != 0, a K_b outside [0, max_k], cu[B] != the number of
+    draft rows) make every sequence a sentinel (n = -1, tokens -1), as a
+    device that only sees the offsets at run time reports them.
+    """
+    target = np.asarray(target)
+    draft = np.asarray(draft)
+    X = np.asarray(draft_tokens).astype(np.int64).reshape(-1)
+    U = np.asarray(uniforms)
+    cu = np.asarray(cu_num_draft, dtype=np.int64).reshape(-1)
+    if U.dtype != np.float32:
+        raise TypeError("uniforms must be float32")
+    if cu.shape[0] < 1:
+        raise ValueError("cu_num_draft needs B + 1 entries")
+    B = cu.shape[0] - 1
+    ND = draft.shape[0]
+    if target.ndim != 2 or draft.ndim != 2 or target.shape[0] != ND + B or draft.shape[1] != target.shape[1]:
+        raise ValueError("target must be [n_draft + B, V] and draft [n_draft, V]")
+    if X.shape[0] != ND or U.reshape(-1).shape[0] != ND + B:
+        raise ValueError("draft_tokens must be [n_draft] and uniforms [n_draft + B]")
+    U = U.reshape(-1)
+    ks = np.diff(cu)
+    if max_k is None:
+        max_k = int(max(0, ks.max(initial=0)))
+    if max_k < 0:
+        raise ValueError("max_k must be >= 0")
+    out_tok = np.full((B, max_k + 1), -1, dtype=np.int32)
+    out_n = np.full((B,), -1, dtype=np.int32)
+    px_all = np.full((ND,), np.nan)
+    qx_all = np.full((ND,), np.nan)
+    Z_all = np.full((B,), np.nan)
+    if ragged_offsets_ok(cu, ND, max_k):
+        # sequences of equal length verified together (the rule is per sequence)
+        for K in np.unique(ks):
+            K = int(K)
+            bs = np.flatnonzero(ks == K)
+            t_idx = (cu[bs] + bs)[:, None] + np.arange(K + 1)[None, :]
+            d_idx = cu[bs][:, None] + np.arange(K)[None, :]
+            tok, n, d = verify(target[t_idx], draft[d_idx], X[d_idx], U[t_idx], temperature, top_k, top_p,
+                               dtype=dtype, diag=True, draft_temperature=draft_temperature)
+            out_tok[bs, :K + 1] = tok
+            out_n[bs] = n
+            px_all[d_idx] = d["px"]
+            qx_all[d_idx] = d["qx"]
+            Z_all[bs] = d["Z"]
     if diag:
         return out_tok, out_n, dict(px=px_all, qx=qx_all, Z=Z_all)
     return out_tok, out_n

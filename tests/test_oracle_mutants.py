@@ -12,8 +12,10 @@ import types
 import pytest
 
 from tests import pins
+from tests import test_oracle_ragged as rag
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "spec_verify.py")
+ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE, "spec_verify.py")
 
 MUTANTS = {
     # residual with the operands swapped: max(0, q - p)
@@ -49,11 +51,29 @@ MUTANTS = {
     # greedy ties to the highest index
     "greedy_ties": ("a = np.argmax(z, axis=1)", "a = z.shape[1] - 1 - np.argmax(z[:, ::-1], axis=1)",
                     lambda m: pins.check_greedy(m)),
+    # ragged: a sequence's uniforms taken from its draft offset, not cu[b] + b
+    "ragged_uniform_base": ("U[t_idx]", "U[t_idx - bs[:, None]]",
+                            lambda m: rag.check_ragged_worked_case(m)),
+    # ragged: target rows taken from the draft offset
+    "ragged_target_base": ("target[t_idx]", "target[cu[bs][:, None] + np.arange(K + 1)[None, :]]",
+                           lambda m: rag.check_ragged_lossless(m, N=60_000)),
+}
+
+# planted mistakes in the draft-length controller (oracle/dynamic_k.py)
+CONTROLLER_MUTANTS = {
+    # the window kept across a change of K
+    "no_restart": ("            self.k += 1\n            self.hist = []", "            self.k += 1"),
+    # non-strict comparison
+    "raise_ge": ("rate > self.hi", "rate >= self.hi"),
+    # the lower bound ignored
+    "lower_bound": ("elif rate < self.lo and self.k > self.k_min:", "elif rate < self.lo:"),
+    # a decision before the window is full
+    "early": ("if len(self.hist) < self.window:", "if len(self.hist) < 1:"),
 }
 
 
-def _load_mutant(name, old, new):
-    with open(SRC) as f:
+def _load_mutant(name, old, new, path=SRC):
+    with open(path) as f:
         src = f.read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
     mod = types.ModuleType(f"oracle_mutant_{name}")
@@ -67,3 +87,27 @@ def test_mutant_is_caught(name):
     mod = _load_mutant(name, old, new)
     with pytest.raises(AssertionError):
         pin(mod)
+
+
+def _controller_pins(cls):
+    rag.check_controller_hand_trace(cls)
+    c = cls(window=2, k_init=5)
+    assert [c.observe(4, 5), c.observe(4, 5)] == [5, 5]
+    c = cls(window=1, k_min=2, k_init=2)
+    assert [c.observe(0, 4), c.observe(0, 4)] == [2, 2]
+    # after a raise the window restarts: a second raise needs a full window
+    c = cls(window=2, k_init=5)
+    assert [c.observe(2, 2) for _ in range(3)] == [5, 6, 6]
+
+
+@pytest.mark.parametrize("name", sorted(CONTROLLER_MUTANTS))
+def test_controller_mutant_is_caught(name):
+    old, new = CONTROLLER_MUTANTS[name]
+    mod = _load_mutant(name, old, new, os.path.join(ORACLE, "dynamic_k.py"))
+    with pytest.raises(AssertionError):
+        _controller_pins(mod.DynamicK)
+
+
+def test_controller_pins_pass_on_the_oracle():
+    from oracle.dynamic_k import DynamicK
+    _controller_pins(DynamicK)
