@@ -143,6 +143,89 @@ int sv_spec_verify_dt(const void* target_logits, const void* draft_logits,
                       void* stream);
 
 /*
+ * sv_spec_verify_ragged - verification of a batch whose sequences carry
+ * different numbers of drafts, as when the draft length is tuned per
+ * sequence from its acceptance history (page www.cf-1.com/news/5155685
+ * section 2.4, page www.2kiu.com/news/5895634 section 4.4; see
+ * sv_dynk_observe).  Each sequence follows the rule of sv_spec_verify with its
+ * own K_b = cu_num_draft[b+1] - cu_num_draft[b] drafts (0 allowed: the
+ * sequence only draws its bonus token from its one target row).
+ *
+ * Packed layout (device pointers), with N = total_draft = cu_num_draft[B]:
+ * target_logits  [N + B, V] dtype   sequence b's K_b + 1 rows from row
+ *                                   cu_num_draft[b] + b
+ * draft_logits   [N, V] dtype       its K_b rows from row cu_num_draft[b]
+ *                                   (not read when temperature == 0)
+ * draft_tokens   [N] int32          its drafts from cu_num_draft[b]
+ * uniforms       [N + B] float32    its K_b accept uniforms, then its one
+ *                                   sampling uniform, from cu_num_draft[b] + b
+ * cu_num_draft   [B + 1] int32      device offsets: cu[0] = 0, nondecreasing,
+ *                                   every K_b <= max_k, cu[B] = total_draft
+ * out_tokens     [B, max_k + 1] int32   as for sv_spec_verify; every entry
+ *                                   after the drawn token is -1
+ * out_num_accepted [B] int32        n in [0, K_b], or -1 for a sentinel
+ * out_p, out_q   [N] double or NULL p_i(x_i), q_i(x_i) at each draft's packed
+ *                                   index (as sv_spec_verify_debug)
+ * out_z          [B] double or NULL as sv_spec_verify_debug
+ * draft_temperature                 as sv_spec_verify_dt (pass temperature
+ *                                   for drafts sampled at the target's)
+ * B, total_draft, max_k, V, dtype   host values; max_k <= SV_MAX_K and
+ *                                   total_draft <= B * max_k (else
+ *                                   SV_ERR_SHAPE)
+ *
+ * The offsets are only read on the device.  When they describe no packing
+ * of the rows (cu[0] != 0, a K_b < 0 or > max_k, or cu[B] != total_draft),
+ * every sequence is written as a sentinel (n = -1, tokens -1; out_p and
+ * out_q are left untouched) and the call still returns SV_OK.  With every
+ * K_b equal to K the results equal sv_spec_verify_dt's on the same rows.
+ */
+int sv_spec_verify_ragged(const void* target_logits, const void* draft_logits,
+                          const int32_t* draft_tokens, const float* uniforms,
+                          const int32_t* cu_num_draft,
+                          float temperature, float draft_temperature,
+                          int32_t top_k, float top_p,
+                          int32_t* out_tokens, int32_t* out_num_accepted,
+                          double* out_p, double* out_q, double* out_z,
+                          int32_t B, int32_t total_draft, int32_t max_k,
+                          int32_t V, int32_t dtype, void* stream);
+
+/*
+ * Draft-length controller (host only; no device work).  The rule of page
+ * www.2kiu.com/news/5895634 section 4.4 (the policy of page
+ * www.cf-1.com/news/5155685 section 2.4): keep the acceptance statistics of
+ * the last `window` batches (100 on the page); once the window is full, a
+ * window acceptance rate above raise_above (0.8) lengthens the draft by one
+ * and one below lower_below (0.6) shortens it by one, within [k_min, k_max]
+ * ([2, 10]).  The window rate is its accepted drafts over its drafted tokens
+ * (exact integer totals, one division).  The window starts empty after every
+ * change of K, so each decision rests on batches drafted at the current K.
+ * A batch that drafted nothing is not observed.
+ *
+ * One handle holds `lanes` independent controllers: 1 for a batch-wide draft
+ * length (observe the batch's totals), B for one draft length per sequence
+ * (observe each sequence's n and K_b; feed the result to
+ * sv_spec_verify_ragged).  Handles are not thread-safe; distinct handles
+ * are independent.
+ *
+ * sv_dynk_create   returns a handle, or NULL if lanes < 1, window < 1,
+ *                  not 0 <= k_min <= k_init <= k_max, not 0 <= lower_below
+ *                  <= raise_above <= 1, or memory is short.
+ * sv_dynk_observe  accepted[l], drafted[l]: host arrays [lanes] for one
+ *                  batch; k_next[l] (host [lanes], may be NULL) receives the
+ *                  draft length to use next.  SV_ERR_NULL for a NULL handle or
+ *                  input; SV_ERR_PARAM (nothing recorded) unless
+ *                  0 <= accepted[l] <= drafted[l] for every lane.
+ * sv_dynk_k        current draft length of a lane (-1 for a bad handle/lane).
+ * sv_dynk_destroy  frees the handle (NULL allowed).
+ */
+typedef struct sv_dynk sv_dynk;
+sv_dynk* sv_dynk_create(int32_t lanes, int32_t window, double raise_above, double lower_below,
+                        int32_t k_min, int32_t k_max, int32_t k_init);
+int sv_dynk_observe(sv_dynk* ctrl, const int64_t* accepted, const int64_t* drafted, int32_t* k_next);
+int32_t sv_dynk_k(const sv_dynk* ctrl, int32_t lane);
+void sv_dynk_destroy(sv_dynk* ctrl);
+
+/*
  * sv_filtered_probs - the filtered distribution of every row: temperature,
  * then top-k, then top-p, then the softmax over the kept tokens (page
  * www.gsyq.cn/news/428210 section 3.3 for the parameters; the distribution
@@ -186,7 +269,7 @@ int sv_sample(const void* logits, const float* uniforms, float temperature,
 /*
  * Launch timing for benchmarks.  Between sv_profile_start() and
  * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug /
- * sv_spec_verify_dt / sv_sample call records three HIP events on its own
+ * sv_spec_verify_dt / sv_spec_verify_ragged / sv_sample call records three HIP events on its own
  * stream: before its streaming kernel (the pass that reads every logit once),
  * after it, and after the call's last kernel.  sv_profile_stop() waits for
  * the recorded events and returns the summed durations in milliseconds of the

@@ -7,6 +7,7 @@ from ._lib import (  # noqa: F401
     SV_BF16,
     SV_F32,
     SV_MAX_K,
+    DraftLengthController,
     SpecVerifyError,
     filtered_probs,
     lib,
@@ -15,8 +16,9 @@ from ._lib import (  # noqa: F401
     release,
     sample,
     spec_verify,
+    spec_verify_ragged,
     status_string,
 )
 
-__all__ = ["spec_verify", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
+__all__ = ["spec_verify", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
            "SpecVerifyError"]

@@ -46,6 +46,17 @@ def lib() -> ctypes.CDLL:
         L.sv_sample.restype = ctypes.c_int
         L.sv_spec_verify_dt.argtypes = [vp, vp, vp, vp, f32, f32, i32, f32, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
         L.sv_spec_verify_dt.restype = ctypes.c_int
+        L.sv_spec_verify_ragged.argtypes = [vp, vp, vp, vp, vp, f32, f32, i32, f32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                            i32, i32, vp]
+        L.sv_spec_verify_ragged.restype = ctypes.c_int
+        L.sv_dynk_create.argtypes = [i32, i32, ctypes.c_double, ctypes.c_double, i32, i32, i32]
+        L.sv_dynk_create.restype = vp
+        L.sv_dynk_observe.argtypes = [vp, vp, vp, vp]
+        L.sv_dynk_observe.restype = ctypes.c_int
+        L.sv_dynk_k.argtypes = [vp, i32]
+        L.sv_dynk_k.restype = i32
+        L.sv_dynk_destroy.argtypes = [vp]
+        L.sv_dynk_destroy.restype = None
         L.sv_release.argtypes = []
         L.sv_release.restype = ctypes.c_int
         L.sv_scratch_bytes.argtypes = [ctypes.c_int]
@@ -158,6 +169,110 @@ def spec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor | None, 
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_spec_verify")
     return out_tokens, out_num_accepted
+
+
+def spec_verify_ragged(target_logits: torch.Tensor, draft_logits: torch.Tensor | None, draft_tokens: torch.Tensor,
+                       uniforms: torch.Tensor, cu_num_draft: torch.Tensor, max_k: int, temperature: float = 1.0,
+                       top_k: int = 0, top_p: float = 1.0, draft_temperature: float | None = None,
+                       out_tokens: torch.Tensor | None = None, out_num_accepted: torch.Tensor | None = None,
+                       stream=None, debug: bool = False):
+    """Verify a batch of sequences with different draft lengths on the GPU.
+
+    Packed: target_logits [N + B, V] (sequence b's K_b + 1 rows from row
+    cu[b] + b), draft_logits [N, V] (its K_b rows from row cu[b]),
+    draft_tokens [N] int32, uniforms [N + B] float32, cu_num_draft [B + 1]
+    int32 on the device, N = total drafts (from the tensors' shapes, not from
+    the device offsets).  Returns (out_tokens [B, max_k + 1] int32,
+    out_num_accepted [B] int32), plus p(x), q(x) [N] and Z [B] when ``debug``.
+    """
+    if target_logits.dim() != 2 or cu_num_draft.dim() != 1:
+        raise ValueError("target_logits must be [N + B, V] and cu_num_draft [B + 1]")
+    B = cu_num_draft.shape[0] - 1
+    NT, V = target_logits.shape
+    N = NT - B
+    if B < 0 or N < 0:
+        raise ValueError("target_logits needs N + B rows")
+    code = _dtype_code(target_logits)
+    dev = target_logits.device
+    tp = _dev(target_logits, "target_logits")
+    if draft_logits is not None and N > 0:
+        if tuple(draft_logits.shape) != (N, V) or draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft_logits must be [N, V] with the target's dtype")
+        dp = _dev(draft_logits, "draft_logits")
+    elif float(temperature) == 0.0 or N == 0:
+        dp = None
+    else:
+        raise ValueError("draft_logits are required unless temperature == 0")
+    if tuple(draft_tokens.shape) != (N,) or tuple(uniforms.shape) != (N + B,):
+        raise ValueError("draft_tokens must be [N] and uniforms [N + B]")
+    xp = _dev(draft_tokens, "draft_tokens", torch.int32) if N > 0 else None
+    up = _dev(uniforms, "uniforms", torch.float32)
+    cp = _dev(cu_num_draft, "cu_num_draft", torch.int32)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, int(max_k) + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if tuple(out_tokens.shape) != (B, int(max_k) + 1):
+        raise ValueError("out_tokens must be [B, max_k + 1]")
+    out_p = torch.empty((N,), dtype=torch.float64, device=dev) if debug else None
+    out_q = torch.empty((N,), dtype=torch.float64, device=dev) if debug else None
+    out_z = torch.empty((B,), dtype=torch.float64, device=dev) if debug else None
+    Td = float(temperature) if draft_temperature is None else float(draft_temperature)
+    st = lib().sv_spec_verify_ragged(tp, dp, xp, up, cp, float(temperature), Td, int(top_k), float(top_p),
+                                     _dev(out_tokens, "out_tokens", torch.int32),
+                                     _dev(out_num_accepted, "out_num_accepted", torch.int32),
+                                     out_p.data_ptr() if debug and N > 0 else None,
+                                     out_q.data_ptr() if debug and N > 0 else None,
+                                     out_z.data_ptr() if debug else None, B, N, int(max_k), V, code, _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_spec_verify_ragged")
+    if debug:
+        return out_tokens, out_num_accepted, dict(p=out_p, q=out_q, z=out_z)
+    return out_tokens, out_num_accepted
+
+
+class DraftLengthController:
+    """Host handle of the library's draft-length controller (``lanes``
+    independent controllers: 1 for a batch-wide K, B for one per sequence)."""
+
+    def __init__(self, lanes: int = 1, window: int = 100, raise_above: float = 0.8, lower_below: float = 0.6,
+                 k_min: int = 2, k_max: int = 10, k_init: int = 5):
+        self._lib = lib()
+        self.lanes = int(lanes)
+        h = self._lib.sv_dynk_create(self.lanes, int(window), float(raise_above), float(lower_below), int(k_min),
+                                     int(k_max), int(k_init))
+        if not h:
+            raise ValueError("invalid controller settings")
+        self._h = ctypes.c_void_p(h)
+
+    def observe(self, accepted, drafted):
+        """One batch: per-lane accepted drafts and drafted tokens (host
+        sequences of ints).  Returns the next draft length of every lane."""
+        if len(accepted) != self.lanes or len(drafted) != self.lanes:
+            raise ValueError("one value per lane")
+        if not self._h:
+            raise ValueError("the controller is closed")
+        acc = (ctypes.c_int64 * self.lanes)(*[int(v) for v in accepted])
+        dr = (ctypes.c_int64 * self.lanes)(*[int(v) for v in drafted])
+        out = (ctypes.c_int32 * self.lanes)()
+        st = self._lib.sv_dynk_observe(self._h, acc, dr, out)
+        if st != SV_OK:
+            raise SpecVerifyError(st, "sv_dynk_observe")
+        return list(out)
+
+    def k(self, lane: int = 0) -> int:
+        return int(self._lib.sv_dynk_k(self._h, int(lane)))
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.sv_dynk_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def filtered_probs(logits: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0,

@@ -3,6 +3,7 @@
 #include "sv_common.hpp"
 #include "specverify.h"
 
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
 #include <mutex>
@@ -193,14 +194,23 @@ void set_scalars(Args& a, float T, int32_t top_k, float top_p, float Td) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A ragged batch: per-sequence draft counts from device offsets cu[B + 1]
+// (nd drafts in total, at most kmax per sequence).
+struct Ragged {
+  const int32_t* cu;
+  int32_t nd, kmax;
+};
+
 // need_n: out_n is required (the sampler passes none).  out_px: probability
 // of each sequence's last drawn token under the row it was drawn from (the
-// sampler, K == 0).
+// sampler, K == 0).  rg: null for a rectangular [B, K] batch.
 int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, float Td,
                 int32_t top_k, float top_p, int32_t* out_tok, int32_t* out_n, bool need_n, double* out_p,
                 double* out_q, double* out_z, double* out_px, int32_t B, int32_t K, int32_t V, int32_t dtype,
-                void* stream) {
+                void* stream, const Ragged* rg = nullptr) {
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > MAX_V) return SV_ERR_SHAPE;
+  if (rg && (rg->nd < 0 || rg->kmax < 0 || rg->kmax > SV_MAX_K || (int64_t)rg->nd > (int64_t)B * rg->kmax))
+    return SV_ERR_SHAPE;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
   int st = check_params(T, top_k, top_p);
   if (st != SV_OK) return st;
@@ -208,12 +218,14 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   if (T > 0.0f && (check_params(Td, top_k, top_p) != SV_OK || !(Td > 0.0f))) return SV_ERR_PARAM;
   if (B == 0) return SV_OK;
   const int mode = pick_mode(T, top_k, top_p, V);
-  if (!tgt || !U || !out_tok || (need_n && !out_n)) return SV_ERR_NULL;
-  if (K > 0 && !X) return SV_ERR_NULL;
-  if (K > 0 && mode != M_GREEDY && !drf) return SV_ERR_NULL;
+  const int64_t nd = rg ? rg->nd : (int64_t)B * K;  // draft rows
+  const int32_t kmax = rg ? rg->kmax : K;
+  if (!tgt || !U || !out_tok || (need_n && !out_n) || (rg && !rg->cu)) return SV_ERR_NULL;
+  if (nd > 0 && !X) return SV_ERR_NULL;
+  if (nd > 0 && mode != M_GREEDY && !drf) return SV_ERR_NULL;
   const int esz = dtype == SV_BF16 ? 2 : 4;
-  const int64_t rps = mode == M_GREEDY ? (int64_t)K + 1 : 2 * (int64_t)K + 1;
-  const int64_t rows = (int64_t)B * rps;
+  const int64_t nt = nd + B;  // target rows
+  const int64_t rows = mode == M_GREEDY ? nt : nt + nd;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
   if (rows * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
@@ -242,9 +254,12 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.out_px = out_px;
   a.out_probs = nullptr;
   a.B = B;
-  a.K = K;
+  a.K = rg ? 0 : K;
   a.V = V;
-  a.rps = (int32_t)rps;
+  a.NT = (int32_t)nt;
+  a.ND = (int32_t)nd;
+  a.Kmax = kmax;
+  a.cu = rg ? rg->cu : nullptr;
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
   a.do_seq = 1;
@@ -254,6 +269,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
   a.ulen = vec ? 16 / esz : 1;
   a.dch = make_udiv((uint32_t)a.nchunks);
+  a.rps = rg ? 1 : mode == M_GREEDY ? a.K + 1 : 2 * a.K + 1;
   a.drps = make_udiv((uint32_t)a.rps);
   hipStream_t s = (hipStream_t)stream;
   ProfSlot* prof = prof_begin();
@@ -301,6 +317,17 @@ int sv_spec_verify_dt(const void* target_logits, const void* draft_logits, const
                      top_p, out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream);
 }
 
+int sv_spec_verify_ragged(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                          const float* uniforms, const int32_t* cu_num_draft, float temperature,
+                          float draft_temperature, int32_t top_k, float top_p, int32_t* out_tokens,
+                          int32_t* out_num_accepted, double* out_p, double* out_q, double* out_z, int32_t B,
+                          int32_t total_draft, int32_t max_k, int32_t V, int32_t dtype, void* stream) {
+  const Ragged rg{cu_num_draft, total_draft, max_k};
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, draft_temperature, top_k,
+                     top_p, out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, 0, V, dtype, stream,
+                     &rg);
+}
+
 // The draw of a verification with no drafts: each row is a sequence of one
 // position whose only token is drawn from its own filtered distribution with
 // its own uniform.
@@ -340,7 +367,7 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   a.B = rows;
   a.K = 0;
   a.V = V;
-  a.rps = 1;
+  a.NT = rows;
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
   a.do_seq = 0;
@@ -349,7 +376,8 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   const bool vec = aligned16(logits) && ((int64_t)V * esz) % 16 == 0;
   a.ulen = vec ? 16 / esz : 1;
   a.dch = make_udiv((uint32_t)a.nchunks);
-  a.drps = make_udiv((uint32_t)a.rps);
+  a.rps = 1;
+  a.drps = make_udiv(1u);
   hipStream_t s = (hipStream_t)stream;
   if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
 
 namespace sv {
 
@@ -94,7 +95,20 @@ struct Args {
   double* out_z;
   double* out_px;  // per sequence: probability of the last drawn token under the row it was drawn from
   float* out_probs;
-  int32_t B, K, V, rps, nchunks, nsc, top_k, do_seq;
+  int32_t B, K, V;
+  int32_t rps;         // rows per sequence (rectangular; 1 for ragged batches, with K = 0)
+  int32_t nchunks, nsc, top_k, do_seq;
+  // Rows are numbered in the order they are streamed, and every per-row
+  // record is kept under that number.  Rectangular batches: sequence by
+  // sequence, row b * rps + j is the sequence's target row j (j <= K) or
+  // draft row j - K - 1.  Ragged batches (cu[B + 1] offsets, K_b = cu[b + 1]
+  // - cu[b]): every target row first (sequence b's from row cu[b] + b), then
+  // every draft row (its from row NT + cu[b]), which is also the order of the
+  // packed inputs.
+  int32_t NT;          // target rows
+  int32_t ND;          // draft rows
+  int32_t Kmax;        // output stride of out_tok is Kmax + 1
+  const int32_t* cu;   // ragged offsets (device), or null for a rectangular batch
   float c2;        // log2(e) / T, the exp2 scale of the streaming pass
   float win;       // top-p candidate window in logit units
   double invT;     // 1 / T in double
@@ -461,6 +475,15 @@ __device__ __forceinline__ bool last_arrival(uint32_t* cnt, uint32_t total, int*
   return *flag != 0;
 }
 
+// Row rl in the order of the packed inputs (every target row, then every
+// draft row).  Rectangular: sequence b = rl / rps, its row j = rl - b * rps
+// is target row b(K + 1) + j, or draft row NT + bK + (j - K - 1).  Ragged
+// batches pass K = 0 and rps = 1, which makes the map the identity.
+__device__ __forceinline__ int lin_row(const Args& a, int rl) {
+  const int b = udiv(rl, a.drps), j = rl - b * a.rps;
+  return b * a.K + j + (j > a.K ? a.NT - a.K - 1 : b);
+}
+
 // Temperature-derived scalars of row rl: the draft rows' own (a draft
 // sampled at its own temperature is verified against that q), the target's
 // for every other row.
@@ -470,21 +493,94 @@ struct RowT {
   double invT;  // 1 / T
 };
 __device__ __forceinline__ RowT row_temp(const Args& a, int rl) {
-  const int j = rl - udiv(rl, a.drps) * a.rps;
-  return j > a.K ? RowT{a.c2d, a.wind, a.invTd} : RowT{a.c2, a.win, a.invT};
+  return lin_row(a, rl) >= a.NT ? RowT{a.c2d, a.wind, a.invTd} : RowT{a.c2, a.win, a.invT};
 }
 
-// Row rl of the verification (per sequence: K+1 target rows, then K draft
-// rows).  The base is chosen by arithmetic on the two pointer values: a
-// choice between the two argument fields themselves can be compiled into a
-// load from a computed address inside the argument block, which moves the
-// whole block to scratch memory.
+// Logits of row rl.  The base is chosen by arithmetic on the two pointer
+// values: a choice between the two argument fields themselves can be
+// compiled into a load from a computed address inside the argument block,
+// which moves the whole block to scratch memory.
 __device__ __forceinline__ const char* row_ptr(const Args& a, int rl, int esz) {
-  const int b = udiv(rl, a.drps), j = rl - b * a.rps;
-  const bool dr = j > a.K;
-  const size_t idx = dr ? (size_t)b * a.K + (j - a.K - 1) : (size_t)b * (a.K + 1) + j;
+  const int L = lin_row(a, rl);
+  const bool dr = L >= a.NT;
+  const size_t idx = (size_t)(dr ? L - a.NT : L);
   const uintptr_t t = (uintptr_t)a.tgt, d = (uintptr_t)a.drf;
   return (const char*)(t + (dr ? d - t : (uintptr_t)0)) + idx * (size_t)a.V * esz;
+}
+
+// RAG: a ragged batch (a.cu set).
+// A sequence: K drafts, its first uniform t0 (= its first target row in
+// the packed order), its first drafted token x0 (its draft rows start at
+// packed row NT + x0) and, for rectangular batches, its first row s0.
+struct SeqGeo {
+  int K, t0, x0, s0;
+};
+template <bool RAG>
+__device__ __forceinline__ SeqGeo seq_geo(const Args& a, int b) {
+  if (RAG) {
+    const int c0 = a.cu[b], c1 = a.cu[b + 1];
+    return SeqGeo{c1 - c0, c0 + b, c0, 0};
+  }
+  return SeqGeo{a.K, b * (a.K + 1), b * a.K, b * a.rps};
+}
+// Row of the sequence's local row j: 0..K target rows, K+1..2K draft rows.
+template <bool RAG>
+__device__ __forceinline__ int seq_row(const Args& a, const SeqGeo& g, int j) {
+  if (!RAG) return g.s0 + j;
+  return j <= g.K ? g.t0 + j : a.NT + g.x0 + (j - g.K - 1);
+}
+
+// Where row rl lies: its sequence b, its position i within the sequence's
+// target (0..K_b) or draft (0..K_b - 1) rows, K_b and x0(b).  bad: the ragged
+// offsets do not describe a packing of the rows (cu[0] != 0, a K_b outside
+// [0, Kmax], or cu[B] != ND); every wave of a workgroup reaches the same
+// answer.  Ragged batches: each lane scans entries lane, lane + 64, ... of
+// cu; b is the number of sequences after the first whose first row (of the
+// same kind) is at or before rl, which the monotone offsets make exact.
+struct RowLoc {
+  int b, i, K, x0;
+  bool draft, bad;
+};
+template <bool RAG>
+__device__ __forceinline__ RowLoc row_loc(const Args& a, int rl) {
+  RowLoc L;
+  L.bad = false;
+  if (!RAG) {
+    L.b = udiv(rl, a.drps);
+    const int j = rl - L.b * a.rps;
+    L.draft = j > a.K;
+    L.i = L.draft ? j - a.K - 1 : j;
+    L.K = a.K;
+    L.x0 = L.b * a.K;
+    return L;
+  }
+  L.draft = rl >= a.NT;
+  const int r = L.draft ? rl - a.NT : rl;
+  int cnt = 0, lo = 0, hi = INT_MAX;
+  bool bad = false;
+  for (int s = (int)(threadIdx.x & 63); s <= a.B; s += 64) {
+    const int c = a.cu[s];
+    const int cn = s < a.B ? a.cu[s + 1] : c;
+    bad |= (s == 0 && c != 0) || (s == a.B && c != a.ND) || (s < a.B && (cn < c || cn - c > a.Kmax));
+    const int st = L.draft ? c : c + s;
+    if (s >= 1 && s < a.B && st <= r) {
+      ++cnt;
+      lo = max(lo, st);
+    }
+    if (s >= 1 && st > r) hi = min(hi, st);
+  }
+  L.bad = __ballot(bad) != 0ull;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    cnt += __shfl_xor(cnt, o);
+    lo = max(lo, __shfl_xor(lo, o));
+    hi = min(hi, __shfl_xor(hi, o));
+  }
+  L.b = cnt;
+  L.i = r - lo;
+  L.K = L.draft ? hi - lo : hi - lo - 1;
+  L.x0 = L.draft ? lo : lo - cnt;
+  return L;
 }
 
 }  // namespace sv

@@ -1712,6 +1712,23 @@ __device__ int wave_list_sample(double u, const int32_t* pidx, const double* ppr
   return tok;
 }
 
+// Sequence b as a sentinel (n = -1, tokens -1), by the threads of one
+// workgroup; its uniform-indexed outputs only (out_p and out_q are left).
+__device__ void sentinel_seq(const Args& a, int b, int t) {
+  const double nanv = __longlong_as_double(0x7FF8000000000000ll);
+  for (int j = t; j <= a.Kmax; j += WG) a.out_tok[(size_t)b * (a.Kmax + 1) + j] = -1;
+  if (t == 0) {
+    if (a.out_n) a.out_n[b] = -1;
+    if (a.out_z) a.out_z[b] = nanv;
+    if (a.out_px) a.out_px[b] = nanv;
+    SeqRec sr;
+    sr.Z = 0.0;
+    sr.n = -1;
+    sr.flags = RF_BAD;
+    a.seq[b] = sr;
+  }
+}
+
 // One workgroup per row.  Its first wave merges the row (wave_row: one round
 // trip for the chunk records and most candidate units, one to read the units
 // back); when the lists cannot decide the cut the whole block merges it
@@ -1720,16 +1737,22 @@ __device__ int wave_list_sample(double u, const int32_t* pidx, const double* ppr
 // kept lists (the whole block draws from full rows when a kept set is too
 // large for a list; unfiltered rows: the sampling kernel draws afterwards).
 // With do_seq == 0 (filtered probabilities) only the merges run.
-template <int DT, int MODE>
+template <int DT, int MODE, bool RAG>
 __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   __shared__ RowKSm sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  const int rl = (int)blockIdx.x, K = a.K, rps = a.rps;
-  const int b = udiv(rl, a.drps), jr = rl - b * rps;
-  const int ir = jr <= K ? jr : jr - K - 1;
-  const int xtok = (a.do_seq && ir < K) ? a.X[(size_t)b * K + ir] : -1;
+  const int rl = (int)blockIdx.x;
+  const RowLoc loc = a.do_seq ? row_loc<RAG>(a, rl) : RowLoc{rl, 0, 0, 0, false, false};
+  if (loc.bad) {
+    // offsets that describe no packing: every sequence is a sentinel, and no
+    // row or sequence record is used
+    if (rl < a.B) sentinel_seq(a, rl, t);
+    return;
+  }
+  const int b = loc.b;
+  const int xtok = (a.do_seq && loc.i < loc.K) ? a.X[(size_t)loc.x0 + loc.i] : -1;
   if (w == 0) {
     RowRec rr;
     const bool ok = wave_row<DT, MODE>(a, rl, xtok, sm.w, rr);
@@ -1737,30 +1760,33 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   }
   __syncthreads();
   if (!sm.fast) (void)row_finalize<DT, MODE, WG>(a, rl, xtok, sm.blk);
+  const int K = loc.K;
+  const int rps = MODE == M_GREEDY ? K + 1 : 2 * K + 1;
   if (!a.do_seq || !last_arrival(&a.seq_cnt[b], (uint32_t)rps, &sm.flag)) return;
 
   // ---- the sequence: its rows' records, drafted tokens and uniforms, and
   // (up to SPEC_ROWS rows) the head of every row's kept list: one round trip
-  const RowRec* rr = a.row + (size_t)b * rps;
+  const SeqGeo g{K, loc.x0 + b, loc.x0, b * a.rps};
   const bool spec = FILT && rps <= SPEC_ROWS;
   int32_t si[SPEC_ROWS / NWAVE];
   double sp[SPEC_ROWS / NWAVE];
   if (spec) {
 #pragma unroll
     for (int i = 0; i < SPEC_ROWS / NWAVE; ++i) {
-      const size_t o = (size_t)(b * rps + min(w + NWAVE * i, rps - 1)) * KEEP_CAP + lane;
+      const size_t o = (size_t)seq_row<RAG>(a, g, min(w + NWAVE * i, rps - 1)) * KEEP_CAP + lane;
       si[i] = ld_dev(&a.kidx[o]);
       sp[i] = ld_dev(&a.kprob[o]);
     }
   }
   for (int j = t; j < rps; j += WG) {
-    sm.px[j] = ld_dev(&rr[j].px);
-    sm.rf[j] = ld_dev(&rr[j].flags);
-    sm.nk[j] = ld_dev(&rr[j].nkept);
-    sm.arg[j] = ld_dev(&rr[j].arg);
+    const RowRec* rj = a.row + seq_row<RAG>(a, g, j);
+    sm.px[j] = ld_dev(&rj->px);
+    sm.rf[j] = ld_dev(&rj->flags);
+    sm.nk[j] = ld_dev(&rj->nkept);
+    sm.arg[j] = ld_dev(&rj->arg);
   }
-  if (t < K) sm.x[t] = a.X[(size_t)b * K + t];
-  if (t <= K) sm.u[t] = a.U[(size_t)b * (K + 1) + t];
+  if (t < K) sm.x[t] = a.X[(size_t)g.x0 + t];
+  if (t <= K) sm.u[t] = a.U[(size_t)g.t0 + t];
   if (spec) {
 #pragma unroll
     for (int i = 0; i < SPEC_ROWS / NWAVE; ++i) {
@@ -1782,13 +1808,13 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     const unsigned long long rm = __ballot(rej);
     const bool bad = __ballot(badx || badr) != 0ull;
     const int n = bad ? -1 : (rm ? __ffsll(rm) - 1 : K);
-    int32_t* ot = a.out_tok + (size_t)b * (K + 1);
+    int32_t* ot = a.out_tok + (size_t)b * (a.Kmax + 1);
     const double nanv = __longlong_as_double(0x7FF8000000000000ll);
     if (lane < K) {
-      if (a.out_p) a.out_p[(size_t)b * K + lane] = n < 0 ? nanv : sm.px[lane];
-      if (a.out_q) a.out_q[(size_t)b * K + lane] = (n < 0 || MODE == M_GREEDY) ? nanv : sm.px[K + 1 + lane];
+      if (a.out_p) a.out_p[(size_t)g.x0 + lane] = n < 0 ? nanv : sm.px[lane];
+      if (a.out_q) a.out_q[(size_t)g.x0 + lane] = (n < 0 || MODE == M_GREEDY) ? nanv : sm.px[K + 1 + lane];
     }
-    for (int j = lane; j <= K; j += 64) {
+    for (int j = lane; j <= a.Kmax; j += 64) {
       if (n < 0 || j > n) ot[j] = -1;
       else if (j < n) ot[j] = sm.x[j];
     }
@@ -1826,7 +1852,7 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
         } else {
           // the two kept lists (one round trip)
           SmemSeq& q = sm.blk.q;
-          const size_t op = (size_t)(b * rps + n) * KEEP_CAP, oq = (size_t)(b * rps + jq) * KEEP_CAP;
+          const size_t op = (size_t)seq_row<RAG>(a, g, n) * KEEP_CAP, oq = (size_t)seq_row<RAG>(a, g, jq) * KEEP_CAP;
           for (int e = lane; e < np; e += 64) {
             q.pidx[e] = ld_dev(&a.kidx[op + e]);
             q.pprob[e] = ld_dev(&a.kprob[op + e]);
@@ -1863,18 +1889,18 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     const int n = sm.n;
     const bool res = n < K;
     const int jq = res ? K + 1 + n : n;
-    set_draw_row(&rr[n], true, 0, row_temp(a, b * rps + n).invT, sm.blk);
-    set_draw_row(&rr[jq], true, 1, row_temp(a, b * rps + jq).invT, sm.blk);
+    const int rn = seq_row<RAG>(a, g, n), rq = seq_row<RAG>(a, g, jq);
+    set_draw_row(&a.row[rn], true, 0, row_temp(a, rn).invT, sm.blk);
+    set_draw_row(&a.row[rq], true, 1, row_temp(a, rq).invT, sm.blk);
     double Z;
-    const int tok = full_row_sample<DT, WG>(a, (double)sm.u[K], row_ptr(a, b * rps + n, ESZ),
-                                            row_ptr(a, b * rps + jq, ESZ), res, sm.blk, &Z);
+    const int tok = full_row_sample<DT, WG>(a, (double)sm.u[K], row_ptr(a, rn, ESZ), row_ptr(a, rq, ESZ), res,
+                                            sm.blk, &Z);
     if (t == 0) {
-      a.out_tok[(size_t)b * (K + 1) + n] = tok;
+      a.out_tok[(size_t)b * (a.Kmax + 1) + n] = tok;
       if (a.out_z) a.out_z[b] = Z;
       if (a.out_px)
         a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll)
-                          : kept_prob<DT>(row_ptr(a, b * rps + n, ESZ), tok, load_row(&rr[n]), true,
-                                          row_temp(a, b * rps + n).invT);
+                          : kept_prob<DT>(row_ptr(a, rn, ESZ), tok, load_row(&a.row[rn]), true, row_temp(a, rn).invT);
     }
   }
 }
@@ -1889,21 +1915,22 @@ __device__ __forceinline__ double plain_weight(const char* pr, const char* qr, i
   return d > 0.0 ? d : 0.0;
 }
 
-template <int DT>
+template <int DT, bool RAG>
 __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   __shared__ Smem sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   const int t = threadIdx.x;
   const int b = (int)(blockIdx.x / (unsigned)a.nsc);
   const int c = (int)blockIdx.x - b * a.nsc;
-  const int K = a.K;
   const int nseg = a.nsc * SEG_PER_SCE;
   const SeqRec sr = a.seq[b];
   const int n = sr.n;
   const bool active = n >= 0;
+  const SeqGeo g = active ? seq_geo<RAG>(a, b) : SeqGeo{0, 0, 0, 0};
+  const int K = g.K;
   const bool res = active && n < K;
-  const int rlP = b * a.rps + (active ? n : 0);
-  const int rlQ = b * a.rps + (res ? K + 1 + n : (active ? n : 0));
+  const int rlP = seq_row<RAG>(a, g, active ? n : 0);
+  const int rlQ = seq_row<RAG>(a, g, res ? K + 1 + n : (active ? n : 0));
   const double iTp = row_temp(a, rlP).invT, iTq = row_temp(a, rlQ).invT;
   RowRec P, Q;
   const char* pr = nullptr;
@@ -1948,7 +1975,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   double Z;
   const double incl = block_incl_scan(loc, sm.red, &Z);
   lastseg = block_max_i(lastseg, sm.red);
-  const double u = (double)a.U[(size_t)b * (K + 1) + K];
+  const double u = (double)a.U[(size_t)g.t0 + K];
   int tok;
   if (!(Z > 0.0)) {
     // empty residual (round-off only): draw from p
@@ -1997,7 +2024,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     }
   }
   if (t == 0) {
-    a.out_tok[(size_t)b * (K + 1) + n] = tok;
+    a.out_tok[(size_t)b * (a.Kmax + 1) + n] = tok;
     if (a.out_z) a.out_z[b] = Z;
     if (a.out_px)
       a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll) : plain_weight<DT>(pr, qr, tok, P, Q, false, iTp, iTq);
@@ -2045,14 +2072,14 @@ static KFn pick_stream_mode(int mode, bool vec) {
   }
 }
 
-template <int DT>
+template <int DT, bool RAG>
 static KFn pick_row(int mode) {
   switch (mode) {
-    case M_PLAIN: return (KFn)row_kernel<DT, M_PLAIN>;
-    case M_TOPK: return (KFn)row_kernel<DT, M_TOPK>;
-    case M_TOPP: return (KFn)row_kernel<DT, M_TOPP>;
-    case M_TOPKP: return (KFn)row_kernel<DT, M_TOPKP>;
-    default: return (KFn)row_kernel<DT, M_GREEDY>;
+    case M_PLAIN: return (KFn)row_kernel<DT, M_PLAIN, RAG>;
+    case M_TOPK: return (KFn)row_kernel<DT, M_TOPK, RAG>;
+    case M_TOPP: return (KFn)row_kernel<DT, M_TOPP, RAG>;
+    case M_TOPKP: return (KFn)row_kernel<DT, M_TOPKP, RAG>;
+    default: return (KFn)row_kernel<DT, M_GREEDY, RAG>;
   }
 }
 
@@ -2074,13 +2101,17 @@ hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned 
 }
 
 hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
-  KFn f = dtype == D_BF16 ? pick_row<D_BF16>(mode) : pick_row<D_F32>(mode);
+  const bool rag = a.cu != nullptr;
+  KFn f = dtype == D_BF16 ? (rag ? pick_row<D_BF16, true>(mode) : pick_row<D_BF16, false>(mode))
+                          : (rag ? pick_row<D_F32, true>(mode) : pick_row<D_F32, false>(mode));
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s) {
-  KFn f = dtype == D_BF16 ? (KFn)sample_kernel<D_BF16> : (KFn)sample_kernel<D_F32>;
+  const bool rag = a.cu != nullptr;
+  KFn f = dtype == D_BF16 ? (rag ? (KFn)sample_kernel<D_BF16, true> : (KFn)sample_kernel<D_BF16, false>)
+                          : (rag ? (KFn)sample_kernel<D_F32, true> : (KFn)sample_kernel<D_F32, false>);
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
   return hipGetLastError();
 }

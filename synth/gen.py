@@ -145,3 +145,37 @@ def make_inputs(w: Workload) -> dict:
         tgt = f32_to_bf16_bits(tgt)
         drf = f32_to_bf16_bits(drf)
     return dict(target=tgt, draft=drf, uniforms=uniforms, draft_u=draft_u)
+
+
+def ragged_lengths(B: int, k_lo: int, k_hi: int, seed: int) -> np.ndarray:
+    """Per-sequence draft lengths, uniform on [k_lo, k_hi] (2 to 10 is the
+    range a draft-length controller keeps K in on page
+    www.2kiu.com/news/5895634 §4.4)."""
+    g = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(1000,)))
+    return g.integers(k_lo, k_hi + 1, size=B).astype(np.int64)
+
+
+def pack_ragged(d: dict, ks) -> dict:
+    """A ragged batch cut from a rectangular one drawn at K >= max(ks):
+    sequence b keeps its first K_b + 1 target rows, its first K_b draft rows
+    and draft-sampling uniforms, and its first K_b + 1 uniforms (the last of
+    them is its sampling uniform).  Returns
+
+    target   [N + B, V]  sequence b's rows from row cu[b] + b
+    draft    [N, V]      its draft rows from row cu[b]
+    uniforms [N + B]     float32, from cu[b] + b
+    draft_u  [N]         float64, from cu[b]
+    cu       [B + 1]     int32 offsets, N = cu[B]
+    """
+    ks = np.asarray(ks, dtype=np.int64)
+    B = ks.shape[0]
+    if d["target"].shape[0] != B or np.any(ks < 0) or np.any(ks > d["draft"].shape[1]):
+        raise ValueError("need one length in [0, K] per sequence")
+    cu = np.concatenate([[0], np.cumsum(ks)]).astype(np.int32)
+    V = d["target"].shape[2]
+    tgt = np.concatenate([d["target"][b, :k + 1] for b, k in enumerate(ks)])
+    drf = (np.concatenate([d["draft"][b, :k] for b, k in enumerate(ks)]) if cu[-1] > 0
+           else np.zeros((0, V), dtype=d["draft"].dtype))
+    uni = np.concatenate([d["uniforms"][b, :k + 1] for b, k in enumerate(ks)]).astype(np.float32)
+    du = np.concatenate([d["draft_u"][b, :k] for b, k in enumerate(ks)]) if cu[-1] > 0 else np.zeros(0)
+    return dict(target=np.ascontiguousarray(tgt), draft=np.ascontiguousarray(drf), uniforms=uni, draft_u=du, cu=cu)

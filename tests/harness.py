@@ -85,3 +85,77 @@ def compare(w: Workload, d: dict, x: np.ndarray, dev_tok, dev_n, dev_dbg=None, p
             stats["max_prob_err"] = float(err)
     stats["flags"] = flags
     return stats, fails
+
+
+# ---------------------------------------------------------------------------
+# ragged batches (a draft length per sequence)
+# ---------------------------------------------------------------------------
+def ragged_draft_tokens(w: Workload, r: dict, Td=None) -> np.ndarray:
+    """x ~ filtered q for every packed draft row, with its draft-sampling
+    uniform (greedy: the row's arg-max)."""
+    if r["draft"].shape[0] == 0:
+        return np.zeros(0, dtype=np.int32)
+    T = w.temperature if Td is None or w.temperature == 0.0 else Td
+    rows = oracle.widen(r["draft"], w.dtype)
+    return oracle.sample_tokens(rows, T, w.top_k, w.top_p, r["draft_u"]).astype(np.int32)
+
+
+def run_device_ragged(w: Workload, r: dict, x: np.ndarray, max_k: int, debug: bool = True, draft_temperature=None,
+                      cu=None):
+    import torch
+
+    from rejection_sampling_verify_09_amd import spec_verify_ragged
+
+    tgt = to_device(r["target"], w.dtype)
+    drf = to_device(r["draft"], w.dtype) if r["draft"].shape[0] > 0 else None
+    X = torch.from_numpy(x.astype(np.int32)).cuda()
+    U = torch.from_numpy(r["uniforms"]).cuda()
+    CU = torch.from_numpy((r["cu"] if cu is None else cu).astype(np.int32)).cuda()
+    res = spec_verify_ragged(tgt, drf, X, U, CU, max_k, w.temperature, w.top_k, w.top_p,
+                             draft_temperature=draft_temperature, debug=debug)
+    torch.cuda.synchronize()
+    return [v.cpu().numpy() if not isinstance(v, dict) else {k: t.cpu().numpy() for k, t in v.items()} for v in res]
+
+
+def compare_ragged(w: Workload, r: dict, x: np.ndarray, max_k: int, dev_tok, dev_n, dev_dbg=None,
+                   draft_temperature=None):
+    """Ragged device outputs against the oracle; near-ties classified per
+    sequence exactly as for rectangular batches."""
+    cu = r["cu"].astype(np.int64)
+    B = cu.shape[0] - 1
+    ref_tok, ref_n, ref_dg = oracle.verify_ragged(r["target"], r["draft"], x, r["uniforms"], cu, w.temperature,
+                                                  w.top_k, w.top_p, dtype=w.dtype, max_k=max_k, diag=True,
+                                                  draft_temperature=draft_temperature)
+    stats = dict(match=0, flagged=0, fail=0, max_prob_err=0.0)
+    fails, flags = [], []
+    for b in range(B):
+        if dev_n[b] == ref_n[b] and np.array_equal(dev_tok[b], ref_tok[b]):
+            stats["match"] += 1
+            continue
+        c0, c1 = int(cu[b]), int(cu[b + 1])
+        K = c1 - c0
+        t0 = c0 + b
+        if np.any(dev_tok[b, K + 1:] != -1):
+            stats["fail"] += 1
+            fails.append((b, "entries past the sequence's own K are not -1"))
+            continue
+        v, why = oracle.classify(r["target"][t0:t0 + K + 1], r["draft"][c0:c1], x[c0:c1], r["uniforms"][t0:t0 + K + 1],
+                                 w.temperature, w.top_k, w.top_p, w.dtype, dev_tok[b, :K + 1], dev_n[b],
+                                 draft_temperature=draft_temperature)
+        if v == oracle.MATCH:
+            stats["match"] += 1
+        elif v == oracle.FLAGGED:
+            stats["flagged"] += 1
+            flags.append((b, why))
+        else:
+            stats["fail"] += 1
+            fails.append((b, why))
+    if dev_dbg is not None and cu[-1] > 0:
+        ok = np.repeat(ref_n >= 0, np.diff(cu))
+        if ok.any():
+            err = np.abs(dev_dbg["p"][ok] - ref_dg["px"][ok]).max()
+            if w.temperature != 0.0:
+                err = max(err, np.abs(dev_dbg["q"][ok] - ref_dg["qx"][ok]).max())
+            stats["max_prob_err"] = float(err)
+    stats["flags"] = flags
+    return stats, fails

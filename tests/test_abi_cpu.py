@@ -21,7 +21,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_spec_verify_dt", "sv_filtered_probs", "sv_sample",
+    for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_spec_verify_dt", "sv_spec_verify_ragged",
+              "sv_filtered_probs", "sv_sample", "sv_dynk_create", "sv_dynk_observe", "sv_dynk_k", "sv_dynk_destroy",
               "sv_release", "sv_scratch_bytes",
               "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
         assert s in syms
@@ -131,3 +132,74 @@ def test_profile_without_calls_reports_nothing():
     L.profile_start()
     r = L.profile_stop()
     assert r == dict(stream_kernel_ms=0.0, other_kernels_ms=0.0, calls=0)
+
+
+def test_ragged_validation():
+    def f(B=3, N=5, max_k=4, V=16, T=1.0, Td=1.0, dtype=0, cu=FAKE, tgt=FAKE, drf=FAKE, X=FAKE, U=FAKE, out_t=FAKE,
+          out_n=FAKE):
+        return L.lib().sv_spec_verify_ragged(tgt, drf, X, U, cu, T, Td, 0, 1.0, out_t, out_n, None, None, None, B, N,
+                                             max_k, V, dtype, None)
+    assert f(B=-1) == L.SV_ERR_SHAPE
+    assert f(N=-1) == L.SV_ERR_SHAPE
+    assert f(max_k=-1) == L.SV_ERR_SHAPE
+    assert f(max_k=L.SV_MAX_K + 1) == L.SV_ERR_SHAPE
+    assert f(N=13, max_k=4) == L.SV_ERR_SHAPE       # more drafts than B * max_k
+    assert f(V=0) == L.SV_ERR_SHAPE
+    assert f(dtype=9) == L.SV_ERR_DTYPE
+    assert f(Td=0.0) == L.SV_ERR_PARAM
+    assert f(cu=None) == L.SV_ERR_NULL
+    assert f(X=None) == L.SV_ERR_NULL
+    assert f(drf=None) == L.SV_ERR_NULL
+    assert f(U=None) == L.SV_ERR_NULL
+    assert f(out_t=None) == L.SV_ERR_NULL
+    assert f(out_n=None) == L.SV_ERR_NULL
+    # no drafts at all: neither drafted tokens nor draft logits are needed
+    assert f(N=0, X=None, drf=None, U=None) == L.SV_ERR_NULL
+    # greedy: no draft logits needed
+    assert f(T=0.0, drf=None, U=None) == L.SV_ERR_NULL
+    assert f(B=0, N=0, cu=None, tgt=None, drf=None, X=None, U=None, out_t=None, out_n=None) == L.SV_OK
+
+
+def test_controller_matches_the_oracle():
+    """The library's controller (host code) against the oracle's on random
+    acceptance traces, several lanes at once."""
+    import numpy as np
+    from oracle import DynamicK
+    rng = np.random.default_rng(5)
+    for window, lo, hi, kmin, kmax, k0 in [(100, 0.6, 0.8, 2, 10, 5), (3, 0.6, 0.8, 2, 4, 3), (1, 0.5, 0.5, 0, 6, 0),
+                                           (7, 0.3, 0.9, 1, 12, 12)]:
+        lanes = 6
+        c = L.DraftLengthController(lanes, window, hi, lo, kmin, kmax, k0)
+        ref = [DynamicK(window, hi, lo, kmin, kmax, k0) for _ in range(lanes)]
+        bias = rng.random(lanes)
+        for step in range(3000):
+            ks = [r.k for r in ref]
+            dr = [int(k * rng.integers(0, 3)) if rng.random() < 0.95 else 0 for k in ks]
+            acc = [int(rng.binomial(d, bias[i])) for i, d in enumerate(dr)]
+            got = c.observe(acc, dr)
+            want = [r.observe(a, d) for r, a, d in zip(ref, acc, dr)]
+            assert got == want, (window, step)
+            if step % 500 == 0:
+                bias = rng.random(lanes)
+        assert [c.k(i) for i in range(lanes)] == [r.k for r in ref]
+        c.close()
+
+
+def test_controller_errors():
+    lib = L.lib()
+    assert not lib.sv_dynk_create(0, 100, 0.8, 0.6, 2, 10, 5)
+    assert not lib.sv_dynk_create(1, 0, 0.8, 0.6, 2, 10, 5)
+    assert not lib.sv_dynk_create(1, 100, 0.5, 0.6, 2, 10, 5)   # lower above raise
+    assert not lib.sv_dynk_create(1, 100, 0.8, 0.6, 2, 10, 11)  # start outside [k_min, k_max]
+    assert not lib.sv_dynk_create(1, 100, 1.5, 0.6, 2, 10, 5)
+    c = L.DraftLengthController(2, window=2, k_init=5)
+    with pytest.raises(L.SpecVerifyError):
+        c.observe([3, 1], [2, 1])          # accepted above drafted: nothing recorded
+    with pytest.raises(L.SpecVerifyError):
+        c.observe([-1, 0], [2, 1])
+    assert c.observe([2, 2], [2, 2]) == [5, 5]
+    assert c.observe([2, 0], [2, 2]) == [6, 4]
+    assert lib.sv_dynk_observe(None, None, None, None) == L.SV_ERR_NULL
+    assert lib.sv_dynk_k(None, 0) == -1 and c.k(2) == -1 and c.k(0) == 6
+    lib.sv_dynk_destroy(None)
+    c.close()
