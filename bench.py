@@ -3,12 +3,17 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --sampler [--steps K] [--warmup W] [--workload NAME]
     python bench.py --draft-temperature TD [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --ragged K_LO K_HI [--steps K] [--warmup W] [--workload NAME]
 
 One step = one sv_spec_verify call (the whole hot path: streaming pass,
 filter thresholds, accept tests, first-rejection scan, final draw) over one
 batch whose logits are already resident in HBM.  The input batch is rotated
 over several device copies whose total exceeds the 256 MB last-level cache,
 so every step reads its logits from HBM.  Prints one JSON line.
+
+With --ragged K_LO K_HI, one step is one sv_spec_verify_ragged call over a
+batch whose sequences draft K_b ~ uniform[K_LO, K_HI] tokens each (drafts
+drawn on the GPU before timing).
 
 With --sampler, one step is one sv_sample call (the drafting draw: x ~ q and
 q(x)) over the workload's B*K draft rows, with their draft uniforms.  With
@@ -57,7 +62,8 @@ def load_draft_tokens(name: str, B: int, K: int):
 def measured_traffic(key: str):
     """HBM bytes per launch of the streaming kernel from the committed counter
     summary for ``key`` (the workload name, "sample-" + name for the draft
-    draw), or None when the summary is absent or predates the kernel source."""
+    draw, "ragged-LO-HI-" + name for a ragged batch), or None when the summary
+    is absent or predates the kernel source."""
     path = os.path.join(PROFILES, f"traffic_stream_kernel_{key}.md")
     if not os.path.exists(path):
         return None
@@ -187,6 +193,114 @@ def run_sampler(args, w, d):
     print(json.dumps(result), flush=True)
 
 
+def run_ragged(args, w, k_lo: int, k_hi: int):
+    """Verification of a batch whose sequences draft between k_lo and k_hi
+    tokens each (sv_spec_verify_ragged), rows cut from the workload drawn at
+    K = k_hi; the drafts are drawn on the GPU before timing."""
+    from dataclasses import replace
+
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_09_amd import profile_start, profile_stop, sample, spec_verify_ragged
+    from synth import make_inputs, pack_ragged, ragged_lengths
+
+    wk = replace(w, K=k_hi)
+    ks = ragged_lengths(w.B, k_lo, k_hi, w.seed)
+    r = pack_ragged(make_inputs(wk), ks)
+    N = int(r["cu"][-1])
+    esz = 2 if w.dtype == "bf16" else 4
+    rows = (N + w.B) + (0 if w.temperature == 0.0 else N)
+    bytes_per_step = rows * w.V * esz
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    tgt0, drf0 = dev(r["target"]), dev(r["draft"])
+    ud = torch.from_numpy(r["draft_u"].astype(np.float32)).cuda()
+    xt, _ = sample(drf0, ud, w.temperature, w.top_k, w.top_p, with_prob=False)  # x ~ q, not timed
+    R = args.copies or max(3, -(-640_000_000 // bytes_per_step))
+    tgts = [tgt0] + [tgt0.clone() for _ in range(R - 1)]
+    drfs = [drf0] + [drf0.clone() for _ in range(R - 1)]
+    U = torch.from_numpy(r["uniforms"]).cuda()
+    CU = torch.from_numpy(r["cu"]).cuda()
+    out_t = torch.empty((w.B, k_hi + 1), dtype=torch.int32, device="cuda")
+    out_n = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        spec_verify_ragged(tgts[i % R], drfs[i % R], xt, U, CU, k_hi, w.temperature, w.top_k, w.top_p,
+                           out_tokens=out_t, out_num_accepted=out_n)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    profile_start()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = profile_stop()
+    stream_ms = prof["stream_kernel_ms"] / max(1, prof["calls"])
+    other_ms = prof["other_kernels_ms"] / max(1, prof["calls"])
+    n_host = out_n.cpu().numpy()
+    emitted = int(np.sum(n_host[n_host >= 0] + 1))
+    achieved = bytes_per_step / (stream_ms / 1e3) / 1e9
+    result = {
+        "metric": f"spec-verify sequences/s + % HBM peak at B={w.B} K_b in [{k_lo},{k_hi}] V={w.V} {w.dtype} "
+                  "(ragged)",
+        "value": w.B / (ms_per_step / 1e3),
+        "unit": "sequences/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded logits of the workload's shape; no model weights)",
+        "config": {"workload": f"{w.name} with K_b uniform in [{k_lo}, {k_hi}]", "B": w.B, "total_drafts": N,
+                   "mean_K": N / w.B, "V": w.V, "logits": w.dtype, "temperature": w.temperature, "top_k": w.top_k,
+                   "top_p": w.top_p, "rows": rows, "input_copies": R, "logit_bytes_per_step": bytes_per_step},
+        "tokens_per_s": emitted / (ms_per_step / 1e3),
+        "mean_emitted_per_sequence": emitted / w.B,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(f"ragged-{k_lo}-{k_hi}-{w.name}"),
+            "kernel": "stream_kernel", "kernel_ms": stream_ms, "other_kernels_ms": other_ms,
+            "timed_calls": prof["calls"],
+            "step_frac": bytes_per_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        x = xt.cpu().numpy()
+        t0 = time.perf_counter()
+        n_done = 0
+        while True:
+            oracle.verify_ragged(r["target"], r["draft"], x, r["uniforms"], r["cu"], w.temperature, w.top_k,
+                                 w.top_p, dtype=w.dtype, max_k=k_hi)
+            n_done += w.B
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        result["cpu_baseline"] = dict(value=n_done / el, unit="sequences/s", cores=1, kind="oracle",
+                                      sample=f"{n_done // w.B} x the full ragged {w.B}-sequence batch, fp64 NumPy, "
+                                             f"single thread, {el:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +316,9 @@ def main():
                     help="measure the drafting draw (sv_sample) over the workload's draft rows instead")
     ap.add_argument("--draft-temperature", type=float, default=None,
                     help="verify drafts drawn (on the GPU) at this temperature (sv_spec_verify_dt)")
+    ap.add_argument("--ragged", type=int, nargs=2, metavar=("K_LO", "K_HI"), default=None,
+                    help="verify a batch whose sequences draft K_b ~ uniform[K_LO, K_HI] tokens "
+                         "(sv_spec_verify_ragged)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -235,6 +352,9 @@ def main():
 
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
+    if args.ragged:
+        run_ragged(args, w, *args.ragged)
+        return
     d = make_inputs(w)
     if args.sampler:
         run_sampler(args, w, d)
