@@ -40,10 +40,13 @@ def _token_reachable(w, u, g, eps):
     return hi > t - eps * Z and lo <= t + eps * Z
 
 
-def _rows_with_top_p(target_b, draft_b, T, top_k, top_p, dtype, pos, Td=None):
+def _rows_with_top_p(target_b, draft_b, T, top_k, top_p, dtype, pos, Td=None, qprobs_b=None):
     t = widen(target_b[pos:pos + 1], dtype)
     P = filtered_probs(t, T, top_k, top_p)[0]
-    if pos < draft_b.shape[0]:
+    if qprobs_b is not None:
+        # a q given as probabilities does not depend on the filters
+        Q = np.asarray(qprobs_b[pos], dtype=np.float64) if pos < qprobs_b.shape[0] else None
+    elif pos < draft_b.shape[0]:
         Q = filtered_probs(widen(draft_b[pos:pos + 1], dtype), T if Td is None or T == 0.0 else Td, top_k, top_p)[0]
     else:
         Q = None
@@ -51,17 +54,18 @@ def _rows_with_top_p(target_b, draft_b, T, top_k, top_p, dtype, pos, Td=None):
 
 
 def classify(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype,
-             dev_tokens_b, dev_n_b, eps: float = 1e-5, draft_temperature=None):
-    """Return (verdict, reason) for one sequence.  verdict in {match, flagged, fail}."""
+             dev_tokens_b, dev_n_b, eps: float = 1e-5, draft_temperature=None, draft_probs_b=None):
+    """Return (verdict, reason) for one sequence.  verdict in {match, flagged, fail}.
+    draft_probs_b: the sequence's q given as probabilities [K, V] (draft_b unused)."""
     ref = verify_one(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype=dtype,
-                     draft_temperature=draft_temperature)
+                     draft_temperature=draft_temperature, draft_probs_b=draft_probs_b)
     dev_tokens_b = np.asarray(dev_tokens_b).astype(np.int64)
     dev_n = int(dev_n_b)
     if dev_n == ref["n"] and np.array_equal(dev_tokens_b, ref["out_tokens"].astype(np.int64)):
         return MATCH, ""
     if ref["n"] < 0 or dev_n < 0:
         return FAIL, f"sentinel mismatch: oracle n={ref['n']} device n={dev_n}"
-    K = draft_b.shape[0]
+    K = np.asarray(x_b).shape[0]
     u = np.asarray(u_b, dtype=np.float32).astype(np.float64)
     # the accepted prefix must be the drafted tokens themselves
     m = min(ref["n"], dev_n)
@@ -77,7 +81,8 @@ def classify(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype,
         if qx > 0.0 and abs(u[i0] - px / qx) <= eps:
             return FLAGGED, f"accept near-tie at position {i0}: u={u[i0]:.9g} p/q={px / qx:.9g}"
         for tp2 in tp_perturb:
-            P, Q = _rows_with_top_p(target_b, draft_b, temperature, top_k, tp2, dtype, i0, draft_temperature)
+            P, Q = _rows_with_top_p(target_b, draft_b, temperature, top_k, tp2, dtype, i0, draft_temperature,
+                                    draft_probs_b)
             x = int(x_b[i0])
             if (u[i0] * Q[x] < P[x]) != bool(ref["accept"][i0]):
                 return FLAGGED, f"top-p boundary near-tie at position {i0}"
@@ -88,7 +93,8 @@ def classify(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype,
     if _token_reachable(ref["w"], u[K], g, eps):
         return FLAGGED, f"sampling near-tie at position {n}: token {g} vs oracle {ref['token']}"
     for tp2 in tp_perturb:
-        P, Q = _rows_with_top_p(target_b, draft_b, temperature, top_k, tp2, dtype, n, draft_temperature)
+        P, Q = _rows_with_top_p(target_b, draft_b, temperature, top_k, tp2, dtype, n, draft_temperature,
+                                draft_probs_b)
         if n < K:
             w = np.maximum(0.0, P - Q)
             if w.sum() == 0.0:

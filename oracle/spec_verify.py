@@ -276,14 +276,30 @@ def _draft_temperature(T, draft_temperature, k, tp):
     return Td
 
 
+def _given_draft_probs(q, dtype_ok=(np.float32, np.float64)):
+    """A draft distribution supplied as probabilities (the q the drafts were
+    actually drawn from), widened exactly to float64."""
+    q = np.asarray(q)
+    if q.dtype not in dtype_ok:
+        raise TypeError("draft probabilities must be float32 (or float64)")
+    q = q.astype(np.float64)
+    if np.isnan(q).any() or np.isinf(q).any() or (q < 0).any():
+        raise ValueError("draft probabilities must be finite and >= 0")
+    return q
+
+
 def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
-           dtype: str = F32, block: int | None = None, diag: bool = False, draft_temperature=None):
+           dtype: str = F32, block: int | None = None, diag: bool = False, draft_temperature=None,
+           draft_probs=None):
     """Run verification for a batch.
 
     target: [B, K+1, V] logits (float32, or uint16 bf16 patterns when
     dtype == "bf16"); draft: [B, K, V]; draft_tokens: [B, K] ints;
     uniforms: float32 [B, K+1].  draft_temperature: the temperature the
     drafts were sampled at, when it differs from the target's.
+    draft_probs: [B, K, V] float32 probabilities to use as q directly, in
+    place of the draft logits (which are then not read and may be None);
+    the rule is unchanged, and lossless for drafts drawn from that q.
 
     Returns (out_tokens int32 [B, K+1], out_num_accepted int32 [B]) and, when
     ``diag``, a dict with p(x_i), q(x_i) float64 [B, K] and Z float64 [B].
@@ -291,13 +307,16 @@ def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
     T, k, tp = _check_params(temperature, top_k, top_p)
     Td = _draft_temperature(T, draft_temperature, k, tp)
     target = np.asarray(target)
-    draft = np.asarray(draft)
     X = np.asarray(draft_tokens).astype(np.int64)
     U = np.asarray(uniforms)
     if U.dtype != np.float32:
         raise TypeError("uniforms must be float32")
     B, K1, V = target.shape
     K = K1 - 1
+    if draft_probs is not None:
+        draft = _given_draft_probs(draft_probs)
+    else:
+        draft = np.asarray(draft)
     if draft.shape != (B, K, V) or X.shape != (B, K) or U.shape != (B, K + 1):
         raise ValueError("shape mismatch")
     out_tok = np.full((B, K + 1), -1, dtype=np.int32)
@@ -316,7 +335,10 @@ def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
         _check_finite(t64)
         P = filtered_probs(t64.reshape(nb * (K + 1), V), T, k, tp).reshape(nb, K + 1, V)
         del t64
-        Q = _draft_probs(draft[s:e], dtype, Td, k, tp)
+        if draft_probs is not None:
+            Q = draft[s:e]
+        else:
+            Q = _draft_probs(draft[s:e], dtype, Td, k, tp)
         x = X[s:e]
         u = U[s:e].astype(np.float64)
         # bad sequences: a row with no distribution, or a drafted token out of range
@@ -441,21 +463,28 @@ def verify_ragged(target, draft, draft_tokens, uniforms, cu_num_draft, temperatu
     return out_tok, out_n
 
 
-def verify_one(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype: str = F32, draft_temperature=None):
+def verify_one(target_b, draft_b, x_b, u_b, temperature, top_k, top_p, dtype: str = F32, draft_temperature=None,
+               draft_probs_b=None):
     """All intermediate values for one sequence (used to classify a mismatch).
 
     Returns a dict: P [K+1, V], Q [K, V], px, qx, accept [K], n, w [V],
     Z, C [V], token.  The arithmetic is exactly that of ``verify``.
+    draft_probs_b: [K, V] probabilities used as q (draft_b is then ignored).
     """
-    out_tok, out_n = verify(target_b[None], draft_b[None], np.asarray(x_b)[None],
+    dp = None if draft_probs_b is None else np.asarray(draft_probs_b)[None]
+    out_tok, out_n = verify(target_b[None], None if dp is not None else draft_b[None], np.asarray(x_b)[None],
                             np.asarray(u_b, dtype=np.float32)[None],
-                            temperature, top_k, top_p, dtype=dtype, draft_temperature=draft_temperature)
+                            temperature, top_k, top_p, dtype=dtype, draft_temperature=draft_temperature,
+                            draft_probs=dp)
     T, k, tp = _check_params(temperature, top_k, top_p)
     Td = _draft_temperature(T, draft_temperature, k, tp)
-    K = draft_b.shape[0]
+    K = np.asarray(x_b).shape[0]
     V = target_b.shape[-1]
     P = filtered_probs(widen(target_b, dtype), T, k, tp)
-    Q = _draft_probs(np.asarray(draft_b)[None], dtype, Td, k, tp)[0]
+    if dp is not None:
+        Q = _given_draft_probs(dp)[0]
+    else:
+        Q = _draft_probs(np.asarray(draft_b)[None], dtype, Td, k, tp)[0]
     x = np.clip(np.asarray(x_b, dtype=np.int64), 0, V - 1)
     u = np.asarray(u_b, dtype=np.float32).astype(np.float64)
     px = P[np.arange(K), x]

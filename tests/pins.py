@@ -311,3 +311,30 @@ def check_zero_weight_never_sampled(mod):
     assert tok[0, 0] in (2, 3, 5), "a zero-weight token was sampled"
     tok, n = mod.verify(tl[None], tl[None, :1], np.array([[3]]), u, 1.0, 0, 1.0)
     assert n[0] == 1 and tok[0, 1] == 2, "bonus at u = 0 must be the first positive-weight token"
+
+
+# ---------------------------------------------------------------------------
+# q supplied as probabilities (the distribution the drafts were drawn from)
+# ---------------------------------------------------------------------------
+def check_lossless_draft_probs(mod, N: int = 300_000, seed: int = 31):
+    """Drafts drawn from arbitrary given distributions q_i (Dirichlet draws,
+    one token of each given zero mass), verified with q_i supplied as
+    probabilities: every emitted token follows the target p (the same law as
+    with logits, page www.cf-1.com/news/5155685 §2.2)."""
+    V, K = 8, 3
+    rng = np.random.default_rng(seed)
+    tl = rng.normal(0, 1.5, (K + 1, V)).astype(np.float32)
+    P = softmax_rows(tl)
+    Q = rng.dirichlet(np.full(V, 0.7), size=K)
+    Q[np.arange(K), rng.integers(0, V, K)] = 0.0
+    Q = (Q / Q.sum(axis=1, keepdims=True)).astype(np.float32)
+    Q64 = Q.astype(np.float64)
+    x = np.stack([rng.choice(V, size=N, p=Q64[i] / Q64[i].sum()) for i in range(K)], axis=1)
+    u = rng.random((N, K + 1), dtype=np.float32)
+    tok, n = mod.verify(tile_rows(tl, N), None, x, u, 1.0, 0, 1.0, draft_probs=tile_rows(Q, N))
+    assert np.all((n >= 0) & (n <= K))
+    for j in range(K + 1):
+        sel = n >= j
+        counts = np.bincount(tok[sel, j], minlength=V)
+        pv = _chi2_pvalue(counts, P[j])
+        assert pv > CHI2_MIN_P, f"given q: position {j} differs from p (chi2 p={pv:.2e})"

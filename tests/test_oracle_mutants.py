@@ -51,6 +51,9 @@ MUTANTS = {
     # greedy ties to the highest index
     "greedy_ties": ("a = np.argmax(z, axis=1)", "a = z.shape[1] - 1 - np.argmax(z[:, ::-1], axis=1)",
                     lambda m: pins.check_greedy(m)),
+    # given draft probabilities used at the wrong position
+    "draft_probs_position": ("            Q = draft[s:e]\n", "            Q = np.roll(draft[s:e], 1, axis=1)\n",
+                             lambda m: pins.check_lossless_draft_probs(m, N=150_000)),
     # ragged: a sequence's uniforms taken from its draft offset, not cu[b] + b
     "ragged_uniform_base": ("U[t_idx]", "U[t_idx - bs[:, None]]",
                             lambda m: rag.check_ragged_worked_case(m)),

@@ -224,3 +224,63 @@ def test_draft_temperature_equal_or_greedy_changes_nothing():
     assert all(np.array_equal(i, j) for i, j in zip(g, h))
     with pytest.raises(ValueError):
         oracle.verify(tl, dl, x, u, 1.0, 0, 1.0, draft_temperature=0.0)
+
+
+def test_draft_probs_keep_the_law():
+    pins.check_lossless_draft_probs(ov)
+
+
+def test_draft_probs_count_law():
+    """q given as probabilities with sum_x min(p, q) = alpha exactly: the
+    accepted count is truncated geometric."""
+    rng = np.random.default_rng(9)
+    V, K, alpha, N = 8, 4, 0.6, 100_000
+    h = V // 2
+    tl = np.full((K + 1, V), -np.inf, dtype=np.float32)
+    Q = np.zeros((K, V))
+    for i in range(K + 1):
+        p = rng.dirichlet(np.ones(h))
+        tl[i, :h] = np.log(p)
+        if i < K:
+            Q[i] = np.concatenate([alpha * p, (1 - alpha) * rng.dirichlet(np.ones(V - h))])
+    P = pins.softmax_rows(tl)
+    Q32 = Q.astype(np.float32)
+    a_true = np.minimum(P[:K], Q32.astype(np.float64)).sum(axis=1)
+    x = np.stack([rng.choice(V, size=N, p=Q[i]) for i in range(K)], axis=1)
+    u = rng.random((N, K + 1), dtype=np.float32)
+    _, n = ov.verify(pins.tile_rows(tl, N), None, x, u, 1.0, 0, 1.0, draft_probs=pins.tile_rows(Q32, N))
+    probs = np.empty(K + 1)
+    run = 1.0
+    for j in range(K):
+        probs[j] = run * (1 - a_true[j])
+        run *= a_true[j]
+    probs[K] = run
+    assert pins._chi2_pvalue(np.bincount(n, minlength=K + 1), probs) > pins.CHI2_MIN_P
+
+
+def test_draft_probs_equal_to_the_logit_q_reproduce_verify():
+    """Consistency: q supplied as the filtered draft distribution (float64)
+    gives exactly the logit path's outcome."""
+    rng = np.random.default_rng(12)
+    B, K, V = 6, 3, 50
+    t = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    d = (t[:, :K] + rng.normal(0, .6, (B, K, V))).astype(np.float32)
+    x = rng.integers(0, V, (B, K))
+    u = rng.random((B, K + 1), dtype=np.float32)
+    for T, k, p in ((1.0, 0, 1.0), (0.8, 7, 0.9), (0.0, 0, 1.0)):
+        Q = ov.filtered_probs(d.reshape(-1, V).astype(np.float64), T, k, p).reshape(B, K, V)
+        a = ov.verify(t, d, x, u, T, k, p, diag=True)
+        b = ov.verify(t, None, x, u, T, k, p, diag=True, draft_probs=Q)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        if T > 0:
+            assert np.array_equal(a[2]["qx"], b[2]["qx"]) and np.array_equal(a[2]["Z"], b[2]["Z"])
+
+
+def test_draft_probs_validation():
+    t = np.zeros((1, 2, 4), np.float32)
+    u = np.zeros((1, 2), np.float32)
+    for bad in (np.array([[[0.5, -0.1, 0.3, 0.3]]], np.float32), np.array([[[np.nan, 0, 0, 1]]], np.float32)):
+        with pytest.raises(ValueError):
+            ov.verify(t, None, np.zeros((1, 1)), u, 1.0, 0, 1.0, draft_probs=bad)
+    with pytest.raises(TypeError):
+        ov.verify(t, None, np.zeros((1, 1)), u, 1.0, 0, 1.0, draft_probs=np.zeros((1, 1, 4), np.float16))
