@@ -190,6 +190,35 @@ int sv_spec_verify_ragged(const void* target_logits, const void* draft_logits,
                           int32_t V, int32_t dtype, void* stream);
 
 /*
+ * sv_spec_verify_probs - sv_spec_verify (with the outputs of
+ * sv_spec_verify_debug) where each draft distribution q_i is supplied as
+ * probabilities instead of logits: the distribution the draft actually drew
+ * x_i from, whatever sampling pipeline produced it (page www.2kiu.com/news/
+ * 5895634 section 7: the drafts are verified against the q they were drawn
+ * from, which keeps the output law p).  The target rows are filtered by
+ * temperature, top_k and top_p as usual; q_i is used exactly as given.
+ *
+ * draft_probs  [B, K, V] float32, device   q_i(j) >= 0, each row summing to 1
+ *                                          (not checked; entries above 1,
+ *                                          negative or non-finite values are
+ *                                          outside the defined range)
+ * Other arguments as sv_spec_verify_debug (out_q returns the given q_i(x_i)).
+ *
+ * Only the target rows are streamed: q enters through q_i(x_i) and, after a
+ * rejection at position n, through q_n at the tokens the residual
+ * max(0, p_n - q_n) can be positive on (the target's kept set; every token
+ * of an unfiltered row).  draft_probs may be NULL when temperature == 0
+ * (greedy verification does not use q) or K == 0.
+ */
+int sv_spec_verify_probs(const void* target_logits, const float* draft_probs,
+                         const int32_t* draft_tokens, const float* uniforms,
+                         float temperature, int32_t top_k, float top_p,
+                         int32_t* out_tokens, int32_t* out_num_accepted,
+                         double* out_p, double* out_q, double* out_z,
+                         int32_t B, int32_t K, int32_t V, int32_t dtype,
+                         void* stream);
+
+/*
  * Draft-length controller (host only; no device work).  The rule of page
  * www.2kiu.com/news/5895634 section 4.4 (the policy of page
  * www.cf-1.com/news/5155685 section 2.4): keep the acceptance statistics of
@@ -269,7 +298,8 @@ int sv_sample(const void* logits, const float* uniforms, float temperature,
 /*
  * Launch timing for benchmarks.  Between sv_profile_start() and
  * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug /
- * sv_spec_verify_dt / sv_spec_verify_ragged / sv_sample call records three HIP events on its own
+ * sv_spec_verify_dt / sv_spec_verify_ragged / sv_spec_verify_probs /
+ * sv_sample call records three HIP events on its own
  * stream: before its streaming kernel (the pass that reads every logit once),
  * after it, and after the call's last kernel.  sv_profile_stop() waits for
  * the recorded events and returns the summed durations in milliseconds of the

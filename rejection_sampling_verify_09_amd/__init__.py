@@ -16,9 +16,10 @@ from ._lib import (  # noqa: F401
     release,
     sample,
     spec_verify,
+    spec_verify_probs,
     spec_verify_ragged,
     status_string,
 )
 
-__all__ = ["spec_verify", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
+__all__ = ["spec_verify", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
            "SpecVerifyError"]

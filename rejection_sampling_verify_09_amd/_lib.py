@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.sv_spec_verify_ragged.argtypes = [vp, vp, vp, vp, vp, f32, f32, i32, f32, vp, vp, vp, vp, vp, i32, i32, i32,
                                             i32, i32, vp]
         L.sv_spec_verify_ragged.restype = ctypes.c_int
+        L.sv_spec_verify_probs.argtypes = [vp, vp, vp, vp, f32, i32, f32, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        L.sv_spec_verify_probs.restype = ctypes.c_int
         L.sv_dynk_create.argtypes = [i32, i32, ctypes.c_double, ctypes.c_double, i32, i32, i32]
         L.sv_dynk_create.restype = vp
         L.sv_dynk_observe.argtypes = [vp, vp, vp, vp]
@@ -226,6 +228,54 @@ def spec_verify_ragged(target_logits: torch.Tensor, draft_logits: torch.Tensor |
                                      out_z.data_ptr() if debug else None, B, N, int(max_k), V, code, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_spec_verify_ragged")
+    if debug:
+        return out_tokens, out_num_accepted, dict(p=out_p, q=out_q, z=out_z)
+    return out_tokens, out_num_accepted
+
+
+def spec_verify_probs(target_logits: torch.Tensor, draft_probs: torch.Tensor | None, draft_tokens: torch.Tensor,
+                      uniforms: torch.Tensor, temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+                      out_tokens: torch.Tensor | None = None, out_num_accepted: torch.Tensor | None = None,
+                      stream=None, debug: bool = False):
+    """Verify one round of drafted tokens whose draft distributions are given
+    as probabilities: target_logits [B, K+1, V] (float32 or bfloat16),
+    draft_probs [B, K, V] float32 (the q each draft was drawn from),
+    draft_tokens [B, K] int32, uniforms [B, K+1] float32.  Returns
+    (out_tokens [B, K+1], out_num_accepted [B]), plus p(x), q(x), Z when
+    ``debug``."""
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    dev = target_logits.device
+    if draft_probs is not None and K > 0:
+        if tuple(draft_probs.shape) != (B, K, V):
+            raise ValueError("draft_probs must be [B, K, V]")
+        qp = _dev(draft_probs, "draft_probs", torch.float32)
+    elif float(temperature) == 0.0 or K == 0:
+        qp = None
+    else:
+        raise ValueError("draft_probs are required unless temperature == 0")
+    if tuple(draft_tokens.shape) != (B, K) or tuple(uniforms.shape) != (B, K + 1):
+        raise ValueError("draft_tokens must be [B, K] and uniforms [B, K+1]")
+    xp = _dev(draft_tokens, "draft_tokens", torch.int32) if K > 0 else None
+    up = _dev(uniforms, "uniforms", torch.float32)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_p = torch.empty((B, K), dtype=torch.float64, device=dev) if debug else None
+    out_q = torch.empty((B, K), dtype=torch.float64, device=dev) if debug else None
+    out_z = torch.empty((B,), dtype=torch.float64, device=dev) if debug else None
+    st = lib().sv_spec_verify_probs(_dev(target_logits, "target_logits"), qp, xp, up, float(temperature), int(top_k),
+                                    float(top_p), _dev(out_tokens, "out_tokens", torch.int32),
+                                    _dev(out_num_accepted, "out_num_accepted", torch.int32),
+                                    out_p.data_ptr() if debug and K > 0 else None,
+                                    out_q.data_ptr() if debug and K > 0 else None,
+                                    out_z.data_ptr() if debug else None, B, K, V, code, _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_spec_verify_probs")
     if debug:
         return out_tokens, out_num_accepted, dict(p=out_p, q=out_q, z=out_z)
     return out_tokens, out_num_accepted

@@ -82,7 +82,7 @@ ProfSlot* prof_begin() {
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, total;
+  size_t seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, qxs, total;
 };
 
 // What one call needs from the scratch.
@@ -107,6 +107,7 @@ Layout make_layout(int64_t cap_seq, const Need& n) {
   L.seq = o; o += al256(n.B * sizeof(SeqRec));
   L.seg_sum = o; o += al256(n.B * n.nseg * sizeof(double));
   L.seg_last = o; o += al256(n.B * n.nseg * sizeof(int32_t));
+  L.qxs = o; o += al256(n.rows * sizeof(float));
   L.total = o;
   return L;
 }
@@ -155,6 +156,7 @@ void bind_scratch(Args& a, char* base, const Layout& L) {
   a.seq = (SeqRec*)(base + L.seq);
   a.seg_sum = (double*)(base + L.seg_sum);
   a.seg_last = (int32_t*)(base + L.seg_last);
+  a.qxs = (float*)(base + L.qxs);
 }
 
 int check_params(float T, int32_t top_k, float top_p) {
@@ -203,11 +205,13 @@ struct Ragged {
 
 // need_n: out_n is required (the sampler passes none).  out_px: probability
 // of each sequence's last drawn token under the row it was drawn from (the
-// sampler, K == 0).  rg: null for a rectangular [B, K] batch.
+// sampler, K == 0).  rg: null for a rectangular [B, K] batch.  qprob: the
+// draft distributions given as probabilities [B, K, V] (rectangular only;
+// drf is then not used).
 int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, float Td,
                 int32_t top_k, float top_p, int32_t* out_tok, int32_t* out_n, bool need_n, double* out_p,
                 double* out_q, double* out_z, double* out_px, int32_t B, int32_t K, int32_t V, int32_t dtype,
-                void* stream, const Ragged* rg = nullptr) {
+                void* stream, const Ragged* rg = nullptr, const float* qprob = nullptr, bool qp = false) {
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > MAX_V) return SV_ERR_SHAPE;
   if (rg && (rg->nd < 0 || rg->kmax < 0 || rg->kmax > SV_MAX_K || (int64_t)rg->nd > (int64_t)B * rg->kmax))
     return SV_ERR_SHAPE;
@@ -222,10 +226,12 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   const int32_t kmax = rg ? rg->kmax : K;
   if (!tgt || !U || !out_tok || (need_n && !out_n) || (rg && !rg->cu)) return SV_ERR_NULL;
   if (nd > 0 && !X) return SV_ERR_NULL;
-  if (nd > 0 && mode != M_GREEDY && !drf) return SV_ERR_NULL;
+  if (nd > 0 && mode != M_GREEDY && !(qp ? (const void*)qprob : drf)) return SV_ERR_NULL;
+  // q given as probabilities: no draft rows to stream (greedy never uses q)
+  const bool use_qp = qp && mode != M_GREEDY && nd > 0;
   const int esz = dtype == SV_BF16 ? 2 : 4;
   const int64_t nt = nd + B;  // target rows
-  const int64_t rows = mode == M_GREEDY ? nt : nt + nd;
+  const int64_t rows = (mode == M_GREEDY || use_qp) ? nt : nt + nd;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
   if (rows * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
@@ -243,7 +249,8 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
 
   Args a;
   a.tgt = tgt;
-  a.drf = mode == M_GREEDY ? nullptr : drf;
+  a.drf = (mode == M_GREEDY || use_qp) ? nullptr : drf;
+  a.qprob = use_qp ? qprob : nullptr;
   a.X = X;
   a.U = U;
   a.out_tok = out_tok;
@@ -269,7 +276,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
   a.ulen = vec ? 16 / esz : 1;
   a.dch = make_udiv((uint32_t)a.nchunks);
-  a.rps = rg ? 1 : mode == M_GREEDY ? a.K + 1 : 2 * a.K + 1;
+  a.rps = rg ? 1 : (mode == M_GREEDY || use_qp) ? a.K + 1 : 2 * a.K + 1;
   a.drps = make_udiv((uint32_t)a.rps);
   hipStream_t s = (hipStream_t)stream;
   ProfSlot* prof = prof_begin();
@@ -326,6 +333,15 @@ int sv_spec_verify_ragged(const void* target_logits, const void* draft_logits, c
   return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, draft_temperature, top_k,
                      top_p, out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, 0, V, dtype, stream,
                      &rg);
+}
+
+int sv_spec_verify_probs(const void* target_logits, const float* draft_probs, const int32_t* draft_tokens,
+                         const float* uniforms, float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
+                         int32_t* out_num_accepted, double* out_p, double* out_q, double* out_z, int32_t B, int32_t K,
+                         int32_t V, int32_t dtype, void* stream) {
+  return verify_impl(target_logits, nullptr, draft_tokens, uniforms, temperature, temperature, top_k, top_p,
+                     out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream,
+                     nullptr, draft_probs, true);
 }
 
 // The draw of a verification with no drafts: each row is a sequence of one

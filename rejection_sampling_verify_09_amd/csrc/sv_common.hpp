@@ -109,6 +109,8 @@ struct Args {
   int32_t ND;          // draft rows
   int32_t Kmax;        // output stride of out_tok is Kmax + 1
   const int32_t* cu;   // ragged offsets (device), or null for a rectangular batch
+  const float* qprob;  // draft distributions given as probabilities [B, K, V] (then no draft rows), or null
+  float* qxs;          // scratch [rows]: q(x) of each target row's drafted token (with qprob)
   float c2;        // log2(e) / T, the exp2 scale of the streaming pass
   float win;       // top-p candidate window in logit units
   double invT;     // 1 / T in double
@@ -507,6 +509,13 @@ __device__ __forceinline__ const char* row_ptr(const Args& a, int rl, int esz) {
   const uintptr_t t = (uintptr_t)a.tgt, d = (uintptr_t)a.drf;
   return (const char*)(t + (dr ? d - t : (uintptr_t)0)) + idx * (size_t)a.V * esz;
 }
+
+// Batch layouts of the row-merge and sampling kernels.
+enum BatchLayout : int {
+  LAY_RECT = 0,  // [B, K+1] target and [B, K] draft logit rows
+  LAY_RAG = 1,   // ragged: packed rows with offsets cu (a.cu set)
+  LAY_QP = 2,    // [B, K+1] target logit rows; q given as probabilities (a.qprob set, no draft rows)
+};
 
 // RAG: a ragged batch (a.cu set).
 // A sequence: K drafts, its first uniform t0 (= its first target row in

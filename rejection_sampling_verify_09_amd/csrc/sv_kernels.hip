@@ -62,6 +62,7 @@ struct DrawRow {
   double invT;
   float m;
   uint32_t tau;
+  const float* prob;  // a row given as probabilities (then the fields above are unused), or null
 };
 
 struct SmemStream {
@@ -657,9 +658,13 @@ __device__ __forceinline__ double draw_weight(const char* pr, const char* qr, in
   const float xp = load_elem<DT>(pr, j);
   double w = ord_key(xp) >= dr[0].tau ? exp_tab(((double)xp - (double)dr[0].m) * dr[0].invT, tab) / dr[0].snorm : 0.0;
   if (use_res) {
-    const float xq = load_elem<DT>(qr, j);
-    const double q =
-        ord_key(xq) >= dr[1].tau ? exp_tab(((double)xq - (double)dr[1].m) * dr[1].invT, tab) / dr[1].snorm : 0.0;
+    double q;
+    if (dr[1].prob) {
+      q = (double)dr[1].prob[j];
+    } else {
+      const float xq = load_elem<DT>(qr, j);
+      q = ord_key(xq) >= dr[1].tau ? exp_tab(((double)xq - (double)dr[1].m) * dr[1].invT, tab) / dr[1].snorm : 0.0;
+    }
     const double d = w - q;
     w = d > 0.0 ? d : 0.0;
   }
@@ -744,7 +749,15 @@ __device__ __forceinline__ void set_draw_row(const RowRec* r, bool filtered, int
     sm.dr[slot].m = ld_dev(&r->m);
     sm.dr[slot].tau = ld_dev(&r->tau);
     sm.dr[slot].snorm = filtered ? ld_dev(&r->S_kept) : ld_dev(&r->S);
+    sm.dr[slot].prob = nullptr;
   }
+  __syncthreads();
+}
+
+// A row given as probabilities for the full-row draw, into sm.dr[slot].
+__device__ __forceinline__ void set_draw_prob_row(const float* prob, int slot, Smem& sm) {
+  __syncthreads();
+  if (threadIdx.x == 0) sm.dr[slot].prob = prob;
   __syncthreads();
 }
 
@@ -1629,8 +1642,11 @@ struct RowKSm {
 // max(0, p - q) over the target's kept tokens, or p itself (bonus, or an
 // empty residual); inverse CDF in ascending vocabulary order.  *Zout gets the
 // total weight, *wout the drawn token's weight.
+// qrow: the draft distribution as a probability row; q of each kept target
+// token is then read from it (the draft list is not used).
 __device__ int wave_list_sample(double u, const int32_t* pidx, const double* pprob, int np, const int32_t* qidx,
-                                const double* qprob, int nq, bool res, double* Zout, double* wout) {
+                                const double* qprob, int nq, bool res, double* Zout, double* wout,
+                                const float* qrow = nullptr) {
   const int lane = threadIdx.x & 63;
   // entries WR_EPL * lane + r: each lane a contiguous run
   int pi[WR_EPL];
@@ -1643,16 +1659,22 @@ __device__ int wave_list_sample(double u, const int32_t* pidx, const double* ppr
     w[r] = pp[r];
   }
   if (res) {
-    // q of each target token: one pass over the draft's kept list (each entry
-    // read by all lanes at once)
     double qv[WR_EPL];
+    if (qrow) {
+      // q read at each kept target token (one round trip)
 #pragma unroll
-    for (int r = 0; r < WR_EPL; ++r) qv[r] = 0.0;
-    for (int j = 0; j < nq; ++j) {
-      const int qi = qidx[j];
-      const double qp = qprob[j];
+      for (int r = 0; r < WR_EPL; ++r) qv[r] = WR_EPL * lane + r < np ? (double)qrow[pi[r]] : 0.0;
+    } else {
+      // q of each target token: one pass over the draft's kept list (each
+      // entry read by all lanes at once)
 #pragma unroll
-      for (int r = 0; r < WR_EPL; ++r) qv[r] = qi == pi[r] ? qp : qv[r];
+      for (int r = 0; r < WR_EPL; ++r) qv[r] = 0.0;
+      for (int j = 0; j < nq; ++j) {
+        const int qi = qidx[j];
+        const double qp = qprob[j];
+#pragma unroll
+        for (int r = 0; r < WR_EPL; ++r) qv[r] = qi == pi[r] ? qp : qv[r];
+      }
     }
 #pragma unroll
     for (int r = 0; r < WR_EPL; ++r) {
@@ -1737,11 +1759,15 @@ __device__ void sentinel_seq(const Args& a, int b, int t) {
 // kept lists (the whole block draws from full rows when a kept set is too
 // large for a list; unfiltered rows: the sampling kernel draws afterwards).
 // With do_seq == 0 (filtered probabilities) only the merges run.
-template <int DT, int MODE, bool RAG>
+// LAY (BatchLayout): rectangular, ragged, or rectangular with q given as
+// probabilities (no draft rows: each target row i < K reads q(x_i) from the
+// given row, and the residual draw reads q at the target's kept tokens).
+template <int DT, int MODE, int LAY>
 __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   __shared__ RowKSm sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
+  constexpr bool RAG = LAY == LAY_RAG, QP = LAY == LAY_QP;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   const int rl = (int)blockIdx.x;
   const RowLoc loc = a.do_seq ? row_loc<RAG>(a, rl) : RowLoc{rl, 0, 0, 0, false, false};
@@ -1753,6 +1779,8 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   }
   const int b = loc.b;
   const int xtok = (a.do_seq && loc.i < loc.K) ? a.X[(size_t)loc.x0 + loc.i] : -1;
+  // q(x_i) from the given draft row (needed only at the sequence's finish)
+  const float qx = (QP && xtok >= 0 && xtok < a.V) ? a.qprob[(size_t)(loc.x0 + loc.i) * a.V + xtok] : 0.0f;
   if (w == 0) {
     RowRec rr;
     const bool ok = wave_row<DT, MODE>(a, rl, xtok, sm.w, rr);
@@ -1761,7 +1789,8 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   __syncthreads();
   if (!sm.fast) (void)row_finalize<DT, MODE, WG>(a, rl, xtok, sm.blk);
   const int K = loc.K;
-  const int rps = MODE == M_GREEDY ? K + 1 : 2 * K + 1;
+  const int rps = (MODE == M_GREEDY || QP) ? K + 1 : 2 * K + 1;
+  if (QP && t == 0) st_dev(&a.qxs[rl], qx);
   if (!a.do_seq || !last_arrival(&a.seq_cnt[b], (uint32_t)rps, &sm.flag)) return;
 
   // ---- the sequence: its rows' records, drafted tokens and uniforms, and
@@ -1784,6 +1813,8 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     sm.rf[j] = ld_dev(&rj->flags);
     sm.nk[j] = ld_dev(&rj->nkept);
     sm.arg[j] = ld_dev(&rj->arg);
+    // q(x_j) in the draft rows' slots
+    if (QP && j < K) sm.px[K + 1 + j] = (double)ld_dev(&a.qxs[seq_row<RAG>(a, g, j)]);
   }
   if (t < K) sm.x[t] = a.X[(size_t)g.x0 + t];
   if (t <= K) sm.u[t] = a.U[(size_t)g.t0 + t];
@@ -1837,7 +1868,7 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     if (FILT && n >= 0) {
       const bool res = n < K;
       const int jq = res ? K + 1 + n : n;
-      const int np = sm.nk[n], nq = sm.nk[jq];
+      const int np = sm.nk[n], nq = QP ? 0 : sm.nk[jq];
       if (np < 0 || (res && nq < 0)) {
         big = 1;
       } else {
@@ -1847,8 +1878,8 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
           // read ahead with the records
           pidx = sm.spec.idx[n];
           pprob = sm.spec.prob[n];
-          qidx = sm.spec.idx[jq];
-          qprob = sm.spec.prob[jq];
+          qidx = QP ? pidx : sm.spec.idx[jq];
+          qprob = QP ? pprob : sm.spec.prob[jq];
         } else {
           // the two kept lists (one round trip)
           SmemSeq& q = sm.blk.q;
@@ -1857,7 +1888,7 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
             q.pidx[e] = ld_dev(&a.kidx[op + e]);
             q.pprob[e] = ld_dev(&a.kprob[op + e]);
           }
-          if (res) {
+          if (res && !QP) {
             for (int e = lane; e < nq; e += 64) {
               q.qidx[e] = ld_dev(&a.kidx[oq + e]);
               q.qprob[e] = ld_dev(&a.kprob[oq + e]);
@@ -1870,7 +1901,8 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
           qprob = q.qprob;
         }
         double Z, wtok;
-        const int tok = wave_list_sample((double)sm.u[K], pidx, pprob, np, qidx, qprob, nq, res, &Z, &wtok);
+        const float* qrow = QP ? a.qprob + (size_t)(g.x0 + n) * a.V : nullptr;
+        const int tok = wave_list_sample((double)sm.u[K], pidx, pprob, np, qidx, qprob, nq, res, &Z, &wtok, qrow);
         if (lane == 0) {
           ot[n] = tok;
           if (a.out_z) a.out_z[b] = Z;
@@ -1889,9 +1921,10 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     const int n = sm.n;
     const bool res = n < K;
     const int jq = res ? K + 1 + n : n;
-    const int rn = seq_row<RAG>(a, g, n), rq = seq_row<RAG>(a, g, jq);
+    const int rn = seq_row<RAG>(a, g, n), rq = QP ? rn : seq_row<RAG>(a, g, jq);
     set_draw_row(&a.row[rn], true, 0, row_temp(a, rn).invT, sm.blk);
-    set_draw_row(&a.row[rq], true, 1, row_temp(a, rq).invT, sm.blk);
+    if (QP) set_draw_prob_row(a.qprob + (size_t)(g.x0 + (res ? n : 0)) * a.V, 1, sm.blk);
+    else set_draw_row(&a.row[rq], true, 1, row_temp(a, rq).invT, sm.blk);
     double Z;
     const int tok = full_row_sample<DT, WG>(a, (double)sm.u[K], row_ptr(a, rn, ESZ), row_ptr(a, rq, ESZ), res,
                                             sm.blk, &Z);
@@ -1905,18 +1938,21 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   }
 }
 
-template <int DT>
+// QP: qr is a row of probabilities (float).
+template <int DT, bool QP = false>
 __device__ __forceinline__ double plain_weight(const char* pr, const char* qr, int j, const RowRec& P,
                                                const RowRec& Q, bool res, double invTp, double invTq) {
   const double p = exp(((double)load_elem<DT>(pr, j) - (double)P.m) * invTp) / P.S;
   if (!res) return p;
-  const double q = exp(((double)load_elem<DT>(qr, j) - (double)Q.m) * invTq) / Q.S;
+  const double q = QP ? (double)reinterpret_cast<const float*>(qr)[j]
+                      : exp(((double)load_elem<DT>(qr, j) - (double)Q.m) * invTq) / Q.S;
   const double d = p - q;
   return d > 0.0 ? d : 0.0;
 }
 
-template <int DT, bool RAG>
+template <int DT, int LAY>
 __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
+  constexpr bool RAG = LAY == LAY_RAG, QP = LAY == LAY_QP;
   __shared__ Smem sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   const int t = threadIdx.x;
@@ -1930,7 +1966,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   const int K = g.K;
   const bool res = active && n < K;
   const int rlP = seq_row<RAG>(a, g, active ? n : 0);
-  const int rlQ = seq_row<RAG>(a, g, res ? K + 1 + n : (active ? n : 0));
+  const int rlQ = QP ? rlP : seq_row<RAG>(a, g, res ? K + 1 + n : (active ? n : 0));
   const double iTp = row_temp(a, rlP).invT, iTq = row_temp(a, rlQ).invT;
   RowRec P, Q;
   const char* pr = nullptr;
@@ -1939,14 +1975,14 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     P = a.row[rlP];
     Q = a.row[rlQ];
     pr = row_ptr(a, rlP, ESZ);
-    qr = row_ptr(a, rlQ, ESZ);
+    qr = QP ? reinterpret_cast<const char*>(a.qprob + (size_t)(g.x0 + (res ? n : 0)) * a.V) : row_ptr(a, rlQ, ESZ);
     const int j0 = c * SCE + t * 8;
     double ts = 0.0;
     int lastp = -1;
     for (int e = 0; e < 8; ++e) {
       const int j = j0 + e;
       if (j < a.V) {
-        const double w = plain_weight<DT>(pr, qr, j, P, Q, res, iTp, iTq);
+        const double w = plain_weight<DT, QP>(pr, qr, j, P, Q, res, iTp, iTq);
         ts += w;
         if (w > 0.0) lastp = j;
       }
@@ -2006,8 +2042,8 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
       __syncthreads();
       const double cs = sm.d0;
       const int j0 = sf * SEG + 2 * t;
-      const double w0 = j0 < a.V ? plain_weight<DT>(pr, qr, j0, P, Q, res, iTp, iTq) : 0.0;
-      const double w1 = j0 + 1 < a.V ? plain_weight<DT>(pr, qr, j0 + 1, P, Q, res, iTp, iTq) : 0.0;
+      const double w0 = j0 < a.V ? plain_weight<DT, QP>(pr, qr, j0, P, Q, res, iTp, iTq) : 0.0;
+      const double w1 = j0 + 1 < a.V ? plain_weight<DT, QP>(pr, qr, j0 + 1, P, Q, res, iTp, iTq) : 0.0;
       double tot;
       const double inc2 = block_incl_scan(w0 + w1, sm.red, &tot);
       __syncthreads();
@@ -2027,7 +2063,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     a.out_tok[(size_t)b * (a.Kmax + 1) + n] = tok;
     if (a.out_z) a.out_z[b] = Z;
     if (a.out_px)
-      a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll) : plain_weight<DT>(pr, qr, tok, P, Q, false, iTp, iTq);
+      a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll) : plain_weight<DT, QP>(pr, qr, tok, P, Q, false, iTp, iTq);
   }
 }
 
@@ -2072,16 +2108,24 @@ static KFn pick_stream_mode(int mode, bool vec) {
   }
 }
 
-template <int DT, bool RAG>
+template <int DT, int LAY>
 static KFn pick_row(int mode) {
   switch (mode) {
-    case M_PLAIN: return (KFn)row_kernel<DT, M_PLAIN, RAG>;
-    case M_TOPK: return (KFn)row_kernel<DT, M_TOPK, RAG>;
-    case M_TOPP: return (KFn)row_kernel<DT, M_TOPP, RAG>;
-    case M_TOPKP: return (KFn)row_kernel<DT, M_TOPKP, RAG>;
-    default: return (KFn)row_kernel<DT, M_GREEDY, RAG>;
+    case M_PLAIN: return (KFn)row_kernel<DT, M_PLAIN, LAY>;
+    case M_TOPK: return (KFn)row_kernel<DT, M_TOPK, LAY>;
+    case M_TOPP: return (KFn)row_kernel<DT, M_TOPP, LAY>;
+    case M_TOPKP: return (KFn)row_kernel<DT, M_TOPKP, LAY>;
+    default: return (KFn)row_kernel<DT, M_GREEDY, LAY>;
   }
 }
+
+template <int DT>
+static KFn pick_row_lay(int mode, int lay) {
+  return lay == LAY_RAG ? pick_row<DT, LAY_RAG>(mode) : lay == LAY_QP ? pick_row<DT, LAY_QP>(mode)
+                                                                      : pick_row<DT, LAY_RECT>(mode);
+}
+
+static int layout_of(const Args& a) { return a.cu ? LAY_RAG : a.qprob ? LAY_QP : LAY_RECT; }
 
 template <int DT>
 static KFn pick_probs(int mode) {
@@ -2101,17 +2145,20 @@ hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned 
 }
 
 hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
-  const bool rag = a.cu != nullptr;
-  KFn f = dtype == D_BF16 ? (rag ? pick_row<D_BF16, true>(mode) : pick_row<D_BF16, false>(mode))
-                          : (rag ? pick_row<D_F32, true>(mode) : pick_row<D_F32, false>(mode));
+  const int lay = layout_of(a);
+  KFn f = dtype == D_BF16 ? pick_row_lay<D_BF16>(mode, lay) : pick_row_lay<D_F32>(mode, lay);
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s) {
-  const bool rag = a.cu != nullptr;
-  KFn f = dtype == D_BF16 ? (rag ? (KFn)sample_kernel<D_BF16, true> : (KFn)sample_kernel<D_BF16, false>)
-                          : (rag ? (KFn)sample_kernel<D_F32, true> : (KFn)sample_kernel<D_F32, false>);
+  const int lay = layout_of(a);
+  KFn f = dtype == D_BF16 ? (lay == LAY_RAG  ? (KFn)sample_kernel<D_BF16, LAY_RAG>
+                             : lay == LAY_QP ? (KFn)sample_kernel<D_BF16, LAY_QP>
+                                             : (KFn)sample_kernel<D_BF16, LAY_RECT>)
+                          : (lay == LAY_RAG  ? (KFn)sample_kernel<D_F32, LAY_RAG>
+                             : lay == LAY_QP ? (KFn)sample_kernel<D_F32, LAY_QP>
+                                             : (KFn)sample_kernel<D_F32, LAY_RECT>);
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
   return hipGetLastError();
 }

@@ -159,3 +159,50 @@ def compare_ragged(w: Workload, r: dict, x: np.ndarray, max_k: int, dev_tok, dev
             stats["max_prob_err"] = float(err)
     stats["flags"] = flags
     return stats, fails
+
+
+# ---------------------------------------------------------------------------
+# q given as probabilities
+# ---------------------------------------------------------------------------
+def run_device_probs(w: Workload, d: dict, Q: np.ndarray, x: np.ndarray, debug: bool = True):
+    import torch
+
+    from rejection_sampling_verify_09_amd import spec_verify_probs
+
+    tgt = to_device(d["target"], w.dtype)
+    qd = torch.from_numpy(np.ascontiguousarray(Q, dtype=np.float32)).cuda() if w.K > 0 else None
+    X = torch.from_numpy(x.astype(np.int32)).cuda()
+    U = torch.from_numpy(d["uniforms"]).cuda()
+    res = spec_verify_probs(tgt, qd, X, U, w.temperature, w.top_k, w.top_p, debug=debug)
+    torch.cuda.synchronize()
+    return [v.cpu().numpy() if not isinstance(v, dict) else {k: t.cpu().numpy() for k, t in v.items()} for v in res]
+
+
+def compare_probs(w: Workload, d: dict, Q: np.ndarray, x: np.ndarray, dev_tok, dev_n, dev_dbg=None):
+    ref_tok, ref_n, ref_dg = oracle.verify(d["target"], None, x, d["uniforms"], w.temperature, w.top_k, w.top_p,
+                                           dtype=w.dtype, diag=True, draft_probs=Q)
+    stats = dict(match=0, flagged=0, fail=0, max_prob_err=0.0)
+    fails, flags = [], []
+    for b in range(w.B):
+        if dev_n[b] == ref_n[b] and np.array_equal(dev_tok[b], ref_tok[b]):
+            stats["match"] += 1
+            continue
+        v, why = oracle.classify(d["target"][b], None, x[b], d["uniforms"][b], w.temperature, w.top_k, w.top_p,
+                                 w.dtype, dev_tok[b], dev_n[b], draft_probs_b=Q[b])
+        if v == oracle.MATCH:
+            stats["match"] += 1
+        elif v == oracle.FLAGGED:
+            stats["flagged"] += 1
+            flags.append((b, why))
+        else:
+            stats["fail"] += 1
+            fails.append((b, why))
+    if dev_dbg is not None and w.K > 0:
+        ok = ref_n >= 0
+        if ok.any():
+            err = np.abs(dev_dbg["p"][ok] - ref_dg["px"][ok]).max()
+            if w.temperature != 0.0:
+                err = max(err, np.abs(dev_dbg["q"][ok] - ref_dg["qx"][ok]).max())
+            stats["max_prob_err"] = float(err)
+    stats["flags"] = flags
+    return stats, fails

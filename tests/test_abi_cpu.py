@@ -22,6 +22,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_spec_verify_dt", "sv_spec_verify_ragged",
+              "sv_spec_verify_probs",
               "sv_filtered_probs", "sv_sample", "sv_dynk_create", "sv_dynk_observe", "sv_dynk_k", "sv_dynk_destroy",
               "sv_release", "sv_scratch_bytes",
               "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
@@ -203,3 +204,19 @@ def test_controller_errors():
     assert lib.sv_dynk_k(None, 0) == -1 and c.k(2) == -1 and c.k(0) == 6
     lib.sv_dynk_destroy(None)
     c.close()
+
+
+def test_probs_validation():
+    def f(B=2, K=3, V=16, T=1.0, q=FAKE, X=FAKE, U=FAKE, tgt=FAKE, out_t=FAKE, out_n=FAKE, top_p=1.0):
+        return L.lib().sv_spec_verify_probs(tgt, q, X, U, T, 0, top_p, out_t, out_n, None, None, None, B, K, V, 0,
+                                            None)
+    assert f(B=-1) == L.SV_ERR_SHAPE
+    assert f(K=L.SV_MAX_K + 1) == L.SV_ERR_SHAPE
+    assert f(top_p=0.0) == L.SV_ERR_PARAM
+    assert f(q=None) == L.SV_ERR_NULL
+    assert f(X=None) == L.SV_ERR_NULL
+    assert f(tgt=None) == L.SV_ERR_NULL
+    # greedy and K == 0 need no draft probabilities
+    assert f(T=0.0, q=None, U=None) == L.SV_ERR_NULL
+    assert f(K=0, q=None, X=None, U=None) == L.SV_ERR_NULL
+    assert f(B=0, q=None, X=None, U=None, tgt=None, out_t=None, out_n=None) == L.SV_OK

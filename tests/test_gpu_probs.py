@@ -1,0 +1,111 @@
+"""GPU parity of verification with the draft distributions given as
+probabilities (sv_spec_verify_probs) with the fp64 oracle: tokens and counts
+identical except flagged near-ties, p(x) within 1e-6, q(x) exactly the given
+value."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS, make_inputs
+from tests.harness import compare_probs, log, run_device_probs
+
+pytestmark = pytest.mark.gpu
+
+PROB_TOL = 1e-6
+
+
+def _filtered_q(w, d):
+    """q_i: the draft rows' filtered distribution (fp64 oracle), as float32."""
+    rows = oracle.widen(d["draft"].reshape(w.B * w.K, w.V), w.dtype)
+    return oracle.filtered_probs(rows, w.temperature, w.top_k, w.top_p).reshape(w.B, w.K, w.V).astype(np.float32)
+
+
+def _dirichlet_q(w, seed, alpha=0.05, zero_frac=0.3):
+    """Arbitrary draft distributions: sparse Dirichlet draws with a share of
+    exact zeros, float32."""
+    rng = np.random.default_rng(seed)
+    Q = rng.gamma(alpha, size=(w.B, w.K, w.V))
+    Q[rng.random(Q.shape) < zero_frac] = 0.0
+    Q /= Q.sum(axis=2, keepdims=True)
+    return Q.astype(np.float32)
+
+
+def _draw_x(w, d, Q):
+    """x_i ~ q_i (the given rows, widened), by the oracle's inverse CDF."""
+    q64 = Q.reshape(w.B * w.K, w.V).astype(np.float64)
+    tok, _ = oracle.inverse_cdf(q64, d["draft_u"].reshape(-1))
+    return tok.reshape(w.B, w.K).astype(np.int32)
+
+
+def _check(w, d, Q, x=None):
+    log(f"[probs] {w.name} B={w.B} K={w.K} V={w.V} T={w.temperature} top_k={w.top_k} top_p={w.top_p}")
+    if x is None:
+        x = _draw_x(w, d, Q)
+    tok, n, dbg = run_device_probs(w, d, Q, x)
+    stats, fails = compare_probs(w, d, Q, x, tok, n, dbg)
+    log(f"   match={stats['match']} flagged={stats['flagged']} fail={stats['fail']} "
+        f"max|dp|={stats['max_prob_err']:.2e} mean_n={np.mean(n):.3f}")
+    assert stats["fail"] == 0, fails[:5]
+    assert stats["flagged"] == 0
+    assert stats["max_prob_err"] <= PROB_TOL
+    if w.temperature > 0:
+        ok = n >= 0
+        want = np.take_along_axis(Q.astype(np.float64), x[:, :, None].astype(np.int64), axis=2)[:, :, 0]
+        assert np.array_equal(dbg["q"][ok], want[ok]), "q(x) must be the given value"
+    return tok, n, dbg
+
+
+@pytest.mark.parametrize("name", [
+    "b64-k6-v128256-bf16-zipf-t0.7-topp0.9",
+    "b8-k5-v32000-f32-zipf",
+    "b32-k6-v128256-bf16-normal-s1.0",
+    "b32-k6-v128256-bf16-normal-greedy",
+])
+def test_probs_filtered_draft_distribution(name):
+    w = WORKLOADS[name]
+    d = make_inputs(w)
+    _check(w, d, _filtered_q(w, d))
+
+
+@pytest.mark.parametrize("name,seed", [
+    ("b64-k6-v128256-bf16-zipf-t0.7-topp0.9", 1),
+    ("b8-k5-v32000-f32-zipf", 2),
+])
+def test_probs_arbitrary_draft_distribution(name, seed):
+    """q unrelated to the draft logits (sparse, with zeros): more rejections
+    and residual draws."""
+    w = WORKLOADS[name]
+    d = make_inputs(w)
+    _check(w, d, _dirichlet_q(w, seed))
+
+
+def test_probs_top_k_and_large_kept_sets():
+    # top-k on the peaked rows (kept lists), then a nucleus far above 256
+    # tokens (the full-row draw with the given q row)
+    w = replace(WORKLOADS["b256-k8-v152064-f32-peaked-topk50"], B=24, seed=61)
+    d = make_inputs(w)
+    _check(w, d, _filtered_q(w, d))
+    w2 = replace(WORKLOADS["b8-k5-v32000-f32-zipf"], name="b8-k5-v32000-f32-normal-topp0.99", shape="normal",
+                 target_sigma=1.0, top_p=0.99, seed=62)
+    d2 = make_inputs(w2)
+    _check(w2, d2, _dirichlet_q(w2, 5, alpha=0.5, zero_frac=0.1))
+
+
+def test_probs_equal_to_the_logit_q_match_the_logit_call():
+    """q given as the draft's own filtered distribution (float32-rounded)
+    against the logit entry point: identical tokens wherever no decision
+    lies within the float32 rounding of q."""
+    from tests.harness import run_device
+
+    w = WORKLOADS["b8-k5-v32000-f32-zipf"]
+    d = make_inputs(w)
+    Q = _filtered_q(w, d)
+    x = _draw_x(w, d, Q)
+    a_tok, a_n, a_dbg = run_device(w, d, x, debug=True)
+    b_tok, b_n, b_dbg = run_device_probs(w, d, Q, x)
+    assert np.max(np.abs(a_dbg["q"] - b_dbg["q"])) < 1e-7
+    assert np.array_equal(a_dbg["p"], b_dbg["p"])
+    same = (a_n == b_n) & np.all(a_tok == b_tok, axis=1)
+    assert same.mean() > 0.95
