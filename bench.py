@@ -4,6 +4,7 @@
     python bench.py --sampler [--steps K] [--warmup W] [--workload NAME]
     python bench.py --draft-temperature TD [--steps K] [--warmup W] [--workload NAME]
     python bench.py --ragged K_LO K_HI [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --draft-probs [--steps K] [--warmup W] [--workload NAME]
 
 One step = one sv_spec_verify call (the whole hot path: streaming pass,
 filter thresholds, accept tests, first-rejection scan, final draw) over one
@@ -14,6 +15,10 @@ so every step reads its logits from HBM.  Prints one JSON line.
 With --ragged K_LO K_HI, one step is one sv_spec_verify_ragged call over a
 batch whose sequences draft K_b ~ uniform[K_LO, K_HI] tokens each (drafts
 drawn on the GPU before timing).
+
+With --draft-probs, one step is one sv_spec_verify_probs call (the draft
+distributions given as float32 probabilities; only the target rows are
+streamed).
 
 With --sampler, one step is one sv_sample call (the drafting draw: x ~ q and
 q(x)) over the workload's B*K draft rows, with their draft uniforms.  With
@@ -62,7 +67,8 @@ def load_draft_tokens(name: str, B: int, K: int):
 def measured_traffic(key: str):
     """HBM bytes per launch of the streaming kernel from the committed counter
     summary for ``key`` (the workload name, "sample-" + name for the draft
-    draw, "ragged-LO-HI-" + name for a ragged batch), or None when the summary
+    draw, "ragged-LO-HI-" + name for a ragged batch, "probs-" + name for q
+    given as probabilities), or None when the summary
     is absent or predates the kernel source."""
     path = os.path.join(PROFILES, f"traffic_stream_kernel_{key}.md")
     if not os.path.exists(path):
@@ -301,6 +307,113 @@ def run_ragged(args, w, k_lo: int, k_hi: int):
     print(json.dumps(result), flush=True)
 
 
+def run_probs(args, w):
+    """Verification with the draft distributions given as probabilities
+    (sv_spec_verify_probs).  q is the draft rows' filtered distribution, made
+    by the library (sv_filtered_probs) and the drafts are drawn from the
+    draft logits (sv_sample), both before timing; only the target rows are
+    streamed."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_09_amd import (filtered_probs, profile_start, profile_stop, sample,
+                                                  spec_verify_probs)
+    from synth import make_inputs
+
+    d = make_inputs(w)
+    esz = 2 if w.dtype == "bf16" else 4
+    bytes_per_step = w.B * (w.K + 1) * w.V * esz  # every target logit once; q is read only where needed
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    drows = dev(d["draft"].reshape(w.B * w.K, w.V))
+    Q = filtered_probs(drows, w.temperature, w.top_k, w.top_p).reshape(w.B, w.K, w.V)
+    ud = torch.from_numpy(d["draft_u"].reshape(-1).astype(np.float32)).cuda()
+    xt, _ = sample(drows, ud, w.temperature, w.top_k, w.top_p, with_prob=False)
+    X = xt.reshape(w.B, w.K).contiguous()
+    del drows
+    tgt0 = dev(d["target"])
+    R = args.copies or max(3, -(-640_000_000 // (bytes_per_step + Q.numel() * 4)))
+    tgts = [tgt0] + [tgt0.clone() for _ in range(R - 1)]
+    Qs = [Q] + [Q.clone() for _ in range(R - 1)]
+    U = torch.from_numpy(d["uniforms"]).cuda()
+    out_t = torch.empty((w.B, w.K + 1), dtype=torch.int32, device="cuda")
+    out_n = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        spec_verify_probs(tgts[i % R], Qs[i % R], X, U, w.temperature, w.top_k, w.top_p, out_tokens=out_t,
+                          out_num_accepted=out_n)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    profile_start()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = profile_stop()
+    stream_ms = prof["stream_kernel_ms"] / max(1, prof["calls"])
+    other_ms = prof["other_kernels_ms"] / max(1, prof["calls"])
+    n_host = out_n.cpu().numpy()
+    emitted = int(np.sum(n_host[n_host >= 0] + 1))
+    achieved = bytes_per_step / (stream_ms / 1e3) / 1e9
+    result = {
+        "metric": f"spec-verify sequences/s + % HBM peak at B={w.B} K={w.K} V={w.V} {w.dtype} (q as probabilities)",
+        "value": w.B / (ms_per_step / 1e3),
+        "unit": "sequences/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded logits of the workload's shape; no model weights)",
+        "config": {"workload": f"{w.name} with q given as float32 probabilities", "B": w.B, "K": w.K, "V": w.V,
+                   "logits": w.dtype, "temperature": w.temperature, "top_k": w.top_k, "top_p": w.top_p,
+                   "rows": w.B * (w.K + 1), "input_copies": R, "logit_bytes_per_step": bytes_per_step},
+        "tokens_per_s": emitted / (ms_per_step / 1e3),
+        "mean_emitted_per_sequence": emitted / w.B,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(f"probs-{w.name}"),
+            "kernel": "stream_kernel", "kernel_ms": stream_ms, "other_kernels_ms": other_ms,
+            "timed_calls": prof["calls"],
+            "step_frac": bytes_per_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        Qh, xh = Q.cpu().numpy(), X.cpu().numpy()
+        t0 = time.perf_counter()
+        n_done = 0
+        while True:
+            oracle.verify(d["target"], None, xh, d["uniforms"], w.temperature, w.top_k, w.top_p, dtype=w.dtype,
+                          draft_probs=Qh)
+            n_done += w.B
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        result["cpu_baseline"] = dict(value=n_done / el, unit="sequences/s", cores=1, kind="oracle",
+                                      sample=f"{n_done // w.B} x the full {w.B}-sequence batch with given q, "
+                                             f"fp64 NumPy, single thread, {el:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,6 +429,8 @@ def main():
                     help="measure the drafting draw (sv_sample) over the workload's draft rows instead")
     ap.add_argument("--draft-temperature", type=float, default=None,
                     help="verify drafts drawn (on the GPU) at this temperature (sv_spec_verify_dt)")
+    ap.add_argument("--draft-probs", action="store_true",
+                    help="verify with the draft distributions given as probabilities (sv_spec_verify_probs)")
     ap.add_argument("--ragged", type=int, nargs=2, metavar=("K_LO", "K_HI"), default=None,
                     help="verify a batch whose sequences draft K_b ~ uniform[K_LO, K_HI] tokens "
                          "(sv_spec_verify_ragged)")
@@ -354,6 +469,9 @@ def main():
     w = WORKLOADS[name]
     if args.ragged:
         run_ragged(args, w, *args.ragged)
+        return
+    if args.draft_probs:
+        run_probs(args, w)
         return
     d = make_inputs(w)
     if args.sampler:
