@@ -1246,37 +1246,39 @@ __device__ __forceinline__ uint32_t wave_radix(const uint32_t (&ek)[WR_EPL], con
   return prefix;
 }
 
-// Descending walk over the distinct keys of the wave's entries: returns the
-// first key at which the running mass reaches target (mass of a key = its
-// number of entries times ew / snorm), 0 when the entries run out first, or 1
-// (not the key of any finite logit) when WR_ITER keys were not enough; the
-// caller then uses the radix search.
-__device__ __forceinline__ uint32_t wave_walk(const uint32_t (&ek)[WR_EPL], const double (&ew)[WR_EPL], double snorm,
-                              double target) {
-  double run = 0.0;
+// Descending walk over the distinct keys of the wave's entries in slots
+// 0..S-1 (key ek, 0 for none; fixed-point weight wt, equal for equal keys):
+// returns the first key at which the running weight reaches target, 0 when
+// the entries run out first, or 1 (not the key of any finite logit) when
+// WR_ITER keys were not enough; the caller then uses the radix search.  The
+// same cut as wave_radix, cheap when it lies within the first few keys, as a
+// nucleus usually does.
+template <int S>
+__device__ __forceinline__ uint32_t wave_walk(const uint32_t (&ek)[WR_EPL], const unsigned long long (&wt)[WR_EPL],
+                                              unsigned long long target) {
+  unsigned long long run = 0;
   uint32_t hi = 0xFFFFFFFFu;
   for (int it = 0; it < WR_ITER; ++it) {
     uint32_t lm = 0;
 #pragma unroll
-    for (int r = 0; r < WR_EPL; ++r)
+    for (int r = 0; r < S; ++r)
       if (ek[r] < hi && ek[r] > lm) lm = ek[r];
     const uint32_t km = dpp_wave_umax(lm);
     if (km == 0u) return 0u;
-    int cnt = 0;
-    double wk = 0.0;
+    int cnt = 0, src = -1;
+    unsigned long long wsel = 0;
 #pragma unroll
-    for (int r = 0; r < WR_EPL; ++r) {
+    for (int r = 0; r < S; ++r) {
       const unsigned long long bm = __ballot(ek[r] == km);
       cnt += __popcll(bm);
-      if (bm != 0ull && wk == 0.0) {
-        const int src = __ffsll(bm) - 1;
-        const uint64_t u = (uint64_t)__double_as_longlong(ew[r]);
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
-        wk = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+      if (src < 0 && bm != 0ull) {  // uniform: the first slot holding the key
+        src = __ffsll(bm) - 1;
+        wsel = wt[r];
       }
     }
-    run += (double)cnt * (wk / snorm);
+    const unsigned long long w = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(wsel >> 32), src) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wsel, src);
+    run += (unsigned long long)cnt * w;
     if (run >= target) return km;
     hi = km;
   }
@@ -1545,17 +1547,16 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
 #pragma unroll
       for (int r = 0; r < WR_EPL; ++r) ekp[r] = ek[r] >= tau ? ek[r] : 0u;
       uint32_t tp;
+      const unsigned long long target = (unsigned long long)(a.top_p * MASS_SCALE);
       if (n <= 64) {
         const unsigned long long w0 = ekp[0] != 0u ? (unsigned long long)(ew[0] / snorm * MASS_SCALE) : 0ull;
-        tp = wave_walk64(ekp[0], w0, (unsigned long long)(a.top_p * MASS_SCALE), n, ws);
+        tp = wave_walk64(ekp[0], w0, target, n, ws);
       } else {
-        tp = wave_walk(ekp, ew, snorm, a.top_p);
-        if (tp == 1u) {
 #pragma unroll
-          for (int r = 0; r < WR_EPL; ++r)
-            wt[r] = ekp[r] != 0u ? (unsigned long long)(ew[r] / snorm * MASS_SCALE) : 0ull;
-          tp = wave_radix(ekp, wt, (unsigned long long)(a.top_p * MASS_SCALE), ws.hist);
-        }
+        for (int r = 0; r < WR_EPL; ++r)
+          wt[r] = ekp[r] != 0u ? (unsigned long long)(ew[r] / snorm * MASS_SCALE) : 0ull;
+        tp = n <= 128 ? wave_walk<2>(ekp, wt, target) : wave_walk<WR_EPL>(ekp, wt, target);
+        if (tp == 1u) tp = wave_radix(ekp, wt, target, ws.hist);
       }
       if (tp == 0u) {
         if (MODE == M_TOPP) return false;  // the nucleus reaches below the candidate window
