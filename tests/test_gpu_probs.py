@@ -109,3 +109,27 @@ def test_probs_equal_to_the_logit_q_match_the_logit_call():
     assert np.array_equal(a_dbg["p"], b_dbg["p"])
     same = (a_n == b_n) & np.all(a_tok == b_tok, axis=1)
     assert same.mean() > 0.95
+
+
+@pytest.mark.parametrize("V,dtype,T,k,p,K", [
+    (4099, "f32", 1.0, 0, 1.0, 1),    # element loads, unfiltered: the full-row residual with the given q
+    (5003, "bf16", 0.9, 20, 0.9, 3),  # element loads, top-k then top-p
+])
+def test_probs_element_path(V, dtype, T, k, p, K):
+    w = replace(WORKLOADS["b8-k5-v32000-f32-zipf"], name=f"b10-k{K}-v{V}-{dtype}", B=10, K=K, V=V, dtype=dtype,
+                temperature=T, top_k=k, top_p=p, seed=80 + K)
+    d = make_inputs(w)
+    _check(w, d, _dirichlet_q(w, 9, alpha=0.3, zero_frac=0.2))
+
+
+def test_probs_bad_token_is_a_sentinel():
+    w = WORKLOADS["b8-k5-v32000-f32-zipf"]
+    d = make_inputs(w)
+    Q = _filtered_q(w, d)
+    x = _draw_x(w, d, Q)
+    x[2, 1] = -3
+    tok, n, _ = run_device_probs(w, d, Q, x)
+    assert n[2] == -1 and np.all(tok[2] == -1)
+    ref_tok, ref_n = oracle.verify(d["target"], None, x, d["uniforms"], w.temperature, w.top_k, w.top_p,
+                                   dtype=w.dtype, draft_probs=Q)
+    assert np.array_equal(n, ref_n) and np.array_equal(tok, ref_tok)

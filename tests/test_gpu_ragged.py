@@ -131,3 +131,35 @@ def test_closed_loop_draft_length_control():
         log(f"   step {step}: mean n {n.mean():.2f}  next K {ks.tolist()}")
     assert len(seen) > 1, "the loop never changed a draft length"
     ctrl.close()
+
+
+@pytest.mark.parametrize("V,dtype,T,k,p", [
+    (4099, "f32", 1.0, 7, 1.0),      # element loads (row length not a multiple of 16 bytes), top-k
+    (5003, "bf16", 0.8, 0, 0.95),    # element loads, top-p
+    (3001, "f32", 1.0, 0, 1.0),      # unfiltered: the full-row draw per sequence
+])
+def test_ragged_element_path(V, dtype, T, k, p):
+    base = replace(WORKLOADS["b8-k5-v32000-f32-zipf"], name=f"b12-v{V}-{dtype}", B=12, V=V, dtype=dtype,
+                   temperature=T, top_k=k, top_p=p, seed=70 + V % 7)
+    w, ks, r = _ragged_case(base, 0, 7)
+    _check(w, ks, r, 7)
+
+
+def test_ragged_longest_drafts():
+    """K_b up to the 64-draft limit (129 rows for one sequence)."""
+    base = replace(WORKLOADS["b8-k5-v32000-f32-zipf"], name="b4-v2048-f32-zipf-k64", B=4, V=2048, seed=77,
+                   temperature=0.9, top_p=0.9)
+    w, ks, r = _ragged_case(base, 60, 64, seed=1)
+    _check(w, ks, r, 64)
+
+
+def test_ragged_bad_token_is_a_sentinel_for_its_sequence_only():
+    w, ks, r = _ragged_case(WORKLOADS["b8-k5-v32000-f32-zipf"], 1, 5, seed=4)
+    x = ragged_draft_tokens(w, r)
+    b = 3
+    x[int(r["cu"][b])] = w.V + 5  # out of range
+    tok, n, _ = run_device_ragged(w, r, x, 5)
+    assert n[b] == -1 and np.all(tok[b] == -1)
+    ref_tok, ref_n = oracle.verify_ragged(r["target"], r["draft"], x, r["uniforms"], r["cu"], w.temperature, w.top_k,
+                                          w.top_p, dtype=w.dtype, max_k=5)
+    assert np.array_equal(n, ref_n) and np.array_equal(tok, ref_tok)
