@@ -299,15 +299,15 @@ int sv_sample(const void* logits, const float* uniforms, float temperature,
  * Launch timing for benchmarks.  Between sv_profile_start() and
  * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug /
  * sv_spec_verify_dt / sv_spec_verify_ragged / sv_spec_verify_probs /
- * sv_sample call records three HIP events on its own
- * stream: before its streaming kernel (the pass that reads every logit once),
- * after it, and after the call's last kernel.  sv_profile_stop() waits for
- * the recorded events and returns the summed durations in milliseconds of the
- * streaming kernel and of the kernels that follow it (row merge, sequence
+ * sv_sample call records three HIP events on its own stream: the start and
+ * the end of its streaming kernel (the pass that reads every logit once),
+ * taken by that kernel's launch (hipExtLaunchKernel), and one after the
+ * call's last kernel.  sv_profile_stop() waits for the recorded events and
+ * returns the summed durations in milliseconds of the streaming kernel and
+ * of what follows it up to the call's end (row merge, sequence
  * finalisation, full-row draw), and the number of calls timed.  Any output
- * pointer may be NULL.  Timing is host-global (not per device); it adds one
- * event record per kernel boundary to each call.  Returns SV_ERR_HIP if an
- * event could not be created, recorded or read.
+ * pointer may be NULL.  Timing is host-global (not per device).  Returns
+ * SV_ERR_HIP if an event could not be created, recorded or read.
  */
 int sv_profile_start(void);
 int sv_profile_stop(double* stream_kernel_ms, double* other_kernels_ms, int64_t* calls);

@@ -9,7 +9,8 @@
 #include <mutex>
 
 namespace sv {
-hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s);
+hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s,
+                         hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
 hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s);
 hipError_t launch_probs(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
@@ -32,10 +33,11 @@ struct Scratch {
 std::mutex g_mu;
 Scratch g_scr[kMaxDevices];
 
-// Launch timing (sv_profile_start / sv_profile_stop): three events per call,
-// recorded on the call's stream before the streaming kernel, after it, and
-// after the call's last kernel.  Slots are reused round-robin; a slot is
-// folded into the totals (synchronising on its last event) before reuse.
+// Launch timing (sv_profile_start / sv_profile_stop): three events per call:
+// the streaming kernel's start and end (recorded by its launch), and one
+// recorded on the call's stream after the call's last kernel.  Slots are
+// reused round-robin; a slot is folded into the totals (synchronising on its
+// last event) before reuse.
 constexpr int kProfSlots = 1024;
 struct ProfSlot {
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
@@ -280,11 +282,12 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.drps = make_udiv((uint32_t)a.rps);
   hipStream_t s = (hipStream_t)stream;
   ProfSlot* prof = prof_begin();
-  if (prof && hipEventRecord(prof->ev[0], s) != hipSuccess) return SV_ERR_HIP;
   // chunk-parallel streaming pass, then one workgroup per row merges it; the
-  // last row of each sequence finishes the sequence
-  if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
-  if (prof && hipEventRecord(prof->ev[1], s) != hipSuccess) return SV_ERR_HIP;
+  // last row of each sequence finishes the sequence.  When timing, the
+  // streaming launch records its own start and end in the slot's events.
+  if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s, prof ? prof->ev[0] : nullptr,
+                    prof ? prof->ev[1] : nullptr) != hipSuccess)
+    return SV_ERR_HIP;
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (mode == M_PLAIN) {
     if (launch_sample(a, dtype, (unsigned)((int64_t)B * nsc), s) != hipSuccess) return SV_ERR_HIP;

@@ -26,6 +26,8 @@
 //   probs_kernel    writes full filtered rows (sv_filtered_probs).
 #include "sv_common.hpp"
 
+#include <hip/hip_ext.h>
+
 #include <climits>
 
 namespace sv {
@@ -2138,9 +2140,15 @@ static KFn pick_probs(int mode) {
   }
 }
 
-// grid: the number of streaming items (one workgroup each).
-hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s) {
+// grid: the number of streaming items (one workgroup each).  With events,
+// the launch itself records the kernel's start and end in them.
+hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s, hipEvent_t e0,
+                         hipEvent_t e1) {
   KFn f = dtype == D_BF16 ? pick_stream_mode<D_BF16>(mode, vec) : pick_stream_mode<D_F32>(mode, vec);
+  if (e0 || e1) {
+    void* args[] = {const_cast<Args*>(&a)};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(f), dim3(grid), dim3(WG), args, 0, s, e0, e1, 0);
+  }
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
   return hipGetLastError();
 }
