@@ -271,6 +271,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.cu = rg ? rg->cu : nullptr;
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
+  a.nsw = (int32_t)((nsc + SPW - 1) / SPW);
   a.do_seq = 1;
   set_scalars(a, T, top_k, top_p, Td);
   bind_scratch(a, base, L);
@@ -290,7 +291,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
     return SV_ERR_HIP;
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (mode == M_PLAIN) {
-    if (launch_sample(a, dtype, (unsigned)((int64_t)B * nsc), s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_sample(a, dtype, (unsigned)((int64_t)B * a.nsw), s) != hipSuccess) return SV_ERR_HIP;
   }
   if (prof) {
     if (hipEventRecord(prof->ev[2], s) != hipSuccess) return SV_ERR_HIP;

@@ -17,6 +17,7 @@ constexpr int KEEP_CAP = 256;    // kept-list capacity per row (one entry per th
 constexpr int SCE = 2048;        // logits per sampling chunk (8 per thread)
 constexpr int SEG = 512;         // logits per sampling segment (one wave)
 constexpr int SEG_PER_SCE = SCE / SEG;
+constexpr int SPW = 4;           // sampling chunks per workgroup of the unfiltered draw
 constexpr int MAX_K = 64;
 // register budget of the streaming kernels: resident workgroups per CU
 template <int DT, bool VEC>
@@ -59,11 +60,17 @@ struct RowRec {
   int32_t pad;
 };
 
-// per sequence, 16 bytes
+// per sequence, 56 bytes: the outcome of the accept tests and, for the
+// unfiltered draw that follows, where its rows lie and their normalisers
 struct SeqRec {
   double Z;
   int32_t n;       // accepted drafts, -1 for a sentinel sequence
   int32_t flags;
+  int32_t rp, rq;  // rows of p and q (q: with given probabilities, the index of its probability row)
+  int32_t tu;      // index of the sequence's sampling uniform
+  int32_t k;       // the sequence's number of drafts
+  float mp, mq;    // row maxima of p and q
+  double sp, sq;   // full-row normalisers of p and q
 };
 
 // Unsigned division by a launch constant d >= 1 as a multiply and a shift:
@@ -98,6 +105,7 @@ struct Args {
   int32_t B, K, V;
   int32_t rps;         // rows per sequence (rectangular; 1 for ragged batches, with K = 0)
   int32_t nchunks, nsc, top_k, do_seq;
+  int32_t nsw;         // sampling workgroups per sequence (SPW sampling chunks each)
   // Rows are numbered in the order they are streamed, and every per-row
   // record is kept under that number.  Rectangular batches: sequence by
   // sequence, row b * rps + j is the sequence's target row j (j <= K) or

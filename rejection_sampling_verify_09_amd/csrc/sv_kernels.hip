@@ -1638,6 +1638,8 @@ struct RowKSm {
   int32_t arg[MAX_RPS];
   int32_t x[MAX_K];
   float u[MAX_K + 1];
+  float rm[MAX_RPS];   // row maxima and normalisers (unfiltered rows: for the draw)
+  double rs[MAX_RPS];
   int32_t fast, big, n, flag;
 };
 
@@ -1746,8 +1748,7 @@ __device__ void sentinel_seq(const Args& a, int b, int t) {
     if (a.out_n) a.out_n[b] = -1;
     if (a.out_z) a.out_z[b] = nanv;
     if (a.out_px) a.out_px[b] = nanv;
-    SeqRec sr;
-    sr.Z = 0.0;
+    SeqRec sr = {};
     sr.n = -1;
     sr.flags = RF_BAD;
     a.seq[b] = sr;
@@ -1816,6 +1817,10 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     sm.rf[j] = ld_dev(&rj->flags);
     sm.nk[j] = ld_dev(&rj->nkept);
     sm.arg[j] = ld_dev(&rj->arg);
+    if (MODE == M_PLAIN) {
+      sm.rm[j] = ld_dev(&rj->m);
+      sm.rs[j] = ld_dev(&rj->S);
+    }
     // q(x_j) in the draft rows' slots
     if (QP && j < K) sm.px[K + 1 + j] = (double)ld_dev(&a.qxs[seq_row<RAG>(a, g, j)]);
   }
@@ -1855,10 +1860,22 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     int big = 0;
     if (lane == 0) {
       if (a.out_n) a.out_n[b] = n;
-      SeqRec sr;
-      sr.Z = 0.0;
+      SeqRec sr = {};
       sr.n = n;
       sr.flags = n < 0 ? RF_BAD : 0;
+      if (MODE == M_PLAIN && n >= 0) {
+        // the unfiltered draw's rows: p at position n; q the draft row n
+        // (or its given probability row) after a rejection
+        const bool res = n < K;
+        sr.rp = seq_row<RAG>(a, g, n);
+        sr.mp = sm.rm[n];
+        sr.sp = sm.rs[n];
+        sr.rq = QP ? g.x0 + (res ? n : 0) : res ? seq_row<RAG>(a, g, K + 1 + n) : sr.rp;
+        sr.mq = (!QP && res) ? sm.rm[K + 1 + n] : 0.0f;
+        sr.sq = (!QP && res) ? sm.rs[K + 1 + n] : 1.0;
+        sr.tu = g.t0 + K;
+        sr.k = K;
+      }
       a.seq[b] = sr;
       if (n < 0 && a.out_z) a.out_z[b] = nanv;
       if (n < 0 && a.out_px) a.out_px[b] = nanv;
@@ -1941,64 +1958,123 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   }
 }
 
-// QP: qr is a row of probabilities (float).
-template <int DT, bool QP = false>
-__device__ __forceinline__ double plain_weight(const char* pr, const char* qr, int j, const RowRec& P,
-                                               const RowRec& Q, bool res, double invTp, double invTq) {
-  const double p = exp(((double)load_elem<DT>(pr, j) - (double)P.m) * invTp) / P.S;
+// Weights of the unfiltered draw: p_j = exp((x_j - m) / T) / S from the
+// row's record, and for a residual max(0, p_j - q_j) with q_j likewise (or
+// read from a row of probabilities, QP).  exp_tab and the reciprocals of the
+// normalisers keep this pass, which touches every logit of two rows, light.
+struct PlainW {
+  float mp, mq;
+  double itp, itq;  // 1 / T of the two rows
+  double rsp, rsq;  // 1 / S of the two rows
+};
+template <bool QP>
+__device__ __forceinline__ double plain_w(float xp, float xq, const PlainW& c, bool res, const double* tab) {
+  const double p = exp_tab(((double)xp - (double)c.mp) * c.itp, tab) * c.rsp;
   if (!res) return p;
-  const double q = QP ? (double)reinterpret_cast<const float*>(qr)[j]
-                      : exp(((double)load_elem<DT>(qr, j) - (double)Q.m) * invTq) / Q.S;
+  const double q = QP ? (double)xq : exp_tab(((double)xq - (double)c.mq) * c.itq, tab) * c.rsq;
   const double d = p - q;
   return d > 0.0 ? d : 0.0;
+}
+template <int DT, bool QP>
+__device__ __forceinline__ double plain_weight(const char* pr, const char* qr, int j, const PlainW& c, bool res,
+                                               const double* tab) {
+  const float xp = load_elem<DT>(pr, j);
+  const float xq = !res ? 0.0f : QP ? reinterpret_cast<const float*>(qr)[j] : load_elem<DT>(qr, j);
+  return plain_w<QP>(xp, xq, c, res, tab);
+}
+// The 8 logits j0 .. j0+7 of a row (-inf past V): one 16-byte load per 8
+// bf16 (two per 8 f32) when rows are 16-byte aligned and the 8 lie in the row.
+template <int DT>
+__device__ __forceinline__ void load8(const char* row, int j0, int V, bool vec, float (&x)[8]) {
+  if (vec && j0 + 8 <= V) {
+    if (DT == D_BF16) {
+      const uint4 r = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 2);
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+      }
+    } else {
+      const uint4 r0 = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 4);
+      const uint4 r1 = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 4 + 16);
+      x[0] = __uint_as_float(r0.x); x[1] = __uint_as_float(r0.y); x[2] = __uint_as_float(r0.z); x[3] = __uint_as_float(r0.w);
+      x[4] = __uint_as_float(r1.x); x[5] = __uint_as_float(r1.y); x[6] = __uint_as_float(r1.z); x[7] = __uint_as_float(r1.w);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = j0 + e < V ? load_elem<DT>(row, j0 + e) : -INFINITY;
+  }
 }
 
 template <int DT, int LAY>
 __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
-  constexpr bool RAG = LAY == LAY_RAG, QP = LAY == LAY_QP;
+  constexpr bool QP = LAY == LAY_QP;
   __shared__ Smem sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   const int t = threadIdx.x;
-  const int b = (int)(blockIdx.x / (unsigned)a.nsc);
-  const int c = (int)blockIdx.x - b * a.nsc;
+  const int b = (int)(blockIdx.x / (unsigned)a.nsw);
+  const int cb = ((int)blockIdx.x - b * a.nsw) * SPW;  // first sampling chunk of this workgroup
   const int nseg = a.nsc * SEG_PER_SCE;
-  const SeqRec sr = a.seq[b];
+  const SeqRec sr = a.seq[b];  // written by the row merge: rows, normalisers, uniform
   const int n = sr.n;
   const bool active = n >= 0;
-  const SeqGeo g = active ? seq_geo<RAG>(a, b) : SeqGeo{0, 0, 0, 0};
-  const int K = g.K;
-  const bool res = active && n < K;
-  const int rlP = seq_row<RAG>(a, g, active ? n : 0);
-  const int rlQ = QP ? rlP : seq_row<RAG>(a, g, res ? K + 1 + n : (active ? n : 0));
-  const double iTp = row_temp(a, rlP).invT, iTq = row_temp(a, rlQ).invT;
-  RowRec P, Q;
-  const char* pr = nullptr;
-  const char* qr = nullptr;
+  const bool res = active && n < sr.k;
+  build_exp_tab(sm.etab);
+  PlainW cw;
+  cw.mp = sr.mp;
+  cw.mq = sr.mq;
+  cw.rsp = 1.0 / sr.sp;
+  cw.rsq = 1.0 / sr.sq;
+  cw.itp = active ? row_temp(a, sr.rp).invT : 0.0;
+  cw.itq = (active && !QP) ? row_temp(a, sr.rq).invT : 0.0;
+  const char* pr = active ? row_ptr(a, sr.rp, ESZ) : nullptr;
+  const char* qr = !active ? nullptr
+                   : QP    ? reinterpret_cast<const char*>(a.qprob + (size_t)sr.rq * a.V)
+                           : row_ptr(a, sr.rq, ESZ);
   if (active) {
-    P = a.row[rlP];
-    Q = a.row[rlQ];
-    pr = row_ptr(a, rlP, ESZ);
-    qr = QP ? reinterpret_cast<const char*>(a.qprob + (size_t)(g.x0 + (res ? n : 0)) * a.V) : row_ptr(a, rlQ, ESZ);
-    const int j0 = c * SCE + t * 8;
-    double ts = 0.0;
-    int lastp = -1;
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + e;
-      if (j < a.V) {
-        const double w = plain_weight<DT, QP>(pr, qr, j, P, Q, res, iTp, iTq);
-        ts += w;
-        if (w > 0.0) lastp = j;
+    // the workgroup's SPW chunks of 2048 logits: every load first, then the
+    // weights and one segment sum per wave and chunk
+    float xp[SPW][8], xq[SPW][8];
+#pragma unroll
+    for (int ci = 0; ci < SPW; ++ci) {
+      const int j0 = (cb + ci) * SCE + t * 8;
+      load8<DT>(pr, j0, a.V, a.ulen > 1, xp[ci]);
+      if (res) {
+        if (QP) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xq[ci][e] = j0 + e < a.V ? reinterpret_cast<const float*>(qr)[j0 + e] : 0.0f;
+        } else {
+          load8<DT>(qr, j0, a.V, a.ulen > 1, xq[ci]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xq[ci][e] = 0.0f;
       }
     }
-    const double ss = wave_sum(ts);
-    const int sl = wave_max(lastp);
-    if ((t & 63) == 0) {
-      const size_t s = (size_t)b * nseg + c * SEG_PER_SCE + (t >> 6);
-      st_dev(&a.seg_sum[s], ss);
-      st_dev(&a.seg_last[s], sl);
+#pragma unroll
+    for (int ci = 0; ci < SPW; ++ci) {
+      const int c = cb + ci;
+      if (c >= a.nsc) break;  // uniform
+      const int j0 = c * SCE + t * 8;
+      double ts = 0.0;
+      int lastp = -1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double w = j0 + e < a.V ? plain_w<QP>(xp[ci][e], xq[ci][e], cw, res, sm.etab) : 0.0;
+        ts += w;
+        if (w > 0.0) lastp = j0 + e;
+      }
+      const double ss = wave_sum(ts);
+      const int sl = wave_max(lastp);
+      if ((t & 63) == 0) {
+        const size_t sg = (size_t)b * nseg + c * SEG_PER_SCE + (t >> 6);
+        st_dev(&a.seg_sum[sg], ss);
+        st_dev(&a.seg_last[sg], sl);
+      }
     }
   }
-  if (!last_arrival(&a.smp_cnt[b], (uint32_t)a.nsc, &sm.flag)) return;
+  if (!last_arrival(&a.smp_cnt[b], (uint32_t)a.nsw, &sm.flag)) return;
   if (!active) return;
 
   const double* ssum = a.seg_sum + (size_t)b * nseg;
@@ -2014,11 +2090,11 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   double Z;
   const double incl = block_incl_scan(loc, sm.red, &Z);
   lastseg = block_max_i(lastseg, sm.red);
-  const double u = (double)a.U[(size_t)g.t0 + K];
+  const double u = (double)a.U[sr.tu];
   int tok;
   if (!(Z > 0.0)) {
     // empty residual (round-off only): draw from p
-    set_draw_row(&a.row[rlP], false, 0, row_temp(a, rlP).invT, sm);
+    set_draw_row(&a.row[sr.rp], false, 0, row_temp(a, sr.rp).invT, sm);
     tok = full_row_sample<DT, WG>(a, u, pr, qr, false, sm, &Z);
   } else {
     const double target = u * Z;
@@ -2045,8 +2121,8 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
       __syncthreads();
       const double cs = sm.d0;
       const int j0 = sf * SEG + 2 * t;
-      const double w0 = j0 < a.V ? plain_weight<DT, QP>(pr, qr, j0, P, Q, res, iTp, iTq) : 0.0;
-      const double w1 = j0 + 1 < a.V ? plain_weight<DT, QP>(pr, qr, j0 + 1, P, Q, res, iTp, iTq) : 0.0;
+      const double w0 = j0 < a.V ? plain_weight<DT, QP>(pr, qr, j0, cw, res, sm.etab) : 0.0;
+      const double w1 = j0 + 1 < a.V ? plain_weight<DT, QP>(pr, qr, j0 + 1, cw, res, sm.etab) : 0.0;
       double tot;
       const double inc2 = block_incl_scan(w0 + w1, sm.red, &tot);
       __syncthreads();
@@ -2066,7 +2142,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     a.out_tok[(size_t)b * (a.Kmax + 1) + n] = tok;
     if (a.out_z) a.out_z[b] = Z;
     if (a.out_px)
-      a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll) : plain_weight<DT, QP>(pr, qr, tok, P, Q, false, iTp, iTq);
+      a.out_px[b] = res ? __longlong_as_double(0x7FF8000000000000ll) : plain_weight<DT, QP>(pr, qr, tok, cw, false, sm.etab);
   }
 }
 
