@@ -84,13 +84,14 @@ ProfSlot* prof_begin() {
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t seq_cnt, smp_cnt, chunk, cand, row, kidx, kprob, seq, seg_sum, seg_last, qxs, total;
+  size_t seq_cnt, smp_cnt, chunk, ctop, cand, row, kidx, kprob, seq, seg_sum, seg_last, qxs, total;
 };
 
 // What one call needs from the scratch.
 struct Need {
   int64_t rows = 0, nchunks = 0, B = 0, nseg = 0;  // nseg: sampling segments per sequence
   bool filt = false;                               // candidate and kept lists
+  bool topk = false;                               // the chunks' largest thread maxima
 };
 
 // Counters first (a fixed region for the life of the allocation: the kernels
@@ -102,6 +103,7 @@ Layout make_layout(int64_t cap_seq, const Need& n) {
   L.seq_cnt = o; o += al256(cap_seq * 4);
   L.smp_cnt = o; o += al256(cap_seq * 4);
   L.chunk = o; o += al256(n.rows * n.nchunks * sizeof(ChunkRec));
+  L.ctop = o; o += n.topk ? al256(n.rows * n.nchunks * CTOP * sizeof(uint32_t)) : 0;
   L.cand = o; o += n.filt ? al256(n.rows * n.nchunks * CAND_CAP * sizeof(uint64_t)) : 0;
   L.row = o; o += al256(n.rows * sizeof(RowRec));
   L.kidx = o; o += n.filt ? al256(n.rows * KEEP_CAP * sizeof(int32_t)) : 0;
@@ -151,6 +153,7 @@ void bind_scratch(Args& a, char* base, const Layout& L) {
   a.seq_cnt = (uint32_t*)(base + L.seq_cnt);
   a.smp_cnt = (uint32_t*)(base + L.smp_cnt);
   a.chunk = (ChunkRec*)(base + L.chunk);
+  a.ctop = (uint32_t*)(base + L.ctop);
   a.cand = (uint64_t*)(base + L.cand);
   a.row = (RowRec*)(base + L.row);
   a.kidx = (int32_t*)(base + L.kidx);
@@ -243,6 +246,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   need.B = B;
   need.nseg = nsc * SEG_PER_SCE;
   need.filt = mode == M_TOPK || mode == M_TOPP || mode == M_TOPKP;
+  need.topk = mode == M_TOPK || mode == M_TOPKP;
 
   char* base = nullptr;
   Layout L;
@@ -376,6 +380,7 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   need.nchunks = nchunks;
   need.B = rows;
   need.filt = mode != M_PLAIN;
+  need.topk = mode == M_TOPK || mode == M_TOPKP;
 
   char* base = nullptr;
   Layout L;

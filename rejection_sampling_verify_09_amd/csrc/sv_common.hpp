@@ -18,6 +18,8 @@ constexpr int SCE = 2048;        // logits per sampling chunk (8 per thread)
 constexpr int SEG = 512;         // logits per sampling segment (one wave)
 constexpr int SEG_PER_SCE = SCE / SEG;
 constexpr int SPW = 4;           // sampling chunks per workgroup of the unfiltered draw
+constexpr int CTOP = 8;          // top-k: largest thread maxima a chunk records for the row merge
+constexpr int CTOP_CHUNKS = 64;  // ... used by the row merge for rows of at most this many chunks
 constexpr int MAX_K = 64;
 // register budget of the streaming kernels: resident workgroups per CU
 template <int DT, bool VEC>
@@ -126,6 +128,7 @@ struct Args {
   double invTd;
   double top_p;
   ChunkRec* chunk;
+  uint32_t* ctop;  // top-k: per (row, chunk), keys of the chunk's CTOP largest thread maxima, descending
   uint64_t* cand;
   RowRec* row;
   int32_t* kidx;

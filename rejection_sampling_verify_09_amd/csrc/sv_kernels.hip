@@ -849,6 +849,9 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
       sm.s.tk[t] = ord_key(tm);
       bitonic_desc(sm.s.tk, WG);
       bound = a.top_k <= WG ? (uint32_t)sm.s.tk[a.top_k - 1] : KEY_NEG_INF;
+      // the chunk's largest thread maxima: values of the row, from which the
+      // row merge bounds the row's k-th largest from below
+      if (t < CTOP) a.ctop[(size_t)chunk_id * CTOP + t] = (uint32_t)sm.s.tk[t];
     }
     thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
     const int w = t >> 6;
@@ -1195,12 +1198,13 @@ struct WaveRowSm {
 // point).  F is non-increasing in t, so the result is the key of an entry.
 // Returns 0 when the total weight is below target.  Radix search over the
 // key, 8 bits per pass, bins in LDS.
-__device__ __forceinline__ uint32_t wave_radix(const uint32_t (&ek)[WR_EPL], const unsigned long long (&wt)[WR_EPL],
+template <int S = WR_EPL>
+__device__ __forceinline__ uint32_t wave_radix(const uint32_t (&ek)[S], const unsigned long long (&wt)[S],
                                unsigned long long target, unsigned long long* hist) {
   const int lane = threadIdx.x & 63;
   unsigned long long tot = 0;
 #pragma unroll
-  for (int r = 0; r < WR_EPL; ++r) tot += wt[r];
+  for (int r = 0; r < S; ++r) tot += wt[r];
   tot = lane63(wave_scan_u64(tot));
   if (tot < target) return 0u;
   uint32_t prefix = 0, pmask = 0;
@@ -1211,7 +1215,7 @@ __device__ __forceinline__ uint32_t wave_radix(const uint32_t (&ek)[WR_EPL], con
     for (int q = 0; q < 4; ++q) hist[lane * 4 + q] = 0ull;
     wave_sync();
 #pragma unroll
-    for (int r = 0; r < WR_EPL; ++r)
+    for (int r = 0; r < S; ++r)
       if (wt[r] != 0ull && (ek[r] & pmask) == prefix) atomicAdd(&hist[(ek[r] >> shift) & 255u], wt[r]);
     wave_sync();
     // lane L holds digits 255 - 4L - q (descending digit order across the wave)
@@ -1379,6 +1383,15 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       if (MODE == M_GREEDY) carg[i] = cr[c].arg;
     }
   }
+  // top-k: the chunks' largest thread maxima (rows of at most CTOP_CHUNKS chunks)
+  constexpr bool TOPKM = MODE == M_TOPK || MODE == M_TOPKP;
+  uint4 ctq[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  const bool use_top = TOPKM && nch <= CTOP_CHUNKS && nch * CTOP >= a.top_k;
+  if (use_top && lane < nch) {
+    const uint4* tp = reinterpret_cast<const uint4*>(a.ctop + ((size_t)rl * nch + lane) * CTOP);
+    ctq[0] = tp[0];
+    ctq[1] = tp[1];
+  }
   const float lx = (MODE != M_GREEDY && hx) ? load_elem<DT>(row_ptr(a, rl, ElemT<DT>::ESZ), xtok) : -INFINITY;
   // with them, speculatively, entry `lane` of the first SPECC chunks' lists
   // (most lists are shorter than 64 units): one round trip for most rows
@@ -1424,6 +1437,17 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     // whose max lies below lo holds none of them
     uint32_t lo = dpp_wave_umax(max(max(cb[0], cb[1]), max(cb[2], cb[3])));
     if (MODE == M_TOPP) lo = max(lo, ord_key(m - rt.win));
+    if (TOPKM && use_top) {
+      // the k-th largest of the chunks' recorded maxima (logits of the row)
+      // is at most the row's k-th largest logit: a tighter bound than any
+      // single chunk's
+      const uint32_t ck[CTOP] = {ctq[0].x, ctq[0].y, ctq[0].z, ctq[0].w, ctq[1].x, ctq[1].y, ctq[1].z, ctq[1].w};
+      unsigned long long cw1[CTOP];
+#pragma unroll
+      for (int i = 0; i < CTOP; ++i) cw1[i] = ck[i] > KEY_NEG_INF ? 1ull : 0ull;
+      lo = max(lo, wave_radix<CTOP>(ck, cw1, (unsigned long long)a.top_k, ws.hist));
+      wave_sync();
+    }
     // a chunk whose max lies below lo holds none of them
     int ce4[4];
 #pragma unroll
