@@ -275,7 +275,10 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.cu = rg ? rg->cu : nullptr;
   a.nchunks = (int32_t)nchunks;
   a.nsc = (int32_t)nsc;
-  a.nsw = (int32_t)((nsc + SPW - 1) / SPW);
+  // sampling chunks per workgroup: up to SPW (fewer, longer workgroups
+  // measured faster), while at least one workgroup per compute unit remains
+  a.spw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(SPW, (int64_t)B * nsc / 256));
+  a.nsw = (int32_t)((nsc + a.spw - 1) / a.spw);
   a.do_seq = 1;
   set_scalars(a, T, top_k, top_p, Td);
   bind_scratch(a, base, L);

@@ -17,7 +17,7 @@ constexpr int KEEP_CAP = 256;    // kept-list capacity per row (one entry per th
 constexpr int SCE = 2048;        // logits per sampling chunk (8 per thread)
 constexpr int SEG = 512;         // logits per sampling segment (one wave)
 constexpr int SEG_PER_SCE = SCE / SEG;
-constexpr int SPW = 4;           // sampling chunks per workgroup of the unfiltered draw
+constexpr int SPW = 4;           // most sampling chunks per workgroup of the unfiltered draw
 constexpr int CTOP = 8;          // top-k: largest thread maxima a chunk records for the row merge
 constexpr int CTOP_CHUNKS = 64;  // ... used by the row merge for rows of at most this many chunks
 constexpr int MAX_K = 64;
@@ -107,7 +107,7 @@ struct Args {
   int32_t B, K, V;
   int32_t rps;         // rows per sequence (rectangular; 1 for ragged batches, with K = 0)
   int32_t nchunks, nsc, top_k, do_seq;
-  int32_t nsw;         // sampling workgroups per sequence (SPW sampling chunks each)
+  int32_t nsw, spw;    // sampling workgroups per sequence, and sampling chunks each (at most SPW)
   // Rows are numbered in the order they are streamed, and every per-row
   // record is kept under that number.  Rectangular batches: sequence by
   // sequence, row b * rps + j is the sequence's target row j (j <= K) or

@@ -2038,7 +2038,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   constexpr int ESZ = ElemT<DT>::ESZ;
   const int t = threadIdx.x;
   const int b = (int)(blockIdx.x / (unsigned)a.nsw);
-  const int cb = ((int)blockIdx.x - b * a.nsw) * SPW;  // first sampling chunk of this workgroup
+  const int cb = ((int)blockIdx.x - b * a.nsw) * a.spw;  // first sampling chunk of this workgroup
   const int nseg = a.nsc * SEG_PER_SCE;
   const SeqRec sr = a.seq[b];  // written by the row merge: rows, normalisers, uniform
   const int n = sr.n;
@@ -2057,11 +2057,12 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
                    : QP    ? reinterpret_cast<const char*>(a.qprob + (size_t)sr.rq * a.V)
                            : row_ptr(a, sr.rq, ESZ);
   if (active) {
-    // the workgroup's SPW chunks of 2048 logits: every load first, then the
+    // the workgroup's spw chunks of 2048 logits: every load first, then the
     // weights and one segment sum per wave and chunk
     float xp[SPW][8], xq[SPW][8];
 #pragma unroll
     for (int ci = 0; ci < SPW; ++ci) {
+      if (ci >= a.spw) break;  // uniform
       const int j0 = (cb + ci) * SCE + t * 8;
       load8<DT>(pr, j0, a.V, a.ulen > 1, xp[ci]);
       if (res) {
@@ -2079,7 +2080,7 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
 #pragma unroll
     for (int ci = 0; ci < SPW; ++ci) {
       const int c = cb + ci;
-      if (c >= a.nsc) break;  // uniform
+      if (ci >= a.spw || c >= a.nsc) break;  // uniform
       const int j0 = c * SCE + t * 8;
       double ts = 0.0;
       int lastp = -1;
