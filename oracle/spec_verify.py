@@ -62,6 +62,7 @@ __all__ = [
 
 BF16 = "bf16"
 F32 = "f32"
+F64 = "f64"  # logits computed by the oracle itself (the language-model head)
 
 
 # ---------------------------------------------------------------------------
@@ -72,7 +73,8 @@ def widen(logits: np.ndarray, dtype: str) -> np.ndarray:
 
     ``dtype == "bf16"``: ``logits`` is a uint16 array of bfloat16 bit patterns;
     the pattern is the upper half of the float32 with the same value, so the
-    widening is exact.  ``dtype == "f32"``: a float32 array.
+    widening is exact.  ``dtype == "f32"``: a float32 array.  ``dtype ==
+    "f64"``: a float64 array, taken as it is.
     """
     if dtype == BF16:
         a = np.asarray(logits)
@@ -84,6 +86,11 @@ def widen(logits: np.ndarray, dtype: str) -> np.ndarray:
         if a.dtype != np.float32:
             raise TypeError("f32 logits must be a float32 array")
         return a.astype(np.float64)
+    if dtype == F64:
+        a = np.asarray(logits)
+        if a.dtype != np.float64:
+            raise TypeError("f64 logits must be a float64 array")
+        return a
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

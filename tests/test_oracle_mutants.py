@@ -62,6 +62,41 @@ MUTANTS = {
                            lambda m: rag.check_ragged_lossless(m, N=60_000)),
 }
 
+# planted mistakes in the language-model-head verification (oracle/lmhead.py)
+LMHEAD_MUTANTS = {
+    # the draft's logits formed with the target's projection
+    "draft_head_weights": ("ld = lm_logits(hidden_d, weight_d, dtype)", "ld = lm_logits(hidden_d, weight_t, dtype)"),
+    # the projection's rows taken in reverse vocabulary order
+    "vocab_order": ("return np.matmul(h, w.T)", "return np.matmul(h, w[::-1].T)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LMHEAD_MUTANTS))
+def test_lmhead_mutant_is_caught(name):
+    import sys
+
+    from tests import test_oracle_lmhead as lmt
+
+    old, new = LMHEAD_MUTANTS[name]
+    path = os.path.join(ORACLE, "lmhead.py")
+    with open(path) as f:
+        src = f.read()
+    assert src.count(old) == 1
+    # the module imports its siblings relatively: load it as part of the package
+    mod = types.ModuleType("oracle.lmhead_mutant")
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    saved = lmt.oracle
+    try:
+        shim = types.SimpleNamespace(verify_lmhead=mod.verify_lmhead, lm_logits=mod.lm_logits)
+        lmt.oracle = shim
+        with pytest.raises(AssertionError):
+            lmt.test_one_hot_hidden_selects_a_column()
+            lmt.test_lmhead_lossless_chi2()
+    finally:
+        lmt.oracle = saved
+
+
 # planted mistakes in the draft-length controller (oracle/dynamic_k.py)
 CONTROLLER_MUTANTS = {
     # the window kept across a change of K
