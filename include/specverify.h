@@ -296,6 +296,60 @@ int sv_sample(const void* logits, const float* uniforms, float temperature,
               int32_t rows, int32_t V, int32_t dtype, void* stream);
 
 /*
+ * sv_lm_logits - the output projection of a language model: logits[m, j] =
+ * sum_i hidden[m, i] * weight[j, i], every position's hidden state mapped to
+ * one logit per vocabulary entry (the step whose weight reads dominate a
+ * decoding step: page www.2kiu.com/news/5895634 section 1, page
+ * www.cf-1.com/news/5155685 section 2.1).  Products of two bfloat16 values
+ * are exact in float32; the sums are accumulated in float32 by the matrix
+ * cores (v_mfma_f32_32x32x16_bf16), in an order the library fixes.
+ *
+ * hidden      [M, d] bfloat16, device, 16-byte aligned
+ * weight      [V, d] bfloat16, device, 16-byte aligned (d contiguous in both)
+ * out_logits  [M, V] float32, device (any alignment), written entirely
+ * M >= 0, 1 <= V <= SV_MAX_V, d a multiple of 64 in [64, 65536] (else
+ * SV_ERR_SHAPE; misaligned operands are SV_ERR_SHAPE too).  M == 0 does
+ * nothing.  The library allocates nothing for this call.
+ */
+int sv_lm_logits(const void* hidden, const void* weight, float* out_logits,
+                 int32_t M, int32_t V, int32_t d, void* stream);
+
+/*
+ * sv_spec_verify_lmhead - verification fed directly by the two models'
+ * output projections: the target's logits for all K+1 positions come from
+ * its hidden states and its projection in one pass (page www.gsyq.cn/news/
+ * 428210 section 3.1), the draft's K rows from its own (a smaller model of
+ * the same family: its width d_draft may differ, the vocabulary is shared;
+ * page www.2kiu.com/news/5895634 section 4.1), and the verification of
+ * sv_spec_verify_debug runs on them.  Equivalent to sv_lm_logits on both
+ * followed by sv_spec_verify_debug with dtype SV_F32.
+ *
+ * hidden_target  [B, K+1, d_target] bfloat16, device, 16-byte aligned
+ * weight_target  [V, d_target] bfloat16, device, 16-byte aligned
+ * hidden_draft   [B, K, d_draft] bfloat16, device, 16-byte aligned
+ * weight_draft   [V, d_draft] bfloat16, device, 16-byte aligned
+ *                (both draft arguments unused, and may be NULL, when
+ *                temperature == 0 or K == 0)
+ * draft_tokens, uniforms, temperature, top_k, top_p, out_tokens,
+ * out_num_accepted, out_p, out_q, out_z, B, K, V: as sv_spec_verify_debug.
+ * d_target, d_draft: as d of sv_lm_logits.
+ *
+ * The logits live in a second per-device buffer of (B(K+1) + BK) * V
+ * float32, grown on demand like the scratch (the growth synchronises the
+ * device) and freed by sv_release.  Under launch timing the first two
+ * events of the call bracket the two projections (its stream_kernel_ms) and
+ * the third follows the verification.
+ */
+int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target,
+                          const void* hidden_draft, const void* weight_draft,
+                          const int32_t* draft_tokens, const float* uniforms,
+                          float temperature, int32_t top_k, float top_p,
+                          int32_t* out_tokens, int32_t* out_num_accepted,
+                          double* out_p, double* out_q, double* out_z,
+                          int32_t B, int32_t K, int32_t V,
+                          int32_t d_target, int32_t d_draft, void* stream);
+
+/*
  * Launch timing for benchmarks.  Between sv_profile_start() and
  * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug /
  * sv_spec_verify_dt / sv_spec_verify_ragged / sv_spec_verify_probs /
@@ -306,16 +360,20 @@ int sv_sample(const void* logits, const float* uniforms, float temperature,
  * returns the summed durations in milliseconds of the streaming kernel and
  * of what follows it up to the call's end (row merge, sequence
  * finalisation, full-row draw), and the number of calls timed.  Any output
- * pointer may be NULL.  Timing is host-global (not per device).  Returns
- * SV_ERR_HIP if an event could not be created, recorded or read.
+ * pointer may be NULL.  An sv_spec_verify_lmhead call is timed too, with
+ * its two projections in place of the streaming kernel.  Timing is
+ * host-global (not per device).  Returns SV_ERR_HIP if an event could not be
+ * created, recorded or read.
  */
 int sv_profile_start(void);
 int sv_profile_stop(double* stream_kernel_ms, double* other_kernels_ms, int64_t* calls);
 
-/* Frees the per-device scratch of every device the library has used. */
+/* Frees the per-device scratch (and logits buffer) of every device the
+ * library has used. */
 int sv_release(void);
 
-/* Bytes of device scratch currently held on `device` (0 if none). */
+/* Bytes of device scratch and logits buffer currently held on `device`
+ * (0 if none). */
 int64_t sv_scratch_bytes(int device);
 
 /* Human-readable name of a status code. */

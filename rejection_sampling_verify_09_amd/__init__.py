@@ -11,15 +11,17 @@ from ._lib import (  # noqa: F401
     SpecVerifyError,
     filtered_probs,
     lib,
+    lm_logits,
     profile_start,
     profile_stop,
     release,
     sample,
     spec_verify,
+    spec_verify_lmhead,
     spec_verify_probs,
     spec_verify_ragged,
     status_string,
 )
 
-__all__ = ["spec_verify", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
+__all__ = ["spec_verify", "spec_verify_lmhead", "lm_logits", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
            "SpecVerifyError"]

@@ -51,6 +51,11 @@ def lib() -> ctypes.CDLL:
         L.sv_spec_verify_ragged.restype = ctypes.c_int
         L.sv_spec_verify_probs.argtypes = [vp, vp, vp, vp, f32, i32, f32, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
         L.sv_spec_verify_probs.restype = ctypes.c_int
+        L.sv_lm_logits.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.sv_lm_logits.restype = ctypes.c_int
+        L.sv_spec_verify_lmhead.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, f32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                            i32, i32, vp]
+        L.sv_spec_verify_lmhead.restype = ctypes.c_int
         L.sv_dynk_create.argtypes = [i32, i32, ctypes.c_double, ctypes.c_double, i32, i32, i32]
         L.sv_dynk_create.restype = vp
         L.sv_dynk_observe.argtypes = [vp, vp, vp, vp]
@@ -279,6 +284,80 @@ def spec_verify_probs(target_logits: torch.Tensor, draft_probs: torch.Tensor | N
     if debug:
         return out_tokens, out_num_accepted, dict(p=out_p, q=out_q, z=out_z)
     return out_tokens, out_num_accepted
+
+
+def lm_logits(hidden: torch.Tensor, weight: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """Output projection: hidden [..., d] bfloat16 times weight [V, d]
+    bfloat16, transposed -> float32 logits [..., V]."""
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    if weight.dim() != 2 or hidden.shape[-1] != weight.shape[1]:
+        raise ValueError("hidden [..., d] and weight [V, d] must share d")
+    V, d = weight.shape
+    M = hidden.numel() // d if d > 0 else 0
+    shape = tuple(hidden.shape[:-1]) + (V,)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=hidden.device)
+    elif tuple(out.shape) != shape:
+        raise ValueError(f"out must be {shape}")
+    st = lib().sv_lm_logits(_dev(hidden, "hidden"), _dev(weight, "weight"), _dev(out, "out", torch.float32), M, V, d,
+                            _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_lm_logits")
+    return out
+
+
+def spec_verify_lmhead(hidden_target: torch.Tensor, weight_target: torch.Tensor, hidden_draft: torch.Tensor | None,
+                       weight_draft: torch.Tensor | None, draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                       temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0, stream=None,
+                       debug: bool = False):
+    """Verification fed by the output projections: hidden_target [B, K+1, d]
+    and weight_target [V, d] (bfloat16), hidden_draft [B, K, d_d] and
+    weight_draft [V, d_d] (bfloat16; may be None at temperature 0),
+    draft_tokens [B, K] int32, uniforms [B, K+1] float32.  Returns
+    (out_tokens, out_num_accepted), plus p(x), q(x), Z when ``debug``."""
+    if hidden_target.dim() != 3 or weight_target.dim() != 2:
+        raise ValueError("hidden_target must be [B, K+1, d] and weight_target [V, d]")
+    B, K1, d = hidden_target.shape
+    K = K1 - 1
+    V = weight_target.shape[0]
+    if weight_target.shape[1] != d:
+        raise ValueError("hidden_target and weight_target must share d")
+    for t, n in ((hidden_target, "hidden_target"), (weight_target, "weight_target")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+    dev = hidden_target.device
+    use_d = float(temperature) != 0.0 and K > 0
+    hd = wd = None
+    dd = 64
+    if use_d:
+        if hidden_draft is None or weight_draft is None:
+            raise ValueError("hidden_draft and weight_draft are required unless temperature == 0")
+        if hidden_draft.dtype != torch.bfloat16 or weight_draft.dtype != torch.bfloat16:
+            raise TypeError("hidden_draft and weight_draft must be bfloat16")
+        dd = weight_draft.shape[1]
+        if tuple(hidden_draft.shape) != (B, K, dd) or tuple(weight_draft.shape) != (V, dd):
+            raise ValueError("hidden_draft must be [B, K, d_d] and weight_draft [V, d_d]")
+        hd, wd = _dev(hidden_draft, "hidden_draft"), _dev(weight_draft, "weight_draft")
+    if tuple(draft_tokens.shape) != (B, K) or tuple(uniforms.shape) != (B, K + 1):
+        raise ValueError("draft_tokens must be [B, K] and uniforms [B, K+1]")
+    xp = _dev(draft_tokens, "draft_tokens", torch.int32) if K > 0 else None
+    up = _dev(uniforms, "uniforms", torch.float32)
+    out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_p = torch.empty((B, K), dtype=torch.float64, device=dev) if debug else None
+    out_q = torch.empty((B, K), dtype=torch.float64, device=dev) if debug else None
+    out_z = torch.empty((B,), dtype=torch.float64, device=dev) if debug else None
+    st = lib().sv_spec_verify_lmhead(_dev(hidden_target, "hidden_target"), _dev(weight_target, "weight_target"), hd, wd,
+                                     xp, up, float(temperature), int(top_k), float(top_p), out_tokens.data_ptr(),
+                                     out_n.data_ptr(), out_p.data_ptr() if debug and K > 0 else None,
+                                     out_q.data_ptr() if debug and K > 0 else None,
+                                     out_z.data_ptr() if debug else None, B, K, V, d, dd, _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_spec_verify_lmhead")
+    if debug:
+        return out_tokens, out_n, dict(p=out_p, q=out_q, z=out_z)
+    return out_tokens, out_n
 
 
 class DraftLengthController:

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["sv_kernels.hip", "sv_api.hip", "sv_dynk.cpp"]
+SOURCES = ["sv_kernels.hip", "sv_api.hip", "sv_lmhead.hip", "sv_dynk.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -14,6 +14,8 @@ hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned 
 hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
 hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s);
 hipError_t launch_probs(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
+hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s);
+int64_t lm_gemm_tiles(int32_t M, int32_t V);
 }  // namespace sv
 
 using namespace sv;
@@ -32,6 +34,14 @@ struct Scratch {
 
 std::mutex g_mu;
 Scratch g_scr[kMaxDevices];
+
+// Logits formed by the output projection for verification (float32, target
+// rows then draft rows), per device, grown on demand (guarded by g_mu).
+struct LogitBuf {
+  float* ptr = nullptr;
+  size_t bytes = 0;
+};
+LogitBuf g_lgt[kMaxDevices];
 
 // Launch timing (sv_profile_start / sv_profile_stop): three events per call:
 // the streaming kernel's start and end (recorded by its launch), and one
@@ -216,7 +226,8 @@ struct Ragged {
 int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, float Td,
                 int32_t top_k, float top_p, int32_t* out_tok, int32_t* out_n, bool need_n, double* out_p,
                 double* out_q, double* out_z, double* out_px, int32_t B, int32_t K, int32_t V, int32_t dtype,
-                void* stream, const Ragged* rg = nullptr, const float* qprob = nullptr, bool qp = false) {
+                void* stream, const Ragged* rg = nullptr, const float* qprob = nullptr, bool qp = false,
+                bool timed = true) {
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > MAX_V) return SV_ERR_SHAPE;
   if (rg && (rg->nd < 0 || rg->kmax < 0 || rg->kmax > SV_MAX_K || (int64_t)rg->nd > (int64_t)B * rg->kmax))
     return SV_ERR_SHAPE;
@@ -289,7 +300,7 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.rps = rg ? 1 : (mode == M_GREEDY || use_qp) ? a.K + 1 : 2 * a.K + 1;
   a.drps = make_udiv((uint32_t)a.rps);
   hipStream_t s = (hipStream_t)stream;
-  ProfSlot* prof = prof_begin();
+  ProfSlot* prof = timed ? prof_begin() : nullptr;
   // chunk-parallel streaming pass, then one workgroup per row merges it; the
   // last row of each sequence finishes the sequence.  When timing, the
   // streaming launch records its own start and end in the slot's events.
@@ -308,9 +319,92 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   return SV_OK;
 }
 
+// Largest hidden width accepted (the kernel needs only d % 64 == 0).
+constexpr int32_t kMaxHidden = 1 << 16;
+
+int check_lm_shape(const void* H, const void* W, int64_t M, int32_t V, int32_t d) {
+  if (M < 0 || V < 1 || V > MAX_V || d < 64 || d > kMaxHidden || d % 64 != 0) return SV_ERR_SHAPE;
+  if (M > 0 && (!H || !W)) return SV_ERR_NULL;
+  if (M > 0 && (!aligned16(H) || !aligned16(W))) return SV_ERR_SHAPE;
+  if (M > INT32_MAX || sv::lm_gemm_tiles((int32_t)std::min<int64_t>(M, INT32_MAX), V) > kMaxGrid) return SV_ERR_SHAPE;
+  return SV_OK;
+}
+
+// The logits buffer of the current device, at least `bytes` long.
+int get_logit_buf(size_t bytes, float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  LogitBuf& b = g_lgt[dev];
+  if (b.bytes < bytes) {
+    if (b.ptr) {
+      if (hipDeviceSynchronize() != hipSuccess) return SV_ERR_HIP;
+      (void)hipFree(b.ptr);
+      b = LogitBuf();
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return SV_ERR_WORKSPACE;
+    b.ptr = (float*)p;
+    b.bytes = bytes;
+  }
+  *out = b.ptr;
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sv_lm_logits(const void* hidden, const void* weight, float* out_logits, int32_t M, int32_t V, int32_t d,
+                 void* stream) {
+  int st = check_lm_shape(hidden, weight, M, V, d);
+  if (st != SV_OK) return st;
+  if (M == 0) return SV_OK;
+  if (!out_logits) return SV_ERR_NULL;
+  return launch_lm_gemm(hidden, weight, out_logits, M, V, d, (hipStream_t)stream) == hipSuccess ? SV_OK
+                                                                                                : SV_ERR_HIP;
+}
+
+int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target, const void* hidden_draft,
+                          const void* weight_draft, const int32_t* draft_tokens, const float* uniforms,
+                          float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
+                          int32_t* out_num_accepted, double* out_p, double* out_q, double* out_z, int32_t B,
+                          int32_t K, int32_t V, int32_t d_target, int32_t d_draft, void* stream) {
+  if (B < 0 || K < 0 || K > SV_MAX_K) return SV_ERR_SHAPE;
+  int st = check_params(temperature, top_k, top_p);
+  if (st != SV_OK) return st;
+  const bool greedy = temperature == 0.0f;
+  const int64_t mt = (int64_t)B * (K + 1), md = greedy ? 0 : (int64_t)B * K;
+  st = check_lm_shape(hidden_target, weight_target, mt, V, d_target);
+  if (st != SV_OK) return st;
+  if (md > 0 && (st = check_lm_shape(hidden_draft, weight_draft, md, V, d_draft)) != SV_OK) return st;
+  if (B == 0) return SV_OK;
+  if (!uniforms || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SV_ERR_NULL;
+  float* lg = nullptr;
+  st = get_logit_buf((size_t)(mt + md) * (size_t)V * sizeof(float), &lg);
+  if (st != SV_OK) return st;
+  float* lt = lg;
+  float* ld = md > 0 ? lg + (size_t)mt * V : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  // when timing, the slot's first two events bracket the two projections and
+  // the third follows the verification
+  ProfSlot* prof = prof_begin();
+  if (prof && hipEventRecord(prof->ev[0], s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_lm_gemm(hidden_target, weight_target, lt, (int32_t)mt, V, d_target, s) != hipSuccess) return SV_ERR_HIP;
+  if (md > 0 && launch_lm_gemm(hidden_draft, weight_draft, ld, (int32_t)md, V, d_draft, s) != hipSuccess)
+    return SV_ERR_HIP;
+  if (prof && hipEventRecord(prof->ev[1], s) != hipSuccess) return SV_ERR_HIP;
+  st = verify_impl(lt, ld, draft_tokens, uniforms, temperature, temperature, top_k, top_p, out_tokens,
+                   out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, SV_F32, stream, nullptr, nullptr,
+                   false, false);
+  if (st != SV_OK) return st;
+  if (prof) {
+    if (hipEventRecord(prof->ev[2], s) != hipSuccess) return SV_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    prof->pending = true;
+  }
+  return SV_OK;
+}
 
 int sv_spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                    const float* uniforms, float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
@@ -444,10 +538,13 @@ int sv_release(void) {
   if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_HIP;
   for (int d = 0; d < kMaxDevices; ++d) {
     Scratch& s = g_scr[d];
-    if (!s.ptr) continue;
-    if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess || hipFree(s.ptr) != hipSuccess)
-      rc = SV_ERR_HIP;
+    LogitBuf& b = g_lgt[d];
+    if (!s.ptr && !b.ptr) continue;
+    if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = SV_ERR_HIP;
+    if (s.ptr && hipFree(s.ptr) != hipSuccess) rc = SV_ERR_HIP;
+    if (b.ptr && hipFree(b.ptr) != hipSuccess) rc = SV_ERR_HIP;
     s = Scratch();
+    b = LogitBuf();
   }
   (void)hipSetDevice(cur);
   return rc;
@@ -456,7 +553,7 @@ int sv_release(void) {
 int64_t sv_scratch_bytes(int device) {
   if (device < 0 || device >= kMaxDevices) return 0;
   std::lock_guard<std::mutex> lk(g_mu);
-  return (int64_t)g_scr[device].bytes;
+  return (int64_t)(g_scr[device].bytes + g_lgt[device].bytes);
 }
 
 const char* sv_status_string(int status) {

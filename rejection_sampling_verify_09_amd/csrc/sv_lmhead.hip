@@ -1,0 +1,184 @@
+// The output projection of a language model on the matrix cores: logits
+// [M, V] (float32) = hidden [M, d] (bfloat16) x W^T, W [V, d] (bfloat16),
+// both operands with d contiguous.  Each scored position's hidden state maps
+// to one logit per vocabulary entry, and a decoding step spends its time
+// reading W (page www.2kiu.com/news/5895634 §1; page www.cf-1.com/news/5155685
+// §2.1); the target scores all K+1 positions of a round in one pass (page
+// www.gsyq.cn/news/428210 §3.1), so W is read once for M = B(K+1) rows.
+//
+// Tiling (gfx950, v_mfma_f32_32x32x16_bf16, 64-wide waves):
+//  * a workgroup (4 waves) owns a 128-row x 256-column tile of the output;
+//    wave w owns columns [64w, 64w + 64) of it for all 128 rows: 4 x 2 tiles
+//    of 32 x 32, 128 float32 accumulators per lane;
+//  * the W operand of a wave is its own: each lane reads 64 contiguous bytes
+//    (32 values of k) of one W row per 64-wide k block straight into
+//    registers, one k block ahead of the matrix instructions;
+//  * the hidden operand is shared by the 4 waves: the workgroup stages each
+//    128 x 64 k block of it in LDS (double-buffered, one barrier per block);
+//  * within a k block the sum over k is taken in a fixed permuted order that
+//    both operands follow: lane half h of step s holds k = 32h + 8s + 0..7,
+//    so every lane's operand bytes are contiguous in memory and in LDS;
+//  * the 128-row tiles of one 256-column W panel are consecutive tile ids
+//    placed on one XCD (workgroup ids go round-robin over the 8 XCDs), so the
+//    panel is read from HBM once and served to the other row tiles by that
+//    XCD's L2.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace sv {
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int LM_BM = 128;      // rows of hidden per tile
+constexpr int LM_BN = 256;      // vocabulary entries per tile
+constexpr int LM_BK = 64;       // k per staged block
+constexpr int LM_WG = 256;      // threads (4 waves)
+constexpr int LM_XCD = 8;       // XCDs the workgroup ids are dealt over
+constexpr int LM_ROWB = 144;    // LDS bytes per staged hidden row: 128 of data, 16 of padding
+
+struct LmArgs {
+  const uint16_t* H;  // [M, d] bfloat16 bit patterns
+  const uint16_t* W;  // [V, d]
+  float* C;           // [M, V]
+  int32_t M, V, d;
+  int32_t mtiles, ntiles, per_xcd;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
+  __shared__ __attribute__((aligned(16))) char As[2][LM_BM * LM_ROWB];
+  // tile q: consecutive ids within one XCD take consecutive tiles, and the
+  // row tiles of a W panel are consecutive
+  const int id = blockIdx.x;
+  const int q = (id % LM_XCD) * a.per_xcd + id / LM_XCD;
+  if (q >= a.mtiles * a.ntiles) return;
+  const int nt = q / a.mtiles, mt = q - nt * a.mtiles;
+  const int m0 = mt * LM_BM, n0 = nt * LM_BN;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int d = a.d, nkb = d / LM_BK;
+
+  // staging role: thread t copies 64 bytes (k half t & 1) of hidden row t >> 1
+  const int ar = t >> 1, ah = t & 1;
+  const bool a_ok = m0 + ar < a.M;
+  const uint4* ag = reinterpret_cast<const uint4*>(a.H + (size_t)(a_ok ? m0 + ar : 0) * d + ah * 32);
+  char* const a_dst0 = As[0] + ar * LM_ROWB + ah * 64;
+  char* const a_dst1 = As[1] + ar * LM_ROWB + ah * 64;
+
+  // this lane's two W rows (one per 32-column block), k half h
+  const uint4* bg[2];
+  bool b_ok[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + 64 * w + 32 * nb + l32;
+    b_ok[nb] = n < a.V;
+    bg[nb] = reinterpret_cast<const uint4*>(a.W + (size_t)(b_ok[nb] ? n : 0) * d + h * 32);
+  }
+  // 32-row blocks of the tile holding any row below M (the same on every lane)
+  const int mblocks = min(4, (a.M - m0 + 31) / 32);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  uint4 an[4], bc[2][4], bn[2][4];
+  // k block 0
+#pragma unroll
+  for (int i = 0; i < 4; ++i) an[i] = a_ok ? ag[i] : z4;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bc[nb][s] = b_ok[nb] ? bg[nb][s] : z4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(a_dst0 + 16 * i) = an[i];
+  __syncthreads();
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      const size_t o = (size_t)(kb + 1) * (LM_BK / 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) an[i] = a_ok ? ag[o + i] : z4;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bn[nb][s] = b_ok[nb] ? bg[nb][o + s] : z4;
+    }
+    const char* Ab = As[kb & 1] + l32 * LM_ROWB + h * 64;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb < mblocks) {
+          const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + mb * 32 * LM_ROWB + 16 * s));
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(bc[nb][s]), acc[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+    if (more) {
+      char* dst = (kb & 1) ? a_dst0 : a_dst1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(dst + 16 * i) = an[i];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bc[nb][s] = bn[nb][s];
+      __syncthreads();
+    }
+  }
+
+  // lane (h, l32), accumulator r of 32 x 32 block (mb, nb) holds row
+  // 32 mb + 8 (r / 4) + 4 h + r % 4, column 32 nb + l32 of the wave's columns
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + 64 * w + 32 * nb + l32;
+    if (n >= a.V) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb >= mblocks) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < a.M) a.C[(size_t)m * a.V + n] = acc[mb][nb][r];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Shapes the caller has checked: M >= 1, V >= 1, d a positive multiple of 64,
+// H, W 16-byte aligned, the tile count within the grid limit.
+hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s) {
+  LmArgs a;
+  a.H = static_cast<const uint16_t*>(H);
+  a.W = static_cast<const uint16_t*>(W);
+  a.C = C;
+  a.M = M;
+  a.V = V;
+  a.d = d;
+  a.mtiles = (M + LM_BM - 1) / LM_BM;
+  a.ntiles = (V + LM_BN - 1) / LM_BN;
+  a.per_xcd = (a.mtiles * a.ntiles + LM_XCD - 1) / LM_XCD;
+  hipLaunchKernelGGL(lm_gemm_kernel, dim3((unsigned)(a.per_xcd * LM_XCD)), dim3(LM_WG), 0, s, a);
+  return hipGetLastError();
+}
+
+int64_t lm_gemm_tiles(int32_t M, int32_t V) {
+  return (int64_t)((M + LM_BM - 1) / LM_BM) * ((V + LM_BN - 1) / LM_BN);
+}
+
+}  // namespace sv

@@ -206,3 +206,78 @@ def compare_probs(w: Workload, d: dict, Q: np.ndarray, x: np.ndarray, dev_tok, d
             stats["max_prob_err"] = float(err)
     stats["flags"] = flags
     return stats, fails
+
+
+# ---------------------------------------------------------------------------
+# verification fed by the output projections
+# ---------------------------------------------------------------------------
+def lm_oracle_logits(d: dict, greedy: bool):
+    """The oracle's float64 logits of both heads (the draft's are still
+    formed when greedy: the drafts are its arg-max)."""
+    lt = oracle.lm_logits(d["hidden_t"], d["weight_t"], "bf16")
+    if d["hidden_d"].shape[1] == 0:
+        ld = np.zeros(lt.shape[:1] + (lt.shape[1] - 1, lt.shape[2]))
+    else:
+        ld = oracle.lm_logits(d["hidden_d"], d["weight_d"], "bf16")
+    return lt, ld
+
+
+def lm_draft_tokens(w, ld: np.ndarray, draft_u: np.ndarray) -> np.ndarray:
+    """x[b, i] ~ filtered q_i of the oracle's draft logits (greedy: arg-max)."""
+    B, K = draft_u.shape
+    x = np.zeros((B, K), dtype=np.int32)
+    if w.temperature == 0.0:
+        return np.argmax(ld, axis=-1).astype(np.int32) if K > 0 else x
+    for i in range(K):
+        x[:, i] = oracle.sample_tokens(ld[:, i], w.temperature, w.top_k, w.top_p, draft_u[:, i])
+    return x
+
+
+def run_device_lmhead(w, d: dict, x: np.ndarray, debug: bool = True):
+    import torch
+
+    from rejection_sampling_verify_09_amd import spec_verify_lmhead
+
+    greedy = w.temperature == 0.0
+    ht = to_device(d["hidden_t"], "bf16")
+    wt = to_device(d["weight_t"], "bf16")
+    hd = None if greedy else to_device(d["hidden_d"], "bf16")
+    wd = None if greedy else to_device(d["weight_d"], "bf16")
+    X = torch.from_numpy(x.astype(np.int32)).cuda()
+    U = torch.from_numpy(d["uniforms"]).cuda()
+    res = spec_verify_lmhead(ht, wt, hd, wd, X, U, w.temperature, w.top_k, w.top_p, debug=debug)
+    torch.cuda.synchronize()
+    return [v.cpu().numpy() if not isinstance(v, dict) else {k: t.cpu().numpy() for k, t in v.items()} for v in res]
+
+
+def compare_lmhead(w, d: dict, lt: np.ndarray, ld: np.ndarray, x: np.ndarray, dev_tok, dev_n, dev_dbg=None):
+    """Device outputs against the oracle's verification of its own float64
+    logits; near-ties classified per sequence as for given logits."""
+    ref_tok, ref_n, ref_dg = oracle.verify(lt, ld, x, d["uniforms"], w.temperature, w.top_k, w.top_p,
+                                           dtype=oracle.F64, diag=True)
+    stats = dict(match=0, flagged=0, fail=0, max_prob_err=0.0)
+    fails, flags = [], []
+    for b in range(w.B):
+        if dev_n[b] == ref_n[b] and np.array_equal(dev_tok[b], ref_tok[b]):
+            stats["match"] += 1
+            continue
+        v, why = oracle.classify(lt[b], ld[b], x[b], d["uniforms"][b], w.temperature, w.top_k, w.top_p, oracle.F64,
+                                 dev_tok[b], dev_n[b])
+        if v == oracle.MATCH:
+            stats["match"] += 1
+        elif v == oracle.FLAGGED:
+            stats["flagged"] += 1
+            flags.append((b, why))
+        else:
+            stats["fail"] += 1
+            fails.append((b, why))
+    if dev_dbg is not None and w.K > 0:
+        ok = ref_n >= 0
+        if ok.any():
+            err = np.abs(dev_dbg["p"][ok] - ref_dg["px"][ok]).max()
+            if w.temperature != 0.0:
+                err = max(err, np.abs(dev_dbg["q"][ok] - ref_dg["qx"][ok]).max())
+            stats["max_prob_err"] = float(err)
+    stats["flags"] = flags
+    stats["ref_dg"] = ref_dg
+    return stats, fails

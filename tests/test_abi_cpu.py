@@ -22,7 +22,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_spec_verify_dt", "sv_spec_verify_ragged",
-              "sv_spec_verify_probs",
+              "sv_spec_verify_probs", "sv_lm_logits", "sv_spec_verify_lmhead",
               "sv_filtered_probs", "sv_sample", "sv_dynk_create", "sv_dynk_observe", "sv_dynk_k", "sv_dynk_destroy",
               "sv_release", "sv_scratch_bytes",
               "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
@@ -220,3 +220,44 @@ def test_probs_validation():
     assert f(T=0.0, q=None, U=None) == L.SV_ERR_NULL
     assert f(K=0, q=None, X=None, U=None) == L.SV_ERR_NULL
     assert f(B=0, q=None, X=None, U=None, tgt=None, out_t=None, out_n=None) == L.SV_OK
+
+
+def test_lm_logits_validation():
+    f = L.lib().sv_lm_logits  # (hidden, weight, out_logits, M, V, d, stream)
+    odd = ctypes.c_void_p(0x1002)
+    assert f(FAKE, FAKE, FAKE, -1, 10, 64, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 0, 64, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 2097153, 64, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 10, 100, None) == L.SV_ERR_SHAPE     # d not a multiple of 64
+    assert f(FAKE, FAKE, FAKE, 4, 10, 0, None) == L.SV_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 10, 1 << 17, None) == L.SV_ERR_SHAPE
+    assert f(odd, FAKE, FAKE, 4, 10, 64, None) == L.SV_ERR_SHAPE       # operands must be 16-byte aligned
+    assert f(FAKE, odd, FAKE, 4, 10, 64, None) == L.SV_ERR_SHAPE
+    assert f(None, FAKE, FAKE, 4, 10, 64, None) == L.SV_ERR_NULL
+    assert f(FAKE, None, FAKE, 4, 10, 64, None) == L.SV_ERR_NULL
+    assert f(FAKE, FAKE, None, 4, 10, 64, None) == L.SV_ERR_NULL
+    assert f(None, None, None, 0, 10, 64, None) == L.SV_OK
+
+
+def test_spec_verify_lmhead_validation():
+    v = L.lib().sv_spec_verify_lmhead
+
+    def f(B=2, K=3, V=16, dt=64, dd=128, T=1.0, top_p=1.0, ht=FAKE, wt=FAKE, hd=FAKE, wd=FAKE, X=FAKE, U=FAKE,
+          out_t=FAKE, out_n=FAKE):
+        return v(ht, wt, hd, wd, X, U, T, 0, top_p, out_t, out_n, None, None, None, B, K, V, dt, dd, None)
+    assert f(B=-1) == L.SV_ERR_SHAPE
+    assert f(K=L.SV_MAX_K + 1) == L.SV_ERR_SHAPE
+    assert f(V=0) == L.SV_ERR_SHAPE
+    assert f(dt=96) == L.SV_ERR_SHAPE
+    assert f(dd=32) == L.SV_ERR_SHAPE
+    assert f(ht=ctypes.c_void_p(0x1008)) == L.SV_ERR_SHAPE
+    assert f(T=-1.0) == L.SV_ERR_PARAM
+    assert f(top_p=0.0) == L.SV_ERR_PARAM
+    assert f(ht=None) == L.SV_ERR_NULL
+    assert f(wd=None) == L.SV_ERR_NULL
+    assert f(X=None) == L.SV_ERR_NULL
+    assert f(U=None) == L.SV_ERR_NULL
+    assert f(out_n=None) == L.SV_ERR_NULL
+    # greedy needs no draft head (its width is not even checked), the rest is validated
+    assert f(T=0.0, hd=None, wd=None, dd=0, U=None) == L.SV_ERR_NULL
+    assert f(B=0) == L.SV_OK

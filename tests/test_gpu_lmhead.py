@@ -1,0 +1,164 @@
+"""GPU parity of verification fed by the output projections
+(sv_lm_logits, sv_spec_verify_lmhead) with the fp64 oracle.
+
+Grid inputs (every hidden value a multiple of 2^-3 in [-1, 1], every weight
+a multiple of 2^-6 below 4 in magnitude, d <= 8192) make every partial sum
+of the float32 accumulation an exactly representable number, so the
+device's logits must equal the oracle's float64 logits bit for bit and the
+verification is held to the bar of given logits: tokens and counts
+identical except flagged near-ties, p(x) and q(x) within 1e-6.  Plain
+bfloat16 normals are held to the worst-case float32 summation bound
+|fl(sum) - sum| <= gamma_d * sum |h_i w_ji|, gamma_d = d u / (1 - d u),
+u = 2^-24 (exact products, d - 1 rounded additions in any order)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+from synth.lmhead import LM_HEADLINE, LM_WORKLOADS, grid_hidden_weight, make_lm_inputs
+from tests.harness import (compare_lmhead, lm_draft_tokens, lm_oracle_logits, log, run_device_lmhead,
+                           to_device)
+
+pytestmark = pytest.mark.gpu
+
+PROB_TOL = 1e-6
+U32 = 2.0 ** -24
+
+
+def _gamma(d):
+    return d * U32 / (1.0 - d * U32)
+
+
+def _device_logits(Hb, Wb):
+    import torch
+
+    from rejection_sampling_verify_09_amd import lm_logits
+
+    out = lm_logits(to_device(Hb, "bf16"), to_device(Wb, "bf16"))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,V,d", [
+    (1, 1, 64),          # one row, one vocabulary entry: every tile guard
+    (9, 3001, 128),      # rows below one 32-row block, a ragged last column tile
+    (130, 5000, 192),    # a second row tile holding 2 rows, three k blocks
+    (448, 20000, 4096),  # the target's row count and width
+    (200, 128256, 256),  # the full vocabulary
+])
+def test_lm_logits_exact_on_the_grid(M, V, d):
+    g = np.random.default_rng(M * 7 + V + d)
+    Hb, Wb = grid_hidden_weight(g, M, V, d)
+    log(f"[lm_logits grid] M={M} V={V} d={d}")
+    got = _device_logits(Hb, Wb)
+    want = oracle.lm_logits(Hb, Wb, "bf16")
+    assert got.shape == (M, V)
+    bad = np.argwhere(got.astype(np.float64) != want)
+    assert bad.size == 0, f"{len(bad)} logits differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("M,V,d", [(96, 7001, 1024), (33, 1000, 4096), (5, 300, 8192)])
+def test_lm_logits_within_the_float32_bound(M, V, d):
+    g = np.random.default_rng(M + V + d)
+    Hb, Wb = grid_hidden_weight(g, M, V, d, grid=False)
+    got = _device_logits(Hb, Wb).astype(np.float64)
+    want = oracle.lm_logits(Hb, Wb, "bf16")
+    absdot = np.abs(oracle.widen(Hb, "bf16")) @ np.abs(oracle.widen(Wb, "bf16")).T
+    err = np.abs(got - want)
+    log(f"[lm_logits normal] M={M} V={V} d={d} max err {err.max():.3g} "
+        f"max err / bound {np.max(err / (_gamma(d) * absdot + 1e-300)):.3g}")
+    assert np.all(err <= _gamma(d) * absdot)
+
+
+def _check(w, d=None, max_flag=0):
+    log(f"[lmhead] {w.name} B={w.B} K={w.K} V={w.V} d={w.d_t}/{w.d_d} T={w.temperature} "
+        f"top_k={w.top_k} top_p={w.top_p} grid={w.grid}")
+    if d is None:
+        d = make_lm_inputs(w)
+    log("   inputs drawn; oracle logits")
+    lt, ld = lm_oracle_logits(d, w.temperature == 0.0)
+    x = lm_draft_tokens(w, ld, d["draft_u"])
+    log("   device")
+    tok, n, dbg = run_device_lmhead(w, d, x)
+    log("   oracle verification")
+    stats, fails = compare_lmhead(w, d, lt, ld, x, tok, n, dbg)
+    log(f"   match={stats['match']} flagged={stats['flagged']} fail={stats['fail']} "
+        f"max|dp|={stats['max_prob_err']:.2e} mean_n={np.mean(n):.3f}")
+    assert stats["fail"] == 0, fails[:5]
+    assert stats["flagged"] <= max_flag, stats["flags"][:5]
+    return tok, n, dbg, stats, lt, ld, x
+
+
+@pytest.mark.parametrize("name", [
+    "lm-b3-k2-v3001-d128-dd64-t0.8-topp0.95",
+    "lm-b8-k5-v32000-d1024-dd512-t1.0",
+    "lm-b16-k4-v50001-d512-dd256-topk50",
+])
+def test_lmhead_parity_grid(name):
+    w = LM_WORKLOADS[name]
+    _, _, _, stats, _, _, _ = _check(w)
+    assert stats["max_prob_err"] <= PROB_TOL
+
+
+def test_lmhead_parity_plain_normals():
+    """Plain bfloat16 normals: decisions may move only where the float32
+    logits' rounding could move them (flagged near-ties), and p(x), q(x)
+    stay within the bound the logit error implies:
+    |dp| <= p (exp(2 delta / T) - 1), delta the row's worst logit bound."""
+    w = LM_WORKLOADS["lm-b8-k5-v32000-d1024-dd512-t1.0-normal"]
+    d = make_lm_inputs(w)
+    tok, n, dbg, stats, lt, ld, x = _check(w, d, max_flag=1)
+    ht = oracle.widen(d["hidden_t"], "bf16")
+    hd = oracle.widen(d["hidden_d"], "bf16")
+    bt = _gamma(w.d_t) * (np.abs(ht) @ np.abs(oracle.widen(d["weight_t"], "bf16")).T).max(axis=-1)[:, :w.K]
+    bd = _gamma(w.d_d) * (np.abs(hd) @ np.abs(oracle.widen(d["weight_d"], "bf16")).T).max(axis=-1)
+    ref = stats["ref_dg"]
+    tp = ref["px"] * (np.exp(2 * bt / w.temperature) - 1.0)
+    tq = ref["qx"] * (np.exp(2 * bd / w.temperature) - 1.0)
+    log(f"   max |dp| / bound {np.max(np.abs(dbg['p'] - ref['px']) / tp):.3g}")
+    assert np.all(np.abs(dbg["p"] - ref["px"]) <= tp)
+    assert np.all(np.abs(dbg["q"] - ref["qx"]) <= tq)
+
+
+@pytest.mark.timeout(900)
+def test_lmhead_headline_parity():
+    """B=64, K=6, V=128256, target width 4096, draft width 2048, T=0.7,
+    top_p 0.9: the shape the streaming path is measured on, fed by its
+    projections."""
+    _, _, _, stats, _, _, _ = _check(LM_HEADLINE)
+    assert stats["max_prob_err"] <= PROB_TOL
+
+
+@pytest.mark.timeout(900)
+def test_lmhead_greedy_full_vocabulary():
+    """Temperature 0: the draft head is not needed (no draft arguments)."""
+    _check(LM_WORKLOADS["lm-b32-k6-v128256-d4096-dd2048-greedy"])
+
+
+def test_lmhead_no_drafts():
+    """K = 0: each sequence draws its bonus token from the target head."""
+    w = replace(LM_WORKLOADS["lm-b3-k2-v3001-d128-dd64-t0.8-topp0.95"], name="lm-b5-k0-v3001", B=5, K=0, seed=31)
+    tok, n, _, _, _, _, _ = _check(w)
+    assert np.all(n == 0)
+
+
+def test_lmhead_equals_logits_then_verify():
+    """The fused entry point equals the projection entry point followed by
+    verification of its float32 logits (the same kernels, the same bits)."""
+    import torch
+
+    from rejection_sampling_verify_09_amd import lm_logits, spec_verify
+
+    w = LM_WORKLOADS["lm-b8-k5-v32000-d1024-dd512-t1.0-normal"]
+    d = make_lm_inputs(w)
+    lt, ld = lm_oracle_logits(d, False)
+    x = lm_draft_tokens(w, ld, d["draft_u"])
+    tok, n, dbg = run_device_lmhead(w, d, x)
+    gt = lm_logits(to_device(d["hidden_t"], "bf16"), to_device(d["weight_t"], "bf16"))
+    gd = lm_logits(to_device(d["hidden_d"], "bf16"), to_device(d["weight_d"], "bf16"))
+    t2, n2, dbg2 = spec_verify(gt, gd, torch.from_numpy(x).cuda(), torch.from_numpy(d["uniforms"]).cuda(),
+                               w.temperature, w.top_k, w.top_p, debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(tok, t2.cpu().numpy()) and np.array_equal(n, n2.cpu().numpy())
+    assert np.array_equal(dbg["p"], dbg2["p"].cpu().numpy()) and np.array_equal(dbg["q"], dbg2["q"].cpu().numpy())
