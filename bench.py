@@ -5,6 +5,7 @@
     python bench.py --draft-temperature TD [--steps K] [--warmup W] [--workload NAME]
     python bench.py --ragged K_LO K_HI [--steps K] [--warmup W] [--workload NAME]
     python bench.py --draft-probs [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --lmhead [--steps K] [--warmup W] [--workload NAME]
 
 One step = one sv_spec_verify call (the whole hot path: streaming pass,
 filter thresholds, accept tests, first-rejection scan, final draw) over one
@@ -24,6 +25,11 @@ With --sampler, one step is one sv_sample call (the drafting draw: x ~ q and
 q(x)) over the workload's B*K draft rows, with their draft uniforms.  With
 --draft-temperature, the drafts are drawn on the GPU (sv_sample) at that
 temperature before timing, and one step is one sv_spec_verify_dt call.
+
+With --lmhead, one step is one sv_spec_verify_lmhead call: the target's and
+the draft's output projections (bf16 hidden states times bf16 weights on the
+matrix cores) and the verification of their float32 logits; its roofline is
+the projection kernel against the bf16 matrix peak.
 
 The CPU-baseline leg times the fp64 oracle (test infrastructure) on a bounded
 sample of the same workload; it is a reported baseline, not the target.
@@ -45,11 +51,13 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_09_amd", "csrc", f)
                   for f in ("sv_common.hpp", "sv_kernels.hip")]
+LM_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_09_amd", "csrc", "sv_lmhead.hip")]
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -64,19 +72,20 @@ def load_draft_tokens(name: str, B: int, K: int):
     return x
 
 
-def measured_traffic(key: str):
-    """HBM bytes per launch of the streaming kernel from the committed counter
-    summary for ``key`` (the workload name, "sample-" + name for the draft
-    draw, "ragged-LO-HI-" + name for a ragged batch, "probs-" + name for q
-    given as probabilities), or None when the summary
-    is absent or predates the kernel source."""
-    path = os.path.join(PROFILES, f"traffic_stream_kernel_{key}.md")
+def measured_traffic(key: str, kernel: str = "stream_kernel", sources=None):
+    """HBM bytes per launch of ``kernel`` (the streaming kernel unless named)
+    from the committed counter summary for ``key`` (the workload name,
+    "sample-" + name for the draft draw, "ragged-LO-HI-" + name for a ragged
+    batch, "probs-" + name for q given as probabilities, the projection
+    workload's name for lm_gemm_kernel), or None when the summary is absent
+    or predates the kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{key}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(sources):
         return None
     return float(m_bytes.group(1))
 
@@ -414,6 +423,119 @@ def run_probs(args, w):
     print(json.dumps(result), flush=True)
 
 
+def run_lmhead(args):
+    """Verification fed by the output projections (sv_spec_verify_lmhead):
+    the target's B(K+1) hidden states times its projection, the draft's BK
+    times its own, then verification.  The drafts are drawn on the GPU
+    (sv_lm_logits of the draft rows, then sv_sample) before timing.  The two
+    projections (two launches of lm_gemm_kernel) are the dominant work; the
+    weights (more than the 256 MB last-level cache) are read from HBM at
+    every step."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_09_amd import lm_logits, profile_start, profile_stop, sample, spec_verify_lmhead
+    from synth.lmhead import LM_HEADLINE, LM_WORKLOADS, make_lm_inputs
+
+    w = LM_WORKLOADS[args.workload] if args.workload else LM_HEADLINE
+    d = make_lm_inputs(w)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    ht, wt, hd, wd = dev(d["hidden_t"]), dev(d["weight_t"]), dev(d["hidden_d"]), dev(d["weight_d"])
+    ud = torch.from_numpy(d["draft_u"].reshape(-1).astype(np.float32)).cuda()
+    if w.K > 0:
+        ql = lm_logits(hd.reshape(w.B * w.K, w.d_d), wd)
+        xt, _ = sample(ql, ud, w.temperature, w.top_k, w.top_p, with_prob=False)
+        X = xt.reshape(w.B, w.K).contiguous()
+        del ql
+    else:
+        X = torch.empty((w.B, 0), dtype=torch.int32, device="cuda")
+    U = torch.from_numpy(d["uniforms"]).cuda()
+    greedy = w.temperature == 0.0
+    mt, md = w.B * (w.K + 1), (0 if greedy else w.B * w.K)
+    flops = 2.0 * (mt * w.V * w.d_t + md * w.V * w.d_d)
+    w_bytes = 2 * w.V * (w.d_t + (0 if greedy else w.d_d))
+    stream = torch.cuda.current_stream()
+    out = [None, None]
+
+    def step(i):
+        out[0], out[1] = spec_verify_lmhead(ht, wt, None if greedy else hd, None if greedy else wd, X, U,
+                                            w.temperature, w.top_k, w.top_p)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    profile_start()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = profile_stop()
+    gemm_ms = prof["stream_kernel_ms"] / max(1, prof["calls"])
+    other_ms = prof["other_kernels_ms"] / max(1, prof["calls"])
+    n_host = out[1].cpu().numpy()
+    emitted = int(np.sum(n_host[n_host >= 0] + 1))
+    achieved = flops / (gemm_ms / 1e3) / 1e12
+    result = {
+        "metric": f"spec-verify sequences/s at B={w.B} K={w.K} V={w.V}, logits from bf16 projections "
+                  f"(d={w.d_t}, draft d={w.d_d})",
+        "value": w.B / (ms_per_step / 1e3),
+        "unit": "sequences/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded hidden states and projection weights of the workload's shape; no model weights)",
+        "config": {"workload": w.name, "B": w.B, "K": w.K, "V": w.V, "d_target": w.d_t, "d_draft": w.d_d,
+                   "temperature": w.temperature, "top_k": w.top_k, "top_p": w.top_p,
+                   "projection_flops_per_step": flops, "weight_bytes_per_step": w_bytes},
+        "tokens_per_s": emitted / (ms_per_step / 1e3),
+        "mean_emitted_per_sequence": emitted / w.B,
+        "roofline": {
+            "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK_TFS,
+            "traffic": measured_traffic(w.name, "lm_gemm_kernel", LM_SOURCES),
+            "kernel": "lm_gemm_kernel (target and draft launches together)", "kernel_ms": gemm_ms,
+            "other_kernels_ms": other_ms, "timed_calls": prof["calls"],
+            "weight_read_GBs": w_bytes / (gemm_ms / 1e3) / 1e9,
+        },
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        import oracle
+
+        nb = min(4, w.B)
+        t0 = time.perf_counter()
+        n_done = 0
+        with threadpool_limits(limits=1):
+            while True:
+                oracle.verify_lmhead(d["hidden_t"][:nb], d["weight_t"], d["hidden_d"][:nb], d["weight_d"],
+                                     X[:nb].cpu().numpy(), d["uniforms"][:nb], w.temperature, w.top_k, w.top_p,
+                                     dtype="bf16")
+                n_done += nb
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        result["cpu_baseline"] = dict(value=n_done / el, unit="sequences/s", cores=1, kind="oracle",
+                                      sample=f"{n_done // nb} x {nb} sequences of {w.name} (projections in "
+                                             f"float64 and verification), NumPy, one BLAS thread, {el:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -434,6 +556,8 @@ def main():
     ap.add_argument("--ragged", type=int, nargs=2, metavar=("K_LO", "K_HI"), default=None,
                     help="verify a batch whose sequences draft K_b ~ uniform[K_LO, K_HI] tokens "
                          "(sv_spec_verify_ragged)")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="verification fed by the output projections (sv_spec_verify_lmhead)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -465,6 +589,9 @@ def main():
 
     from rejection_sampling_verify_09_amd import profile_start, profile_stop, sample, spec_verify
 
+    if args.lmhead:
+        run_lmhead(args)
+        return
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
     if args.ragged:

@@ -366,6 +366,7 @@ __device__ void sort_keys_desc(int n, Smem& sm) {
 // for top-p also a finite normaliser rr.S).
 template <int DT, int MODE, int BS>
 __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRec& rr, Smem& sm) {
+  static_assert(ROW_CAND % BS == 0 && ROW_CAND <= 4 * BS, "top-p scan holds ROW_CAND / BS entries per thread");
   const int t = threadIdx.x, nch = a.nchunks;
   const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
   const RowT rt = row_temp(a, rl);
@@ -389,11 +390,11 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
   bool fb = ncand_total > ROW_LOAD_MAX;
 
   if (!fb) {
-    // Candidates at or above lo, read in batches of LOAD_BATCH loads per
-    // thread: top-p gathers them straight into sm.r.keys (at most KEEP_CAP),
-    // top-k into sm.r.cand (at most ROW_CAND) for the radix select.
-    uint64_t* dstv = (MODE == M_TOPP) ? sm.r.keys : sm.r.cand;
-    const int cap = (MODE == M_TOPP) ? KEEP_CAP : ROW_CAND;
+    // Candidates at or above lo (at most ROW_CAND), read in batches of
+    // LOAD_BATCH loads per thread into sm.r.cand: for the radix select of
+    // top-k, for the sort of top-p.
+    uint64_t* dstv = sm.r.cand;
+    constexpr int cap = ROW_CAND;
     if (t == 0) sm.ncand = 0;
     __syncthreads();
     for (int base = 0; base < ncand_total; base += BS * LOAD_BATCH) {
@@ -475,17 +476,35 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
           fb = true;  // top-p over a top-k set too large for LDS
         }
       }
-    } else {  // M_TOPP
-      sort_keys_desc<BS>(cnt, sm);
+    } else {  // M_TOPP: every candidate, sorted descending in sm.r.cand
+      const int np2 = pow2_at_least(cnt < 2 ? 2 : cnt);
+      __syncthreads();
+      for (int e = cnt + t; e < np2; e += BS) sm.r.cand[e] = 0;
+      bitonic_desc<BS>(sm.r.cand, np2);
       ns = cnt;
     }
     if (!fb && (MODE == M_TOPP || MODE == M_TOPKP)) {
-      // smallest descending prefix whose mass reaches top_p, ties included
-      const uint32_t key = t < ns ? (uint32_t)(sm.r.keys[t] >> 32) : 0u;
-      const double w = t < ns ? exp(((double)key_val(key) - (double)m) * invT) / snorm : 0.0;
+      // smallest descending prefix whose mass reaches top_p, ties included;
+      // thread t holds sorted entries PT t .. PT t + PT - 1
+      constexpr int PT = ROW_CAND / BS;
+      const uint64_t* srt = MODE == M_TOPP ? sm.r.cand : sm.r.keys;
+      uint32_t kv[PT];
+      double wv[PT], ls = 0.0;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int e = t * PT + i;
+        kv[i] = e < ns ? (uint32_t)(srt[e] >> 32) : 0u;
+        wv[i] = e < ns ? exp(((double)key_val(kv[i]) - (double)m) * invT) / snorm : 0.0;
+        ls += wv[i];
+      }
       double tot;
-      const double C = block_incl_scan<BS / 64>(w, sm.red, &tot);
-      int first = (t < ns && C >= a.top_p) ? t : INT_MAX;
+      double C = block_incl_scan<BS / 64>(ls, sm.red, &tot) - ls;
+      int first = INT_MAX;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        C += wv[i];
+        if (t * PT + i < ns && C >= a.top_p && first == INT_MAX) first = t * PT + i;
+      }
       first = block_min_i<BS / 64>(first, sm.red);
       if (first == INT_MAX) {
         if (MODE == M_TOPP) fb = true;  // the nucleus reaches below the candidate window
@@ -494,9 +513,27 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
       if (!fb) {
         if (first < 0) first = 0;
         __syncthreads();
-        const uint32_t tp = (uint32_t)(sm.r.keys[first] >> 32);
+        const uint32_t tp = (uint32_t)(srt[first] >> 32);
         tau = tp > tau ? tp : tau;
-        nk = block_sum_i<BS / 64>((t < ns && key >= tau) ? 1 : 0, sm.red);
+        int c = 0;
+        double sk = 0.0;
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+          const bool kept = t * PT + i < ns && kv[i] >= tau;
+          c += kept ? 1 : 0;
+          sk += kept ? wv[i] : 0.0;
+        }
+        nk = block_sum_i<BS / 64>(c, sm.red);
+        if (MODE == M_TOPP) {
+          // the kept entries lead the sorted candidates
+          if (nk <= KEEP_CAP) {
+            __syncthreads();
+            for (int e = t; e < nk; e += BS) sm.r.keys[e] = sm.r.cand[e];
+          } else {
+            big = true;
+            skept = block_sum<BS / 64>(sk, sm.red) * snorm;
+          }
+        }
       }
     }
   }

@@ -8,16 +8,18 @@
 //
 // Tiling (gfx950, v_mfma_f32_32x32x16_bf16, 64-wide waves):
 //  * a workgroup (4 waves) owns a 128-row x 256-column tile of the output;
-//    wave w owns columns [64w, 64w + 64) of it for all 128 rows: 4 x 2 tiles
+//    wave w owns columns [64w, 64w + 64) of it for all 128 rows: 4 x 2 blocks
 //    of 32 x 32, 128 float32 accumulators per lane;
-//  * the W operand of a wave is its own: each lane reads 64 contiguous bytes
-//    (32 values of k) of one W row per 64-wide k block straight into
-//    registers, one k block ahead of the matrix instructions;
-//  * the hidden operand is shared by the 4 waves: the workgroup stages each
-//    128 x 64 k block of it in LDS (double-buffered, one barrier per block);
-//  * within a k block the sum over k is taken in a fixed permuted order that
-//    both operands follow: lane half h of step s holds k = 32h + 8s + 0..7,
-//    so every lane's operand bytes are contiguous in memory and in LDS;
+//  * both operands are staged in LDS in k blocks of 32 (128 hidden rows and
+//    256 W rows of 64 bytes, rows padded to 80 bytes so that the fragment
+//    reads of 16 consecutive rows fall in distinct banks), double-buffered
+//    with one barrier per block; the global loads are whole 64-byte row
+//    segments, four lanes per row, issued one block ahead;
+//  * 61,440 bytes of LDS and at most 256 registers per lane keep two
+//    workgroups (8 waves) on each compute unit, so one computes while the
+//    other waits on its loads;
+//  * lane half h of step s holds k = 16h + 8s + 0..7 of the block for both
+//    operands (an order of the sum over k that both follow);
 //  * the 128-row tiles of one 256-column W panel are consecutive tile ids
 //    placed on one XCD (workgroup ids go round-robin over the 8 XCDs), so the
 //    panel is read from HBM once and served to the other row tiles by that
@@ -36,10 +38,10 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int LM_BM = 128;      // rows of hidden per tile
 constexpr int LM_BN = 256;      // vocabulary entries per tile
-constexpr int LM_BK = 64;       // k per staged block
+constexpr int LM_BK = 32;       // k per staged block
 constexpr int LM_WG = 256;      // threads (4 waves)
 constexpr int LM_XCD = 8;       // XCDs the workgroup ids are dealt over
-constexpr int LM_ROWB = 144;    // LDS bytes per staged hidden row: 128 of data, 16 of padding
+constexpr int LM_ROWB = 80;     // LDS bytes per staged row: 64 of data, 16 of padding
 
 struct LmArgs {
   const uint16_t* H;  // [M, d] bfloat16 bit patterns
@@ -53,6 +55,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_b
 
 __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
   __shared__ __attribute__((aligned(16))) char As[2][LM_BM * LM_ROWB];
+  __shared__ __attribute__((aligned(16))) char Ws[2][LM_BN * LM_ROWB];
   // tile q: consecutive ids within one XCD take consecutive tiles, and the
   // row tiles of a W panel are consecutive
   const int id = blockIdx.x;
@@ -64,24 +67,45 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
   const int h = lane >> 5, l32 = lane & 31;
   const int d = a.d, nkb = d / LM_BK;
 
-  // staging role: thread t copies 64 bytes (k half t & 1) of hidden row t >> 1
-  const int ar = t >> 1, ah = t & 1;
-  const bool a_ok = m0 + ar < a.M;
-  const uint4* ag = reinterpret_cast<const uint4*>(a.H + (size_t)(a_ok ? m0 + ar : 0) * d + ah * 32);
-  char* const a_dst0 = As[0] + ar * LM_ROWB + ah * 64;
-  char* const a_dst1 = As[1] + ar * LM_ROWB + ah * 64;
-
-  // this lane's two W rows (one per 32-column block), k half h
-  const uint4* bg[2];
-  bool b_ok[2];
+  // staging role: thread t copies 16-byte chunk t % 4 of rows 64 i + t / 4
+  // (hidden rows i < 2, W rows i < 4); rows past M or V read row 0 (a valid
+  // address) and are zeroed in registers
+  const int sr = t >> 2, sc = t & 3;
+  const uint4* ap[2];
+  const uint4* wp[4];
+  bool aok[2], wok[4];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + 64 * w + 32 * nb + l32;
-    b_ok[nb] = n < a.V;
-    bg[nb] = reinterpret_cast<const uint4*>(a.W + (size_t)(b_ok[nb] ? n : 0) * d + h * 32);
+  for (int i = 0; i < 2; ++i) {
+    const int r = 64 * i + sr;
+    aok[i] = m0 + r < a.M;
+    ap[i] = reinterpret_cast<const uint4*>(a.H + (size_t)(aok[i] ? m0 + r : 0) * d) + sc;
   }
-  // 32-row blocks of the tile holding any row below M (the same on every lane)
-  const int mblocks = min(4, (a.M - m0 + 31) / 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * i + sr;
+    wok[i] = n0 + r < a.V;
+    wp[i] = reinterpret_cast<const uint4*>(a.W + (size_t)(wok[i] ? n0 + r : 0) * d) + sc;
+  }
+  uint4 ra[2], rw[4];
+  auto gload = [&](int kb) {
+    const size_t o = (size_t)kb * (LM_BK / 8);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 v = ap[i][o];
+      ra[i] = aok[i] ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = wp[i][o];
+      rw[i] = wok[i] ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(As[buf] + (64 * i + sr) * LM_ROWB + 16 * sc) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(Ws[buf] + (64 * i + sr) * LM_ROWB + 16 * sc) = rw[i];
+  };
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -91,57 +115,37 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-  uint4 an[4], bc[2][4], bn[2][4];
-  // k block 0
-#pragma unroll
-  for (int i = 0; i < 4; ++i) an[i] = a_ok ? ag[i] : z4;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) bc[nb][s] = b_ok[nb] ? bg[nb][s] : z4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(a_dst0 + 16 * i) = an[i];
+  gload(0);
+  lstore(0);
   __syncthreads();
-
   for (int kb = 0; kb < nkb; ++kb) {
     const bool more = kb + 1 < nkb;
-    if (more) {
-      const size_t o = (size_t)(kb + 1) * (LM_BK / 8);
+    if (more) gload(kb + 1);
+    const int buf = kb & 1;
+    const char* Ab = As[buf] + l32 * LM_ROWB + h * 32;
+    const char* Bb = Ws[buf] + (64 * w + l32) * LM_ROWB + h * 32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) an[i] = a_ok ? ag[o + i] : z4;
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 bf[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bn[nb][s] = b_ok[nb] ? bg[nb][o + s] : z4;
-    }
-    const char* Ab = As[kb & 1] + l32 * LM_ROWB + h * 64;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int nb = 0; nb < 2; ++nb) bf[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(Bb + nb * 32 * LM_ROWB + 16 * s));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        if (mb < mblocks) {
-          const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + mb * 32 * LM_ROWB + 16 * s));
+        const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + mb * 32 * LM_ROWB + 16 * s));
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(bc[nb][s]), acc[mb][nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[nb], acc[mb][nb], 0, 0, 0);
       }
     }
     if (more) {
-      char* dst = (kb & 1) ? a_dst0 : a_dst1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(dst + 16 * i) = an[i];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bc[nb][s] = bn[nb][s];
+      lstore(buf ^ 1);
       __syncthreads();
     }
   }
 
   // lane (h, l32), accumulator r of 32 x 32 block (mb, nb) holds row
   // 32 mb + 8 (r / 4) + 4 h + r % 4, column 32 nb + l32 of the wave's columns
+  const int mblocks = min(4, (a.M - m0 + 31) / 32);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = n0 + 64 * w + 32 * nb + l32;
@@ -160,7 +164,7 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
 
 }  // namespace
 
-// Shapes the caller has checked: M >= 1, V >= 1, d a positive multiple of 64,
+// Shapes the caller has checked: M >= 1, V >= 1, d a positive multiple of 64 (the k block is 32),
 // H, W 16-byte aligned, the tile count within the grid limit.
 hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s) {
   LmArgs a;
