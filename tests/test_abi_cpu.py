@@ -261,3 +261,23 @@ def test_spec_verify_lmhead_validation():
     # greedy needs no draft head (its width is not even checked), the rest is validated
     assert f(T=0.0, hd=None, wd=None, dd=0, U=None) == L.SV_ERR_NULL
     assert f(B=0) == L.SV_OK
+
+
+def test_lm_bindings_check_their_arguments_before_any_call():
+    import torch
+
+    from rejection_sampling_verify_09_amd import lm_logits, spec_verify_lmhead
+
+    h = torch.zeros((2, 64), dtype=torch.bfloat16)
+    w = torch.zeros((10, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        lm_logits(h.float(), w)
+    with pytest.raises(ValueError):
+        lm_logits(h, torch.zeros((10, 128), dtype=torch.bfloat16))
+    x = torch.zeros((1, 2), dtype=torch.int32)
+    u = torch.zeros((1, 3))
+    with pytest.raises(ValueError):  # a draft head is needed at T > 0
+        spec_verify_lmhead(torch.zeros((1, 3, 64), dtype=torch.bfloat16), w, None, None, x, u, 1.0)
+    with pytest.raises(ValueError):  # draft rows of the wrong count
+        spec_verify_lmhead(torch.zeros((1, 3, 64), dtype=torch.bfloat16), w,
+                           torch.zeros((1, 3, 64), dtype=torch.bfloat16), w, x, u, 1.0)

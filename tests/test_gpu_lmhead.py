@@ -46,6 +46,7 @@ def _device_logits(Hb, Wb):
     (130, 5000, 192),    # a second row tile holding 2 rows, three k blocks
     (448, 20000, 4096),  # the target's row count and width
     (200, 128256, 256),  # the full vocabulary
+    (257, 4099, 8192),   # three row tiles, V not a multiple of 4, the widest exact grid
 ])
 def test_lm_logits_exact_on_the_grid(M, V, d):
     g = np.random.default_rng(M * 7 + V + d)
