@@ -115,6 +115,9 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
+  // a tile with at most 64 rows below M (the last one of M = 448, for one)
+  // skips the matrix instructions of its empty lower half
+  const bool full = a.M - m0 > 64;
   gload(0);
   lstore(0);
   __syncthreads();
@@ -131,10 +134,12 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
       for (int nb = 0; nb < 2; ++nb) bf[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(Bb + nb * 32 * LM_ROWB + 16 * s));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + mb * 32 * LM_ROWB + 16 * s));
+        if (mb < 2 || full) {
+          const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + mb * 32 * LM_ROWB + 16 * s));
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[nb], acc[mb][nb], 0, 0, 0);
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[nb], acc[mb][nb], 0, 0, 0);
+        }
       }
     }
     if (more) {
