@@ -74,6 +74,7 @@ _lw("lm-b8-k5-v32000-d1024-dd512-t1.0-normal", 8, 5, 32000, 1024, 512, 1.0, 0, 1
 _lw("lm-b16-k4-v50001-d512-dd256-topk50", 16, 4, 50001, 512, 256, 1.0, 50, 1.0, 24, shared=128)
 _lw("lm-b32-k6-v128256-d4096-dd2048-greedy", 32, 6, 128256, 4096, 2048, 0.0, 0, 1.0, 25)
 _lw("lm-b3-k2-v3001-d128-dd64-t0.8-topp0.95", 3, 2, 3001, 128, 64, 0.8, 0, 0.95, 26, shared=32)
+_lw("lm-b12-k3-v20000-d256-dd128-t0.9-topk40-topp0.8", 12, 3, 20000, 256, 128, 0.9, 40, 0.8, 27, shared=64)
 
 
 def _q(x: np.ndarray, scale: float, lim: int) -> np.ndarray:

@@ -95,6 +95,7 @@ def _check(w, d=None, max_flag=0):
     "lm-b3-k2-v3001-d128-dd64-t0.8-topp0.95",
     "lm-b8-k5-v32000-d1024-dd512-t1.0",
     "lm-b16-k4-v50001-d512-dd256-topk50",
+    "lm-b12-k3-v20000-d256-dd128-t0.9-topk40-topp0.8",
 ])
 def test_lmhead_parity_grid(name):
     w = LM_WORKLOADS[name]
