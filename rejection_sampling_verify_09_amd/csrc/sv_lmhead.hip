@@ -26,6 +26,7 @@
 //    XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 
@@ -167,11 +168,143 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
   }
 }
 
+// The wide tile: 256 rows x 256 columns per workgroup of 8 waves (2 x 4,
+// each wave 128 x 64 as in lm_gemm_kernel), k blocks of 64 (whole 128-byte
+// lines of each operand row per load), both operands in LDS as 128-byte
+// rows whose 16-byte chunks are XOR-swizzled by row (so the fragment reads
+// of 16 consecutive rows hit distinct banks without padding), two stages:
+// 128 KB of LDS, one workgroup per CU.  Per flop it moves half the operand
+// bytes of the 128-row tile from L2; it pays when the rows fill 256-row
+// tiles about as well as 128-row ones (M = 448, not M = 384).
+__device__ __forceinline__ int sw64(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }  // byte of chunk c, row r
+__global__ void __launch_bounds__(512, 1) lm_gemm_w8k64(LmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* As = smem;                    // [2][256 * 128]
+  char* Ws = smem + 2 * 256 * 128;    // [2][256 * 128]
+  const int id = blockIdx.x;
+  const int q = (id % LM_XCD) * a.per_xcd + id / LM_XCD;
+  if (q >= a.mtiles * a.ntiles) return;
+  const int nt = q / a.mtiles, mt = q - nt * a.mtiles;
+  const int m0 = mt * 256, n0 = nt * 256;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 2, wn = w & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int d = a.d, nkb = d / 64;
+  // staging role: 16-byte chunk t % 8 of rows 64 i + t / 8 (i < 4) of both operands;
+  // rows past M or V read row 0 (a valid address) and are zeroed in registers
+  const int sr = t >> 3, sc = t & 7;
+  const uint4* ap[4]; const uint4* wp[4]; bool aok[4], wok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * i + sr;
+    aok[i] = m0 + r < a.M; ap[i] = reinterpret_cast<const uint4*>(a.H + (size_t)(aok[i] ? m0 + r : 0) * d) + sc;
+    wok[i] = n0 + r < a.V; wp[i] = reinterpret_cast<const uint4*>(a.W + (size_t)(wok[i] ? n0 + r : 0) * d) + sc;
+  }
+  uint4 ra[4], rw[4];
+  auto gload = [&](int kb) {
+    const size_t o = (size_t)kb * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = ap[i][o]; ra[i] = aok[i] ? v : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 u = wp[i][o]; rw[i] = wok[i] ? u : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(As + buf * 256 * 128 + sw64(64 * i + sr, sc)) = ra[i];
+      *reinterpret_cast<uint4*>(Ws + buf * 256 * 128 + sw64(64 * i + sr, sc)) = rw[i];
+    }
+  };
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+  // this wave's first row; a wave whose rows all lie past M, or whose lower
+  // 64 rows do, skips those matrix instructions
+  const int wrow0 = m0 + 128 * wm;
+  const bool full = a.M - wrow0 > 64;
+  const bool any = a.M > wrow0;
+  gload(0); lstore(0); __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool more = kb + 1 < nkb;
+    if (more) gload(kb + 1);
+    const char* Ab = As + (kb & 1) * 256 * 128;
+    const char* Bb = Ws + (kb & 1) * 256 * 128;
+    if (any) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // lane half h of step s holds chunk c: k = 8c .. 8c + 7 of the block
+        const int c = 2 * h + (s & 1) + 4 * (s >> 1);
+        bf16x8 bf[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bf[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(Bb + sw64(64 * wn + 32 * nb + l32, c)));
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          if (mb < 2 || full) {
+            const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + sw64(128 * wm + 32 * mb + l32, c)));
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[nb], acc[mb][nb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (more) { lstore((kb & 1) ^ 1); __syncthreads(); }
+  }
+  const int mblocks = any ? min(4, (a.M - wrow0 + 31) / 32) : 0;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + 64 * wn + 32 * nb + l32;
+    if (n >= a.V) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb >= mblocks) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wrow0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < a.M) a.C[(size_t)m * a.V + n] = acc[mb][nb][r];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // Shapes the caller has checked: M >= 1, V >= 1, d a positive multiple of 64 (the k block is 32),
 // H, W 16-byte aligned, the tile count within the grid limit.
 hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s) {
+  // the wide tile when 256-row tiles waste no more rows than 128-row ones
+  // (plus 5%): M = 448 takes it, M = 384 does not
+  const double w256 = 1.0 - (double)M / (256.0 * ((M + 255) / 256));
+  const double w128 = 1.0 - (double)M / (128.0 * ((M + 127) / 128));
+  if (d % 64 == 0 && w256 <= w128 + 0.05) {
+    LmArgs a;
+    a.H = static_cast<const uint16_t*>(H);
+    a.W = static_cast<const uint16_t*>(W);
+    a.C = C;
+    a.M = M;
+    a.V = V;
+    a.d = d;
+    a.mtiles = (M + 255) / 256;
+    a.ntiles = (V + 255) / 256;
+    a.per_xcd = (a.mtiles * a.ntiles + LM_XCD - 1) / LM_XCD;
+    // 128 KB of dynamic LDS needs the kernel's limit raised, once per device
+    // (setting it twice from racing first calls is harmless)
+    static std::atomic<bool> attr_set[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
+      const hipError_t e =
+          hipFuncSetAttribute((const void*)lm_gemm_w8k64, hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 256 * 128);
+      if (e != hipSuccess) return e;
+      attr_set[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(lm_gemm_w8k64, dim3((unsigned)(a.per_xcd * LM_XCD)), dim3(512), 4 * 256 * 128, s, a);
+    return hipGetLastError();
+  }
   LmArgs a;
   a.H = static_cast<const uint16_t*>(H);
   a.W = static_cast<const uint16_t*>(W);
