@@ -55,6 +55,8 @@ __all__ = [
     "sample_tokens",
     "sample",
     "verify",
+    "verify_given",
+    "decide",
     "verify_ragged",
     "ragged_offsets_ok",
     "verify_one",
@@ -161,9 +163,15 @@ def filtered_probs(logits: np.ndarray, temperature: float, top_k: int, top_p: fl
         desc = -np.sort(-pi, axis=1)
         mass = np.cumsum(desc, axis=1)
         reach = mass >= tp
-        # first prefix length whose mass reaches top_p (the whole row if
-        # round-off keeps the total just below top_p)
-        nstar = np.where(reach.any(axis=1), np.argmax(reach, axis=1), V - 1)
+        # Some prefix always reaches top_p: the total mass is 1 up to
+        # round-off, less than 2 V 2^-53 below it (the quotients e_j / sum e
+        # and the two sums each lose at most V 2^-53), while a float32 top_p
+        # below 1 is at most 1 - 2^-24; so for any V below 2^28 the whole row
+        # reaches it.  The check makes a violation loud instead of silent.
+        if not reach[:, -1].all():
+            raise AssertionError("cumulative mass below top_p: round-off beyond its bound")
+        # first prefix length whose mass reaches top_p
+        nstar = np.argmax(reach, axis=1)
         tau = desc[rows, nstar]
         keep &= pi >= tau[:, None]
 
@@ -295,6 +303,84 @@ def _given_draft_probs(q, dtype_ok=(np.float32, np.float64)):
     return q
 
 
+def decide(P: np.ndarray, Q: np.ndarray, x: np.ndarray, uniforms: np.ndarray):
+    """The accept tests, the first rejection and the final draw (A4..A7) for
+    sequences whose filtered distributions are already formed.
+
+    P [nb, K+1, V] and Q [nb, K, V]: float64 probabilities (a row of NaN has
+    no distribution); x [nb, K] drafted tokens; uniforms [nb, K+1] float32.
+    Returns (tokens [nb, K+1], n [nb], px [nb, K], qx [nb, K], Z [nb]) with
+    the sentinel rows (n = -1, tokens -1, Z NaN) of bad sequences: a row with
+    no distribution, or a drafted token outside [0, V).
+    """
+    nb, K1, V = P.shape
+    K = K1 - 1
+    x = np.asarray(x).astype(np.int64)
+    u = np.asarray(uniforms).astype(np.float64)
+    # bad sequences: a row with no distribution, or a drafted token out of range
+    bad = np.isnan(P).any(axis=(1, 2))
+    if K > 0:
+        bad |= np.isnan(Q).any(axis=(1, 2))
+    bad |= ((x < 0) | (x >= V)).any(axis=1)
+    xs = np.clip(x, 0, V - 1)
+    ii = np.arange(nb)[:, None]
+    kk = np.arange(K)[None, :]
+    px = P[ii, kk, xs]
+    qx = Q[ii, kk, xs]
+    # accept test at each position
+    acc = u[:, :K] * qx < px
+    # first rejection
+    n = np.where(acc.all(axis=1), K, np.argmin(acc, axis=1)) if K > 0 else np.zeros(nb, np.int64)
+    # sampled row: residual at n < K, bonus at n == K
+    rows_p = P[np.arange(nb), n]
+    w = np.empty((nb, V))
+    rej = n < K
+    if rej.any():
+        nr = n[rej]
+        idx = np.flatnonzero(rej)
+        res = np.maximum(0.0, P[idx, nr] - Q[idx, nr])
+        empty = res.sum(axis=1) == 0.0
+        res[empty] = P[idx[empty], nr[empty]]
+        w[rej] = res
+    w[~rej] = rows_p[~rej]
+    w = np.where(np.isnan(w), 0.0, w)
+    tok, Z = inverse_cdf(w, u[:, K])
+    # emit: accepted drafts, then the sampled token, then -1 padding
+    pos = np.arange(K + 1)[None, :]
+    row = np.where(pos < n[:, None], np.pad(x, ((0, 0), (0, 1))), -1)
+    row = np.where(pos == n[:, None], tok[:, None], row)
+    row[bad] = -1
+    return row, np.where(bad, -1, n), px, qx, np.where(bad, np.nan, Z)
+
+
+def verify_given(P, Q, draft_tokens, uniforms, diag: bool = False):
+    """Verification of a batch whose filtered distributions are given: P
+    [B, K+1, V] (the target's p_0..p_K) and Q [B, K, V] (the draft's q_i, the
+    distributions the drafts were drawn from), both float64 probabilities with
+    a row of NaN for a row that has no distribution.  The rule is that of
+    ``verify``, which is this function applied to the filtered rows of the
+    logits.  uniforms: float32 [B, K+1].  Returns as ``verify``.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    X = np.asarray(draft_tokens).astype(np.int64)
+    U = np.asarray(uniforms)
+    if U.dtype != np.float32:
+        raise TypeError("uniforms must be float32")
+    if P.ndim != 3:
+        raise ValueError("P must be [B, K+1, V]")
+    B, K1, V = P.shape
+    K = K1 - 1
+    if Q.shape != (B, K, V) or X.shape != (B, K) or U.shape != (B, K + 1):
+        raise ValueError("shape mismatch")
+    if B == 0:
+        e = (np.full((0, K + 1), -1, np.int32), np.full((0,), -1, np.int32))
+        return e + (dict(px=np.zeros((0, K)), qx=np.zeros((0, K)), Z=np.zeros(0)),) if diag else e
+    row, n, px, qx, Z = decide(P, Q, X, U)
+    out = (row.astype(np.int32), n.astype(np.int32))
+    return out + (dict(px=px, qx=qx, Z=Z),) if diag else out
+
+
 def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
            dtype: str = F32, block: int | None = None, diag: bool = False, draft_temperature=None,
            draft_probs=None):
@@ -346,47 +432,12 @@ def verify(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
             Q = draft[s:e]
         else:
             Q = _draft_probs(draft[s:e], dtype, Td, k, tp)
-        x = X[s:e]
-        u = U[s:e].astype(np.float64)
-        # bad sequences: a row with no distribution, or a drafted token out of range
-        bad = np.isnan(P).any(axis=(1, 2))
-        if T != 0.0 and K > 0:
-            # at T == 0 only the target rows matter (q drops out of the rule)
-            bad |= np.isnan(Q).any(axis=(1, 2))
-        bad |= ((x < 0) | (x >= V)).any(axis=1)
-        xs = np.clip(x, 0, V - 1)
-        ii = np.arange(nb)[:, None]
-        kk = np.arange(K)[None, :]
-        px = P[ii, kk, xs]
-        qx = Q[ii, kk, xs]
-        # accept test at each position
-        acc = u[:, :K] * qx < px
-        # first rejection
-        n = np.where(acc.all(axis=1), K, np.argmin(acc, axis=1)) if K > 0 else np.zeros(nb, np.int64)
-        # sampled row: residual at n < K, bonus at n == K
-        rows_p = P[np.arange(nb), n]
-        w = np.empty((nb, V))
-        rej = n < K
-        if rej.any():
-            nr = n[rej]
-            idx = np.flatnonzero(rej)
-            res = np.maximum(0.0, P[idx, nr] - Q[idx, nr])
-            empty = res.sum(axis=1) == 0.0
-            res[empty] = P[idx[empty], nr[empty]]
-            w[rej] = res
-        w[~rej] = rows_p[~rej]
-        w = np.where(np.isnan(w), 0.0, w)
-        tok, Z = inverse_cdf(w, u[:, K])
-        # emit: accepted drafts, then the sampled token, then -1 padding
-        pos = np.arange(K + 1)[None, :]
-        row = np.where(pos < n[:, None], np.pad(x, ((0, 0), (0, 1))), -1)
-        row = np.where(pos == n[:, None], tok[:, None], row)
-        row[bad] = -1
+        row, n, px, qx, Z = decide(P, Q, X[s:e], U[s:e])
         out_tok[s:e] = row
-        out_n[s:e] = np.where(bad, -1, n)
+        out_n[s:e] = n
         px_all[s:e] = px
         qx_all[s:e] = qx
-        Z_all[s:e] = np.where(bad, np.nan, Z)
+        Z_all[s:e] = Z
     if diag:
         return out_tok, out_n, dict(px=px_all, qx=qx_all, Z=Z_all)
     return out_tok, out_n

@@ -281,3 +281,87 @@ def compare_lmhead(w, d: dict, lt: np.ndarray, ld: np.ndarray, x: np.ndarray, de
     stats["flags"] = flags
     stats["ref_dg"] = ref_dg
     return stats, fails
+
+
+# ---------------------------------------------------------------------------
+# near-tie rates over many verifications of the same rows
+# ---------------------------------------------------------------------------
+def filtered_rows(rows: np.ndarray, dtype: str, T, top_k, top_p, block: int = 256) -> np.ndarray:
+    """The oracle's filtered distributions of logit rows [N, V], a block of
+    rows at a time (bounded temporaries at full vocabulary sizes)."""
+    out = np.empty(rows.shape, dtype=np.float64)
+    for s in range(0, rows.shape[0], block):
+        out[s:s + block] = oracle.filtered_probs(oracle.widen(rows[s:s + block], dtype), T, top_k, top_p)
+    return out
+
+
+def rate_inputs(w: Workload, d: dict, n_min: int, seed_key: int = 7):
+    """Draw tables of the batch ``d`` and R = ceil(n_min / B) fresh draws of
+    (drafted tokens, uniforms) for it.  Drafts follow the filtered q (greedy:
+    the target's arg-max with probability 0.6, else a uniform token).
+    Returns (tables, x [R, B, K], u [R, B, K+1] float32)."""
+    from oracle.rate import DrawTables
+
+    B, K, V = w.B, w.K, w.V
+    P = filtered_rows(d["target"].reshape(-1, V), w.dtype, w.temperature, w.top_k, w.top_p).reshape(B, K + 1, V)
+    if w.temperature == 0.0:
+        # greedy: q is one-hot at the draft's arg-max and drops out of the rule
+        Q = filtered_rows(d["draft"].reshape(-1, V), w.dtype, 0.0, 0, 1.0).reshape(B, K, V) if K > 0 else \
+            np.zeros((B, 0, V))
+    else:
+        Q = filtered_rows(d["draft"].reshape(-1, V), w.dtype, w.temperature, w.top_k, w.top_p).reshape(B, K, V)
+    tabs = DrawTables(P, Q)
+    R = -(-n_min // B)
+    rng = np.random.default_rng(np.random.SeedSequence(w.seed, spawn_key=tuple(w.spawn_key) + (seed_key,)))
+    if w.temperature == 0.0:
+        amax = np.argmax(P[:, :K], axis=2)
+        x = np.where(rng.random((R, B, K)) < 0.6, amax[None], rng.integers(0, V, (R, B, K)))
+    else:
+        x = tabs.draw_drafts(rng.random((R, B, K)))
+    u = rng.random((R, B, K + 1), dtype=np.float32)
+    return tabs, x, u
+
+
+def rate_check(w: Workload, d: dict, tabs, x: np.ndarray, u: np.ndarray, dev_tok: np.ndarray, dev_n: np.ndarray):
+    """Compare R verifications of the batch with the oracle's: exact matches,
+    near-ties (flagged) and failures, with the informational count of
+    sequences whose own decisions lie within 1e-5 of a boundary (at risk)."""
+    ref_tok, ref_n = tabs.decide(x, u)
+    risk = tabs.at_risk(x, u)
+    mism = (dev_tok != ref_tok).any(axis=2) | (dev_n != ref_n)
+    stats = dict(sequences=int(dev_n.size), mismatched=int(mism.sum()), flagged=0, fail=0,
+                 at_risk=int(risk.sum()), accepted_mean=float(np.mean(ref_n[ref_n >= 0])) if (ref_n >= 0).any() else 0.0)
+    fails, flags = [], []
+    for r, b in np.argwhere(mism):
+        v, why = oracle.classify(d["target"][b], d["draft"][b], x[r, b], u[r, b], w.temperature, w.top_k, w.top_p,
+                                 w.dtype, dev_tok[r, b], dev_n[r, b])
+        if v == oracle.FLAGGED:
+            stats["flagged"] += 1
+            flags.append((int(r), int(b), why))
+        elif v == oracle.FAIL:
+            stats["fail"] += 1
+            fails.append((int(r), int(b), why))
+    stats["flagged_rate"] = stats["flagged"] / max(1, stats["sequences"])
+    return stats, fails, flags
+
+
+def run_device_many(w: Workload, d: dict, x: np.ndarray, u: np.ndarray):
+    """R calls of the library's verification on the same device rows, one per
+    draw of (drafted tokens, uniforms); outputs gathered on the device and
+    copied back once."""
+    import torch
+
+    from rejection_sampling_verify_09_amd import spec_verify
+
+    R, B, K = x.shape
+    tgt = to_device(d["target"], w.dtype)
+    drf = to_device(d["draft"], w.dtype) if K > 0 else None
+    X = torch.from_numpy(x.astype(np.int32)).cuda()
+    U = torch.from_numpy(np.ascontiguousarray(u)).cuda()
+    out_t = torch.empty((R, B, K + 1), dtype=torch.int32, device="cuda")
+    out_n = torch.empty((R, B), dtype=torch.int32, device="cuda")
+    for r in range(R):
+        spec_verify(tgt, drf, X[r], U[r], w.temperature, w.top_k, w.top_p, out_tokens=out_t[r],
+                    out_num_accepted=out_n[r])
+    torch.cuda.synchronize()
+    return out_t.cpu().numpy(), out_n.cpu().numpy()

@@ -338,3 +338,44 @@ def check_lossless_draft_probs(mod, N: int = 300_000, seed: int = 31):
         counts = np.bincount(tok[sel, j], minlength=V)
         pv = _chi2_pvalue(counts, P[j])
         assert pv > CHI2_MIN_P, f"given q: position {j} differs from p (chi2 p={pv:.2e})"
+
+
+# ---------------------------------------------------------------------------
+# the empty residual (reached through a given q at or above p everywhere)
+# ---------------------------------------------------------------------------
+def empty_residual_case(V: int = 8, K: int = 2, seed: int = 41):
+    """Target logits and a given q with q >= p at every token, extra mass on
+    one token per position (rows summing past 1): a rejection then leaves
+    max(0, p - q) with no mass.  Returns (target logits [K+1, V] float32,
+    q [K, V] float32, P [K+1, V] float64 from scipy's softmax, the bumped
+    token of each position)."""
+    rng = np.random.default_rng(seed)
+    tl = rng.normal(0, 1.2, (K + 1, V)).astype(np.float32)
+    P = softmax_rows(tl)
+    bump = rng.integers(0, V, K)
+    Q = P[:K] * (1.0 + 1e-6)
+    Q[np.arange(K), bump] += 0.3
+    Qf = Q.astype(np.float32)
+    Qf = np.where(Qf.astype(np.float64) < Q, np.nextafter(Qf, np.float32(np.inf)), Qf)
+    assert np.all(Qf.astype(np.float64) > P[:K])
+    return tl, Qf, P, bump
+
+
+def check_empty_residual(mod, N: int = 4096, seed: int = 41):
+    """After a rejection whose residual max(0, p - q) is empty, the
+    replacement is drawn from p by the inverse CDF: the emitted token is
+    searchsorted(cumsum(p), u * sum(p)) with the sampling uniform."""
+    V, K = 8, 2
+    tl, Qf, P, bump = empty_residual_case(V, K, seed)
+    rng = np.random.default_rng(seed + 1)
+    x = np.tile(bump, (N, 1))
+    u = rng.random((N, K + 1), dtype=np.float32)
+    tok, n = mod.verify(tile_rows(tl, N), None, x, u, 1.0, 0, 1.0, draft_probs=tile_rows(Qf, N))
+    rej = n < K
+    assert rej.sum() > N // 4, "the case must reject often"
+    C = np.cumsum(P, axis=1)
+    for r in np.flatnonzero(rej):
+        j = n[r]
+        ref = int(np.searchsorted(C[j], float(u[r, K]) * P[j].sum(), side="right"))
+        ref = min(ref, V - 1)
+        assert tok[r, j] == ref, f"empty residual at position {j}: token {tok[r, j]}, p's inverse CDF {ref}"

@@ -176,3 +176,14 @@ def test_gpu_lossless_chi2(case):
     m = 20000
     ref_tok, ref_n = oracle.verify(tl[None].repeat(m, 0), dl[None].repeat(m, 0), x[:m], u[:m], 1.0, 0, 1.0)
     assert np.array_equal(ref_n, n[:m]) and np.array_equal(ref_tok, tok[:m])
+
+
+def test_top_p_just_below_one():
+    """top_p = 1 - 2^-24 (the largest float32 below 1): the nucleus is the
+    whole row but for its least probable tokens, and the device's mass sums may
+    fall just short of top_p.  No failure is allowed; sequences whose kept set
+    differs only at that boundary are near-ties (top_p moved by 1e-5)."""
+    tp = float(np.nextafter(np.float32(1.0), np.float32(0.0)))
+    for dt in ("f32", "bf16"):
+        w = Workload(f"topp-near-one-{dt}", 8, 3, 3000, dt, "normal", 2.0, 0.5, 1.0, 0, tp, 31)
+        _check(w, max_flagged=w.B)

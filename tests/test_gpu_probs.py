@@ -133,3 +133,29 @@ def test_probs_bad_token_is_a_sentinel():
     ref_tok, ref_n = oracle.verify(d["target"], None, x, d["uniforms"], w.temperature, w.top_k, w.top_p,
                                    dtype=w.dtype, draft_probs=Q)
     assert np.array_equal(n, ref_n) and np.array_equal(tok, ref_tok)
+
+
+@pytest.mark.parametrize("params", [(1.0, 0, 0.9, "zipf", 1.0), (1.0, 0, 1.0, "normal", 2.0),
+                                    (1.0, 0, 0.995, "normal", 0.05)],
+                         ids=["kept-lists", "unfiltered", "large-kept-set"])
+def test_empty_residual_draws_from_p(params):
+    """A given q at or above p at every token, with extra mass on the drafted
+    token: every rejection leaves max(0, p - q) empty and the replacement is
+    drawn from p (the oracle's reading, pinned on the CPU).  Covers the draw
+    from kept lists, the unfiltered full-row draw and the draw from a kept set
+    too large for a list."""
+    from synth import Workload
+
+    T, k, p, shape, sig = params
+    w = Workload("empty-res", 16, 3, 3000, "f32", shape, sig, 0.5, T, k, p, 13)
+    d = make_inputs(w)
+    P = oracle.filtered_probs(oracle.widen(d["target"].reshape(-1, w.V), w.dtype), T, k, p).reshape(w.B, w.K + 1,
+                                                                                                      w.V)
+    rng = np.random.default_rng(14)
+    x = np.stack([rng.choice(np.flatnonzero(P[b, i] > 0)) for b in range(w.B) for i in range(w.K)]).reshape(w.B, w.K)
+    Q = P[:, :w.K] * (1.0 + 1e-6)
+    Q[np.arange(w.B)[:, None], np.arange(w.K)[None, :], x] += 0.3
+    Qf = Q.astype(np.float32)
+    Qf = np.where(Qf.astype(np.float64) < Q, np.nextafter(Qf, np.float32(np.inf)), Qf)
+    tok, n, dbg = _check(w, d, Qf, x.astype(np.int32))
+    assert (n < w.K).sum() >= w.B // 2, "the case must reject often"

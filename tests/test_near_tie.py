@@ -92,3 +92,31 @@ def test_sample_classifier():
     # top_p = 0.5 keeps token 2 alone: a token outside the kept set is never a near-tie
     assert classify_sample(row, 1.0, 0, 0.5, 0.49, 2, 2) == MATCH
     assert classify_sample(row, 1.0, 0, 0.5, 0.49, 0, 2) == FAIL
+
+
+def test_accept_near_tie_then_wrong_draw_is_fail():
+    """A device that flips an accept decision at a near-tie must still draw
+    what the oracle draws on the device's path: a wrong bonus token after the
+    flip is a failure, the right one is flagged."""
+    tl, dl = _case()
+    ref = oracle.verify_one(tl, dl, [0], np.array([0.5, 0.5], np.float32), 1.0, 0, 1.0)
+    r = ref["px"][0] / ref["qx"][0]
+    u_hi = np.array([np.nextafter(np.float32(r), np.float32(1)), 0.5], np.float32)
+    # the device accepted draft 0 and drew its bonus from p_1 with u = 0.5
+    P1 = ref["P"][1]
+    C = np.cumsum(P1)
+    good = int(np.searchsorted(C, 0.5 * P1.sum(), side="right"))
+    far = [j for j in range(4) if j != good and not (C[j] - P1[j] <= 0.5 * P1.sum() + 1e-5 and
+                                                      C[j] > 0.5 * P1.sum() - 1e-5)]
+    assert classify(tl, dl, [0], u_hi, 1.0, 0, 1.0, "f32", np.array([0, good]), 1)[0] == FLAGGED
+    v, why = classify(tl, dl, [0], u_hi, 1.0, 0, 1.0, "f32", np.array([0, far[0]]), 1)
+    assert v == FAIL, why
+    # and a device that rejected where the oracle accepted must draw the residual
+    u_lo = np.array([np.nextafter(np.float32(r), np.float32(0)), 0.5], np.float32)
+    assert oracle.verify_one(tl, dl, [0], u_lo, 1.0, 0, 1.0)["n"] == 1
+    w = np.maximum(0.0, ref["P"][0] - ref["Q"][0])
+    Cw = np.cumsum(w)
+    res_tok = int(np.searchsorted(Cw, 0.5 * w.sum(), side="right"))
+    assert classify(tl, dl, [0], u_lo, 1.0, 0, 1.0, "f32", np.array([res_tok, -1]), 0)[0] == FLAGGED
+    wrong = [j for j in range(4) if w[j] == 0.0][0]
+    assert classify(tl, dl, [0], u_lo, 1.0, 0, 1.0, "f32", np.array([wrong, -1]), 0)[0] == FAIL

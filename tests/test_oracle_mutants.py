@@ -54,6 +54,12 @@ MUTANTS = {
     # given draft probabilities used at the wrong position
     "draft_probs_position": ("            Q = draft[s:e]\n", "            Q = np.roll(draft[s:e], 1, axis=1)\n",
                              lambda m: pins.check_lossless_draft_probs(m, N=150_000)),
+    # an empty residual drawn from q instead of p
+    "empty_residual_from_q": ("res[empty] = P[idx[empty], nr[empty]]", "res[empty] = Q[idx[empty], nr[empty]]",
+                              lambda m: pins.check_empty_residual(m)),
+    # an empty residual left empty (nothing to draw from)
+    "empty_residual_kept_empty": ("res[empty] = P[idx[empty], nr[empty]]", "res[empty] = 0.0",
+                                  lambda m: pins.check_empty_residual(m)),
     # ragged: a sequence's uniforms taken from its draft offset, not cu[b] + b
     "ragged_uniform_base": ("U[t_idx]", "U[t_idx - bs[:, None]]",
                             lambda m: rag.check_ragged_worked_case(m)),

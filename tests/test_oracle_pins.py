@@ -284,3 +284,31 @@ def test_draft_probs_validation():
             ov.verify(t, None, np.zeros((1, 1)), u, 1.0, 0, 1.0, draft_probs=bad)
     with pytest.raises(TypeError):
         ov.verify(t, None, np.zeros((1, 1)), u, 1.0, 0, 1.0, draft_probs=np.zeros((1, 1, 4), np.float16))
+
+
+def test_empty_residual_draws_from_p():
+    """A given q at or above p everywhere: after a rejection the residual is
+    empty and the oracle draws from p (pinned to p's inverse CDF by
+    searchsorted, not by the oracle's own sampler)."""
+    pins.check_empty_residual(ov)
+
+
+def test_top_p_mass_reaches_every_float32_top_p():
+    """The top-p cut's cumulative mass ends within 2^-31 of 1 even on the
+    widest rows and on rows of one dominant token among many tiny ones, so
+    every float32 top_p < 1 (at most 1 - 2^-24) is reached by some prefix and
+    the oracle never needs a fallback cut."""
+    rng = np.random.default_rng(7)
+    tp = float(np.nextafter(np.float32(1.0), np.float32(0.0)))
+    rows = [rng.normal(0, 3, 1 << 21), np.concatenate([[60.0], rng.normal(0, 1, (1 << 21) - 1)]),
+            np.concatenate([rng.normal(0, 0.01, 1 << 20), np.full(1 << 20, -30.0)]), np.zeros(1 << 21)]
+    for z in rows:
+        e = np.exp(z - z.max())
+        pi = e / e.sum()
+        mass = np.cumsum(-np.sort(-pi))
+        assert mass[-1] >= 1.0 - 2.0 ** -31
+        assert mass[-1] >= tp
+    # the oracle's top-p filter at that top_p keeps a prefix and raises nothing
+    z = rng.normal(0, 2, (3, 5000))
+    p = ov.filtered_probs(z, 1.0, 0, tp)
+    assert np.all((p > 0).sum(axis=1) >= 4990)
