@@ -26,11 +26,17 @@
  *   V * sizeof(dtype) a multiple of 16 take the vectorised path.
  * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *   enqueues work on it and returns without synchronising.
- * - Scratch: the library keeps one device scratch buffer per device, grown on
- *   demand (a call that needs more than the buffer holds synchronises the
- *   device, reallocates and zero-fills it).  Calls on one device that may
- *   overlap in time (different streams without ordering) race on it and must
- *   be serialised by the caller.  sv_release() frees it.
+ * - Scratch: the library keeps device scratch per (device, stream): calls on
+ *   different streams never share it, so they may run concurrently, from any
+ *   host threads.  A stream's scratch is allocated on its first call and grown
+ *   when a call needs more; a growth synchronises that stream only (the one
+ *   stream whose queued work can still use the old buffer) before freeing
+ *   it.  sv_init() sizes a stream's scratch up front, after which calls
+ *   within its bounds never allocate or synchronise.  Calls on one stream
+ *   from several host threads are serialised by the library (each holds the
+ *   stream's scratch from its look-up to its last launch).  No call depends
+ *   on what an earlier call left in the scratch.  sv_stream_release() and
+ *   sv_release() free it.
  * - Temperature T: 0 selects greedy decoding (p and q one-hot at their
  *   arg-max, ties to the lowest index); otherwise T must be a finite normal
  *   float >= FLT_MIN.  top_k: 0 or >= V disables it.  top_p in (0, 1]; 1
@@ -66,6 +72,9 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 #define SV_MAX_K 64
 #define SV_MAX_V 2097152 /* 256 chunks of 8192 logits per row */
+/* sv_init flag: also size the stream's buffer of projection logits for
+ * sv_spec_verify_lmhead. */
+#define SV_INIT_LMHEAD 1
 
 /*
  * sv_spec_verify - verify one round of K drafted tokens for B sequences.
@@ -334,9 +343,10 @@ int sv_lm_logits(const void* hidden, const void* weight, float* out_logits,
  * out_num_accepted, out_p, out_q, out_z, B, K, V: as sv_spec_verify_debug.
  * d_target, d_draft: as d of sv_lm_logits.
  *
- * The logits live in a second per-device buffer of (B(K+1) + BK) * V
- * float32, grown on demand like the scratch (the growth synchronises the
- * device) and freed by sv_release.  Under launch timing the first two
+ * The logits live in a second buffer of the stream's scratch set, of
+ * (B(K+1) + BK) * V float32, grown on demand like the scratch (a growth
+ * synchronises the stream) or sized by sv_init with SV_INIT_LMHEAD, and freed
+ * by sv_stream_release and sv_release.  Under launch timing the first two
  * events of the call bracket the two projections (its stream_kernel_ms) and
  * the third follows the verification.
  */
@@ -368,12 +378,34 @@ int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target,
 int sv_profile_start(void);
 int sv_profile_stop(double* stream_kernel_ms, double* other_kernels_ms, int64_t* calls);
 
-/* Frees the per-device scratch (and logits buffer) of every device the
- * library has used. */
+/*
+ * sv_init - size the scratch of calls on `stream` (on `device`) up front, so
+ * that every later call on that stream within the bounds runs without
+ * allocating or synchronising: verification of B <= max_B sequences of
+ * K <= max_K drafts with V <= max_V (any mode, dtype and variant; ragged
+ * batches of total_draft <= max_B * max_K; sv_sample and sv_filtered_probs
+ * of rows <= max_B * (2 * max_K + 1)).  flags: 0, or SV_INIT_LMHEAD to also
+ * size the logits buffer of sv_spec_verify_lmhead for those bounds.  The
+ * current device is restored before returning.  Errors: SV_ERR_PARAM (device
+ * outside [0, 64) or unknown flags), SV_ERR_SHAPE (max_B < 0, max_K outside
+ * [0, SV_MAX_K], max_V outside [1, SV_MAX_V]), SV_ERR_WORKSPACE (allocation
+ * failed), SV_ERR_HIP.  Calling it again with larger bounds grows the
+ * buffers (synchronising the stream); with smaller ones it does nothing.
+ */
+int sv_init(int device, void* stream, int32_t max_B, int32_t max_K, int32_t max_V, int32_t flags);
+
+/* Frees the scratch (and logits buffer) bound to `stream` on the current
+ * device, after synchronising the stream.  The next call on the stream
+ * allocates again.  Call it before destroying a stream whose handle may be
+ * reused. */
+int sv_stream_release(void* stream);
+
+/* Frees the scratch (and logits buffers) of every stream on every device the
+ * library has used, after synchronising those devices. */
 int sv_release(void);
 
-/* Bytes of device scratch and logits buffer currently held on `device`
- * (0 if none). */
+/* Bytes of device scratch and logits buffers currently held on `device`,
+ * summed over its streams (0 if none). */
 int64_t sv_scratch_bytes(int device);
 
 /* Human-readable name of a status code. */

@@ -10,11 +10,14 @@ from ._lib import (  # noqa: F401
     DraftLengthController,
     SpecVerifyError,
     filtered_probs,
+    init,
     lib,
     lm_logits,
     profile_start,
     profile_stop,
     release,
+    scratch_bytes,
+    stream_release,
     sample,
     spec_verify,
     spec_verify_lmhead,
@@ -23,5 +26,5 @@ from ._lib import (  # noqa: F401
     status_string,
 )
 
-__all__ = ["spec_verify", "spec_verify_lmhead", "lm_logits", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "status_string", "lib",
+__all__ = ["spec_verify", "spec_verify_lmhead", "lm_logits", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "init", "stream_release", "scratch_bytes", "status_string", "lib",
            "SpecVerifyError"]

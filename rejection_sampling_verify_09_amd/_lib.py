@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_PARAM, SV_ERR_HIP, SV_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_K = 64
+SV_INIT_LMHEAD = 1
 
 _lib = None
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.sv_dynk_destroy.restype = None
         L.sv_release.argtypes = []
         L.sv_release.restype = ctypes.c_int
+        L.sv_init.argtypes = [ctypes.c_int, vp, i32, i32, i32, i32]
+        L.sv_init.restype = ctypes.c_int
+        L.sv_stream_release.argtypes = [vp]
+        L.sv_stream_release.restype = ctypes.c_int
         L.sv_scratch_bytes.argtypes = [ctypes.c_int]
         L.sv_scratch_bytes.restype = ctypes.c_int64
         L.sv_status_string.argtypes = [ctypes.c_int]
@@ -467,3 +472,25 @@ def release() -> None:
     st = lib().sv_release()
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_release")
+
+
+def init(max_B: int, max_K: int, max_V: int, stream=None, device: int | None = None, lmhead: bool = False) -> None:
+    """Size the scratch of calls on ``stream`` (the current stream by
+    default) up front (sv_init): calls within the bounds then never allocate
+    or synchronise."""
+    dev = torch.cuda.current_device() if device is None else int(device)
+    st = lib().sv_init(dev, _stream(stream), int(max_B), int(max_K), int(max_V), SV_INIT_LMHEAD if lmhead else 0)
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_init")
+
+
+def stream_release(stream=None) -> None:
+    """Free the scratch bound to ``stream`` on the current device."""
+    st = lib().sv_stream_release(_stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_stream_release")
+
+
+def scratch_bytes(device: int | None = None) -> int:
+    """Bytes of scratch the library holds on ``device`` (all streams)."""
+    return int(lib().sv_scratch_bytes(torch.cuda.current_device() if device is None else int(device)))

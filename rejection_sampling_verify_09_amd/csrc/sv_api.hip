@@ -6,12 +6,17 @@
 #include <algorithm>
 #include <cfloat>
 #include <cmath>
+#include <map>
+#include <memory>
 #include <mutex>
+#include <new>
+#include <utility>
 
 namespace sv {
 hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s,
                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
+hipError_t launch_seq(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
 hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s);
 hipError_t launch_probs(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
 hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s);
@@ -26,22 +31,52 @@ constexpr int kMaxDevices = 64;
 // A launch must satisfy grid * WG < 2^32.
 constexpr int64_t kMaxGrid = (int64_t(1) << 32) / WG - 1;
 
-struct Scratch {
-  char* ptr = nullptr;
+// Scratch of the verification calls and the projection logits of
+// sv_spec_verify_lmhead, one set per (device, stream): calls on different
+// streams never share memory.  A call holds its set's mutex from the look-up
+// to its last launch, so a growth on another host thread (same stream) waits
+// for it; a growth synchronises only that stream (the only work that can
+// still use the old buffer) before freeing it.  Entries live until the
+// process ends (sv_release frees their memory, not the entries, so a pointer
+// a concurrent call already holds stays valid).
+struct StreamBufs {
+  std::mutex mu;
+  char* ptr = nullptr;   // verification scratch
   size_t bytes = 0;
-  int64_t cap_seq = 0;   // sequences the (zero-filled) arrival counters cover
+  char* lgt = nullptr;   // float32 logits formed by the output projections
+  size_t lgt_bytes = 0;
 };
 
-std::mutex g_mu;
-Scratch g_scr[kMaxDevices];
+std::mutex g_mu;  // guards g_bufs (the map, not the buffers)
+std::map<std::pair<int, uintptr_t>, std::unique_ptr<StreamBufs>> g_bufs;
 
-// Logits formed by the output projection for verification (float32, target
-// rows then draft rows), per device, grown on demand (guarded by g_mu).
-struct LogitBuf {
-  float* ptr = nullptr;
-  size_t bytes = 0;
-};
-LogitBuf g_lgt[kMaxDevices];
+StreamBufs* bufs_for(int dev, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto& e = g_bufs[{dev, (uintptr_t)s}];
+  if (!e) e.reset(new (std::nothrow) StreamBufs());
+  return e.get();
+}
+
+// Grows *p to at least `want` bytes (the caller holds the set's mutex).
+int grow(char** p, size_t* have, size_t want, hipStream_t s) {
+  if (*have >= want && *p) return SV_OK;
+  if (*p) {
+    if (hipStreamSynchronize(s) != hipSuccess) return SV_ERR_HIP;
+    (void)hipFree(*p);
+    *p = nullptr;
+    *have = 0;
+  }
+  void* q = nullptr;
+  if (hipMalloc(&q, want) != hipSuccess) return SV_ERR_WORKSPACE;
+  *p = (char*)q;
+  *have = want;
+  return SV_OK;
+}
+
+int current_device(int* dev) {
+  if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= kMaxDevices) return SV_ERR_HIP;
+  return SV_OK;
+}
 
 // Launch timing (sv_profile_start / sv_profile_stop): three events per call:
 // the streaming kernel's start and end (recorded by its launch), and one
@@ -94,7 +129,7 @@ ProfSlot* prof_begin() {
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t seq_cnt, smp_cnt, chunk, ctop, cand, row, kidx, kprob, seq, seg_sum, seg_last, qxs, total;
+  size_t seq_cnt, smp_cnt, cflag, chunk, ctop, cand, row, kidx, kprob, seq, seg_sum, seg_last, qxs, total;
 };
 
 // What one call needs from the scratch.
@@ -104,14 +139,15 @@ struct Need {
   bool topk = false;                               // the chunks' largest thread maxima
 };
 
-// Counters first (a fixed region for the life of the allocation: the kernels
-// leave every counter at zero, so it never needs clearing), then the data
-// records of the call.
-Layout make_layout(int64_t cap_seq, const Need& n) {
+// Arrival counters (cleared by each call's streaming kernel), then the data
+// records of the call.  Every region's size grows with each field of Need, so
+// a buffer laid out for larger bounds holds any call within them.
+Layout make_layout(const Need& n) {
   Layout L;
   size_t o = 0;
-  L.seq_cnt = o; o += al256(cap_seq * 4);
-  L.smp_cnt = o; o += al256(cap_seq * 4);
+  L.seq_cnt = o; o += al256(n.B * 4);
+  L.smp_cnt = o; o += al256(n.B * 4);
+  L.cflag = o; o += al256(4);
   L.chunk = o; o += al256(n.rows * n.nchunks * sizeof(ChunkRec));
   L.ctop = o; o += n.topk ? al256(n.rows * n.nchunks * CTOP * sizeof(uint32_t)) : 0;
   L.cand = o; o += n.filt ? al256(n.rows * n.nchunks * CAND_CAP * sizeof(uint64_t)) : 0;
@@ -126,42 +162,10 @@ Layout make_layout(int64_t cap_seq, const Need& n) {
   return L;
 }
 
-// Returns the scratch of the current device, large enough for this call.
-int get_scratch(const Need& n, char** base, Layout* lay) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
-  std::lock_guard<std::mutex> lk(g_mu);
-  Scratch& s = g_scr[dev];
-  Layout L = make_layout(s.cap_seq, n);
-  if (s.ptr == nullptr || s.cap_seq < n.B || s.bytes < L.total) {
-    const int64_t cs = std::max(n.B, s.cap_seq);
-    L = make_layout(cs, n);
-    const size_t want = std::max(L.total, s.bytes);
-    if (s.ptr) {
-      if (hipDeviceSynchronize() != hipSuccess) return SV_ERR_HIP;
-      (void)hipFree(s.ptr);
-      s.ptr = nullptr;
-      s.bytes = 0;
-      s.cap_seq = 0;
-    }
-    void* p = nullptr;
-    if (hipMalloc(&p, want) != hipSuccess) return SV_ERR_WORKSPACE;
-    if (hipMemset(p, 0, want) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-      (void)hipFree(p);
-      return SV_ERR_HIP;
-    }
-    s.ptr = (char*)p;
-    s.bytes = want;
-    s.cap_seq = cs;
-  }
-  *base = s.ptr;
-  *lay = make_layout(s.cap_seq, n);
-  return SV_OK;
-}
-
 void bind_scratch(Args& a, char* base, const Layout& L) {
   a.seq_cnt = (uint32_t*)(base + L.seq_cnt);
   a.smp_cnt = (uint32_t*)(base + L.smp_cnt);
+  a.cflag = (int32_t*)(base + L.cflag);
   a.chunk = (ChunkRec*)(base + L.chunk);
   a.ctop = (uint32_t*)(base + L.ctop);
   a.cand = (uint64_t*)(base + L.cand);
@@ -218,40 +222,70 @@ struct Ragged {
   int32_t nd, kmax;
 };
 
-// need_n: out_n is required (the sampler passes none).  out_px: probability
-// of each sequence's last drawn token under the row it was drawn from (the
-// sampler, K == 0).  rg: null for a rectangular [B, K] batch.  qprob: the
-// draft distributions given as probabilities [B, K, V] (rectangular only;
-// drf is then not used).
-int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float* U, float T, float Td,
-                int32_t top_k, float top_p, int32_t* out_tok, int32_t* out_n, bool need_n, double* out_p,
-                double* out_q, double* out_z, double* out_px, int32_t B, int32_t K, int32_t V, int32_t dtype,
-                void* stream, const Ragged* rg = nullptr, const float* qprob = nullptr, bool qp = false,
-                bool timed = true) {
+// One verification call's inputs.  need_n: out_n is required (the sampler
+// passes none).  out_px: probability of each sequence's last drawn token under
+// the row it was drawn from (the sampler, K == 0).  rg: null for a
+// rectangular [B, K] batch.  qp / qprob: the draft distributions given as
+// probabilities [B, K, V] (rectangular only; drf is then not used).
+struct VerifyIn {
+  const void* tgt = nullptr;
+  const void* drf = nullptr;
+  const int32_t* X = nullptr;
+  const float* U = nullptr;
+  float T = 1.0f, Td = 1.0f;
+  int32_t top_k = 0;
+  float top_p = 1.0f;
+  int32_t* out_tok = nullptr;
+  int32_t* out_n = nullptr;
+  bool need_n = true;
+  double *out_p = nullptr, *out_q = nullptr, *out_z = nullptr, *out_px = nullptr;
+  int32_t B = 0, K = 0, V = 0, dtype = 0;
+  const Ragged* rg = nullptr;
+  const float* qprob = nullptr;
+  bool qp = false;
+};
+
+// A validated call: its kernel arguments (all but the scratch pointers), its
+// launch grids and its scratch needs.
+struct Plan {
+  Args a;
+  int mode = 0, dtype = 0;
+  bool vec = false;
+  unsigned g_stream = 0, g_seq = 0, g_sample = 0;
+  Need need;
+  bool empty = false;  // B == 0: nothing to launch
+};
+
+int plan_verify(const VerifyIn& in, Plan* p) {
+  const int32_t B = in.B, K = in.K, V = in.V;
+  const Ragged* rg = in.rg;
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > MAX_V) return SV_ERR_SHAPE;
   if (rg && (rg->nd < 0 || rg->kmax < 0 || rg->kmax > SV_MAX_K || (int64_t)rg->nd > (int64_t)B * rg->kmax))
     return SV_ERR_SHAPE;
-  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
-  int st = check_params(T, top_k, top_p);
+  if (in.dtype != SV_F32 && in.dtype != SV_BF16) return SV_ERR_DTYPE;
+  int st = check_params(in.T, in.top_k, in.top_p);
   if (st != SV_OK) return st;
   // at T > 0 the draft temperature must be a valid temperature above 0
-  if (T > 0.0f && (check_params(Td, top_k, top_p) != SV_OK || !(Td > 0.0f))) return SV_ERR_PARAM;
-  if (B == 0) return SV_OK;
-  const int mode = pick_mode(T, top_k, top_p, V);
+  if (in.T > 0.0f && (check_params(in.Td, in.top_k, in.top_p) != SV_OK || !(in.Td > 0.0f))) return SV_ERR_PARAM;
+  if (B == 0) {
+    p->empty = true;
+    return SV_OK;
+  }
+  const int mode = pick_mode(in.T, in.top_k, in.top_p, V);
   const int64_t nd = rg ? rg->nd : (int64_t)B * K;  // draft rows
   const int32_t kmax = rg ? rg->kmax : K;
-  if (!tgt || !U || !out_tok || (need_n && !out_n) || (rg && !rg->cu)) return SV_ERR_NULL;
-  if (nd > 0 && !X) return SV_ERR_NULL;
-  if (nd > 0 && mode != M_GREEDY && !(qp ? (const void*)qprob : drf)) return SV_ERR_NULL;
+  if (!in.tgt || !in.U || !in.out_tok || (in.need_n && !in.out_n) || (rg && !rg->cu)) return SV_ERR_NULL;
+  if (nd > 0 && !in.X) return SV_ERR_NULL;
+  if (nd > 0 && mode != M_GREEDY && !(in.qp ? (const void*)in.qprob : in.drf)) return SV_ERR_NULL;
   // q given as probabilities: no draft rows to stream (greedy never uses q)
-  const bool use_qp = qp && mode != M_GREEDY && nd > 0;
-  const int esz = dtype == SV_BF16 ? 2 : 4;
+  const bool use_qp = in.qp && mode != M_GREEDY && nd > 0;
+  const int esz = in.dtype == SV_BF16 ? 2 : 4;
   const int64_t nt = nd + B;  // target rows
   const int64_t rows = (mode == M_GREEDY || use_qp) ? nt : nt + nd;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
   if (rows * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
-  Need need;
+  Need& need = p->need;
   need.rows = rows;
   need.nchunks = nchunks;
   need.B = B;
@@ -259,23 +293,19 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   need.filt = mode == M_TOPK || mode == M_TOPP || mode == M_TOPKP;
   need.topk = mode == M_TOPK || mode == M_TOPKP;
 
-  char* base = nullptr;
-  Layout L;
-  st = get_scratch(need, &base, &L);
-  if (st != SV_OK) return st;
-
-  Args a;
-  a.tgt = tgt;
-  a.drf = (mode == M_GREEDY || use_qp) ? nullptr : drf;
-  a.qprob = use_qp ? qprob : nullptr;
-  a.X = X;
-  a.U = U;
-  a.out_tok = out_tok;
-  a.out_n = out_n;
-  a.out_p = out_p;
-  a.out_q = out_q;
-  a.out_z = out_z;
-  a.out_px = out_px;
+  Args& a = p->a;
+  a = Args{};
+  a.tgt = in.tgt;
+  a.drf = (mode == M_GREEDY || use_qp) ? nullptr : in.drf;
+  a.qprob = use_qp ? in.qprob : nullptr;
+  a.X = in.X;
+  a.U = in.U;
+  a.out_tok = in.out_tok;
+  a.out_n = in.out_n;
+  a.out_p = in.out_p;
+  a.out_q = in.out_q;
+  a.out_z = in.out_z;
+  a.out_px = in.out_px;
   a.out_probs = nullptr;
   a.B = B;
   a.K = rg ? 0 : K;
@@ -291,32 +321,60 @@ int verify_impl(const void* tgt, const void* drf, const int32_t* X, const float*
   a.spw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(SPW, (int64_t)B * nsc / 256));
   a.nsw = (int32_t)((nsc + a.spw - 1) / a.spw);
   a.do_seq = 1;
-  set_scalars(a, T, top_k, top_p, Td);
-  bind_scratch(a, base, L);
-
-  const bool vec = aligned16(tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
+  set_scalars(a, in.T, in.top_k, in.top_p, in.Td);
+  const bool vec = aligned16(in.tgt) && (a.drf == nullptr || aligned16(a.drf)) && ((int64_t)V * esz) % 16 == 0;
   a.ulen = vec ? 16 / esz : 1;
   a.dch = make_udiv((uint32_t)a.nchunks);
   a.rps = rg ? 1 : (mode == M_GREEDY || use_qp) ? a.K + 1 : 2 * a.K + 1;
   a.drps = make_udiv((uint32_t)a.rps);
-  hipStream_t s = (hipStream_t)stream;
-  ProfSlot* prof = timed ? prof_begin() : nullptr;
-  // chunk-parallel streaming pass, then one workgroup per row merges it; the
-  // last row of each sequence finishes the sequence.  When timing, the
-  // streaming launch records its own start and end in the slot's events.
-  if (launch_stream(a, dtype, mode, vec, (unsigned)(rows * nchunks), s, prof ? prof->ev[0] : nullptr,
+  p->mode = mode;
+  p->dtype = in.dtype;
+  p->vec = vec;
+  p->g_stream = (unsigned)(rows * nchunks);
+  p->g_seq = (unsigned)B;
+  p->g_sample = mode == M_PLAIN ? (unsigned)((int64_t)B * a.nsw) : 0u;
+  return SV_OK;
+}
+
+// Binds the call to scratch at `base` (at least make_layout(need).total
+// bytes) and enqueues its kernels: the chunk-parallel streaming pass, then one
+// workgroup per sequence merges the sequence's rows and finishes it (accept
+// tests, first rejection, draw), then for unfiltered rows the full-row draw.  When timing, the
+// streaming launch records its own start and end in the slot's events.
+int launch_plan(Plan& p, char* base, hipStream_t s, ProfSlot* prof) {
+  bind_scratch(p.a, base, make_layout(p.need));
+  if (launch_stream(p.a, p.dtype, p.mode, p.vec, p.g_stream, s, prof ? prof->ev[0] : nullptr,
                     prof ? prof->ev[1] : nullptr) != hipSuccess)
     return SV_ERR_HIP;
-  if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
-  if (mode == M_PLAIN) {
-    if (launch_sample(a, dtype, (unsigned)((int64_t)B * a.nsw), s) != hipSuccess) return SV_ERR_HIP;
-  }
+  if (launch_seq(p.a, p.dtype, p.mode, p.g_seq, s) != hipSuccess) return SV_ERR_HIP;
+  if (p.g_sample > 0 && launch_sample(p.a, p.dtype, p.g_sample, s) != hipSuccess) return SV_ERR_HIP;
   if (prof) {
     if (hipEventRecord(prof->ev[2], s) != hipSuccess) return SV_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     prof->pending = true;
   }
   return SV_OK;
+}
+
+// A planned call on the stream's own scratch; the caller holds b->mu.
+int run_plan_locked(Plan& p, StreamBufs* b, hipStream_t s, bool timed) {
+  int st = grow(&b->ptr, &b->bytes, make_layout(p.need).total, s);
+  if (st != SV_OK) return st;
+  ProfSlot* prof = timed ? prof_begin() : nullptr;
+  return launch_plan(p, b->ptr, s, prof);
+}
+
+int verify_impl(const VerifyIn& in, void* stream, bool timed = true) {
+  Plan p;
+  int st = plan_verify(in, &p);
+  if (st != SV_OK || p.empty) return st;
+  int dev = 0;
+  if ((st = current_device(&dev)) != SV_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  StreamBufs* b = bufs_for(dev, s);
+  if (!b) return SV_ERR_WORKSPACE;
+  std::lock_guard<std::mutex> lk(b->mu);
+  return run_plan_locked(p, b, s, timed);
 }
 
 // Largest hidden width accepted (the kernel needs only d % 64 == 0).
@@ -327,27 +385,6 @@ int check_lm_shape(const void* H, const void* W, int64_t M, int32_t V, int32_t d
   if (M > 0 && (!H || !W)) return SV_ERR_NULL;
   if (M > 0 && (!aligned16(H) || !aligned16(W))) return SV_ERR_SHAPE;
   if (M > INT32_MAX || sv::lm_gemm_tiles((int32_t)std::min<int64_t>(M, INT32_MAX), V) > kMaxGrid) return SV_ERR_SHAPE;
-  return SV_OK;
-}
-
-// The logits buffer of the current device, at least `bytes` long.
-int get_logit_buf(size_t bytes, float** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
-  std::lock_guard<std::mutex> lk(g_mu);
-  LogitBuf& b = g_lgt[dev];
-  if (b.bytes < bytes) {
-    if (b.ptr) {
-      if (hipDeviceSynchronize() != hipSuccess) return SV_ERR_HIP;
-      (void)hipFree(b.ptr);
-      b = LogitBuf();
-    }
-    void* p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) return SV_ERR_WORKSPACE;
-    b.ptr = (float*)p;
-    b.bytes = bytes;
-  }
-  *out = b.ptr;
   return SV_OK;
 }
 
@@ -380,12 +417,35 @@ int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target, 
   if (md > 0 && (st = check_lm_shape(hidden_draft, weight_draft, md, V, d_draft)) != SV_OK) return st;
   if (B == 0) return SV_OK;
   if (!uniforms || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SV_ERR_NULL;
-  float* lg = nullptr;
-  st = get_logit_buf((size_t)(mt + md) * (size_t)V * sizeof(float), &lg);
-  if (st != SV_OK) return st;
-  float* lt = lg;
-  float* ld = md > 0 ? lg + (size_t)mt * V : nullptr;
+  int dev = 0;
+  if ((st = current_device(&dev)) != SV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  StreamBufs* b = bufs_for(dev, s);
+  if (!b) return SV_ERR_WORKSPACE;
+  std::lock_guard<std::mutex> lk(b->mu);
+  st = grow(&b->lgt, &b->lgt_bytes, (size_t)(mt + md) * (size_t)V * sizeof(float), s);
+  if (st != SV_OK) return st;
+  float* lt = (float*)b->lgt;
+  float* ld = md > 0 ? lt + (size_t)mt * V : nullptr;
+  VerifyIn in;
+  in.tgt = lt;
+  in.drf = ld;
+  in.X = draft_tokens;
+  in.U = uniforms;
+  in.T = in.Td = temperature;
+  in.top_k = top_k;
+  in.top_p = top_p;
+  in.out_tok = out_tokens;
+  in.out_n = out_num_accepted;
+  in.out_p = out_p;
+  in.out_q = out_q;
+  in.out_z = out_z;
+  in.B = B;
+  in.K = K;
+  in.V = V;
+  in.dtype = SV_F32;
+  Plan p;
+  if ((st = plan_verify(in, &p)) != SV_OK) return st;
   // when timing, the slot's first two events bracket the two projections and
   // the third follows the verification
   ProfSlot* prof = prof_begin();
@@ -394,39 +454,65 @@ int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target, 
   if (md > 0 && launch_lm_gemm(hidden_draft, weight_draft, ld, (int32_t)md, V, d_draft, s) != hipSuccess)
     return SV_ERR_HIP;
   if (prof && hipEventRecord(prof->ev[1], s) != hipSuccess) return SV_ERR_HIP;
-  st = verify_impl(lt, ld, draft_tokens, uniforms, temperature, temperature, top_k, top_p, out_tokens,
-                   out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, SV_F32, stream, nullptr, nullptr,
-                   false, false);
+  st = run_plan_locked(p, b, s, false);
   if (st != SV_OK) return st;
   if (prof) {
     if (hipEventRecord(prof->ev[2], s) != hipSuccess) return SV_ERR_HIP;
-    std::lock_guard<std::mutex> lk(g_prof_mu);
+    std::lock_guard<std::mutex> lk2(g_prof_mu);
     prof->pending = true;
   }
   return SV_OK;
 }
 
+static VerifyIn verify_in(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                          const float* uniforms, float temperature, float draft_temperature, int32_t top_k,
+                          float top_p, int32_t* out_tokens, int32_t* out_num_accepted, double* out_p, double* out_q,
+                          double* out_z, int32_t B, int32_t K, int32_t V, int32_t dtype) {
+  VerifyIn in;
+  in.tgt = target_logits;
+  in.drf = draft_logits;
+  in.X = draft_tokens;
+  in.U = uniforms;
+  in.T = temperature;
+  in.Td = draft_temperature;
+  in.top_k = top_k;
+  in.top_p = top_p;
+  in.out_tok = out_tokens;
+  in.out_n = out_num_accepted;
+  in.out_p = out_p;
+  in.out_q = out_q;
+  in.out_z = out_z;
+  in.B = B;
+  in.K = K;
+  in.V = V;
+  in.dtype = dtype;
+  return in;
+}
+
 int sv_spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                    const float* uniforms, float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
                    int32_t* out_num_accepted, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
-  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, temperature, top_k, top_p,
-                     out_tokens, out_num_accepted, true, nullptr, nullptr, nullptr, nullptr, B, K, V, dtype, stream);
+  return verify_impl(verify_in(target_logits, draft_logits, draft_tokens, uniforms, temperature, temperature, top_k,
+                               top_p, out_tokens, out_num_accepted, nullptr, nullptr, nullptr, B, K, V, dtype),
+                     stream);
 }
 
 int sv_spec_verify_debug(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                          const float* uniforms, float temperature, int32_t top_k, float top_p,
                          int32_t* out_tokens, int32_t* out_num_accepted, double* out_p, double* out_q,
                          double* out_z, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
-  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, temperature, top_k, top_p,
-                     out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream);
+  return verify_impl(verify_in(target_logits, draft_logits, draft_tokens, uniforms, temperature, temperature, top_k,
+                               top_p, out_tokens, out_num_accepted, out_p, out_q, out_z, B, K, V, dtype),
+                     stream);
 }
 
 int sv_spec_verify_dt(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                       const float* uniforms, float temperature, float draft_temperature, int32_t top_k, float top_p,
                       int32_t* out_tokens, int32_t* out_num_accepted, double* out_p, double* out_q, double* out_z,
                       int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
-  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, draft_temperature, top_k,
-                     top_p, out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream);
+  return verify_impl(verify_in(target_logits, draft_logits, draft_tokens, uniforms, temperature, draft_temperature,
+                               top_k, top_p, out_tokens, out_num_accepted, out_p, out_q, out_z, B, K, V, dtype),
+                     stream);
 }
 
 int sv_spec_verify_ragged(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
@@ -435,18 +521,21 @@ int sv_spec_verify_ragged(const void* target_logits, const void* draft_logits, c
                           int32_t* out_num_accepted, double* out_p, double* out_q, double* out_z, int32_t B,
                           int32_t total_draft, int32_t max_k, int32_t V, int32_t dtype, void* stream) {
   const Ragged rg{cu_num_draft, total_draft, max_k};
-  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, draft_temperature, top_k,
-                     top_p, out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, 0, V, dtype, stream,
-                     &rg);
+  VerifyIn in = verify_in(target_logits, draft_logits, draft_tokens, uniforms, temperature, draft_temperature, top_k,
+                          top_p, out_tokens, out_num_accepted, out_p, out_q, out_z, B, 0, V, dtype);
+  in.rg = &rg;
+  return verify_impl(in, stream);
 }
 
 int sv_spec_verify_probs(const void* target_logits, const float* draft_probs, const int32_t* draft_tokens,
                          const float* uniforms, float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
                          int32_t* out_num_accepted, double* out_p, double* out_q, double* out_z, int32_t B, int32_t K,
                          int32_t V, int32_t dtype, void* stream) {
-  return verify_impl(target_logits, nullptr, draft_tokens, uniforms, temperature, temperature, top_k, top_p,
-                     out_tokens, out_num_accepted, true, out_p, out_q, out_z, nullptr, B, K, V, dtype, stream,
-                     nullptr, draft_probs, true);
+  VerifyIn in = verify_in(target_logits, nullptr, draft_tokens, uniforms, temperature, temperature, top_k, top_p,
+                          out_tokens, out_num_accepted, out_p, out_q, out_z, B, K, V, dtype);
+  in.qprob = draft_probs;
+  in.qp = true;
+  return verify_impl(in, stream);
 }
 
 // The draw of a verification with no drafts: each row is a sequence of one
@@ -454,8 +543,11 @@ int sv_spec_verify_probs(const void* target_logits, const float* draft_probs, co
 // its own uniform.
 int sv_sample(const void* logits, const float* uniforms, float temperature, int32_t top_k, float top_p,
               int32_t* out_tokens, double* out_prob, int32_t rows, int32_t V, int32_t dtype, void* stream) {
-  return verify_impl(logits, nullptr, nullptr, uniforms, temperature, temperature, top_k, top_p, out_tokens, nullptr,
-                     false, nullptr, nullptr, nullptr, out_prob, rows, 0, V, dtype, stream);
+  VerifyIn in = verify_in(logits, nullptr, nullptr, uniforms, temperature, temperature, top_k, top_p, out_tokens,
+                          nullptr, nullptr, nullptr, nullptr, rows, 0, V, dtype);
+  in.need_n = false;
+  in.out_px = out_prob;
+  return verify_impl(in, stream);
 }
 
 int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype, float temperature, int32_t top_k,
@@ -478,11 +570,6 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   need.B = rows;
   need.filt = mode != M_PLAIN;
   need.topk = mode == M_TOPK || mode == M_TOPKP;
-
-  char* base = nullptr;
-  Layout L;
-  st = get_scratch(need, &base, &L);
-  if (st != SV_OK) return st;
   Args a = {};
   a.tgt = logits;
   a.out_probs = out_probs;
@@ -494,17 +581,57 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   a.nsc = (int32_t)nsc;
   a.do_seq = 0;
   set_scalars(a, temperature, top_k, top_p, temperature);
-  bind_scratch(a, base, L);
   const bool vec = aligned16(logits) && ((int64_t)V * esz) % 16 == 0;
   a.ulen = vec ? 16 / esz : 1;
   a.dch = make_udiv((uint32_t)a.nchunks);
   a.rps = 1;
   a.drps = make_udiv(1u);
+  int dev = 0;
+  if ((st = current_device(&dev)) != SV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  StreamBufs* b = bufs_for(dev, s);
+  if (!b) return SV_ERR_WORKSPACE;
+  std::lock_guard<std::mutex> lk(b->mu);
+  if ((st = grow(&b->ptr, &b->bytes, make_layout(need).total, s)) != SV_OK) return st;
+  bind_scratch(a, b->ptr, make_layout(need));
   if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (launch_probs(a, dtype, mode, (unsigned)((int64_t)rows * nsc), s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
+}
+
+int sv_init(int device, void* stream, int32_t max_B, int32_t max_K, int32_t max_V, int32_t flags) {
+  if (device < 0 || device >= kMaxDevices) return SV_ERR_PARAM;
+  if (max_B < 0 || max_K < 0 || max_K > SV_MAX_K || max_V < 1 || max_V > MAX_V) return SV_ERR_SHAPE;
+  if (flags & ~SV_INIT_LMHEAD) return SV_ERR_PARAM;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_HIP;
+  if (hipSetDevice(device) != hipSuccess) return SV_ERR_HIP;
+  int st = SV_OK;
+  {
+    // the largest call within the bounds, in every mode: its rows also bound
+    // the sampler's and sv_filtered_probs' rows (each of them a sequence)
+    const int64_t rows = (int64_t)max_B * (2 * (int64_t)max_K + 1);
+    Need need;
+    need.rows = rows;
+    need.nchunks = ((int64_t)max_V + CE - 1) / CE;
+    need.B = rows;
+    need.nseg = (((int64_t)max_V + SCE - 1) / SCE) * SEG_PER_SCE;
+    need.filt = true;
+    need.topk = true;
+    hipStream_t s = (hipStream_t)stream;
+    StreamBufs* b = bufs_for(device, s);
+    if (!b) {
+      st = SV_ERR_WORKSPACE;
+    } else {
+      std::lock_guard<std::mutex> lk(b->mu);
+      st = grow(&b->ptr, &b->bytes, std::max<size_t>(make_layout(need).total, 256), s);
+      if (st == SV_OK && (flags & SV_INIT_LMHEAD))
+        st = grow(&b->lgt, &b->lgt_bytes, std::max<size_t>((size_t)rows * (size_t)max_V * sizeof(float), 256), s);
+    }
+  }
+  if (hipSetDevice(cur) != hipSuccess && st == SV_OK) st = SV_ERR_HIP;
+  return st;
 }
 
 int sv_profile_start(void) {
@@ -531,29 +658,70 @@ int sv_profile_stop(double* stream_kernel_ms, double* other_kernels_ms, int64_t*
   return rc;
 }
 
+// Frees the memory of every (device, stream) set, after synchronising each
+// device that holds one.  The sets themselves stay (empty), so a call that
+// is about to use one allocates afresh.
 int sv_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   int rc = SV_OK;
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_HIP;
-  for (int d = 0; d < kMaxDevices; ++d) {
-    Scratch& s = g_scr[d];
-    LogitBuf& b = g_lgt[d];
-    if (!s.ptr && !b.ptr) continue;
-    if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = SV_ERR_HIP;
-    if (s.ptr && hipFree(s.ptr) != hipSuccess) rc = SV_ERR_HIP;
-    if (b.ptr && hipFree(b.ptr) != hipSuccess) rc = SV_ERR_HIP;
-    s = Scratch();
-    b = LogitBuf();
+  bool synced[kMaxDevices] = {};
+  for (auto& e : g_bufs) {
+    StreamBufs* b = e.second.get();
+    if (!b) continue;
+    std::lock_guard<std::mutex> lb(b->mu);
+    if (!b->ptr && !b->lgt) continue;
+    const int d = e.first.first;
+    if (hipSetDevice(d) != hipSuccess) {
+      rc = SV_ERR_HIP;
+      continue;
+    }
+    if (!synced[d]) {
+      if (hipDeviceSynchronize() != hipSuccess) rc = SV_ERR_HIP;
+      synced[d] = true;
+    }
+    if (b->ptr && hipFree(b->ptr) != hipSuccess) rc = SV_ERR_HIP;
+    if (b->lgt && hipFree(b->lgt) != hipSuccess) rc = SV_ERR_HIP;
+    b->ptr = b->lgt = nullptr;
+    b->bytes = b->lgt_bytes = 0;
   }
   (void)hipSetDevice(cur);
   return rc;
 }
 
+int sv_stream_release(void* stream) {
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != SV_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  StreamBufs* b = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_bufs.find({dev, (uintptr_t)s});
+    if (it == g_bufs.end() || !it->second) return SV_OK;
+    b = it->second.get();
+  }
+  std::lock_guard<std::mutex> lb(b->mu);
+  if (!b->ptr && !b->lgt) return SV_OK;
+  if (hipStreamSynchronize(s) != hipSuccess) return SV_ERR_HIP;
+  if (b->ptr && hipFree(b->ptr) != hipSuccess) st = SV_ERR_HIP;
+  if (b->lgt && hipFree(b->lgt) != hipSuccess) st = SV_ERR_HIP;
+  b->ptr = b->lgt = nullptr;
+  b->bytes = b->lgt_bytes = 0;
+  return st;
+}
+
 int64_t sv_scratch_bytes(int device) {
   if (device < 0 || device >= kMaxDevices) return 0;
   std::lock_guard<std::mutex> lk(g_mu);
-  return (int64_t)(g_scr[device].bytes + g_lgt[device].bytes);
+  int64_t total = 0;
+  for (auto& e : g_bufs) {
+    if (e.first.first != device || !e.second) continue;
+    std::lock_guard<std::mutex> lb(e.second->mu);
+    total += (int64_t)(e.second->bytes + e.second->lgt_bytes);
+  }
+  return total;
 }
 
 const char* sv_status_string(int status) {
@@ -569,6 +737,6 @@ const char* sv_status_string(int status) {
   }
 }
 
-int sv_version(void) { return 100; }
+int sv_version(void) { return 200; }
 
 }  // extern "C"

@@ -134,8 +134,9 @@ struct Args {
   int32_t* kidx;
   double* kprob;
   SeqRec* seq;
-  uint32_t* seq_cnt;  // per-sequence arrival counters (reset to 0 by the last arrival)
+  uint32_t* seq_cnt;  // per-sequence arrival counters (cleared by the call's streaming kernel)
   uint32_t* smp_cnt;
+  int32_t* cflag;     // [1]: ragged offsets valid (written by the streaming kernel)
   double* seg_sum;
   int32_t* seg_last;
   int32_t ulen;   // logits per candidate unit (16-byte vector; 1 on the element-load path)
@@ -473,19 +474,44 @@ __device__ __forceinline__ T ld_dev(const T* p) {
 // Last-arrival detection for a counter shared by `total` workgroups.  Every
 // thread first waits until its own st_dev stores have completed; the barrier
 // then orders all of them before thread 0's increment.  The workgroup that
-// sees the final count reads the others' records with ld_dev, and resets the
-// counter to zero for the next launch.
+// sees the final count reads the others' records with ld_dev.  The counters
+// start every call at zero: the streaming kernel, the call's first launch,
+// clears them (clear_counters).
 __device__ __forceinline__ bool last_arrival(uint32_t* cnt, uint32_t total, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev == total - 1;
-    if (last) st_dev(cnt, 0u);
-    *flag = last;
+    *flag = prev == total - 1;
   }
   __syncthreads();
   return *flag != 0;
+}
+
+// Ragged batches: whether the offsets cu[B + 1] describe a packing of the
+// rows (cu[0] = 0, nondecreasing, every K_b <= Kmax, cu[B] = ND), decided
+// once per call by the streaming kernel's first workgroup and read by the
+// sequence kernel (a.cflag[0]: 1 if they do, 0 if not).
+__device__ __forceinline__ void check_offsets(const Args& a) {
+  if (!a.cu || blockIdx.x != 0) return;
+  bool bad = false;
+  for (int s = (int)threadIdx.x; s <= a.B; s += (int)blockDim.x) {
+    const int c = a.cu[s];
+    const int cn = s < a.B ? a.cu[s + 1] : c;
+    bad |= (s == 0 && c != 0) || (s == a.B && c != a.ND) || (s < a.B && (cn < c || cn - c > a.Kmax));
+  }
+  const int any = __syncthreads_or(bad ? 1 : 0);
+  if (threadIdx.x == 0) a.cflag[0] = any ? 0 : 1;
+}
+
+// The arrival counters of the launches that follow, cleared by the call's
+// streaming kernel (one per sequence; its grid has at least B workgroups):
+// no call depends on what an earlier call left in the scratch.
+__device__ __forceinline__ void clear_counters(const Args& a) {
+  if (threadIdx.x == 0 && (int)blockIdx.x < a.B) {
+    a.seq_cnt[blockIdx.x] = 0u;
+    a.smp_cnt[blockIdx.x] = 0u;
+  }
 }
 
 // Row rl in the order of the packed inputs (every target row, then every
@@ -548,59 +574,6 @@ template <bool RAG>
 __device__ __forceinline__ int seq_row(const Args& a, const SeqGeo& g, int j) {
   if (!RAG) return g.s0 + j;
   return j <= g.K ? g.t0 + j : a.NT + g.x0 + (j - g.K - 1);
-}
-
-// Where row rl lies: its sequence b, its position i within the sequence's
-// target (0..K_b) or draft (0..K_b - 1) rows, K_b and x0(b).  bad: the ragged
-// offsets do not describe a packing of the rows (cu[0] != 0, a K_b outside
-// [0, Kmax], or cu[B] != ND); every wave of a workgroup reaches the same
-// answer.  Ragged batches: each lane scans entries lane, lane + 64, ... of
-// cu; b is the number of sequences after the first whose first row (of the
-// same kind) is at or before rl, which the monotone offsets make exact.
-struct RowLoc {
-  int b, i, K, x0;
-  bool draft, bad;
-};
-template <bool RAG>
-__device__ __forceinline__ RowLoc row_loc(const Args& a, int rl) {
-  RowLoc L;
-  L.bad = false;
-  if (!RAG) {
-    L.b = udiv(rl, a.drps);
-    const int j = rl - L.b * a.rps;
-    L.draft = j > a.K;
-    L.i = L.draft ? j - a.K - 1 : j;
-    L.K = a.K;
-    L.x0 = L.b * a.K;
-    return L;
-  }
-  L.draft = rl >= a.NT;
-  const int r = L.draft ? rl - a.NT : rl;
-  int cnt = 0, lo = 0, hi = INT_MAX;
-  bool bad = false;
-  for (int s = (int)(threadIdx.x & 63); s <= a.B; s += 64) {
-    const int c = a.cu[s];
-    const int cn = s < a.B ? a.cu[s + 1] : c;
-    bad |= (s == 0 && c != 0) || (s == a.B && c != a.ND) || (s < a.B && (cn < c || cn - c > a.Kmax));
-    const int st = L.draft ? c : c + s;
-    if (s >= 1 && s < a.B && st <= r) {
-      ++cnt;
-      lo = max(lo, st);
-    }
-    if (s >= 1 && st > r) hi = min(hi, st);
-  }
-  L.bad = __ballot(bad) != 0ull;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    cnt += __shfl_xor(cnt, o);
-    lo = max(lo, __shfl_xor(lo, o));
-    hi = min(hi, __shfl_xor(hi, o));
-  }
-  L.b = cnt;
-  L.i = r - lo;
-  L.K = L.draft ? hi - lo : hi - lo - 1;
-  L.x0 = L.draft ? lo : lo - cnt;
-  return L;
 }
 
 }  // namespace sv

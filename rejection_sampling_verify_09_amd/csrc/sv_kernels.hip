@@ -67,6 +67,13 @@ struct DrawRow {
   const float* prob;  // a row given as probabilities (then the fields above are unused), or null
 };
 
+// Where a merge writes its row's kept list: sink.put(nk, pos, index,
+// probability) for each of the nk kept tokens, at its position in ascending
+// index order.  Merges of rows that belong to no sequence keep no list.
+struct NoSink {
+  __device__ __forceinline__ void put(int, int, int32_t, double) const {}
+};
+
 struct SmemStream {
   uint64_t cand[NWAVE * CAND_CAP];  // per-wave candidate lists (one flat list after an overflow cut)
   uint64_t tk[WG];
@@ -108,7 +115,7 @@ struct Smem {
     SmemStream s;
     SmemRow r;
     SmemSeq q;
-    double scan[WG];
+    double scan[1024];  // one per thread of the largest workgroup (the sequence kernel's)
   };
   Red red;
   DrawRow dr[2];
@@ -364,8 +371,8 @@ __device__ void sort_keys_desc(int n, Smem& sm) {
 // Top-k / top-p threshold of one row and its kept list.  On entry the chunk
 // records are in sm.r (cm, cb, cn) and the row is valid (finite max m;
 // for top-p also a finite normaliser rr.S).
-template <int DT, int MODE, int BS>
-__device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRec& rr, Smem& sm) {
+template <int DT, int MODE, int BS, class Sink>
+__device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRec& rr, Smem& sm, const Sink& sink) {
   static_assert(ROW_CAND % BS == 0 && ROW_CAND <= 4 * BS, "top-p scan holds ROW_CAND / BS entries per thread");
   const int t = threadIdx.x, nch = a.nchunks;
   const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
@@ -576,10 +583,8 @@ __device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRe
     __syncthreads();
     if (t < nk) {
       const uint64_t f = sm.r.keys[t];
-      const int idx = (int)~(uint32_t)(f >> 32);
       const float x = key_val((uint32_t)f);
-      st_dev(&a.kidx[(size_t)rl * KEEP_CAP + t], idx);
-      st_dev(&a.kprob[(size_t)rl * KEEP_CAP + t], exp(((double)x - (double)m) * invT) / skept);
+      sink.put(nk, t, (int)~(uint32_t)(f >> 32), exp(((double)x - (double)m) * invT) / skept);
     }
   }
   rr.tau = tau;
@@ -612,8 +617,8 @@ __device__ __forceinline__ RowRec load_row(const RowRec* p) {
   return r;
 }
 
-template <int DT, int MODE, int BS>
-__device__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
+template <int DT, int MODE, int BS, class Sink>
+__device__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm, const Sink& sink) {
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x, nch = a.nchunks;
@@ -657,7 +662,7 @@ __device__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm) {
     rr.arg = best == INT_MAX ? 0 : best;
   }
   if (FILT) {
-    if (!bad) filter_row<DT, MODE, BS>(a, rl, rp, m, rr, sm);
+    if (!bad) filter_row<DT, MODE, BS>(a, rl, rp, m, rr, sm, sink);
   }
   if (!bad && hx) {
     if (MODE == M_GREEDY) {
@@ -971,6 +976,8 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, false>())) stream_ke
   const int c0 = (item - rl * a.nchunks) * CE;
   const int cn = min(CE, a.V - c0);
   const char* rp = row_ptr(a, rl, ESZ);
+  clear_counters(a);
+  check_offsets(a);
   float v[EPT];
   load_chunk<DT, false>(rp, c0, cn, v);
   // units are single logits here: the unit maxima are v itself
@@ -1172,6 +1179,8 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_ker
   const int cn = min(CE, a.V - c0);
   ChunkRaw<DT> cr;
   issue_chunk<DT>(a, rl, c0, cn, cr);
+  clear_counters(a);
+  check_offsets(a);
   stream_vec_body<DT, MODE>(a, item, rl, c0, cn, cr, sm);
 }
 
@@ -1226,7 +1235,6 @@ struct WaveRowSm {
       unsigned long long ws[64];
     } cut;
   };
-  int32_t off[MAX_CHUNKS + 1];     // candidate offsets of the row's chunks
 };
 
 // Largest key t among the wave's entries (key ek, weight wt; weight 0 = no
@@ -1387,8 +1395,9 @@ __device__ __forceinline__ uint32_t wave_walk64(uint32_t k, unsigned long long w
 // token, and the row record.  Returns false, having written nothing, when the
 // candidate lists cannot decide the threshold this way (the block-level merge
 // then takes the row).
-template <int DT, int MODE>
-__device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, RowRec& rr) {
+template <int DT, int MODE, class Sink>
+__device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, RowRec& rr,
+                                         const Sink& sink) {
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int lane = threadIdx.x & 63, nch = a.nchunks;
   const ChunkRec* cr = a.chunk + (size_t)rl * nch;
@@ -1657,12 +1666,8 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       for (int r = 0; r < WR_EPL; ++r) pos[r] += kj < ei[r] ? 1 : 0;
     }
 #pragma unroll
-    for (int r = 0; r < WR_EPL; ++r) {
-      if (kp[r]) {
-        st_dev(&a.kidx[(size_t)rl * KEEP_CAP + pos[r]], ei[r]);
-        st_dev(&a.kprob[(size_t)rl * KEEP_CAP + pos[r]], ew[r] / skept);
-      }
-    }
+    for (int r = 0; r < WR_EPL; ++r)
+      if (kp[r]) sink.put(nk, pos[r], ei[r], ew[r] / skept);
     rr.tau = tau;
     rr.S_kept = skept;
     rr.nkept = nk;
@@ -1679,30 +1684,31 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
   return true;
 }
 
-// Kept lists read ahead at a sequence's finish: the first 64 entries of each
-// of up to SPEC_ROWS rows.
-constexpr int SPEC_ROWS = 16;
-struct SpecLists {
-  int32_t idx[SPEC_ROWS][64];
-  double prob[SPEC_ROWS][64];
-};
-
+// Row merges without sequences (sv_filtered_probs): one workgroup per row,
+// its first wave merges the row (wave_row); when the candidate lists cannot
+// decide the cut the whole block merges it (row_finalize).  Only the row
+// records are kept (the probabilities kernel reads them).
 struct RowKSm {
   union {
-    WaveRowSm w;     // wave-level merge
-    Smem blk;        // block-level merge, list copies and full-row draw
-    SpecLists spec;  // kept lists read with the sequence's records
+    WaveRowSm w;  // wave-level merge
+    Smem blk;     // block-level merge
   };
-  double px[MAX_RPS];  // p or q of each row's drafted token
-  int32_t rf[MAX_RPS];
-  int32_t nk[MAX_RPS];
-  int32_t arg[MAX_RPS];
-  int32_t x[MAX_K];
-  float u[MAX_K + 1];
-  float rm[MAX_RPS];   // row maxima and normalisers (unfiltered rows: for the draw)
-  double rs[MAX_RPS];
-  int32_t fast, big, n, flag;
+  int32_t fast;
 };
+
+template <int DT, int MODE>
+__global__ void __launch_bounds__(WG) row_kernel(Args a) {
+  __shared__ RowKSm sm;
+  const int t = threadIdx.x;
+  const int rl = (int)blockIdx.x;
+  if (t < 64) {
+    RowRec rr;
+    const bool ok = wave_row<DT, MODE>(a, rl, -1, sm.w, rr, NoSink{});
+    if (t == 0) sm.fast = ok;
+  }
+  __syncthreads();
+  if (!sm.fast) (void)row_finalize<DT, MODE, WG>(a, rl, -1, sm.blk, NoSink{});
+}
 
 // Final draw from kept lists by one wave (filtered rows): residual
 // max(0, p - q) over the target's kept tokens, or p itself (bonus, or an
@@ -1804,7 +1810,7 @@ __device__ int wave_list_sample(double u, const int32_t* pidx, const double* ppr
 // workgroup; its uniform-indexed outputs only (out_p and out_q are left).
 __device__ void sentinel_seq(const Args& a, int b, int t) {
   const double nanv = __longlong_as_double(0x7FF8000000000000ll);
-  for (int j = t; j <= a.Kmax; j += WG) a.out_tok[(size_t)b * (a.Kmax + 1) + j] = -1;
+  for (int j = t; j <= a.Kmax; j += blockDim.x) a.out_tok[(size_t)b * (a.Kmax + 1) + j] = -1;
   if (t == 0) {
     if (a.out_n) a.out_n[b] = -1;
     if (a.out_z) a.out_z[b] = nanv;
@@ -1816,85 +1822,147 @@ __device__ void sentinel_seq(const Args& a, int b, int t) {
   }
 }
 
-// One workgroup per row.  Its first wave merges the row (wave_row: one round
-// trip for the chunk records and most candidate units, one to read the units
-// back); when the lists cannot decide the cut the whole block merges it
-// (row_finalize).  The last row of a sequence to be merged then runs, on its
-// first wave, the accept tests, the first-rejection scan and the draw from the
-// kept lists (the whole block draws from full rows when a kept set is too
-// large for a list; unfiltered rows: the sampling kernel draws afterwards).
-// With do_seq == 0 (filtered probabilities) only the merges run.
-// LAY (BatchLayout): rectangular, ragged, or rectangular with q given as
-// probabilities (no draft rows: each target row i < K reads q(x_i) from the
-// given row, and the residual draw reads q at the target's kept tokens).
+// ---------------------------------------------------------------------------
+// sequence kernel: one workgroup per sequence merges all of the sequence's
+// rows at once (one wave per row) and then runs its accept tests, its
+// first-rejection scan and its draw, with everything in the workgroup's LDS
+// ---------------------------------------------------------------------------
+constexpr int SQ_WAVES = 16;              // waves of a sequence workgroup (rows merged at once)
+constexpr int SQ_BS = SQ_WAVES * 64;      // its threads
+constexpr int SQ_SLOTS = SQ_WAVES;        // rows whose kept lists can stay in LDS
+constexpr int SQ_SLOT_CAP = 64;           // ... when they have at most this many entries
+static_assert(SQ_BS <= 1024, "Smem.scan holds one entry per thread");
+
+struct SeqKSm {
+  union {
+    WaveRowSm w[SQ_WAVES];  // the waves' row merges
+    Smem blk;               // block-level merge, list copies and full-row draw
+  };
+  int32_t kidx[SQ_SLOTS][SQ_SLOT_CAP];
+  double kprob[SQ_SLOTS][SQ_SLOT_CAP];
+  // per row of the sequence: target rows 0..K, then draft rows K+1..2K (with
+  // q given as probabilities, slot K+1+i holds the given q(x_i))
+  double px[MAX_RPS];   // p or q of the row's drafted token
+  double rs[MAX_RPS];   // full-row normaliser (unfiltered rows: for the draw)
+  float rm[MAX_RPS];    // row maximum
+  int32_t rf[MAX_RPS];  // row flags
+  int32_t nk[MAX_RPS];  // kept-list length (-1: too large for a list)
+  int32_t arg[MAX_RPS]; // greedy arg-max
+  int32_t x[MAX_K];
+  float u[MAX_K + 1];
+  uint32_t fail[(MAX_RPS + 31) / 32];  // rows the waves could not merge from the candidate lists
+  int32_t n, big;
+};
+
+// The kept list of the sequence's row j: in the workgroup's LDS slot j when
+// j < SQ_SLOTS and the list has at most SQ_SLOT_CAP entries, otherwise in the
+// row's scratch list (read back by the same workgroup only).
+struct SeqSink {
+  SeqKSm& sm;
+  int j;
+  int32_t* gidx;
+  double* gprob;
+  __device__ __forceinline__ void put(int nk, int pos, int32_t idx, double prob) const {
+    if (j < SQ_SLOTS && nk <= SQ_SLOT_CAP) {
+      sm.kidx[j][pos] = idx;
+      sm.kprob[j][pos] = prob;
+    } else {
+      gidx[pos] = idx;
+      gprob[pos] = prob;
+    }
+  }
+};
+__device__ __forceinline__ SeqSink seq_sink(const Args& a, SeqKSm& sm, int j, int rl) {
+  return SeqSink{sm, j, a.kidx + (size_t)rl * KEEP_CAP, a.kprob + (size_t)rl * KEEP_CAP};
+}
+
+// One workgroup of SQ_BS threads per sequence.  Wave w merges the
+// sequence's rows w, w + SQ_WAVES, ... (wave_row: the chunk records and most
+// candidate units in one round trip, the units' logits in a second); a row
+// the lists cannot decide is merged afterwards by the whole workgroup
+// (row_finalize).  Then the first wave runs the accept tests, the
+// first-rejection scan and the draw from the kept lists (from full rows,
+// by the whole workgroup, when a kept set is too large for a list;
+// unfiltered rows: the sampling kernel draws afterwards).  No data passes
+// between workgroups.
+// LAY (BatchLayout): rectangular, ragged (offsets validated by the streaming
+// kernel's first workgroup), or rectangular with q given as probabilities
+// (no draft rows: each target row i < K reads the given q(x_i), and the
+// residual draw reads q at the target's kept tokens).
 template <int DT, int MODE, int LAY>
-__global__ void __launch_bounds__(WG) row_kernel(Args a) {
-  __shared__ RowKSm sm;
+__global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
+  __shared__ SeqKSm sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   constexpr bool RAG = LAY == LAY_RAG, QP = LAY == LAY_QP;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  const int rl = (int)blockIdx.x;
-  const RowLoc loc = a.do_seq ? row_loc<RAG>(a, rl) : RowLoc{rl, 0, 0, 0, false, false};
-  if (loc.bad) {
-    // offsets that describe no packing: every sequence is a sentinel, and no
-    // row or sequence record is used
-    if (rl < a.B) sentinel_seq(a, rl, t);
+  const int b = (int)blockIdx.x;
+  if (RAG && a.cflag[0] == 0) {
+    // offsets that describe no packing: every sequence is a sentinel
+    sentinel_seq(a, b, t);
     return;
   }
-  const int b = loc.b;
-  const int xtok = (a.do_seq && loc.i < loc.K) ? a.X[(size_t)loc.x0 + loc.i] : -1;
-  // q(x_i) from the given draft row (needed only at the sequence's finish)
-  const float qx = (QP && xtok >= 0 && xtok < a.V) ? a.qprob[(size_t)(loc.x0 + loc.i) * a.V + xtok] : 0.0f;
-  if (w == 0) {
-    RowRec rr;
-    const bool ok = wave_row<DT, MODE>(a, rl, xtok, sm.w, rr);
-    if (lane == 0) sm.fast = ok;
-  }
-  __syncthreads();
-  if (!sm.fast) (void)row_finalize<DT, MODE, WG>(a, rl, xtok, sm.blk);
-  const int K = loc.K;
+  const SeqGeo g = seq_geo<RAG>(a, b);
+  const int K = g.K;
   const int rps = (MODE == M_GREEDY || QP) ? K + 1 : 2 * K + 1;
-  if (QP && t == 0) st_dev(&a.qxs[rl], qx);
-  if (!a.do_seq || !last_arrival(&a.seq_cnt[b], (uint32_t)rps, &sm.flag)) return;
-
-  // ---- the sequence: its rows' records, drafted tokens and uniforms, and
-  // (up to SPEC_ROWS rows) the head of every row's kept list: one round trip
-  const SeqGeo g{K, loc.x0 + b, loc.x0, b * a.rps};
-  const bool spec = FILT && rps <= SPEC_ROWS;
-  int32_t si[SPEC_ROWS / NWAVE];
-  double sp[SPEC_ROWS / NWAVE];
-  if (spec) {
-#pragma unroll
-    for (int i = 0; i < SPEC_ROWS / NWAVE; ++i) {
-      const size_t o = (size_t)seq_row<RAG>(a, g, min(w + NWAVE * i, rps - 1)) * KEEP_CAP + lane;
-      si[i] = ld_dev(&a.kidx[o]);
-      sp[i] = ld_dev(&a.kprob[o]);
-    }
-  }
-  for (int j = t; j < rps; j += WG) {
-    const RowRec* rj = a.row + seq_row<RAG>(a, g, j);
-    sm.px[j] = ld_dev(&rj->px);
-    sm.rf[j] = ld_dev(&rj->flags);
-    sm.nk[j] = ld_dev(&rj->nkept);
-    sm.arg[j] = ld_dev(&rj->arg);
-    if (MODE == M_PLAIN) {
-      sm.rm[j] = ld_dev(&rj->m);
-      sm.rs[j] = ld_dev(&rj->S);
-    }
-    // q(x_j) in the draft rows' slots
-    if (QP && j < K) sm.px[K + 1 + j] = (double)ld_dev(&a.qxs[seq_row<RAG>(a, g, j)]);
+  // rows j >= SQ_WAVES (sequences of more than SQ_WAVES rows) are merged by
+  // the whole workgroup below, one after another
+  if (t < (MAX_RPS + 31) / 32) {
+    const int j0 = 32 * t;
+    sm.fail[t] = j0 >= SQ_WAVES ? ~0u : (SQ_WAVES - j0 >= 32 ? 0u : ~0u << (SQ_WAVES - j0));
   }
   if (t < K) sm.x[t] = a.X[(size_t)g.x0 + t];
-  if (t <= K) sm.u[t] = a.U[(size_t)g.t0 + t];
-  if (spec) {
-#pragma unroll
-    for (int i = 0; i < SPEC_ROWS / NWAVE; ++i) {
-      sm.spec.idx[w + NWAVE * i][lane] = si[i];
-      sm.spec.prob[w + NWAVE * i][lane] = sp[i];
+  if (t >= 256 && t - 256 <= K) sm.u[t - 256] = a.U[(size_t)g.t0 + (t - 256)];
+  __syncthreads();
+
+  // ---- the sequence's rows, one wave each (a loop here would keep values
+  // across its iterations and spill registers)
+  if (w < rps) {
+    const int j = w;
+    const int rl = seq_row<RAG>(a, g, j);
+    const int i = j <= K ? j : j - K - 1;  // position of the row
+    const int xtok = i < K ? sm.x[i] : -1;
+    RowRec rr;
+    const bool ok = wave_row<DT, MODE>(a, rl, xtok, sm.w[w], rr, seq_sink(a, sm, j, rl));
+    if (lane == 0) {
+      if (ok) {
+        sm.px[j] = rr.px;
+        sm.rf[j] = rr.flags;
+        sm.nk[j] = rr.nkept;
+        sm.arg[j] = rr.arg;
+        sm.rm[j] = rr.m;
+        sm.rs[j] = rr.S;
+      } else {
+        atomicOr(&sm.fail[j >> 5], 1u << (j & 31));
+      }
+      // q(x_i) from the given draft row
+      if (QP && i < K && j <= K)
+        sm.px[K + 1 + i] = (xtok >= 0 && xtok < a.V) ? (double)a.qprob[(size_t)(g.x0 + i) * a.V + xtok] : 0.0;
     }
   }
+  // the kept lists written to the scratch are read back by this workgroup only
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // ---- rows the candidate lists could not decide: the whole workgroup
+  for (int j = 0; j < rps; ++j) {
+    if (!(sm.fail[j >> 5] & (1u << (j & 31)))) continue;  // uniform
+    const int rl = seq_row<RAG>(a, g, j);
+    const int i = j <= K ? j : j - K - 1;
+    const int xtok = i < K ? sm.x[i] : -1;
+    const RowRec rr = row_finalize<DT, MODE, SQ_BS>(a, rl, xtok, sm.blk, seq_sink(a, sm, j, rl));
+    if (t == 0) {
+      sm.px[j] = rr.px;
+      sm.rf[j] = rr.flags;
+      sm.nk[j] = rr.nkept;
+      sm.arg[j] = rr.arg;
+      sm.rm[j] = rr.m;
+      sm.rs[j] = rr.S;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // ---- the sequence
   if (w == 0) {
     // accept tests: draft i is accepted iff u_i * q_i(x_i) < p_i(x_i)
     bool rej = false, badx = false;
@@ -1953,34 +2021,37 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
       if (np < 0 || (res && nq < 0)) {
         big = 1;
       } else {
-        const int32_t *pidx, *qidx;
-        const double *pprob, *qprob;
-        if (spec && np <= 64 && nq <= 64) {
-          // read ahead with the records
-          pidx = sm.spec.idx[n];
-          pprob = sm.spec.prob[n];
-          qidx = QP ? pidx : sm.spec.idx[jq];
-          qprob = QP ? pprob : sm.spec.prob[jq];
-        } else {
-          // the two kept lists (one round trip)
-          SmemSeq& q = sm.blk.q;
-          const size_t op = (size_t)seq_row<RAG>(a, g, n) * KEEP_CAP, oq = (size_t)seq_row<RAG>(a, g, jq) * KEEP_CAP;
+        // each list from its LDS slot, or copied from the scratch (one round trip)
+        SmemSeq& q = sm.blk.q;
+        const int32_t* pidx = sm.kidx[n < SQ_SLOTS ? n : 0];
+        const double* pprob = sm.kprob[n < SQ_SLOTS ? n : 0];
+        const int32_t* qidx = sm.kidx[jq < SQ_SLOTS ? jq : 0];
+        const double* qprob = sm.kprob[jq < SQ_SLOTS ? jq : 0];
+        const bool pg = !(n < SQ_SLOTS && np <= SQ_SLOT_CAP);
+        const bool qg = res && !QP && !(jq < SQ_SLOTS && nq <= SQ_SLOT_CAP);
+        if (pg) {
+          const size_t op = (size_t)seq_row<RAG>(a, g, n) * KEEP_CAP;
           for (int e = lane; e < np; e += 64) {
             q.pidx[e] = ld_dev(&a.kidx[op + e]);
             q.pprob[e] = ld_dev(&a.kprob[op + e]);
           }
-          if (res && !QP) {
-            for (int e = lane; e < nq; e += 64) {
-              q.qidx[e] = ld_dev(&a.kidx[oq + e]);
-              q.qprob[e] = ld_dev(&a.kprob[oq + e]);
-            }
-          }
-          wave_sync();
           pidx = q.pidx;
           pprob = q.pprob;
+        }
+        if (qg) {
+          const size_t oq = (size_t)seq_row<RAG>(a, g, jq) * KEEP_CAP;
+          for (int e = lane; e < nq; e += 64) {
+            q.qidx[e] = ld_dev(&a.kidx[oq + e]);
+            q.qprob[e] = ld_dev(&a.kprob[oq + e]);
+          }
           qidx = q.qidx;
           qprob = q.qprob;
         }
+        if (QP) {
+          qidx = pidx;
+          qprob = pprob;
+        }
+        wave_sync();
         double Z, wtok;
         const float* qrow = QP ? a.qprob + (size_t)(g.x0 + n) * a.V : nullptr;
         const int tok = wave_list_sample((double)sm.u[K], pidx, pprob, np, qidx, qprob, nq, res, &Z, &wtok, qrow);
@@ -1998,7 +2069,7 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   }
   __syncthreads();
   if (FILT && sm.big) {
-    // a kept set too large for a list: the whole block draws from the full rows
+    // a kept set too large for a list: the whole workgroup draws from the full rows
     const int n = sm.n;
     const bool res = n < K;
     const int jq = res ? K + 1 + n : n;
@@ -2007,8 +2078,8 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
     if (QP) set_draw_prob_row(a.qprob + (size_t)(g.x0 + (res ? n : 0)) * a.V, 1, sm.blk);
     else set_draw_row(&a.row[rq], true, 1, row_temp(a, rq).invT, sm.blk);
     double Z;
-    const int tok = full_row_sample<DT, WG>(a, (double)sm.u[K], row_ptr(a, rn, ESZ), row_ptr(a, rq, ESZ), res,
-                                            sm.blk, &Z);
+    const int tok = full_row_sample<DT, SQ_BS>(a, (double)sm.u[K], row_ptr(a, rn, ESZ), row_ptr(a, rq, ESZ), res,
+                                               sm.blk, &Z);
     if (t == 0) {
       a.out_tok[(size_t)b * (a.Kmax + 1) + n] = tok;
       if (a.out_z) a.out_z[b] = Z;
@@ -2250,23 +2321,33 @@ static KFn pick_stream_mode(int mode, bool vec) {
 }
 
 template <int DT, int LAY>
-static KFn pick_row(int mode) {
+static KFn pick_seq(int mode) {
   switch (mode) {
-    case M_PLAIN: return (KFn)row_kernel<DT, M_PLAIN, LAY>;
-    case M_TOPK: return (KFn)row_kernel<DT, M_TOPK, LAY>;
-    case M_TOPP: return (KFn)row_kernel<DT, M_TOPP, LAY>;
-    case M_TOPKP: return (KFn)row_kernel<DT, M_TOPKP, LAY>;
-    default: return (KFn)row_kernel<DT, M_GREEDY, LAY>;
+    case M_PLAIN: return (KFn)seq_kernel<DT, M_PLAIN, LAY>;
+    case M_TOPK: return (KFn)seq_kernel<DT, M_TOPK, LAY>;
+    case M_TOPP: return (KFn)seq_kernel<DT, M_TOPP, LAY>;
+    case M_TOPKP: return (KFn)seq_kernel<DT, M_TOPKP, LAY>;
+    default: return (KFn)seq_kernel<DT, M_GREEDY, LAY>;
   }
 }
 
 template <int DT>
-static KFn pick_row_lay(int mode, int lay) {
-  return lay == LAY_RAG ? pick_row<DT, LAY_RAG>(mode) : lay == LAY_QP ? pick_row<DT, LAY_QP>(mode)
-                                                                      : pick_row<DT, LAY_RECT>(mode);
+static KFn pick_seq_lay(int mode, int lay) {
+  return lay == LAY_RAG ? pick_seq<DT, LAY_RAG>(mode) : lay == LAY_QP ? pick_seq<DT, LAY_QP>(mode)
+                                                                      : pick_seq<DT, LAY_RECT>(mode);
 }
 
 static int layout_of(const Args& a) { return a.cu ? LAY_RAG : a.qprob ? LAY_QP : LAY_RECT; }
+
+template <int DT>
+static KFn pick_row(int mode) {
+  switch (mode) {
+    case M_PLAIN: return (KFn)row_kernel<DT, M_PLAIN>;
+    case M_TOPK: return (KFn)row_kernel<DT, M_TOPK>;
+    case M_TOPP: return (KFn)row_kernel<DT, M_TOPP>;
+    default: return (KFn)row_kernel<DT, M_TOPKP>;
+  }
+}
 
 template <int DT>
 static KFn pick_probs(int mode) {
@@ -2291,10 +2372,18 @@ hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned 
   return hipGetLastError();
 }
 
+// Row merges without sequences (sv_filtered_probs): one workgroup per row.
 hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
-  const int lay = layout_of(a);
-  KFn f = dtype == D_BF16 ? pick_row_lay<D_BF16>(mode, lay) : pick_row_lay<D_F32>(mode, lay);
+  KFn f = dtype == D_BF16 ? pick_row<D_BF16>(mode) : pick_row<D_F32>(mode);
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
+  return hipGetLastError();
+}
+
+// The sequences: one workgroup of SQ_BS threads per sequence.
+hipError_t launch_seq(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
+  const int lay = layout_of(a);
+  KFn f = dtype == D_BF16 ? pick_seq_lay<D_BF16>(mode, lay) : pick_seq_lay<D_F32>(mode, lay);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(SQ_BS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
     for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_spec_verify_dt", "sv_spec_verify_ragged",
               "sv_spec_verify_probs", "sv_lm_logits", "sv_spec_verify_lmhead",
               "sv_filtered_probs", "sv_sample", "sv_dynk_create", "sv_dynk_observe", "sv_dynk_k", "sv_dynk_destroy",
-              "sv_release", "sv_scratch_bytes",
+              "sv_release", "sv_scratch_bytes", "sv_init", "sv_stream_release",
               "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
         assert s in syms
 
@@ -281,3 +281,13 @@ def test_lm_bindings_check_their_arguments_before_any_call():
     with pytest.raises(ValueError):  # draft rows of the wrong count
         spec_verify_lmhead(torch.zeros((1, 3, 64), dtype=torch.bfloat16), w,
                            torch.zeros((1, 3, 64), dtype=torch.bfloat16), w, x, u, 1.0)
+
+
+def test_init_validation():
+    lib = L.lib()
+    assert lib.sv_init(-1, None, 64, 6, 128256, 0) == L.SV_ERR_PARAM
+    assert lib.sv_init(64, None, 64, 6, 128256, 0) == L.SV_ERR_PARAM
+    assert lib.sv_init(0, None, -1, 6, 128256, 0) == L.SV_ERR_SHAPE
+    assert lib.sv_init(0, None, 64, L.SV_MAX_K + 1, 128256, 0) == L.SV_ERR_SHAPE
+    assert lib.sv_init(0, None, 64, 6, 0, 0) == L.SV_ERR_SHAPE
+    assert lib.sv_init(0, None, 64, 6, 128256, 2) == L.SV_ERR_PARAM

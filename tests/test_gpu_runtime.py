@@ -129,3 +129,117 @@ def test_small_batch_after_large_batch_rectangular_and_ragged():
         tok, n, dbg = run_device_ragged(wr, r, xr, w.K)
         stats, fails = compare_ragged(wr, r, xr, w.K, tok, n, dbg)
         assert stats["fail"] == 0 and stats["flagged"] == 0, fails[:3]
+
+
+def _expected(w, d, x):
+    """The oracle's results for a batch (all sequences must match exactly:
+    the batches used here have no near-tie)."""
+    return oracle.verify(d["target"], d["draft"], x, d["uniforms"], w.temperature, w.top_k, w.top_p, dtype=w.dtype)
+
+
+def test_concurrent_streams_match_the_oracle():
+    """Two streams of default priority verify different batches at the same
+    time, with no ordering between them (each stream has its own scratch):
+    every call on both equals the oracle."""
+    import torch
+
+    from rejection_sampling_verify_09_amd import spec_verify
+
+    ws = [WORKLOADS["b64-k6-v128256-bf16-zipf-t0.7-topp0.9"], WORKLOADS["b32-k6-v128256-bf16-normal-s0.6"]]
+    batches = []
+    for w in ws:
+        d = make_inputs(w)
+        x = draft_tokens_for(w, d)
+        ref_tok, ref_n = _expected(w, d, x)
+        batches.append((w, _dev_inputs(w, d, x), ref_tok, ref_n))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    reps = 12
+    outs = [[], []]
+    for r in range(reps):
+        for i, (w, (tgt, drf, X, U), _, _) in enumerate(batches):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(spec_verify(tgt, drf, X, U, w.temperature, w.top_k, w.top_p, stream=streams[i]))
+    torch.cuda.synchronize()
+    for i, (w, _, ref_tok, ref_n) in enumerate(batches):
+        log(f"[streams] {w.name}: {reps} calls on stream {i}")
+        for tok, n in outs[i]:
+            assert np.array_equal(n.cpu().numpy(), ref_n) and np.array_equal(tok.cpu().numpy(), ref_tok)
+
+
+def test_concurrent_host_threads_on_their_own_streams():
+    """Two host threads, each with its own stream and batch, calling at the
+    same time: both match the oracle."""
+    import threading
+
+    import torch
+
+    from rejection_sampling_verify_09_amd import spec_verify
+
+    ws = [WORKLOADS["b8-k5-v32000-f32-zipf"], WORKLOADS["b64-k6-v128256-bf16-zipf-t0.7-topp0.9"]]
+    res, errs = {}, []
+
+    def work(i, w, d, x):
+        try:
+            torch.cuda.set_device(0)
+            s = torch.cuda.Stream()
+            tgt, drf, X, U = _dev_inputs(w, d, x)
+            s.wait_stream(torch.cuda.current_stream())
+            outs = []
+            with torch.cuda.stream(s):
+                for _ in range(10):
+                    outs.append(spec_verify(tgt, drf, X, U, w.temperature, w.top_k, w.top_p, stream=s))
+            s.synchronize()
+            res[i] = [(t.cpu().numpy(), n.cpu().numpy()) for t, n in outs]
+        except Exception as e:  # reported below
+            errs.append(repr(e))
+
+    inputs = []
+    for w in ws:
+        d = make_inputs(w)
+        inputs.append((w, d, draft_tokens_for(w, d)))
+    th = [threading.Thread(target=work, args=(i, *inp)) for i, inp in enumerate(inputs)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join(timeout=120)
+    assert not errs, errs
+    for i, (w, d, x) in enumerate(inputs):
+        ref_tok, ref_n = _expected(w, d, x)
+        log(f"[threads] {w.name}: {len(res[i])} calls")
+        for tok, n in res[i]:
+            assert np.array_equal(n, ref_n) and np.array_equal(tok, ref_tok)
+
+
+def test_init_sizes_the_stream_scratch_once():
+    """After sv_init on a stream, calls within its bounds (every variant and
+    mode) leave the library's scratch unchanged: no allocation."""
+    import torch
+
+    from rejection_sampling_verify_09_amd import init, sample, scratch_bytes, spec_verify, stream_release
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    init(64, 8, 152064, stream=s)
+    held = scratch_bytes()
+    log(f"[init] scratch after sv_init: {held} bytes")
+    cases = [WORKLOADS["b64-k6-v128256-bf16-zipf-t0.7-topp0.9"], WORKLOADS["b8-k5-v32000-f32-zipf"],
+             WORKLOADS["b32-k6-v128256-bf16-normal-greedy"],
+             Workload("b16-k8-v152064-topk", 16, 8, 152064, "f32", "peaked", 2.5, 0.6, 1.0, 50, 1.0, 3)]
+    with torch.cuda.stream(s):
+        for w in cases:
+            d = make_inputs(w)
+            x = draft_tokens_for(w, d)
+            tgt, drf, X, U = _dev_inputs(w, d, x)
+            tok, n = spec_verify(tgt, drf, X, U, w.temperature, w.top_k, w.top_p, stream=s)
+            s.synchronize()
+            ref_tok, ref_n = _expected(w, d, x)
+            assert np.array_equal(n.cpu().numpy(), ref_n) and np.array_equal(tok.cpu().numpy(), ref_tok)
+            rows = drf.reshape(-1, w.V)
+            sample(rows, torch.rand(rows.shape[0], device="cuda"), max(w.temperature, 0.5), w.top_k, w.top_p,
+                   stream=s)
+            s.synchronize()
+            assert scratch_bytes() == held, (w.name, scratch_bytes(), held)
+    stream_release(s)
+    assert scratch_bytes() < held
