@@ -72,6 +72,11 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 #define SV_MAX_K 64
 #define SV_MAX_V 2097152 /* 256 chunks of 8192 logits per row */
+/* Size of the device array that sv_spec_verify_noalloc works in (one per
+ * device the library runs on, held until the process ends).  It holds every
+ * call with B <= 64, K <= 6 and V <= 128256, in any mode and dtype; a call
+ * whose scratch would not fit returns SV_ERR_WORKSPACE. */
+#define SV_NOALLOC_SCRATCH_BYTES (32 << 20)
 /* sv_init flag: also size the stream's buffer of projection logits for
  * sv_spec_verify_lmhead. */
 #define SV_INIT_LMHEAD 1
@@ -109,6 +114,29 @@ int sv_spec_verify(const void* target_logits, const void* draft_logits,
                    int32_t* out_tokens, int32_t* out_num_accepted,
                    int32_t B, int32_t K, int32_t V, int32_t dtype,
                    void* stream);
+
+/*
+ * sv_spec_verify_noalloc - sv_spec_verify for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  Same arguments, results and errors as
+ * sv_spec_verify, but the call never allocates or frees memory and never
+ * synchronises: its scratch is one file-scope device array per device of
+ * SV_NOALLOC_SCRATCH_BYTES bytes, loaded with the library's code.  A call
+ * whose scratch would exceed it returns SV_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on a device works in that device's one array: calls
+ * that may overlap on one device (different streams, or different host
+ * threads without ordering) race on it and must be serialised by the
+ * caller.  No call depends on what an earlier call left in the array (the
+ * call's first kernel clears what must start at zero).  Not timed by
+ * sv_profile_start.  sv_init() resolves the array's address on a device
+ * (otherwise the first call on the device does).
+ */
+int sv_spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, const float* uniforms,
+                           float temperature, int32_t top_k, float top_p,
+                           int32_t* out_tokens, int32_t* out_num_accepted,
+                           int32_t B, int32_t K, int32_t V, int32_t dtype,
+                           void* stream);
 
 /*
  * sv_spec_verify_debug - sv_spec_verify plus the intermediate values the
@@ -385,7 +413,8 @@ int sv_profile_stop(double* stream_kernel_ms, double* other_kernels_ms, int64_t*
  * K <= max_K drafts with V <= max_V (any mode, dtype and variant; ragged
  * batches of total_draft <= max_B * max_K; sv_sample and sv_filtered_probs
  * of rows <= max_B * (2 * max_K + 1)).  flags: 0, or SV_INIT_LMHEAD to also
- * size the logits buffer of sv_spec_verify_lmhead for those bounds.  The
+ * size the logits buffer of sv_spec_verify_lmhead for those bounds.  Also
+ * resolves the address of sv_spec_verify_noalloc's array on `device`.  The
  * current device is restored before returning.  Errors: SV_ERR_PARAM (device
  * outside [0, 64) or unknown flags), SV_ERR_SHAPE (max_B < 0, max_K outside
  * [0, SV_MAX_K], max_V outside [1, SV_MAX_V]), SV_ERR_WORKSPACE (allocation
@@ -405,7 +434,8 @@ int sv_stream_release(void* stream);
 int sv_release(void);
 
 /* Bytes of device scratch and logits buffers currently held on `device`,
- * summed over its streams (0 if none). */
+ * summed over its streams (0 if none; the array of sv_spec_verify_noalloc is
+ * not counted). */
 int64_t sv_scratch_bytes(int device);
 
 /* Human-readable name of a status code. */

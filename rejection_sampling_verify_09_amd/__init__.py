@@ -20,11 +20,12 @@ from ._lib import (  # noqa: F401
     stream_release,
     sample,
     spec_verify,
+    spec_verify_noalloc,
     spec_verify_lmhead,
     spec_verify_probs,
     spec_verify_ragged,
     status_string,
 )
 
-__all__ = ["spec_verify", "spec_verify_lmhead", "lm_logits", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "init", "stream_release", "scratch_bytes", "status_string", "lib",
+__all__ = ["spec_verify", "spec_verify_noalloc", "spec_verify_lmhead", "lm_logits", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "init", "stream_release", "scratch_bytes", "status_string", "lib",
            "SpecVerifyError"]

@@ -19,6 +19,7 @@ SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_PARAM, SV_ERR_HIP, SV_ERR
 SV_F32, SV_BF16 = 0, 1
 SV_MAX_K = 64
 SV_INIT_LMHEAD = 1
+SV_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.sv_dynk_destroy.restype = None
         L.sv_release.argtypes = []
         L.sv_release.restype = ctypes.c_int
+        L.sv_spec_verify_noalloc.argtypes = [vp, vp, vp, vp, f32, i32, f32, vp, vp, i32, i32, i32, i32, vp]
+        L.sv_spec_verify_noalloc.restype = ctypes.c_int
         L.sv_init.argtypes = [ctypes.c_int, vp, i32, i32, i32, i32]
         L.sv_init.restype = ctypes.c_int
         L.sv_stream_release.argtypes = [vp]
@@ -180,6 +183,46 @@ def spec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor | None, 
     st = lib().sv_spec_verify(tp, dp, xp, up, float(temperature), int(top_k), float(top_p), op, onp, B, K, V, code, s)
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_spec_verify")
+    return out_tokens, out_num_accepted
+
+
+def spec_verify_noalloc(target_logits: torch.Tensor, draft_logits: torch.Tensor | None, draft_tokens: torch.Tensor,
+                        uniforms: torch.Tensor, temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+                        out_tokens: torch.Tensor | None = None, out_num_accepted: torch.Tensor | None = None,
+                        stream=None):
+    """spec_verify through sv_spec_verify_noalloc: the library allocates
+    nothing (its scratch is a fixed per-device array; calls that overlap on
+    one device race on it).  Pass the output tensors to allocate nothing on
+    this side either."""
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    dev = target_logits.device
+    tp = _dev(target_logits, "target_logits")
+    if draft_logits is not None and K > 0:
+        if tuple(draft_logits.shape) != (B, K, V) or draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft_logits must be [B, K, V] with the target's dtype")
+        dp = _dev(draft_logits, "draft_logits")
+    elif float(temperature) == 0.0 or K == 0:
+        dp = None
+    else:
+        raise ValueError("draft_logits are required unless temperature == 0")
+    if tuple(draft_tokens.shape) != (B, K) or tuple(uniforms.shape) != (B, K + 1):
+        raise ValueError("draft_tokens must be [B, K] and uniforms [B, K+1]")
+    xp = _dev(draft_tokens, "draft_tokens", torch.int32) if K > 0 else None
+    up = _dev(uniforms, "uniforms", torch.float32)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = lib().sv_spec_verify_noalloc(tp, dp, xp, up, float(temperature), int(top_k), float(top_p),
+                                      _dev(out_tokens, "out_tokens", torch.int32),
+                                      _dev(out_num_accepted, "out_num_accepted", torch.int32), B, K, V, code,
+                                      _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_spec_verify_noalloc")
     return out_tokens, out_num_accepted
 
 

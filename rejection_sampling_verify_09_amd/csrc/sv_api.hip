@@ -47,7 +47,7 @@ struct StreamBufs {
   size_t lgt_bytes = 0;
 };
 
-std::mutex g_mu;  // guards g_bufs (the map, not the buffers)
+std::mutex g_mu;  // guards g_bufs (the map, not the buffers) and g_static
 std::map<std::pair<int, uintptr_t>, std::unique_ptr<StreamBufs>> g_bufs;
 
 StreamBufs* bufs_for(int dev, hipStream_t s) {
@@ -70,6 +70,26 @@ int grow(char** p, size_t* have, size_t want, hipStream_t s) {
   if (hipMalloc(&q, want) != hipSuccess) return SV_ERR_WORKSPACE;
   *p = (char*)q;
   *have = want;
+  return SV_OK;
+}
+
+// The no-allocation entry point's scratch: one array per device, placed by
+// the loader with the library's code, at its own address on each device.
+// The host only ever uses the address hipGetSymbolAddress returns for the
+// current device (g_static), never the array's name.
+static __device__ __align__(256) char scratch[SV_NOALLOC_SCRATCH_BYTES];
+char* g_static[kMaxDevices];
+
+// The device address of `scratch` on device dev (resolved once per device,
+// with that device current).
+int static_scratch(int dev, char** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_static[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SV_ERR_HIP;
+    g_static[dev] = (char*)ptr;
+  }
+  *out = g_static[dev];
   return SV_OK;
 }
 
@@ -497,6 +517,22 @@ int sv_spec_verify(const void* target_logits, const void* draft_logits, const in
                      stream);
 }
 
+int sv_spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                           const float* uniforms, float temperature, int32_t top_k, float top_p, int32_t* out_tokens,
+                           int32_t* out_num_accepted, int32_t B, int32_t K, int32_t V, int32_t dtype, void* stream) {
+  Plan p;
+  int st = plan_verify(verify_in(target_logits, draft_logits, draft_tokens, uniforms, temperature, temperature,
+                                 top_k, top_p, out_tokens, out_num_accepted, nullptr, nullptr, nullptr, B, K, V,
+                                 dtype),
+                       &p);
+  if (st != SV_OK || p.empty) return st;
+  if (make_layout(p.need).total > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_WORKSPACE;
+  int dev = 0;
+  char* base = nullptr;
+  if ((st = current_device(&dev)) != SV_OK || (st = static_scratch(dev, &base)) != SV_OK) return st;
+  return launch_plan(p, base, (hipStream_t)stream, nullptr);
+}
+
 int sv_spec_verify_debug(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                          const float* uniforms, float temperature, int32_t top_k, float top_p,
                          int32_t* out_tokens, int32_t* out_num_accepted, double* out_p, double* out_q,
@@ -629,6 +665,9 @@ int sv_init(int device, void* stream, int32_t max_B, int32_t max_K, int32_t max_
       if (st == SV_OK && (flags & SV_INIT_LMHEAD))
         st = grow(&b->lgt, &b->lgt_bytes, std::max<size_t>((size_t)rows * (size_t)max_V * sizeof(float), 256), s);
     }
+    // set-up of the no-allocation entry point on this device
+    char* base = nullptr;
+    if (st == SV_OK) st = static_scratch(device, &base);
   }
   if (hipSetDevice(cur) != hipSuccess && st == SV_OK) st = SV_ERR_HIP;
   return st;

@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
     for s in ["sv_spec_verify", "sv_spec_verify_debug", "sv_spec_verify_dt", "sv_spec_verify_ragged",
               "sv_spec_verify_probs", "sv_lm_logits", "sv_spec_verify_lmhead",
               "sv_filtered_probs", "sv_sample", "sv_dynk_create", "sv_dynk_observe", "sv_dynk_k", "sv_dynk_destroy",
-              "sv_release", "sv_scratch_bytes", "sv_init", "sv_stream_release",
+              "sv_release", "sv_scratch_bytes", "sv_init", "sv_stream_release", "sv_spec_verify_noalloc",
               "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
         assert s in syms
 
@@ -281,6 +281,26 @@ def test_lm_bindings_check_their_arguments_before_any_call():
     with pytest.raises(ValueError):  # draft rows of the wrong count
         spec_verify_lmhead(torch.zeros((1, 3, 64), dtype=torch.bfloat16), w,
                            torch.zeros((1, 3, 64), dtype=torch.bfloat16), w, x, u, 1.0)
+
+
+def call_noalloc(B=2, K=3, V=16, T=1.0, top_k=0, top_p=1.0, dtype=L.SV_F32):
+    return L.lib().sv_spec_verify_noalloc(FAKE, FAKE, FAKE, FAKE, T, top_k, top_p, FAKE, FAKE, B, K, V, dtype, None)
+
+
+def test_noalloc_validation_and_capacity():
+    """The no-allocation entry point validates like sv_spec_verify and refuses,
+    before any HIP call, a call whose scratch would exceed its fixed array."""
+    assert call_noalloc(B=-1) == L.SV_ERR_SHAPE
+    assert call_noalloc(T=-1.0) == L.SV_ERR_PARAM
+    assert call_noalloc(dtype=9) == L.SV_ERR_DTYPE
+    assert call_noalloc(B=0) == L.SV_OK
+    # B = 256, K = 8, V = 152064: far beyond the array
+    assert call_noalloc(B=256, K=8, V=152064, top_k=50) == L.SV_ERR_WORKSPACE
+    # the largest call the header promises fits (any mode): past the size check
+    for k, p in [(0, 0.9), (50, 0.9), (50, 1.0), (0, 1.0)]:
+        assert call_noalloc(B=64, K=6, V=128256, T=0.7, top_k=k, top_p=p, dtype=L.SV_BF16) != L.SV_ERR_WORKSPACE
+        assert call_noalloc(B=64, K=6, V=128256, T=0.7, top_k=k, top_p=p, dtype=L.SV_F32) != L.SV_ERR_WORKSPACE
+    assert L.SV_NOALLOC_SCRATCH_BYTES == 32 << 20
 
 
 def test_init_validation():
