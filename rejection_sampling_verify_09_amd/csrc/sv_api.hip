@@ -304,7 +304,7 @@ int plan_verify(const VerifyIn& in, Plan* p) {
   const int64_t rows = (mode == M_GREEDY || use_qp) ? nt : nt + nd;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
-  if (rows * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
+  if ((rows + NXCD) * nchunks > kMaxGrid || (int64_t)B * nsc > kMaxGrid) return SV_ERR_SHAPE;
   Need& need = p->need;
   need.rows = rows;
   need.nchunks = nchunks;
@@ -350,7 +350,8 @@ int plan_verify(const VerifyIn& in, Plan* p) {
   p->mode = mode;
   p->dtype = in.dtype;
   p->vec = vec;
-  p->g_stream = (unsigned)(rows * nchunks);
+  a.nitems = (int32_t)(rows * nchunks);
+  p->g_stream = (unsigned)(((rows + NXCD - 1) / NXCD) * NXCD * nchunks);
   p->g_seq = (unsigned)B;
   p->g_sample = mode == M_PLAIN ? (unsigned)((int64_t)B * a.nsw) : 0u;
   return SV_OK;
@@ -599,7 +600,7 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   const int esz = dtype == SV_BF16 ? 2 : 4;
   const int64_t nchunks = ((int64_t)V + CE - 1) / CE;
   const int64_t nsc = ((int64_t)V + SCE - 1) / SCE;
-  if ((int64_t)rows * nchunks > kMaxGrid || (int64_t)rows * nsc > kMaxGrid) return SV_ERR_SHAPE;
+  if (((int64_t)rows + NXCD) * nchunks > kMaxGrid || (int64_t)rows * nsc > kMaxGrid) return SV_ERR_SHAPE;
   Need need;
   need.rows = rows;
   need.nchunks = nchunks;
@@ -622,6 +623,7 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   a.dch = make_udiv((uint32_t)a.nchunks);
   a.rps = 1;
   a.drps = make_udiv(1u);
+  a.nitems = (int32_t)((int64_t)rows * nchunks);
   int dev = 0;
   if ((st = current_device(&dev)) != SV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -630,7 +632,9 @@ int sv_filtered_probs(const void* logits, int32_t rows, int32_t V, int32_t dtype
   std::lock_guard<std::mutex> lk(b->mu);
   if ((st = grow(&b->ptr, &b->bytes, make_layout(need).total, s)) != SV_OK) return st;
   bind_scratch(a, b->ptr, make_layout(need));
-  if (launch_stream(a, dtype, mode, vec, (unsigned)((int64_t)rows * nchunks), s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_stream(a, dtype, mode, vec, (unsigned)((((int64_t)rows + NXCD - 1) / NXCD) * NXCD * nchunks), s) !=
+      hipSuccess)
+    return SV_ERR_HIP;
   if (launch_row(a, dtype, mode, (unsigned)rows, s) != hipSuccess) return SV_ERR_HIP;
   if (launch_probs(a, dtype, mode, (unsigned)((int64_t)rows * nsc), s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;

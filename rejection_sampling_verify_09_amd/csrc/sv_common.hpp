@@ -29,7 +29,7 @@ constexpr int64_t MAX_V = (int64_t)MAX_CHUNKS * CE;  // 2,097,152
 constexpr int MAX_RPS = 2 * MAX_K + 1;
 // top-p candidates: every logit within this many units of z = logit / T below
 // the row maximum (the cut is verified against the mass at the row merge)
-constexpr float TOPP_WINDOW_Z = 8.0f;
+constexpr float TOPP_WINDOW_Z = 5.0f;
 
 enum Mode : int { M_PLAIN = 0, M_TOPK = 1, M_TOPP = 2, M_TOPKP = 3, M_GREEDY = 4 };
 enum DType : int { D_F32 = 0, D_BF16 = 1 };
@@ -139,6 +139,7 @@ struct Args {
   int32_t* cflag;     // [1]: ragged offsets valid (written by the streaming kernel)
   double* seg_sum;
   int32_t* seg_last;
+  int32_t nitems;  // streaming items (row, chunk): rows * nchunks
   int32_t ulen;   // logits per candidate unit (16-byte vector; 1 on the element-load path)
   UDiv dch;       // division by nchunks
   UDiv drps;      // division by rps
@@ -147,12 +148,14 @@ struct Args {
 // Weight of chunk record (m_c, s_c) in a row whose max is m: the chunk's sum
 // of exp((x - m) / T).  The streaming pass sums exp2(x * c2) (c2 = log2(e) / T
 // in float) against the integer offset 2^ceil(m_c * c2), or against 2^(m_c * c2)
-// itself when that offset overflows float.
+// itself when that offset overflows float; the record's sum is moved to 2^(m_c *
+// c2) by the offset's remainder and then to the row max by exp((m_c - m) / T),
+// both in one exp2 of a double exponent.
 __device__ __forceinline__ double chunk_weight(double s_c, float m_c, float m, float c2, double invT) {
   if (!(m_c > -INFINITY)) return 0.0;
   const float Mi = __builtin_ceilf(m_c * c2);
-  const double f = Mi < INFINITY ? exp2((double)Mi - (double)m_c * (double)c2) : 1.0;
-  return s_c * f * exp(((double)m_c - (double)m) * invT);
+  const double f = Mi < INFINITY ? (double)Mi - (double)m_c * (double)c2 : 0.0;
+  return s_c * exp2(f + ((double)m_c - (double)m) * (invT * 1.4426950408889634074));
 }
 
 // Order-preserving map float -> uint32 (larger float, larger key).
@@ -488,6 +491,21 @@ __device__ __forceinline__ bool last_arrival(uint32_t* cnt, uint32_t total, int*
   return *flag != 0;
 }
 
+// The streaming item of this workgroup.  A launch's workgroups go to the
+// NXCD XCDs in turn (workgroup i to XCD i mod NXCD); rows are dealt to the
+// XCDs in the same turn, so that each XCD streams its rows' chunks in order
+// while the XCDs together work on NXCD neighbouring rows at a time: row
+// NXCD * (k / nchunks) + (i mod NXCD), chunk k mod nchunks, with k = i / NXCD.
+// Measured faster than chunks dealt to the XCDs one by one.  Workgroups past
+// the last row (the last turn may be partial) have no item.
+constexpr int NXCD = 8;
+__device__ __forceinline__ int stream_item(const Args& a) {
+  const int i = (int)blockIdx.x;
+  const int k = i / NXCD;
+  const int r = udiv(k, a.dch);
+  return (NXCD * r + i % NXCD) * a.nchunks + (k - r * a.nchunks);
+}
+
 // Ragged batches: whether the offsets cu[B + 1] describe a packing of the
 // rows (cu[0] = 0, nondecreasing, every K_b <= Kmax, cu[B] = ND), decided
 // once per call by the streaming kernel's first workgroup and read by the
@@ -505,7 +523,8 @@ __device__ __forceinline__ void check_offsets(const Args& a) {
 }
 
 // The arrival counters of the launches that follow, cleared by the call's
-// streaming kernel (one per sequence; its grid has at least B workgroups):
+// streaming kernel (one per sequence, by workgroup index; its grid has at
+// least B workgroups):
 // no call depends on what an earlier call left in the scratch.
 __device__ __forceinline__ void clear_counters(const Args& a) {
   if (threadIdx.x == 0 && (int)blockIdx.x < a.B) {

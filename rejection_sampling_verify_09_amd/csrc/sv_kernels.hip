@@ -241,7 +241,7 @@ constexpr double MASS_SCALE = 4503599627370496.0;  // 2^52
 // search, 8 key bits per pass over the whole row (used only when the
 // candidate lists cannot decide the cut).
 template <int DT, int BS>
-__device__ uint32_t row_radix(const char* rp, int V, uint32_t lo, bool mass, float m, double invT, double snorm,
+__device__ __forceinline__ uint32_t row_radix(const char* rp, int V, uint32_t lo, bool mass, float m, double invT, double snorm,
                               double target, Smem& sm) {
   const int t = threadIdx.x;
   const unsigned long long tgt = mass ? (unsigned long long)(target * MASS_SCALE) : (unsigned long long)target;
@@ -285,7 +285,7 @@ __device__ uint32_t row_radix(const char* rp, int V, uint32_t lo, bool mass, flo
 // normaliser sum exp((x - m) / T), and (when they fit) the kept entries in
 // sm.r.keys.
 template <int DT, int BS>
-__device__ int row_keep(const char* rp, int V, uint32_t tau, float m, double invT, double* skept, Smem& sm) {
+__device__ __forceinline__ int row_keep(const char* rp, int V, uint32_t tau, float m, double invT, double* skept, Smem& sm) {
   const int t = threadIdx.x;
   __syncthreads();
   if (t == 0) sm.ncand = 0;
@@ -307,7 +307,7 @@ __device__ int row_keep(const char* rp, int V, uint32_t tau, float m, double inv
 // Radix select (8 bits per pass, counts in LDS) of the k-th largest key among
 // the n candidates in sm.r.cand.
 template <int BS>
-__device__ uint32_t cand_select(int n, int k, Smem& sm) {
+__device__ __forceinline__ uint32_t cand_select(int n, int k, Smem& sm) {
   const int t = threadIdx.x;
   uint32_t prefix = 0, pmask = 0;
   int need = k;
@@ -361,7 +361,7 @@ __device__ __forceinline__ int block_excl_scan_i(int v, Red& r, int* total) {
 
 // Sort the first n entries of sm.r.keys descending (pads with zeros).
 template <int BS>
-__device__ void sort_keys_desc(int n, Smem& sm) {
+__device__ __forceinline__ void sort_keys_desc(int n, Smem& sm) {
   const int np2 = pow2_at_least(n < 2 ? 2 : n);
   __syncthreads();
   for (int e = n + threadIdx.x; e < np2; e += BS) sm.r.keys[e] = 0;
@@ -372,7 +372,7 @@ __device__ void sort_keys_desc(int n, Smem& sm) {
 // records are in sm.r (cm, cb, cn) and the row is valid (finite max m;
 // for top-p also a finite normaliser rr.S).
 template <int DT, int MODE, int BS, class Sink>
-__device__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRec& rr, Smem& sm, const Sink& sink) {
+__device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp, float m, RowRec& rr, Smem& sm, const Sink& sink) {
   static_assert(ROW_CAND % BS == 0 && ROW_CAND <= 4 * BS, "top-p scan holds ROW_CAND / BS entries per thread");
   const int t = threadIdx.x, nch = a.nchunks;
   const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
@@ -618,7 +618,7 @@ __device__ __forceinline__ RowRec load_row(const RowRec* p) {
 }
 
 template <int DT, int MODE, int BS, class Sink>
-__device__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm, const Sink& sink) {
+__device__ __forceinline__ RowRec row_finalize(const Args& a, int rl, int xtok, Smem& sm, const Sink& sink) {
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int t = threadIdx.x, nch = a.nchunks;
@@ -716,7 +716,7 @@ __device__ __forceinline__ double draw_weight(const char* pr, const char* qr, in
 }
 
 template <int DT, int BS>
-__device__ int full_row_sample(const Args& a, double u, const char* pr, const char* qr, bool res, Smem& sm,
+__device__ __forceinline__ int full_row_sample(const Args& a, double u, const char* pr, const char* qr, bool res, Smem& sm,
                                double* Zout) {
   const int t = threadIdx.x, V = a.V;
   const DrawRow* dr = sm.dr;
@@ -865,7 +865,8 @@ __device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elem
 // of this thread, tm its max.  Shared memory written here is first written
 // after a barrier of this call, so a workgroup can run it for consecutive
 // items without a barrier in between.  Only the next launch reads what is
-// stored here, so plain stores suffice.
+// stored here, so no atomic or fence is needed; the stores are nontemporal,
+// so that the records and lists do not sit dirty in this launch's cache.
 template <int DT, int MODE, bool VEC>
 __device__ __forceinline__ void stream_emit(const Args& a, int item, const float (&um)[UnitT<DT, VEC>::N],
                                             const float (&gm)[4], float tm, float mc, double s, int arg,
@@ -893,7 +894,7 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
       bound = a.top_k <= WG ? (uint32_t)sm.s.tk[a.top_k - 1] : KEY_NEG_INF;
       // the chunk's largest thread maxima: values of the row, from which the
       // row merge bounds the row's k-th largest from below
-      if (t < CTOP) a.ctop[(size_t)chunk_id * CTOP + t] = (uint32_t)sm.s.tk[t];
+      if (t < CTOP) __builtin_nontemporal_store((uint32_t)sm.s.tk[t], &a.ctop[(size_t)chunk_id * CTOP + t]);
     }
     thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
     const int w = t >> 6;
@@ -905,7 +906,7 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
     uint64_t* dst = a.cand + (size_t)chunk_id * CAND_CAP;
     if (nc <= CAND_CAP) {
       const int off = (w > 0 ? n0 : 0) + (w > 1 ? n1 : 0) + (w > 2 ? n2 : 0);
-      for (int j = t & 63; j < wn; j += 64) dst[off + j] = sm.s.cand[w * CAND_CAP + j];
+      for (int j = t & 63; j < wn; j += 64) __builtin_nontemporal_store(sm.s.cand[w * CAND_CAP + j], &dst[off + j]);
     } else {
       // Too many: keep exactly the units above the (CAND_CAP+1)-th largest
       // unit max (radix select over the registers) and raise the bound to match.
@@ -948,18 +949,17 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
       }
       __syncthreads();
       nc = sm.ncand;
-      for (int j = t; j < nc; j += WG) dst[j] = sm.s.cand[j];
+      for (int j = t; j < nc; j += WG) __builtin_nontemporal_store(sm.s.cand[j], &dst[j]);
     }
   }
   if (t == 0) {
-    ChunkRec rec;
-    rec.s = s;
-    rec.m = mc;
-    rec.bound = bound;
-    rec.ncand = nc;
-    rec.arg = arg;
-    rec.pad0 = rec.pad1 = 0;
-    a.chunk[chunk_id] = rec;
+    // the record as two 16-byte stores that do not stay in this cache (only
+    // the next launch reads them)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4* rp4 = reinterpret_cast<u32x4*>(&a.chunk[chunk_id]);
+    const uint64_t sb = (uint64_t)__double_as_longlong(s);
+    __builtin_nontemporal_store(u32x4{(uint32_t)sb, (uint32_t)(sb >> 32), __float_as_uint(mc), bound}, rp4);
+    __builtin_nontemporal_store(u32x4{(uint32_t)nc, (uint32_t)arg, 0u, 0u}, rp4 + 1);
   }
 }
 
@@ -971,13 +971,14 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, false>())) stream_ke
   __shared__ Smem sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   const int t = threadIdx.x;
-  const int item = (int)blockIdx.x;
+  clear_counters(a);
+  check_offsets(a);
+  const int item = stream_item(a);
+  if (item >= a.nitems) return;
   const int rl = udiv(item, a.dch);
   const int c0 = (item - rl * a.nchunks) * CE;
   const int cn = min(CE, a.V - c0);
   const char* rp = row_ptr(a, rl, ESZ);
-  clear_counters(a);
-  check_offsets(a);
   float v[EPT];
   load_chunk<DT, false>(rp, c0, cn, v);
   // units are single logits here: the unit maxima are v itself
@@ -1173,14 +1174,15 @@ __device__ __forceinline__ void stream_vec_body(const Args& a, int item, int rl,
 template <int DT, int MODE>
 __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_kernel_vec(Args a) {
   __shared__ Smem sm;
-  const int item = (int)blockIdx.x;
+  clear_counters(a);
+  check_offsets(a);
+  const int item = stream_item(a);
+  if (item >= a.nitems) return;
   const int rl = udiv(item, a.dch);
   const int c0 = (item - rl * a.nchunks) * CE;
   const int cn = min(CE, a.V - c0);
   ChunkRaw<DT> cr;
   issue_chunk<DT>(a, rl, c0, cn, cr);
-  clear_counters(a);
-  check_offsets(a);
   stream_vec_body<DT, MODE>(a, item, rl, c0, cn, cr, sm);
 }
 
@@ -1367,29 +1369,6 @@ __device__ __forceinline__ uint32_t wave_cut64(uint32_t k, unsigned long long wt
   return hit ? (uint32_t)__builtin_amdgcn_readlane((int)ks, __ffsll(hit) - 1) : 0u;
 }
 
-// The same cut for at most 64 entries, one per lane, by a walk down the
-// distinct keys (entries with equal keys have equal weights, so a key's
-// weight is its count times one of them, exactly): cheap when the cut lies
-// within the first few keys, as a nucleus usually does.  After WR_ITER keys
-// the rank cut takes over.
-__device__ __forceinline__ uint32_t wave_walk64(uint32_t k, unsigned long long wt, unsigned long long target, int n,
-                                                WaveRowSm& ws) {
-  unsigned long long run = 0;
-  uint32_t hi = 0xFFFFFFFFu;
-  for (int it = 0; it < WR_ITER; ++it) {
-    const uint32_t km = dpp_wave_umax(k < hi ? k : 0u);
-    if (km == 0u) return 0u;
-    const unsigned long long bm = __ballot(k == km);
-    const int src = __ffsll(bm) - 1;
-    const unsigned long long w = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(wt >> 32), src) << 32) |
-                                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wt, src);
-    run += (unsigned long long)__popcll(bm) * w;
-    if (run >= target) return km;
-    hi = km;
-  }
-  return wave_cut64(k, wt, target, n, ws);
-}
-
 // Merge of one row by one wave: max, normaliser, filter threshold, kept list
 // (ascending index, into the scratch lists), the probability of the drafted
 // token, and the row record.  Returns false, having written nothing, when the
@@ -1464,7 +1443,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     double sl = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      sl += chunk_weight(cs[i], cm[i], m, rt.c2, invT);
+      if (64 * i < nch) sl += chunk_weight(cs[i], cm[i], m, rt.c2, invT);  // uniform
     const double S = dpp_wave_sum(sl);
     rr.S = S;
     if (!(S > 0.0 && S < INFINITY)) bad = true;
@@ -1595,7 +1574,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       // k-th largest key among the candidates, ties kept
 #pragma unroll
       for (int r = 0; r < WR_EPL; ++r) wt[r] = ek[r] != 0u ? 1ull : 0ull;
-      const uint32_t tk = n <= 64 ? wave_walk64(ek[0], wt[0], (unsigned long long)a.top_k, n, ws)
+      const uint32_t tk = n <= 64 ? wave_cut64(ek[0], wt[0], (unsigned long long)a.top_k, n, ws)
                                   : wave_radix(ek, wt, (unsigned long long)a.top_k, ws.hist);
       if (tk == 0u) {
         // fewer than k candidates: with every bound at -inf the row has fewer
@@ -1622,7 +1601,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       const unsigned long long target = (unsigned long long)(a.top_p * MASS_SCALE);
       if (n <= 64) {
         const unsigned long long w0 = ekp[0] != 0u ? (unsigned long long)(ew[0] / snorm * MASS_SCALE) : 0ull;
-        tp = wave_walk64(ekp[0], w0, target, n, ws);
+        tp = wave_cut64(ekp[0], w0, target, n, ws);
       } else {
 #pragma unroll
         for (int r = 0; r < WR_EPL; ++r)
@@ -1716,7 +1695,7 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
 // total weight, *wout the drawn token's weight.
 // qrow: the draft distribution as a probability row; q of each kept target
 // token is then read from it (the draft list is not used).
-__device__ int wave_list_sample(double u, const int32_t* pidx, const double* pprob, int np, const int32_t* qidx,
+__device__ __forceinline__ int wave_list_sample(double u, const int32_t* pidx, const double* pprob, int np, const int32_t* qidx,
                                 const double* qprob, int nq, bool res, double* Zout, double* wout,
                                 const float* qrow = nullptr) {
   const int lane = threadIdx.x & 63;
@@ -1944,22 +1923,27 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // ---- rows the candidate lists could not decide: the whole workgroup
-  for (int j = 0; j < rps; ++j) {
-    if (!(sm.fail[j >> 5] & (1u << (j & 31)))) continue;  // uniform
-    const int rl = seq_row<RAG>(a, g, j);
-    const int i = j <= K ? j : j - K - 1;
-    const int xtok = i < K ? sm.x[i] : -1;
-    const RowRec rr = row_finalize<DT, MODE, SQ_BS>(a, rl, xtok, sm.blk, seq_sink(a, sm, j, rl));
-    if (t == 0) {
-      sm.px[j] = rr.px;
-      sm.rf[j] = rr.flags;
-      sm.nk[j] = rr.nkept;
-      sm.arg[j] = rr.arg;
-      sm.rm[j] = rr.m;
-      sm.rs[j] = rr.S;
+  for (int wd = 0; 32 * wd < rps; ++wd) {
+    uint32_t bits = sm.fail[wd];  // the same in every thread
+    if (rps - 32 * wd < 32) bits &= (1u << (rps - 32 * wd)) - 1u;
+    while (bits) {
+      const int j = 32 * wd + __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int rl = seq_row<RAG>(a, g, j);
+      const int i = j <= K ? j : j - K - 1;
+      const int xtok = i < K ? sm.x[i] : -1;
+      const RowRec rr = row_finalize<DT, MODE, SQ_BS>(a, rl, xtok, sm.blk, seq_sink(a, sm, j, rl));
+      if (t == 0) {
+        sm.px[j] = rr.px;
+        sm.rf[j] = rr.flags;
+        sm.nk[j] = rr.nkept;
+        sm.arg[j] = rr.arg;
+        sm.rm[j] = rr.m;
+        sm.rs[j] = rr.S;
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
 
   // ---- the sequence
@@ -2359,8 +2343,9 @@ static KFn pick_probs(int mode) {
   }
 }
 
-// grid: the number of streaming items (one workgroup each).  With events,
-// the launch itself records the kernel's start and end in them.
+// grid: ceil(rows / NXCD) * NXCD * nchunks workgroups for a.nitems
+// streaming items (stream_item).
+// With events, the launch itself records the kernel's start and end in them.
 hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned grid, hipStream_t s, hipEvent_t e0,
                          hipEvent_t e1) {
   KFn f = dtype == D_BF16 ? pick_stream_mode<D_BF16>(mode, vec) : pick_stream_mode<D_F32>(mode, vec);
