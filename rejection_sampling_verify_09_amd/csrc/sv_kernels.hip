@@ -1174,15 +1174,21 @@ __device__ __forceinline__ void stream_vec_body(const Args& a, int item, int rl,
 template <int DT, int MODE>
 __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_kernel_vec(Args a) {
   __shared__ Smem sm;
-  clear_counters(a);
-  check_offsets(a);
-  const int item = stream_item(a);
-  if (item >= a.nitems) return;
+  // The chunk's loads go out first, before the per-call bookkeeping: a
+  // workgroup past the last item (idle) addresses item 0 with an empty range,
+  // so its loads touch no memory, and leaves after the bookkeeping (the first
+  // workgroup, which checks the offsets, is never idle).
+  const int it = stream_item(a);
+  const bool idle = it >= a.nitems;
+  const int item = idle ? 0 : it;
   const int rl = udiv(item, a.dch);
   const int c0 = (item - rl * a.nchunks) * CE;
-  const int cn = min(CE, a.V - c0);
+  const int cn = idle ? 0 : min(CE, a.V - c0);
   ChunkRaw<DT> cr;
   issue_chunk<DT>(a, rl, c0, cn, cr);
+  clear_counters(a);
+  check_offsets(a);
+  if (idle) return;
   stream_vec_body<DT, MODE>(a, item, rl, c0, cn, cr, sm);
 }
 
