@@ -90,9 +90,25 @@ def measured_traffic(key: str, kernel: str = "stream_kernel", sources=None):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(w, d, x, budget_s: float, draft_temperature=None):
-    """Time the fp64 oracle on whole batches of the workload until about
-    budget_s of CPU time has been spent (at least one batch)."""
+CPU_SHARE = 16  # host threads one GPU's job may use on the GPU hosts
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline_single(w, d, x, budget_s: float, draft_temperature=None):
+    """Time the fp64 oracle on whole batches of the workload, in this
+    process, until about budget_s has been spent (at least one batch)."""
     import numpy as np
 
     import oracle
@@ -109,9 +125,177 @@ def cpu_baseline(w, d, x, budget_s: float, draft_temperature=None):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return dict(value=n_done / el, unit="sequences/s", cores=1, kind="oracle",
+    return dict(value=n_done / el, unit="sequences/s", cores=1, kind="oracle", cpu=cpu_model(),
                 sample=f"{n_done // sample_B} x the full {sample_B}-sequence batch of {w.name}, "
                        f"fp64 NumPy, single thread, {el:.1f} s", tokens_per_s=toks / el)
+
+
+_CPU_JOB = {}
+
+
+def _cpu_one_sequence(b: int) -> int:
+    """One sequence of the batch in _CPU_JOB through the oracle (a worker of
+    the all-cores leg; the batch reaches it by fork)."""
+    import oracle
+
+    w, d, x = _CPU_JOB["w"], _CPU_JOB["d"], _CPU_JOB["x"]
+    _, n = oracle.verify(d["target"][b:b + 1], d["draft"][b:b + 1], x[b:b + 1], d["uniforms"][b:b + 1],
+                         w.temperature, w.top_k, w.top_p, dtype=w.dtype)
+    return int(n[0])
+
+
+def cpu_baseline(w, d, x, budget_s: float):
+    """The fp64 oracle on all the host cores this job may use: one forked
+    worker per core (at most CPU_SHARE), each verifying whole sequences of
+    the batch, over repeated passes of the batch until about budget_s.  Must
+    run before this process initialises the GPU."""
+    import multiprocessing as mp
+
+    visible = len(os.sched_getaffinity(0))
+    workers = max(1, min(visible, CPU_SHARE))
+    _CPU_JOB.update(w=w, d=d, x=x)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(_cpu_one_sequence, range(min(w.B, workers)), chunksize=1)  # workers import the oracle
+        t0 = time.perf_counter()
+        n_done = 0
+        while True:
+            n_done += len(pool.map(_cpu_one_sequence, range(w.B), chunksize=1))
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    _CPU_JOB.clear()
+    return dict(value=n_done / el, unit="sequences/s", cores=workers, kind="oracle", cpu=cpu_model(),
+                cores_visible=visible,
+                sample=f"{n_done // w.B} x the full {w.B}-sequence batch of {w.name}, one sequence per task, "
+                       f"{workers} forked workers (fp64 NumPy, one thread each), {el:.1f} s")
+
+
+def _percentiles(ms):
+    import numpy as np
+
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "calls": int(a.size)}
+
+
+def measure_verify(w, d, x, steps: int, warmup: int, copies: int, Td=None) -> dict:
+    """Time sv_spec_verify on one batch of workload w (logits resident in
+    HBM, rotated over enough copies to defeat the last-level cache).  Three
+    timed regions of `steps` calls each: back to back (the step time),
+    with the library's launch timing (the streaming kernel's duration), and
+    one event pair around each call (the per-call distribution)."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verify_09_amd import profile_start, profile_stop, spec_verify
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    tgt0 = dev(d["target"])
+    drf0 = dev(d["draft"]) if w.K > 0 else None
+    bytes_per_step = w.logit_bytes  # every logit the step must read, once
+    R = copies or max(3, -(-640_000_000 // bytes_per_step))
+    tgts = [tgt0] + [tgt0.clone() for _ in range(R - 1)]
+    drfs = [drf0] + [drf0.clone() for _ in range(R - 1)] if drf0 is not None else [None] * R
+    X = torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+    U = torch.from_numpy(d["uniforms"]).cuda()
+    out_t = torch.empty((w.B, w.K + 1), dtype=torch.int32, device="cuda")
+    out_n = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        spec_verify(tgts[i % R], drfs[i % R], X, U, w.temperature, w.top_k, w.top_p, out_tokens=out_t,
+                    out_num_accepted=out_n, draft_temperature=Td)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # region 1 (the step time): `steps` calls back to back, events on the
+    # launch stream around the whole loop
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+
+    # region 2 (the roofline): the library records HIP events around its
+    # streaming kernel on the launch stream, so that kernel's own average
+    # duration is measured live (the extra event records would inflate the
+    # step time, hence a region of their own)
+    profile_start()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = profile_stop()
+    stream_ms = prof["stream_kernel_ms"] / max(1, prof["calls"])
+    other_ms = prof["other_kernels_ms"] / max(1, prof["calls"])
+
+    # region 3 (per-call distribution): an event pair around each call
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (e0, e1) in enumerate(pairs):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = _percentiles([e0.elapsed_time(e1) for e0, e1 in pairs])
+
+    n_host = out_n.cpu().numpy()
+    emitted = int(np.sum(n_host[n_host >= 0] + 1))
+    del tgts, drfs
+    return {
+        "value": w.B / (ms_per_step / 1e3),
+        "ms_per_step": ms_per_step,
+        "per_call_ms": per_call,
+        "wall_s_timed": t_wall,
+        "tokens_per_s": emitted / (ms_per_step / 1e3),
+        "mean_emitted_per_sequence": emitted / w.B,
+        "bytes_per_step": bytes_per_step,
+        "input_copies": R,
+        "achieved": bytes_per_step / (stream_ms / 1e3) / 1e9,  # the streaming kernel reads every logit once
+        "kernel_ms": stream_ms,
+        "other_kernels_ms": other_ms,
+        "timed_calls": prof["calls"],
+        "step_frac": bytes_per_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
+def read_floor_leg(nbytes: int, steps: int, warmup: int, stream_kernel_ms: float) -> dict:
+    """The plain-read floor (sv_read_floor) over as many bytes as one step
+    streams, one launch per step over rotating copies, each launch timed by
+    an event pair on the launch stream."""
+    import torch
+
+    from rejection_sampling_verify_09_amd import read_floor
+
+    R = max(3, -(-640_000_000 // nbytes))
+    bufs = [torch.empty((nbytes,), dtype=torch.uint8, device="cuda").fill_(1 + i % 250) for i in range(R)]
+    outs = [torch.zeros((-(-nbytes // 16384),), dtype=torch.int32, device="cuda") for _ in range(R)]
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        read_floor(bufs[i % R], out=outs[i % R])
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (e0, e1) in enumerate(pairs):
+        e0.record(stream)
+        read_floor(bufs[i % R], out=outs[i % R])
+        e1.record(stream)
+    torch.cuda.synchronize()
+    pc = _percentiles([e0.elapsed_time(e1) for e0, e1 in pairs])
+    del bufs, outs
+    gbs = nbytes / (pc["mean"] / 1e3) / 1e9
+    return {"kernel": "read_kernel (sv_read_floor)", "what": "one plain read of the step's logit bytes with the "
+            "streaming kernel's 16-byte buffer loads and nothing else", "bytes": nbytes, "ms": pc["mean"],
+            "ms_p50": pc["p50"], "achieved": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "stream_kernel_over_floor": stream_kernel_ms / pc["mean"]}
 
 
 def cpu_baseline_sample(w, rows, u, budget_s: float):
@@ -547,6 +731,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="device copies of the inputs (0 = enough for 640 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload measurements that follow the headline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--sampler", action="store_true",
@@ -570,14 +756,20 @@ def main():
         sys.exit(2)
 
     import numpy as np
-    import torch
 
     from synth import HEADLINE, WORKLOADS, make_inputs
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
+    headline_path = not (args.copy_calibration or args.lmhead or args.ragged or args.draft_probs or args.sampler
+                         or args.draft_temperature is not None)
+    if not headline_path:
+        # the headline path first runs the oracle on the host (forking), and
+        # only then touches the GPU
+        import torch
+
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        torch.cuda.set_device(0)
 
     if args.copy_calibration:
         n = 1 << 28
@@ -588,8 +780,6 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": 5}), flush=True)
         return
-
-    from rejection_sampling_verify_09_amd import profile_start, profile_stop, sample, spec_verify
 
     if args.lmhead:
         run_lmhead(args)
@@ -607,9 +797,22 @@ def main():
         run_sampler(args, w, d)
         return
     Td = args.draft_temperature
+    cpu = None
     if Td is None:
         x = load_draft_tokens(name, w.B, w.K)
-    else:
+        if not args.no_cpu_baseline:
+            # before this process touches the GPU: the all-cores leg forks
+            cpu = cpu_baseline(w, d, x, args.cpu_seconds)
+            cpu["single_core"] = cpu_baseline_single(w, d, x, args.cpu_seconds)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    from rejection_sampling_verify_09_amd import sample
+
+    if Td is not None:
         # the drafts x ~ q at Td, drawn by the library itself (not timed)
         rows = torch.from_numpy(np.ascontiguousarray(d["draft"].reshape(w.B * w.K, w.V)))
         if w.dtype == "bf16":
@@ -619,71 +822,17 @@ def main():
         x = xt.cpu().numpy().reshape(w.B, w.K).astype(np.int32)
         del rows, ud, xt
 
-    def dev(a):
-        if w.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-    tgt0 = dev(d["target"])
-    drf0 = dev(d["draft"]) if w.K > 0 else None
-    bytes_per_step = w.logit_bytes  # every logit the step must read, once
-    R = args.copies or max(3, -(-640_000_000 // bytes_per_step))
-    tgts = [tgt0] + [tgt0.clone() for _ in range(R - 1)]
-    drfs = [drf0] + [drf0.clone() for _ in range(R - 1)] if drf0 is not None else [None] * R
-    X = torch.from_numpy(x).cuda()
-    U = torch.from_numpy(d["uniforms"]).cuda()
-    out_t = torch.empty((w.B, w.K + 1), dtype=torch.int32, device="cuda")
-    out_n = torch.empty((w.B,), dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        spec_verify(tgts[i % R], drfs[i % R], X, U, w.temperature, w.top_k, w.top_p, out_tokens=out_t,
-                    out_num_accepted=out_n, draft_temperature=Td)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # timed region 1 (the headline): K steps back to back, events on the
-    # launch stream around the whole loop
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t_wall0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
-
-    # timed region 2 (the roofline): the same K steps with the library
-    # recording HIP events around its streaming kernel on the launch stream,
-    # so that kernel's own average duration is measured live (the extra event
-    # records would inflate the step time, hence a region of their own)
-    profile_start()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    prof = profile_stop()
-    stream_ms = prof["stream_kernel_ms"] / max(1, prof["calls"])
-    other_ms = prof["other_kernels_ms"] / max(1, prof["calls"])
-
-    n_host = out_n.cpu().numpy()
-    emitted = int(np.sum(n_host[n_host >= 0] + 1))
-    seq_per_s = w.B / (ms_per_step / 1e3)
-    achieved = bytes_per_step / (stream_ms / 1e3) / 1e9  # the streaming kernel reads every logit once
-    traffic = measured_traffic(name)
-
+    m = measure_verify(w, d, x, args.steps, args.warmup, args.copies, Td=Td)
+    bytes_per_step = m["bytes_per_step"]
     result = {
         "metric": "spec-verify sequences/s + % HBM peak at B=64 K=6 V=128256 bf16"
                   + ("" if Td is None else f" (drafts at T_d={Td})"),
-        "value": seq_per_s,
+        "value": m["value"],
         "unit": "sequences/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -691,29 +840,50 @@ def main():
         "data": "synthetic (seeded logits of the workload's shape; no model weights)",
         "config": {
             "workload": name, "B": w.B, "K": w.K, "V": w.V, "logits": w.dtype, "temperature": w.temperature,
-            "top_k": w.top_k, "top_p": w.top_p, "rows": w.rows, "input_copies": R,
+            "top_k": w.top_k, "top_p": w.top_p, "rows": w.rows, "input_copies": m["input_copies"],
             "logit_bytes_per_step": bytes_per_step,
             **({} if Td is None else {"draft_temperature": Td}),
         },
-        "tokens_per_s": emitted / (ms_per_step / 1e3),
-        "mean_emitted_per_sequence": emitted / w.B,
-        "wall_s_timed": t_wall,
+        "tokens_per_s": m["tokens_per_s"],
+        "mean_emitted_per_sequence": m["mean_emitted_per_sequence"],
+        "per_call_ms": m["per_call_ms"],
+        "wall_s_timed": m["wall_s_timed"],
         "roofline": {
             "bound": "hbm",
-            "achieved": achieved,
+            "achieved": m["achieved"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
+            "frac": m["achieved"] / HBM_PEAK_GBS,
+            "traffic": measured_traffic(name),
             "kernel": "stream_kernel",
-            "kernel_ms": stream_ms,
-            "other_kernels_ms": other_ms,
-            "timed_calls": prof["calls"],
-            "step_frac": bytes_per_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_ms": m["kernel_ms"],
+            "other_kernels_ms": m["other_kernels_ms"],
+            "timed_calls": m["timed_calls"],
+            "step_frac": m["step_frac"],
         },
+        "achievable": read_floor_leg(bytes_per_step, args.steps, args.warmup, m["kernel_ms"]),
     }
+    if not args.no_configs and Td is None:
+        per = []
+        for cname, cw in WORKLOADS.items():
+            if cname == name:
+                continue
+            cd = make_inputs(cw)
+            cm = measure_verify(cw, cd, load_draft_tokens(cname, cw.B, cw.K), min(args.steps, 100),
+                                min(args.warmup, 10), 0)
+            del cd
+            line = {"workload": cname, "value": cm["value"], "unit": "sequences/s", "ms_per_step": cm["ms_per_step"],
+                    "per_call_ms": cm["per_call_ms"], "tokens_per_s": cm["tokens_per_s"],
+                    "logit_bytes_per_step": cm["bytes_per_step"], "stream_kernel_ms": cm["kernel_ms"],
+                    "other_kernels_ms": cm["other_kernels_ms"], "frac": cm["achieved"] / HBM_PEAK_GBS,
+                    "step_frac": cm["step_frac"], "steps": min(args.steps, 100)}
+            print(json.dumps({"config_line": line}), file=sys.stderr, flush=True)
+            per.append(line)
+            torch.cuda.empty_cache()
+        result["per_config"] = per
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, d, x, args.cpu_seconds, draft_temperature=Td)
+        result["cpu_baseline"] = cpu if cpu is not None else \
+            cpu_baseline_single(w, d, x, args.cpu_seconds, draft_temperature=Td)
     print(json.dumps(result), flush=True)
 
 

@@ -388,6 +388,23 @@ int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target,
                           int32_t d_target, int32_t d_draft, void* stream);
 
 /*
+ * sv_read_floor - measurement aid, not part of the verification: reads the
+ * nbytes at `data` (device memory) once, 16 KiB per workgroup with the
+ * loads of the streaming pass (16-byte buffer loads, four per thread), and
+ * does nothing else with them.  Its duration over a batch's logit bytes is
+ * the plain-read floor that the streaming pass of sv_spec_verify is compared
+ * against (that pass reads every logit once, as the pages' decode-step cost
+ * model has it: page www.gsyq.cn/news/428210 section 1.2).  out (device,
+ * ceil(nbytes / 16384) words, caller-owned) receives at out[i] the xor of
+ * block i's 32-bit words only when that xor equals key; other words are left
+ * as they were.  Asynchronous on `stream`.  Errors: SV_ERR_SHAPE (nbytes < 0,
+ * not a multiple of 16, or too many blocks for one launch; data must be
+ * 16-byte aligned), SV_ERR_NULL (data or out NULL with
+ * nbytes > 0), SV_ERR_HIP (launch failure).  nbytes == 0 does nothing.
+ */
+int sv_read_floor(const void* data, int64_t nbytes, uint32_t key, uint32_t* out, void* stream);
+
+/*
  * Launch timing for benchmarks.  Between sv_profile_start() and
  * sv_profile_stop(), every sv_spec_verify / sv_spec_verify_debug /
  * sv_spec_verify_dt / sv_spec_verify_ragged / sv_spec_verify_probs /

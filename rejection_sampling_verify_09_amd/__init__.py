@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     lm_logits,
     profile_start,
     profile_stop,
+    read_floor,
     release,
     scratch_bytes,
     stream_release,
@@ -27,5 +28,5 @@ from ._lib import (  # noqa: F401
     status_string,
 )
 
-__all__ = ["spec_verify", "spec_verify_noalloc", "spec_verify_lmhead", "lm_logits", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "release", "init", "stream_release", "scratch_bytes", "status_string", "lib",
+__all__ = ["spec_verify", "spec_verify_noalloc", "spec_verify_lmhead", "lm_logits", "spec_verify_probs", "spec_verify_ragged", "DraftLengthController", "sample", "filtered_probs", "profile_start", "profile_stop", "read_floor", "release", "init", "stream_release", "scratch_bytes", "status_string", "lib",
            "SpecVerifyError"]

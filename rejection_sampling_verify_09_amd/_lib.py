@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_version.argtypes = []
         L.sv_version.restype = ctypes.c_int
+        L.sv_read_floor.argtypes = [vp, ctypes.c_int64, ctypes.c_uint32, vp, vp]
+        L.sv_read_floor.restype = ctypes.c_int
         L.sv_profile_start.argtypes = []
         L.sv_profile_start.restype = ctypes.c_int
         L.sv_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
@@ -492,6 +494,28 @@ def sample(logits: torch.Tensor, uniforms: torch.Tensor, temperature: float = 1.
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_sample")
     return out_tokens, (out_prob if with_prob else None)
+
+
+READ_BLOCK = 16384  # bytes per workgroup of sv_read_floor
+
+
+def read_floor(data: torch.Tensor, key: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Plain read of a contiguous device tensor's bytes (sv_read_floor), the
+    floor the streaming pass is measured against.  Returns out: one int32
+    word per 16 KiB block, written only where the block's words xor to key."""
+    if not data.is_cuda or not data.is_contiguous() or data.data_ptr() % 16 != 0:
+        raise ValueError("data must be a contiguous, 16-byte aligned device tensor")
+    nbytes = data.numel() * data.element_size()
+    nblk = max(1, -(-nbytes // READ_BLOCK))
+    if out is None:
+        out = torch.zeros((nblk,), dtype=torch.int32, device=data.device)
+    if out.dtype != torch.int32 or not out.is_cuda or out.numel() < nblk:
+        raise ValueError("out must be an int32 device tensor of one word per 16 KiB block")
+    st = lib().sv_read_floor(ctypes.c_void_p(data.data_ptr()), nbytes, int(key) & 0xFFFFFFFF,
+                             ctypes.c_void_p(out.data_ptr()), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_read_floor")
+    return out
 
 
 def profile_start() -> None:

@@ -19,6 +19,7 @@ hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStre
 hipError_t launch_seq(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
 hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s);
 hipError_t launch_probs(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
+hipError_t launch_read(const void* p, int64_t nbytes, uint32_t key, uint32_t* out, unsigned grid, hipStream_t s);
 hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s);
 int64_t lm_gemm_tiles(int32_t M, int32_t V);
 }  // namespace sv
@@ -338,7 +339,7 @@ int plan_verify(const VerifyIn& in, Plan* p) {
   a.nsc = (int32_t)nsc;
   // sampling chunks per workgroup: up to SPW (fewer, longer workgroups
   // measured faster), while at least one workgroup per compute unit remains
-  a.spw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(SPW, (int64_t)B * nsc / 256));
+  a.spw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(SPW, (int64_t)B * nsc / 1024));
   a.nsw = (int32_t)((nsc + a.spw - 1) / a.spw);
   a.do_seq = 1;
   set_scalars(a, in.T, in.top_k, in.top_p, in.Td);
@@ -675,6 +676,14 @@ int sv_init(int device, void* stream, int32_t max_B, int32_t max_K, int32_t max_
   }
   if (hipSetDevice(cur) != hipSuccess && st == SV_OK) st = SV_ERR_HIP;
   return st;
+}
+
+int sv_read_floor(const void* data, int64_t nbytes, uint32_t key, uint32_t* out, void* stream) {
+  if (nbytes < 0 || nbytes % 16 != 0 || (nbytes + READ_BLOCK - 1) / READ_BLOCK > kMaxGrid) return SV_ERR_SHAPE;
+  if (nbytes == 0) return SV_OK;
+  if (!data || !out) return SV_ERR_NULL;
+  const unsigned grid = (unsigned)((nbytes + READ_BLOCK - 1) / READ_BLOCK);
+  return launch_read(data, nbytes, key, out, grid, (hipStream_t)stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 int sv_profile_start(void) {

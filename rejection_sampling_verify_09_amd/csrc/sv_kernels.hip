@@ -53,6 +53,21 @@ __device__ __forceinline__ double exp_tab(double x, const double* tab) {
   const int j = ki & 63;
   return ldexp(tab[j] * p, (ki - j) >> 6);
 }
+// 2^(y / 64) in double for y <= 0 (the weights of the unfiltered draw, whose
+// exponent, scaling and normaliser fold into y = x * A + B): y = k + f with
+// integer k and |f| <= 1/2, 2^(y/64) = 2^(k >> 6) * 2^((k & 63)/64) * e^r with
+// r = f ln2/64, |r| <= ln2/128, the powers from the LDS table and e^r from its
+// degree-5 Taylor polynomial as in exp_tab.  0 below -64 * 1100 (also -inf).
+__device__ __forceinline__ double exp2_64(double y, const double* tab) {
+  if (!(y > -70400.0)) return 0.0;
+  const double kf = rint(y);
+  const double r = (y - kf) * 0.010830424696249145;  // ln2 / 64
+  const double p = fma(fma(fma(fma(fma(r, 1.0 / 120.0, 1.0 / 24.0), r, 1.0 / 6.0), r, 0.5), r, 1.0), r, 1.0);
+  const int ki = (int)kf;
+  const int j = ki & 63;
+  return ldexp(tab[j] * p, (ki - j) >> 6);
+}
+
 __device__ __forceinline__ void build_exp_tab(double* tab) {
   __syncthreads();
   if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
@@ -1026,6 +1041,10 @@ struct ChunkRaw {
   uint4 r[EPT / ElemT<DT>::EPV];
 };
 
+// Cache policy of the streaming loads: non-temporal (the logits are read
+// once; measured 7% faster than the default policy for a plain read).
+constexpr int CPOL_NT = 2;
+
 // Issue the loads of the chunk of row rl at logit c0 (cn logits) as buffer
 // loads whose range ends with the chunk: a vector past the row end reads as
 // zero without a memory access, so no load depends on a lane condition.
@@ -1042,7 +1061,7 @@ __device__ __forceinline__ void issue_chunk(const Args& a, int rl, int c0, int c
     const int ub = u * WG * 16;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(cp + ub), (short)0, max(nbytes - ub, 0), 0x00020000);
-    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16, 0, 0);
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16, 0, CPOL_NT);
     cr.r[u] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
@@ -1346,7 +1365,7 @@ __device__ __forceinline__ uint32_t wave_walk(const uint32_t (&ek)[WR_EPL], cons
 
 // The same cut as wave_radix for at most n <= 64 entries, one per lane (key k,
 // 0 for none; weight wt): each entry's stable rank in descending key order
-// (one pass over the others' keys), the weights in that order, one prefix
+// (one pass over the n keys), the weights in that order, one prefix
 // sum, and the key at the first position where it reaches target.  The
 // weights of a key's ties all precede the next smaller key, so that key is
 // the largest t whose weight at or above t reaches target.
@@ -1356,8 +1375,7 @@ __device__ __forceinline__ uint32_t wave_cut64(uint32_t k, unsigned long long wt
   ws.cut.k[lane] = k;  // lanes from n on hold key 0 and never precede an entry
   wave_sync();
   int rank = 0;
-#pragma unroll
-  for (int j0 = 0; j0 < 64; j0 += 4) {
+  for (int j0 = 0; j0 < n; j0 += 4) {  // entries past n hold key 0 and never count
     const uint4 q = *reinterpret_cast<const uint4*>(&ws.cut.k[j0]);
     const uint32_t kq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -1424,14 +1442,20 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     ctq[1] = tp[1];
   }
   const float lx = (MODE != M_GREEDY && hx) ? load_elem<DT>(row_ptr(a, rl, ElemT<DT>::ESZ), xtok) : -INFINITY;
-  // with them, speculatively, entry `lane` of the first SPECC chunks' lists
-  // (most lists are shorter than 64 units): one round trip for most rows
+  // with them, speculatively, the first SE entries of the first SPECC
+  // chunks' lists (most top-p lists are shorter than 32 units, top-k lists
+  // than 64): one round trip for most rows.  Load i holds entry lane % SE of
+  // chunk i * SPL + lane / SE.
   constexpr int SPECC = 16;
-  uint64_t spec[SPECC];
+  constexpr int SE = MODE == M_TOPP ? 32 : 64, SPL = 64 / SE, NSPEC = SPECC / SPL;
+  uint64_t spec[NSPEC];
   const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
   if (FILT) {
 #pragma unroll
-    for (int i = 0; i < SPECC; ++i) spec[i] = i < nch ? cand[(size_t)i * CAND_CAP + lane] : 0ull;
+    for (int i = 0; i < NSPEC; ++i) {
+      const int c = i * SPL + lane / SE;
+      spec[i] = c < nch ? cand[(size_t)c * CAND_CAP + lane % SE] : 0ull;
+    }
   }
 
   const float m = dpp_wave_fmax(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])));
@@ -1494,24 +1518,22 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       n += __popcll(bm);
     };
     bool more = nch > SPECC;
-    {
-      uint64_t sv[SPECC];
-      bool sp[SPECC];
+    // the speculated entries of the chunks that hold candidates (most chunks
+    // of a row hold none: their max lies below lo); chunk c < 64 lives in lane c
 #pragma unroll
-      for (int i = 0; i < SPECC; ++i) {
-        const int cei = i < nch ? __builtin_amdgcn_readlane(ce4[0], i) : 0;  // chunk i < 64 lives in lane i
-        more |= cei > 64;
-        sv[i] = cand_entry_key(spec[i]);
-        sp[i] = lane < cei && (uint32_t)(sv[i] >> 32) >= lo;
-      }
-      n = wave_append(sv, sp, ws.keys, n, KEEP_CAP);
+    for (int i = 0; i < NSPEC; ++i) {
+      const int ce0 = __builtin_amdgcn_readlane(ce4[0], i * SPL);
+      const int ce1 = SPL == 2 ? __builtin_amdgcn_readlane(ce4[0], i * SPL + 1) : 0;
+      if (ce0 == 0 && ce1 == 0) continue;
+      more |= ce0 > SE || ce1 > SE;
+      take(spec[i], (lane % SE) < (lane / SE == 0 ? ce0 : ce1));
     }
     if (more) {
-      // the rest: chunks past the speculated ones, entries past the first 64
+      // the rest: chunks past the speculated ones, entries past the first SE
       for (int c = 0; c < nch; ++c) {
         const int cv = c < 64 ? ce4[0] : c < 128 ? ce4[1] : c < 192 ? ce4[2] : ce4[3];
         const int cec = __builtin_amdgcn_readlane(cv, c & 63);
-        for (int e0 = c < SPECC ? 64 : 0; e0 < cec; e0 += 64) {
+        for (int e0 = c < SPECC ? SE : 0; e0 < cec; e0 += 64) {
           const int e = e0 + lane;
           take(e < cec ? cand[(size_t)c * CAND_CAP + e] : 0ull, e < cec);
         }
@@ -1645,10 +1667,15 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     int pos[WR_EPL];
 #pragma unroll
     for (int r = 0; r < WR_EPL; ++r) pos[r] = 0;
-    for (int j = 0; j < nk; ++j) {
-      const int kj = ws.kept[j];
 #pragma unroll
-      for (int r = 0; r < WR_EPL; ++r) pos[r] += kj < ei[r] ? 1 : 0;
+    for (int r = 0; r < WR_EPL; ++r) {
+      if (64 * r >= n) break;  // no entries in this slot on any lane
+      for (int j0 = 0; j0 < nk; j0 += 4) {
+        const int4 q = *reinterpret_cast<const int4*>(&ws.kept[j0]);
+        const int kq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pos[r] += (j0 + i < nk && kq[i] < ei[r]) ? 1 : 0;
+      }
     }
 #pragma unroll
     for (int r = 0; r < WR_EPL; ++r)
@@ -1909,6 +1936,10 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
     const int xtok = i < K ? sm.x[i] : -1;
     RowRec rr;
     const bool ok = wave_row<DT, MODE>(a, rl, xtok, sm.w[w], rr, seq_sink(a, sm, j, rl));
+    // a kept list written to the scratch (too long for an LDS slot) is read
+    // back by this workgroup below: the wave that wrote it waits for its
+    // stores (no other wave's stores need waiting for)
+    if (FILT && ok && (j >= SQ_SLOTS || rr.nkept > SQ_SLOT_CAP)) __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) {
       if (ok) {
         sm.px[j] = rr.px;
@@ -1925,8 +1956,6 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
         sm.px[K + 1 + i] = (xtok >= 0 && xtok < a.V) ? (double)a.qprob[(size_t)(g.x0 + i) * a.V + xtok] : 0.0;
     }
   }
-  // the kept lists written to the scratch are read back by this workgroup only
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // ---- rows the candidate lists could not decide: the whole workgroup
   for (int wd = 0; 32 * wd < rps; ++wd) {
@@ -2084,16 +2113,23 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
 // row's record, and for a residual max(0, p_j - q_j) with q_j likewise (or
 // read from a row of probabilities, QP).  exp_tab and the reciprocals of the
 // normalisers keep this pass, which touches every logit of two rows, light.
+// p_j = exp((x_j - m) / T) / S = 2^(y / 64) with y = x_j * A + B, where
+// A = 64 log2(e) / T and B = -m A - 64 log2(S): one fma and exp2_64 per
+// weight.  (The rounding of A, B and y leaves a relative error of a few
+// 1e-15 in each weight.)
 struct PlainW {
-  float mp, mq;
-  double itp, itq;  // 1 / T of the two rows
-  double rsp, rsq;  // 1 / S of the two rows
+  double ap, bp;  // p's row
+  double aq, bq;  // q's row (logits)
 };
+__device__ __forceinline__ void plain_affine(float m, double invT, double S, double& A, double& B) {
+  A = invT * 92.33248261689366;  // 64 log2(e)
+  B = fma(-(double)m, A, -64.0 * log2(S));
+}
 template <bool QP>
 __device__ __forceinline__ double plain_w(float xp, float xq, const PlainW& c, bool res, const double* tab) {
-  const double p = exp_tab(((double)xp - (double)c.mp) * c.itp, tab) * c.rsp;
+  const double p = exp2_64(fma((double)xp, c.ap, c.bp), tab);
   if (!res) return p;
-  const double q = QP ? (double)xq : exp_tab(((double)xq - (double)c.mq) * c.itq, tab) * c.rsq;
+  const double q = QP ? (double)xq : exp2_64(fma((double)xq, c.aq, c.bq), tab);
   const double d = p - q;
   return d > 0.0 ? d : 0.0;
 }
@@ -2143,13 +2179,9 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   const bool active = n >= 0;
   const bool res = active && n < sr.k;
   build_exp_tab(sm.etab);
-  PlainW cw;
-  cw.mp = sr.mp;
-  cw.mq = sr.mq;
-  cw.rsp = 1.0 / sr.sp;
-  cw.rsq = 1.0 / sr.sq;
-  cw.itp = active ? row_temp(a, sr.rp).invT : 0.0;
-  cw.itq = (active && !QP) ? row_temp(a, sr.rq).invT : 0.0;
+  PlainW cw = {0.0, 0.0, 0.0, 0.0};
+  if (active) plain_affine(sr.mp, row_temp(a, sr.rp).invT, sr.sp, cw.ap, cw.bp);
+  if (active && res && !QP) plain_affine(sr.mq, row_temp(a, sr.rq).invT, sr.sq, cw.aq, cw.bq);
   const char* pr = active ? row_ptr(a, sr.rp, ESZ) : nullptr;
   const char* qr = !active ? nullptr
                    : QP    ? reinterpret_cast<const char*>(a.qprob + (size_t)sr.rq * a.V)
@@ -2387,6 +2419,43 @@ hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s)
                              : lay == LAY_QP ? (KFn)sample_kernel<D_F32, LAY_QP>
                                              : (KFn)sample_kernel<D_F32, LAY_RECT>);
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
+  return hipGetLastError();
+}
+
+// Plain read of nbytes from p, 16 KiB per workgroup with the streaming
+// kernel's loads (four 16-byte non-temporal buffer loads per thread, each range ending
+// with the workgroup's block, so a tail block reads zeros past the end
+// without a memory access), and nothing else: the floor that the streaming
+// pass's loads alone reach.  The xor of a block's words is written to
+// out[block] only when it equals key, so that the loads cannot be dropped and
+// almost nothing is written.
+__global__ void __launch_bounds__(WG) read_kernel(const char* p, int64_t nbytes, uint32_t key, uint32_t* out) {
+  const int64_t b0 = (int64_t)blockIdx.x * READ_BLOCK;
+  const int nb = (int)(nbytes - b0 < READ_BLOCK ? nbytes - b0 : READ_BLOCK);
+  uint32_t x = 0;
+#pragma unroll
+  for (int u = 0; u < READ_BLOCK / (WG * 16); ++u) {
+    const int ub = u * WG * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p + b0 + ub), (short)0, max(nb - ub, 0), 0x00020000);
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16, 0, CPOL_NT);
+    x ^= (w[0] ^ w[1]) ^ (w[2] ^ w[3]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+  __shared__ uint32_t wx[NWAVE];
+  if ((threadIdx.x & 63) == 0) wx[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t y = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVE; ++i) y ^= wx[i];
+    if (y == key) out[blockIdx.x] = y;
+  }
+}
+
+hipError_t launch_read(const void* p, int64_t nbytes, uint32_t key, uint32_t* out, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(WG), 0, s, (const char*)p, nbytes, key, out);
   return hipGetLastError();
 }
 

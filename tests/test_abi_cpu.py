@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
               "sv_spec_verify_probs", "sv_lm_logits", "sv_spec_verify_lmhead",
               "sv_filtered_probs", "sv_sample", "sv_dynk_create", "sv_dynk_observe", "sv_dynk_k", "sv_dynk_destroy",
               "sv_release", "sv_scratch_bytes", "sv_init", "sv_stream_release", "sv_spec_verify_noalloc",
-              "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop"]:
+              "sv_status_string", "sv_version", "sv_profile_start", "sv_profile_stop", "sv_read_floor"]:
         assert s in syms
 
 
@@ -127,6 +127,16 @@ def test_draft_temperature_validation():
     assert f(B=-1) == L.SV_ERR_SHAPE
     assert f(out_n=None) == L.SV_ERR_NULL
     assert f(B=0) == L.SV_OK
+
+
+def test_read_floor_validation():
+    lib = L.lib()
+    assert lib.sv_read_floor(FAKE, -1, 0, FAKE, None) == L.SV_ERR_SHAPE
+    assert lib.sv_read_floor(FAKE, 24, 0, FAKE, None) == L.SV_ERR_SHAPE
+    assert lib.sv_read_floor(FAKE, (1 << 62), 0, FAKE, None) == L.SV_ERR_SHAPE
+    assert lib.sv_read_floor(None, 0, 0, None, None) == L.SV_OK
+    assert lib.sv_read_floor(None, 16, 0, FAKE, None) == L.SV_ERR_NULL
+    assert lib.sv_read_floor(FAKE, 16, 0, None, None) == L.SV_ERR_NULL
 
 
 def test_profile_without_calls_reports_nothing():

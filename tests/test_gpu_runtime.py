@@ -243,3 +243,27 @@ def test_init_sizes_the_stream_scratch_once():
             assert scratch_bytes() == held, (w.name, scratch_bytes(), held)
     stream_release(s)
     assert scratch_bytes() < held
+
+
+def test_read_floor_reads_every_block():
+    """sv_read_floor: the xor of each 16 KiB block's words, taken on the
+    host, is the key that makes the kernel write that block's word (and no
+    other); a tail block shorter than 16 KiB is read up to the end only."""
+    import torch
+
+    from rejection_sampling_verify_09_amd import read_floor
+
+    rng = np.random.default_rng(5)
+    nbytes = 5 * 16384 + 4096 + 48
+    words = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    data = torch.from_numpy(words.view(np.int32)).cuda()
+    nblk = -(-nbytes // 16384)
+    xors = [int(np.bitwise_xor.reduce(words[i * 4096:(i + 1) * 4096])) for i in range(nblk)]
+    for blk in (0, 3, nblk - 1):
+        out = torch.full((nblk,), 7, dtype=torch.int32, device="cuda")
+        read_floor(data, key=xors[blk], out=out)
+        got = out.cpu().numpy().view(np.uint32)
+        want = np.full(nblk, 7, dtype=np.uint32)
+        want[[i for i in range(nblk) if xors[i] == xors[blk]]] = xors[blk]
+        log(f"[read floor] block {blk} of {nblk}")
+        assert np.array_equal(got, want)
