@@ -339,7 +339,7 @@ int plan_verify(const VerifyIn& in, Plan* p) {
   a.nsc = (int32_t)nsc;
   // sampling chunks per workgroup: up to SPW (fewer, longer workgroups
   // measured faster), while at least one workgroup per compute unit remains
-  a.spw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(SPW, (int64_t)B * nsc / 1024));
+  a.spw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(SPW, (int64_t)B * nsc / 256));
   a.nsw = (int32_t)((nsc + a.spw - 1) / a.spw);
   a.do_seq = 1;
   set_scalars(a, in.T, in.top_k, in.top_p, in.Td);

@@ -10,20 +10,28 @@
 //
 // Data flow (one call, all rows of all sequences):
 //   stream_kernel   one workgroup per (row, 8192-logit chunk).  Reads the
-//                   chunk once from HBM with 16-byte loads into registers,
-//                   and produces the chunk max, sum exp((x - max) / T) and
-//                   the filter candidates.  The last chunk of a row to finish
-//                   merges the row (max, normaliser, top-k / top-p threshold,
-//                   kept list, probability of the drafted token); the last
-//                   row of a sequence to finish runs the accept tests, the
-//                   first-rejection scan and, for filtered and greedy rows,
-//                   the final draw.
+//                   chunk once from HBM (16-byte non-temporal loads into
+//                   registers) and writes the chunk's record: max, sum of
+//                   exp((x - max) / T) in the record's convention, the filter
+//                   candidates (16-byte units at or above the chunk's bound)
+//                   and the greedy arg-max.  Its first workgroups also clear
+//                   the call's arrival counters and check ragged offsets.
+//   seq_kernel      one workgroup per sequence.  Wave j merges row j of the
+//                   sequence (max, normaliser, top-k / top-p threshold, kept
+//                   list in LDS, p or q of the drafted token); a row the
+//                   candidate lists cannot decide is merged by the whole
+//                   workgroup from the full row.  Then one wave runs the
+//                   accept tests, the first-rejection scan and, for filtered
+//                   and greedy rows, the final draw from the kept lists.
 //   sample_kernel   unfiltered rows only: the final draw needs the whole
-//                   residual / bonus row.  One workgroup per (sequence,
-//                   2048-logit chunk) computes the weights in double and their
-//                   per-segment sums; the last one scans the segment sums,
-//                   finds the segment holding u*Z and rescans it.
-//   probs_kernel    writes full filtered rows (sv_filtered_probs).
+//                   residual / bonus row.  One workgroup per (sequence, up to
+//                   four 2048-logit chunks) computes the weights in double
+//                   and their per-segment sums; the last one to arrive scans
+//                   the segment sums, finds the segment holding u*Z and
+//                   rescans it.
+//   row_kernel      sv_filtered_probs only: the row merges, without
+//                   sequences;  probs_kernel then writes full filtered rows.
+//   read_kernel     measurement aid (sv_read_floor): a plain read.
 #include "sv_common.hpp"
 
 #include <hip/hip_ext.h>
@@ -66,6 +74,16 @@ __device__ __forceinline__ double exp2_64(double y, const double* tab) {
   const int ki = (int)kf;
   const int j = ki & 63;
   return ldexp(tab[j] * p, (ki - j) >> 6);
+}
+
+// chunk_weight with exp2_64 for the power of two (the same value up to a few
+// units in the last place).
+__device__ __forceinline__ double chunk_weight_tab(double s_c, float m_c, float m, float c2, double invT,
+                                                   const double* tab) {
+  if (!(m_c > -INFINITY)) return 0.0;
+  const float Mi = __builtin_ceilf(m_c * c2);
+  const double f = Mi < INFINITY ? (double)Mi - (double)m_c * (double)c2 : 0.0;
+  return s_c * exp2_64(64.0 * (f + ((double)m_c - (double)m) * (invT * 1.4426950408889634074)), tab);
 }
 
 __device__ __forceinline__ void build_exp_tab(double* tab) {
@@ -912,7 +930,7 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
       if (t < CTOP) __builtin_nontemporal_store((uint32_t)sm.s.tk[t], &a.ctop[(size_t)chunk_id * CTOP + t]);
     }
     thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
-    const int w = t >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wn = wave_emit<DT, VEC>(um, gm, thr, c0, &sm.s.cand[w * CAND_CAP], CAND_CAP);
     if ((t & 63) == 0) sm.s.wn[w] = wn;
     __syncthreads();
@@ -1109,7 +1127,7 @@ __device__ __forceinline__ void stream_vec_body(const Args& a, int item, int rl,
                                                 const ChunkRaw<DT>& cr, Smem& sm) {
   constexpr int EPV = ElemT<DT>::EPV, NV = EPT / EPV;
   constexpr bool SUM = MODE == M_PLAIN || MODE == M_TOPP;
-  const int t = threadIdx.x, w = t >> 6;
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const float c2 = row_temp(a, rl).c2;
 
   float v[EPT], um[NV];
@@ -1212,7 +1230,8 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_ker
 }
 
 // ---------------------------------------------------------------------------
-// row kernel: wave-level row merge, then the sequence's accept tests and draw
+// row merges: one wave per row (wave_row), the whole workgroup when the
+// candidate lists cannot decide (row_finalize)
 // ---------------------------------------------------------------------------
 
 // Orders LDS accesses of the lanes of one wave (the wave's LDS operations
@@ -1400,13 +1419,14 @@ __device__ __forceinline__ uint32_t wave_cut64(uint32_t k, unsigned long long wt
 // then takes the row).
 template <int DT, int MODE, class Sink>
 __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRowSm& ws, RowRec& rr,
-                                         const Sink& sink) {
+                                         const Sink& sink, const double* tab) {
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   const int lane = threadIdx.x & 63, nch = a.nchunks;
   const ChunkRec* cr = a.chunk + (size_t)rl * nch;
   const bool hx = xtok >= 0 && xtok < a.V;
   const RowT rt = row_temp(a, rl);
   const double invT = rt.invT;
+  const double A64 = invT * 92.33248261689366;  // 64 log2(e) / T: exp((x - m) / T) = exp2_64((x - m) * A64)
 
   // one round trip: the chunk records (chunk lane + 64 i) and the drafted
   // token's logit
@@ -1473,7 +1493,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     double sl = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (64 * i < nch) sl += chunk_weight(cs[i], cm[i], m, rt.c2, invT);  // uniform
+      if (64 * i < nch) sl += chunk_weight_tab(cs[i], cm[i], m, rt.c2, invT, tab);  // uniform
     const double S = dpp_wave_sum(sl);
     rr.S = S;
     if (!(S > 0.0 && S < INFINITY)) bad = true;
@@ -1591,7 +1611,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
         const uint64_t v = e < n ? ws.keys[e] : 0ull;
         ek[r] = (uint32_t)(v >> 32);
         ei[r] = (int)(uint32_t)v;
-        ew[r] = e < n ? exp(((double)key_val(ek[r]) - (double)m) * invT) : 0.0;
+        ew[r] = e < n ? exp2_64(((double)key_val(ek[r]) - (double)m) * A64, tab) : 0.0;
       }
     }
     wave_sync();
@@ -1688,7 +1708,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
     if (MODE == M_GREEDY) {
       rr.px = xtok == rr.arg ? 1.0 : 0.0;
     } else if (ord_key(lx) >= rr.tau) {
-      rr.px = exp(((double)lx - (double)m) * invT) / (MODE == M_PLAIN ? rr.S : rr.S_kept);
+      rr.px = exp2_64(((double)lx - (double)m) * A64, tab) / (MODE == M_PLAIN ? rr.S : rr.S_kept);
     }
   }
   if (bad) rr.flags |= RF_BAD;
@@ -1705,6 +1725,7 @@ struct RowKSm {
     WaveRowSm w;  // wave-level merge
     Smem blk;     // block-level merge
   };
+  double etab[64];  // 2^(j/64) for exp2_64
   int32_t fast;
 };
 
@@ -1714,8 +1735,10 @@ __global__ void __launch_bounds__(WG) row_kernel(Args a) {
   const int t = threadIdx.x;
   const int rl = (int)blockIdx.x;
   if (t < 64) {
+    sm.etab[t] = exp2((double)t / 64.0);  // read by this wave only
+    wave_sync();
     RowRec rr;
-    const bool ok = wave_row<DT, MODE>(a, rl, -1, sm.w, rr, NoSink{});
+    const bool ok = wave_row<DT, MODE>(a, rl, -1, sm.w, rr, NoSink{}, sm.etab);
     if (t == 0) sm.fast = ok;
   }
   __syncthreads();
@@ -1862,6 +1885,7 @@ struct SeqKSm {
   int32_t arg[MAX_RPS]; // greedy arg-max
   int32_t x[MAX_K];
   float u[MAX_K + 1];
+  double etab[64];  // 2^(j/64) for exp2_64
   uint32_t fail[(MAX_RPS + 31) / 32];  // rows the waves could not merge from the candidate lists
   int32_t n, big;
 };
@@ -1901,13 +1925,18 @@ __device__ __forceinline__ SeqSink seq_sink(const Args& a, SeqKSm& sm, int j, in
 // kernel's first workgroup), or rectangular with q given as probabilities
 // (no draft rows: each target row i < K reads the given q(x_i), and the
 // residual draw reads q at the target's kept tokens).
-template <int DT, int MODE, int LAY>
+// NR: rows per wave (2 for sequences of more than SQ_WAVES rows; a separate
+// instantiation, so that the common case keeps its register allocation).
+template <int DT, int MODE, int LAY, int NR>
 __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
   __shared__ SeqKSm sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   constexpr bool RAG = LAY == LAY_RAG, QP = LAY == LAY_QP;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  // the wave index, made a scalar (the compiler does not see that t >> 6 is
+  // the same in every lane of a wave): the per-row code then branches and
+  // indexes on scalars
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int b = (int)blockIdx.x;
   if (RAG && a.cflag[0] == 0) {
     // offsets that describe no packing: every sequence is a sentinel
@@ -1917,25 +1946,25 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
   const SeqGeo g = seq_geo<RAG>(a, b);
   const int K = g.K;
   const int rps = (MODE == M_GREEDY || QP) ? K + 1 : 2 * K + 1;
-  // rows j >= SQ_WAVES (sequences of more than SQ_WAVES rows) are merged by
-  // the whole workgroup below, one after another
+  // rows j >= NR SQ_WAVES (sequences of more rows than the waves take) are
+  // merged by the whole workgroup below, one after another
   if (t < (MAX_RPS + 31) / 32) {
-    const int j0 = 32 * t;
-    sm.fail[t] = j0 >= SQ_WAVES ? ~0u : (SQ_WAVES - j0 >= 32 ? 0u : ~0u << (SQ_WAVES - j0));
+    const int j0 = 32 * t, nw = NR * SQ_WAVES;
+    sm.fail[t] = j0 >= nw ? ~0u : (nw - j0 >= 32 ? 0u : ~0u << (nw - j0));
   }
   if (t < K) sm.x[t] = a.X[(size_t)g.x0 + t];
   if (t >= 256 && t - 256 <= K) sm.u[t - 256] = a.U[(size_t)g.t0 + (t - 256)];
+  if (t >= 512 && t < 576) sm.etab[t - 512] = exp2((double)(t - 512) / 64.0);
   __syncthreads();
 
-  // ---- the sequence's rows, one wave each (a loop here would keep values
-  // across its iterations and spill registers)
-  if (w < rps) {
-    const int j = w;
+  // ---- the sequence's rows, one wave each: wave w merges row w, and (NR = 2)
+  // row w + SQ_WAVES when the sequence has that many
+  auto merge_row = [&](const int j) {
     const int rl = seq_row<RAG>(a, g, j);
     const int i = j <= K ? j : j - K - 1;  // position of the row
     const int xtok = i < K ? sm.x[i] : -1;
     RowRec rr;
-    const bool ok = wave_row<DT, MODE>(a, rl, xtok, sm.w[w], rr, seq_sink(a, sm, j, rl));
+    const bool ok = wave_row<DT, MODE>(a, rl, xtok, sm.w[w], rr, seq_sink(a, sm, j, rl), sm.etab);
     // a kept list written to the scratch (too long for an LDS slot) is read
     // back by this workgroup below: the wave that wrote it waits for its
     // stores (no other wave's stores need waiting for)
@@ -1955,7 +1984,9 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
       if (QP && i < K && j <= K)
         sm.px[K + 1 + i] = (xtok >= 0 && xtok < a.V) ? (double)a.qprob[(size_t)(g.x0 + i) * a.V + xtok] : 0.0;
     }
-  }
+  };
+  if (w < rps) merge_row(w);
+  if (NR > 1 && w + SQ_WAVES < rps) merge_row(w + SQ_WAVES);
   __syncthreads();
   // ---- rows the candidate lists could not decide: the whole workgroup
   for (int wd = 0; 32 * wd < rps; ++wd) {
@@ -2342,21 +2373,21 @@ static KFn pick_stream_mode(int mode, bool vec) {
   }
 }
 
-template <int DT, int LAY>
+template <int DT, int LAY, int NR>
 static KFn pick_seq(int mode) {
   switch (mode) {
-    case M_PLAIN: return (KFn)seq_kernel<DT, M_PLAIN, LAY>;
-    case M_TOPK: return (KFn)seq_kernel<DT, M_TOPK, LAY>;
-    case M_TOPP: return (KFn)seq_kernel<DT, M_TOPP, LAY>;
-    case M_TOPKP: return (KFn)seq_kernel<DT, M_TOPKP, LAY>;
-    default: return (KFn)seq_kernel<DT, M_GREEDY, LAY>;
+    case M_PLAIN: return (KFn)seq_kernel<DT, M_PLAIN, LAY, NR>;
+    case M_TOPK: return (KFn)seq_kernel<DT, M_TOPK, LAY, NR>;
+    case M_TOPP: return (KFn)seq_kernel<DT, M_TOPP, LAY, NR>;
+    case M_TOPKP: return (KFn)seq_kernel<DT, M_TOPKP, LAY, NR>;
+    default: return (KFn)seq_kernel<DT, M_GREEDY, LAY, NR>;
   }
 }
 
-template <int DT>
+template <int DT, int NR>
 static KFn pick_seq_lay(int mode, int lay) {
-  return lay == LAY_RAG ? pick_seq<DT, LAY_RAG>(mode) : lay == LAY_QP ? pick_seq<DT, LAY_QP>(mode)
-                                                                      : pick_seq<DT, LAY_RECT>(mode);
+  return lay == LAY_RAG ? pick_seq<DT, LAY_RAG, NR>(mode) : lay == LAY_QP ? pick_seq<DT, LAY_QP, NR>(mode)
+                                                                          : pick_seq<DT, LAY_RECT, NR>(mode);
 }
 
 static int layout_of(const Args& a) { return a.cu ? LAY_RAG : a.qprob ? LAY_QP : LAY_RECT; }
@@ -2405,7 +2436,13 @@ hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStre
 // The sequences: one workgroup of SQ_BS threads per sequence.
 hipError_t launch_seq(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
   const int lay = layout_of(a);
-  KFn f = dtype == D_BF16 ? pick_seq_lay<D_BF16>(mode, lay) : pick_seq_lay<D_F32>(mode, lay);
+  // the most rows a sequence of this call has
+  const int rps_max = (mode == M_GREEDY || lay == LAY_QP) ? a.Kmax + 1 : 2 * a.Kmax + 1;
+  KFn f;
+  if (rps_max > SQ_WAVES)
+    f = dtype == D_BF16 ? pick_seq_lay<D_BF16, 2>(mode, lay) : pick_seq_lay<D_F32, 2>(mode, lay);
+  else
+    f = dtype == D_BF16 ? pick_seq_lay<D_BF16, 1>(mode, lay) : pick_seq_lay<D_F32, 1>(mode, lay);
   hipLaunchKernelGGL(f, dim3(grid), dim3(SQ_BS), 0, s, a);
   return hipGetLastError();
 }
