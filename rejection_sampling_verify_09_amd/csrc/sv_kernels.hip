@@ -337,6 +337,204 @@ __device__ __forceinline__ int row_keep(const char* rp, int V, uint32_t tau, flo
   return sm.ncand;
 }
 
+// The 8 logits j0 .. j0+7 of a row (-inf past V): one 16-byte load per 8
+// bf16 (two per 8 f32) when rows are 16-byte aligned and the 8 lie in the row.
+template <int DT>
+__device__ __forceinline__ void load8(const char* row, int j0, int V, bool vec, float (&x)[8]) {
+  if (vec && j0 + 8 <= V) {
+    if (DT == D_BF16) {
+      const uint4 r = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 2);
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+      }
+    } else {
+      const uint4 r0 = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 4);
+      const uint4 r1 = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 4 + 16);
+      x[0] = __uint_as_float(r0.x); x[1] = __uint_as_float(r0.y); x[2] = __uint_as_float(r0.z); x[3] = __uint_as_float(r0.w);
+      x[4] = __uint_as_float(r1.x); x[5] = __uint_as_float(r1.y); x[6] = __uint_as_float(r1.z); x[7] = __uint_as_float(r1.w);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = j0 + e < V ? load_elem<DT>(row, j0 + e) : -INFINITY;
+  }
+}
+
+// Bins of the full-row top-p search: ZB bins per unit of z = (m - x) / T, the
+// last bin also holding everything past TOPP_NB / ZB units.  The same f32
+// arithmetic in both passes, so an element lands in the same bin each time,
+// and bins are monotone in x (a lower bin holds only larger logits).
+constexpr int TOPP_NB = 2048;
+constexpr float TOPP_ZB = 51.2f;
+__device__ __forceinline__ int topp_bin(float x, float m, float itf) {
+  const float z = (m - x) * itf;
+  return (int)fminf(z * TOPP_ZB, (float)(TOPP_NB - 1));
+}
+
+// Top-p cut over the whole row, for rows whose nucleus reaches below the
+// candidate window: two pipelined passes instead of row_radix's five
+// element-by-element ones.  Pass 1 adds every logit's f32 mass exp(-z) into
+// its bin (LDS float atomics) and finds the bin where the cumulative mass
+// crosses top_p.  Pass 2 takes, exactly (the fixed-point weights of the wave
+// cut, summed as integers), the mass of every logit in the bins above a
+// window of five bins around that one, and collects the window's entries;
+// they are sorted by key and the cut is the first key at which the mass
+// reaches the target, ties included, as in wave_cut64.  Returns false,
+// having decided nothing, when the exact cut lies outside the window (the
+// f32 masses misplaced it) or the window holds more than ROW_CAND entries;
+// the caller then runs row_radix.  Otherwise *tau is the cut, *nall the kept
+// count, *skept the sum of exp((x - m) / T) over the kept set and, when
+// *nall <= KEEP_CAP, the kept entries (key << 32 | index) are in sm.r.keys.
+// Needs sm.etab (build_exp_tab).
+template <int DT, int BS>
+__device__ __forceinline__ bool row_topp_cut(const char* rp, int V, bool vec, float m, double invT, double snorm,
+                                             double top_p, Smem& sm, uint32_t* tau, int* nall, double* skept) {
+  static_assert(TOPP_NB % BS == 0 && TOPP_NB * sizeof(float) <= ROW_CAND * sizeof(uint64_t), "histogram layout");
+  constexpr int PB = TOPP_NB / BS;  // bins per thread in the scan
+  const int t = threadIdx.x;
+  const float itf = (float)invT;
+  const double A64 = invT * 92.33248261689366;  // 64 log2(e) / T
+  float* H = reinterpret_cast<float*>(sm.r.cand);
+  __syncthreads();
+  for (int d = t; d < TOPP_NB; d += BS) H[d] = 0.0f;
+  __syncthreads();
+  // pass 1: f32 masses by bin; two tiles of 8 logits per thread in flight
+  {
+    float xa[8], xb[8];
+    int j0 = 8 * t;
+    load8<DT>(rp, j0, V, vec, xa);
+    for (; j0 < V; j0 += 16 * BS) {
+      const int j1 = j0 + 8 * BS;
+      load8<DT>(rp, j1, V, vec, xb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (xa[e] > -INFINITY)
+          atomicAdd(&H[topp_bin(xa[e], m, itf)], __builtin_amdgcn_exp2f((xa[e] - m) * itf * 1.44269504f));
+      load8<DT>(rp, j1 + 8 * BS, V, vec, xa);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (xb[e] > -INFINITY)
+          atomicAdd(&H[topp_bin(xb[e], m, itf)], __builtin_amdgcn_exp2f((xb[e] - m) * itf * 1.44269504f));
+    }
+  }
+  __syncthreads();
+  // the bin where the cumulative f32 mass crosses top_p of the total
+  double hb[PB], ls = 0.0;
+#pragma unroll
+  for (int i = 0; i < PB; ++i) {
+    hb[i] = (double)H[t * PB + i];
+    ls += hb[i];
+  }
+  double total;
+  const double incl = block_incl_scan<BS / 64>(ls, sm.red, &total);
+  const double tf = top_p * total;
+  int bx = INT_MAX;
+  double c = incl - ls;
+#pragma unroll
+  for (int i = 0; i < PB; ++i) {
+    c += hb[i];
+    if (bx == INT_MAX && c >= tf) bx = t * PB + i;
+  }
+  bx = block_min_i<BS / 64>(bx, sm.red);
+  if (bx == INT_MAX) bx = TOPP_NB - 1;
+  const int bl = max(bx - 2, 0), bh = min(bx + 3, TOPP_NB);
+  // pass 2: exact mass above the window, the window's entries
+  __syncthreads();
+  if (t == 0) {
+    sm.ncand = 0;  // kept entries above the window (listed while they fit)
+    sm.i1 = 0;     // window entries
+  }
+  __syncthreads();
+  double wa = 0.0, ea = 0.0;  // fixed-point weights (integers, exact as doubles) and exp sums above
+  int na = 0;
+  {
+    float xa[8];
+    for (int j0 = 8 * t; j0 < V; j0 += 8 * BS) {
+      load8<DT>(rp, j0, V, vec, xa);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = xa[e];
+        if (!(x > -INFINITY)) continue;
+        const int bin = topp_bin(x, m, itf);
+        if (bin >= bh) continue;
+        const uint64_t ent = ((uint64_t)ord_key(x) << 32) | (uint32_t)(j0 + e);
+        if (bin < bl) {
+          const double ew = exp2_64(((double)x - (double)m) * A64, sm.etab);
+          wa += (double)(unsigned long long)(ew / snorm * MASS_SCALE);
+          ea += ew;
+          ++na;
+          const int slot = atomicAdd(&sm.ncand, 1);
+          if (slot < KEEP_CAP) sm.r.keys[slot] = ent;
+        } else {
+          const int slot = atomicAdd(&sm.i1, 1);
+          if (slot < ROW_CAND) sm.r.cand[slot] = ent;
+        }
+      }
+    }
+  }
+  const double A = block_sum<BS / 64>(wa, sm.red);
+  const double EA = block_sum<BS / 64>(ea, sm.red);
+  const int NA = block_sum_i<BS / 64>(na, sm.red);
+  const int nw = sm.i1;
+  const double tgt = (double)(unsigned long long)(top_p * MASS_SCALE);
+  if (nw > ROW_CAND || A >= tgt) return false;  // uniform
+  const int np2 = pow2_at_least(nw < 2 ? 2 : nw);
+  __syncthreads();
+  for (int e = nw + t; e < np2; e += BS) sm.r.cand[e] = 0ull;
+  bitonic_desc<BS>(sm.r.cand, np2);
+  // the window's weights in key order (contiguous entries per thread)
+  constexpr int PW = ROW_CAND / BS;
+  uint32_t kw[PW];
+  double ww[PW], ew2[PW], lw = 0.0;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int e = t * PW + i;
+    const uint64_t en = e < nw ? sm.r.cand[e] : 0ull;
+    kw[i] = (uint32_t)(en >> 32);
+    ew2[i] = e < nw ? exp2_64(((double)key_val(kw[i]) - (double)m) * A64, sm.etab) : 0.0;
+    ww[i] = e < nw ? (double)(unsigned long long)(ew2[i] / snorm * MASS_SCALE) : 0.0;
+    lw += ww[i];
+  }
+  double wtot;
+  const double wincl = block_incl_scan<BS / 64>(lw, sm.red, &wtot);
+  double cw = A + (wincl - lw);
+  int ex = INT_MAX;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    cw += ww[i];
+    if (ex == INT_MAX && t * PW + i < nw && cw >= tgt) ex = t * PW + i;
+  }
+  ex = block_min_i<BS / 64>(ex, sm.red);
+  if (ex == INT_MAX) return false;  // the cut lies below the window (uniform)
+  __syncthreads();
+  const uint32_t tk = (uint32_t)(sm.r.cand[ex] >> 32);
+  // kept: everything above the window, and the window's keys >= tk
+  int nk = 0;
+  double ek = 0.0;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    if (t * PW + i < nw && kw[i] >= tk) {
+      ++nk;
+      ek += ew2[i];
+    }
+  }
+  const int NW = block_sum_i<BS / 64>(nk, sm.red);
+  const double EW = block_sum<BS / 64>(ek, sm.red);
+  const int n = NA + NW;
+  if (n <= KEEP_CAP) {
+    // the window's kept entries lead the sorted window: append them
+    __syncthreads();
+    for (int e = t; e < NW; e += BS) sm.r.keys[NA + e] = sm.r.cand[e];
+    __syncthreads();
+  }
+  *tau = tk;
+  *nall = n;
+  *skept = EA + EW;
+  return true;
+}
+
 // Radix select (8 bits per pass, counts in LDS) of the k-th largest key among
 // the n candidates in sm.r.cand.
 template <int BS>
@@ -429,8 +627,15 @@ __device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp
   double skept = 0.0;  // normaliser over the kept set (when big)
   bool fb = ncand_total > ROW_LOAD_MAX;
 
-  if (!fb) {
-    // Candidates at or above lo (at most ROW_CAND), read in batches of
+  // Top-p whose nucleus reaches below lo takes a second pass with the window
+  // doubled (lo2): the lists of the chunks whose own bound lies at or below
+  // lo2 hold every unit at or above it, and the few chunks whose bound lies
+  // above it (their max is near the row max) are scanned whole.
+  const uint32_t lo2 = MODE == M_TOPP ? ord_key(m - 2.0f * rt.win) : lo;
+  for (int pass = 0; pass < 2 && !fb; ++pass) {
+    const uint32_t lg = pass == 0 ? lo : lo2;
+    bool again = false;
+    // Candidates at or above lg (at most ROW_CAND), read in batches of
     // LOAD_BATCH loads per thread into sm.r.cand: for the radix select of
     // top-k, for the sort of top-p.
     uint64_t* dstv = sm.r.cand;
@@ -450,12 +655,14 @@ __device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp
             if (sm.r.off[mid] <= e) lo_c = mid;
             else hi_c = mid;
           }
-          ck[j] = cand_entry_key(ld_dev(&cand[(size_t)lo_c * CAND_CAP + (e - sm.r.off[lo_c])]));
+          // (a chunk whose bound lies above lg is scanned below instead)
+          if (sm.r.cb[lo_c] <= lg)
+            ck[j] = cand_entry_key(ld_dev(&cand[(size_t)lo_c * CAND_CAP + (e - sm.r.off[lo_c])]));
         }
       }
 #pragma unroll
       for (int j = 0; j < LOAD_BATCH; ++j) {
-        if (ck[j] != 0ull && (uint32_t)(ck[j] >> 32) >= lo) {
+        if (ck[j] != 0ull && (uint32_t)(ck[j] >> 32) >= lg) {
           if (a.ulen > 1) {
             // a candidate unit: its logits at or above lo
             const int st = (int)(uint32_t)ck[j];
@@ -463,7 +670,7 @@ __device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp
             for (int i = 0; i < 16 / ElemT<DT>::ESZ; ++i) {
               const float x = unit_elem<DT>(r, i);
               const uint32_t key = ord_key(x);
-              if (key >= lo && x > -INFINITY) {
+              if (key >= lg && x > -INFINITY) {
                 const int slot = atomicAdd(&sm.ncand, 1);
                 if (slot < cap) dstv[slot] = ((uint64_t)key << 32) | (uint32_t)(st + i);
               }
@@ -471,6 +678,25 @@ __device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp
           } else {
             const int slot = atomicAdd(&sm.ncand, 1);
             if (slot < cap) dstv[slot] = ck[j];
+          }
+        }
+      }
+    }
+    if (pass == 1) {
+      for (int c = 0; c < nch; ++c) {
+        if (sm.r.cb[c] <= lg) continue;  // uniform
+        const int c0 = c * CE, cn = min(CE, a.V - c0);
+        const char* cp = rp + (size_t)c0 * ElemT<DT>::ESZ;
+        for (int j = 8 * t; j < cn; j += 8 * BS) {
+          float x8[8];
+          load8<DT>(cp, j, cn, a.ulen > 1, x8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t key = ord_key(x8[e]);
+            if (j + e < cn && key >= lg && x8[e] > -INFINITY) {
+              const int slot = atomicAdd(&sm.ncand, 1);
+              if (slot < cap) dstv[slot] = ((uint64_t)key << 32) | (uint32_t)(c0 + j + e);
+            }
           }
         }
       }
@@ -547,10 +773,11 @@ __device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp
       }
       first = block_min_i<BS / 64>(first, sm.red);
       if (first == INT_MAX) {
-        if (MODE == M_TOPP) fb = true;  // the nucleus reaches below the candidate window
-        else first = ns - 1;             // round-off kept the top-k mass just below top_p
+        // the nucleus reaches below the candidate window: widen it once
+        if (MODE == M_TOPP) (pass == 0 ? again : fb) = true;
+        else first = ns - 1;  // round-off kept the top-k mass just below top_p
       }
-      if (!fb) {
+      if (!fb && !again) {
         if (first < 0) first = 0;
         __syncthreads();
         const uint32_t tp = (uint32_t)(srt[first] >> 32);
@@ -576,6 +803,7 @@ __device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp
         }
       }
     }
+    if (!again) break;
   }
 
   if (fb) {
@@ -588,13 +816,26 @@ __device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp
       tk = row_radix<DT, BS>(rp, a.V, 0u, false, m, invT, 1.0, (double)a.top_k, sm);
       if (MODE == M_TOPKP) (void)row_keep<DT, BS>(rp, a.V, tk, m, invT, &sk, sm);
     }
-    if (MODE == M_TOPP || MODE == M_TOPKP) {
-      const double sn = MODE == M_TOPP ? rr.S : sk;
-      tau = row_radix<DT, BS>(rp, a.V, tk, true, m, invT, sn, a.top_p, sm);
-    } else {
-      tau = tk;
+    int nall = -1;
+    if (MODE == M_TOPP) {
+      uint32_t tp;
+      int na;
+      double sk2;
+      if (row_topp_cut<DT, BS>(rp, a.V, a.ulen > 1, m, invT, rr.S, a.top_p, sm, &tp, &na, &sk2)) {
+        tau = tp;
+        nall = na;
+        skept = sk2;
+      }
     }
-    const int nall = row_keep<DT, BS>(rp, a.V, tau, m, invT, &skept, sm);
+    if (nall < 0) {
+      if (MODE == M_TOPP || MODE == M_TOPKP) {
+        const double sn = MODE == M_TOPP ? rr.S : sk;
+        tau = row_radix<DT, BS>(rp, a.V, tk, true, m, invT, sn, a.top_p, sm);
+      } else {
+        tau = tk;
+      }
+      nall = row_keep<DT, BS>(rp, a.V, tau, m, invT, &skept, sm);
+    }
     if (nall <= KEEP_CAP) {
       sort_keys_desc<BS>(nall, sm);
       nk = nall;
@@ -1992,7 +2233,9 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
   for (int wd = 0; 32 * wd < rps; ++wd) {
     uint32_t bits = sm.fail[wd];  // the same in every thread
     if (rps - 32 * wd < 32) bits &= (1u << (rps - 32 * wd)) - 1u;
-    while (bits) {
+    // (rare: marked unlikely, so that the register spills this block-level
+    // path needs are placed on it and not on the common path)
+    while (__builtin_expect(bits != 0u, 0)) {
       const int j = 32 * wd + __ffs(bits) - 1;
       bits &= bits - 1u;
       const int rl = seq_row<RAG>(a, g, j);
@@ -2118,7 +2361,7 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
     }
   }
   __syncthreads();
-  if (FILT && sm.big) {
+  if (__builtin_expect(FILT && sm.big, 0)) {
     // a kept set too large for a list: the whole workgroup draws from the full rows
     const int n = sm.n;
     const bool res = n < K;
@@ -2171,31 +2414,6 @@ __device__ __forceinline__ double plain_weight(const char* pr, const char* qr, i
   const float xq = !res ? 0.0f : QP ? reinterpret_cast<const float*>(qr)[j] : load_elem<DT>(qr, j);
   return plain_w<QP>(xp, xq, c, res, tab);
 }
-// The 8 logits j0 .. j0+7 of a row (-inf past V): one 16-byte load per 8
-// bf16 (two per 8 f32) when rows are 16-byte aligned and the 8 lie in the row.
-template <int DT>
-__device__ __forceinline__ void load8(const char* row, int j0, int V, bool vec, float (&x)[8]) {
-  if (vec && j0 + 8 <= V) {
-    if (DT == D_BF16) {
-      const uint4 r = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 2);
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_lo(w[i]);
-        x[2 * i + 1] = bf16_hi(w[i]);
-      }
-    } else {
-      const uint4 r0 = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 4);
-      const uint4 r1 = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 4 + 16);
-      x[0] = __uint_as_float(r0.x); x[1] = __uint_as_float(r0.y); x[2] = __uint_as_float(r0.z); x[3] = __uint_as_float(r0.w);
-      x[4] = __uint_as_float(r1.x); x[5] = __uint_as_float(r1.y); x[6] = __uint_as_float(r1.z); x[7] = __uint_as_float(r1.w);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = j0 + e < V ? load_elem<DT>(row, j0 + e) : -INFINITY;
-  }
-}
-
 template <int DT, int LAY>
 __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   constexpr bool QP = LAY == LAY_QP;
@@ -2263,66 +2481,97 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   if (!last_arrival(&a.smp_cnt[b], (uint32_t)a.nsw, &sm.flag)) return;
   if (!active) return;
 
+  // The last workgroup of the sequence draws.  Wave 0 alone: no block-wide
+  // scans.  Lane l sums the segments of its contiguous run, one exclusive
+  // scan over the lanes gives every run's start, and the run holding u*Z
+  // is walked segment by segment; the segment is then rescanned, 8 logits a
+  // lane.
   const double* ssum = a.seg_sum + (size_t)b * nseg;
   const int32_t* slast = a.seg_last + (size_t)b * nseg;
-  const int per = (nseg + WG - 1) / WG;
-  const int s0 = min(t * per, nseg), s1 = min(s0 + per, nseg);
-  double loc = 0.0;
-  int lastseg = -1;
-  for (int s = s0; s < s1; ++s) {
-    loc += ld_dev(&ssum[s]);
-    if (ld_dev(&slast[s]) >= 0) lastseg = s;
-  }
-  double Z;
-  const double incl = block_incl_scan(loc, sm.red, &Z);
-  lastseg = block_max_i(lastseg, sm.red);
   const double u = (double)a.U[sr.tu];
-  int tok;
-  if (!(Z > 0.0)) {
-    // empty residual (round-off only): draw from p
+  const int lane = t & 63;
+  int tok = 0;
+  double Z = 0.0;
+  if (t < 64) {
+    const int per = (nseg + 63) / 64;
+    const int s0 = min(lane * per, nseg), s1 = min(s0 + per, nseg);
+    double loc = 0.0;
+    int lastseg = -1;
+    for (int sg = s0; sg < s1; ++sg) {
+      loc += ld_dev(&ssum[sg]);
+      if (ld_dev(&slast[sg]) >= 0) lastseg = sg;
+    }
+    const double incl = wave_scan_f64(loc);
+    Z = lane63(incl);
+    lastseg = wave_max(lastseg);
+    if (lane == 0) {
+      sm.d0 = Z;
+      sm.i0 = lastseg;
+    }
+    if (Z > 0.0) {
+      const double target = u * Z;
+      // the run (lane) holding the target: the lanes' [previous lane's
+      // inclusive sum, own inclusive sum) ranges tile [0, Z) exactly; then
+      // the segment within the run (its last one if round-off in the run's
+      // own sum leaves the target past it)
+      const double excl = lane_bcast(incl, lane > 0 ? lane - 1 : 0);
+      double run = lane > 0 ? excl : 0.0;
+      int found = INT_MAX;
+      double cstart = 0.0;
+      if (run <= target && target < incl && s0 < s1) {
+        for (int sg = s0; sg < s1; ++sg) {
+          const double ce = run + ld_dev(&ssum[sg]);
+          if (target < ce || sg == s1 - 1) {
+            found = sg;
+            cstart = run;
+            break;
+          }
+          run = ce;
+        }
+      }
+      const unsigned long long fm = __ballot(found != INT_MAX);
+      if (!fm) {
+        // round-off left the target past the last sum: the last positive token
+        tok = lastseg >= 0 ? ld_dev(&slast[lastseg]) : 0;
+      } else {
+        const int src = __ffsll(fm) - 1;
+        const int sf = lane_bcast(found, src);
+        const double cs = lane_bcast(cstart, src);
+        // rescan segment sf: logits sf*SEG + 8 lane .. + 7
+        const int j0 = sf * SEG + 8 * lane;
+        float xp[8], xq[8];
+        load8<DT>(pr, j0, a.V, a.ulen > 1, xp);
+        if (res && !QP) {
+          load8<DT>(qr, j0, a.V, a.ulen > 1, xq);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            xq[e] = (res && j0 + e < a.V) ? reinterpret_cast<const float*>(qr)[j0 + e] : 0.0f;
+        }
+        double w8[8], ls = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          w8[e] = j0 + e < a.V ? plain_w<QP>(xp[e], xq[e], cw, res, sm.etab) : 0.0;
+          ls += w8[e];
+        }
+        double C = cs + wave_scan_f64(ls) - ls;
+        int first = INT_MAX;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          C += w8[e];
+          if (first == INT_MAX && w8[e] > 0.0 && target < C) first = j0 + e;
+        }
+        first = wave_min(first);
+        tok = first != INT_MAX ? first : ld_dev(&slast[sf]);
+        if (tok < 0) tok = lastseg >= 0 ? ld_dev(&slast[lastseg]) : 0;
+      }
+    }
+  }
+  __syncthreads();
+  if (!(sm.d0 > 0.0)) {
+    // empty residual (round-off only): the whole workgroup draws from p
     set_draw_row(&a.row[sr.rp], false, 0, row_temp(a, sr.rp).invT, sm);
     tok = full_row_sample<DT, WG>(a, u, pr, qr, false, sm, &Z);
-  } else {
-    const double target = u * Z;
-    __syncthreads();
-    sm.scan[t] = incl;
-    __syncthreads();
-    double run = t > 0 ? sm.scan[t - 1] : 0.0;
-    int found = INT_MAX;
-    double cstart = 0.0;
-    for (int s = s0; s < s1; ++s) {
-      const double ce = run + ld_dev(&ssum[s]);
-      if (found == INT_MAX && target < ce) {
-        found = s;
-        cstart = run;
-      }
-      run = ce;
-    }
-    const int sf = block_min_i(found, sm.red);
-    if (sf == INT_MAX) {
-      tok = lastseg >= 0 ? ld_dev(&slast[lastseg]) : 0;
-    } else {
-      __syncthreads();
-      if (found == sf) sm.d0 = cstart;
-      __syncthreads();
-      const double cs = sm.d0;
-      const int j0 = sf * SEG + 2 * t;
-      const double w0 = j0 < a.V ? plain_weight<DT, QP>(pr, qr, j0, cw, res, sm.etab) : 0.0;
-      const double w1 = j0 + 1 < a.V ? plain_weight<DT, QP>(pr, qr, j0 + 1, cw, res, sm.etab) : 0.0;
-      double tot;
-      const double inc2 = block_incl_scan(w0 + w1, sm.red, &tot);
-      __syncthreads();
-      sm.scan[t] = inc2;
-      __syncthreads();
-      const double C0 = cs + (t > 0 ? sm.scan[t - 1] : 0.0) + w0;
-      const double C1 = C0 + w1;
-      int first = INT_MAX;
-      if (j0 < a.V && w0 > 0.0 && target < C0) first = j0;
-      else if (j0 + 1 < a.V && w1 > 0.0 && target < C1) first = j0 + 1;
-      first = block_min_i(first, sm.red);
-      tok = first != INT_MAX ? first : ld_dev(&slast[sf]);
-      if (tok < 0) tok = lastseg >= 0 ? ld_dev(&slast[lastseg]) : 0;
-    }
   }
   if (t == 0) {
     a.out_tok[(size_t)b * (a.Kmax + 1) + n] = tok;

@@ -80,6 +80,18 @@ def test_flat_rows_take_the_full_row_paths():
     _check(w)
 
 
+def test_nucleus_below_the_window():
+    """Broad rows whose top-p nucleus reaches below the candidate window but
+    whose cut region is sparse: the two-pass full-row cut decides them (kept
+    sets that fit a list, and ones that do not), in both dtypes."""
+    for w in [Workload("wide-list", 6, 3, 3000, "f32", "normal", 3.5, 0.5, 1.0, 0, 0.9, 31),
+              Workload("wide-big", 4, 3, 30000, "f32", "normal", 3.0, 0.5, 1.0, 0, 0.9, 32),
+              Workload("wide-bf16", 4, 4, 32000, "bf16", "normal", 3.0, 0.7, 1.0, 0, 0.85, 33),
+              Workload("wide-t07", 4, 3, 20000, "f32", "normal", 2.0, 0.5, 0.7, 0, 0.95, 34)]:
+        log(f"[nucleus below window] {w.name}")
+        _check(w)
+
+
 def test_ties_at_the_cut():
     """bf16-coarse logits with many equal values: top-k and top-p keep whole tie groups."""
     rng = np.random.default_rng(5)
