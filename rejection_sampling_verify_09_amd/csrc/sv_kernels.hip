@@ -65,15 +65,21 @@ __device__ __forceinline__ double exp_tab(double x, const double* tab) {
 // exponent, scaling and normaliser fold into y = x * A + B): y = k + f with
 // integer k and |f| <= 1/2, 2^(y/64) = 2^(k >> 6) * 2^((k & 63)/64) * e^r with
 // r = f ln2/64, |r| <= ln2/128, the powers from the LDS table and e^r from its
-// degree-5 Taylor polynomial as in exp_tab.  0 below -64 * 1100 (also -inf).
+// degree-5 Taylor polynomial as in exp_tab.  k is taken by the 1.5 * 2^52
+// shift (the sum's low mantissa bits hold round-to-nearest-even of y) and
+// 2^(k >> 6) is added to the exponent field, so no conversion or scaling
+// instruction is needed.  0 below -64 * 1020 (also -inf), where the result
+// would leave the normal range.
 __device__ __forceinline__ double exp2_64(double y, const double* tab) {
-  if (!(y > -70400.0)) return 0.0;
-  const double kf = rint(y);
+  if (!(y > -65280.0)) return 0.0;
+  const double S = 6755399441055744.0;  // 1.5 * 2^52
+  const double ys = y + S;
+  const double kf = ys - S;
+  const int ki = (int)(uint32_t)__double_as_longlong(ys);
   const double r = (y - kf) * 0.010830424696249145;  // ln2 / 64
   const double p = fma(fma(fma(fma(fma(r, 1.0 / 120.0, 1.0 / 24.0), r, 1.0 / 6.0), r, 0.5), r, 1.0), r, 1.0);
-  const int ki = (int)kf;
-  const int j = ki & 63;
-  return ldexp(tab[j] * p, (ki - j) >> 6);
+  const double v = tab[ki & 63] * p;
+  return __longlong_as_double(__double_as_longlong(v) + ((long long)(ki >> 6) << 52));
 }
 
 // chunk_weight with exp2_64 for the power of two (the same value up to a few
@@ -92,6 +98,23 @@ __device__ __forceinline__ void build_exp_tab(double* tab) {
   __syncthreads();
 }
 
+// The 64 lanes' keys sorted descending across the wave (lane l gets the
+// l-th largest): a bitonic network on lane exchanges, no LDS.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t key) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t other = (uint32_t)__shfl_xor((int)key, j);
+      const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
+      const uint32_t mx = max(key, other), mn = min(key, other);
+      key = (lower == desc) ? mx : mn;
+    }
+  }
+  return key;
+}
+
 struct DrawRow {
   double snorm;
   double invT;
@@ -107,9 +130,12 @@ struct NoSink {
   __device__ __forceinline__ void put(int, int, int32_t, double) const {}
 };
 
+constexpr int TK_WAVE_TOP = 16;  // top-k bound: thread maxima each wave posts (k up to NWAVE times this)
 struct SmemStream {
   uint64_t cand[NWAVE * CAND_CAP];  // per-wave candidate lists (one flat list after an overflow cut)
   uint64_t tk[WG];
+  uint32_t tk16[NWAVE * TK_WAVE_TOP];
+  uint32_t tkb;
   uint32_t hist[256];
   int32_t wn[NWAVE];
   float rm[NWAVE];   // per-wave chunk maxima
@@ -1159,6 +1185,25 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
     if (MODE == M_TOPP) {
       // window below the chunk max (which is <= the row max)
       bound = ord_key(mc - row_temp(a, rl).win);
+    } else if (a.top_k <= NWAVE * TK_WAVE_TOP) {
+      // k <= 64: each wave sorts its 64 thread maxima in registers and posts
+      // its 16 largest; wave 0 sorts those 64.  Their k-th largest is at most
+      // the k-th largest of all 256 thread maxima (a subset's), so at least
+      // k logits of the row lie at or above it, and it equals it whenever no
+      // wave holds more than 16 of the chunk's k largest; their 8 largest
+      // are the chunk's 8 largest thread maxima (each wave posted its own 8).
+      // Two barriers instead of the sorting network's 36.
+      const int lane = t & 63, w = t >> 6;
+      const uint32_t kw = wave_sort_desc(ord_key(tm));
+      if (lane < TK_WAVE_TOP) sm.s.tk16[w * TK_WAVE_TOP + lane] = kw;
+      __syncthreads();
+      if (t < 64) {
+        const uint32_t k2 = wave_sort_desc(sm.s.tk16[lane]);
+        if (lane == a.top_k - 1) sm.s.tkb = k2;
+        if (lane < CTOP) __builtin_nontemporal_store(k2, &a.ctop[(size_t)chunk_id * CTOP + lane]);
+      }
+      __syncthreads();
+      bound = sm.s.tkb;
     } else {
       // the k-th largest of the 256 thread maxima is <= the row's k-th largest
       // logit (for k > 256 no bound follows: every finite logit qualifies)
