@@ -21,6 +21,7 @@ constexpr int SPW = 4;           // most sampling chunks per workgroup of the un
 constexpr int CTOP = 8;          // top-k: largest thread maxima a chunk records for the row merge
 constexpr int CTOP_CHUNKS = 64;  // ... used by the row merge for rows of at most this many chunks
 constexpr int MAX_K = 64;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // four 32-bit words (16-byte loads and stores)
 constexpr int READ_BLOCK = 16384;  // bytes per workgroup of the plain-read kernel (as a bf16 chunk)
 // register budget of the streaming kernels: resident workgroups per CU
 template <int DT, bool VEC>

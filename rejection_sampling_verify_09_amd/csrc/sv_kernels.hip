@@ -363,29 +363,75 @@ __device__ __forceinline__ int row_keep(const char* rp, int V, uint32_t tau, flo
   return sm.ncand;
 }
 
-// The 8 logits j0 .. j0+7 of a row (-inf past V): one 16-byte load per 8
-// bf16 (two per 8 f32) when rows are 16-byte aligned and the 8 lie in the row.
+// The 8 logits j0 .. j0+7 of a row (-inf past V).  Rows that are 16-byte
+// aligned with a length of whole 16-byte vectors (vec) take one 16-byte
+// buffer load per 8 bf16 (two per 8 f32), ranged to the row: a vector past
+// the row end reads as zero without a memory access.  No load sits behind a
+// lane condition, so the compiler keeps a caller's loads in flight together
+// (plain loads under a per-lane bounds branch were each waited for before
+// the next was issued).
 template <int DT>
 __device__ __forceinline__ void load8(const char* row, int j0, int V, bool vec, float (&x)[8]) {
-  if (vec && j0 + 8 <= V) {
+  if (vec) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, V * ElemT<DT>::ESZ, 0x00020000);
     if (DT == D_BF16) {
-      const uint4 r = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 2);
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, j0 * 2, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[2 * i] = bf16_lo(w[i]);
         x[2 * i + 1] = bf16_hi(w[i]);
       }
     } else {
-      const uint4 r0 = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 4);
-      const uint4 r1 = *reinterpret_cast<const uint4*>(row + (size_t)j0 * 4 + 16);
-      x[0] = __uint_as_float(r0.x); x[1] = __uint_as_float(r0.y); x[2] = __uint_as_float(r0.z); x[3] = __uint_as_float(r0.w);
-      x[4] = __uint_as_float(r1.x); x[5] = __uint_as_float(r1.y); x[6] = __uint_as_float(r1.z); x[7] = __uint_as_float(r1.w);
+      const auto w0 = __builtin_amdgcn_raw_buffer_load_b128(rs, j0 * 4, 0, 0);
+      const auto w1 = __builtin_amdgcn_raw_buffer_load_b128(rs, j0 * 4 + 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = __uint_as_float(w0[i]);
+        x[4 + i] = __uint_as_float(w1[i]);
+      }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = j0 + e < V ? x[e] : -INFINITY;
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = j0 + e < V ? load_elem<DT>(row, j0 + e) : -INFINITY;
   }
+}
+
+// load8's vector path split in two, so that a caller can issue every load
+// before it unpacks any (the unpacking needs the data, and a wait placed
+// before it would hold back the loads behind it).
+template <int DT>
+struct Raw8 {
+  u32x4 w[DT == D_BF16 ? 1 : 2];
+};
+template <int DT>
+__device__ __forceinline__ Raw8<DT> load8_raw(const char* row, int j0, int V) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, V * ElemT<DT>::ESZ, 0x00020000);
+  Raw8<DT> r;
+#pragma unroll
+  for (int h = 0; h < (DT == D_BF16 ? 1 : 2); ++h) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, j0 * ElemT<DT>::ESZ + 16 * h, 0, 0);
+    r.w[h] = u32x4{v[0], v[1], v[2], v[3]};
+  }
+  return r;
+}
+template <int DT>
+__device__ __forceinline__ void unpack8(const Raw8<DT>& r, int j0, int V, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (DT == D_BF16) {
+      x[2 * i] = bf16_lo(r.w[0][i]);
+      x[2 * i + 1] = bf16_hi(r.w[0][i]);
+    } else {
+      x[i] = __uint_as_float(r.w[0][i]);
+      x[4 + i] = __uint_as_float(r.w[1][i]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = j0 + e < V ? x[e] : -INFINITY;
 }
 
 // Bins of the full-row top-p search: ZB bins per unit of z = (m - x) / T, the
@@ -1274,7 +1320,6 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
   if (t == 0) {
     // the record as two 16-byte stores that do not stay in this cache (only
     // the next launch reads them)
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4* rp4 = reinterpret_cast<u32x4*>(&a.chunk[chunk_id]);
     const uint64_t sb = (uint64_t)__double_as_longlong(s);
     __builtin_nontemporal_store(u32x4{(uint32_t)sb, (uint32_t)(sb >> 32), __float_as_uint(mc), bound}, rp4);
@@ -1714,40 +1759,51 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
   const double invT = rt.invT;
   const double A64 = invT * 92.33248261689366;  // 64 log2(e) / T: exp((x - m) / T) = exp2_64((x - m) * A64)
 
-  // one round trip: the chunk records (chunk lane + 64 i) and the drafted
-  // token's logit
-  float cm[4];
-  double cs[4];
-  uint32_t cb[4];
-  int cn[4], carg[4];
+  // one round trip: the chunk records (chunk lane + 64 i), the drafted
+  // token's logit and the speculated list entries.  Every load is a buffer
+  // load ranged to what it reads (past the end it returns zeros without a
+  // memory access), issued before any of their data is used: loads under
+  // per-lane conditions were each waited for before the next was issued.
+  constexpr bool TOPKM = MODE == M_TOPK || MODE == M_TOPKP;
+  const __amdgpu_buffer_rsrc_t rrec =
+      __builtin_amdgcn_make_buffer_rsrc((void*)cr, (short)0, nch * (int)sizeof(ChunkRec), 0x00020000);
+  u32x4 rA[4], rB[4];  // the two 16-byte halves of record lane + 64 i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = lane + 64 * i;
-    cm[i] = -INFINITY;
-    cs[i] = 0.0;
-    cb[i] = 0u;
-    cn[i] = 0;
-    carg[i] = INT_MAX;
-    if (c < nch) {
-      cm[i] = cr[c].m;
-      if (MODE == M_PLAIN || MODE == M_TOPP) cs[i] = cr[c].s;
-      if (FILT) {
-        cb[i] = cr[c].bound;
-        cn[i] = min(cr[c].ncand, CAND_CAP);
+    rA[i] = u32x4{0u, 0u, 0u, 0u};
+    rB[i] = u32x4{0u, 0u, 0u, 0u};
+    if (64 * i < nch) {  // uniform
+      const int off = (lane + 64 * i) * (int)sizeof(ChunkRec);
+      const auto va = __builtin_amdgcn_raw_buffer_load_b128(rrec, off, 0, 0);
+      rA[i] = u32x4{va[0], va[1], va[2], va[3]};
+      if (FILT || MODE == M_GREEDY) {
+        const auto vb = __builtin_amdgcn_raw_buffer_load_b128(rrec, off + 16, 0, 0);
+        rB[i] = u32x4{vb[0], vb[1], vb[2], vb[3]};
       }
-      if (MODE == M_GREEDY) carg[i] = cr[c].arg;
     }
   }
   // top-k: the chunks' largest thread maxima (rows of at most CTOP_CHUNKS chunks)
-  constexpr bool TOPKM = MODE == M_TOPK || MODE == M_TOPKP;
-  uint4 ctq[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  u32x4 ctq[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
   const bool use_top = TOPKM && nch <= CTOP_CHUNKS && nch * CTOP >= a.top_k;
-  if (use_top && lane < nch) {
-    const uint4* tp = reinterpret_cast<const uint4*>(a.ctop + ((size_t)rl * nch + lane) * CTOP);
-    ctq[0] = tp[0];
-    ctq[1] = tp[1];
+  if (use_top) {
+    const __amdgpu_buffer_rsrc_t rct = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.ctop + (size_t)rl * nch * CTOP), (short)0, nch * CTOP * 4, 0x00020000);
+    const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rct, lane * CTOP * 4, 0, 0);
+    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rct, lane * CTOP * 4 + 16, 0, 0);
+    ctq[0] = u32x4{v0[0], v0[1], v0[2], v0[3]};
+    ctq[1] = u32x4{v1[0], v1[1], v1[2], v1[3]};
   }
-  const float lx = (MODE != M_GREEDY && hx) ? load_elem<DT>(row_ptr(a, rl, ElemT<DT>::ESZ), xtok) : -INFINITY;
+  // the drafted token's logit (its index clamped into the row; unused when
+  // the token is outside it)
+  uint32_t lxw = 0u;
+  if (MODE != M_GREEDY) {
+    constexpr int ESZ = ElemT<DT>::ESZ;
+    const __amdgpu_buffer_rsrc_t rrow =
+        __builtin_amdgcn_make_buffer_rsrc((void*)row_ptr(a, rl, ESZ), (short)0, a.V * ESZ, 0x00020000);
+    const int xc = hx ? xtok : 0;
+    lxw = DT == D_BF16 ? ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rrow, xc * 2, 0, 0) << 16)
+                       : __builtin_amdgcn_raw_buffer_load_b32(rrow, xc * 4, 0, 0);
+  }
   // with them, speculatively, the first SE entries of the first SPECC
   // chunks' lists (most top-p lists are shorter than 32 units, top-k lists
   // than 64): one round trip for most rows.  Load i holds entry lane % SE of
@@ -1757,12 +1813,30 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
   uint64_t spec[NSPEC];
   const uint64_t* cand = a.cand + (size_t)rl * nch * CAND_CAP;
   if (FILT) {
+    const __amdgpu_buffer_rsrc_t rsp =
+        __builtin_amdgcn_make_buffer_rsrc((void*)cand, (short)0, nch * CAND_CAP * 8, 0x00020000);
 #pragma unroll
     for (int i = 0; i < NSPEC; ++i) {
       const int c = i * SPL + lane / SE;
-      spec[i] = c < nch ? cand[(size_t)c * CAND_CAP + lane % SE] : 0ull;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsp, (c * CAND_CAP + lane % SE) * 8, 0, 0);
+      spec[i] = ((uint64_t)v[1] << 32) | v[0];
     }
   }
+  // the records' fields (defaults for chunks past the row's)
+  float cm[4];
+  double cs[4];
+  uint32_t cb[4];
+  int cn[4], carg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = lane + 64 * i < nch;
+    cm[i] = ok ? __uint_as_float(rA[i][2]) : -INFINITY;
+    cs[i] = ok ? __longlong_as_double((long long)(((uint64_t)rA[i][1] << 32) | rA[i][0])) : 0.0;
+    cb[i] = ok ? rA[i][3] : 0u;
+    cn[i] = ok ? min((int)rB[i][0], CAND_CAP) : 0;
+    carg[i] = ok ? (int)rB[i][1] : INT_MAX;
+  }
+  const float lx = (MODE != M_GREEDY && hx) ? __uint_as_float(lxw) : -INFINITY;
 
   const float m = dpp_wave_fmax(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])));
   rr.S = 0.0;
@@ -1802,7 +1876,7 @@ __device__ __forceinline__ bool wave_row(const Args& a, int rl, int xtok, WaveRo
       // the k-th largest of the chunks' recorded maxima (logits of the row)
       // is at most the row's k-th largest logit: a tighter bound than any
       // single chunk's
-      const uint32_t ck[CTOP] = {ctq[0].x, ctq[0].y, ctq[0].z, ctq[0].w, ctq[1].x, ctq[1].y, ctq[1].z, ctq[1].w};
+      const uint32_t ck[CTOP] = {ctq[0][0], ctq[0][1], ctq[0][2], ctq[0][3], ctq[1][0], ctq[1][1], ctq[1][2], ctq[1][3]};
       unsigned long long cw1[CTOP];
 #pragma unroll
       for (int i = 0; i < CTOP; ++i) cw1[i] = ck[i] > KEY_NEG_INF ? 1ull : 0ull;
@@ -2484,6 +2558,27 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
     // the workgroup's spw chunks of 2048 logits: every load first, then the
     // weights and one segment sum per wave and chunk
     float xp[SPW][8], xq[SPW][8];
+    if (a.ulen > 1 && !QP) {
+      // every load issued before any is unpacked
+      Raw8<DT> rpv[SPW], rqv[SPW];
+#pragma unroll
+      for (int ci = 0; ci < SPW; ++ci) {
+        const int j0 = (cb + ci) * SCE + t * 8;
+        rpv[ci] = load8_raw<DT>(pr, ci < a.spw ? j0 : a.V, a.V);
+        if (res) rqv[ci] = load8_raw<DT>(qr, ci < a.spw ? j0 : a.V, a.V);
+      }
+#pragma unroll
+      for (int ci = 0; ci < SPW; ++ci) {
+        const int j0 = (cb + ci) * SCE + t * 8;
+        unpack8<DT>(rpv[ci], j0, a.V, xp[ci]);
+        if (res) {
+          unpack8<DT>(rqv[ci], j0, a.V, xq[ci]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xq[ci][e] = 0.0f;
+        }
+      }
+    } else
 #pragma unroll
     for (int ci = 0; ci < SPW; ++ci) {
       if (ci >= a.spw) break;  // uniform
