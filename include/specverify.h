@@ -358,8 +358,17 @@ int sv_lm_logits(const void* hidden, const void* weight, float* out_logits,
  * 428210 section 3.1), the draft's K rows from its own (a smaller model of
  * the same family: its width d_draft may differ, the vocabulary is shared;
  * page www.2kiu.com/news/5895634 section 4.1), and the verification of
- * sv_spec_verify_debug runs on them.  Equivalent to sv_lm_logits on both
- * followed by sv_spec_verify_debug with dtype SV_F32.
+ * sv_spec_verify_debug runs on them.  Decides as sv_lm_logits on both
+ * followed by sv_spec_verify_debug with dtype SV_F32 (the same logits; the
+ * normalisers may differ in float rounding, well within the verification's
+ * 1e-6 bound on p(x) and q(x)).
+ *
+ * When V % 4 == 0 the verification does not stream the logits again: the
+ * projections' epilogues reduce each row's 64-column tiles to a record (the
+ * tile max and its exp2 sum, or its arg-max at temperature 0), the chunk
+ * statistics are formed from those records, and only the tiles that can
+ * hold a filter candidate are read back.  The logits are still written once
+ * (the kept lists and the full-row draws read them).  Other V stream them.
  *
  * hidden_target  [B, K+1, d_target] bfloat16, device, 16-byte aligned
  * weight_target  [V, d_target] bfloat16, device, 16-byte aligned
@@ -372,7 +381,8 @@ int sv_lm_logits(const void* hidden, const void* weight, float* out_logits,
  * d_target, d_draft: as d of sv_lm_logits.
  *
  * The logits live in a second buffer of the stream's scratch set, of
- * (B(K+1) + BK) * V float32, grown on demand like the scratch (a growth
+ * (B(K+1) + BK) * V float32 and 8 bytes per row and 64 columns of tile
+ * records, grown on demand like the scratch (a growth
  * synchronises the stream) or sized by sv_init with SV_INIT_LMHEAD, and freed
  * by sv_stream_release and sv_release.  Under launch timing the first two
  * events of the call bracket the two projections (its stream_kernel_ms) and

@@ -20,7 +20,10 @@ hipError_t launch_seq(const Args& a, int dtype, int mode, unsigned grid, hipStre
 hipError_t launch_sample(const Args& a, int dtype, unsigned grid, hipStream_t s);
 hipError_t launch_probs(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s);
 hipError_t launch_read(const void* p, int64_t nbytes, uint32_t key, uint32_t* out, unsigned grid, hipStream_t s);
-hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s);
+hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s,
+                          void* R, int32_t rstride, int32_t roff, int stat, float c2);
+hipError_t launch_tile_chunk(const Args& a, int mode, unsigned grid, const void* R, int32_t rstride, int32_t ntg,
+                             hipStream_t s);
 int64_t lm_gemm_tiles(int32_t M, int32_t V);
 }  // namespace sv
 
@@ -44,7 +47,7 @@ struct StreamBufs {
   std::mutex mu;
   char* ptr = nullptr;   // verification scratch
   size_t bytes = 0;
-  char* lgt = nullptr;   // float32 logits formed by the output projections
+  char* lgt = nullptr;   // float32 logits formed by the output projections, then their tile records
   size_t lgt_bytes = 0;
 };
 
@@ -148,6 +151,21 @@ ProfSlot* prof_begin() {
 }
 
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The projection-fed call's buffer: rows x V float32 logits, then the tile
+// records of those rows (8 bytes per row and TILE_N columns, in groups of
+// TILE_GROUP tiles).
+size_t lm_logit_bytes(int64_t rows, int64_t V) { return al256((size_t)rows * (size_t)V * sizeof(float)); }
+size_t lm_buf_bytes(int64_t rows, int64_t V) {
+  const int64_t groups = (V + TILE_N * TILE_GROUP - 1) / (TILE_N * TILE_GROUP);
+  return lm_logit_bytes(rows, V) + al256((size_t)groups * (size_t)rows * TILE_GROUP * sizeof(uint2));
+}
+
+// Tile records that stand in for the streaming pass (launch_plan).
+struct TileIn {
+  const void* R;
+  int32_t rstride, ntg;
+};
 
 struct Layout {
   size_t seq_cnt, smp_cnt, cflag, chunk, ctop, cand, row, kidx, kprob, seq, seg_sum, seg_last, qxs, total;
@@ -363,11 +381,17 @@ int plan_verify(const VerifyIn& in, Plan* p) {
 // workgroup per sequence merges the sequence's rows and finishes it (accept
 // tests, first rejection, draw), then for unfiltered rows the full-row draw.  When timing, the
 // streaming launch records its own start and end in the slot's events.
-int launch_plan(Plan& p, char* base, hipStream_t s, ProfSlot* prof) {
+int launch_plan(Plan& p, char* base, hipStream_t s, ProfSlot* prof, const TileIn* tiles = nullptr) {
   bind_scratch(p.a, base, make_layout(p.need));
-  if (launch_stream(p.a, p.dtype, p.mode, p.vec, p.g_stream, s, prof ? prof->ev[0] : nullptr,
-                    prof ? prof->ev[1] : nullptr) != hipSuccess)
+  if (tiles) {
+    // the chunk records from the projections' tile statistics (the rows
+    // are already in HBM; only the candidate tiles are read back)
+    if (launch_tile_chunk(p.a, p.mode, p.g_stream, tiles->R, tiles->rstride, tiles->ntg, s) != hipSuccess)
+      return SV_ERR_HIP;
+  } else if (launch_stream(p.a, p.dtype, p.mode, p.vec, p.g_stream, s, prof ? prof->ev[0] : nullptr,
+                           prof ? prof->ev[1] : nullptr) != hipSuccess) {
     return SV_ERR_HIP;
+  }
   if (launch_seq(p.a, p.dtype, p.mode, p.g_seq, s) != hipSuccess) return SV_ERR_HIP;
   if (p.g_sample > 0 && launch_sample(p.a, p.dtype, p.g_sample, s) != hipSuccess) return SV_ERR_HIP;
   if (prof) {
@@ -379,11 +403,11 @@ int launch_plan(Plan& p, char* base, hipStream_t s, ProfSlot* prof) {
 }
 
 // A planned call on the stream's own scratch; the caller holds b->mu.
-int run_plan_locked(Plan& p, StreamBufs* b, hipStream_t s, bool timed) {
+int run_plan_locked(Plan& p, StreamBufs* b, hipStream_t s, bool timed, const TileIn* tiles = nullptr) {
   int st = grow(&b->ptr, &b->bytes, make_layout(p.need).total, s);
   if (st != SV_OK) return st;
   ProfSlot* prof = timed ? prof_begin() : nullptr;
-  return launch_plan(p, b->ptr, s, prof);
+  return launch_plan(p, b->ptr, s, prof, tiles);
 }
 
 int verify_impl(const VerifyIn& in, void* stream, bool timed = true) {
@@ -420,8 +444,10 @@ int sv_lm_logits(const void* hidden, const void* weight, float* out_logits, int3
   if (st != SV_OK) return st;
   if (M == 0) return SV_OK;
   if (!out_logits) return SV_ERR_NULL;
-  return launch_lm_gemm(hidden, weight, out_logits, M, V, d, (hipStream_t)stream) == hipSuccess ? SV_OK
-                                                                                                : SV_ERR_HIP;
+  return launch_lm_gemm(hidden, weight, out_logits, M, V, d, (hipStream_t)stream, nullptr, 0, 0, TS_NONE, 0.0f) ==
+                 hipSuccess
+             ? SV_OK
+             : SV_ERR_HIP;
 }
 
 int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target, const void* hidden_draft,
@@ -445,10 +471,18 @@ int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target, 
   StreamBufs* b = bufs_for(dev, s);
   if (!b) return SV_ERR_WORKSPACE;
   std::lock_guard<std::mutex> lk(b->mu);
-  st = grow(&b->lgt, &b->lgt_bytes, (size_t)(mt + md) * (size_t)V * sizeof(float), s);
+  st = grow(&b->lgt, &b->lgt_bytes, lm_buf_bytes(mt + md, V), s);
   if (st != SV_OK) return st;
   float* lt = (float*)b->lgt;
   float* ld = md > 0 ? lt + (size_t)mt * V : nullptr;
+  // Rows of 16 bytes' multiple (V % 4 == 0) take the fused path: the
+  // projections' epilogues write tile records beside the logits, and the
+  // chunk records are formed from them instead of a streaming pass over the
+  // logits.  Other rows are streamed (the element-load path).
+  const bool fused = V % 4 == 0;
+  TileIn tiles{b->lgt + lm_logit_bytes(mt + md, V), (int32_t)(mt + md), (V + TILE_N - 1) / TILE_N};
+  const int stat = !fused ? TS_NONE : greedy ? TS_ARG : TS_SUM;
+  void* R = fused ? const_cast<void*>(tiles.R) : nullptr;
   VerifyIn in;
   in.tgt = lt;
   in.drf = ld;
@@ -472,11 +506,14 @@ int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target, 
   // the third follows the verification
   ProfSlot* prof = prof_begin();
   if (prof && hipEventRecord(prof->ev[0], s) != hipSuccess) return SV_ERR_HIP;
-  if (launch_lm_gemm(hidden_target, weight_target, lt, (int32_t)mt, V, d_target, s) != hipSuccess) return SV_ERR_HIP;
-  if (md > 0 && launch_lm_gemm(hidden_draft, weight_draft, ld, (int32_t)md, V, d_draft, s) != hipSuccess)
+  if (launch_lm_gemm(hidden_target, weight_target, lt, (int32_t)mt, V, d_target, s, R, tiles.rstride, 0, stat,
+                     p.a.c2) != hipSuccess)
+    return SV_ERR_HIP;
+  if (md > 0 && launch_lm_gemm(hidden_draft, weight_draft, ld, (int32_t)md, V, d_draft, s, R, tiles.rstride,
+                               (int32_t)mt, stat, p.a.c2d) != hipSuccess)
     return SV_ERR_HIP;
   if (prof && hipEventRecord(prof->ev[1], s) != hipSuccess) return SV_ERR_HIP;
-  st = run_plan_locked(p, b, s, false);
+  st = run_plan_locked(p, b, s, false, fused ? &tiles : nullptr);
   if (st != SV_OK) return st;
   if (prof) {
     if (hipEventRecord(prof->ev[2], s) != hipSuccess) return SV_ERR_HIP;
@@ -668,7 +705,7 @@ int sv_init(int device, void* stream, int32_t max_B, int32_t max_K, int32_t max_
       std::lock_guard<std::mutex> lk(b->mu);
       st = grow(&b->ptr, &b->bytes, std::max<size_t>(make_layout(need).total, 256), s);
       if (st == SV_OK && (flags & SV_INIT_LMHEAD))
-        st = grow(&b->lgt, &b->lgt_bytes, std::max<size_t>((size_t)rows * (size_t)max_V * sizeof(float), 256), s);
+        st = grow(&b->lgt, &b->lgt_bytes, lm_buf_bytes(rows, max_V), s);
     }
     // set-up of the no-allocation entry point on this device
     char* base = nullptr;

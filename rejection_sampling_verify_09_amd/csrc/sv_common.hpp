@@ -36,6 +36,18 @@ constexpr float TOPP_WINDOW_Z = 5.0f;
 enum Mode : int { M_PLAIN = 0, M_TOPK = 1, M_TOPP = 2, M_TOPKP = 3, M_GREEDY = 4 };
 enum DType : int { D_F32 = 0, D_BF16 = 1 };
 
+// Tile statistics of logits formed by the output projections: for each row
+// and tile of TILE_N consecutive columns (one wave's columns of a projection
+// tile), 8 bytes: the tile max (float bits) and either the sum over the tile
+// of exp2(x * c2 - ceil(max * c2)) (TS_SUM, float bits) or the lowest column
+// holding the max (TS_ARG).  Stored in groups of TILE_GROUP tiles (the 256
+// columns of one projection workgroup): tile g of row r at
+// [(g / TILE_GROUP) * rows + r] * TILE_GROUP + g % TILE_GROUP.
+constexpr int TILE_N = 64;
+constexpr int TILE_GROUP = 4;
+constexpr int TILES_PER_CHUNK = CE / TILE_N;  // 128
+enum TileStat : int { TS_NONE = 0, TS_SUM = 1, TS_ARG = 2 };
+
 // row flags
 constexpr int RF_BAD = 1;       // no distribution (all -inf or non-finite normaliser)
 constexpr int RF_BIG = 2;       // kept set larger than KEEP_CAP: no kept list stored

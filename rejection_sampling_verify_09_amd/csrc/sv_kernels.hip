@@ -1205,17 +1205,55 @@ __device__ __forceinline__ int wave_emit(const float (&um)[UnitT<DT, VEC>::N], c
 // v_maximum3_f32); logits are never NaN inside the defined input range.
 __device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// Top-k candidate bound of chunk chunk_id from tm, one group max per thread
+// (each the max of disjoint logits of the chunk): the k-th largest of the
+// workgroup's group maxima, which is at most the row's k-th largest logit
+// (k <= 256; for larger k no bound follows and every finite logit
+// qualifies).  Also stores the chunk's CTOP largest group maxima, values of
+// the row from which the row merge bounds the row's k-th largest from below.
+// Shared memory written here is first written after a barrier of this call.
+__device__ __forceinline__ uint32_t chunk_topk_bound(const Args& a, int chunk_id, float tm, Smem& sm) {
+  const int t = threadIdx.x;
+  if (a.top_k <= NWAVE * TK_WAVE_TOP) {
+    // k <= 64: each wave sorts its 64 group maxima in registers and posts
+    // its 16 largest; wave 0 sorts those 64.  Their k-th largest is at most
+    // the k-th largest of all 256 group maxima (a subset's), so at least
+    // k logits of the row lie at or above it, and it equals it whenever no
+    // wave holds more than 16 of the chunk's k largest; their 8 largest
+    // are the chunk's 8 largest group maxima (each wave posted its own 8).
+    // Two barriers instead of the sorting network's 36.
+    const int lane = t & 63, w = t >> 6;
+    const uint32_t kw = wave_sort_desc(ord_key(tm));
+    if (lane < TK_WAVE_TOP) sm.s.tk16[w * TK_WAVE_TOP + lane] = kw;
+    __syncthreads();
+    if (t < 64) {
+      const uint32_t k2 = wave_sort_desc(sm.s.tk16[lane]);
+      if (lane == a.top_k - 1) sm.s.tkb = k2;
+      if (lane < CTOP) __builtin_nontemporal_store(k2, &a.ctop[(size_t)chunk_id * CTOP + lane]);
+    }
+    __syncthreads();
+    return sm.s.tkb;
+  }
+  __syncthreads();
+  sm.s.tk[t] = ord_key(tm);
+  bitonic_desc(sm.s.tk, WG);
+  const uint32_t bound = a.top_k <= WG ? (uint32_t)sm.s.tk[a.top_k - 1] : KEY_NEG_INF;
+  if (t < CTOP) __builtin_nontemporal_store((uint32_t)sm.s.tk[t], &a.ctop[(size_t)chunk_id * CTOP + t]);
+  return bound;
+}
+
 // Candidate emission and the chunk record, once the chunk max mc (and for
 // sum modes the chunk sum s in the record's convention, chunk_weight; in
-// greedy mode the arg-max) are known.  um / gm are the unit and group maxima
-// of this thread, tm its max.  Shared memory written here is first written
-// after a barrier of this call, so a workgroup can run it for consecutive
-// items without a barrier in between.  Only the next launch reads what is
-// stored here, so no atomic or fence is needed; the stores are nontemporal,
-// so that the records and lists do not sit dirty in this launch's cache.
+// greedy mode the arg-max) and, for filtered modes, the candidate bound are
+// known.  um / gm are the unit and group maxima of this thread.  Shared
+// memory written here is first written after a barrier of this call, so a
+// workgroup can run it for consecutive items without a barrier in between.
+// Only the next launch reads what is stored here, so no atomic or fence is
+// needed; the stores are nontemporal, so that the records and lists do not
+// sit dirty in this launch's cache.
 template <int DT, int MODE, bool VEC>
-__device__ __forceinline__ void stream_emit(const Args& a, int item, const float (&um)[UnitT<DT, VEC>::N],
-                                            const float (&gm)[4], float tm, float mc, double s, int arg,
+__device__ __forceinline__ void chunk_lists(const Args& a, int item, const float (&um)[UnitT<DT, VEC>::N],
+                                            const float (&gm)[4], float mc, double s, int arg, uint32_t bound,
                                             Smem& sm) {
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
   constexpr int UL = UnitT<DT, VEC>::L, UN = UnitT<DT, VEC>::N;
@@ -1223,45 +1261,9 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
   const int rl = udiv(item, a.dch);
   const int c0 = (item - rl * a.nchunks) * CE;
   const int chunk_id = item;
-  // candidate bound of this chunk: every finite logit at or above it is emitted
-  uint32_t bound = 0u;
   int nc = 0;
   if (FILT) {
-    float thr;
-    if (MODE == M_TOPP) {
-      // window below the chunk max (which is <= the row max)
-      bound = ord_key(mc - row_temp(a, rl).win);
-    } else if (a.top_k <= NWAVE * TK_WAVE_TOP) {
-      // k <= 64: each wave sorts its 64 thread maxima in registers and posts
-      // its 16 largest; wave 0 sorts those 64.  Their k-th largest is at most
-      // the k-th largest of all 256 thread maxima (a subset's), so at least
-      // k logits of the row lie at or above it, and it equals it whenever no
-      // wave holds more than 16 of the chunk's k largest; their 8 largest
-      // are the chunk's 8 largest thread maxima (each wave posted its own 8).
-      // Two barriers instead of the sorting network's 36.
-      const int lane = t & 63, w = t >> 6;
-      const uint32_t kw = wave_sort_desc(ord_key(tm));
-      if (lane < TK_WAVE_TOP) sm.s.tk16[w * TK_WAVE_TOP + lane] = kw;
-      __syncthreads();
-      if (t < 64) {
-        const uint32_t k2 = wave_sort_desc(sm.s.tk16[lane]);
-        if (lane == a.top_k - 1) sm.s.tkb = k2;
-        if (lane < CTOP) __builtin_nontemporal_store(k2, &a.ctop[(size_t)chunk_id * CTOP + lane]);
-      }
-      __syncthreads();
-      bound = sm.s.tkb;
-    } else {
-      // the k-th largest of the 256 thread maxima is <= the row's k-th largest
-      // logit (for k > 256 no bound follows: every finite logit qualifies)
-      __syncthreads();
-      sm.s.tk[t] = ord_key(tm);
-      bitonic_desc(sm.s.tk, WG);
-      bound = a.top_k <= WG ? (uint32_t)sm.s.tk[a.top_k - 1] : KEY_NEG_INF;
-      // the chunk's largest thread maxima: values of the row, from which the
-      // row merge bounds the row's k-th largest from below
-      if (t < CTOP) __builtin_nontemporal_store((uint32_t)sm.s.tk[t], &a.ctop[(size_t)chunk_id * CTOP + t]);
-    }
-    thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
+    const float thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wn = wave_emit<DT, VEC>(um, gm, thr, c0, &sm.s.cand[w * CAND_CAP], CAND_CAP);
     if ((t & 63) == 0) sm.s.wn[w] = wn;
@@ -1325,6 +1327,22 @@ __device__ __forceinline__ void stream_emit(const Args& a, int item, const float
     __builtin_nontemporal_store(u32x4{(uint32_t)sb, (uint32_t)(sb >> 32), __float_as_uint(mc), bound}, rp4);
     __builtin_nontemporal_store(u32x4{(uint32_t)nc, (uint32_t)arg, 0u, 0u}, rp4 + 1);
   }
+}
+
+// The streaming kernel's candidate bound (top-p: the window below the chunk
+// max, which is <= the row max; top-k: chunk_topk_bound over the thread
+// maxima tm), then the lists and the record.
+template <int DT, int MODE, bool VEC>
+__device__ __forceinline__ void stream_emit(const Args& a, int item, const float (&um)[UnitT<DT, VEC>::N],
+                                            const float (&gm)[4], float tm, float mc, double s, int arg,
+                                            Smem& sm) {
+  constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
+  uint32_t bound = 0u;
+  if (FILT) {
+    const int rl = udiv(item, a.dch);
+    bound = MODE == M_TOPP ? ord_key(mc - row_temp(a, rl).win) : chunk_topk_bound(a, item, tm, sm);
+  }
+  chunk_lists<DT, MODE, VEC>(a, item, um, gm, mc, s, arg, bound, sm);
 }
 
 // Element-load path (rows not 16-byte aligned): one workgroup per (row,
@@ -1558,6 +1576,119 @@ __global__ void __launch_bounds__(WG, (stream_wg_per_cu<DT, true>())) stream_ker
   check_offsets(a);
   if (idle) return;
   stream_vec_body<DT, MODE>(a, item, rl, c0, cn, cr, sm);
+}
+
+// ---------------------------------------------------------------------------
+// chunk records from the output projections' tile statistics
+// ---------------------------------------------------------------------------
+
+// In place of the streaming kernel when the float32 logit rows were written
+// by the output projections together with their tile statistics (TS_SUM or
+// TS_ARG records of TILE_N-column tiles in R, whose rows number rstride, of
+// ntg tiles per row).  One workgroup per (row, chunk) item, as there.  The
+// chunk's record follows from its 128 tiles': the max is the largest tile
+// max; the sum is the tiles' sums moved from their offsets ceil(max_t * c2)
+// to the chunk's ceil(mc * c2) by exact ldexp (the record's convention,
+// chunk_weight); the greedy arg-max is the lowest arg-max among the tiles
+// holding mc.  Filtered rows read back only the tiles whose max reaches the
+// chunk's candidate bound (no unit of another tile can reach it), with the
+// top-k bound taken over the tile maxima, and emit those units as the
+// streaming kernel does.  When mc * c2 overflows float the sum is taken from
+// the logits, as there.
+template <int MODE>
+__global__ void __launch_bounds__(WG, (stream_wg_per_cu<D_F32, true>()))
+    tile_chunk_kernel(Args a, const uint2* __restrict__ R, int rstride, int ntg) {
+  constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
+  constexpr bool SUM = MODE == M_PLAIN || MODE == M_TOPP;
+  constexpr int EPV = ElemT<D_F32>::EPV, NV = EPT / EPV;
+  __shared__ Smem sm;
+  __shared__ float tmx[TILES_PER_CHUNK];  // the chunk's tile maxima
+  const int item = stream_item(a);
+  clear_counters(a);
+  check_offsets(a);
+  if (item >= a.nitems) return;
+  const int rl = udiv(item, a.dch);
+  const int c0 = (item - rl * a.nchunks) * CE;
+  const int cn = min(CE, a.V - c0);
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const RowT rt = row_temp(a, rl);
+
+  // thread t < 128: tile c0 / TILE_N + t
+  const int g = c0 / TILE_N + t;
+  const bool has = t < TILES_PER_CHUNK && g < ntg;
+  float tmax = -INFINITY;
+  uint32_t tv = 0u;
+  if (has) {
+    const uint2 r = R[((size_t)(g / TILE_GROUP) * rstride + lin_row(a, rl)) * TILE_GROUP + g % TILE_GROUP];
+    tmax = __uint_as_float(r.x);
+    tv = r.y;
+  }
+  if (FILT && t < TILES_PER_CHUNK) tmx[t] = tmax;
+  const float mw = dpp_wave_fmax(tmax);
+  if ((t & 63) == 0) sm.s.rm[w] = mw;
+  __syncthreads();
+  float mc = sm.s.rm[0];
+#pragma unroll
+  for (int i = 1; i < NWAVE; ++i) mc = fmax2(mc, sm.s.rm[i]);
+
+  double s = 0.0;
+  if (SUM && mc > -INFINITY) {
+    const float Mi = __builtin_ceilf(mc * rt.c2);
+    if (Mi < INFINITY) {
+      double term = 0.0;
+      if (tmax > -INFINITY)
+        term = __builtin_amdgcn_ldexp((double)__uint_as_float(tv),
+                                      (int)fmaxf(__builtin_ceilf(tmax * rt.c2) - Mi, -2048.0f));
+      s = block_sum(term, sm.red);
+    } else {
+      s = block_sum(chunk_sum_slow<D_F32>(row_ptr(a, rl, 4) + (size_t)c0 * 4, cn, mc, rt.c2), sm.red);
+    }
+  }
+  int arg = 0;
+  if (MODE == M_GREEDY) {
+    const int best = block_min_i(has && tmax == mc ? (int)tv : INT_MAX, sm.red);
+    arg = best == INT_MAX ? c0 : best;
+  }
+
+  float um[NV], gm[4];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) um[u] = -INFINITY;
+  uint32_t bound = 0u;
+  if (FILT) {
+    bound = MODE == M_TOPP ? ord_key(mc - rt.win) : chunk_topk_bound(a, item, tmax, sm);
+    const float thr = bound > KEY_NEG_INF ? key_val(bound) : -3.402823466e38f;
+    // Vector u * WG + t of the chunk (logits 4 (u * WG + t) .. + 3) lies in
+    // tile 16 u + t / 16.  A vector of a tile below thr addresses the end of
+    // its descriptor's range instead: it reads as zero and touches no memory.
+    const char* cp = row_ptr(a, rl, 4) + (size_t)c0 * 4;
+    const int nbytes = cn * 4;
+    uint4 raw[NV];
+    bool rd[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int ub = u * WG * 16;
+      const int nrec = max(nbytes - ub, 0);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(cp + ub), (short)0, nrec, 0x00020000);
+      rd[u] = tmx[(WG * EPV / TILE_N) * u + t / (TILE_N / EPV)] >= thr;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, rd[u] ? t * 16 : nrec, 0, CPOL_NT);
+      raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    const int nvec = cn / EPV;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      float v[EPV];
+      unpack16<D_F32>(raw[u], v);
+      const bool out = !rd[u] || t >= nvec - u * WG;
+      float x = v[0];
+#pragma unroll
+      for (int e = 1; e < EPV; ++e) x = fmax2(x, v[e]);
+      um[u] = out ? -INFINITY : x;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gm[q] = fmax2(um[2 * q], um[2 * q + 1]);
+  chunk_lists<D_F32, MODE, true>(a, item, um, gm, mc, s, arg, bound, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -2812,6 +2943,20 @@ hipError_t launch_stream(const Args& a, int dtype, int mode, bool vec, unsigned 
     return hipExtLaunchKernel(reinterpret_cast<const void*>(f), dim3(grid), dim3(WG), args, 0, s, e0, e1, 0);
   }
   hipLaunchKernelGGL(f, dim3(grid), dim3(WG), 0, s, a);
+  return hipGetLastError();
+}
+
+// Chunk records from tile statistics: the streaming kernel's grid.
+hipError_t launch_tile_chunk(const Args& a, int mode, unsigned grid, const void* R, int32_t rstride, int32_t ntg,
+                             hipStream_t s) {
+  const uint2* r = static_cast<const uint2*>(R);
+  switch (mode) {
+    case M_PLAIN: hipLaunchKernelGGL(tile_chunk_kernel<M_PLAIN>, dim3(grid), dim3(WG), 0, s, a, r, rstride, ntg); break;
+    case M_TOPK: hipLaunchKernelGGL(tile_chunk_kernel<M_TOPK>, dim3(grid), dim3(WG), 0, s, a, r, rstride, ntg); break;
+    case M_TOPP: hipLaunchKernelGGL(tile_chunk_kernel<M_TOPP>, dim3(grid), dim3(WG), 0, s, a, r, rstride, ntg); break;
+    case M_TOPKP: hipLaunchKernelGGL(tile_chunk_kernel<M_TOPKP>, dim3(grid), dim3(WG), 0, s, a, r, rstride, ntg); break;
+    default: hipLaunchKernelGGL(tile_chunk_kernel<M_GREEDY>, dim3(grid), dim3(WG), 0, s, a, r, rstride, ntg); break;
+  }
   return hipGetLastError();
 }
 

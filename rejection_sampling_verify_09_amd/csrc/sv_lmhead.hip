@@ -23,8 +23,12 @@
 //  * the 128-row tiles of one 256-column W panel are consecutive tile ids
 //    placed on one XCD (workgroup ids go round-robin over the 8 XCDs), so the
 //    panel is read from HBM once and served to the other row tiles by that
-//    XCD's L2.
-#include <hip/hip_runtime.h>
+//    XCD's L2;
+//  * for the verification that follows, the epilogue can also reduce each
+//    wave's 64 columns of every row to a tile record (max, and the tile's
+//    exp2 sum or arg-max: TileStat), so that the chunk statistics need not
+//    read the logits again (tile_stats).
+#include "sv_common.hpp"
 
 #include <atomic>
 #include <cstddef>
@@ -50,9 +54,94 @@ struct LmArgs {
   float* C;           // [M, V]
   int32_t M, V, d;
   int32_t mtiles, ntiles, per_xcd;
+  // tile statistics (stat != TS_NONE): records of rstride rows in R, this
+  // projection's rows from row roff; c2 = log2(e) / T of its rows
+  uint2* R;
+  int32_t rstride, roff, stat;
+  float c2;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// All-reductions over each 32-lane half of the wave (lanes 0-31 and 32-63),
+// for the 16 rows of a block at once (independent chains interleave, so no
+// step waits on the one before): DPP quad swaps and half-row / row mirrors
+// within each row of 16 lanes, then v_permlane16_swap, which hands each lane
+// the value of its partner in the other row of its half.  Each step combines
+// a lane with a partner that combines it back, so every lane of a half ends
+// with the same bits.
+template <typename F>
+__device__ __forceinline__ void half_reduce16(uint32_t (&v)[16], F op) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = op(v[r], dpp_mov<DPP_QP_1032>(v[r]));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = op(v[r], dpp_mov<DPP_QP_2301>(v[r]));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = op(v[r], dpp_mov<DPP_HALF_MIRROR>(v[r]));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = op(v[r], dpp_mov<DPP_MIRROR>(v[r]));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(v[r], v[r], false, false);
+    v[r] = op(sw[0], sw[1]);
+  }
+}
+
+// Tile records of one wave's block of logits: rows row0 + 0 .. 32 mblocks - 1
+// (those below M), columns col0 .. col0 + 63 (those below V; col0 is a
+// multiple of TILE_N).  Lane (h, l32), accumulator r of block (mb, nb) holds
+// row 32 mb + 8 (r / 4) + 4 h + r % 4, column col0 + 32 nb + l32.  For each
+// row: the max over the tile's columns, then the sum of exp2(x * c2 - Mt),
+// Mt = ceil(max * c2) (every term at most 1; as the streaming kernel's sums
+// against an integer offset), or the lowest column holding the max.  Lane
+// l32 = r of each half keeps the record of its row (mb, r), so one store per
+// block writes 32 records.
+__device__ __forceinline__ void tile_stats(const LmArgs& a, const f32x16 (&acc)[4][2], int row0, int mblocks,
+                                           int col0, int h, int l32) {
+  if (col0 >= a.V) return;
+  const bool ok0 = col0 + l32 < a.V, ok1 = col0 + 32 + l32 < a.V;
+  const int g = col0 / TILE_N;
+  uint2* rg = a.R + ((size_t)(g / TILE_GROUP) * a.rstride + a.roff) * TILE_GROUP + g % TILE_GROUP;
+  const bool sum = a.stat == TS_SUM;
+  const auto umax = [](uint32_t x, uint32_t y) { return max(x, y); };
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if (mb >= mblocks) continue;
+    float x0[16], x1[16];
+    uint32_t k[16], v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x0[r] = ok0 ? acc[mb][0][r] : -INFINITY;
+      x1[r] = ok1 ? acc[mb][1][r] : -INFINITY;
+      k[r] = max(ord_key(x0[r]), ord_key(x1[r]));
+    }
+    half_reduce16(k, umax);
+    if (sum) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float Mt = fmaxf(__builtin_ceilf(key_val(k[r]) * a.c2), -1.0e30f);
+        v[r] = __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(x0[r], a.c2, -Mt)) +
+                               __builtin_amdgcn_exp2f(__builtin_fmaf(x1[r], a.c2, -Mt)));
+      }
+      half_reduce16(v, [](uint32_t x, uint32_t y) { return __float_as_uint(__uint_as_float(x) + __uint_as_float(y)); });
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float m = key_val(k[r]);
+        v[r] = (uint32_t)(x0[r] == m ? col0 + l32 : x1[r] == m ? col0 + 32 + l32 : INT_MAX);
+      }
+      half_reduce16(v, [](uint32_t x, uint32_t y) { return (uint32_t)min((int32_t)x, (int32_t)y); });
+    }
+    uint32_t km = 0u, kv = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      km = l32 == r ? k[r] : km;
+      kv = l32 == r ? v[r] : kv;
+    }
+    const int m = row0 + 32 * mb + 8 * (l32 >> 2) + 4 * h + (l32 & 3);
+    if (l32 < 16 && m < a.M) rg[(size_t)m * TILE_GROUP] = make_uint2(__float_as_uint(key_val(km)), kv);
+  }
+}
 
 __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
   __shared__ __attribute__((aligned(16))) char As[2][LM_BM * LM_ROWB];
@@ -152,6 +241,7 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
   // lane (h, l32), accumulator r of 32 x 32 block (mb, nb) holds row
   // 32 mb + 8 (r / 4) + 4 h + r % 4, column 32 nb + l32 of the wave's columns
   const int mblocks = min(4, (a.M - m0 + 31) / 32);
+  if (a.stat != TS_NONE) tile_stats(a, acc, m0, mblocks, n0 + 64 * w, h, l32);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = n0 + 64 * w + 32 * nb + l32;
@@ -255,6 +345,7 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8k64(LmArgs a) {
     if (more) { lstore((kb & 1) ^ 1); __syncthreads(); }
   }
   const int mblocks = any ? min(4, (a.M - wrow0 + 31) / 32) : 0;
+  if (a.stat != TS_NONE) tile_stats(a, acc, wrow0, mblocks, n0 + 64 * wn, h, l32);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = n0 + 64 * wn + 32 * nb + l32;
@@ -274,8 +365,12 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8k64(LmArgs a) {
 }  // namespace
 
 // Shapes the caller has checked: M >= 1, V >= 1, d a positive multiple of 64 (the k block is 32),
-// H, W 16-byte aligned, the tile count within the grid limit.
-hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s) {
+// H, W 16-byte aligned, the tile count within the grid limit.  With stat !=
+// TS_NONE the epilogue also writes the tile records of the M rows to R, as
+// rows roff .. roff + M - 1 of rstride (records of 64-column tiles, grouped by
+// 256 columns: TileStat), with c2 = log2(e) / T.
+hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s,
+                          void* R, int32_t rstride, int32_t roff, int stat, float c2) {
   // the wide tile when 256-row tiles waste no more rows than 128-row ones
   // (plus 5%): M = 448 takes it, M = 384 does not
   const double w256 = 1.0 - (double)M / (256.0 * ((M + 255) / 256));
@@ -288,6 +383,11 @@ hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int
     a.M = M;
     a.V = V;
     a.d = d;
+    a.R = static_cast<uint2*>(R);
+    a.rstride = rstride;
+    a.roff = roff;
+    a.stat = R ? stat : TS_NONE;
+    a.c2 = c2;
     a.mtiles = (M + 255) / 256;
     a.ntiles = (V + 255) / 256;
     a.per_xcd = (a.mtiles * a.ntiles + LM_XCD - 1) / LM_XCD;
@@ -312,6 +412,11 @@ hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int
   a.M = M;
   a.V = V;
   a.d = d;
+  a.R = static_cast<uint2*>(R);
+  a.rstride = rstride;
+  a.roff = roff;
+  a.stat = R ? stat : TS_NONE;
+  a.c2 = c2;
   a.mtiles = (M + LM_BM - 1) / LM_BM;
   a.ntiles = (V + LM_BN - 1) / LM_BN;
   a.per_xcd = (a.mtiles * a.ntiles + LM_XCD - 1) / LM_XCD;
