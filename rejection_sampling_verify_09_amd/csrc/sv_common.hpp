@@ -172,6 +172,19 @@ __device__ __forceinline__ double chunk_weight(double s_c, float m_c, float m, f
   return s_c * exp2(f + ((double)m_c - (double)m) * (invT * 1.4426950408889634074));
 }
 
+// A buffer resource over nbytes at p, for a range every lane of the wave
+// shares (a row, or a chunk of one): base and size are read from the first
+// lane, so they sit in scalar registers.  Built from a value the compiler
+// cannot prove uniform, the resource would be taken lane by lane in a loop
+// around every load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, int nbytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
+}
+
 // Order-preserving map float -> uint32 (larger float, larger key).
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -363,18 +363,17 @@ __device__ __forceinline__ int row_keep(const char* rp, int V, uint32_t tau, flo
   return sm.ncand;
 }
 
-// The 8 logits j0 .. j0+7 of a row (-inf past V).  Rows that are 16-byte
-// aligned with a length of whole 16-byte vectors (vec) take one 16-byte
-// buffer load per 8 bf16 (two per 8 f32), ranged to the row: a vector past
-// the row end reads as zero without a memory access.  No load sits behind a
-// lane condition, so the compiler keeps a caller's loads in flight together
-// (plain loads under a per-lane bounds branch were each waited for before
-// the next was issued).
+// The 8 logits j0 .. j0+7 of a row (-inf past V); row and V are the same on
+// every lane of the wave.  Rows that are 16-byte aligned with a length of
+// whole 16-byte vectors (vec) take one 16-byte buffer load per 8 bf16 (two
+// per 8 f32), ranged to the row: a vector past the row end reads as zero
+// without a memory access.  No load sits behind a lane condition, so the
+// compiler keeps a caller's loads in flight together (plain loads under a
+// per-lane bounds branch were each waited for before the next was issued).
 template <int DT>
 __device__ __forceinline__ void load8(const char* row, int j0, int V, bool vec, float (&x)[8]) {
   if (vec) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, V * ElemT<DT>::ESZ, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = wave_rsrc(row, V * ElemT<DT>::ESZ);
     if (DT == D_BF16) {
       const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, j0 * 2, 0, 0);
 #pragma unroll
@@ -408,8 +407,7 @@ struct Raw8 {
 };
 template <int DT>
 __device__ __forceinline__ Raw8<DT> load8_raw(const char* row, int j0, int V) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, V * ElemT<DT>::ESZ, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = wave_rsrc(row, V * ElemT<DT>::ESZ);
   Raw8<DT> r;
 #pragma unroll
   for (int h = 0; h < (DT == D_BF16 ? 1 : 2); ++h) {
@@ -815,13 +813,22 @@ __device__ __forceinline__ void filter_row(const Args& a, int rl, const char* rp
         }
       }
     } else {  // M_TOPP: every candidate, sorted descending in sm.r.cand
-      const int np2 = pow2_at_least(cnt < 2 ? 2 : cnt);
-      __syncthreads();
-      for (int e = cnt + t; e < np2; e += BS) sm.r.cand[e] = 0;
-      bitonic_desc<BS>(sm.r.cand, np2);
-      ns = cnt;
+      // Candidates whose mass stays below top_p cannot decide (the nucleus
+      // reaches below lg): the next tier is taken without a sort or a walk.
+      double ls = 0.0;
+      for (int e = t; e < cnt; e += BS)
+        ls += exp(((double)key_val((uint32_t)(sm.r.cand[e] >> 32)) - (double)m) * invT);
+      if (block_sum<BS / 64>(ls, sm.red) < a.top_p * snorm) {
+        (pass == 0 ? again : fb) = true;
+      } else {
+        const int np2 = pow2_at_least(cnt < 2 ? 2 : cnt);
+        __syncthreads();
+        for (int e = cnt + t; e < np2; e += BS) sm.r.cand[e] = 0;
+        bitonic_desc<BS>(sm.r.cand, np2);
+        ns = cnt;
+      }
     }
-    if (!fb && (MODE == M_TOPP || MODE == M_TOPKP)) {
+    if (!fb && !again && (MODE == M_TOPP || MODE == M_TOPKP)) {
       // smallest descending prefix whose mass reaches top_p, ties included;
       // thread t holds sorted entries PT t .. PT t + PT - 1
       constexpr int PT = ROW_CAND / BS;
