@@ -63,83 +63,75 @@ struct LmArgs {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// All-reductions over each 32-lane half of the wave (lanes 0-31 and 32-63),
-// for the 16 rows of a block at once (independent chains interleave, so no
-// step waits on the one before): DPP quad swaps and half-row / row mirrors
-// within each row of 16 lanes, then v_permlane16_swap, which hands each lane
-// the value of its partner in the other row of its half.  Each step combines
-// a lane with a partner that combines it back, so every lane of a half ends
-// with the same bits.
-template <typename F>
-__device__ __forceinline__ void half_reduce16(uint32_t (&v)[16], F op) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = op(v[r], dpp_mov<DPP_QP_1032>(v[r]));
-#pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = op(v[r], dpp_mov<DPP_QP_2301>(v[r]));
-#pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = op(v[r], dpp_mov<DPP_HALF_MIRROR>(v[r]));
-#pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = op(v[r], dpp_mov<DPP_MIRROR>(v[r]));
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const auto sw = __builtin_amdgcn_permlane16_swap(v[r], v[r], false, false);
-    v[r] = op(sw[0], sw[1]);
-  }
-}
-
 // Tile records of one wave's block of logits: rows row0 + 0 .. 32 mblocks - 1
 // (those below M), columns col0 .. col0 + 63 (those below V; col0 is a
 // multiple of TILE_N).  Lane (h, l32), accumulator r of block (mb, nb) holds
-// row 32 mb + 8 (r / 4) + 4 h + r % 4, column col0 + 32 nb + l32.  For each
-// row: the max over the tile's columns, then the sum of exp2(x * c2 - Mt),
-// Mt = ceil(max * c2) (every term at most 1; as the streaming kernel's sums
-// against an integer offset), or the lowest column holding the max.  Lane
-// l32 = r of each half keeps the record of its row (mb, r), so one store per
-// block writes 32 records.
-__device__ __forceinline__ void tile_stats(const LmArgs& a, const f32x16 (&acc)[4][2], int row0, int mblocks,
-                                           int col0, int h, int l32) {
+// row 32 mb + 8 (r / 4) + 4 h + r % 4, column col0 + 32 nb + l32.  Each
+// 32-row block goes through the wave's own LDS tile (TS_LDS floats: 32 rows
+// of 64 columns, rows padded to 68), and lane pair (2 rho, 2 rho + 1) then
+// takes row rho, 32 columns a lane: the max, then the sum of exp2(x * c2 -
+// Mt), Mt = ceil(max * c2) (every term at most 1; as the streaming kernel's
+// sums against an integer offset), or the lowest column holding the max;
+// the two lanes of a pair combine with one DPP swap (a + b on both, the
+// same bits), and the even lane stores the record.
+constexpr int TS_ROW = 68;
+constexpr int TS_LDS = 32 * TS_ROW;
+// lm_gemm_kernel: waves 0-1 take As, waves 2-3 Ws; lm_gemm_w8k64: 8 tiles in its 128 KB
+static_assert(2 * TS_LDS * 4 <= 2 * LM_BM * LM_ROWB && 2 * TS_LDS * 4 <= 2 * LM_BN * LM_ROWB, "tile fits");
+static_assert(8 * TS_LDS * 4 <= 4 * 256 * 128, "tile fits");
+__device__ __forceinline__ void tile_stats(const LmArgs& a, const f32x16 (&acc)[4][2], float* lds, int row0,
+                                           int mblocks, int col0, int h, int l32) {
   if (col0 >= a.V) return;
-  const bool ok0 = col0 + l32 < a.V, ok1 = col0 + 32 + l32 < a.V;
+  const int lane = threadIdx.x & 63, rho = lane >> 1, eta = lane & 1;
   const int g = col0 / TILE_N;
   uint2* rg = a.R + ((size_t)(g / TILE_GROUP) * a.rstride + a.roff) * TILE_GROUP + g % TILE_GROUP;
+  const int cb = col0 + 32 * eta;  // this lane's first column
+  const int nval = min(32, a.V - cb);  // its columns below V (may be <= 0)
   const bool sum = a.stat == TS_SUM;
-  const auto umax = [](uint32_t x, uint32_t y) { return max(x, y); };
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if (mb >= mblocks) continue;
-    float x0[16], x1[16];
-    uint32_t k[16], v[16];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x0[r] = ok0 ? acc[mb][0][r] : -INFINITY;
-      x1[r] = ok1 ? acc[mb][1][r] : -INFINITY;
-      k[r] = max(ord_key(x0[r]), ord_key(x1[r]));
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lds[(8 * (r >> 2) + 4 * h + (r & 3)) * TS_ROW + 32 * nb + l32] = acc[mb][nb][r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float x[32];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(lds + rho * TS_ROW + 32 * eta + 4 * k);
+      x[4 * k] = v.x;
+      x[4 * k + 1] = v.y;
+      x[4 * k + 2] = v.z;
+      x[4 * k + 3] = v.w;
     }
-    half_reduce16(k, umax);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) x[k] = k < nval ? x[k] : -INFINITY;
+    uint32_t mk = ord_key(x[0]);
+#pragma unroll
+    for (int k = 1; k < 32; ++k) mk = max(mk, ord_key(x[k]));
+    mk = max(mk, dpp_mov<DPP_QP_1032>(mk));
+    const float m = key_val(mk);
+    uint32_t v;
     if (sum) {
+      const float Mt = fmaxf(__builtin_ceilf(m * a.c2), -1.0e30f);
+      float e = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float Mt = fmaxf(__builtin_ceilf(key_val(k[r]) * a.c2), -1.0e30f);
-        v[r] = __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(x0[r], a.c2, -Mt)) +
-                               __builtin_amdgcn_exp2f(__builtin_fmaf(x1[r], a.c2, -Mt)));
-      }
-      half_reduce16(v, [](uint32_t x, uint32_t y) { return __float_as_uint(__uint_as_float(x) + __uint_as_float(y)); });
+      for (int k = 0; k < 32; ++k) e += __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], a.c2, -Mt));
+      v = __float_as_uint(e + __uint_as_float(dpp_mov<DPP_QP_1032>(__float_as_uint(e))));
     } else {
+      int c = INT_MAX;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float m = key_val(k[r]);
-        v[r] = (uint32_t)(x0[r] == m ? col0 + l32 : x1[r] == m ? col0 + 32 + l32 : INT_MAX);
-      }
-      half_reduce16(v, [](uint32_t x, uint32_t y) { return (uint32_t)min((int32_t)x, (int32_t)y); });
+      for (int k = 31; k >= 0; --k) c = x[k] == m ? cb + k : c;
+      v = (uint32_t)min(c, (int)dpp_mov<DPP_QP_1032>((uint32_t)c));
     }
-    uint32_t km = 0u, kv = 0u;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      km = l32 == r ? k[r] : km;
-      kv = l32 == r ? v[r] : kv;
-    }
-    const int m = row0 + 32 * mb + 8 * (l32 >> 2) + 4 * h + (l32 & 3);
-    if (l32 < 16 && m < a.M) rg[(size_t)m * TILE_GROUP] = make_uint2(__float_as_uint(key_val(km)), kv);
+    const int row = row0 + 32 * mb + rho;
+    if (eta == 0 && row < a.M) rg[(size_t)row * TILE_GROUP] = make_uint2(__float_as_uint(m), v);
   }
 }
 
@@ -241,7 +233,12 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
   // lane (h, l32), accumulator r of 32 x 32 block (mb, nb) holds row
   // 32 mb + 8 (r / 4) + 4 h + r % 4, column 32 nb + l32 of the wave's columns
   const int mblocks = min(4, (a.M - m0 + 31) / 32);
-  if (a.stat != TS_NONE) tile_stats(a, acc, m0, mblocks, n0 + 64 * w, h, l32);
+  if (a.stat != TS_NONE) {
+    // every wave is done with the staged operands: each takes TS_LDS floats of them
+    __syncthreads();
+    float* lds = w < 2 ? reinterpret_cast<float*>(As[0]) + w * TS_LDS : reinterpret_cast<float*>(Ws[0]) + (w - 2) * TS_LDS;
+    tile_stats(a, acc, lds, m0, mblocks, n0 + 64 * w, h, l32);
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = n0 + 64 * w + 32 * nb + l32;
@@ -345,7 +342,11 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8k64(LmArgs a) {
     if (more) { lstore((kb & 1) ^ 1); __syncthreads(); }
   }
   const int mblocks = any ? min(4, (a.M - wrow0 + 31) / 32) : 0;
-  if (a.stat != TS_NONE) tile_stats(a, acc, wrow0, mblocks, n0 + 64 * wn, h, l32);
+  if (a.stat != TS_NONE) {
+    // every wave is done with the staged operands: each takes TS_LDS floats of them
+    __syncthreads();
+    tile_stats(a, acc, reinterpret_cast<float*>(smem) + w * TS_LDS, wrow0, mblocks, n0 + 64 * wn, h, l32);
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = n0 + 64 * wn + 32 * nb + l32;
