@@ -2483,7 +2483,13 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
         sm.px[K + 1 + i] = (xtok >= 0 && xtok < a.V) ? (double)a.qprob[(size_t)(g.x0 + i) * a.V + xtok] : 0.0;
     }
   };
-  if (w < rps) merge_row(w);
+  // Wave w runs on SIMD w % 4.  With 4k + 1 rows (2K + 1 at even K) SIMD 0
+  // runs one row wave more than the others: it takes the first rows (target
+  // rows, whose merges are lighter than the draft rows'), and the other
+  // SIMDs take the rest slot by slot, a target row and draft rows each.
+  const bool spread = NR == 1 && (rps & 3) == 1;
+  const int wrow = !spread ? w : (w & 3) == 0 ? (w >> 2) : (rps + 3) / 4 + 3 * (w >> 2) + (w & 3) - 1;
+  if (w < rps) merge_row(wrow);
   if (NR > 1 && w + SQ_WAVES < rps) merge_row(w + SQ_WAVES);
   __syncthreads();
   // ---- rows the candidate lists could not decide: the whole workgroup
