@@ -51,7 +51,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_09_amd", "csrc", f)
                   for f in ("sv_common.hpp", "sv_kernels.hip")]
-LM_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_09_amd", "csrc", "sv_lmhead.hip")]
+LM_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_09_amd", "csrc", f) for f in ("sv_lmhead.hip", "sv_common.hpp")]
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
 
 
@@ -613,7 +613,8 @@ def run_lmhead(args):
     times its own, then verification.  The drafts are drawn on the GPU
     (sv_lm_logits of the draft rows, then sv_sample) before timing.  The two
     projections (lm_gemm_w8k64 for the target's 448 rows, lm_gemm_kernel for
-    the draft's 384) are the dominant work; the
+    the draft's 384, whose epilogues also write the tile records the chunk
+    records are formed from) are the dominant work; the
     weights (more than the 256 MB last-level cache) are read from HBM at
     every step."""
     import numpy as np
@@ -693,7 +694,8 @@ def run_lmhead(args):
             "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
             "frac": achieved / MFMA_BF16_PEAK_TFS,
             "traffic": measured_traffic(w.name, "lm_gemm_kernel", LM_SOURCES),
-            "kernel": "lm_gemm_w8k64 + lm_gemm_kernel (the target's and the draft's projections together)",
+            "kernel": "lm_gemm_w8k64 + lm_gemm_kernel (the target's and the draft's projections together, "
+                      "with their tile records); other_kernels_ms: tile_chunk_kernel and the sequence kernel",
             "kernel_ms": gemm_ms,
             "other_kernels_ms": other_ms, "timed_calls": prof["calls"],
             "weight_read_GBs": w_bytes / (gemm_ms / 1e3) / 1e9,
