@@ -423,6 +423,14 @@ int verify_impl(const VerifyIn& in, void* stream, bool timed = true) {
   return run_plan_locked(p, b, s, timed);
 }
 
+// Top-p candidate window (units of z = logit / T below the chunk max) on
+// rows whose chunk records come from the projections' tile records, where a
+// wider window costs only the tiles it reaches.  The flatter tops of
+// projection-fed rows put a few nuclei just past the streaming path's 5
+// units, and each such row takes the block-level merge; 6 measured best on
+// those rows (wider windows overflow the candidate lists instead).
+constexpr float TOPP_WINDOW_Z_TILES = 6.0f;
+
 // Largest hidden width accepted (the kernel needs only d % 64 == 0).
 constexpr int32_t kMaxHidden = 1 << 16;
 
@@ -502,6 +510,7 @@ int sv_spec_verify_lmhead(const void* hidden_target, const void* weight_target, 
   in.dtype = SV_F32;
   Plan p;
   if ((st = plan_verify(in, &p)) != SV_OK) return st;
+  if (fused && temperature > 0.0f) p.a.win = p.a.wind = TOPP_WINDOW_Z_TILES * temperature;
   // when timing, the slot's first two events bracket the two projections and
   // the third follows the verification
   ProfSlot* prof = prof_begin();
