@@ -55,3 +55,54 @@ def test_near_tie_rate(name):
     assert stats["sequences"] >= N_MIN
     assert stats["fail"] == 0, fails[:5]
     assert stats["flagged_rate"] < RATE_MAX, stats
+
+
+def test_near_tie_rate_projection_fed():
+    """The projection-fed path on the headline projection batch (B 64, K 6,
+    V 128256, d 4096 / 2048, T 0.7, top_p 0.9): chunk records formed from
+    the projections' tile records (V % 4 = 0), over >= 1e5 sequences.  Grid
+    inputs make the device's float32 logits equal the oracle's float64
+    ones, so the oracle's draw tables of those logits decide every draw; the
+    device recomputes the projections at every call."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from rejection_sampling_verify_09_amd import spec_verify_lmhead
+    from synth.lmhead import LM_HEADLINE, make_lm_inputs
+    from tests.harness import lm_oracle_logits, to_device
+
+    wl = LM_HEADLINE
+    log(f"[rate] {wl.name}: B={wl.B} K={wl.K} V={wl.V} d={wl.d_t}/{wl.d_d} T={wl.temperature} top_p={wl.top_p}")
+    t0 = time.time()
+    dl = make_lm_inputs(wl)
+    lt, ld = lm_oracle_logits(dl, False)
+    w = Workload(wl.name, wl.B, wl.K, wl.V, oracle.F64, "projection", 0.0, 0.0, wl.temperature, wl.top_k, wl.top_p,
+                 wl.seed, (9,))
+    d = {"target": lt, "draft": ld}
+    tabs, x, u = rate_inputs(w, d, N_MIN)
+    t1 = time.time()
+    log(f"   logits, tables and {x.shape[0]} draws in {t1 - t0:.1f} s; device calls")
+    R, B, K = x.shape
+    ht, wt = to_device(dl["hidden_t"], "bf16"), to_device(dl["weight_t"], "bf16")
+    hd, wd = to_device(dl["hidden_d"], "bf16"), to_device(dl["weight_d"], "bf16")
+    X = torch.from_numpy(x.astype(np.int32)).cuda()
+    U = torch.from_numpy(np.ascontiguousarray(u)).cuda()
+    out_t = torch.empty((R, B, K + 1), dtype=torch.int32, device="cuda")
+    out_n = torch.empty((R, B), dtype=torch.int32, device="cuda")
+    for r in range(R):
+        tok, n = spec_verify_lmhead(ht, wt, hd, wd, X[r], U[r], w.temperature, w.top_k, w.top_p)
+        out_t[r].copy_(tok)
+        out_n[r].copy_(n)
+    torch.cuda.synchronize()
+    dev_tok, dev_n = out_t.cpu().numpy(), out_n.cpu().numpy()
+    t2 = time.time()
+    stats, fails, flags = rate_check(w, d, tabs, x, u, dev_tok, dev_n)
+    log(f"   sequences={stats['sequences']} mismatched={stats['mismatched']} flagged={stats['flagged']} "
+        f"fail={stats['fail']} at_risk={stats['at_risk']} flagged_rate={stats['flagged_rate']:.2e} "
+        f"mean_n={stats['accepted_mean']:.3f} device={t2 - t1:.1f}s check={time.time() - t2:.1f}s")
+    for r, b, why in fails[:10]:
+        log(f"   FAIL draw {r} seq {b}: {why}")
+    assert stats["sequences"] >= N_MIN
+    assert stats["fail"] == 0, fails[:5]
+    assert stats["flagged_rate"] < RATE_MAX, stats
