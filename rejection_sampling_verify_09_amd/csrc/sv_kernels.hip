@@ -16,8 +16,13 @@
 //                   candidates (16-byte units at or above the chunk's bound)
 //                   and the greedy arg-max.  Its first workgroups also clear
 //                   the call's arrival counters and check ragged offsets.
-//   seq_kernel      one workgroup per sequence.  Wave j merges row j of the
-//                   sequence (max, normaliser, top-k / top-p threshold, kept
+//   tile_chunk_kernel in the streaming kernel's place when the float32 rows
+//                   come from the output projections, whose epilogues
+//                   reduced every 64-column tile to a record: the chunk
+//                   record from the chunk's 128 tile records, and only the
+//                   tiles that reach the candidate bound are read back.
+//   seq_kernel      one workgroup per sequence.  One wave merges each row of
+//                   the sequence (max, normaliser, top-k / top-p threshold, kept
 //                   list in LDS, p or q of the drafted token); a row the
 //                   candidate lists cannot decide is merged by the whole
 //                   workgroup from the full row.  Then one wave runs the
