@@ -127,6 +127,28 @@ def test_lmhead_parity_fused_filters(w):
     assert stats["max_prob_err"] <= PROB_TOL
 
 
+_FUSED_EDGES = [
+    replace(LM_WORKLOADS["lm-b3-k2-v3001-d128-dd64-t0.8-topp0.95"], name=f"lm-b3-k2-v{V}-{tag}", V=V,
+            temperature=T, top_k=k, top_p=p, seed=50 + i)
+    for i, (V, tag, T, k, p) in enumerate([
+        (68, "topp", 0.8, 0, 0.95),      # two tiles, the second with 4 columns
+        (68, "topk3", 1.0, 3, 1.0),
+        (8196, "topp", 0.8, 0, 0.95),    # a second chunk of 4 logits in one partial tile
+        (8196, "plain", 1.0, 0, 1.0),
+        (8196, "greedy", 0.0, 0, 1.0),
+        (4, "topp", 1.0, 0, 0.9),        # one tile of 4 columns
+    ])
+]
+
+
+@pytest.mark.parametrize("w", _FUSED_EDGES, ids=lambda w: w.name)
+def test_lmhead_parity_fused_edges(w):
+    """Tile records of partial tiles and of a chunk holding a few logits
+    (V % 4 = 0, so the chunk records come from the tile records)."""
+    _, _, _, stats, _, _, _ = _check(w)
+    assert stats["max_prob_err"] <= PROB_TOL
+
+
 def test_lmhead_parity_plain_normals():
     """Plain bfloat16 normals: decisions may move only where the float32
     logits' rounding could move them (flagged near-ties), and p(x), q(x)
