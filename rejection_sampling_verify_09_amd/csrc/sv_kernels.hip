@@ -2784,11 +2784,31 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
   if (t < 64) {
     const int per = (nseg + 63) / 64;
     const int s0 = min(lane * per, nseg), s1 = min(s0 + per, nseg);
-    double loc = 0.0;
+    // the run's sums RUNQ at a time, every load of a group in flight together
+    // (addresses clamped to the run; values past it are not used); the first
+    // group is kept for the walk below (the whole run when per <= RUNQ)
+    constexpr int RUNQ = 4;
+    double loc = 0.0, rv[RUNQ];
     int lastseg = -1;
-    for (int sg = s0; sg < s1; ++sg) {
-      loc += ld_dev(&ssum[sg]);
-      if (ld_dev(&slast[sg]) >= 0) lastseg = sg;
+#pragma unroll
+    for (int q = 0; q < RUNQ; ++q) rv[q] = 0.0;
+    for (int g0 = s0; g0 < s1; g0 += RUNQ) {
+      double v[RUNQ];
+      int l[RUNQ];
+#pragma unroll
+      for (int q = 0; q < RUNQ; ++q) {
+        const int sg = min(g0 + q, s1 - 1);
+        v[q] = ld_dev(&ssum[sg]);
+        l[q] = ld_dev(&slast[sg]);
+      }
+#pragma unroll
+      for (int q = 0; q < RUNQ; ++q) {
+        if (g0 == s0) rv[q] = v[q];
+        if (g0 + q < s1) {
+          loc += v[q];
+          if (l[q] >= 0) lastseg = g0 + q;
+        }
+      }
     }
     const double incl = wave_scan_f64(loc);
     Z = lane63(incl);
@@ -2808,14 +2828,23 @@ __global__ void __launch_bounds__(WG) sample_kernel(Args a) {
       int found = INT_MAX;
       double cstart = 0.0;
       if (run <= target && target < incl && s0 < s1) {
-        for (int sg = s0; sg < s1; ++sg) {
-          const double ce = run + ld_dev(&ssum[sg]);
-          if (target < ce || sg == s1 - 1) {
-            found = sg;
-            cstart = run;
-            break;
+        for (int g0 = s0; g0 < s1 && found == INT_MAX; g0 += RUNQ) {
+          double v[RUNQ];
+#pragma unroll
+          for (int q = 0; q < RUNQ; ++q) v[q] = g0 == s0 ? rv[q] : ld_dev(&ssum[min(g0 + q, s1 - 1)]);
+#pragma unroll
+          for (int q = 0; q < RUNQ; ++q) {
+            const int sg = g0 + q;
+            if (found == INT_MAX && sg < s1) {
+              const double ce = run + v[q];
+              if (target < ce || sg == s1 - 1) {
+                found = sg;
+                cstart = run;
+              } else {
+                run = ce;
+              }
+            }
           }
-          run = ce;
         }
       }
       const unsigned long long fm = __ballot(found != INT_MAX);
