@@ -69,6 +69,24 @@ def test_small_shapes(case):
     _check(w)
 
 
+LARGEST = [
+    # (B, K, V, dtype, shape, T, top_k, top_p): the boundary's largest vocabulary
+    # (256 chunks of 8192, 4096 draw segments per row) and drafts per sequence
+    (2, 2, 2097152, "bf16", "zipf", 0.8, 0, 0.9),
+    (2, 1, 2097152, "f32", "normal", 1.0, 50, 1.0),
+    (2, 2, 2097152, "bf16", "normal", 1.0, 0, 1.0),      # unfiltered: the full-row draw's tail
+    (3, 64, 1024, "f32", "zipf", 1.0, 0, 0.9),           # 129 rows a sequence
+    (2, 64, 1024, "bf16", "normal", 1.0, 0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", LARGEST, ids=lambda c: "B{}-K{}-V{}-{}-{}-T{}-k{}-p{}".format(*c))
+def test_largest_shapes(case):
+    B, K, V, dt, shape, T, k, p = case
+    w = Workload(f"largest-{B}-{K}-{V}", B, K, V, dt, shape, 2.0 if shape != "zipf" else 1.0, 0.7, T, k, p, 12)
+    _check(w)
+
+
 def test_flat_rows_take_the_full_row_paths():
     """Nearly uniform rows: the top-p nucleus is thousands of tokens (beyond
     the candidate window and the kept-list capacity)."""
