@@ -2367,6 +2367,7 @@ __device__ void sentinel_seq(const Args& a, int b, int t) {
 // ---------------------------------------------------------------------------
 constexpr int SQ_WAVES = 16;              // waves of a sequence workgroup (rows merged at once)
 constexpr int SQ_BS = SQ_WAVES * 64;      // its threads
+constexpr int SQ_WAVES_SMALL = 8;         // waves of the workgroups of sequences of at most 8 rows
 constexpr int SQ_SLOTS = SQ_WAVES;        // rows whose kept lists can stay in LDS
 constexpr int SQ_SLOT_CAP = 64;           // ... when they have at most this many entries
 static_assert(SQ_BS <= 1024, "Smem.scan holds one entry per thread");
@@ -2415,8 +2416,8 @@ __device__ __forceinline__ SeqSink seq_sink(const Args& a, SeqKSm& sm, int j, in
   return SeqSink{sm, j, a.kidx + (size_t)rl * KEEP_CAP, a.kprob + (size_t)rl * KEEP_CAP};
 }
 
-// One workgroup of SQ_BS threads per sequence.  Wave w merges the
-// sequence's rows w, w + SQ_WAVES, ... (wave_row: the chunk records and most
+// One workgroup of NW waves per sequence.  Each wave merges one of the
+// sequence's rows, and one more with NR = 2 (wave_row: the chunk records and most
 // candidate units in one round trip, the units' logits in a second); a row
 // the lists cannot decide is merged afterwards by the whole workgroup
 // (row_finalize).  Then the first wave runs the accept tests, the
@@ -2430,8 +2431,14 @@ __device__ __forceinline__ SeqSink seq_sink(const Args& a, SeqKSm& sm, int j, in
 // residual draw reads q at the target's kept tokens).
 // NR: rows per wave (2 for sequences of more than SQ_WAVES rows; a separate
 // instantiation, so that the common case keeps its register allocation).
-template <int DT, int MODE, int LAY, int NR>
-__global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
+// NW: waves of the workgroup, SQ_WAVES, or SQ_WAVES_SMALL when every
+// sequence of the call has at most that many rows: at 128 registers a lane
+// one workgroup of 16 waves fills a compute unit's register file, and two
+// of 8 waves share it (the drafting draw's one-row sequences, or K <= 3,
+// then take one round of workgroups instead of two).
+template <int DT, int MODE, int LAY, int NR, int NW>
+__global__ void __launch_bounds__(NW * 64, 4) seq_kernel(Args a) {
+  constexpr int BS = NW * 64;
   __shared__ SeqKSm sm;
   constexpr int ESZ = ElemT<DT>::ESZ;
   constexpr bool FILT = MODE == M_TOPK || MODE == M_TOPP || MODE == M_TOPKP;
@@ -2449,19 +2456,19 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
   const SeqGeo g = seq_geo<RAG>(a, b);
   const int K = g.K;
   const int rps = (MODE == M_GREEDY || QP) ? K + 1 : 2 * K + 1;
-  // rows j >= NR SQ_WAVES (sequences of more rows than the waves take) are
+  // rows j >= NR NW (sequences of more rows than the waves take) are
   // merged by the whole workgroup below, one after another
   if (t < (MAX_RPS + 31) / 32) {
-    const int j0 = 32 * t, nw = NR * SQ_WAVES;
+    const int j0 = 32 * t, nw = NR * NW;
     sm.fail[t] = j0 >= nw ? ~0u : (nw - j0 >= 32 ? 0u : ~0u << (nw - j0));
   }
   if (t < K) sm.x[t] = a.X[(size_t)g.x0 + t];
   if (t >= 256 && t - 256 <= K) sm.u[t - 256] = a.U[(size_t)g.t0 + (t - 256)];
-  if (t >= 512 && t < 576) sm.etab[t - 512] = exp2((double)(t - 512) / 64.0);
+  if (t >= BS - 64) sm.etab[t - (BS - 64)] = exp2((double)(t - (BS - 64)) / 64.0);
   __syncthreads();
 
   // ---- the sequence's rows, one wave each: wave w merges row w, and (NR = 2)
-  // row w + SQ_WAVES when the sequence has that many
+  // row w + NW when the sequence has that many
   auto merge_row = [&](const int j) {
     const int rl = seq_row<RAG>(a, g, j);
     const int i = j <= K ? j : j - K - 1;  // position of the row
@@ -2495,7 +2502,7 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
   const bool spread = NR == 1 && (rps & 3) == 1;
   const int wrow = !spread ? w : (w & 3) == 0 ? (w >> 2) : (rps + 3) / 4 + 3 * (w >> 2) + (w & 3) - 1;
   if (w < rps) merge_row(wrow);
-  if (NR > 1 && w + SQ_WAVES < rps) merge_row(w + SQ_WAVES);
+  if (NR > 1 && w + NW < rps) merge_row(w + NW);
   __syncthreads();
   // ---- rows the candidate lists could not decide: the whole workgroup
   for (int wd = 0; 32 * wd < rps; ++wd) {
@@ -2509,7 +2516,7 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
       const int rl = seq_row<RAG>(a, g, j);
       const int i = j <= K ? j : j - K - 1;
       const int xtok = i < K ? sm.x[i] : -1;
-      const RowRec rr = row_finalize<DT, MODE, SQ_BS>(a, rl, xtok, sm.blk, seq_sink(a, sm, j, rl));
+      const RowRec rr = row_finalize<DT, MODE, BS>(a, rl, xtok, sm.blk, seq_sink(a, sm, j, rl));
       if (t == 0) {
         sm.px[j] = rr.px;
         sm.rf[j] = rr.flags;
@@ -2639,7 +2646,7 @@ __global__ void __launch_bounds__(SQ_BS) seq_kernel(Args a) {
     if (QP) set_draw_prob_row(a.qprob + (size_t)(g.x0 + (res ? n : 0)) * a.V, 1, sm.blk);
     else set_draw_row(&a.row[rq], true, 1, row_temp(a, rq).invT, sm.blk);
     double Z;
-    const int tok = full_row_sample<DT, SQ_BS>(a, (double)sm.u[K], row_ptr(a, rn, ESZ), row_ptr(a, rq, ESZ), res,
+    const int tok = full_row_sample<DT, BS>(a, (double)sm.u[K], row_ptr(a, rn, ESZ), row_ptr(a, rq, ESZ), res,
                                                sm.blk, &Z);
     if (t == 0) {
       a.out_tok[(size_t)b * (a.Kmax + 1) + n] = tok;
@@ -2940,21 +2947,22 @@ static KFn pick_stream_mode(int mode, bool vec) {
   }
 }
 
-template <int DT, int LAY, int NR>
+template <int DT, int LAY, int NR, int NW>
 static KFn pick_seq(int mode) {
   switch (mode) {
-    case M_PLAIN: return (KFn)seq_kernel<DT, M_PLAIN, LAY, NR>;
-    case M_TOPK: return (KFn)seq_kernel<DT, M_TOPK, LAY, NR>;
-    case M_TOPP: return (KFn)seq_kernel<DT, M_TOPP, LAY, NR>;
-    case M_TOPKP: return (KFn)seq_kernel<DT, M_TOPKP, LAY, NR>;
-    default: return (KFn)seq_kernel<DT, M_GREEDY, LAY, NR>;
+    case M_PLAIN: return (KFn)seq_kernel<DT, M_PLAIN, LAY, NR, NW>;
+    case M_TOPK: return (KFn)seq_kernel<DT, M_TOPK, LAY, NR, NW>;
+    case M_TOPP: return (KFn)seq_kernel<DT, M_TOPP, LAY, NR, NW>;
+    case M_TOPKP: return (KFn)seq_kernel<DT, M_TOPKP, LAY, NR, NW>;
+    default: return (KFn)seq_kernel<DT, M_GREEDY, LAY, NR, NW>;
   }
 }
 
-template <int DT, int NR>
+template <int DT, int NR, int NW>
 static KFn pick_seq_lay(int mode, int lay) {
-  return lay == LAY_RAG ? pick_seq<DT, LAY_RAG, NR>(mode) : lay == LAY_QP ? pick_seq<DT, LAY_QP, NR>(mode)
-                                                                          : pick_seq<DT, LAY_RECT, NR>(mode);
+  return lay == LAY_RAG ? pick_seq<DT, LAY_RAG, NR, NW>(mode)
+         : lay == LAY_QP ? pick_seq<DT, LAY_QP, NR, NW>(mode)
+                         : pick_seq<DT, LAY_RECT, NR, NW>(mode);
 }
 
 static int layout_of(const Args& a) { return a.cu ? LAY_RAG : a.qprob ? LAY_QP : LAY_RECT; }
@@ -3014,17 +3022,25 @@ hipError_t launch_row(const Args& a, int dtype, int mode, unsigned grid, hipStre
   return hipGetLastError();
 }
 
-// The sequences: one workgroup of SQ_BS threads per sequence.
+// The sequences: one workgroup per sequence, of SQ_WAVES waves (two rows a
+// wave for sequences of more rows than that), or of SQ_WAVES_SMALL waves
+// when no sequence of the call has more rows.
 hipError_t launch_seq(const Args& a, int dtype, int mode, unsigned grid, hipStream_t s) {
   const int lay = layout_of(a);
   // the most rows a sequence of this call has
   const int rps_max = (mode == M_GREEDY || lay == LAY_QP) ? a.Kmax + 1 : 2 * a.Kmax + 1;
   KFn f;
-  if (rps_max > SQ_WAVES)
-    f = dtype == D_BF16 ? pick_seq_lay<D_BF16, 2>(mode, lay) : pick_seq_lay<D_F32, 2>(mode, lay);
-  else
-    f = dtype == D_BF16 ? pick_seq_lay<D_BF16, 1>(mode, lay) : pick_seq_lay<D_F32, 1>(mode, lay);
-  hipLaunchKernelGGL(f, dim3(grid), dim3(SQ_BS), 0, s, a);
+  int nw = SQ_WAVES;
+  if (rps_max > SQ_WAVES) {
+    f = dtype == D_BF16 ? pick_seq_lay<D_BF16, 2, SQ_WAVES>(mode, lay) : pick_seq_lay<D_F32, 2, SQ_WAVES>(mode, lay);
+  } else if (rps_max > SQ_WAVES_SMALL) {
+    f = dtype == D_BF16 ? pick_seq_lay<D_BF16, 1, SQ_WAVES>(mode, lay) : pick_seq_lay<D_F32, 1, SQ_WAVES>(mode, lay);
+  } else {
+    f = dtype == D_BF16 ? pick_seq_lay<D_BF16, 1, SQ_WAVES_SMALL>(mode, lay)
+                        : pick_seq_lay<D_F32, 1, SQ_WAVES_SMALL>(mode, lay);
+    nw = SQ_WAVES_SMALL;
+  }
+  hipLaunchKernelGGL(f, dim3(grid), dim3(nw * 64), 0, s, a);
   return hipGetLastError();
 }
 
