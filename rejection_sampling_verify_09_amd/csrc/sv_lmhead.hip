@@ -76,10 +76,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_b
 // same bits), and the even lane stores the record.
 constexpr int TS_ROW = 68;
 constexpr int TS_LDS = 32 * TS_ROW;
-// lm_gemm_kernel: waves 0-1 take As, waves 2-3 Ws; lm_gemm_w8k64: 8 tiles in its 128 KB
+// lm_gemm_kernel: waves 0-1 take As, waves 2-3 Ws; lm_gemm_w8: 8 tiles in its staging LDS
 static_assert(2 * TS_LDS * 4 <= 2 * LM_BM * LM_ROWB && 2 * TS_LDS * 4 <= 2 * LM_BN * LM_ROWB, "tile fits");
-static_assert(8 * TS_LDS * 4 <= 4 * 256 * 128, "tile fits");
-__device__ __forceinline__ void tile_stats(const LmArgs& a, const f32x16 (&acc)[4][2], float* lds, int row0,
+template <int MB>
+__device__ __forceinline__ void tile_stats(const LmArgs& a, const f32x16 (&acc)[MB][2], float* lds, int row0,
                                            int mblocks, int col0, int h, int l32) {
   if (col0 >= a.V) return;
   const int lane = threadIdx.x & 63, rho = lane >> 1, eta = lane & 1;
@@ -89,7 +89,7 @@ __device__ __forceinline__ void tile_stats(const LmArgs& a, const f32x16 (&acc)[
   const int nval = min(32, a.V - cb);  // its columns below V (may be <= 0)
   const bool sum = a.stat == TS_SUM;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     if (mb >= mblocks) continue;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -237,7 +237,7 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
     // every wave is done with the staged operands: each takes TS_LDS floats of them
     __syncthreads();
     float* lds = w < 2 ? reinterpret_cast<float*>(As[0]) + w * TS_LDS : reinterpret_cast<float*>(Ws[0]) + (w - 2) * TS_LDS;
-    tile_stats(a, acc, lds, m0, mblocks, n0 + 64 * w, h, l32);
+    tile_stats<4>(a, acc, lds, m0, mblocks, n0 + 64 * w, h, l32);
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -255,73 +255,87 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
   }
 }
 
-// The wide tile: 256 rows x 256 columns per workgroup of 8 waves (2 x 4,
-// each wave 128 x 64 as in lm_gemm_kernel), k blocks of 64 (whole 128-byte
-// lines of each operand row per load), both operands in LDS as 128-byte
-// rows whose 16-byte chunks are XOR-swizzled by row (so the fragment reads
-// of 16 consecutive rows hit distinct banks without padding), two stages:
-// 128 KB of LDS, one workgroup per CU.  Per flop it moves half the operand
-// bytes of the 128-row tile from L2; it pays when the rows fill 256-row
-// tiles about as well as 128-row ones (M = 448, not M = 384).
+// The wide tiles: 64 MB rows x 256 columns per workgroup of 8 waves (2 x 4,
+// each wave 32 MB x 64: MB = 4 as in lm_gemm_kernel, MB = 3 for row counts
+// that fill 192-row tiles), k blocks of 64 (whole 128-byte lines of each
+// operand row per load), both operands in LDS as 128-byte rows whose 16-byte
+// chunks are XOR-swizzled by row (so the fragment reads of 16 consecutive
+// rows hit distinct banks without padding), two stages: 128 KB (MB = 4) or
+// 112 KB (MB = 3) of LDS, one workgroup per CU.  Per flop the 256-row tile
+// moves half the operand bytes of the 128-row tile from L2 and the 192-row
+// tile three quarters (22% less); each W panel is staged by fewer
+// workgroups.
 __device__ __forceinline__ int sw64(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }  // byte of chunk c, row r
-__global__ void __launch_bounds__(512, 1) lm_gemm_w8k64(LmArgs a) {
+template <int MB>
+constexpr int w8_lds_bytes() { return 2 * (64 * MB + 256) * 128; }
+template <int MB>
+__global__ void __launch_bounds__(512, 1) lm_gemm_w8(LmArgs a) {
+  constexpr int TM = 64 * MB;                        // rows of the tile
+  constexpr int AST = TM * 128, WST = 256 * 128;     // bytes of one stage of each operand
+  static_assert(8 * TS_LDS * 4 <= w8_lds_bytes<MB>(), "the epilogue's tiles fit the staging LDS");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* As = smem;                    // [2][256 * 128]
-  char* Ws = smem + 2 * 256 * 128;    // [2][256 * 128]
+  char* As = smem;                // [2][AST]
+  char* Ws = smem + 2 * AST;      // [2][WST]
   const int id = blockIdx.x;
   const int q = (id % LM_XCD) * a.per_xcd + id / LM_XCD;
   if (q >= a.mtiles * a.ntiles) return;
   const int nt = q / a.mtiles, mt = q - nt * a.mtiles;
-  const int m0 = mt * 256, n0 = nt * 256;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int m0 = mt * TM, n0 = nt * 256;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 2, wn = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
   const int d = a.d, nkb = d / 64;
-  // staging role: 16-byte chunk t % 8 of rows 64 i + t / 8 (i < 4) of both operands;
-  // rows past M or V read row 0 (a valid address) and are zeroed in registers
+  // staging role: 16-byte chunk t % 8 of rows 64 i + t / 8 (hidden rows i < MB,
+  // W rows i < 4); rows past M or V read row 0 (a valid address) and are
+  // zeroed in registers
   const int sr = t >> 3, sc = t & 7;
-  const uint4* ap[4]; const uint4* wp[4]; bool aok[4], wok[4];
+  const uint4* ap[MB]; const uint4* wp[4]; bool aok[MB], wok[4];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = 64 * i + sr;
+    aok[i] = m0 + r < a.M; ap[i] = reinterpret_cast<const uint4*>(a.H + (size_t)(aok[i] ? m0 + r : 0) * d) + sc;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 64 * i + sr;
-    aok[i] = m0 + r < a.M; ap[i] = reinterpret_cast<const uint4*>(a.H + (size_t)(aok[i] ? m0 + r : 0) * d) + sc;
     wok[i] = n0 + r < a.V; wp[i] = reinterpret_cast<const uint4*>(a.W + (size_t)(wok[i] ? n0 + r : 0) * d) + sc;
   }
-  uint4 ra[4], rw[4];
+  uint4 ra[MB], rw[4];
   auto gload = [&](int kb) {
     const size_t o = (size_t)kb * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MB; ++i) {
       const uint4 v = ap[i][o]; ra[i] = aok[i] ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       const uint4 u = wp[i][o]; rw[i] = wok[i] ? u : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(As + buf * 256 * 128 + sw64(64 * i + sr, sc)) = ra[i];
-      *reinterpret_cast<uint4*>(Ws + buf * 256 * 128 + sw64(64 * i + sr, sc)) = rw[i];
-    }
-  };
-  f32x16 acc[4][2];
+    for (int i = 0; i < MB; ++i) *reinterpret_cast<uint4*>(As + buf * AST + sw64(64 * i + sr, sc)) = ra[i];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(Ws + buf * WST + sw64(64 * i + sr, sc)) = rw[i];
+  };
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
-  // this wave's first row; a wave whose rows all lie past M, or whose lower
-  // 64 rows do, skips those matrix instructions
-  const int wrow0 = m0 + 128 * wm;
-  const bool full = a.M - wrow0 > 64;
-  const bool any = a.M > wrow0;
+  // this wave's first row; the wave skips the matrix instructions of its
+  // 32-row blocks that lie wholly past M
+  const int wrow0 = m0 + 32 * MB * wm;
+  const int nblk = a.M > wrow0 ? min(MB, (a.M - wrow0 + 31) / 32) : 0;
   gload(0); lstore(0); __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const bool more = kb + 1 < nkb;
     if (more) gload(kb + 1);
-    const char* Ab = As + (kb & 1) * 256 * 128;
-    const char* Bb = Ws + (kb & 1) * 256 * 128;
-    if (any) {
+    const char* Ab = As + (kb & 1) * AST;
+    const char* Bb = Ws + (kb & 1) * WST;
+    if (nblk > 0) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         // lane half h of step s holds chunk c: k = 8c .. 8c + 7 of the block
@@ -330,9 +344,9 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8k64(LmArgs a) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) bf[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(Bb + sw64(64 * wn + 32 * nb + l32, c)));
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          if (mb < 2 || full) {
-            const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + sw64(128 * wm + 32 * mb + l32, c)));
+        for (int mb = 0; mb < MB; ++mb) {
+          if (mb < nblk) {
+            const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + sw64(32 * MB * wm + 32 * mb + l32, c)));
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[nb], acc[mb][nb], 0, 0, 0);
           }
@@ -341,19 +355,18 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8k64(LmArgs a) {
     }
     if (more) { lstore((kb & 1) ^ 1); __syncthreads(); }
   }
-  const int mblocks = any ? min(4, (a.M - wrow0 + 31) / 32) : 0;
   if (a.stat != TS_NONE) {
     // every wave is done with the staged operands: each takes TS_LDS floats of them
     __syncthreads();
-    tile_stats(a, acc, reinterpret_cast<float*>(smem) + w * TS_LDS, wrow0, mblocks, n0 + 64 * wn, h, l32);
+    tile_stats<MB>(a, acc, reinterpret_cast<float*>(smem) + w * TS_LDS, wrow0, nblk, n0 + 64 * wn, h, l32);
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = n0 + 64 * wn + 32 * nb + l32;
     if (n >= a.V) continue;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb >= mblocks) continue;
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb >= nblk) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = wrow0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -370,42 +383,36 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8k64(LmArgs a) {
 // TS_NONE the epilogue also writes the tile records of the M rows to R, as
 // rows roff .. roff + M - 1 of rstride (records of 64-column tiles, grouped by
 // 256 columns: TileStat), with c2 = log2(e) / T.
+namespace {
+
+// Launches the wide-tile kernel of 64 MB-row tiles; its dynamic LDS limit is
+// raised once per device (setting it twice from racing first calls is harmless).
+template <int MB>
+hipError_t launch_w8(LmArgs a, hipStream_t s) {
+  constexpr int TM = 64 * MB;
+  a.mtiles = (a.M + TM - 1) / TM;
+  a.ntiles = (a.V + 255) / 256;
+  a.per_xcd = (a.mtiles * a.ntiles + LM_XCD - 1) / LM_XCD;
+  static std::atomic<bool> attr_set[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)lm_gemm_w8<MB>, hipFuncAttributeMaxDynamicSharedMemorySize, w8_lds_bytes<MB>());
+    if (e != hipSuccess) return e;
+    attr_set[dev].store(true, std::memory_order_release);
+  }
+  hipLaunchKernelGGL(lm_gemm_w8<MB>, dim3((unsigned)(a.per_xcd * LM_XCD)), dim3(512), w8_lds_bytes<MB>(), s, a);
+  return hipGetLastError();
+}
+
+// Rows wasted in the last tile of M rows, as a fraction of the tiles' rows.
+double tile_waste(int32_t M, int tm) { return 1.0 - (double)M / ((double)tm * ((M + tm - 1) / tm)); }
+
+}  // namespace
+
 hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int32_t V, int32_t d, hipStream_t s,
                           void* R, int32_t rstride, int32_t roff, int stat, float c2) {
-  // the wide tile when 256-row tiles waste no more rows than 128-row ones
-  // (plus 5%): M = 448 takes it, M = 384 does not
-  const double w256 = 1.0 - (double)M / (256.0 * ((M + 255) / 256));
-  const double w128 = 1.0 - (double)M / (128.0 * ((M + 127) / 128));
-  if (d % 64 == 0 && w256 <= w128 + 0.05) {
-    LmArgs a;
-    a.H = static_cast<const uint16_t*>(H);
-    a.W = static_cast<const uint16_t*>(W);
-    a.C = C;
-    a.M = M;
-    a.V = V;
-    a.d = d;
-    a.R = static_cast<uint2*>(R);
-    a.rstride = rstride;
-    a.roff = roff;
-    a.stat = R ? stat : TS_NONE;
-    a.c2 = c2;
-    a.mtiles = (M + 255) / 256;
-    a.ntiles = (V + 255) / 256;
-    a.per_xcd = (a.mtiles * a.ntiles + LM_XCD - 1) / LM_XCD;
-    // 128 KB of dynamic LDS needs the kernel's limit raised, once per device
-    // (setting it twice from racing first calls is harmless)
-    static std::atomic<bool> attr_set[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev].load(std::memory_order_acquire)) {
-      const hipError_t e =
-          hipFuncSetAttribute((const void*)lm_gemm_w8k64, hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 256 * 128);
-      if (e != hipSuccess) return e;
-      attr_set[dev].store(true, std::memory_order_release);
-    }
-    hipLaunchKernelGGL(lm_gemm_w8k64, dim3((unsigned)(a.per_xcd * LM_XCD)), dim3(512), 4 * 256 * 128, s, a);
-    return hipGetLastError();
-  }
   LmArgs a;
   a.H = static_cast<const uint16_t*>(H);
   a.W = static_cast<const uint16_t*>(W);
@@ -418,6 +425,11 @@ hipError_t launch_lm_gemm(const void* H, const void* W, float* C, int32_t M, int
   a.roff = roff;
   a.stat = R ? stat : TS_NONE;
   a.c2 = c2;
+  // The larger tile when its row tiles waste no more rows than the 128-row
+  // tile's (plus 5%): M = 448 takes 256-row tiles, M = 384 192-row tiles.
+  const double w128 = tile_waste(M, 128), w192 = tile_waste(M, 192), w256 = tile_waste(M, 256);
+  if (d % 64 == 0 && w256 <= w128 + 0.05 && w256 <= w192) return launch_w8<4>(a, s);
+  if (d % 64 == 0 && w192 <= w128 + 0.05) return launch_w8<3>(a, s);
   a.mtiles = (M + LM_BM - 1) / LM_BM;
   a.ntiles = (V + LM_BN - 1) / LM_BN;
   a.per_xcd = (a.mtiles * a.ntiles + LM_XCD - 1) / LM_XCD;
