@@ -77,7 +77,7 @@ def measured_traffic(key: str, kernel: str = "stream_kernel", sources=None):
     from the committed counter summary for ``key`` (the workload name,
     "sample-" + name for the draft draw, "ragged-LO-HI-" + name for a ragged
     batch, "probs-" + name for q given as probabilities, the projection
-    workload's name for lm_gemm_kernel), or None when the summary is absent
+    workload's name for "lm_gemm", the two projections), or None when the summary is absent
     or predates the kernel source."""
     path = os.path.join(PROFILES, f"traffic_{kernel}_{key}.md")
     if not os.path.exists(path):
@@ -612,7 +612,7 @@ def run_lmhead(args):
     the target's B(K+1) hidden states times its projection, the draft's BK
     times its own, then verification.  The drafts are drawn on the GPU
     (sv_lm_logits of the draft rows, then sv_sample) before timing.  The two
-    projections (lm_gemm_w8k64 for the target's 448 rows, lm_gemm_kernel for
+    projections (lm_gemm_w8<4> for the target's 448 rows, lm_gemm_w8<3> for
     the draft's 384, whose epilogues also write the tile records the chunk
     records are formed from) are the dominant work; the
     weights (more than the 256 MB last-level cache) are read from HBM at
@@ -693,8 +693,8 @@ def run_lmhead(args):
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
             "frac": achieved / MFMA_BF16_PEAK_TFS,
-            "traffic": measured_traffic(w.name, "lm_gemm_kernel", LM_SOURCES),
-            "kernel": "lm_gemm_w8k64 + lm_gemm_kernel (the target's and the draft's projections together, "
+            "traffic": measured_traffic(w.name, "lm_gemm", LM_SOURCES),
+            "kernel": "lm_gemm_w8<4> + lm_gemm_w8<3> (the target's and the draft's projections together, "
                       "with their tile records); other_kernels_ms: tile_chunk_kernel and the sequence kernel",
             "kernel_ms": gemm_ms,
             "other_kernels_ms": other_ms, "timed_calls": prof["calls"],
