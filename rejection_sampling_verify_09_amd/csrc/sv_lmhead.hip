@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < a.M) a.C[(size_t)m * a.V + n] = acc[mb][nb][r];
+        if (m < a.M) __builtin_nontemporal_store(acc[mb][nb][r], a.C + (size_t)m * a.V + n);
       }
     }
   }
@@ -261,7 +261,10 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
 // operand row per load), both operands in LDS as 128-byte rows whose 16-byte
 // chunks are XOR-swizzled by row (so the fragment reads of 16 consecutive
 // rows hit distinct banks without padding), two stages: 128 KB (MB = 4) or
-// 112 KB (MB = 3) of LDS, one workgroup per CU.  Per flop the 256-row tile
+// 112 KB (MB = 3) of LDS, one workgroup per CU, fed from two register stages
+// (each load is issued two k blocks before its block is multiplied).  The
+// logits are written with non-temporal stores: nothing reads them before the
+// launch ends.  Per flop the 256-row tile
 // moves half the operand bytes of the 128-row tile from L2 and the 192-row
 // tile three quarters (22% less); each W panel is staged by fewer
 // workgroups.
@@ -286,33 +289,28 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8(LmArgs a) {
   const int h = lane >> 5, l32 = lane & 31;
   const int d = a.d, nkb = d / 64;
   // staging role: 16-byte chunk t % 8 of rows 64 i + t / 8 (hidden rows i < MB,
-  // W rows i < 4); rows past M or V read row 0 (a valid address) and are
-  // zeroed in registers
+  // W rows i < 4), read by buffer loads whose resource ends at the tile's
+  // last row below M or V, so rows past them read as zeros
   const int sr = t >> 3, sc = t & 7;
-  const uint4* ap[MB]; const uint4* wp[4]; bool aok[MB], wok[4];
+  const char* abase = reinterpret_cast<const char*>(a.H + (size_t)m0 * d);
+  const char* wbase = reinterpret_cast<const char*>(a.W + (size_t)n0 * d);
+  const int abytes = min(TM, a.M - m0) * d * 2, wbytes = min(256, a.V - n0) * d * 2;
+  int aoff[MB], woff[4];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int r = 64 * i + sr;
-    aok[i] = m0 + r < a.M; ap[i] = reinterpret_cast<const uint4*>(a.H + (size_t)(aok[i] ? m0 + r : 0) * d) + sc;
-  }
+  for (int i = 0; i < MB; ++i) aoff[i] = (64 * i + sr) * d * 2 + sc * 16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 64 * i + sr;
-    wok[i] = n0 + r < a.V; wp[i] = reinterpret_cast<const uint4*>(a.W + (size_t)(wok[i] ? n0 + r : 0) * d) + sc;
-  }
-  uint4 ra[MB], rw[4];
-  auto gload = [&](int kb) {
-    const size_t o = (size_t)kb * 8;
+  for (int i = 0; i < 4; ++i) woff[i] = (64 * i + sr) * d * 2 + sc * 16;
+  // k block kb of both operands into registers: the resources start at the
+  // block, so every offset stays below the bound exactly for valid rows
+  auto gload = [&](uint4 (&ra)[MB], uint4 (&rw)[4], int kb) {
+    const auto rsa = wave_rsrc(abase + kb * 128, abytes - kb * 128);
+    const auto rsw = wave_rsrc(wbase + kb * 128, wbytes - kb * 128);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const uint4 v = ap[i][o]; ra[i] = aok[i] ? v : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int i = 0; i < MB; ++i) ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff[i], 0, 0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 u = wp[i][o]; rw[i] = wok[i] ? u : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int i = 0; i < 4; ++i) rw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsw, woff[i], 0, 0));
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const uint4 (&ra)[MB], const uint4 (&rw)[4], int buf) {
 #pragma unroll
     for (int i = 0; i < MB; ++i) *reinterpret_cast<uint4*>(As + buf * AST + sw64(64 * i + sr, sc)) = ra[i];
 #pragma unroll
@@ -329,31 +327,49 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8(LmArgs a) {
   // 32-row blocks that lie wholly past M
   const int wrow0 = m0 + 32 * MB * wm;
   const int nblk = a.M > wrow0 ? min(MB, (a.M - wrow0 + 31) / 32) : 0;
-  gload(0); lstore(0); __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (more) gload(kb + 1);
-    const char* Ab = As + (kb & 1) * AST;
-    const char* Bb = Ws + (kb & 1) * WST;
-    if (nblk > 0) {
+  auto compute = [&](int buf) {
+    const char* Ab = As + buf * AST;
+    const char* Bb = Ws + buf * WST;
+    if (nblk == 0) return;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        // lane half h of step s holds chunk c: k = 8c .. 8c + 7 of the block
-        const int c = 2 * h + (s & 1) + 4 * (s >> 1);
-        bf16x8 bf[2];
+    for (int s = 0; s < 4; ++s) {
+      // lane half h of step s holds chunk c: k = 8c .. 8c + 7 of the block
+      const int c = 2 * h + (s & 1) + 4 * (s >> 1);
+      bf16x8 bf[2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bf[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(Bb + sw64(64 * wn + 32 * nb + l32, c)));
+      for (int nb = 0; nb < 2; ++nb) bf[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(Bb + sw64(64 * wn + 32 * nb + l32, c)));
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          if (mb < nblk) {
-            const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + sw64(32 * MB * wm + 32 * mb + l32, c)));
+      for (int mb = 0; mb < MB; ++mb) {
+        if (mb < nblk) {
+          const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + sw64(32 * MB * wm + 32 * mb + l32, c)));
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[nb], acc[mb][nb], 0, 0, 0);
-          }
+          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[nb], acc[mb][nb], 0, 0, 0);
         }
       }
     }
-    if (more) { lstore((kb & 1) ^ 1); __syncthreads(); }
+  };
+  // Two register stages ahead of the LDS stage: while block b is multiplied
+  // from LDS, block b + 1 waits in one register set and block b + 2 is
+  // fetched into the other (the set just stored), so each load has two
+  // blocks of matrix work to arrive in.  The loop runs two blocks per pass so
+  // that the register sets are named statically; past the last block the
+  // loads repeat it (in bounds, unused).
+  uint4 ra0[MB], rw0[4], ra1[MB], rw1[4];
+  gload(ra0, rw0, 0);
+  gload(ra1, rw1, min(1, nkb - 1));
+  lstore(ra0, rw0, 0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    gload(ra0, rw0, min(kb + 2, nkb - 1));
+    compute(0);
+    if (kb + 1 >= nkb) break;
+    lstore(ra1, rw1, 1);
+    __syncthreads();
+    gload(ra1, rw1, min(kb + 3, nkb - 1));
+    compute(1);
+    if (kb + 2 >= nkb) break;
+    lstore(ra0, rw0, 0);
+    __syncthreads();
   }
   if (a.stat != TS_NONE) {
     // every wave is done with the staged operands: each takes TS_LDS floats of them
@@ -370,7 +386,7 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8(LmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = wrow0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < a.M) a.C[(size_t)m * a.V + n] = acc[mb][nb][r];
+        if (m < a.M) __builtin_nontemporal_store(acc[mb][nb][r], a.C + (size_t)m * a.V + n);
       }
     }
   }
