@@ -394,7 +394,7 @@ __global__ void __launch_bounds__(512, 1) lm_gemm_w8(LmArgs a) {
 
 }  // namespace
 
-// Shapes the caller has checked: M >= 1, V >= 1, d a positive multiple of 64 (the k block is 32),
+// Shapes the caller has checked: M >= 1, V >= 1, d a positive multiple of 64 (k blocks of 32 and 64),
 // H, W 16-byte aligned, the tile count within the grid limit.  With stat !=
 // TS_NONE the epilogue also writes the tile records of the M rows to R, as
 // rows roff .. roff + M - 1 of rstride (records of 64-column tiles, grouped by
