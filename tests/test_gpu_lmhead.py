@@ -43,10 +43,13 @@ def _device_logits(Hb, Wb):
 @pytest.mark.parametrize("M,V,d", [
     (1, 1, 64),          # one row, one vocabulary entry: every tile guard
     (9, 3001, 128),      # rows below one 32-row block, a ragged last column tile
-    (130, 5000, 192),    # a second row tile holding 2 rows, three k blocks
+    (130, 5000, 192),    # one partial 192-row tile, three k blocks
     (448, 20000, 4096),  # the target's row count and width
     (200, 128256, 256),  # the full vocabulary
-    (257, 4099, 8192),   # three row tiles, V not a multiple of 4, the widest exact grid
+    (257, 4099, 8192),   # two 192-row tiles (65 rows in the second), V not a multiple of 4, the widest exact grid
+    (130, 3000, 320),    # 192-row tiles, five k blocks: the two-block pipeline's odd tail
+    (200, 1500, 448),    # one partial 256-row tile, seven k blocks
+    (384, 2049, 2048),   # the draft's row count (two 192-row tiles), one column past a panel
 ])
 def test_lm_logits_exact_on_the_grid(M, V, d):
     g = np.random.default_rng(M * 7 + V + d)
