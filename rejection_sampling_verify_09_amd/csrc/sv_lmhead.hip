@@ -262,12 +262,11 @@ __global__ void __launch_bounds__(LM_WG, 2) lm_gemm_kernel(LmArgs a) {
 // chunks are XOR-swizzled by row (so the fragment reads of 16 consecutive
 // rows hit distinct banks without padding), two stages: 128 KB (MB = 4) or
 // 112 KB (MB = 3) of LDS, one workgroup per CU, fed from two register stages
-// (each load is issued two k blocks before its block is multiplied).  The
-// logits are written with non-temporal stores: nothing reads them before the
-// launch ends.  Per flop the 256-row tile
-// moves half the operand bytes of the 128-row tile from L2 and the 192-row
-// tile three quarters (22% less); each W panel is staged by fewer
-// workgroups.
+// (each load is issued two k blocks before its block is multiplied).  Per
+// flop the 256-row tile moves half the operand bytes of the 128-row tile
+// from L2 and the 192-row tile three quarters (22% less); each W panel is
+// staged by fewer workgroups.  The logits are written with non-temporal
+// stores: only later launches read them.
 __device__ __forceinline__ int sw64(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }  // byte of chunk c, row r
 template <int MB>
 constexpr int w8_lds_bytes() { return 2 * (64 * MB + 256) * 128; }
